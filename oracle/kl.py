@@ -1,0 +1,215 @@
+"""Plain fp64 CPU oracle of the fused chunked KL loss (TEST INFRASTRUCTURE).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may use this module. It shares no code with the GPU path.
+
+What it computes
+----------------
+The pages describe three ways to compute one and the same distillation loss
+and call them mathematically equivalent; the textbook dense KL is their
+correctness baseline [P1 "Making knowledge distillation cheap enough to run at
+scale", section "Two system changes", the three bullets]. The oracle is that
+definition written out in fp64:
+
+* student logits ``z_i = W . H_i`` over the full vocabulary (the output
+  projection that the fused loss folds into the loss, same section, fused
+  chunked KL bullet); tempered ``s_i = z_i / T``;
+  ``log q_i = s_i - logsumexp(s_i)`` (full-vocabulary log-softmax);
+* teacher: the cached top-K (id, logit) pairs of each position [same page,
+  "Two system changes", offline distillation paragraph]; probability mass is
+  zero outside the top-K and the K logits are renormalised with a softmax at
+  temperature T: ``p_i = softmax(l_i / T)``;
+* per-position forward KL ``KL_i = sum_k p_ik (log p_ik - log q_i[id_ik])``;
+* ``loss = (1/N) sum_i KL_i`` (mean over positions).
+
+Gradient (derived here; the pages say a closed form exists but do not print
+it [P1, section "The resulting student model", last paragraph]): with
+upstream scalar ``g``,
+``dZ_i = g / (N T) * (softmax(s_i) - scatter_add(ids_i, p_i))``,
+``dH = dZ W`` and ``dW = dZ^T H``.
+
+Readings where the pages are silent (temperature on both sides with no T**2
+factor, forward KL direction, mean reduction, duplicate ids add their mass)
+are listed with the rest of the design notes.
+
+Rows are processed in blocks only to bound memory; rows are independent, so
+the block size does not enter the result except through summation order.
+"""
+from __future__ import annotations
+
+import math
+from typing import Dict, Iterable, Tuple
+
+import numpy as np
+
+__all__ = [
+    "teacher_distribution",
+    "student_log_softmax",
+    "forward",
+    "backward",
+    "loss_and_grads",
+    "dense_kl_loss",
+    "sampled_rows",
+]
+
+
+def _f64(x) -> np.ndarray:
+    """Exact upcast of a torch tensor (fp32/bf16) or array to fp64 numpy."""
+    try:
+        import torch
+
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu", torch.float64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.float64)
+
+
+def _ids(x) -> np.ndarray:
+    try:
+        import torch
+
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu", torch.int64).numpy()
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.int64)
+
+
+def _logsumexp_rows(a: np.ndarray) -> np.ndarray:
+    m = a.max(axis=1, keepdims=True)
+    return m[:, 0] + np.log(np.exp(a - m).sum(axis=1))
+
+
+def teacher_distribution(topk_logits, T: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Teacher top-K renormalised at temperature T: returns (p, log p), [N, K].
+
+    The cache keeps the teacher's top-K tokens per position [P1, "Two system
+    changes", offline distillation paragraph]; outside them the teacher mass
+    is taken as zero and the K logits are renormalised with a softmax.
+    """
+    a = _f64(topk_logits) / float(T)
+    logp = a - _logsumexp_rows(a)[:, None]
+    return np.exp(logp), logp
+
+
+def student_log_softmax(H_rows, W, T: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Full-vocabulary student log-softmax of ``z = H W^T`` at temperature T.
+
+    Returns (log q [rows, V], lse [rows]) with ``lse = logsumexp(z / T)``.
+    """
+    s = (_f64(H_rows) @ _f64(W).T) / float(T)
+    lse = _logsumexp_rows(s)
+    return s - lse[:, None], lse
+
+
+def forward(H, W, ids, logits, T: float, block: int = 256) -> Dict[str, object]:
+    """Loss, per-row logsumexp of z/T and per-row KL.
+
+    Returns dict(loss=float, row_lse=[N], row_kl=[N]) in fp64.
+    """
+    H = _f64(H)
+    W = _f64(W)
+    ids = _ids(ids)
+    N = H.shape[0]
+    row_lse = np.empty(N)
+    row_kl = np.empty(N)
+    for r0 in range(0, N, block):
+        r1 = min(N, r0 + block)
+        logq, lse = student_log_softmax(H[r0:r1], W, T)
+        p, logp = teacher_distribution(logits[r0:r1], T)
+        logq_at = np.take_along_axis(logq, ids[r0:r1], axis=1)
+        row_kl[r0:r1] = (p * (logp - logq_at)).sum(axis=1)
+        row_lse[r0:r1] = lse
+    loss = math.fsum(row_kl.tolist()) / N if N else float("nan")
+    return {"loss": loss, "row_lse": row_lse, "row_kl": row_kl}
+
+
+def _dz_rows(H_rows, W, ids_rows, logits_rows, T, coef):
+    logq, _ = student_log_softmax(H_rows, W, T)
+    q = np.exp(logq)
+    p, _ = teacher_distribution(logits_rows, T)
+    target = np.zeros_like(q)
+    rows = np.repeat(np.arange(q.shape[0]), p.shape[1])
+    np.add.at(target, (rows, ids_rows.reshape(-1)), p.reshape(-1))
+    return coef * (q - target)
+
+
+def backward(H, W, ids, logits, T: float, g: float = 1.0,
+             block: int = 256) -> Tuple[np.ndarray, np.ndarray]:
+    """Gradients (dH [N, d], dW [V, d]) of ``g * loss`` in fp64."""
+    H = _f64(H)
+    W = _f64(W)
+    ids = _ids(ids)
+    N = H.shape[0]
+    coef = float(g) / (N * float(T))
+    dH = np.empty_like(H)
+    dW = np.zeros_like(W)
+    for r0 in range(0, N, block):
+        r1 = min(N, r0 + block)
+        dZ = _dz_rows(H[r0:r1], W, ids[r0:r1], logits[r0:r1], T, coef)
+        dH[r0:r1] = dZ @ W
+        dW += dZ.T @ H[r0:r1]
+    return dH, dW
+
+
+def loss_and_grads(H, W, ids, logits, T: float, g: float = 1.0,
+                   block: int = 256) -> Dict[str, object]:
+    out = forward(H, W, ids, logits, T, block)
+    out["dH"], out["dW"] = backward(H, W, ids, logits, T, g, block)
+    return out
+
+
+def dense_kl_loss(H, W, ids, logits, T: float) -> float:
+    """The pages' dense baseline on a tiny problem: build the full teacher
+    probability grid (zeros off the top-K) and the full student log-prob grid,
+    then sum ``P (log P - log Q)`` over the grid where P > 0, divided by N
+    [P1, "Two system changes", dense KL bullet]."""
+    H = _f64(H)
+    W = _f64(W)
+    ids = _ids(ids)
+    N, K = ids.shape
+    V = W.shape[0]
+    a = _f64(logits) / float(T)
+    P = np.zeros((N, V))
+    for i in range(N):
+        e = np.exp(a[i] - a[i].max())
+        for k in range(K):
+            P[i, ids[i, k]] += e[k] / e.sum()
+    Z = H @ W.T / float(T)
+    logQ = np.empty_like(Z)
+    for i in range(N):
+        m = Z[i].max()
+        logQ[i] = Z[i] - (m + math.log(np.exp(Z[i] - m).sum()))
+    total = 0.0
+    for i in range(N):
+        for v in range(V):
+            if P[i, v] > 0:
+                total += P[i, v] * (math.log(P[i, v]) - logQ[i, v])
+    return total / N
+
+
+def sampled_rows(H, W, ids, logits, T: float, rows: Iterable[int],
+                 N_total: int, g: float = 1.0) -> Dict[str, np.ndarray]:
+    """Per-row results for a few rows of a large problem, one row at a time.
+
+    Returns dict(rows, row_lse, row_kl, dH_rows) where ``dH_rows`` are the rows
+    of the gradient of ``g * loss`` for a problem of ``N_total`` positions.
+    """
+    rows = np.asarray(list(rows), dtype=np.int64)
+    Wf = _f64(W)
+    coef = float(g) / (N_total * float(T))
+    lse_out = np.empty(rows.size)
+    kl_out = np.empty(rows.size)
+    dh_out = np.empty((rows.size, Wf.shape[1]))
+    for j, r in enumerate(rows.tolist()):
+        Hr = _f64(H[r:r + 1])
+        idr = _ids(ids[r:r + 1])
+        lgr = _f64(logits[r:r + 1])
+        logq, lse = student_log_softmax(Hr, Wf, T)
+        p, logp = teacher_distribution(lgr, T)
+        kl_out[j] = (p * (logp - np.take_along_axis(logq, idr, axis=1))).sum()
+        lse_out[j] = lse[0]
+        dz = _dz_rows(Hr, Wf, idr, lgr, T, coef)
+        dh_out[j] = (dz @ Wf)[0]
+    return {"rows": rows, "row_lse": lse_out, "row_kl": kl_out, "dH_rows": dh_out}

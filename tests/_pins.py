@@ -1,0 +1,239 @@
+"""Pins that tie the CPU oracle to things other than itself.
+
+Each ``pin_*`` takes an oracle-like module (``forward``, ``backward``,
+``dense_kl_loss``) and raises AssertionError when the module disagrees with
+a closed form, a library routine, finite differences or an invariant of the
+mathematics. ``tests/test_oracle_pins.py`` runs them on the real oracle and on
+mutated copies of it (each mutant must fail at least one pin).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import scipy.special as sps
+import scipy.stats as sst
+import torch
+import torch.nn.functional as F
+
+
+def _rand_problem(rng, N, d, V, K, scale=1.0):
+    H = rng.standard_normal((N, d)) * scale
+    W = rng.standard_normal((V, d)) / math.sqrt(d)
+    ids = np.stack([rng.choice(V, size=K, replace=False) for _ in range(N)])
+    logits = rng.standard_normal((N, K)) * 1.7
+    return H, W, ids, logits
+
+
+def _close(a, b, rtol, atol=0.0, what=""):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    err = np.max(np.abs(a - b)) if a.size else 0.0
+    tol = atol + rtol * (np.max(np.abs(b)) if b.size else 0.0)
+    assert err <= tol, f"{what}: max|diff|={err:.3e} > tol={tol:.3e}"
+
+
+# --- closed forms ----------------------------------------------------------
+
+def pin_two_token_softplus(o):
+    """V = 2, K = 1: KL_i = softplus((z_other - z_id) / T), written with
+    explicit dot products; gradient from the derivative of softplus."""
+    rng = np.random.default_rng(11)
+    N, d, T, g = 4, 3, 1.7, 0.9
+    H = rng.standard_normal((N, d))
+    W = rng.standard_normal((2, d))
+    ids = np.array([[0], [1], [1], [0]])
+    logits = rng.standard_normal((N, 1))
+    kl = []
+    dH = np.zeros((N, d))
+    dW = np.zeros((2, d))
+    for i in range(N):
+        a = ids[i, 0]
+        b = 1 - a
+        za = sum(H[i, j] * W[a, j] for j in range(d))
+        zb = sum(H[i, j] * W[b, j] for j in range(d))
+        u = (zb - za) / T
+        kl.append(math.log1p(math.exp(u)))
+        sig = 1.0 / (1.0 + math.exp(-u))  # d softplus / du
+        c = g / N * sig / T
+        for j in range(d):
+            dH[i, j] = c * (W[b, j] - W[a, j])
+            dW[b, j] += c * H[i, j]
+            dW[a, j] -= c * H[i, j]
+    out = o.forward(H, W, ids, logits, T)
+    _close(out["loss"], sum(kl) / N, 1e-13, what="two-token loss")
+    _close(out["row_kl"], kl, 1e-13, what="two-token row_kl")
+    gdH, gdW = o.backward(H, W, ids, logits, T, g)
+    _close(gdH, dH, 1e-12, what="two-token dH")
+    _close(gdW, dW, 1e-12, what="two-token dW")
+
+
+def pin_uniform_student(o):
+    """W = 0 makes the student uniform: KL_i = log V - entropy(p_i) with the
+    entropy from scipy.stats; dH = 0 and dW_v = g/(N T) sum_i (1/V - P_iv) H_i."""
+    rng = np.random.default_rng(12)
+    N, d, V, K, T, g = 5, 4, 9, 3, 2.0, 1.3
+    H, _, ids, logits = _rand_problem(rng, N, d, V, K)
+    W = np.zeros((V, d))
+    out = o.forward(H, W, ids, logits, T)
+    ent = np.array([sst.entropy(np.exp(logits[i] / T)) for i in range(N)])
+    _close(out["row_kl"], math.log(V) - ent, 1e-12, what="uniform row_kl")
+    _close(out["row_lse"], np.full(N, math.log(V)), 1e-13, what="uniform lse")
+    dH, dW = o.backward(H, W, ids, logits, T, g)
+    assert np.all(dH == 0.0), "uniform student: dH must vanish when W = 0"
+    P = np.zeros((N, V))
+    for i in range(N):
+        pi = sps.softmax(logits[i] / T)
+        for k in range(K):
+            P[i, ids[i, k]] += pi[k]
+    ref = np.zeros((V, d))
+    for v in range(V):
+        for i in range(N):
+            ref[v] += g / (N * T) * (1.0 / V - P[i, v]) * H[i]
+    _close(dW, ref, 1e-12, what="uniform dW")
+
+
+def pin_cross_entropy(o):
+    """K = 1: the teacher is one-hot, so the loss is torch's cross-entropy of
+    Z / T; gradients from torch autograd through that library routine."""
+    rng = np.random.default_rng(13)
+    N, d, V, T, g = 6, 5, 17, 1.5, 0.8
+    H, W, ids, logits = _rand_problem(rng, N, d, V, 1)
+    Ht = torch.tensor(H, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    ce = F.cross_entropy(Ht @ Wt.T / T, torch.tensor(ids[:, 0]))
+    (g * ce).backward()
+    out = o.forward(H, W, ids, logits, T)
+    _close(out["loss"], ce.item(), 1e-13, what="K=1 loss vs cross_entropy")
+    dH, dW = o.backward(H, W, ids, logits, T, g)
+    _close(dH, Ht.grad.numpy(), 1e-12, what="K=1 dH")
+    _close(dW, Wt.grad.numpy(), 1e-12, what="K=1 dW")
+
+
+def pin_dense_grid_libraries(o):
+    """The pages' dense baseline (full teacher grid, zeros off the top-K)
+    evaluated with library routines: scipy rel_entr and torch kl_div."""
+    rng = np.random.default_rng(14)
+    N, d, V, K, T = 5, 4, 13, 4, 1.5
+    H, W, ids, logits = _rand_problem(rng, N, d, V, K)
+    P = np.zeros((N, V))
+    for i in range(N):
+        P[i, ids[i]] = sps.softmax(logits[i] / T)
+    logQ = sps.log_softmax(H @ W.T / T, axis=1)
+    ref1 = sps.rel_entr(P, np.exp(logQ)).sum() / N
+    ref2 = F.kl_div(torch.tensor(logQ), torch.tensor(P), reduction="sum").item() / N
+    _close(ref1, ref2, 1e-12, what="library cross-check")
+    _close(o.forward(H, W, ids, logits, T)["loss"], ref1, 1e-12, what="loss vs rel_entr")
+    _close(o.dense_kl_loss(H, W, ids, logits, T), ref1, 1e-12, what="dense grid vs rel_entr")
+
+
+def pin_equality_case(o):
+    """K = V and teacher logits equal to the student logits: KL = 0 and all
+    gradients vanish, for any T."""
+    rng = np.random.default_rng(15)
+    N, d, V, T = 4, 3, 7, 1.7
+    H = rng.standard_normal((N, d))
+    W = rng.standard_normal((V, d))
+    ids = np.stack([rng.permutation(V) for _ in range(N)])
+    Z = H @ W.T
+    logits = np.take_along_axis(Z, ids, axis=1)
+    out = o.forward(H, W, ids, logits, T)
+    assert abs(out["loss"]) < 1e-13 and np.all(np.abs(out["row_kl"]) < 1e-13), out
+    dH, dW = o.backward(H, W, ids, logits, T, 1.0)
+    assert np.max(np.abs(dH)) < 1e-14 and np.max(np.abs(dW)) < 1e-14
+
+
+# --- finite differences ----------------------------------------------------
+
+def pin_finite_differences(o):
+    """Central differences of g * loss (fp64, h = 1e-6) for every entry of H
+    and W agree with the oracle's dH and dW to rel 1e-6."""
+    rng = np.random.default_rng(16)
+    N, d, V, K, T, g = 3, 5, 11, 3, 1.3, 0.7
+    H, W, ids, logits = _rand_problem(rng, N, d, V, K)
+    dH, dW = o.backward(H, W, ids, logits, T, g)
+    h = 1e-6
+
+    def L(Hx, Wx):
+        return g * o.forward(Hx, Wx, ids, logits, T)["loss"]
+
+    fH = np.zeros_like(H)
+    for idx in np.ndindex(H.shape):
+        Hp = H.copy(); Hp[idx] += h
+        Hm = H.copy(); Hm[idx] -= h
+        fH[idx] = (L(Hp, W) - L(Hm, W)) / (2 * h)
+    fW = np.zeros_like(W)
+    for idx in np.ndindex(W.shape):
+        Wp = W.copy(); Wp[idx] += h
+        Wm = W.copy(); Wm[idx] -= h
+        fW[idx] = (L(H, Wp) - L(H, Wm)) / (2 * h)
+    _close(dH, fH, 1e-6, what="finite differences dH")
+    _close(dW, fW, 1e-6, what="finite differences dW")
+
+
+# --- invariants --------------------------------------------------------------
+
+def pin_invariants(o):
+    rng = np.random.default_rng(17)
+    N, d, V, K, T, g = 9, 6, 23, 5, 1.4, 1.1
+    H, W, ids, logits = _rand_problem(rng, N, d, V, K)
+    base = o.forward(H, W, ids, logits, T)
+    dH, dW = o.backward(H, W, ids, logits, T, g)
+    # KL >= 0 per row
+    assert np.all(base["row_kl"] >= -1e-15), base["row_kl"]
+    # permuting the K (id, logit) pairs changes nothing
+    perm = rng.permutation(K)
+    p2 = o.forward(H, W, ids[:, perm], logits[:, perm], T)
+    _close(p2["row_kl"], base["row_kl"], 1e-13, what="K-permutation row_kl")
+    dH2, dW2 = o.backward(H, W, ids[:, perm], logits[:, perm], T, g)
+    _close(dH2, dH, 1e-13, what="K-permutation dH")
+    _close(dW2, dW, 1e-13, what="K-permutation dW")
+    # permuting rows permutes row outputs and dH, keeps loss and dW
+    rp = rng.permutation(N)
+    r2 = o.forward(H[rp], W, ids[rp], logits[rp], T)
+    _close(r2["loss"], base["loss"], 1e-13, what="row-permutation loss")
+    _close(r2["row_lse"], base["row_lse"][rp], 1e-13, what="row-permutation lse")
+    dH3, dW3 = o.backward(H[rp], W, ids[rp], logits[rp], T, g)
+    _close(dH3, dH[rp], 1e-13, what="row-permutation dH")
+    _close(dW3, dW, 1e-12, what="row-permutation dW")
+    # block (chunk) size does not change the result
+    for blk in (1, 4, N):
+        _close(o.forward(H, W, ids, logits, T, block=blk)["loss"], base["loss"], 1e-13,
+               what=f"block {blk} loss")
+        dHb, dWb = o.backward(H, W, ids, logits, T, g, block=blk)
+        _close(dHb, dH, 1e-13, what=f"block {blk} dH")
+        _close(dWb, dW, 1e-12, what=f"block {blk} dW")
+    # linear in the upstream gradient
+    dH4, dW4 = o.backward(H, W, ids, logits, T, 2.5 * g)
+    _close(dH4, 2.5 * dH, 1e-13, what="linearity dH")
+    _close(dW4, 2.5 * dW, 1e-13, what="linearity dW")
+    # each dZ row sums to zero, so the columns of dW sum to zero
+    _close(dW.sum(axis=0), np.zeros(d), 0.0, atol=1e-14 * max(1.0, np.abs(dW).max() * V),
+           what="column sums of dW")
+    # shifting every row of W by one vector leaves the softmax, hence loss,
+    # dH and dW, unchanged
+    c = rng.standard_normal(d)
+    s = o.forward(H, W + c[None, :], ids, logits, T)
+    _close(s["row_kl"], base["row_kl"], 1e-11, what="W-shift row_kl")
+    dH5, dW5 = o.backward(H, W + c[None, :], ids, logits, T, g)
+    _close(dH5, dH, 1e-10, what="W-shift dH")
+    _close(dW5, dW, 1e-10, what="W-shift dW")
+    # temperature identity: loss(H, W, l, T) = loss(H/T, W, l/T, 1);
+    # dH_T = dH_1(H/T) / T and dW_T = dW_1(H/T)
+    t1 = o.forward(H / T, W, ids, logits / T, 1.0)
+    _close(t1["loss"], base["loss"], 1e-13, what="temperature identity loss")
+    dH6, dW6 = o.backward(H / T, W, ids, logits / T, 1.0, g)
+    # backward at T scales dZ by 1/(N T); at T = 1 by 1/N, hence the 1/T
+    _close(dH6 / T, dH, 1e-12, what="temperature identity dH")
+    _close(dW6, dW, 1e-12, what="temperature identity dW")
+
+
+ALL_PINS = [
+    pin_two_token_softplus,
+    pin_uniform_student,
+    pin_cross_entropy,
+    pin_dense_grid_libraries,
+    pin_equality_case,
+    pin_finite_differences,
+    pin_invariants,
+]

@@ -1,0 +1,58 @@
+"""The CPU oracle, pinned to closed forms, library routines, finite
+differences and invariants; plus mutation checks showing that plausible
+mistakes in the oracle (a dropped term, a wrong sign, a misplaced temperature,
+a misaligned gather) fail at least one pin."""
+import importlib.util
+import os
+import sys
+import types
+
+import numpy as np
+import pytest
+
+from oracle import kl as oracle_kl
+from tests import _pins
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.mark.parametrize("pin", _pins.ALL_PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin):
+    pin(oracle_kl)
+
+
+# (name, original text, replacement) applied to oracle/kl.py's source
+MUTANTS = [
+    ("drop_teacher_entropy", "(p * (logp - logq_at))", "(p * (-logq_at))"),
+    ("kl_sign_flipped", "(p * (logp - logq_at))", "(p * (logq_at - logp))"),
+    ("teacher_no_temperature", "a = _f64(topk_logits) / float(T)", "a = _f64(topk_logits)"),
+    ("student_no_temperature", "s = (_f64(H_rows) @ _f64(W).T) / float(T)",
+     "s = (_f64(H_rows) @ _f64(W).T)"),
+    ("teacher_not_renormalised", "logp = a - _logsumexp_rows(a)[:, None]", "logp = a - a.max()"),
+    ("grad_missing_T", "coef = float(g) / (N * float(T))", "coef = float(g) / N"),
+    ("gather_sorted_ids", "np.add.at(target, (rows, ids_rows.reshape(-1)), p.reshape(-1))",
+     "np.add.at(target, (rows, np.sort(ids_rows, axis=1).reshape(-1)), p.reshape(-1))"),
+    ("dW_wrong_operand", "dW += dZ.T @ H[r0:r1]", "dW += dZ.T @ (H[r0:r1] * 0.5)"),
+    ("sum_not_mean", "loss = math.fsum(row_kl.tolist()) / N if N",
+     "loss = math.fsum(row_kl.tolist()) if N"),
+]
+
+
+def _mutant(orig, new):
+    src = open(os.path.join(ROOT, "oracle", "kl.py")).read()
+    assert src.count(orig) >= 1, f"mutation anchor not found: {orig}"
+    mod = types.ModuleType("oracle_mutant")
+    exec(compile(src.replace(orig, new), "oracle_mutant", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,orig,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(name, orig, new):
+    mod = _mutant(orig, new)
+    failed = []
+    for pin in _pins.ALL_PINS:
+        try:
+            pin(mod)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
