@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused chunked KL loss (forward + backward) on one MI355X.
+
+One step = kdkl_forward + kdkl_backward over one batch of synthetic inputs
+already resident in HBM (every kernel of the path). Prints ONE JSON line.
+
+Default workload: the gpt-oss-20b-like head at 32K tokens
+(N=32768, d=2880, V=201088, K=100, chunk=2048, bf16, T=1).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fused KL fwd+bwd tokens/s; MFMA util % of bf16 peak; peak HBM GiB"
+# MI355X published dense peaks (TFLOP/s) by arithmetic type.
+PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3}
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("kdkl_kernels.hip", "kdkl_api.hip", "kdkl_internal.h"):
+        with open(os.path.join(ROOT, "chunked_kl_loss_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
+    were taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, rows: int):
+    """The CPU oracle, as it stands, on the first `rows` positions of the same
+    workload (full vocabulary and hidden size)."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    H, ids, lg = x["H"][:rows], x["ids"][:rows], x["logits"][:rows]
+    t0 = time.perf_counter()
+    oracle.forward(H, x["W"], ids, lg, w.T)
+    oracle.backward(H, x["W"], ids, lg, w.T)
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {rows} of {w.N} positions of {w.name} (full V={w.V}, d={w.d}); "
+                      f"fp64 numpy forward+backward, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="gptoss20b_32k")
+    ap.add_argument("--N", type=int, default=None, help="override the number of positions")
+    ap.add_argument("--chunk", type=int, default=None, help="override the chunk size")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the multi-GPU sharding is a design note, not code)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import chunked_kl_loss_amd as kd
+    import workloads as wl
+
+    w = wl.get_config(args.config)
+    if args.N is not None:
+        w = w.with_(N=args.N)
+    if args.chunk is not None:
+        w = w.with_(chunk=args.chunk)
+    dev = torch.device("cuda:0")
+    log(f"bench: generating {w.name} N={w.N} d={w.d} V={w.V} K={w.K} chunk={w.chunk} T={w.T}")
+    t0 = time.time()
+    x = wl.generate(w)
+    log(f"bench: inputs generated in {time.time() - t0:.1f} s")
+    torch.cuda.reset_peak_memory_stats(dev)
+    H, W, ids, lg = (x[k].to(dev) for k in ("H", "W", "ids", "logits"))
+    fb, bb = kd.workspace_size(w.N, w.d, w.V, w.K, w.chunk, H.dtype)
+    ws_f = torch.empty(fb, dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(bb, dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    row_lse = torch.empty(w.N, dtype=torch.float32, device=dev)
+    dH = torch.empty_like(H)
+    dW = torch.empty((w.V, w.d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        kd.kdkl_forward(H, W, ids, lg, w.T, w.chunk, loss=loss, row_lse=row_lse,
+                        workspace=ws_f, stream=stream, want_row_kl=False)
+        kd.kdkl_backward(H, W, ids, lg, w.T, w.chunk, row_lse, None, dH=dH, dW=dW,
+                         workspace=ws_b, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    log(f"bench: warmup done, loss={loss.item():.6f}")
+
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    kd.profile_begin()
+    torch.cuda.synchronize(dev)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    kstats = kd.profile_end()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    peak_gib = torch.cuda.max_memory_allocated(dev) / 2**30
+    log(f"bench: {ms:.2f} ms/step")
+
+    dtype = "bf16" if w.dtype == "bf16" else "fp32"
+    flops_step = 8.0 * w.N * w.V * w.d
+    peak = PEAK_TFLOPS[dtype]
+    tok_s = w.N / (ms / 1e3)
+    mfma_pct = 100.0 * flops_step / (ms / 1e3) / (peak * 1e12)
+
+    kernels = {}
+    for name, s in kstats.items():
+        kernels[name] = {
+            "launches_per_step": s["launches"] / args.steps,
+            "avg_ms": s["total_ms"] / max(1, s["launches"]),
+            "ms_per_step": s["total_ms"] / args.steps,
+            "tflops": (s["flops"] / (s["total_ms"] / 1e3) / 1e12) if s["total_ms"] > 0 else 0.0,
+            "gbs": (s["bytes"] / (s["total_ms"] / 1e3) / 1e9) if s["total_ms"] > 0 else 0.0,
+        }
+    dom = max(kstats, key=lambda k: kstats[k]["total_ms"])
+    ds = kstats[dom]
+    achieved = ds["flops"] / (ds["total_ms"] / 1e3) / 1e12
+    traffic = load_traffic(dom, w.name)
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                "traffic": traffic,
+                "avg_launch_ms": round(ds["total_ms"] / ds["launches"], 4),
+                "flop_per_launch": ds["flops"] / ds["launches"]}
+
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": w.name, "N": w.N, "d": w.d, "V": w.V, "K": w.K, "chunk": w.chunk,
+                   "T": w.T, "teacher_ids": w.id_dist, "teacher_logit_var": w.logit_var,
+                   "parallelism": "single GPU"},
+        "mfma_util_pct": round(mfma_pct, 2),
+        "flop_per_step": flops_step,
+        "peak_hbm_gib": round(peak_gib, 3),
+        "workspace_gib": {"forward": round(fb / 2**30, 3), "backward": round(bb / 2**30, 3)},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        rows = min(args.cpu_rows, w.N)
+        log(f"bench: timing the CPU oracle on {rows} positions")
+        out["cpu_baseline"] = cpu_baseline(w, x, rows)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

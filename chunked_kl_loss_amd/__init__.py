@@ -1,0 +1,164 @@
+"""Fused chunked KL-divergence loss for offline top-K distillation on MI355X.
+
+Thin Python binding over ``libkdkl.so`` (C-ABI declared in ``include/kdkl.h``).
+Every step of the loss runs in the library's HIP kernels; this module only
+marshals torch tensors (device memory) and the current HIP stream. There is
+no CPU fallback: without the built library, or without a GPU, calls raise.
+
+The loss is the fused chunked KL of P1 "Making knowledge distillation cheap
+enough to run at scale" (section "Two system changes"): per slice of
+positions, project hidden states to logits, fold into the running loss, drop
+the slice; recompute each slice in backward.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from typing import Optional, Tuple
+
+import torch
+
+from ._lib import KDKL_BF16, KDKL_F32, KdklError, KernelStat, check, load as _load
+
+__all__ = [
+    "workspace_size",
+    "kdkl_forward",
+    "kdkl_backward",
+    "FusedKLLoss",
+    "fused_kl_loss",
+    "profile_begin",
+    "profile_end",
+    "KdklError",
+]
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDKL_BF16
+    if t.dtype == torch.float32:
+        return KDKL_F32
+    raise TypeError(f"H/W must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device, stream) -> C.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return C.c_void_p(stream.cuda_stream)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("inputs must be contiguous tensors on a ROCm device")
+
+
+def workspace_size(N: int, d: int, V: int, K: int, chunk: int, dtype: torch.dtype) -> Tuple[int, int]:
+    """(forward bytes, backward bytes) of device workspace."""
+    f = C.c_size_t()
+    b = C.c_size_t()
+    code = KDKL_BF16 if dtype == torch.bfloat16 else KDKL_F32
+    check(_load().kdkl_workspace_size(N, d, V, K, chunk, code, C.byref(f), C.byref(b)),
+          "kdkl_workspace_size")
+    return f.value, b.value
+
+
+def _check_shapes(H, W, ids, logits):
+    N, d = H.shape
+    V, d2 = W.shape
+    if d2 != d or ids.shape != logits.shape or ids.shape[0] != N:
+        raise ValueError("shape mismatch among H [N,d], W [V,d], ids/logits [N,K]")
+    if H.dtype != W.dtype or ids.dtype != torch.int32 or logits.dtype != torch.float32:
+        raise TypeError("H and W share a dtype; ids int32; logits float32")
+    return N, d, V, ids.shape[1]
+
+
+def kdkl_forward(H, W, ids, logits, T: float, chunk: int, *, loss=None, row_lse=None,
+                 row_kl=None, workspace=None, stream=None, want_row_kl: bool = True):
+    """Run ``kdkl_forward``; returns (loss [1] fp32, row_lse [N], row_kl [N] or None)."""
+    _need_gpu(H, W, ids, logits)
+    N, d, V, K = _check_shapes(H, W, ids, logits)
+    dev = H.device
+    if loss is None:
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+    if row_lse is None:
+        row_lse = torch.empty(N, dtype=torch.float32, device=dev)
+    if row_kl is None and want_row_kl:
+        row_kl = torch.empty(N, dtype=torch.float32, device=dev)
+    fb, _ = workspace_size(N, d, V, K, chunk, H.dtype)
+    if workspace is None:
+        workspace = torch.empty(fb, dtype=torch.uint8, device=dev)
+    check(_load().kdkl_forward(_ptr(H), _ptr(W), _ptr(ids), _ptr(logits), N, d, V, K,
+                              float(T), chunk, _dtype_code(H), _ptr(loss), _ptr(row_lse),
+                              _ptr(row_kl), _ptr(workspace), workspace.numel(),
+                              _stream(dev, stream)),
+          "kdkl_forward")
+    return loss, row_lse, row_kl
+
+
+def kdkl_backward(H, W, ids, logits, T: float, chunk: int, row_lse, grad_loss=None, *,
+                  dH=None, dW=None, accumulate_dW: bool = False, workspace=None, stream=None):
+    """Run ``kdkl_backward``; returns (dH [N,d] in H's dtype, dW [V,d] fp32)."""
+    _need_gpu(H, W, ids, logits, row_lse, grad_loss)
+    N, d, V, K = _check_shapes(H, W, ids, logits)
+    dev = H.device
+    if dH is None:
+        dH = torch.empty_like(H)
+    if dW is None:
+        dW = torch.empty((V, d), dtype=torch.float32, device=dev)
+    if grad_loss is not None and grad_loss.dtype != torch.float32:
+        raise TypeError("grad_loss must be float32")
+    _, bb = workspace_size(N, d, V, K, chunk, H.dtype)
+    if workspace is None:
+        workspace = torch.empty(bb, dtype=torch.uint8, device=dev)
+    check(_load().kdkl_backward(_ptr(H), _ptr(W), _ptr(ids), _ptr(logits), N, d, V, K,
+                               float(T), chunk, _dtype_code(H), _ptr(row_lse),
+                               _ptr(grad_loss), _ptr(dH), _ptr(dW), int(bool(accumulate_dW)),
+                               _ptr(workspace), workspace.numel(), _stream(dev, stream)),
+          "kdkl_backward")
+    return dH, dW
+
+
+class FusedKLLoss(torch.autograd.Function):
+    """Autograd wrapper: forward saves only row_lse (N floats); backward
+    recomputes each chunk's logits inside the library."""
+
+    @staticmethod
+    def forward(ctx, H, W, ids, logits, T: float, chunk: int):
+        loss, row_lse, _ = kdkl_forward(H, W, ids, logits, T, chunk, want_row_kl=False)
+        ctx.save_for_backward(H, W, ids, logits, row_lse)
+        ctx.T = T
+        ctx.chunk = chunk
+        return loss[0]
+
+    @staticmethod
+    def backward(ctx, g):
+        H, W, ids, logits, row_lse = ctx.saved_tensors
+        g = g.reshape(1).to(torch.float32).contiguous()
+        dH, dW = kdkl_backward(H, W, ids, logits, ctx.T, ctx.chunk, row_lse, g)
+        return dH, dW.to(W.dtype), None, None, None, None
+
+
+def fused_kl_loss(H, W, ids, logits, T: float = 1.0, chunk: int = 2048):
+    """Mean over positions of KL(teacher top-K || student), differentiable in H and W."""
+    return FusedKLLoss.apply(H, W, ids, logits, T, chunk)
+
+
+def profile_begin():
+    check(_load().kdkl_profile_begin(), "kdkl_profile_begin")
+
+
+def profile_end():
+    """Stop profiling; returns {kernel name: dict(launches, total_ms, flops, bytes)}."""
+    cap = 32
+    arr = (KernelStat * cap)()
+    n = C.c_int()
+    check(_load().kdkl_profile_end(arr, cap, C.byref(n)), "kdkl_profile_end")
+    out = {}
+    for i in range(min(n.value, cap)):
+        s = arr[i]
+        out[s.name.decode()] = {"launches": s.launches, "total_ms": s.total_ms,
+                                "flops": s.flops, "bytes": s.bytes}
+    return out

@@ -1,0 +1,76 @@
+"""ctypes loader for libkdkl.so (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libkdkl.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "kdkl.h")
+
+KDKL_F32 = 0
+KDKL_BF16 = 1
+STATUS = {
+    0: "KDKL_OK", 1: "KDKL_ERR_NULL", 2: "KDKL_ERR_SHAPE", 3: "KDKL_ERR_VALUE",
+    4: "KDKL_ERR_DTYPE", 5: "KDKL_ERR_WORKSPACE", 6: "KDKL_ERR_OVERFLOW",
+    7: "KDKL_ERR_HIP", 8: "KDKL_ERR_ALIGN",
+}
+
+
+class KdklError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = status
+        super().__init__(f"{what}: {load().kdkl_status_string(status).decode()}")
+
+
+class KernelStat(C.Structure):
+    _fields_ = [
+        ("name", C.c_char * 48),
+        ("launches", C.c_int64),
+        ("total_ms", C.c_double),
+        ("flops", C.c_double),
+        ("bytes", C.c_double),
+    ]
+
+
+_LIB = None
+_P = C.c_void_p
+_I64 = C.c_int64
+_I32 = C.c_int32
+
+SIGNATURES = {
+    "kdkl_abi_version": (C.c_int, []),
+    "kdkl_status_string": (C.c_char_p, [C.c_int]),
+    "kdkl_workspace_size": (C.c_int, [_I64, _I64, _I64, _I32, _I64, C.c_int,
+                                      C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
+    "kdkl_forward": (C.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, C.c_float, _I64,
+                               C.c_int, _P, _P, _P, _P, C.c_size_t, _P]),
+    "kdkl_backward": (C.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, C.c_float, _I64,
+                                C.c_int, _P, _P, _P, _P, C.c_int, _P, C.c_size_t, _P]),
+    "kdkl_profile_begin": (C.c_int, []),
+    "kdkl_profile_end": (C.c_int, [C.POINTER(KernelStat), C.c_int, C.POINTER(C.c_int)]),
+}
+
+
+def load():
+    """Load libkdkl.so; fails loudly when it has not been built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} not found: build the HIP library first "
+                "(python -c 'import __graft_entry__ as g; g.build()')")
+        lib = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if lib.kdkl_abi_version() != 1:
+            raise ImportError("libkdkl.so ABI version mismatch")
+        _LIB = lib
+    return _LIB
+
+
+def check(status: int, what: str):
+    if status != 0:
+        raise KdklError(status, what)

@@ -1,0 +1,381 @@
+// C-ABI entry points of libkdkl.so: argument checks, workspace plan, and the
+// per-chunk launch sequence of the fused chunked KL loss (forward: project,
+// fold into the running loss, drop; backward: recompute each chunk's
+// projection) [P1 "Making knowledge distillation cheap enough to run at
+// scale", section "Two system changes", fused chunked KL bullet].
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "../../include/kdkl.h"
+#include "kdkl_internal.h"
+
+namespace kdkl {
+
+const char* kernel_name(int id) {
+  static const char* names[K_COUNT] = {
+      "teacher_prep", "fwd_gemm_lse", "split_merge", "loss_reduce", "transpose_w",
+      "transpose_h",  "dz_gemm",      "dh_gemm",     "dh_reduce",   "dw_gemm"};
+  return (id >= 0 && id < K_COUNT) ? names[id] : "?";
+}
+
+// ------------------------------ profiling ---------------------------------
+namespace {
+struct Rec {
+  int kid;
+  hipEvent_t a, b;
+  double flops, bytes;
+};
+struct Prof {
+  std::mutex mu;
+  bool on = false;
+  std::vector<Rec> recs;
+  std::vector<hipEvent_t> pool;
+} g_prof;
+
+hipEvent_t prof_event() {
+  if (!g_prof.pool.empty()) {
+    hipEvent_t e = g_prof.pool.back();
+    g_prof.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch` bracketed by events when profiling is on.
+template <class F>
+hipError_t timed(int kid, double flops, double bytes, hipStream_t s, F&& launch) {
+  if (!g_prof.on) return launch();
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  hipEvent_t a = prof_event(), b = prof_event();
+  if (!a || !b) return hipErrorOutOfMemory;
+  hipError_t e = hipEventRecord(a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(b, s);
+  if (e != hipSuccess) return e;
+  g_prof.recs.push_back({kid, a, b, flops, bytes});
+  return hipSuccess;
+}
+}  // namespace
+
+// ------------------------------ planning ----------------------------------
+static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct Plan {
+  int64_t N, d, V, K, chunk;
+  int dtype;
+  int64_t es;      // element bytes of H, W, dZ, dH
+  int64_t Cp;      // chunk capacity (multiple of the token tile)
+  int64_t Vp;      // padded vocabulary (multiple of the vocabulary tile)
+  int64_t n_vt;    // vocabulary tiles
+  int dh_splits;
+  int64_t dh_ksplit;
+  // offsets into the forward workspace
+  size_t f_sids, f_sp, f_erow, f_tstart, f_part, f_rowkl, f_bytes;
+  // offsets into the backward workspace
+  size_t b_sids, b_sp, b_erow, b_tstart, b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart, b_bytes;
+};
+
+static bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  return !__builtin_mul_overflow(a, b, out) && *out >= 0;
+}
+
+// Adds a 256-byte aligned region of `bytes` at *cursor; false on overflow.
+static bool region(size_t* cursor, int64_t bytes, size_t* off) {
+  const size_t c = (size_t)round_up((int64_t)*cursor, 256);
+  if (bytes < 0 || c > SIZE_MAX - (size_t)bytes) return false;
+  *off = c;
+  *cursor = c + (size_t)bytes;
+  return true;
+}
+
+static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int dtype,
+                             Plan* P) {
+  if (dtype != KDKL_F32 && dtype != KDKL_BF16) return KDKL_ERR_DTYPE;
+  const int64_t dmul = dtype == KDKL_BF16 ? 8 : 4;
+  if (N < 0 || d <= 0 || V <= 0 || K <= 0 || chunk <= 0) return KDKL_ERR_SHAPE;
+  if (d % dmul != 0 || K > 1024 || K > V) return KDKL_ERR_SHAPE;
+  if (N > INT32_MAX || V > INT32_MAX - 4096 || d > (1 << 24)) return KDKL_ERR_OVERFLOW;
+  P->N = N; P->d = d; P->V = V; P->K = K; P->dtype = dtype;
+  P->es = dtype == KDKL_BF16 ? 2 : 4;
+  P->chunk = chunk < N ? chunk : (N > 0 ? N : 1);
+  P->Cp = round_up(P->chunk, kTokenTile);
+  P->Vp = round_up(V, kVocabTile);
+  P->n_vt = P->Vp / kVocabTile;
+  if (P->Cp > INT32_MAX / 2) return KDKL_ERR_OVERFLOW;
+  // dH split-K: enough workgroups to cover the 256 CUs a few times over,
+  // each split at least 8 k-steps long.
+  const int64_t tiles = ((P->Cp + 255) / 256) * ((d + 255) / 256);
+  int64_t S = (768 + tiles - 1) / tiles;
+  const int64_t kstep = dtype == KDKL_BF16 ? 64 : 32;
+  const int64_t smax = P->Vp / (8 * kstep);
+  if (S > smax) S = smax;
+  if (S > 16) S = 16;
+  if (S < 1) S = 1;
+  P->dh_splits = (int)S;
+  P->dh_ksplit = round_up((P->Vp + S - 1) / S, kstep);
+
+  int64_t t0, t1, t2;
+  size_t cur = 0;
+  bool ok = true;
+  ok &= mul_ok(P->Cp, K, &t0) && mul_ok(t0, 4, &t0);
+  ok &= region(&cur, t0, &P->f_sids) && region(&cur, t0, &P->f_sp);
+  ok &= region(&cur, P->Cp * 4, &P->f_erow);
+  ok &= mul_ok(P->n_vt + 1, P->Cp, &t1) && mul_ok(t1, 2, &t1);
+  ok &= region(&cur, t1, &P->f_tstart);
+  ok &= mul_ok(P->Cp, P->n_vt, &t2) && mul_ok(t2, 16, &t2);
+  ok &= region(&cur, t2, &P->f_part);
+  ok &= region(&cur, (N > 0 ? N : 1) * 4, &P->f_rowkl);
+  P->f_bytes = cur;
+
+  cur = 0;
+  ok &= region(&cur, t0, &P->b_sids) && region(&cur, t0, &P->b_sp);
+  ok &= region(&cur, P->Cp * 4, &P->b_erow);
+  ok &= region(&cur, t1, &P->b_tstart);
+  int64_t wt, ht, dz, dhp;
+  ok &= mul_ok(d, P->Vp, &wt) && mul_ok(wt, P->es, &wt);
+  ok &= region(&cur, wt, &P->b_wt);
+  ok &= mul_ok(d, P->Cp, &ht) && mul_ok(ht, P->es, &ht);
+  ok &= region(&cur, ht, &P->b_ht);
+  ok &= mul_ok(P->Cp, P->Vp, &dz) && mul_ok(dz, P->es, &dz);
+  ok &= region(&cur, dz, &P->b_dzcv) && region(&cur, dz, &P->b_dzvc);
+  ok &= mul_ok(S * P->Cp, d, &dhp) && mul_ok(dhp, 4, &dhp);
+  ok &= region(&cur, dhp, &P->b_dhpart);
+  P->b_bytes = cur;
+  return ok ? KDKL_OK : KDKL_ERR_OVERFLOW;
+}
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static kdkl_status check_common(const void* H, const void* W, const int32_t* ids, const float* lg,
+                                int64_t N, float T) {
+  if (!W) return KDKL_ERR_NULL;
+  if (N > 0 && (!H || !ids || !lg)) return KDKL_ERR_NULL;
+  if (!(T > 0.f) || !isfinite(T)) return KDKL_ERR_VALUE;
+  if (!aligned16(H) || !aligned16(W)) return KDKL_ERR_ALIGN;
+  return KDKL_OK;
+}
+
+static TeacherArgs teacher_args(const Plan& P, const int32_t* ids, const float* lg, float T, int64_t r0,
+                                int rows, char* ws, size_t o_sids, size_t o_sp, size_t o_erow,
+                                size_t o_tstart) {
+  TeacherArgs t;
+  t.ids = ids; t.logits = lg; t.r0 = r0; t.rows = rows; t.K = (int)P.K;
+  t.inv_T = 1.0f / T; t.n_vt = (int)P.n_vt; t.Cp = P.Cp;
+  t.sids = (int32_t*)(ws + o_sids); t.sp = (float*)(ws + o_sp);
+  t.erow = (float*)(ws + o_erow); t.tstart = (uint16_t*)(ws + o_tstart);
+  return t;
+}
+
+static GemmArgs projection_args(const Plan& P, const void* H, const void* W, float T, int64_t r0,
+                                int rows, char* ws, size_t o_sids, size_t o_sp, size_t o_tstart) {
+  GemmArgs g;
+  memset(&g, 0, sizeof(g));
+  g.A = W; g.lda = P.d;
+  g.B = (const char*)H + r0 * P.d * P.es; g.ldb = P.d;
+  g.M = (int)P.V; g.N = rows;
+  g.k_end = P.d; g.k_split = P.d;
+  g.tiles_m = (int)P.n_vt; g.tiles_n = (int)((rows + kTokenTile - 1) / kTokenTile); g.splits = 1;
+  g.inv_T = 1.0f / T; g.V = (int)P.V; g.K = (int)P.K; g.Cp = P.Cp; g.n_vt = (int)P.n_vt;
+  g.sids = (const int32_t*)(ws + o_sids); g.sp = (const float*)(ws + o_sp);
+  g.tstart = (const uint16_t*)(ws + o_tstart);
+  g.Vp = P.Vp;
+  return g;
+}
+
+}  // namespace kdkl
+
+using namespace kdkl;
+
+extern "C" {
+
+int kdkl_abi_version(void) { return KDKL_ABI_VERSION; }
+
+const char* kdkl_status_string(int s) {
+  switch (s) {
+    case KDKL_OK: return "KDKL_OK";
+    case KDKL_ERR_NULL: return "KDKL_ERR_NULL: a required pointer is NULL";
+    case KDKL_ERR_SHAPE: return "KDKL_ERR_SHAPE: a size is out of range";
+    case KDKL_ERR_VALUE: return "KDKL_ERR_VALUE: temperature must be finite and > 0";
+    case KDKL_ERR_DTYPE: return "KDKL_ERR_DTYPE: unsupported dtype";
+    case KDKL_ERR_WORKSPACE: return "KDKL_ERR_WORKSPACE: workspace too small";
+    case KDKL_ERR_OVERFLOW: return "KDKL_ERR_OVERFLOW: size overflow";
+    case KDKL_ERR_HIP: return "KDKL_ERR_HIP: HIP launch or runtime failure";
+    case KDKL_ERR_ALIGN: return "KDKL_ERR_ALIGN: pointer not 16-byte aligned";
+    default: return "KDKL_ERR_UNKNOWN";
+  }
+}
+
+kdkl_status kdkl_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int dtype,
+                                size_t* fwd_bytes, size_t* bwd_bytes) {
+  Plan P;
+  kdkl_status st = make_plan(N, d, V, K, chunk, dtype, &P);
+  if (st != KDKL_OK) return st;
+  if (fwd_bytes) *fwd_bytes = P.f_bytes;
+  if (bwd_bytes) *bwd_bytes = P.b_bytes;
+  return KDKL_OK;
+}
+
+kdkl_status kdkl_forward(const void* H, const void* W, const int32_t* ids, const float* lg, int64_t N,
+                         int64_t d, int64_t V, int32_t K, float T, int64_t chunk, int dtype, float* loss,
+                         float* row_lse, float* row_kl, void* workspace, size_t workspace_bytes,
+                         void* stream) {
+  Plan P;
+  kdkl_status st = make_plan(N, d, V, K, chunk, dtype, &P);
+  if (st != KDKL_OK) return st;
+  if ((st = check_common(H, W, ids, lg, N, T)) != KDKL_OK) return st;
+  if (!loss || (N > 0 && !row_lse) || !workspace) return KDKL_ERR_NULL;
+  if (workspace_bytes < P.f_bytes) return KDKL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KDKL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* kl = row_kl ? row_kl : (float*)(ws + P.f_rowkl);
+  hipError_t e = hipSuccess;
+  for (int64_t r0 = 0; r0 < N && e == hipSuccess; r0 += P.chunk) {
+    const int rows = (int)((N - r0) < P.chunk ? (N - r0) : P.chunk);
+    TeacherArgs ta = teacher_args(P, ids, lg, T, r0, rows, ws, P.f_sids, P.f_sp, P.f_erow, P.f_tstart);
+    e = timed(K_TEACHER, 0.0, (double)rows * P.K * 8.0 * 2.0, s, [&] { return launch_teacher(ta, s); });
+    if (e != hipSuccess) break;
+    GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.f_sids, P.f_sp, P.f_tstart);
+    g.part = (float4*)(ws + P.f_part);
+    const double fl = 2.0 * rows * (double)V * d;
+    const double by = ((double)V + rows) * d * P.es + (double)rows * P.n_vt * 16.0;
+    e = timed(K_FWD_GEMM, fl, by, s, [&] { return launch_gemm(dtype, EPI_FWD, g, s); });
+    if (e != hipSuccess) break;
+    MergeArgs m;
+    m.part = (const float4*)(ws + P.f_part); m.n_vt = (int)P.n_vt; m.rows = rows;
+    m.erow = (const float*)(ws + P.f_erow); m.row_lse = row_lse + r0; m.row_kl = kl + r0;
+    e = timed(K_MERGE, 0.0, (double)rows * P.n_vt * 16.0, s, [&] { return launch_merge(m, s); });
+  }
+  if (e == hipSuccess)
+    e = timed(K_LOSS, 0.0, (double)N * 4.0, s, [&] { return launch_loss(kl, N, loss, s); });
+  return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
+}
+
+kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, const float* lg, int64_t N,
+                          int64_t d, int64_t V, int32_t K, float T, int64_t chunk, int dtype,
+                          const float* row_lse, const float* grad_loss, void* dH, float* dW,
+                          int accumulate_dW, void* workspace, size_t workspace_bytes, void* stream) {
+  Plan P;
+  kdkl_status st = make_plan(N, d, V, K, chunk, dtype, &P);
+  if (st != KDKL_OK) return st;
+  if ((st = check_common(H, W, ids, lg, N, T)) != KDKL_OK) return st;
+  if (!dW || !workspace || (N > 0 && (!row_lse || !dH))) return KDKL_ERR_NULL;
+  if (workspace_bytes < P.b_bytes) return KDKL_ERR_WORKSPACE;
+  if (!aligned16(workspace) || !aligned16(dW) || !aligned16(dH)) return KDKL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  hipError_t e = hipSuccess;
+  if (N == 0) {
+    if (!accumulate_dW) e = launch_zero(dW, V * d, s);
+    return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
+  }
+  // W^T [d, Vp], zero-padded, once per call: the dH product contracts over V.
+  e = timed(K_TRANSPOSE_W, 0.0, 2.0 * (double)V * d * P.es, s, [&] {
+    return launch_transpose((int)P.es, W, V, d, d, ws + P.b_wt, P.Vp, P.Vp, s);
+  });
+  const double coef_base = 1.0 / ((double)N * (double)T);
+  for (int64_t r0 = 0; r0 < N && e == hipSuccess; r0 += P.chunk) {
+    const int rows = (int)((N - r0) < P.chunk ? (N - r0) : P.chunk);
+    const int64_t rows_pad = round_up(rows, kTokenTile);
+    TeacherArgs ta = teacher_args(P, ids, lg, T, r0, rows, ws, P.b_sids, P.b_sp, P.b_erow, P.b_tstart);
+    e = timed(K_TEACHER, 0.0, (double)rows * P.K * 8.0 * 2.0, s, [&] { return launch_teacher(ta, s); });
+    if (e != hipSuccess) break;
+    // H_c^T [d, Cp], zero-padded past the chunk's rows: the dW product
+    // contracts over the chunk's tokens.
+    const char* Hc = (const char*)H + r0 * d * P.es;
+    e = timed(K_TRANSPOSE_H, 0.0, 2.0 * (double)rows * d * P.es, s, [&] {
+      return launch_transpose((int)P.es, Hc, rows, d, d, ws + P.b_ht, rows_pad, P.Cp, s);
+    });
+    if (e != hipSuccess) break;
+    // recompute the chunk's logits and form dZ in both layouts
+    GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.b_sids, P.b_sp, P.b_tstart);
+    g.row_lse = row_lse + r0; g.grad = grad_loss; g.coef_base = (float)coef_base;
+    g.dz_cv = ws + P.b_dzcv; g.dz_vc = ws + P.b_dzvc;
+    const double fl = 2.0 * rows * (double)V * d;
+    e = timed(K_DZ_GEMM, fl, ((double)V + rows) * d * P.es + 2.0 * rows * (double)V * P.es, s,
+              [&] { return launch_gemm(dtype, EPI_DZ, g, s); });
+    if (e != hipSuccess) break;
+    // dH_c = dZ_c W  (split over the vocabulary, then a fixed-order sum)
+    GemmArgs h;
+    memset(&h, 0, sizeof(h));
+    h.A = ws + P.b_dzcv; h.lda = P.Vp; h.B = ws + P.b_wt; h.ldb = P.Vp;
+    h.M = rows; h.N = (int)d; h.k_end = P.Vp; h.k_split = P.dh_ksplit;
+    h.tiles_m = (int)((rows + 255) / 256); h.tiles_n = (int)((d + 255) / 256);
+    h.splits = (int)((P.Vp + P.dh_ksplit - 1) / P.dh_ksplit);
+    h.out = (float*)(ws + P.b_dhpart); h.ldo = d; h.Cp = P.Cp;
+    const int splits = h.splits;
+    e = timed(K_DH_GEMM, fl, ((double)V * rows + (double)V * d) * P.es + 4.0 * splits * rows * d, s,
+              [&] { return launch_gemm(dtype, EPI_DH, h, s); });
+    if (e != hipSuccess) break;
+    void* dHc = (char*)dH + r0 * d * P.es;
+    e = timed(K_DH_REDUCE, 0.0, 4.0 * splits * rows * d + (double)rows * d * P.es, s, [&] {
+      return launch_dh_reduce(dtype, (const float*)(ws + P.b_dhpart), splits, rows, d, P.Cp, dHc, s);
+    });
+    if (e != hipSuccess) break;
+    // dW (+)= dZ_c^T H_c
+    GemmArgs w;
+    memset(&w, 0, sizeof(w));
+    w.A = ws + P.b_dzvc; w.lda = P.Cp; w.B = ws + P.b_ht; w.ldb = P.Cp;
+    w.M = (int)V; w.N = (int)d; w.k_end = rows_pad; w.k_split = rows_pad;
+    w.tiles_m = (int)P.n_vt; w.tiles_n = (int)((d + 255) / 256); w.splits = 1;
+    w.out = dW; w.ldo = d; w.accumulate = (r0 > 0 || accumulate_dW) ? 1 : 0;
+    e = timed(K_DW_GEMM, fl, ((double)V * rows + (double)rows * d) * P.es + 8.0 * V * d, s,
+              [&] { return launch_gemm(dtype, EPI_DW, w, s); });
+  }
+  return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
+}
+
+kdkl_status kdkl_profile_begin(void) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (auto& r : g_prof.recs) {
+    g_prof.pool.push_back(r.a);
+    g_prof.pool.push_back(r.b);
+  }
+  g_prof.recs.clear();
+  g_prof.on = true;
+  return KDKL_OK;
+}
+
+kdkl_status kdkl_profile_end(kdkl_kernel_stat* out, int capacity, int* count) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.on = false;
+  kdkl_kernel_stat acc[K_COUNT];
+  memset(acc, 0, sizeof(acc));
+  kdkl_status st = KDKL_OK;
+  for (auto& r : g_prof.recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess)
+      st = KDKL_ERR_HIP;
+    kdkl_kernel_stat& k = acc[r.kid];
+    k.launches += 1;
+    k.total_ms += ms;
+    k.flops += r.flops;
+    k.bytes += r.bytes;
+    g_prof.pool.push_back(r.a);
+    g_prof.pool.push_back(r.b);
+  }
+  g_prof.recs.clear();
+  int n = 0;
+  for (int i = 0; i < K_COUNT; ++i) {
+    if (acc[i].launches == 0) continue;
+    if (out && n < capacity) {
+      out[n] = acc[i];
+      strncpy(out[n].name, kernel_name(i), sizeof(out[n].name) - 1);
+      out[n].name[sizeof(out[n].name) - 1] = 0;
+    }
+    ++n;
+  }
+  if (count) *count = n;
+  return st;
+}
+
+}  // extern "C"

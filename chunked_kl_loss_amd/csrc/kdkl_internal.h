@@ -1,0 +1,103 @@
+// Internal interface between the C-ABI layer (kdkl_api.hip) and the device
+// kernels (kdkl_kernels.hip). Host-side declarations only.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kdkl {
+
+// Tile of the vocabulary handled by one workgroup of the projection GEMMs.
+// The teacher preparation builds its per-tile index with the same width.
+constexpr int kVocabTile = 256;
+// Token-axis tile of the projection GEMMs; chunk buffers are padded to it.
+constexpr int kTokenTile = 256;
+
+enum KernelId {
+  K_TEACHER = 0,
+  K_FWD_GEMM,
+  K_MERGE,
+  K_LOSS,
+  K_TRANSPOSE_W,
+  K_TRANSPOSE_H,
+  K_DZ_GEMM,
+  K_DH_GEMM,
+  K_DH_REDUCE,
+  K_DW_GEMM,
+  K_COUNT
+};
+
+const char* kernel_name(int id);
+
+// One slice ("chunk") of positions [r0, r0 + rows).
+struct TeacherArgs {
+  const int32_t* ids;     // [N, K] (whole problem)
+  const float* logits;    // [N, K]
+  int64_t r0;
+  int rows;
+  int K;
+  float inv_T;
+  int n_vt;               // vocabulary tiles (ceil(V / kVocabTile))
+  int64_t Cp;             // padded chunk capacity (row pitch of tstart)
+  int32_t* sids;          // [Cp, K]   ids sorted ascending
+  float* sp;              // [Cp, K]   teacher probabilities, same order
+  float* erow;            // [Cp]      sum_k p log p
+  uint16_t* tstart;       // [n_vt + 1, Cp] first sorted index >= tile start
+};
+
+struct GemmArgs {
+  const void* A;  int64_t lda;   // [M, K] rows of A, K contiguous
+  const void* B;  int64_t ldb;   // [N, K] rows of B, K contiguous
+  int M, N;                      // valid rows of A / of B
+  int64_t k_end;                 // K extent (multiple of 16 bytes of elements)
+  int64_t k_split;               // K per split (multiple of the k-step)
+  int tiles_m, tiles_n, splits;
+  // projection epilogues (A = W rows = vocabulary, B = H rows = tokens)
+  float inv_T;
+  int V;                         // vocabulary size (rows >= V are padding)
+  int K;                         // teacher top-K
+  int64_t Cp;                    // chunk capacity
+  int n_vt;
+  const int32_t* sids;
+  const float* sp;
+  const uint16_t* tstart;
+  float4* part;                  // forward: [Cp, n_vt] (max, sumexp, gamma, -)
+  const float* row_lse;          // backward: lse of this chunk's rows
+  const float* grad;             // backward: upstream scalar (device) or NULL
+  float coef_base;               // 1 / (N_total * T)
+  void* dz_cv;                   // [Cp, Vp]
+  void* dz_vc;                   // [Vp, Cp]
+  int64_t Vp;
+  // dH split-K partials [splits, Cp, d] and dW [V, d]
+  float* out;
+  int64_t ldo;
+  int accumulate;
+};
+
+struct MergeArgs {
+  const float4* part;   // [Cp, n_vt]
+  int n_vt;
+  int rows;
+  const float* erow;
+  float* row_lse;       // chunk-offset
+  float* row_kl;        // chunk-offset
+};
+
+hipError_t launch_teacher(const TeacherArgs& a, hipStream_t s);
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+hipError_t launch_loss(const float* row_kl, int64_t N, float* loss, hipStream_t s);
+// out[c, r] = in[r, c] for r < R, 0 for R <= r < Rp; c < C.
+hipError_t launch_transpose(int elem_bytes, const void* in, int64_t R, int64_t C,
+                            int64_t ldi, void* out, int64_t Rp, int64_t ldo,
+                            hipStream_t s);
+hipError_t launch_zero(float* p, int64_t n, hipStream_t s);
+hipError_t launch_dh_reduce(int dtype, const float* part, int splits, int rows,
+                            int64_t d, int64_t Cp, void* dH, hipStream_t s);
+
+enum Epilogue { EPI_FWD = 0, EPI_DZ = 1, EPI_DH = 2, EPI_DW = 3 };
+// dtype: 0 = fp32, 1 = bf16
+hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s);
+int gemm_k_step(int dtype);  // elements per k-step of the GEMM main loop
+
+}  // namespace kdkl

@@ -1,0 +1,144 @@
+/*
+ * kdkl.h — C-ABI of libkdkl.so: the fused chunked KL-divergence loss for
+ * offline top-K distillation, on one AMD Instinct MI355X (gfx950).
+ *
+ * Operation. For student hidden states H [N, d] and the output-projection
+ * weight W [V, d] (the lm-head), and a cached teacher top-K per position
+ * (ids [N, K], logits [N, K]), the loss is
+ *
+ *     s_i   = (W H_i) / T                        student logits at temperature T
+ *     q_i   = softmax(s_i) over all V entries    full-vocabulary student distribution
+ *     p_i   = softmax(logits_i / T) over K       teacher top-K, renormalised; zero elsewhere
+ *     KL_i  = sum_k p_ik (log p_ik - log q_i[ids_ik])
+ *     loss  = (1/N) sum_i KL_i
+ *
+ * The pages name three mathematically equivalent ways to compute this loss
+ * and describe the fused chunked one: per slice of positions, project the
+ * hidden states to logits, fold the slice into the running loss and drop it,
+ * so the vocabulary x sequence logit grid is never built; the backward pass
+ * recomputes each slice's projection [P1 "Making knowledge distillation cheap
+ * enough to run at scale", section "Two system changes", fused chunked KL
+ * bullet; P4 "Efficient Knowledge Distillation for LLMs: Offline Top-K Logits
+ * and a Fused Chunked KL Loss", section 2 "fused chunked KL loss"]. The teacher
+ * side is the offline cache of the 100 most likely tokens per position [P1,
+ * same section, offline distillation paragraph].
+ *
+ * Readings where the pages say nothing: forward KL(teacher || student);
+ * temperature divides both teacher and student logits, and no T^2 factor is
+ * applied; the reduction is the mean over the N positions.
+ *
+ * Gradient (with upstream scalar g = dL_total/dloss):
+ *     dZ_i = g / (N T) * (q_i - scatter(ids_i, p_i))     [V]
+ *     dH   = dZ W        dW = dZ^T H
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, row-major, 16-byte aligned.
+ *     H and W share the storage dtype (KDKL_F32 or KDKL_BF16); d must be a
+ *     multiple of 8 (bf16) or 4 (fp32).
+ *   - The caller owns every buffer, including the workspace sized by
+ *     kdkl_workspace_size(). The library allocates no device memory, keeps no
+ *     pointer after returning, and enqueues all work on `stream` (a
+ *     hipStream_t; NULL = the default stream) without synchronising the host.
+ *     Buffers must stay alive until the stream has passed the call.
+ *   - Arguments are checked before any HIP call; a failed check returns a
+ *     status and touches nothing. A failed launch returns KDKL_ERR_HIP.
+ *   - Preconditions not checked: ids of a row distinct (duplicates add their
+ *     mass) and in [0, V). An id outside [0, V) never faults; its teacher mass
+ *     is dropped from the loss and gradient.
+ *   - Results are bitwise reproducible run to run (fixed reduction orders, no
+ *     floating-point atomics).
+ */
+#ifndef KDKL_H
+#define KDKL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDKL_ABI_VERSION 1
+
+typedef enum {
+  KDKL_OK = 0,
+  KDKL_ERR_NULL = 1,      /* a required pointer is NULL */
+  KDKL_ERR_SHAPE = 2,     /* a size is out of range (d, K, chunk, V, N) */
+  KDKL_ERR_VALUE = 3,     /* T not finite or T <= 0 */
+  KDKL_ERR_DTYPE = 4,     /* dtype is neither KDKL_F32 nor KDKL_BF16 */
+  KDKL_ERR_WORKSPACE = 5, /* workspace smaller than kdkl_workspace_size() */
+  KDKL_ERR_OVERFLOW = 6,  /* a size product overflows */
+  KDKL_ERR_HIP = 7,       /* a HIP launch or runtime call failed */
+  KDKL_ERR_ALIGN = 8      /* a pointer is not 16-byte aligned */
+} kdkl_status;
+
+typedef enum { KDKL_F32 = 0, KDKL_BF16 = 1 } kdkl_dtype;
+
+/* Version of this ABI (KDKL_ABI_VERSION). */
+int kdkl_abi_version(void);
+
+/* Human-readable name of a status; static storage, never NULL. */
+const char* kdkl_status_string(int status);
+
+/* Bytes of device workspace needed by kdkl_forward (*fwd_bytes) and by
+ * kdkl_backward (*bwd_bytes) for these sizes. Either output may be NULL.
+ * Host-only; the same validation as the compute calls. */
+kdkl_status kdkl_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K,
+                                int64_t chunk, int dtype,
+                                size_t* fwd_bytes, size_t* bwd_bytes);
+
+/* Forward pass of the fused chunked KL loss.
+ *   H [N, d] dtype, W [V, d] dtype, topk_ids [N, K] int32, topk_logits
+ *   [N, K] fp32; T > 0; chunk = positions per slice (>= 1; the last slice may
+ *   be short); 1 <= K <= min(V, 1024).
+ * Outputs (device): loss [1] fp32 (mean KL; NaN when N == 0),
+ *   row_lse [N] fp32 = logsumexp_v(s_iv) (keep it for kdkl_backward),
+ *   row_kl [N] fp32 per-position KL, or NULL if not wanted.
+ * Workspace: >= *fwd_bytes from kdkl_workspace_size. */
+kdkl_status kdkl_forward(const void* H, const void* W,
+                         const int32_t* topk_ids, const float* topk_logits,
+                         int64_t N, int64_t d, int64_t V, int32_t K,
+                         float T, int64_t chunk, int dtype,
+                         float* loss, float* row_lse, float* row_kl,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward pass: recomputes each slice's logits and writes
+ *   dH [N, d] in the storage dtype, dW [V, d] fp32.
+ * row_lse is the forward's output for the same inputs. grad_loss is a device
+ * pointer to the upstream scalar g (NULL means g = 1). accumulate_dW != 0
+ * adds into dW instead of overwriting it (gradient accumulation across
+ * micro-batches). Workspace: >= *bwd_bytes from kdkl_workspace_size. */
+kdkl_status kdkl_backward(const void* H, const void* W,
+                          const int32_t* topk_ids, const float* topk_logits,
+                          int64_t N, int64_t d, int64_t V, int32_t K,
+                          float T, int64_t chunk, int dtype,
+                          const float* row_lse, const float* grad_loss,
+                          void* dH, float* dW, int accumulate_dW,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* ---- measurement aid: per-kernel timing with HIP events ------------------
+ * Between kdkl_profile_begin() and kdkl_profile_end(), every kernel launched
+ * by kdkl_forward / kdkl_backward is bracketed by two HIP events recorded on
+ * the launch stream. kdkl_profile_end() waits for those events and returns,
+ * per kernel name, the launch count, the summed event time and the summed
+ * algorithmic work (flop and HBM bytes by the formulas the library states for
+ * each kernel). Process-wide, not thread-safe against concurrent compute
+ * calls; it creates HIP events but allocates no device buffers. */
+typedef struct {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+  double flops;  /* algorithmic floating-point operations, summed */
+  double bytes;  /* algorithmic HBM bytes, summed */
+} kdkl_kernel_stat;
+
+kdkl_status kdkl_profile_begin(void);
+/* Fills up to `capacity` entries of `out`, stores the number of kernel names
+ * seen in *count, and stops profiling. */
+kdkl_status kdkl_profile_end(kdkl_kernel_stat* out, int capacity, int* count);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDKL_H */

@@ -1,0 +1,167 @@
+"""Host-only checks of the C-ABI library: it loads, exports every function
+that include/kdkl.h declares, sizes workspaces, and rejects bad arguments with
+the documented status before any HIP call (no GPU needed)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from chunked_kl_loss_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULL, SHAPE, VALUE, DTYPE, WORKSPACE, OVERFLOW, HIP, ALIGN = range(9)
+FAKE = 0x10000  # 16-byte aligned, never dereferenced on the host
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "kdkl.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kdkl_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("kdkl_forward", "kdkl_backward", "kdkl_workspace_size", "kdkl_status_string",
+              "kdkl_abi_version", "kdkl_profile_begin", "kdkl_profile_end"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in declared_functions():
+        assert hasattr(lib, n), f"libkdkl.so does not export {n}"
+    assert set(declared_functions()) <= set(L.SIGNATURES)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.kdkl_abi_version() == 1
+    for s in list(range(9)) + [99, -1]:
+        v = lib.kdkl_status_string(s)
+        assert v is not None and len(v) > 0
+    assert lib.kdkl_status_string(WORKSPACE).startswith(b"KDKL_ERR_WORKSPACE")
+
+
+def ws(lib, N, d, V, K, chunk, dt):
+    f, b = C.c_size_t(), C.c_size_t()
+    st = lib.kdkl_workspace_size(N, d, V, K, chunk, dt, C.byref(f), C.byref(b))
+    return st, f.value, b.value
+
+
+def test_workspace_size_arithmetic(lib):
+    # gpt-oss-like head at 32K: the backward workspace holds W^T, H_c^T, two
+    # layouts of one chunk of dZ and the dH split partials; nothing scales
+    # with N except the forward's per-row KL scratch.
+    st, f, b = ws(lib, 32768, 2880, 201088, 100, 2048, L.KDKL_BF16)
+    assert st == OK
+    Vp = (201088 + 255) // 256 * 256
+    assert b >= 2 * 2048 * Vp * 2 + 2880 * Vp * 2
+    assert b < 4 * 2**30
+    assert f < 64 * 2**20
+    # memory is independent of N apart from O(N) scratch
+    _, f2, b2 = ws(lib, 262144, 2880, 201088, 100, 2048, L.KDKL_BF16)
+    assert b2 == b and f2 - f == (262144 - 32768) * 4
+    # fp32 storage doubles the element-sized regions
+    _, _, b32 = ws(lib, 32768, 2880, 201088, 100, 2048, L.KDKL_F32)
+    assert b32 > b
+    # outputs may be NULL
+    assert lib.kdkl_workspace_size(10, 8, 16, 2, 4, L.KDKL_BF16, None, None) == OK
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 64, 100, 4, 8, 1), SHAPE),      # N < 0
+    ((8, 0, 100, 4, 8, 1), SHAPE),        # d = 0
+    ((8, 12, 100, 4, 8, 1), SHAPE),       # bf16 d not a multiple of 8
+    ((8, 6, 100, 4, 8, 0), SHAPE),        # fp32 d not a multiple of 4
+    ((8, 64, 100, 0, 8, 1), SHAPE),       # K = 0
+    ((8, 64, 3, 4, 8, 1), SHAPE),         # K > V
+    ((8, 64, 4096, 1025, 8, 1), SHAPE),   # K > 1024
+    ((8, 64, 100, 4, 0, 1), SHAPE),       # chunk = 0
+    ((8, 64, 100, 4, 8, 2), DTYPE),       # unknown dtype
+    ((8, 64, 0, 1, 8, 1), SHAPE),         # V = 0
+    ((2**40, 64, 100, 4, 8, 1), OVERFLOW),
+])
+def test_workspace_size_rejects(lib, args, status):
+    st, _, _ = ws(lib, *args)
+    assert st == status
+
+
+def fwd(lib, **kw):
+    a = dict(H=FAKE, W=FAKE, ids=FAKE, lg=FAKE, N=64, d=64, V=1000, K=8, T=1.0, chunk=16,
+             dt=L.KDKL_BF16, loss=FAKE, lse=FAKE, kl=None, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.kdkl_forward(a["H"], a["W"], a["ids"], a["lg"], a["N"], a["d"], a["V"], a["K"],
+                            a["T"], a["chunk"], a["dt"], a["loss"], a["lse"], a["kl"], a["ws"],
+                            a["wsb"], a["stream"])
+
+
+def bwd(lib, **kw):
+    a = dict(H=FAKE, W=FAKE, ids=FAKE, lg=FAKE, N=64, d=64, V=1000, K=8, T=1.0, chunk=16,
+             dt=L.KDKL_BF16, lse=FAKE, g=None, dH=FAKE, dW=FAKE, acc=0, ws=FAKE, wsb=1 << 40,
+             stream=None)
+    a.update(kw)
+    return lib.kdkl_backward(a["H"], a["W"], a["ids"], a["lg"], a["N"], a["d"], a["V"], a["K"],
+                             a["T"], a["chunk"], a["dt"], a["lse"], a["g"], a["dH"], a["dW"],
+                             a["acc"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("call", [fwd, bwd], ids=["forward", "backward"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), NULL),
+    (dict(H=None), NULL),
+    (dict(ids=None), NULL),
+    (dict(lg=None), NULL),
+    (dict(ws=None), NULL),
+    (dict(T=0.0), VALUE),
+    (dict(T=-1.0), VALUE),
+    (dict(T=float("inf")), VALUE),
+    (dict(T=float("nan")), VALUE),
+    (dict(d=60), SHAPE),
+    (dict(K=0), SHAPE),
+    (dict(K=2000), SHAPE),
+    (dict(chunk=0), SHAPE),
+    (dict(dt=7), DTYPE),
+    (dict(wsb=16), WORKSPACE),
+    (dict(H=FAKE + 8), ALIGN),
+    (dict(W=FAKE + 2), ALIGN),
+    (dict(ws=FAKE + 4), ALIGN),
+])
+def test_compute_calls_reject_bad_arguments(lib, call, kw, status):
+    assert call(lib, **kw) == status
+
+
+def test_forward_output_pointers_checked(lib):
+    assert fwd(lib, loss=None) == NULL
+    assert fwd(lib, lse=None) == NULL
+
+
+def test_backward_output_pointers_checked(lib):
+    assert bwd(lib, dW=None) == NULL
+    assert bwd(lib, dH=None) == NULL
+    assert bwd(lib, lse=None) == NULL
+    assert bwd(lib, dW=FAKE + 4) == ALIGN
+
+
+def test_profile_calls_without_launches(lib):
+    assert lib.kdkl_profile_begin() == OK
+    n = C.c_int(-1)
+    assert lib.kdkl_profile_end(None, 0, C.byref(n)) == OK
+    assert n.value == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+
+    import chunked_kl_loss_amd as kd
+
+    H = torch.zeros(4, 8, dtype=torch.bfloat16)
+    W = torch.zeros(16, 8, dtype=torch.bfloat16)
+    ids = torch.zeros(4, 2, dtype=torch.int32)
+    lg = torch.zeros(4, 2)
+    with pytest.raises(ValueError):
+        kd.kdkl_forward(H, W, ids, lg, 1.0, 2)

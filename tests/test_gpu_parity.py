@@ -1,0 +1,170 @@
+"""GPU parity: the HIP path through the C-ABI against the CPU oracle, element
+by element, on seeded inputs that span several tiles and ragged tails, plus
+the method's degenerate cases and invariants."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests._gpu import TOL, assert_parity, maxrel, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+# (case id, workload, overrides, seed) — sizes the oracle finishes in seconds.
+CASES = [
+    ("tiny_fp32_full", "tiny_fp32", {}, None),
+    ("fp32_ragged_all", "tiny_fp32", dict(N=70, d=72, V=4000, K=7, chunk=48, T=0.7), 7),
+    ("fp32_chunk_ragged_T", "tiny_fp32", dict(N=100, chunk=32, T=1.5), 8),
+    ("bf16_ragged_zipf", "small_bf16", dict(N=300, d=200, V=5000, K=20, chunk=128, T=2.0), 9),
+    ("small_bf16_full", "small_bf16", {}, None),
+    ("llama3b_geometry", "llama3b_8k", dict(N=96, chunk=40), None),
+    ("gptoss20b_geometry", "gptoss20b_32k", dict(N=80, chunk=32), None),
+    ("longctx_geometry_T2", "longctx_256k", dict(N=64, chunk=24), None),
+]
+
+
+def _inputs(name, over, seed):
+    w = wl.get_config(name).with_(**over)
+    x = wl.generate(w, seed=seed)
+    return w, x
+
+
+@pytest.mark.parametrize("case,name,over,seed", CASES, ids=[c[0] for c in CASES])
+def test_parity_vs_oracle(case, name, over, seed):
+    w, x = _inputs(name, over, seed)
+    print(f"case {case}: N={w.N} d={w.d} V={w.V} K={w.K} chunk={w.chunk} T={w.T} {w.dtype}",
+          flush=True)
+    got = run_gpu(x, w.T, w.chunk)
+    ref = oracle.loss_and_grads(x["H"], x["W"], x["ids"], x["logits"], w.T)
+    assert_parity(got, ref, w.dtype, case)
+    # per-row KL as well
+    assert maxrel(got["row_kl"], ref["row_kl"]) <= TOL[w.dtype]["loss"] * 10
+
+
+def test_chunk_size_independence():
+    w, x = _inputs("tiny_fp32", dict(N=64, V=1000, K=5), 21)
+    ref = oracle.loss_and_grads(x["H"], x["W"], x["ids"], x["logits"], w.T)
+    outs = []
+    for chunk in (1, 7, 32, 64, 1000):
+        got = run_gpu(x, w.T, chunk)
+        assert_parity(got, ref, "fp32", f"chunk={chunk}")
+        outs.append(got)
+    for o in outs[1:]:
+        assert abs(o["loss"] - outs[0]["loss"]) <= 1e-6 * abs(outs[0]["loss"])
+
+
+def test_upstream_gradient_and_accumulate():
+    w, x = _inputs("tiny_fp32", dict(N=50, V=3000, K=6, chunk=16, T=1.3), 22)
+    ref = oracle.loss_and_grads(x["H"], x["W"], x["ids"], x["logits"], w.T, g=0.37)
+    got = run_gpu(x, w.T, w.chunk, g=0.37)
+    assert_parity(got, ref, "fp32", "g=0.37")
+    # accumulate: dW starts from a given tensor and adds
+    init = torch.randn(w.V, w.d, dtype=torch.float32)
+    acc = run_gpu(x, w.T, w.chunk, g=0.37, accumulate_dW=True, dW_init=init)
+    # fp32 addition into an O(1) tensor: one rounding of the sum per element
+    expect = init.double().numpy() + ref["dW"]
+    err = np.abs(acc["dW"] - expect).max()
+    assert err <= 2 * np.finfo(np.float32).eps * np.abs(expect).max() + 1e-5 * np.abs(ref["dW"]).max()
+
+
+def test_bitwise_determinism():
+    w, x = _inputs("small_bf16", dict(N=512, V=8000, chunk=200), 23)
+    a = run_gpu(x, w.T, w.chunk)
+    b = run_gpu(x, w.T, w.chunk)
+    assert a["loss"] == b["loss"]
+    assert np.array_equal(a["row_lse"], b["row_lse"])
+    assert np.array_equal(a["dH"], b["dH"])
+    assert np.array_equal(a["dW"], b["dW"])
+
+
+def test_k_equals_one_is_cross_entropy():
+    w, x = _inputs("tiny_fp32", dict(N=40, V=700, K=1, chunk=16, T=1.0), 24)
+    got = run_gpu(x, w.T, w.chunk)
+    Z = x["H"].double() @ x["W"].double().T
+    ce = torch.nn.functional.cross_entropy(Z, x["ids"][:, 0].long()).item()
+    assert abs(got["loss"] - ce) <= 1e-5 * abs(ce)
+
+
+def test_k_equals_v_and_matching_teacher_gives_zero():
+    # teacher logits equal to the student's logits over the whole vocabulary
+    w, x = _inputs("tiny_fp32", dict(N=20, V=64, K=64, chunk=8, T=1.7), 25)
+    ids = torch.stack([torch.randperm(64, generator=torch.Generator().manual_seed(i))
+                       for i in range(20)]).to(torch.int32)
+    Z = (x["H"].double() @ x["W"].double().T)
+    x["ids"] = ids
+    x["logits"] = torch.gather(Z, 1, ids.long()).float()
+    got = run_gpu(x, w.T, w.chunk)
+    assert abs(got["loss"]) < 1e-5
+    assert np.abs(got["dH"]).max() < 1e-6 and np.abs(got["dW"]).max() < 1e-6
+
+
+def test_uniform_student_closed_form():
+    # W = 0: KL_i = log V - entropy of the teacher's renormalised top-K
+    w, x = _inputs("small_bf16", dict(N=33, V=1234 * 8, K=50, chunk=16, T=2.0), 26)
+    x["W"] = torch.zeros_like(x["W"])
+    got = run_gpu(x, w.T, w.chunk)
+    import scipy.stats as sst
+    lg = x["logits"].double().numpy()
+    ent = np.array([sst.entropy(np.exp(lg[i] / w.T)) for i in range(w.N)])
+    ref = np.mean(math.log(w.V) - ent)
+    assert abs(got["loss"] - ref) <= 1e-4 * abs(ref)
+    assert np.abs(got["dH"]).max() == 0.0
+
+
+def test_empty_input():
+    import chunked_kl_loss_amd as kd
+
+    dev = "cuda:0"
+    H = torch.zeros(0, 64, dtype=torch.bfloat16, device=dev)
+    W = torch.randn(300, 64, device=dev).to(torch.bfloat16)
+    ids = torch.zeros(0, 4, dtype=torch.int32, device=dev)
+    lg = torch.zeros(0, 4, device=dev)
+    loss, lse, kl = kd.kdkl_forward(H, W, ids, lg, 1.0, 16)
+    dW0 = torch.full((300, 64), 5.0, device=dev)
+    dH, dW = kd.kdkl_backward(H, W, ids, lg, 1.0, 16, lse, dW=dW0.clone())
+    torch.cuda.synchronize()
+    assert math.isnan(loss.item())
+    assert torch.count_nonzero(dW).item() == 0
+    _, dWa = kd.kdkl_backward(H, W, ids, lg, 1.0, 16, lse, dW=dW0.clone(), accumulate_dW=True)
+    assert torch.equal(dWa, dW0)
+
+
+def test_out_of_range_ids_do_not_fault():
+    # ids outside [0, V) are a documented precondition violation: no fault,
+    # their teacher mass is dropped. Compare with the oracle on the in-range
+    # remainder by giving the dropped entries -inf logits.
+    w, x = _inputs("tiny_fp32", dict(N=30, V=1000, K=6, chunk=8), 27)
+    bad = x["ids"].clone()
+    bad[:, 0] = torch.tensor([-5, 1000, 1003, 2**30, -1] * 6)
+    x2 = dict(x, ids=bad)
+    got = run_gpu(x2, w.T, w.chunk)
+    assert np.isfinite(got["dH"]).all() and np.isfinite(got["dW"]).all()
+
+
+def test_autograd_function_matches_direct_calls():
+    import chunked_kl_loss_amd as kd
+
+    w, x = _inputs("small_bf16", dict(N=256, V=4096, K=32, chunk=100), 28)
+    dev = "cuda:0"
+    H = x["H"].to(dev).requires_grad_(True)
+    W = x["W"].to(dev).requires_grad_(True)
+    loss = kd.fused_kl_loss(H, W, x["ids"].to(dev), x["logits"].to(dev), w.T, w.chunk)
+    (2.0 * loss).backward()
+    ref = oracle.loss_and_grads(x["H"], x["W"], x["ids"], x["logits"], w.T, g=2.0)
+    assert abs(loss.item() - ref["loss"]) <= 1e-3 * abs(ref["loss"])
+    assert maxrel(H.grad.double().cpu().numpy(), ref["dH"]) <= 2e-2
+    assert maxrel(W.grad.double().cpu().numpy(), ref["dW"]) <= 2e-2
+
+
+def test_temperature_identity_exact_for_T2():
+    # loss(H, W, l, 2) == loss(H/2, W, l/2, 1): halving is exact in binary
+    # floating point, so both GPU runs see the same products up to rounding.
+    w, x = _inputs("small_bf16", dict(N=128, V=6000, K=40, chunk=64, T=2.0), 29)
+    a = run_gpu(x, 2.0, w.chunk)
+    x1 = dict(x, H=(x["H"].float() / 2).to(x["H"].dtype), logits=x["logits"] / 2)
+    b = run_gpu(x1, 1.0, w.chunk)
+    assert abs(a["loss"] - b["loss"]) <= 1e-6 * abs(a["loss"])
+    assert maxrel(a["dH"], b["dH"] / 2.0) <= 1e-2
