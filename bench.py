@@ -102,6 +102,8 @@ def main():
     t0 = time.time()
     x = wl.generate(w)
     log(f"bench: inputs generated in {time.time() - t0:.1f} s")
+    torch.cuda.set_device(dev)
+    torch.zeros(1, device=dev)  # initialise the device before reading memory stats
     torch.cuda.reset_peak_memory_stats(dev)
     H, W, ids, lg = (x[k].to(dev) for k in ("H", "W", "ids", "logits"))
     fb, bb = kd.workspace_size(w.N, w.d, w.V, w.K, w.chunk, H.dtype)

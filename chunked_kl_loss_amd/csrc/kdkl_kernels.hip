@@ -271,46 +271,336 @@ hipError_t launch_dh_reduce(int dtype, const float* part, int splits, int rows, 
 }
 
 // ---------------------------------------------------------------------------
-// MFMA GEMM main loop.
+// Projection GEMMs.
 //
 // C[m, n] = sum_k A[m, k] B[n, k]; A and B row-major with k contiguous.
-// Workgroup tile BM x BN, 4 wavefronts in a 2 x 2 grid, each owning a
-// (BM/2) x (BN/2) sub-tile made of 32 x 32 MFMA blocks. Each LDS row holds
-// 128 bytes of k (64 bf16 or 32 fp32) as eight 16-byte chunks stored at
-// chunk ^ (row & 7), so the 32 lanes that read one column of chunks from 32
-// consecutive rows hit distinct banks. Two LDS stages; global loads for the
-// next k-step are issued before the MFMAs of the current one.
+// Workgroup tile 256 x 256, four wavefronts in a 2 x 2 grid, each owning a
+// 128 x 128 sub-tile of 4 x 4 MFMA blocks of 32 x 32. An LDS row holds 128
+// bytes of k (64 bf16 or 32 fp32) as eight 16-byte chunks stored at position
+// chunk ^ (row & 7), so the 32 lanes that read one chunk column from 32
+// consecutive rows hit distinct banks.
 //
-// MFMA operand layout used (32 x 32 output block): lane l feeds row (l & 31)
-// of A and column (l & 31) of B with 8 consecutive k elements taken at
-// offset 8 * (l >> 5) of the current 16-element k-group; accumulator
-// register r of lane l holds output row 8 * (r >> 2) + 4 * (l >> 5) + (r & 3),
-// column (l & 31).
+// MFMA operand layout (32 x 32 output block): lane l feeds row (l & 31) of A
+// and column (l & 31) of B with 8 consecutive k elements taken at offset
+// 8 * (l >> 5) of the current 16-element k-group; accumulator register r of
+// lane l holds output row 8 * (r >> 2) + 4 * (l >> 5) + (r & 3), column
+// (l & 31).
 // ---------------------------------------------------------------------------
+constexpr int BM = 256, BN = 256;        // workgroup tile
+constexpr int WM = 128, WN = 128;        // wavefront tile
+constexpr int MB = WM / 32, NB = WN / 32;
+constexpr int kStage = (BM + BN) * 128;  // one LDS stage: A and B tiles
+constexpr int kDwPitch = BN + 8;         // fp32 row pitch of the dW staging tile
+constexpr int kDzPitch = BM + 8;         // bf16 row pitch of the dZ staging tile
+constexpr int kSmem = (2 * kStage > 128 * kDwPitch * 4) ? 2 * kStage : 128 * kDwPitch * 4;
+
+typedef f32x16_t Acc[MB][NB];
+
+__device__ __forceinline__ int acc_row(int wm, int mb, int r, int lane) {
+  return wm * WM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+struct Tile {
+  int tm, tn, ks;
+};
+
+// XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
+// each XCD gets a contiguous run of tiles (neighbours share an A tile and
+// stay in that XCD's L2). Returns false for the padding workgroups.
+__device__ __forceinline__ bool tile_of(const GemmArgs& p, Tile& t) {
+  const int total = p.tiles_m * p.tiles_n * p.splits;
+  const int per = (total + 7) >> 3;
+  const int L = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
+  if (L >= total) return false;
+  t.tn = L % p.tiles_n;
+  t.tm = (L / p.tiles_n) % p.tiles_m;
+  t.ks = L / (p.tiles_n * p.tiles_m);
+  return true;
+}
+
+// Teacher entries of this lane's token columns: [lo, hi) into the sorted list.
+__device__ __forceinline__ void hit_ranges(const GemmArgs& p, const Tile& t, int (&lo)[NB], int (&hi)[NB]) {
+  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+#pragma unroll
+  for (int nb = 0; nb < NB; ++nb) {
+    const int col = t.tn * BN + wn * WN + nb * 32 + (lane & 31);
+    if (col < p.N) {
+      lo[nb] = p.tstart[(int64_t)t.tm * p.Cp + col];
+      hi[nb] = p.tstart[(int64_t)(t.tm + 1) * p.Cp + col];
+    } else {
+      lo[nb] = hi[nb] = 0;
+    }
+  }
+}
+
+// Accumulator slot (mb * 16 + r) of vocabulary row `id` in this lane, or -1.
+__device__ __forceinline__ int hit_slot(int id, int V, int m0, int wm, int lane) {
+  const int r = id - m0 - wm * WM;
+  if (id >= V || r < 0 || r >= WM) return -1;
+  const int rin = r & 31;
+  if (((rin >> 2) & 1) != (lane >> 5)) return -1;
+  return (r >> 5) * 16 + ((rin >> 3) << 2) + (rin & 3);
+}
+
+template <int ES, int EPI>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, Acc& acc, const Tile& t, char* smem,
+                                              const int (&hit_lo)[NB], const int (&hit_hi)[NB]) {
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int m0 = t.tm * BM, n0 = t.tn * BN;
+  if constexpr (EPI == EPI_FWD) {
+    // s = z / T over the tile's vocabulary rows (A rows), per token column:
+    // max, sum of exp(s - max), and sum of p * s over the teacher ids here.
+    float* red = (float*)smem;  // [2][BN][3]
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int ct = wn * WN + nb * 32 + (lane & 31);
+      const int col = n0 + ct;
+      float mx = kNegInf;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + acc_row(wm, mb, r, lane);
+          const float s = row < p.V ? acc[mb][nb][r] * p.inv_T : kNegInf;
+          acc[mb][nb][r] = s;
+          mx = fmaxf(mx, s);
+        }
+      mx = fmaxf(mx, shfl_xor(mx, 32));
+      float se = 0.f;
+      if (mx > kNegInf) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) se += fast_exp(acc[mb][nb][r] - mx);
+      }
+      se += shfl_xor(se, 32);
+      float gam = 0.f;
+      for (int h = hit_lo[nb]; h < hit_hi[nb]; ++h) {
+        const int slot = hit_slot(p.sids[(int64_t)col * p.K + h], p.V, m0, wm, lane);
+        if (slot < 0) continue;
+        float v = 0.f;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) v = (mb * 16 + rr == slot) ? acc[mb][nb][rr] : v;
+        gam += p.sp[(int64_t)col * p.K + h] * v;
+      }
+      gam += shfl_xor(gam, 32);
+      if (lane < 32) {
+        float* e = red + (wm * BN + ct) * 3;
+        e[0] = mx;
+        e[1] = se;
+        e[2] = gam;
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < BN; c += 256) {
+      const int col = n0 + c;
+      if (col >= p.N) continue;
+      const float* e0 = red + c * 3;
+      const float* e1 = red + (BN + c) * 3;
+      const float m = fmaxf(e0[0], e1[0]);
+      float s = 0.f;
+      if (m > kNegInf) {
+        if (e0[0] > kNegInf) s += e0[1] * fast_exp(e0[0] - m);
+        if (e1[0] > kNegInf) s += e1[1] * fast_exp(e1[0] - m);
+      }
+      p.part[(int64_t)col * p.n_vt + t.tm] = make_float4(m, s, e0[2] + e1[2], 0.f);
+    }
+  } else if constexpr (EPI == EPI_DZ) {
+    // dZ = coef * (softmax(s) - teacher) for the tile, written to the chunk
+    // buffers token-major (dz_cv [Cp, Vp]) and vocabulary-major (dz_vc [Vp, Cp]).
+    const float g = p.grad ? p.grad[0] : 1.0f;
+    const float coef = g * p.coef_base;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = n0 + wn * WN + nb * 32 + (lane & 31);
+      const bool cval = col < p.N;
+      const float lse = cval ? p.row_lse[col] : 0.f;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + acc_row(wm, mb, r, lane);
+          const float q = fast_exp(acc[mb][nb][r] * p.inv_T - lse);
+          acc[mb][nb][r] = (row < p.V && cval) ? q : 0.f;
+        }
+      for (int h = hit_lo[nb]; h < hit_hi[nb]; ++h) {
+        const int slot = hit_slot(p.sids[(int64_t)col * p.K + h], p.V, m0, wm, lane);
+        if (slot < 0) continue;
+        const float pk = p.sp[(int64_t)col * p.K + h];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr)
+            acc[mb][nb][rr] = (mb * 16 + rr == slot) ? acc[mb][nb][rr] - pk : acc[mb][nb][rr];
+      }
+    }
+    if constexpr (ES == 2) {
+      // Stage one half of the token columns at a time as bf16 [128 n][256 v]
+      // in LDS, then write both layouts with 16-byte stores.
+      uint16_t* T = (uint16_t*)smem;
+      uint16_t* cv = (uint16_t*)p.dz_cv;
+      uint16_t* vc = (uint16_t*)p.dz_vc;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        __syncthreads();
+        if (wn == half) {
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+              for (int r4 = 0; r4 < 4; ++r4) {
+                const int nl = nb * 32 + (lane & 31);
+                const int vl = acc_row(wm, mb, r4 * 4, lane);
+                ushort4 o;
+                o.x = f32_to_bf16_bits(acc[mb][nb][r4 * 4 + 0] * coef);
+                o.y = f32_to_bf16_bits(acc[mb][nb][r4 * 4 + 1] * coef);
+                o.z = f32_to_bf16_bits(acc[mb][nb][r4 * 4 + 2] * coef);
+                o.w = f32_to_bf16_bits(acc[mb][nb][r4 * 4 + 3] * coef);
+                *(ushort4*)(T + nl * kDzPitch + vl) = o;
+              }
+        }
+        __syncthreads();
+        const int nb0 = n0 + half * WN;
+        // token-major rows: 512 bytes of vocabulary each
+#pragma unroll 4
+        for (int j = tid; j < WN * 32; j += 256) {
+          const int i = j >> 5, c = j & 31;
+          *(uint4*)(cv + (int64_t)(nb0 + i) * p.Vp + m0 + c * 8) = *(const uint4*)(T + i * kDzPitch + c * 8);
+        }
+        // vocabulary-major rows: 256 bytes of tokens each
+#pragma unroll 4
+        for (int j = tid; j < BM * 16; j += 256) {
+          const int v = j & (BM - 1), c = j >> 8;
+          uint16_t e[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) e[q] = T[(c * 8 + q) * kDzPitch + v];
+          uint4 o;
+          o.x = e[0] | ((uint32_t)e[1] << 16);
+          o.y = e[2] | ((uint32_t)e[3] << 16);
+          o.z = e[4] | ((uint32_t)e[5] << 16);
+          o.w = e[6] | ((uint32_t)e[7] << 16);
+          *(uint4*)(vc + (int64_t)(m0 + v) * p.Cp + nb0 + c * 8) = o;
+        }
+      }
+    } else {
+      float* cv = (float*)p.dz_cv;
+      float* vc = (float*)p.dz_vc;
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb) {
+        const int col = n0 + wn * WN + nb * 32 + (lane & 31);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int row = m0 + acc_row(wm, mb, r4 * 4, lane);
+            const float v0 = acc[mb][nb][r4 * 4 + 0] * coef, v1 = acc[mb][nb][r4 * 4 + 1] * coef;
+            const float v2 = acc[mb][nb][r4 * 4 + 2] * coef, v3 = acc[mb][nb][r4 * 4 + 3] * coef;
+            *(float4*)(cv + (int64_t)col * p.Vp + row) = make_float4(v0, v1, v2, v3);
+            vc[(int64_t)(row + 0) * p.Cp + col] = v0;
+            vc[(int64_t)(row + 1) * p.Cp + col] = v1;
+            vc[(int64_t)(row + 2) * p.Cp + col] = v2;
+            vc[(int64_t)(row + 3) * p.Cp + col] = v3;
+          }
+      }
+    }
+  } else if constexpr (EPI == EPI_DH) {
+    // fp32 partial of split ks: out[ks, row, col]
+    float* out = p.out + (int64_t)t.ks * p.Cp * p.ldo;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int col = n0 + wn * WN + nb * 32 + (lane & 31);
+      if (col >= p.N) continue;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + acc_row(wm, mb, r, lane);
+          if (row < p.M) out[(int64_t)row * p.ldo + col] = acc[mb][nb][r];
+        }
+    }
+  } else {
+    // EPI_DW: dW[row, col] (+)= tile, staged through LDS half by half so the
+    // read-modify-write of dW uses 16-byte accesses on whole rows.
+    float* F = (float*)smem;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      __syncthreads();
+      if (wm == half) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              F[(mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kDwPitch + wn * WN + nb * 32 +
+                (lane & 31)] = acc[mb][nb][r];
+      }
+      __syncthreads();
+      const int r0 = m0 + half * WM;
+#pragma unroll
+      for (int it = 0; it < (WM * BN / 4) / 256; it += 8) {
+        float4 v[8], o[8];
+        int64_t off[8];
+        bool ok[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int j = (it + u) * 256 + tid;
+          const int r = j >> 6, c4 = j & 63;
+          const int row = r0 + r, col = n0 + c4 * 4;
+          ok[u] = row < p.M && col < p.N;
+          off[u] = (int64_t)row * p.ldo + col;
+          v[u] = *(const float4*)(F + r * kDwPitch + c4 * 4);
+          o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (ok[u] && p.accumulate) o[u] = *(const float4*)(p.out + off[u]);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          if (ok[u]) {
+            float4 s = make_float4(o[u].x + v[u].x, o[u].y + v[u].y, o[u].z + v[u].z, o[u].w + v[u].w);
+            *(float4*)(p.out + off[u]) = s;
+          }
+        }
+      }
+    }
+  }
+}
+
+// ------------------------- generic main loop --------------------------------
+// Register-staged loads with zero fill past M / N rows and past the K extent.
+// Serves fp32 and any K that is not a multiple of the 64-element k-step.
 template <typename TE>
 struct Mfma;
 
 template <>
 struct Mfma<uint16_t> {  // bf16 storage
-  struct Frag { bf16x8_t v; };
-  static __device__ __forceinline__ Frag load(const char* p) {
+  struct Frag {
+    bf16x8_t v;
+  };
+  static __device__ __forceinline__ Frag load(const char* s, int row, int kk, int lane) {
+    const int c = kk * 2 + (lane >> 5);
     Frag f;
-    f.v = *(const bf16x8_t*)p;
+    f.v = *(const bf16x8_t*)(s + row * 128 + ((c ^ (row & 7)) << 4));
     return f;
   }
   static __device__ __forceinline__ void mma(const Frag& a, const Frag& b, f32x16_t& c) {
     c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a.v, b.v, c, 0, 0, 0);
   }
-  static constexpr int kChunksPerGroup = 1;  // 16-byte chunks per lane per k-group
 };
 
 template <>
 struct Mfma<float> {
-  struct Frag { f32x4_t lo, hi; };
-  static __device__ __forceinline__ Frag load(const char* p0, const char* p1) {
+  struct Frag {
+    f32x4_t lo, hi;
+  };
+  static __device__ __forceinline__ Frag load(const char* s, int row, int kk, int lane) {
+    const int c = kk * 4 + (lane >> 5) * 2;
     Frag f;
-    f.lo = *(const f32x4_t*)p0;
-    f.hi = *(const f32x4_t*)p1;
+    f.lo = *(const f32x4_t*)(s + row * 128 + ((c ^ (row & 7)) << 4));
+    f.hi = *(const f32x4_t*)(s + row * 128 + (((c + 1) ^ (row & 7)) << 4));
     return f;
   }
   static __device__ __forceinline__ void mma(const Frag& a, const Frag& b, f32x16_t& c) {
@@ -319,10 +609,9 @@ struct Mfma<float> {
 #pragma unroll
     for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_32x32x2f32(a.hi[e], b.hi[e], c, 0, 0, 0);
   }
-  static constexpr int kChunksPerGroup = 2;
 };
 
-template <typename TE, int ROWS>
+template <int ROWS>
 __device__ __forceinline__ void g2r(uint4 (&r)[ROWS * 8 / 256], const char* __restrict__ base, int64_t ld_bytes,
                                     int row0, int nrows, int64_t k0_bytes, int64_t kend_bytes, int tid) {
 #pragma unroll
@@ -348,53 +637,25 @@ __device__ __forceinline__ void r2s(const uint4 (&r)[ROWS * 8 / 256], char* s, i
   }
 }
 
-__device__ __forceinline__ int acc_row(int wm, int WMr, int mb, int r, int lane) {
-  return wm * WMr + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-}
-
-template <typename TE, int BM, int BN, int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmArgs p) {
+template <typename TE, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_generic_kernel(const GemmArgs p) {
   using M_ = Mfma<TE>;
   constexpr int ES = sizeof(TE);
-  constexpr int BK = 128 / ES;  // elements per k-step
-  constexpr int WM = BM / 2, WN = BN / 2;
-  constexpr int MB = WM / 32, NB = WN / 32;
-  constexpr int STAGE = (BM + BN) * 128;
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
-
-  // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
-  // give each XCD a contiguous run of tiles (neighbours share an A tile).
-  const int total = p.tiles_m * p.tiles_n * p.splits;
-  const int per = (total + 7) >> 3;
-  const int L = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
-  if (L >= total) return;
-  const int tn = L % p.tiles_n;
-  const int tm = (L / p.tiles_n) % p.tiles_m;
-  const int ks = L / (p.tiles_n * p.tiles_m);
-
+  constexpr int BK = 128 / ES;
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
+  Tile t;
+  if (!tile_of(p, t)) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int64_t kb = (int64_t)ks * p.k_split;
+  const int m0 = t.tm * BM, n0 = t.tn * BN;
+  const int64_t kb = (int64_t)t.ks * p.k_split;
   const int64_t ke = kb + p.k_split < p.k_end ? kb + p.k_split : p.k_end;
   const int nk = ke > kb ? (int)((ke - kb + BK - 1) / BK) : 0;
 
-  // Teacher ranges of this lane's token columns, fetched before the main loop.
   int hit_lo[NB], hit_hi[NB];
-  if constexpr (EPI == EPI_FWD || EPI == EPI_DZ) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int col = n0 + wn * WN + nb * 32 + (lane & 31);
-      if (col < p.N) {
-        hit_lo[nb] = p.tstart[(int64_t)tm * p.Cp + col];
-        hit_hi[nb] = p.tstart[(int64_t)(tm + 1) * p.Cp + col];
-      } else {
-        hit_lo[nb] = hit_hi[nb] = 0;
-      }
-    }
-  }
+  if constexpr (EPI == EPI_FWD || EPI == EPI_DZ) hit_ranges(p, t, hit_lo, hit_hi);
 
-  f32x16_t acc[MB][NB];
+  Acc acc;
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -409,8 +670,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmArgs p) {
   uint4 ra[BM * 8 / 256], rb[BN * 8 / 256];
 
   if (nk > 0) {
-    g2r<TE, BM>(ra, Ab, lda_b, m0, p.M, kb * ES, kend_b, tid);
-    g2r<TE, BN>(rb, Bb, ldb_b, n0, p.N, kb * ES, kend_b, tid);
+    g2r<BM>(ra, Ab, lda_b, m0, p.M, kb * ES, kend_b, tid);
+    g2r<BN>(rb, Bb, ldb_b, n0, p.N, kb * ES, kend_b, tid);
     r2s<BM>(ra, smem, tid);
     r2s<BN>(rb, smem + BM * 128, tid);
     __syncthreads();
@@ -418,222 +679,148 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(const GemmArgs p) {
       const bool more = kt + 1 < nk;
       if (more) {
         const int64_t k0b = (kb + (int64_t)(kt + 1) * BK) * ES;
-        g2r<TE, BM>(ra, Ab, lda_b, m0, p.M, k0b, kend_b, tid);
-        g2r<TE, BN>(rb, Bb, ldb_b, n0, p.N, k0b, kend_b, tid);
+        g2r<BM>(ra, Ab, lda_b, m0, p.M, k0b, kend_b, tid);
+        g2r<BN>(rb, Bb, ldb_b, n0, p.N, k0b, kend_b, tid);
       }
-      const char* sA = smem + (kt & 1) * STAGE;
+      const char* sA = smem + (kt & 1) * kStage;
       const char* sB = sA + BM * 128;
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
         typename M_::Frag fa[MB], fb[NB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const int row = wm * WM + mb * 32 + (lane & 31);
-          if constexpr (M_::kChunksPerGroup == 1) {
-            const int c = kk * 2 + (lane >> 5);
-            fa[mb] = M_::load(sA + row * 128 + ((c ^ (row & 7)) << 4));
-          } else {
-            const int c = kk * 4 + (lane >> 5) * 2;
-            fa[mb] = M_::load(sA + row * 128 + ((c ^ (row & 7)) << 4),
-                              sA + row * 128 + (((c + 1) ^ (row & 7)) << 4));
-          }
-        }
+        for (int mb = 0; mb < MB; ++mb) fa[mb] = M_::load(sA, wm * WM + mb * 32 + (lane & 31), kk, lane);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) {
-          const int row = wn * WN + nb * 32 + (lane & 31);
-          if constexpr (M_::kChunksPerGroup == 1) {
-            const int c = kk * 2 + (lane >> 5);
-            fb[nb] = M_::load(sB + row * 128 + ((c ^ (row & 7)) << 4));
-          } else {
-            const int c = kk * 4 + (lane >> 5) * 2;
-            fb[nb] = M_::load(sB + row * 128 + ((c ^ (row & 7)) << 4),
-                              sB + row * 128 + (((c + 1) ^ (row & 7)) << 4));
-          }
-        }
+        for (int nb = 0; nb < NB; ++nb) fb[nb] = M_::load(sB, wn * WN + nb * 32 + (lane & 31), kk, lane);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) M_::mma(fa[mb], fb[nb], acc[mb][nb]);
       }
       if (more) {
-        char* s = smem + ((kt + 1) & 1) * STAGE;
+        char* s = smem + ((kt + 1) & 1) * kStage;
         r2s<BM>(ra, s, tid);
         r2s<BN>(rb, s + BM * 128, tid);
       }
       __syncthreads();
     }
   }
-
-  // ------------------------------- epilogues -------------------------------
-  if constexpr (EPI == EPI_FWD) {
-    // s = z / T for the tile's vocabulary rows (A rows) and token columns.
-    float* red = (float*)smem;  // [2][BN][3]
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int ct = wn * WN + nb * 32 + (lane & 31);
-      const int col = n0 + ct;
-      float mx = kNegInf;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + acc_row(wm, WM, mb, r, lane);
-          const float s = row < p.V ? acc[mb][nb][r] * p.inv_T : kNegInf;
-          acc[mb][nb][r] = s;
-          mx = fmaxf(mx, s);
-        }
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      float se = 0.f;
-      if (mx > kNegInf) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) se += fast_exp(acc[mb][nb][r] - mx);
-      }
-      se += shfl_xor(se, 32);
-      // teacher-weighted logits of the ids that fall in this lane's rows
-      float gam = 0.f;
-      for (int h = hit_lo[nb]; h < hit_hi[nb]; ++h) {
-        const int id = p.sids[(int64_t)col * p.K + h];
-        const int r = id - m0 - wm * WM;
-        if (id >= p.V || r < 0 || r >= WM) continue;
-        const int rin = r & 31;
-        if (((rin >> 2) & 1) != (lane >> 5)) continue;
-        const int slot = (r >> 5) * 16 + ((rin >> 3) << 2) + (rin & 3);
-        float v = 0.f;
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr) v = (mb * 16 + rr == slot) ? acc[mb][nb][rr] : v;
-        gam += p.sp[(int64_t)col * p.K + h] * v;
-      }
-      gam += shfl_xor(gam, 32);
-      if (lane < 32) {
-        float* e = red + (wm * BN + ct) * 3;
-        e[0] = mx; e[1] = se; e[2] = gam;
-      }
-    }
-    __syncthreads();
-    for (int c = tid; c < BN; c += 256) {
-      const int col = n0 + c;
-      if (col >= p.N) continue;
-      const float* e0 = red + c * 3;
-      const float* e1 = red + (BN + c) * 3;
-      const float m = fmaxf(e0[0], e1[0]);
-      float s = 0.f;
-      if (m > kNegInf) {
-        if (e0[0] > kNegInf) s += e0[1] * fast_exp(e0[0] - m);
-        if (e1[0] > kNegInf) s += e1[1] * fast_exp(e1[0] - m);
-      }
-      p.part[(int64_t)col * p.n_vt + tm] = make_float4(m, s, e0[2] + e1[2], 0.f);
-    }
-  } else if constexpr (EPI == EPI_DZ) {
-    const float g = p.grad ? p.grad[0] : 1.0f;
-    const float coef = g * p.coef_base;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int ct = wn * WN + nb * 32 + (lane & 31);
-      const int col = n0 + ct;
-      const bool cval = col < p.N;
-      const float lse = cval ? p.row_lse[col] : 0.f;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + acc_row(wm, WM, mb, r, lane);
-          const float q = fast_exp(acc[mb][nb][r] * p.inv_T - lse);
-          acc[mb][nb][r] = (row < p.V && cval) ? q : 0.f;
-        }
-      for (int h = hit_lo[nb]; h < hit_hi[nb]; ++h) {
-        const int id = p.sids[(int64_t)col * p.K + h];
-        const int r = id - m0 - wm * WM;
-        if (id >= p.V || r < 0 || r >= WM) continue;
-        const int rin = r & 31;
-        if (((rin >> 2) & 1) != (lane >> 5)) continue;
-        const int slot = (r >> 5) * 16 + ((rin >> 3) << 2) + (rin & 3);
-        const float pk = p.sp[(int64_t)col * p.K + h];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-          for (int rr = 0; rr < 16; ++rr)
-            acc[mb][nb][rr] = (mb * 16 + rr == slot) ? acc[mb][nb][rr] - pk : acc[mb][nb][rr];
-      }
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const int row = m0 + acc_row(wm, WM, mb, r4 * 4, lane);  // 4 consecutive rows
-          const float v0 = acc[mb][nb][r4 * 4 + 0] * coef, v1 = acc[mb][nb][r4 * 4 + 1] * coef;
-          const float v2 = acc[mb][nb][r4 * 4 + 2] * coef, v3 = acc[mb][nb][r4 * 4 + 3] * coef;
-          if constexpr (ES == 2) {
-            uint16_t* cv = (uint16_t*)p.dz_cv;
-            uint16_t* vc = (uint16_t*)p.dz_vc;
-            ushort4 o;
-            o.x = f32_to_bf16_bits(v0); o.y = f32_to_bf16_bits(v1);
-            o.z = f32_to_bf16_bits(v2); o.w = f32_to_bf16_bits(v3);
-            *(ushort4*)(cv + (int64_t)col * p.Vp + row) = o;
-            vc[(int64_t)(row + 0) * p.Cp + col] = o.x;
-            vc[(int64_t)(row + 1) * p.Cp + col] = o.y;
-            vc[(int64_t)(row + 2) * p.Cp + col] = o.z;
-            vc[(int64_t)(row + 3) * p.Cp + col] = o.w;
-          } else {
-            float* cv = (float*)p.dz_cv;
-            float* vc = (float*)p.dz_vc;
-            *(float4*)(cv + (int64_t)col * p.Vp + row) = make_float4(v0, v1, v2, v3);
-            vc[(int64_t)(row + 0) * p.Cp + col] = v0;
-            vc[(int64_t)(row + 1) * p.Cp + col] = v1;
-            vc[(int64_t)(row + 2) * p.Cp + col] = v2;
-            vc[(int64_t)(row + 3) * p.Cp + col] = v3;
-          }
-        }
-    }
-  } else {
-    // EPI_DH: out = partials of split ks, [Cp, ldo]; EPI_DW: out = dW [V, ldo]
-    float* out = p.out + (EPI == EPI_DH ? (int64_t)ks * p.Cp * p.ldo : 0);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int col = n0 + wn * WN + nb * 32 + (lane & 31);
-      if (col >= p.N) continue;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + acc_row(wm, WM, mb, r, lane);
-          if (row < p.M) {
-            float* o = out + (int64_t)row * p.ldo + col;
-            if (EPI == EPI_DW && p.accumulate)
-              *o += acc[mb][nb][r];
-            else
-              *o = acc[mb][nb][r];
-          }
-        }
-    }
-  }
+  gemm_epilogue<ES, EPI>(p, acc, t, smem, hit_lo, hit_hi);
 }
 
-template <typename TE, int EPI>
-static hipError_t launch_gemm_t(const GemmArgs& a, hipStream_t s) {
+// --------------------------- bf16 fast main loop ----------------------------
+// For K extents that are whole 64-element k-steps. Global->LDS loads go
+// straight into LDS (global_load_lds_dwordx4: each lane's 16 bytes land at
+// lane * 16 of the wave's 1 KiB destination), so the XOR layout is produced
+// by choosing which global chunk each lane fetches. Rows past M / N are
+// clamped to the last valid row (their outputs are masked in the epilogue).
+// The LDS fragments of k-group kk+1 are read while the MFMAs of kk run.
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_fast_kernel(const GemmArgs p) {
+  constexpr int BK = 64;
+  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
+  Tile t;
+  if (!tile_of(p, t)) return;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int m0 = t.tm * BM, n0 = t.tn * BN;
+  const int64_t kb = (int64_t)t.ks * p.k_split;
+  const int64_t ke = kb + p.k_split < p.k_end ? kb + p.k_split : p.k_end;
+  const int nk = ke > kb ? (int)((ke - kb) / BK) : 0;
+
+  int hit_lo[NB], hit_hi[NB];
+  if constexpr (EPI == EPI_FWD || EPI == EPI_DZ) hit_ranges(p, t, hit_lo, hit_hi);
+
+  // Per-lane sources of the 8 + 8 direct loads of one stage.
+  const char* srcA[8];
+  const char* srcB[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int slot = (i * 4 + wid) * 64 + lane;  // 16-byte slot in the tile
+    const int row = slot >> 3, c = (slot & 7) ^ (row & 7);
+    const int ga = min(m0 + row, p.M - 1);
+    const int gb = min(n0 + row, p.N - 1);
+    srcA[i] = (const char*)p.A + ((int64_t)ga * p.lda + kb) * 2 + c * 16;
+    srcB[i] = (const char*)p.B + ((int64_t)gb * p.ldb + kb) * 2 + c * 16;
+  }
+  auto issue = [&](int stage, int kt) {
+    char* base = smem + stage * kStage;
+    const int64_t ko = (int64_t)kt * BK * 2;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(srcA[i] + ko), (lds_void*)(base + (i * 4 + wid) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(srcB[i] + ko),
+                                       (lds_void*)(base + BM * 128 + (i * 4 + wid) * 1024), 16, 0, 0);
+  };
+
+  Acc acc;
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  using M_ = Mfma<uint16_t>;
+  typename M_::Frag fa[2][MB], fb[2][NB];
+  auto load_frags = [&](int stage, int kk, int buf) {
+    const char* sA = smem + stage * kStage;
+    const char* sB = sA + BM * 128;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) fa[buf][mb] = M_::load(sA, wm * WM + mb * 32 + (lane & 31), kk, lane);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) fb[buf][nb] = M_::load(sB, wn * WN + nb * 32 + (lane & 31), kk, lane);
+  };
+
+  if (nk > 0) {
+    issue(0, 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    load_frags(0, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) issue(cur ^ 1, kt + 1);
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        if (kk < 3) load_frags(cur, kk + 1, (kk + 1) & 1);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < NB; ++nb) M_::mma(fa[kk & 1][mb], fb[kk & 1][nb], acc[mb][nb]);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (kt + 1 < nk) load_frags(cur ^ 1, 0, 0);
+    }
+  }
+  gemm_epilogue<2, EPI>(p, acc, t, smem, hit_lo, hit_hi);
+}
+
+template <int EPI>
+static hipError_t launch_gemm_e(int dtype, const GemmArgs& a, hipStream_t s) {
   const int total = a.tiles_m * a.tiles_n * a.splits;
   if (total <= 0) return hipSuccess;
   const int per = (total + 7) / 8;
-  hipLaunchKernelGGL((gemm_kernel<TE, 256, 256, EPI>), dim3(per * 8), dim3(256), 0, s, a);
+  const dim3 grid(per * 8), block(256);
+  const bool fast = dtype == 1 && a.k_end % 64 == 0 && a.k_split % 64 == 0;
+  if (fast)
+    hipLaunchKernelGGL(gemm_bf16_fast_kernel<EPI>, grid, block, 0, s, a);
+  else if (dtype == 1)
+    hipLaunchKernelGGL((gemm_generic_kernel<uint16_t, EPI>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_generic_kernel<float, EPI>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
-  if (dtype == 1) {
-    switch (epi) {
-      case EPI_FWD: return launch_gemm_t<uint16_t, EPI_FWD>(a, s);
-      case EPI_DZ: return launch_gemm_t<uint16_t, EPI_DZ>(a, s);
-      case EPI_DH: return launch_gemm_t<uint16_t, EPI_DH>(a, s);
-      default: return launch_gemm_t<uint16_t, EPI_DW>(a, s);
-    }
-  }
   switch (epi) {
-    case EPI_FWD: return launch_gemm_t<float, EPI_FWD>(a, s);
-    case EPI_DZ: return launch_gemm_t<float, EPI_DZ>(a, s);
-    case EPI_DH: return launch_gemm_t<float, EPI_DH>(a, s);
-    default: return launch_gemm_t<float, EPI_DW>(a, s);
+    case EPI_FWD: return launch_gemm_e<EPI_FWD>(dtype, a, s);
+    case EPI_DZ: return launch_gemm_e<EPI_DZ>(dtype, a, s);
+    case EPI_DH: return launch_gemm_e<EPI_DH>(dtype, a, s);
+    default: return launch_gemm_e<EPI_DW>(dtype, a, s);
   }
 }
 
