@@ -5,7 +5,9 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libkdkl.so")
+# KDKL_LIB may point at another build of the same library (e.g. a variant
+# compiled with different tuning constants); default: the in-tree build.
+LIB_PATH = os.environ.get("KDKL_LIB") or os.path.join(HERE, "libkdkl.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "kdkl.h")
 
 KDKL_F32 = 0

@@ -17,6 +17,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "kdkl_internal.h"
 
 namespace kdkl {
@@ -274,11 +276,13 @@ hipError_t launch_dh_reduce(int dtype, const float* part, int splits, int rows, 
 // Projection GEMMs.
 //
 // C[m, n] = sum_k A[m, k] B[n, k]; A and B row-major with k contiguous.
-// Workgroup tile 256 x 256, four wavefronts in a 2 x 2 grid, each owning a
-// 128 x 128 sub-tile of 4 x 4 MFMA blocks of 32 x 32. An LDS row holds 128
-// bytes of k (64 bf16 or 32 fp32) as eight 16-byte chunks stored at position
-// chunk ^ (row & 7), so the 32 lanes that read one chunk column from 32
-// consecutive rows hit distinct banks.
+// Workgroup tile 256 x 256 split over a grid of wavefronts; each wavefront
+// owns a sub-tile of 32 x 32 MFMA blocks. LDS rows hold 128 bytes of k
+// (64 bf16 or 32 fp32) as eight 16-byte chunks stored at position
+// chunk ^ ((row >> 1) & 7), or 64 bytes as four chunks at chunk ^ ((row >> 2)
+// & 3). gfx950 serves a 128-bit LDS read 16 lanes (256 bytes, all 64 banks)
+// at a time, and both layouts give the 16 rows read by one lane group 16
+// distinct 16-byte bank slots.
 //
 // MFMA operand layout (32 x 32 output block): lane l feeds row (l & 31) of A
 // and column (l & 31) of B with 8 consecutive k elements taken at offset
@@ -286,18 +290,31 @@ hipError_t launch_dh_reduce(int dtype, const float* part, int splits, int rows, 
 // lane l holds output row 8 * (r >> 2) + 4 * (l >> 5) + (r & 3), column
 // (l & 31).
 // ---------------------------------------------------------------------------
-constexpr int BM = 256, BN = 256;        // workgroup tile
-constexpr int WM = 128, WN = 128;        // wavefront tile
-constexpr int MB = WM / 32, NB = WN / 32;
-constexpr int kStage = (BM + BN) * 128;  // one LDS stage: A and B tiles
-constexpr int kDwPitch = BN + 8;         // fp32 row pitch of the dW staging tile
-constexpr int kDzPitch = BM + 8;         // bf16 row pitch of the dZ staging tile
-constexpr int kSmem = (2 * kStage > 128 * kDwPitch * 4) ? 2 * kStage : 128 * kDwPitch * 4;
+constexpr int BM = 256, BN = 256;      // workgroup tile
+constexpr int kDwPitch = BN + 8;       // fp32 row pitch of the dW staging tile
+constexpr int kDzPitch = BM + 8;       // bf16 row pitch of the dZ staging tile
+constexpr int kEpiSmem = 128 * kDwPitch * 4;
 
-typedef f32x16_t Acc[MB][NB];
+template <int WAVES_M, int WAVES_N>
+struct Grid {
+  static constexpr int kWavesM = WAVES_M, kWavesN = WAVES_N;
+  static constexpr int kWaves = WAVES_M * WAVES_N;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int MB = WM / 32, NB = WN / 32;
+  static __device__ __forceinline__ int wm() { return (int)(threadIdx.x >> 6) / WAVES_N; }
+  static __device__ __forceinline__ int wn() { return (int)(threadIdx.x >> 6) % WAVES_N; }
+};
+using Grid4 = Grid<2, 2>;  // 4 wavefronts of 128 x 128
+using Grid8 = Grid<2, 4>;  // 8 wavefronts of 128 x 64 (two per SIMD)
 
+__device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
+__device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
+
+// Output row of accumulator register r of block mb in this lane, tile-relative.
+template <class G>
 __device__ __forceinline__ int acc_row(int wm, int mb, int r, int lane) {
-  return wm * WM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  return wm * G::WM + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 
 struct Tile {
@@ -319,11 +336,13 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& p, Tile& t) {
 }
 
 // Teacher entries of this lane's token columns: [lo, hi) into the sorted list.
-__device__ __forceinline__ void hit_ranges(const GemmArgs& p, const Tile& t, int (&lo)[NB], int (&hi)[NB]) {
-  const int lane = threadIdx.x & 63, wn = (threadIdx.x >> 6) & 1;
+template <class G>
+__device__ __forceinline__ void hit_ranges(const GemmArgs& p, const Tile& t, int (&lo)[G::NB],
+                                           int (&hi)[G::NB]) {
+  const int lane = threadIdx.x & 63, wn = G::wn();
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int col = t.tn * BN + wn * WN + nb * 32 + (lane & 31);
+  for (int nb = 0; nb < G::NB; ++nb) {
+    const int col = t.tn * BN + wn * G::WN + nb * 32 + (lane & 31);
     if (col < p.N) {
       lo[nb] = p.tstart[(int64_t)t.tm * p.Cp + col];
       hi[nb] = p.tstart[(int64_t)(t.tm + 1) * p.Cp + col];
@@ -334,34 +353,37 @@ __device__ __forceinline__ void hit_ranges(const GemmArgs& p, const Tile& t, int
 }
 
 // Accumulator slot (mb * 16 + r) of vocabulary row `id` in this lane, or -1.
+template <class G>
 __device__ __forceinline__ int hit_slot(int id, int V, int m0, int wm, int lane) {
-  const int r = id - m0 - wm * WM;
-  if (id >= V || r < 0 || r >= WM) return -1;
+  const int r = id - m0 - wm * G::WM;
+  if (id >= V || r < 0 || r >= G::WM) return -1;
   const int rin = r & 31;
   if (((rin >> 2) & 1) != (lane >> 5)) return -1;
   return (r >> 5) * 16 + ((rin >> 3) << 2) + (rin & 3);
 }
 
-template <int ES, int EPI>
-__device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, Acc& acc, const Tile& t, char* smem,
-                                              const int (&hit_lo)[NB], const int (&hit_hi)[NB]) {
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+template <class G, int ES, int EPI>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)[G::MB][G::NB], const Tile& t,
+                                              char* smem, const int (&hit_lo)[G::NB],
+                                              const int (&hit_hi)[G::NB]) {
+  constexpr int MB = G::MB, NB = G::NB, NT = G::kThreads;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wm = G::wm(), wn = G::wn();
   const int m0 = t.tm * BM, n0 = t.tn * BN;
   if constexpr (EPI == EPI_FWD) {
     // s = z / T over the tile's vocabulary rows (A rows), per token column:
     // max, sum of exp(s - max), and sum of p * s over the teacher ids here.
-    float* red = (float*)smem;  // [2][BN][3]
+    float* red = (float*)smem;  // [WAVES_M][BN][3]
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int ct = wn * WN + nb * 32 + (lane & 31);
+      const int ct = wn * G::WN + nb * 32 + (lane & 31);
       const int col = n0 + ct;
       float mx = kNegInf;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + acc_row(wm, mb, r, lane);
+          const int row = m0 + acc_row<G>(wm, mb, r, lane);
           const float s = row < p.V ? acc[mb][nb][r] * p.inv_T : kNegInf;
           acc[mb][nb][r] = s;
           mx = fmaxf(mx, s);
@@ -377,7 +399,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, Acc& acc, const
       se += shfl_xor(se, 32);
       float gam = 0.f;
       for (int h = hit_lo[nb]; h < hit_hi[nb]; ++h) {
-        const int slot = hit_slot(p.sids[(int64_t)col * p.K + h], p.V, m0, wm, lane);
+        const int slot = hit_slot<G>(p.sids[(int64_t)col * p.K + h], p.V, m0, wm, lane);
         if (slot < 0) continue;
         float v = 0.f;
 #pragma unroll
@@ -395,18 +417,24 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, Acc& acc, const
       }
     }
     __syncthreads();
-    for (int c = tid; c < BN; c += 256) {
+    for (int c = tid; c < BN; c += NT) {
       const int col = n0 + c;
       if (col >= p.N) continue;
-      const float* e0 = red + c * 3;
-      const float* e1 = red + (BN + c) * 3;
-      const float m = fmaxf(e0[0], e1[0]);
+      float m = kNegInf, g = 0.f;
+#pragma unroll
+      for (int w = 0; w < G::kWavesM; ++w) {
+        m = fmaxf(m, red[(w * BN + c) * 3]);
+        g += red[(w * BN + c) * 3 + 2];
+      }
       float s = 0.f;
       if (m > kNegInf) {
-        if (e0[0] > kNegInf) s += e0[1] * fast_exp(e0[0] - m);
-        if (e1[0] > kNegInf) s += e1[1] * fast_exp(e1[0] - m);
+#pragma unroll
+        for (int w = 0; w < G::kWavesM; ++w) {
+          const float* e = red + (w * BN + c) * 3;
+          if (e[0] > kNegInf) s += e[1] * fast_exp(e[0] - m);
+        }
       }
-      p.part[(int64_t)col * p.n_vt + t.tm] = make_float4(m, s, e0[2] + e1[2], 0.f);
+      p.part[(int64_t)col * p.n_vt + t.tm] = make_float4(m, s, g, 0.f);
     }
   } else if constexpr (EPI == EPI_DZ) {
     // dZ = coef * (softmax(s) - teacher) for the tile, written to the chunk
@@ -415,19 +443,19 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, Acc& acc, const
     const float coef = g * p.coef_base;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int col = n0 + wn * WN + nb * 32 + (lane & 31);
+      const int col = n0 + wn * G::WN + nb * 32 + (lane & 31);
       const bool cval = col < p.N;
       const float lse = cval ? p.row_lse[col] : 0.f;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + acc_row(wm, mb, r, lane);
+          const int row = m0 + acc_row<G>(wm, mb, r, lane);
           const float q = fast_exp(acc[mb][nb][r] * p.inv_T - lse);
           acc[mb][nb][r] = (row < p.V && cval) ? q : 0.f;
         }
       for (int h = hit_lo[nb]; h < hit_hi[nb]; ++h) {
-        const int slot = hit_slot(p.sids[(int64_t)col * p.K + h], p.V, m0, wm, lane);
+        const int slot = hit_slot<G>(p.sids[(int64_t)col * p.K + h], p.V, m0, wm, lane);
         if (slot < 0) continue;
         const float pk = p.sp[(int64_t)col * p.K + h];
 #pragma unroll
@@ -438,23 +466,23 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, Acc& acc, const
       }
     }
     if constexpr (ES == 2) {
-      // Stage one half of the token columns at a time as bf16 [128 n][256 v]
-      // in LDS, then write both layouts with 16-byte stores.
+      // Stage 128 token columns at a time as bf16 [128 n][256 v] in LDS, then
+      // write both layouts with 16-byte stores.
       uint16_t* T = (uint16_t*)smem;
       uint16_t* cv = (uint16_t*)p.dz_cv;
       uint16_t* vc = (uint16_t*)p.dz_vc;
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         __syncthreads();
-        if (wn == half) {
+        if ((wn * G::WN) / 128 == half) {
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
               for (int r4 = 0; r4 < 4; ++r4) {
-                const int nl = nb * 32 + (lane & 31);
-                const int vl = acc_row(wm, mb, r4 * 4, lane);
+                const int nl = wn * G::WN + nb * 32 + (lane & 31) - half * 128;
+                const int vl = acc_row<G>(wm, mb, r4 * 4, lane);
                 ushort4 o;
                 o.x = f32_to_bf16_bits(acc[mb][nb][r4 * 4 + 0] * coef);
                 o.y = f32_to_bf16_bits(acc[mb][nb][r4 * 4 + 1] * coef);
@@ -464,16 +492,16 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, Acc& acc, const
               }
         }
         __syncthreads();
-        const int nb0 = n0 + half * WN;
+        const int nb0 = n0 + half * 128;
         // token-major rows: 512 bytes of vocabulary each
 #pragma unroll 4
-        for (int j = tid; j < WN * 32; j += 256) {
+        for (int j = tid; j < 128 * 32; j += NT) {
           const int i = j >> 5, c = j & 31;
           *(uint4*)(cv + (int64_t)(nb0 + i) * p.Vp + m0 + c * 8) = *(const uint4*)(T + i * kDzPitch + c * 8);
         }
         // vocabulary-major rows: 256 bytes of tokens each
 #pragma unroll 4
-        for (int j = tid; j < BM * 16; j += 256) {
+        for (int j = tid; j < BM * 16; j += NT) {
           const int v = j & (BM - 1), c = j >> 8;
           uint16_t e[8];
 #pragma unroll
@@ -491,12 +519,12 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, Acc& acc, const
       float* vc = (float*)p.dz_vc;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) {
-        const int col = n0 + wn * WN + nb * 32 + (lane & 31);
+        const int col = n0 + wn * G::WN + nb * 32 + (lane & 31);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const int row = m0 + acc_row(wm, mb, r4 * 4, lane);
+            const int row = m0 + acc_row<G>(wm, mb, r4 * 4, lane);
             const float v0 = acc[mb][nb][r4 * 4 + 0] * coef, v1 = acc[mb][nb][r4 * 4 + 1] * coef;
             const float v2 = acc[mb][nb][r4 * 4 + 2] * coef, v3 = acc[mb][nb][r4 * 4 + 3] * coef;
             *(float4*)(cv + (int64_t)col * p.Vp + row) = make_float4(v0, v1, v2, v3);
@@ -512,19 +540,20 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, Acc& acc, const
     float* out = p.out + (int64_t)t.ks * p.Cp * p.ldo;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      const int col = n0 + wn * WN + nb * 32 + (lane & 31);
+      const int col = n0 + wn * G::WN + nb * 32 + (lane & 31);
       if (col >= p.N) continue;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + acc_row(wm, mb, r, lane);
+          const int row = m0 + acc_row<G>(wm, mb, r, lane);
           if (row < p.M) out[(int64_t)row * p.ldo + col] = acc[mb][nb][r];
         }
     }
   } else {
-    // EPI_DW: dW[row, col] (+)= tile, staged through LDS half by half so the
-    // read-modify-write of dW uses 16-byte accesses on whole rows.
+    // EPI_DW: dW[row, col] (+)= tile, staged through LDS 128 rows at a time
+    // so the read-modify-write of dW uses 16-byte accesses on whole rows.
+    static_assert(G::WM == 128, "dW staging assumes 128-row wavefront tiles");
     float* F = (float*)smem;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
@@ -536,19 +565,20 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, Acc& acc, const
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              F[(mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kDwPitch + wn * WN + nb * 32 +
+              F[(mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kDwPitch + wn * G::WN + nb * 32 +
                 (lane & 31)] = acc[mb][nb][r];
       }
       __syncthreads();
-      const int r0 = m0 + half * WM;
+      const int r0 = m0 + half * 128;
+      constexpr int ITER = (128 * BN / 4) / NT;
 #pragma unroll
-      for (int it = 0; it < (WM * BN / 4) / 256; it += 8) {
+      for (int it = 0; it < ITER; it += 8) {
         float4 v[8], o[8];
         int64_t off[8];
         bool ok[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int j = (it + u) * 256 + tid;
+          const int j = (it + u) * NT + tid;
           const int r = j >> 6, c4 = j & 63;
           const int row = r0 + r, col = n0 + c4 * 4;
           ok[u] = row < p.M && col < p.N;
@@ -569,6 +599,16 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, Acc& acc, const
   }
 }
 
+template <class G>
+__device__ __forceinline__ void zero_acc(f32x16_t (&acc)[G::MB][G::NB]) {
+#pragma unroll
+  for (int i = 0; i < G::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < G::NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+}
+
 // ------------------------- generic main loop --------------------------------
 // Register-staged loads with zero fill past M / N rows and past the K extent.
 // Serves fp32 and any K that is not a multiple of the 64-element k-step.
@@ -583,7 +623,7 @@ struct Mfma<uint16_t> {  // bf16 storage
   static __device__ __forceinline__ Frag load(const char* s, int row, int kk, int lane) {
     const int c = kk * 2 + (lane >> 5);
     Frag f;
-    f.v = *(const bf16x8_t*)(s + row * 128 + ((c ^ (row & 7)) << 4));
+    f.v = *(const bf16x8_t*)(s + row * 128 + ((c ^ swz8(row)) << 4));
     return f;
   }
   static __device__ __forceinline__ void mma(const Frag& a, const Frag& b, f32x16_t& c) {
@@ -599,8 +639,8 @@ struct Mfma<float> {
   static __device__ __forceinline__ Frag load(const char* s, int row, int kk, int lane) {
     const int c = kk * 4 + (lane >> 5) * 2;
     Frag f;
-    f.lo = *(const f32x4_t*)(s + row * 128 + ((c ^ (row & 7)) << 4));
-    f.hi = *(const f32x4_t*)(s + row * 128 + (((c + 1) ^ (row & 7)) << 4));
+    f.lo = *(const f32x4_t*)(s + row * 128 + ((c ^ swz8(row)) << 4));
+    f.hi = *(const f32x4_t*)(s + row * 128 + (((c + 1) ^ swz8(row)) << 4));
     return f;
   }
   static __device__ __forceinline__ void mma(const Frag& a, const Frag& b, f32x16_t& c) {
@@ -633,35 +673,32 @@ __device__ __forceinline__ void r2s(const uint4 (&r)[ROWS * 8 / 256], char* s, i
   for (int i = 0; i < ROWS * 8 / 256; ++i) {
     const int idx = i * 256 + tid;
     const int row = idx >> 3, c = idx & 7;
-    *(uint4*)(s + row * 128 + ((c ^ (row & 7)) << 4)) = r[i];
+    *(uint4*)(s + row * 128 + ((c ^ swz8(row)) << 4)) = r[i];
   }
 }
 
 template <typename TE, int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_generic_kernel(const GemmArgs p) {
+  using G = Grid4;
   using M_ = Mfma<TE>;
   constexpr int ES = sizeof(TE);
   constexpr int BK = 128 / ES;
-  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
+  constexpr int kStage = (BM + BN) * 128;
+  constexpr int SMEM = 2 * kStage > kEpiSmem ? 2 * kStage : kEpiSmem;
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   Tile t;
   if (!tile_of(p, t)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wm = G::wm(), wn = G::wn();
   const int m0 = t.tm * BM, n0 = t.tn * BN;
   const int64_t kb = (int64_t)t.ks * p.k_split;
   const int64_t ke = kb + p.k_split < p.k_end ? kb + p.k_split : p.k_end;
   const int nk = ke > kb ? (int)((ke - kb + BK - 1) / BK) : 0;
 
-  int hit_lo[NB], hit_hi[NB];
-  if constexpr (EPI == EPI_FWD || EPI == EPI_DZ) hit_ranges(p, t, hit_lo, hit_hi);
-
-  Acc acc;
-#pragma unroll
-  for (int i = 0; i < MB; ++i)
-#pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  int hit_lo[G::NB], hit_hi[G::NB];
+  if constexpr (EPI == EPI_FWD || EPI == EPI_DZ) hit_ranges<G>(p, t, hit_lo, hit_hi);
+  f32x16_t acc[G::MB][G::NB];
+  zero_acc<G>(acc);
 
   const char* Ab = (const char*)p.A;
   const char* Bb = (const char*)p.B;
@@ -686,15 +723,15 @@ __global__ __launch_bounds__(256, 1) void gemm_generic_kernel(const GemmArgs p) 
       const char* sB = sA + BM * 128;
 #pragma unroll
       for (int kk = 0; kk < BK / 16; ++kk) {
-        typename M_::Frag fa[MB], fb[NB];
+        typename M_::Frag fa[G::MB], fb[G::NB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) fa[mb] = M_::load(sA, wm * WM + mb * 32 + (lane & 31), kk, lane);
+        for (int mb = 0; mb < G::MB; ++mb) fa[mb] = M_::load(sA, wm * G::WM + mb * 32 + (lane & 31), kk, lane);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) fb[nb] = M_::load(sB, wn * WN + nb * 32 + (lane & 31), kk, lane);
+        for (int nb = 0; nb < G::NB; ++nb) fb[nb] = M_::load(sB, wn * G::WN + nb * 32 + (lane & 31), kk, lane);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) M_::mma(fa[mb], fb[nb], acc[mb][nb]);
+          for (int nb = 0; nb < G::NB; ++nb) M_::mma(fa[mb], fb[nb], acc[mb][nb]);
       }
       if (more) {
         char* s = smem + ((kt + 1) & 1) * kStage;
@@ -704,114 +741,155 @@ __global__ __launch_bounds__(256, 1) void gemm_generic_kernel(const GemmArgs p) 
       __syncthreads();
     }
   }
-  gemm_epilogue<ES, EPI>(p, acc, t, smem, hit_lo, hit_hi);
+  gemm_epilogue<G, ES, EPI>(p, acc, t, smem, hit_lo, hit_hi);
 }
 
-// --------------------------- bf16 fast main loop ----------------------------
-// For K extents that are whole 64-element k-steps. Global->LDS loads go
+// ----------------------------- bf16 main loop -------------------------------
+// For K extents that are whole 64-element steps. Global->LDS loads go
 // straight into LDS (global_load_lds_dwordx4: each lane's 16 bytes land at
-// lane * 16 of the wave's 1 KiB destination), so the XOR layout is produced
-// by choosing which global chunk each lane fetches. Rows past M / N are
-// clamped to the last valid row (their outputs are masked in the epilogue).
-// The LDS fragments of k-group kk+1 are read while the MFMAs of kk run.
+// lane * 16 of the wave's 1 KiB destination), so the bank-spreading layout
+// is produced by choosing which global chunk each lane fetches. Rows past
+// M / N are clamped to the last valid row (their outputs are masked in the
+// epilogue). BK-element k-steps, NSTAGE stages in flight: the loads for
+// k-step kt + NSTAGE - 1 are issued while k-step kt is multiplied and only
+// the oldest stage is waited for; the LDS fragments of the next 16-element
+// k-group are read while the MFMAs of the current one run.
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_bf16_fast_kernel(const GemmArgs p) {
-  constexpr int BK = 64;
-  __shared__ __attribute__((aligned(1024))) char smem[kSmem];
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <class G, int EPI, int BK, int NSTAGE>
+__global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArgs p) {
+  constexpr int MB = G::MB, NB = G::NB;
+  constexpr int RB = BK * 2;                 // LDS row bytes
+  constexpr int CPR = RB / 16;               // 16-byte chunks per row
+  constexpr int STG = (BM + BN) * RB;        // bytes per stage
+  constexpr int SMEM = NSTAGE * STG > kEpiSmem ? NSTAGE * STG : kEpiSmem;
+  constexpr int LPO = BM * CPR / (64 * G::kWaves);  // direct loads per wave per operand per stage
+  constexpr int LPS = 2 * LPO;
+  constexpr int KG = BK / 16;                // 16-element k-groups per step
+  static_assert(BM == BN, "loads assume equal A and B tile heights");
+  __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   Tile t;
   if (!tile_of(p, t)) return;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = G::wm(), wn = G::wn();
   const int m0 = t.tm * BM, n0 = t.tn * BN;
   const int64_t kb = (int64_t)t.ks * p.k_split;
   const int64_t ke = kb + p.k_split < p.k_end ? kb + p.k_split : p.k_end;
   const int nk = ke > kb ? (int)((ke - kb) / BK) : 0;
 
   int hit_lo[NB], hit_hi[NB];
-  if constexpr (EPI == EPI_FWD || EPI == EPI_DZ) hit_ranges(p, t, hit_lo, hit_hi);
+  if constexpr (EPI == EPI_FWD || EPI == EPI_DZ) hit_ranges<G>(p, t, hit_lo, hit_hi);
 
-  // Per-lane sources of the 8 + 8 direct loads of one stage.
-  const char* srcA[8];
-  const char* srcB[8];
+  auto swz = [](int row) { return CPR == 8 ? swz8(row) : swz4(row); };
+  const char* srcA[LPO];
+  const char* srcB[LPO];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int slot = (i * 4 + wid) * 64 + lane;  // 16-byte slot in the tile
-    const int row = slot >> 3, c = (slot & 7) ^ (row & 7);
+  for (int i = 0; i < LPO; ++i) {
+    const int slot = (i * G::kWaves + wid) * 64 + lane;  // 16-byte slot within a tile
+    const int row = slot / CPR, c = (slot % CPR) ^ swz(row);
     const int ga = min(m0 + row, p.M - 1);
     const int gb = min(n0 + row, p.N - 1);
     srcA[i] = (const char*)p.A + ((int64_t)ga * p.lda + kb) * 2 + c * 16;
     srcB[i] = (const char*)p.B + ((int64_t)gb * p.ldb + kb) * 2 + c * 16;
   }
-  auto issue = [&](int stage, int kt) {
-    char* base = smem + stage * kStage;
-    const int64_t ko = (int64_t)kt * BK * 2;
+  auto issue = [&](int kt) {
+    char* base = smem + (kt % NSTAGE) * STG;
+    const int64_t ko = (int64_t)kt * RB;
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(srcA[i] + ko), (lds_void*)(base + (i * 4 + wid) * 1024), 16, 0, 0);
+    for (int i = 0; i < LPO; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(srcA[i] + ko),
+                                       (lds_void*)(base + (i * G::kWaves + wid) * 1024), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < LPO; ++i)
       __builtin_amdgcn_global_load_lds((const void*)(srcB[i] + ko),
-                                       (lds_void*)(base + BM * 128 + (i * 4 + wid) * 1024), 16, 0, 0);
+                                       (lds_void*)(base + BM * RB + (i * G::kWaves + wid) * 1024), 16, 0, 0);
   };
 
-  Acc acc;
+  f32x16_t acc[MB][NB];
+  zero_acc<G>(acc);
+  bf16x8_t fa[2][MB], fb[2][NB];
+  auto load_frags = [&](int kt, int kk, int buf) {
+    const char* sA = smem + (kt % NSTAGE) * STG;
+    const char* sB = sA + BM * RB;
+    const int c = kk * 2 + (lane >> 5);
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+    for (int mb = 0; mb < MB; ++mb) {
+      const int row = wm * G::WM + mb * 32 + (lane & 31);
+      fa[buf][mb] = *(const bf16x8_t*)(sA + row * RB + ((c ^ swz(row)) << 4));
+    }
 #pragma unroll
-    for (int j = 0; j < NB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
-  using M_ = Mfma<uint16_t>;
-  typename M_::Frag fa[2][MB], fb[2][NB];
-  auto load_frags = [&](int stage, int kk, int buf) {
-    const char* sA = smem + stage * kStage;
-    const char* sB = sA + BM * 128;
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) fa[buf][mb] = M_::load(sA, wm * WM + mb * 32 + (lane & 31), kk, lane);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) fb[buf][nb] = M_::load(sB, wn * WN + nb * 32 + (lane & 31), kk, lane);
+    for (int nb = 0; nb < NB; ++nb) {
+      const int row = wn * G::WN + nb * 32 + (lane & 31);
+      fb[buf][nb] = *(const bf16x8_t*)(sB + row * RB + ((c ^ swz(row)) << 4));
+    }
   };
 
   if (nk > 0) {
-    issue(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int s = 0; s < NSTAGE - 1; ++s)
+      if (s < nk) issue(s);
+    if (nk >= NSTAGE - 1)
+      wait_vmcnt<LPS * (NSTAGE - 2)>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();
     load_frags(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) issue(cur ^ 1, kt + 1);
+      const bool more = kt + NSTAGE - 1 < nk;
+      if (more) issue(kt + NSTAGE - 1);
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        if (kk < 3) load_frags(cur, kk + 1, (kk + 1) & 1);
+      for (int kk = 0; kk < KG; ++kk) {
+        if (kk + 1 < KG) load_frags(kt, kk + 1, (kk + 1) & 1);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb) M_::mma(fa[kk & 1][mb], fb[kk & 1][nb], acc[mb][nb]);
+          for (int nb = 0; nb < NB; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][mb], fb[kk & 1][nb], acc[mb][nb], 0, 0, 0);
       }
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      // stage kt + 1 must have landed; later stages may still be in flight
+      if (more)
+        wait_vmcnt<LPS * (NSTAGE - 2)>();
+      else
+        wait_vmcnt<0>();
       __syncthreads();
-      if (kt + 1 < nk) load_frags(cur ^ 1, 0, 0);
+      if (kt + 1 < nk) load_frags(kt + 1, 0, 0);
     }
   }
-  gemm_epilogue<2, EPI>(p, acc, t, smem, hit_lo, hit_hi);
+  gemm_epilogue<G, 2, EPI>(p, acc, t, smem, hit_lo, hit_hi);
 }
+
+// Main-loop configuration of the bf16 path (wave grid, k-step, stages).
+#ifndef KDKL_GEMM_WAVES
+#define KDKL_GEMM_WAVES 8
+#endif
+#ifndef KDKL_GEMM_BK
+#define KDKL_GEMM_BK 64
+#endif
+#ifndef KDKL_GEMM_STAGES
+#define KDKL_GEMM_STAGES 2
+#endif
+using FastGrid = typename std::conditional<KDKL_GEMM_WAVES == 8, Grid8, Grid4>::type;
 
 template <int EPI>
 static hipError_t launch_gemm_e(int dtype, const GemmArgs& a, hipStream_t s) {
   const int total = a.tiles_m * a.tiles_n * a.splits;
   if (total <= 0) return hipSuccess;
   const int per = (total + 7) / 8;
-  const dim3 grid(per * 8), block(256);
-  const bool fast = dtype == 1 && a.k_end % 64 == 0 && a.k_split % 64 == 0;
+  const dim3 grid(per * 8);
+  const bool fast = dtype == 1 && a.k_end % KDKL_GEMM_BK == 0 && a.k_split % KDKL_GEMM_BK == 0;
   if (fast)
-    hipLaunchKernelGGL(gemm_bf16_fast_kernel<EPI>, grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_bf16_kernel<FastGrid, EPI, KDKL_GEMM_BK, KDKL_GEMM_STAGES>), grid,
+                       dim3(FastGrid::kThreads), 0, s, a);
   else if (dtype == 1)
-    hipLaunchKernelGGL((gemm_generic_kernel<uint16_t, EPI>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_generic_kernel<uint16_t, EPI>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_generic_kernel<float, EPI>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((gemm_generic_kernel<float, EPI>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -824,6 +902,6 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
   }
 }
 
-int gemm_k_step(int dtype) { return dtype == 1 ? 64 : 32; }
+int gemm_k_step(int dtype) { return dtype == 1 ? KDKL_GEMM_BK : 32; }
 
 }  // namespace kdkl
