@@ -78,6 +78,7 @@ struct Plan {
   int64_t n_vt;    // vocabulary tiles
   int dh_splits;
   int64_t dh_ksplit;
+  bool fast;       // bf16 main loop: reads W, H and dZ in place (no transposes)
   // offsets into the forward workspace
   size_t f_sids, f_sp, f_erow, f_tstart, f_part, f_rowkl, f_bytes;
   // offsets into the backward workspace
@@ -107,6 +108,7 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   P->N = N; P->d = d; P->V = V; P->K = K; P->dtype = dtype;
   P->es = dtype == KDKL_BF16 ? 2 : 4;
   P->chunk = chunk < N ? chunk : (N > 0 ? N : 1);
+  P->fast = gemm_fast_path(dtype, d);
   P->Cp = round_up(P->chunk, kTokenTile);
   P->Vp = round_up(V, kVocabTile);
   P->n_vt = P->Vp / kVocabTile;
@@ -142,11 +144,20 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   ok &= region(&cur, t1, &P->b_tstart);
   int64_t wt, ht, dz, dhp;
   ok &= mul_ok(d, P->Vp, &wt) && mul_ok(wt, P->es, &wt);
-  ok &= region(&cur, wt, &P->b_wt);
   ok &= mul_ok(d, P->Cp, &ht) && mul_ok(ht, P->es, &ht);
-  ok &= region(&cur, ht, &P->b_ht);
   ok &= mul_ok(P->Cp, P->Vp, &dz) && mul_ok(dz, P->es, &dz);
-  ok &= region(&cur, dz, &P->b_dzcv) && region(&cur, dz, &P->b_dzvc);
+  if (P->fast) {
+    // dW reads H and the token-major dZ in place through the LDS transpose;
+    // dH reads W^T, transposed once per call (cheaper than transposed reads
+    // of W in every chunk).
+    P->b_ht = P->b_dzvc = 0;
+    ok &= region(&cur, wt, &P->b_wt);
+    ok &= region(&cur, dz, &P->b_dzcv);
+  } else {
+    ok &= region(&cur, wt, &P->b_wt);
+    ok &= region(&cur, ht, &P->b_ht);
+    ok &= region(&cur, dz, &P->b_dzcv) && region(&cur, dz, &P->b_dzvc);
+  }
   ok &= mul_ok(S * P->Cp, d, &dhp) && mul_ok(dhp, 4, &dhp);
   ok &= region(&cur, dhp, &P->b_dhpart);
   P->b_bytes = cur;
@@ -188,6 +199,7 @@ static GemmArgs projection_args(const Plan& P, const void* H, const void* W, flo
   g.sids = (const int32_t*)(ws + o_sids); g.sp = (const float*)(ws + o_sp);
   g.tstart = (const uint16_t*)(ws + o_tstart);
   g.Vp = P.Vp;
+  g.a_layout = g.b_layout = LAYOUT_KC;
   return g;
 }
 
@@ -278,10 +290,11 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
     if (!accumulate_dW) e = launch_zero(dW, V * d, s);
     return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
   }
-  // W^T [d, Vp], zero-padded, once per call: the dH product contracts over V.
+  // W^T [d, Vp], zero-padded, once per call: the dH product contracts over
+  // V and reads both operands K-contiguous.
   e = timed(K_TRANSPOSE_W, 0.0, 2.0 * (double)V * d * P.es, s, [&] {
-    return launch_transpose((int)P.es, W, V, d, d, ws + P.b_wt, P.Vp, P.Vp, s);
-  });
+      return launch_transpose((int)P.es, W, V, d, d, ws + P.b_wt, P.Vp, P.Vp, s);
+    });
   const double coef_base = 1.0 / ((double)N * (double)T);
   for (int64_t r0 = 0; r0 < N && e == hipSuccess; r0 += P.chunk) {
     const int rows = (int)((N - r0) < P.chunk ? (N - r0) : P.chunk);
@@ -289,25 +302,29 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
     TeacherArgs ta = teacher_args(P, ids, lg, T, r0, rows, ws, P.b_sids, P.b_sp, P.b_erow, P.b_tstart);
     e = timed(K_TEACHER, 0.0, (double)rows * P.K * 8.0 * 2.0, s, [&] { return launch_teacher(ta, s); });
     if (e != hipSuccess) break;
-    // H_c^T [d, Cp], zero-padded past the chunk's rows: the dW product
-    // contracts over the chunk's tokens.
     const char* Hc = (const char*)H + r0 * d * P.es;
-    e = timed(K_TRANSPOSE_H, 0.0, 2.0 * (double)rows * d * P.es, s, [&] {
-      return launch_transpose((int)P.es, Hc, rows, d, d, ws + P.b_ht, rows_pad, P.Cp, s);
-    });
-    if (e != hipSuccess) break;
-    // recompute the chunk's logits and form dZ in both layouts
+    if (!P.fast) {
+      // H_c^T [d, Cp], zero-padded past the chunk's rows: the dW product
+      // contracts over the chunk's tokens.
+      e = timed(K_TRANSPOSE_H, 0.0, 2.0 * (double)rows * d * P.es, s, [&] {
+        return launch_transpose((int)P.es, Hc, rows, d, d, ws + P.b_ht, rows_pad, P.Cp, s);
+      });
+      if (e != hipSuccess) break;
+    }
+    // recompute the chunk's logits and form dZ (token-major; the generic
+    // path also writes the vocabulary-major copy)
     GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.b_sids, P.b_sp, P.b_tstart);
     g.row_lse = row_lse + r0; g.grad = grad_loss; g.coef_base = (float)coef_base;
-    g.dz_cv = ws + P.b_dzcv; g.dz_vc = ws + P.b_dzvc;
+    g.dz_cv = ws + P.b_dzcv; g.dz_vc = P.fast ? nullptr : ws + P.b_dzvc;
     const double fl = 2.0 * rows * (double)V * d;
-    e = timed(K_DZ_GEMM, fl, ((double)V + rows) * d * P.es + 2.0 * rows * (double)V * P.es, s,
+    e = timed(K_DZ_GEMM, fl, ((double)V + rows) * d * P.es + (P.fast ? 1.0 : 2.0) * rows * (double)V * P.es, s,
               [&] { return launch_gemm(dtype, EPI_DZ, g, s); });
     if (e != hipSuccess) break;
     // dH_c = dZ_c W  (split over the vocabulary, then a fixed-order sum)
     GemmArgs h;
     memset(&h, 0, sizeof(h));
-    h.A = ws + P.b_dzcv; h.lda = P.Vp; h.B = ws + P.b_wt; h.ldb = P.Vp;
+    h.A = ws + P.b_dzcv; h.lda = P.Vp; h.a_layout = LAYOUT_KC;
+    h.B = ws + P.b_wt; h.ldb = P.Vp; h.b_layout = LAYOUT_KC;
     h.M = rows; h.N = (int)d; h.k_end = P.Vp; h.k_split = P.dh_ksplit;
     h.tiles_m = (int)((rows + 255) / 256); h.tiles_n = (int)((d + 255) / 256);
     h.splits = (int)((P.Vp + P.dh_ksplit - 1) / P.dh_ksplit);
@@ -324,7 +341,13 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
     // dW (+)= dZ_c^T H_c
     GemmArgs w;
     memset(&w, 0, sizeof(w));
-    w.A = ws + P.b_dzvc; w.lda = P.Cp; w.B = ws + P.b_ht; w.ldb = P.Cp;
+    if (P.fast) {
+      w.A = ws + P.b_dzcv; w.lda = P.Vp; w.a_layout = LAYOUT_MC; w.a_krows = P.Cp; w.a_mcols = P.Vp;
+      w.B = Hc; w.ldb = d; w.b_layout = LAYOUT_MC; w.b_krows = N - r0; w.b_mcols = d;
+    } else {
+      w.A = ws + P.b_dzvc; w.lda = P.Cp; w.a_layout = LAYOUT_KC;
+      w.B = ws + P.b_ht; w.ldb = P.Cp; w.b_layout = LAYOUT_KC;
+    }
     w.M = (int)V; w.N = (int)d; w.k_end = rows_pad; w.k_split = rows_pad;
     w.tiles_m = (int)P.n_vt; w.tiles_n = (int)((d + 255) / 256); w.splits = 1;
     w.out = dW; w.ldo = d; w.accumulate = (r0 > 0 || accumulate_dW) ? 1 : 0;

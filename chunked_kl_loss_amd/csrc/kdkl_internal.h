@@ -73,7 +73,20 @@ struct GemmArgs {
   float* out;
   int64_t ldo;
   int accumulate;
+  // Operand layouts of the bf16 main loop: LAYOUT_KC = rows along the
+  // output axis with K contiguous; LAYOUT_MC = rows along K with the output
+  // axis contiguous (fragments through the LDS transpose read). For MC, the
+  // operand has *_krows valid rows and *_mcols valid columns; reads past
+  // them are clamped (their products are zero or masked).
+  int a_layout, b_layout;
+  int64_t a_krows, a_mcols, b_krows, b_mcols;
 };
+
+enum { LAYOUT_KC = 0, LAYOUT_MC = 1 };
+
+// True when the bf16 main loop (direct-to-LDS loads, no zero fill) serves
+// the projections: bf16 storage and d a multiple of the 64-element k-step.
+bool gemm_fast_path(int dtype, int64_t d);
 
 struct MergeArgs {
   const float4* part;   // [Cp, n_vt]

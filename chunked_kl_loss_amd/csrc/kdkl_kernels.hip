@@ -26,6 +26,9 @@ namespace kdkl {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(16))) float f32x16_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(4))) short s16x4_t;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4_t;
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
 
 static constexpr float kNegInf = -__builtin_huge_valf();
 static constexpr float kLog2e = 1.4426950408889634f;
@@ -499,7 +502,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
           const int i = j >> 5, c = j & 31;
           *(uint4*)(cv + (int64_t)(nb0 + i) * p.Vp + m0 + c * 8) = *(const uint4*)(T + i * kDzPitch + c * 8);
         }
-        // vocabulary-major rows: 256 bytes of tokens each
+        // vocabulary-major rows: 256 bytes of tokens each (only for the
+        // generic path, whose dW product needs K-contiguous operands)
+        if (vc == nullptr) continue;
 #pragma unroll 4
         for (int j = tid; j < BM * 16; j += NT) {
           const int v = j & (BM - 1), c = j >> 8;
@@ -762,17 +767,28 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <class G, int EPI, int BK, int NSTAGE>
+// Main-loop configuration of the bf16 path (wave grid, k-step, stages).
+#ifndef KDKL_GEMM_WAVES
+#define KDKL_GEMM_WAVES 8
+#endif
+#ifndef KDKL_GEMM_BK
+#define KDKL_GEMM_BK 64
+#endif
+#ifndef KDKL_GEMM_STAGES
+#define KDKL_GEMM_STAGES 2
+#endif
+template <class G, int EPI, int BK, int NSTAGE, int LA, int LB>
 __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArgs p) {
   constexpr int MB = G::MB, NB = G::NB;
-  constexpr int RB = BK * 2;                 // LDS row bytes
-  constexpr int CPR = RB / 16;               // 16-byte chunks per row
-  constexpr int STG = (BM + BN) * RB;        // bytes per stage
+  constexpr int RB = BK * 2;                 // bytes of one k-contiguous LDS row
+  constexpr int CPR = RB / 16;               // 16-byte chunks per such row
+  constexpr int TILE = BM * RB;              // bytes of one operand tile per stage
+  constexpr int STG = 2 * TILE;
   constexpr int SMEM = NSTAGE * STG > kEpiSmem ? NSTAGE * STG : kEpiSmem;
-  constexpr int LPO = BM * CPR / (64 * G::kWaves);  // direct loads per wave per operand per stage
+  constexpr int LPO = TILE / (1024 * G::kWaves);  // direct loads per wave per operand per stage
   constexpr int LPS = 2 * LPO;
   constexpr int KG = BK / 16;                // 16-element k-groups per step
-  static_assert(BM == BN, "loads assume equal A and B tile heights");
+  static_assert(BM == BN && BM == 256, "k-major LDS rows hold 256 elements");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   Tile t;
   if (!tile_of(p, t)) return;
@@ -787,47 +803,88 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
   if constexpr (EPI == EPI_FWD || EPI == EPI_DZ) hit_ranges<G>(p, t, hit_lo, hit_hi);
 
   auto swz = [](int row) { return CPR == 8 ? swz8(row) : swz4(row); };
-  const char* srcA[LPO];
-  const char* srcB[LPO];
+
+  // Per-lane sources of the direct loads. KC: 16-byte chunk of an output-
+  // axis row, advanced by RB bytes per k-step. MC: 16-byte unit of a k row;
+  // the row index is clamped per k-step.
+  struct Src {
+    const char* base;  // KC: full pointer at k-step 0; MC: row 0 pointer + column offset
+    int krow;          // MC: row within the stage
+  };
+  auto make_src = [&](int layout, const void* X, int64_t ld, int rows, int row0, int64_t krows,
+                      int64_t mcols, int i) {
+    Src s;
+    const int slot = (i * G::kWaves + wid) * 64 + lane;
+    if (layout == LAYOUT_KC) {
+      const int row = slot / CPR, c = (slot % CPR) ^ swz(row);
+      const int g = min(row0 + row, rows - 1);
+      s.base = (const char*)X + ((int64_t)g * ld + kb) * 2 + c * 16;
+      s.krow = 0;
+    } else {
+      const int kr = slot >> 5, u = (slot & 31) ^ (4 * (kr & 3));
+      const int64_t col = min((int64_t)row0 + u * 8, mcols - 8);
+      s.base = (const char*)X + col * 2;
+      s.krow = kr;
+    }
+    return s;
+  };
+  Src sa[LPO], sb[LPO];
 #pragma unroll
   for (int i = 0; i < LPO; ++i) {
-    const int slot = (i * G::kWaves + wid) * 64 + lane;  // 16-byte slot within a tile
-    const int row = slot / CPR, c = (slot % CPR) ^ swz(row);
-    const int ga = min(m0 + row, p.M - 1);
-    const int gb = min(n0 + row, p.N - 1);
-    srcA[i] = (const char*)p.A + ((int64_t)ga * p.lda + kb) * 2 + c * 16;
-    srcB[i] = (const char*)p.B + ((int64_t)gb * p.ldb + kb) * 2 + c * 16;
+    sa[i] = make_src(LA, p.A, p.lda, p.M, m0, p.a_krows, p.a_mcols, i);
+    sb[i] = make_src(LB, p.B, p.ldb, p.N, n0, p.b_krows, p.b_mcols, i);
   }
+  auto src_at = [&](int layout, const Src& s, int64_t ld, int64_t krows, int kt) -> const char* {
+    if (layout == LAYOUT_KC) return s.base + (int64_t)kt * RB;
+    const int64_t k = min(kb + (int64_t)kt * BK + s.krow, krows - 1);
+    return s.base + k * ld * 2;
+  };
   auto issue = [&](int kt) {
     char* base = smem + (kt % NSTAGE) * STG;
-    const int64_t ko = (int64_t)kt * RB;
 #pragma unroll
     for (int i = 0; i < LPO; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(srcA[i] + ko),
+      __builtin_amdgcn_global_load_lds((const void*)src_at(LA, sa[i], p.lda, p.a_krows, kt),
                                        (lds_void*)(base + (i * G::kWaves + wid) * 1024), 16, 0, 0);
 #pragma unroll
     for (int i = 0; i < LPO; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(srcB[i] + ko),
-                                       (lds_void*)(base + BM * RB + (i * G::kWaves + wid) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void*)src_at(LB, sb[i], p.ldb, p.b_krows, kt),
+                                       (lds_void*)(base + TILE + (i * G::kWaves + wid) * 1024), 16, 0, 0);
   };
 
   f32x16_t acc[MB][NB];
   zero_acc<G>(acc);
   bf16x8_t fa[2][MB], fb[2][NB];
+  // One MFMA operand fragment (8 consecutive k of output row/column `r0 +
+  // (lane & 31)`) from an operand tile in either layout.
+  auto frag = [&](int layout, const char* s, int r0, int kk) -> bf16x8_t {
+    if (layout == LAYOUT_KC) {
+      const int row = r0 + (lane & 31);
+      const int c = kk * 2 + (lane >> 5);
+      return *(const bf16x8_t*)(s + row * RB + ((c ^ swz(row)) << 4));
+    } else {
+      const int q = ((r0 + 16 * ((lane >> 4) & 1)) >> 2) + (lane & 3);
+      bf16x8_t v;
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+        const int k = kk * 16 + 8 * (lane >> 5) + 4 * j2 + ((lane & 15) >> 2);
+        const int pq = q ^ (8 * (k & 3));
+        const s16x4_t h = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s + k * 512 + pq * 8));
+        const bf16x4_t hb = __builtin_bit_cast(bf16x4_t, h);
+        v[4 * j2 + 0] = hb[0];
+        v[4 * j2 + 1] = hb[1];
+        v[4 * j2 + 2] = hb[2];
+        v[4 * j2 + 3] = hb[3];
+      }
+      return v;
+    }
+  };
   auto load_frags = [&](int kt, int kk, int buf) {
     const char* sA = smem + (kt % NSTAGE) * STG;
-    const char* sB = sA + BM * RB;
-    const int c = kk * 2 + (lane >> 5);
+    const char* sB = sA + TILE;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      const int row = wm * G::WM + mb * 32 + (lane & 31);
-      fa[buf][mb] = *(const bf16x8_t*)(sA + row * RB + ((c ^ swz(row)) << 4));
-    }
+    for (int mb = 0; mb < MB; ++mb) fa[buf][mb] = frag(LA, sA, wm * G::WM + mb * 32, kk);
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int row = wn * G::WN + nb * 32 + (lane & 31);
-      fb[buf][nb] = *(const bf16x8_t*)(sB + row * RB + ((c ^ swz(row)) << 4));
-    }
+    for (int nb = 0; nb < NB; ++nb) fb[buf][nb] = frag(LB, sB, wn * G::WN + nb * 32, kk);
   };
 
   if (nk > 0) {
@@ -850,7 +907,8 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][mb], fb[kk & 1][nb], acc[mb][nb], 0, 0, 0);
+            acc[mb][nb] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][mb], fb[kk & 1][nb], acc[mb][nb], 0, 0, 0);
       }
       // stage kt + 1 must have landed; later stages may still be in flight
       if (more)
@@ -864,17 +922,16 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
   gemm_epilogue<G, 2, EPI>(p, acc, t, smem, hit_lo, hit_hi);
 }
 
-// Main-loop configuration of the bf16 path (wave grid, k-step, stages).
-#ifndef KDKL_GEMM_WAVES
-#define KDKL_GEMM_WAVES 8
-#endif
-#ifndef KDKL_GEMM_BK
-#define KDKL_GEMM_BK 64
-#endif
-#ifndef KDKL_GEMM_STAGES
-#define KDKL_GEMM_STAGES 2
-#endif
 using FastGrid = typename std::conditional<KDKL_GEMM_WAVES == 8, Grid8, Grid4>::type;
+
+bool gemm_fast_path(int dtype, int64_t d) { return dtype == 1 && d % KDKL_GEMM_BK == 0; }
+
+template <int EPI, int LA, int LB>
+static hipError_t launch_fast(const GemmArgs& a, dim3 grid, hipStream_t s) {
+  hipLaunchKernelGGL((gemm_bf16_kernel<FastGrid, EPI, KDKL_GEMM_BK, KDKL_GEMM_STAGES, LA, LB>), grid,
+                     dim3(FastGrid::kThreads), 0, s, a);
+  return hipGetLastError();
+}
 
 template <int EPI>
 static hipError_t launch_gemm_e(int dtype, const GemmArgs& a, hipStream_t s) {
@@ -883,10 +940,15 @@ static hipError_t launch_gemm_e(int dtype, const GemmArgs& a, hipStream_t s) {
   const int per = (total + 7) / 8;
   const dim3 grid(per * 8);
   const bool fast = dtype == 1 && a.k_end % KDKL_GEMM_BK == 0 && a.k_split % KDKL_GEMM_BK == 0;
-  if (fast)
-    hipLaunchKernelGGL((gemm_bf16_kernel<FastGrid, EPI, KDKL_GEMM_BK, KDKL_GEMM_STAGES>), grid,
-                       dim3(FastGrid::kThreads), 0, s, a);
-  else if (dtype == 1)
+  if (fast) {
+    // the operand layouts each projection uses
+    if (a.a_layout == LAYOUT_KC && a.b_layout == LAYOUT_KC) return launch_fast<EPI, LAYOUT_KC, LAYOUT_KC>(a, grid, s);
+    if constexpr (EPI == EPI_DW)
+      if (a.a_layout == LAYOUT_MC && a.b_layout == LAYOUT_MC) return launch_fast<EPI, LAYOUT_MC, LAYOUT_MC>(a, grid, s);
+    return hipErrorInvalidValue;
+  }
+  if (a.a_layout != LAYOUT_KC || a.b_layout != LAYOUT_KC) return hipErrorInvalidValue;
+  if (dtype == 1)
     hipLaunchKernelGGL((gemm_generic_kernel<uint16_t, EPI>), grid, dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((gemm_generic_kernel<float, EPI>), grid, dim3(256), 0, s, a);
