@@ -38,16 +38,38 @@ def kernel_source_hash() -> str:
 
 
 def load_traffic(kernel: str, workload: str):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
-    were taken on the current kernel sources; else None."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (profiles/traffic_<kernel>_<workload>.txt, lines "key: value"),
+    if it was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
     if not os.path.exists(path):
         return None
+    kv = {}
     with open(path) as fh:
-        t = json.load(fh)
-    if t.get("source_hash") != kernel_source_hash():
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_hash") != kernel_source_hash():
         return None
-    return t.get("hbm_bytes_per_launch")
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_calibration():
+    """A plain device copy of known size, profiled with the same rocprofv3
+    counters as the kernels to scale FETCH_SIZE / WRITE_SIZE to bytes."""
+    import torch
+
+    n = 1 << 28  # 2^28 fp32 = 1 GiB each way
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
 
 
 def cpu_baseline(w, x, rows: int):
@@ -78,9 +100,14 @@ def main():
     ap.add_argument("--config", default="gptoss20b_32k")
     ap.add_argument("--N", type=int, default=None, help="override the number of positions")
     ap.add_argument("--chunk", type=int, default=None, help="override the chunk size")
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "

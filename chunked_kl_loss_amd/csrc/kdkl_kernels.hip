@@ -308,8 +308,9 @@ struct Grid {
   static __device__ __forceinline__ int wm() { return (int)(threadIdx.x >> 6) / WAVES_N; }
   static __device__ __forceinline__ int wn() { return (int)(threadIdx.x >> 6) % WAVES_N; }
 };
-using Grid4 = Grid<2, 2>;  // 4 wavefronts of 128 x 128
-using Grid8 = Grid<2, 4>;  // 8 wavefronts of 128 x 64 (two per SIMD)
+using Grid4 = Grid<2, 2>;   // 4 wavefronts of 128 x 128
+using Grid8 = Grid<2, 4>;   // 8 wavefronts of 128 x 64 (two per SIMD)
+using Grid16 = Grid<4, 4>;  // 16 wavefronts of 64 x 64 (four per SIMD)
 
 __device__ __forceinline__ int swz8(int row) { return (row >> 1) & 7; }
 __device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
@@ -558,19 +559,20 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
   } else {
     // EPI_DW: dW[row, col] (+)= tile, staged through LDS 128 rows at a time
     // so the read-modify-write of dW uses 16-byte accesses on whole rows.
-    static_assert(G::WM == 128, "dW staging assumes 128-row wavefront tiles");
+    static_assert(128 % G::WM == 0, "dW staging takes whole wavefront tiles per 128-row half");
     float* F = (float*)smem;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       __syncthreads();
-      if (wm == half) {
+      if ((wm * G::WM) / 128 == half) {
+        const int rb = wm * G::WM - half * 128;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              F[(mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kDwPitch + wn * G::WN + nb * 32 +
+              F[(rb + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kDwPitch + wn * G::WN + nb * 32 +
                 (lane & 31)] = acc[mb][nb][r];
       }
       __syncthreads();
@@ -792,8 +794,12 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   Tile t;
   if (!tile_of(p, t)) return;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = G::wm(), wn = G::wn();
+  // The wavefront index is uniform across a wavefront; reading it through
+  // readfirstlane lets every LDS destination (M0) be computed in scalar
+  // registers instead of a vector-to-scalar move per load.
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid / G::kWavesN, wn = wid % G::kWavesN;
   const int m0 = t.tm * BM, n0 = t.tn * BN;
   const int64_t kb = (int64_t)t.ks * p.k_split;
   const int64_t ke = kb + p.k_split < p.k_end ? kb + p.k_split : p.k_end;
@@ -922,7 +928,8 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
   gemm_epilogue<G, 2, EPI>(p, acc, t, smem, hit_lo, hit_hi);
 }
 
-using FastGrid = typename std::conditional<KDKL_GEMM_WAVES == 8, Grid8, Grid4>::type;
+using FastGrid = typename std::conditional<
+    KDKL_GEMM_WAVES == 16, Grid16, typename std::conditional<KDKL_GEMM_WAVES == 8, Grid8, Grid4>::type>::type;
 
 bool gemm_fast_path(int dtype, int64_t d) { return dtype == 1 && d % KDKL_GEMM_BK == 0; }
 

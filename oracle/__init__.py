@@ -14,4 +14,5 @@ from .kl import (  # noqa: F401
     loss_and_grads,
     dense_kl_loss,
     sampled_rows,
+    dw_rows,
 )

@@ -50,6 +50,7 @@ __all__ = [
     "loss_and_grads",
     "dense_kl_loss",
     "sampled_rows",
+    "dw_rows",
 ]
 
 
@@ -213,3 +214,27 @@ def sampled_rows(H, W, ids, logits, T: float, rows: Iterable[int],
         dz = _dz_rows(Hr, Wf, idr, lgr, T, coef)
         dh_out[j] = (dz @ Wf)[0]
     return {"rows": rows, "row_lse": lse_out, "row_kl": kl_out, "dH_rows": dh_out}
+
+
+def dw_rows(H, W, ids, logits, T: float, vrows: Iterable[int], row_lse,
+            g: float = 1.0) -> np.ndarray:
+    """Rows ``vrows`` of dW for the whole problem, given every position's
+    logsumexp of z/T (``row_lse``, as written by ``forward``):
+    ``dW_v = sum_n dZ_nv H_n`` with ``dZ_nv = g/(N T) (exp(z_nv/T - lse_n)
+    - P_nv)`` and ``P_nv`` the teacher mass on id v (same definition as
+    ``backward``, evaluated one vocabulary row at a time)."""
+    Hf = _f64(H)
+    ids_ = _ids(ids)
+    vrows = np.asarray(list(vrows), dtype=np.int64)
+    N = Hf.shape[0]
+    coef = float(g) / (N * float(T))
+    Wv = _f64(W[vrows])  # [nv, d]
+    p, _ = teacher_distribution(logits, T)
+    lse = np.asarray(row_lse, dtype=np.float64)
+    out = np.zeros((vrows.size, Hf.shape[1]))
+    for j, v in enumerate(vrows.tolist()):
+        z = Hf @ Wv[j] / float(T)
+        P = (p * (ids_ == v)).sum(axis=1)
+        dz = coef * (np.exp(z - lse) - P)
+        out[j] = dz @ Hf
+    return out

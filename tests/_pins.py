@@ -228,6 +228,26 @@ def pin_invariants(o):
     _close(dW6, dW, 1e-12, what="temperature identity dW")
 
 
+def pin_row_functions(o):
+    """The one-row-at-a-time helpers used at full size agree with the full
+    forward/backward (themselves pinned by finite differences above)."""
+    if not hasattr(o, "sampled_rows"):
+        return
+    rng = np.random.default_rng(18)
+    N, d, V, K, T, g = 12, 5, 31, 4, 1.6, 0.9
+    H, W, ids, logits = _rand_problem(rng, N, d, V, K)
+    f = o.forward(H, W, ids, logits, T)
+    dH, dW = o.backward(H, W, ids, logits, T, g)
+    rows = [0, 5, 11]
+    sr = o.sampled_rows(H, W, ids, logits, T, rows, N, g)
+    _close(sr["row_lse"], f["row_lse"][rows], 1e-13, what="sampled lse")
+    _close(sr["row_kl"], f["row_kl"][rows], 1e-13, what="sampled kl")
+    _close(sr["dH_rows"], dH[rows], 1e-13, what="sampled dH rows")
+    vrows = [0, 7, int(ids[3, 1]), 30]
+    _close(o.dw_rows(H, W, ids, logits, T, vrows, f["row_lse"], g), dW[vrows], 1e-12,
+           what="sampled dW rows")
+
+
 ALL_PINS = [
     pin_two_token_softplus,
     pin_uniform_student,
@@ -236,4 +256,5 @@ ALL_PINS = [
     pin_equality_case,
     pin_finite_differences,
     pin_invariants,
+    pin_row_functions,
 ]
