@@ -147,11 +147,12 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   ok &= mul_ok(d, P->Cp, &ht) && mul_ok(ht, P->es, &ht);
   ok &= mul_ok(P->Cp, P->Vp, &dz) && mul_ok(dz, P->es, &dz);
   if (P->fast) {
-    // dW reads H and the token-major dZ in place through the LDS transpose;
-    // dH reads W^T, transposed once per call (cheaper than transposed reads
-    // of W in every chunk).
-    P->b_ht = P->b_dzvc = 0;
+    // dW reads the token-major dZ in place through the LDS transpose and
+    // H_c^T (one small transpose per chunk); dH reads W^T, transposed once
+    // per call (cheaper than transposed reads of W in every chunk).
+    P->b_dzvc = 0;
     ok &= region(&cur, wt, &P->b_wt);
+    ok &= region(&cur, ht, &P->b_ht);
     ok &= region(&cur, dz, &P->b_dzcv);
   } else {
     ok &= region(&cur, wt, &P->b_wt);
@@ -302,15 +303,13 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
     TeacherArgs ta = teacher_args(P, ids, lg, T, r0, rows, ws, P.b_sids, P.b_sp, P.b_erow, P.b_tstart);
     e = timed(K_TEACHER, 0.0, (double)rows * P.K * 8.0 * 2.0, s, [&] { return launch_teacher(ta, s); });
     if (e != hipSuccess) break;
+    // H_c^T [d, Cp], zero-padded past the chunk's rows: the dW product
+    // contracts over the chunk's tokens.
     const char* Hc = (const char*)H + r0 * d * P.es;
-    if (!P.fast) {
-      // H_c^T [d, Cp], zero-padded past the chunk's rows: the dW product
-      // contracts over the chunk's tokens.
-      e = timed(K_TRANSPOSE_H, 0.0, 2.0 * (double)rows * d * P.es, s, [&] {
-        return launch_transpose((int)P.es, Hc, rows, d, d, ws + P.b_ht, rows_pad, P.Cp, s);
-      });
-      if (e != hipSuccess) break;
-    }
+    e = timed(K_TRANSPOSE_H, 0.0, 2.0 * (double)rows * d * P.es, s, [&] {
+      return launch_transpose((int)P.es, Hc, rows, d, d, ws + P.b_ht, rows_pad, P.Cp, s);
+    });
+    if (e != hipSuccess) break;
     // recompute the chunk's logits and form dZ (token-major; the generic
     // path also writes the vocabulary-major copy)
     GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.b_sids, P.b_sp, P.b_tstart);
@@ -343,11 +342,10 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
     memset(&w, 0, sizeof(w));
     if (P.fast) {
       w.A = ws + P.b_dzcv; w.lda = P.Vp; w.a_layout = LAYOUT_MC; w.a_krows = P.Cp; w.a_mcols = P.Vp;
-      w.B = Hc; w.ldb = d; w.b_layout = LAYOUT_MC; w.b_krows = N - r0; w.b_mcols = d;
     } else {
       w.A = ws + P.b_dzvc; w.lda = P.Cp; w.a_layout = LAYOUT_KC;
-      w.B = ws + P.b_ht; w.ldb = P.Cp; w.b_layout = LAYOUT_KC;
     }
+    w.B = ws + P.b_ht; w.ldb = P.Cp; w.b_layout = LAYOUT_KC;
     w.M = (int)V; w.N = (int)d; w.k_end = rows_pad; w.k_split = rows_pad;
     w.tiles_m = (int)P.n_vt; w.tiles_n = (int)((d + 255) / 256); w.splits = 1;
     w.out = dW; w.ldo = d; w.accumulate = (r0 > 0 || accumulate_dW) ? 1 : 0;

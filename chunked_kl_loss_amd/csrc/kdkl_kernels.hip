@@ -949,9 +949,11 @@ static hipError_t launch_gemm_e(int dtype, const GemmArgs& a, hipStream_t s) {
   const bool fast = dtype == 1 && a.k_end % KDKL_GEMM_BK == 0 && a.k_split % KDKL_GEMM_BK == 0;
   if (fast) {
     // the operand layouts each projection uses
-    if (a.a_layout == LAYOUT_KC && a.b_layout == LAYOUT_KC) return launch_fast<EPI, LAYOUT_KC, LAYOUT_KC>(a, grid, s);
+    if (a.a_layout == LAYOUT_KC && a.b_layout == LAYOUT_KC) {
+      return launch_fast<EPI, LAYOUT_KC, LAYOUT_KC>(a, grid, s);
+    }
     if constexpr (EPI == EPI_DW)
-      if (a.a_layout == LAYOUT_MC && a.b_layout == LAYOUT_MC) return launch_fast<EPI, LAYOUT_MC, LAYOUT_MC>(a, grid, s);
+      if (a.a_layout == LAYOUT_MC && a.b_layout == LAYOUT_KC) return launch_fast<EPI, LAYOUT_MC, LAYOUT_KC>(a, grid, s);
     return hipErrorInvalidValue;
   }
   if (a.a_layout != LAYOUT_KC || a.b_layout != LAYOUT_KC) return hipErrorInvalidValue;
