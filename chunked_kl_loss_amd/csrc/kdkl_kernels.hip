@@ -763,6 +763,20 @@ __global__ __launch_bounds__(256, 1) void gemm_generic_kernel(const GemmArgs p) 
 // k-group are read while the MFMAs of the current one run.
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Workgroup barrier for the main loops, which wait for their own loads with
+// explicit vmcnt counts: a bare s_barrier (no implicit wait for every
+// outstanding load, unlike __syncthreads, which would drain the prefetched
+// stages), fenced so that neither the compiler's IR passes (memory clobber)
+// nor its scheduler (MFMAs included, which touch only registers) move
+// anything across it.
+__device__ __forceinline__ void phase_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -778,6 +792,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 #endif
 #ifndef KDKL_GEMM_STAGES
 #define KDKL_GEMM_STAGES 2
+#endif
+#ifndef KDKL_DW_GRID42
+#define KDKL_DW_GRID42 1
 #endif
 template <class G, int EPI, int BK, int NSTAGE, int LA, int LB>
 __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArgs p) {
@@ -901,7 +918,7 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
       wait_vmcnt<LPS * (NSTAGE - 2)>();
     else
       wait_vmcnt<0>();
-    __syncthreads();
+    phase_barrier();
     load_frags(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
       const bool more = kt + NSTAGE - 1 < nk;
@@ -921,7 +938,7 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
         wait_vmcnt<LPS * (NSTAGE - 2)>();
       else
         wait_vmcnt<0>();
-      __syncthreads();
+      phase_barrier();
       if (kt + 1 < nk) load_frags(kt + 1, 0, 0);
     }
   }
@@ -933,10 +950,16 @@ using FastGrid = typename std::conditional<
 
 bool gemm_fast_path(int dtype, int64_t d) { return dtype == 1 && d % KDKL_GEMM_BK == 0; }
 
+// dW multiplies a k-major dZ tile (two transposed LDS reads per fragment)
+// by a K-contiguous H^T tile: a 4 x 2 wave grid (64 x 128 per wave) gives
+// each wave fewer dZ fragments than the 2 x 4 grid of the other products.
+using DwGrid = typename std::conditional<KDKL_GEMM_WAVES == 8 && KDKL_DW_GRID42, Grid<4, 2>, FastGrid>::type;
+
 template <int EPI, int LA, int LB>
 static hipError_t launch_fast(const GemmArgs& a, dim3 grid, hipStream_t s) {
-  hipLaunchKernelGGL((gemm_bf16_kernel<FastGrid, EPI, KDKL_GEMM_BK, KDKL_GEMM_STAGES, LA, LB>), grid,
-                     dim3(FastGrid::kThreads), 0, s, a);
+  using GG = typename std::conditional<EPI == EPI_DW, DwGrid, FastGrid>::type;
+  hipLaunchKernelGGL((gemm_bf16_kernel<GG, EPI, KDKL_GEMM_BK, KDKL_GEMM_STAGES, LA, LB>), grid,
+                     dim3(GG::kThreads), 0, s, a);
   return hipGetLastError();
 }
 
