@@ -559,8 +559,28 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
   } else {
     // EPI_DW: dW[row, col] (+)= tile, staged through LDS 128 rows at a time
     // so the read-modify-write of dW uses 16-byte accesses on whole rows.
+    // The old values of each half are loaded into registers before that
+    // half's accumulators go through LDS, so the load latency overlaps the
+    // staging (and, for the second half, the first half's stores).
     static_assert(128 % G::WM == 0, "dW staging takes whole wavefront tiles per 128-row half");
     float* F = (float*)smem;
+    constexpr int ITER = (128 * BN / 4) / NT;
+    float4 o[ITER];
+    // Rows and columns past the edge read a clamped (valid) address; their
+    // sums are never stored.
+    auto load_old = [&](int half) {
+#pragma unroll
+      for (int u = 0; u < ITER; ++u) o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (p.accumulate) {
+#pragma unroll
+        for (int u = 0; u < ITER; ++u) {
+          const int j = u * NT + tid;
+          const int row = min(m0 + half * 128 + (j >> 6), p.M - 1), col = min(n0 + (j & 63) * 4, p.N - 4);
+          o[u] = *(const float4*)(p.out + (int64_t)row * p.ldo + col);
+        }
+      }
+    };
+    load_old(0);
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       __syncthreads();
@@ -576,32 +596,18 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
                 (lane & 31)] = acc[mb][nb][r];
       }
       __syncthreads();
-      const int r0 = m0 + half * 128;
-      constexpr int ITER = (128 * BN / 4) / NT;
 #pragma unroll
-      for (int it = 0; it < ITER; it += 8) {
-        float4 v[8], o[8];
-        int64_t off[8];
-        bool ok[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int j = (it + u) * NT + tid;
-          const int r = j >> 6, c4 = j & 63;
-          const int row = r0 + r, col = n0 + c4 * 4;
-          ok[u] = row < p.M && col < p.N;
-          off[u] = (int64_t)row * p.ldo + col;
-          v[u] = *(const float4*)(F + r * kDwPitch + c4 * 4);
-          o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (ok[u] && p.accumulate) o[u] = *(const float4*)(p.out + off[u]);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          if (ok[u]) {
-            float4 s = make_float4(o[u].x + v[u].x, o[u].y + v[u].y, o[u].z + v[u].z, o[u].w + v[u].w);
-            *(float4*)(p.out + off[u]) = s;
-          }
+      for (int u = 0; u < ITER; ++u) {
+        const int j = u * NT + tid;
+        const int r = j >> 6, c4 = j & 63;
+        const int row = m0 + half * 128 + r, col = n0 + c4 * 4;
+        if (row < p.M && col < p.N) {
+          const float4 v = *(const float4*)(F + r * kDwPitch + c4 * 4);
+          *(float4*)(p.out + (int64_t)row * p.ldo + col) =
+              make_float4(o[u].x + v.x, o[u].y + v.y, o[u].z + v.z, o[u].w + v.w);
         }
       }
+      if (half == 0) load_old(1);
     }
   }
 }
