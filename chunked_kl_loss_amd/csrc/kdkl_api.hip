@@ -108,9 +108,9 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   P->N = N; P->d = d; P->V = V; P->K = K; P->dtype = dtype;
   P->es = dtype == KDKL_BF16 ? 2 : 4;
   P->chunk = chunk < N ? chunk : (N > 0 ? N : 1);
-  P->fast = gemm_fast_path(dtype, d);
   P->Cp = round_up(P->chunk, kTokenTile);
   P->Vp = round_up(V, kVocabTile);
+  P->fast = gemm_fast_path(dtype, d, P->Vp, P->Cp);
   P->n_vt = P->Vp / kVocabTile;
   if (P->Cp > INT32_MAX / 2) return KDKL_ERR_OVERFLOW;
   // dH split-K: enough workgroups to cover the 256 CUs a few times over,

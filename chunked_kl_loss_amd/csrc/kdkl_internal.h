@@ -85,8 +85,10 @@ struct GemmArgs {
 enum { LAYOUT_KC = 0, LAYOUT_MC = 1 };
 
 // True when the bf16 main loop (direct-to-LDS loads, no zero fill) serves
-// the projections: bf16 storage and d a multiple of the 64-element k-step.
-bool gemm_fast_path(int dtype, int64_t d);
+// the projections: bf16 storage, d a multiple of the 64-element k-step, and
+// every operand's leading dimension (d, padded V, padded chunk) small enough
+// for 32-bit load offsets within a tile.
+bool gemm_fast_path(int dtype, int64_t d, int64_t Vp, int64_t Cp);
 
 struct MergeArgs {
   const float4* part;   // [Cp, n_vt]

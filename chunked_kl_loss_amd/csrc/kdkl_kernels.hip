@@ -769,6 +769,17 @@ __global__ __launch_bounds__(256, 1) void gemm_generic_kernel(const GemmArgs p) 
 // k-group are read while the MFMAs of the current one run.
 typedef __attribute__((address_space(3))) void lds_void;
 
+// Word 3 of a raw buffer resource on CDNA (32-bit data format, no swizzle).
+constexpr int kBufferRsrcWord3 = 0x00020000;
+
+// 16 bytes per lane from base + off (off < 2^31) straight into LDS at the
+// wavefront's 1 KiB destination `lds` (lane i lands at lds + 16 i).
+__device__ __forceinline__ void load16_lds(const void* base, uint32_t off, void* lds) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7fffffff, kBufferRsrcWord3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds, 16, off, 0, 0, 0);
+}
+
 // Workgroup barrier for the main loops, which wait for their own loads with
 // explicit vmcnt counts: a bare s_barrier (no implicit wait for every
 // outstanding load, unlike __syncthreads, which would drain the prefetched
@@ -833,26 +844,31 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
 
   auto swz = [](int row) { return CPR == 8 ? swz8(row) : swz4(row); };
 
-  // Per-lane sources of the direct loads. KC: 16-byte chunk of an output-
-  // axis row, advanced by RB bytes per k-step. MC: 16-byte unit of a k row;
-  // the row index is clamped per k-step.
+  // Direct loads go through buffer instructions (buffer_load ... lds): the
+  // compiler's wait-count pass treats the global_load form as a FLAT access
+  // to both memory and LDS and then waits for every outstanding LDS read
+  // (lgkmcnt(0)) at each use, which serializes fragment reads with MFMAs.
+  // The buffer resource holds a wavefront-uniform base per k-step; each lane
+  // adds a 32-bit byte offset (the host keeps a tile's span below 2 GiB).
+  // KC: lane offset = 16-byte chunk of an output-axis row, fixed over the
+  // k-steps (the base advances RB bytes per step). MC: 16-byte unit of a k
+  // row; the k row is clamped to the last one per step.
   struct Src {
-    const char* base;  // KC: full pointer at k-step 0; MC: row 0 pointer + column offset
-    int krow;          // MC: row within the stage
+    uint32_t off;  // KC: byte offset from the tile base; MC: column byte offset
+    int krow;      // MC: k row within the stage
   };
-  auto make_src = [&](int layout, const void* X, int64_t ld, int rows, int row0, int64_t krows,
-                      int64_t mcols, int i) {
+  auto make_src = [&](int layout, int64_t ld, int rows, int row0, int64_t mcols, int i) {
     Src s;
     const int slot = (i * G::kWaves + wid) * 64 + lane;
     if (layout == LAYOUT_KC) {
       const int row = slot / CPR, c = (slot % CPR) ^ swz(row);
       const int g = min(row0 + row, rows - 1);
-      s.base = (const char*)X + ((int64_t)g * ld + kb) * 2 + c * 16;
+      s.off = (uint32_t)(((int64_t)(g - row0) * ld) * 2 + c * 16);
       s.krow = 0;
     } else {
       const int kr = slot >> 5, u = (slot & 31) ^ (4 * (kr & 3));
       const int64_t col = min((int64_t)row0 + u * 8, mcols - 8);
-      s.base = (const char*)X + col * 2;
+      s.off = (uint32_t)(col * 2);
       s.krow = kr;
     }
     return s;
@@ -860,24 +876,31 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
   Src sa[LPO], sb[LPO];
 #pragma unroll
   for (int i = 0; i < LPO; ++i) {
-    sa[i] = make_src(LA, p.A, p.lda, p.M, m0, p.a_krows, p.a_mcols, i);
-    sb[i] = make_src(LB, p.B, p.ldb, p.N, n0, p.b_krows, p.b_mcols, i);
+    sa[i] = make_src(LA, p.lda, p.M, m0, p.a_mcols, i);
+    sb[i] = make_src(LB, p.ldb, p.N, n0, p.b_mcols, i);
   }
-  auto src_at = [&](int layout, const Src& s, int64_t ld, int64_t krows, int kt) -> const char* {
-    if (layout == LAYOUT_KC) return s.base + (int64_t)kt * RB;
-    const int64_t k = min(kb + (int64_t)kt * BK + s.krow, krows - 1);
-    return s.base + k * ld * 2;
+  // Uniform base of one operand's stage kt.
+  auto stage_base = [&](int layout, const void* X, int64_t ld, int row0, int kt) -> const char* {
+    const int64_t k0 = kb + (int64_t)kt * BK;
+    if (layout == LAYOUT_KC) return (const char*)X + ((int64_t)row0 * ld + k0) * 2;
+    return (const char*)X + k0 * ld * 2;
+  };
+  auto lane_off = [&](int layout, const Src& s, int64_t ld, int64_t krows, int kt) -> uint32_t {
+    if (layout == LAYOUT_KC) return s.off;
+    const int64_t k0 = kb + (int64_t)kt * BK;
+    const int64_t kr = min((int64_t)s.krow, krows - 1 - k0);
+    return (uint32_t)(kr * ld * 2) + s.off;
   };
   auto issue = [&](int kt) {
     char* base = smem + (kt % NSTAGE) * STG;
+    const char* ba = stage_base(LA, p.A, p.lda, m0, kt);
+    const char* bb = stage_base(LB, p.B, p.ldb, n0, kt);
 #pragma unroll
     for (int i = 0; i < LPO; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)src_at(LA, sa[i], p.lda, p.a_krows, kt),
-                                       (lds_void*)(base + (i * G::kWaves + wid) * 1024), 16, 0, 0);
+      load16_lds(ba, lane_off(LA, sa[i], p.lda, p.a_krows, kt), base + (i * G::kWaves + wid) * 1024);
 #pragma unroll
     for (int i = 0; i < LPO; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)src_at(LB, sb[i], p.ldb, p.b_krows, kt),
-                                       (lds_void*)(base + TILE + (i * G::kWaves + wid) * 1024), 16, 0, 0);
+      load16_lds(bb, lane_off(LB, sb[i], p.ldb, p.b_krows, kt), base + TILE + (i * G::kWaves + wid) * 1024);
   };
 
   f32x16_t acc[MB][NB];
@@ -954,7 +977,17 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
 using FastGrid = typename std::conditional<
     KDKL_GEMM_WAVES == 16, Grid16, typename std::conditional<KDKL_GEMM_WAVES == 8, Grid8, Grid4>::type>::type;
 
-bool gemm_fast_path(int dtype, int64_t d) { return dtype == 1 && d % KDKL_GEMM_BK == 0; }
+// Byte span of one stage's direct loads from its buffer-resource base: the
+// lane offsets are 32-bit and the resource's range is 2^31 - 1 bytes.
+static bool span_fits(int layout, int64_t ld, int64_t mcols) {
+  const int64_t span = layout == LAYOUT_KC ? (256 * ld + KDKL_GEMM_BK) * 2 : (KDKL_GEMM_BK * ld + mcols) * 2;
+  return span < ((int64_t)1 << 31);
+}
+
+bool gemm_fast_path(int dtype, int64_t d, int64_t Vp, int64_t Cp) {
+  const int64_t ld = d > Vp ? (d > Cp ? d : Cp) : (Vp > Cp ? Vp : Cp);
+  return dtype == 1 && d % KDKL_GEMM_BK == 0 && span_fits(LAYOUT_KC, ld, 0) && span_fits(LAYOUT_MC, Vp, Vp);
+}
 
 // dW multiplies a k-major dZ tile (two transposed LDS reads per fragment)
 // by a K-contiguous H^T tile: a 4 x 2 wave grid (64 x 128 per wave) gives
@@ -975,7 +1008,8 @@ static hipError_t launch_gemm_e(int dtype, const GemmArgs& a, hipStream_t s) {
   if (total <= 0) return hipSuccess;
   const int per = (total + 7) / 8;
   const dim3 grid(per * 8);
-  const bool fast = dtype == 1 && a.k_end % KDKL_GEMM_BK == 0 && a.k_split % KDKL_GEMM_BK == 0;
+  const bool fast = dtype == 1 && a.k_end % KDKL_GEMM_BK == 0 && a.k_split % KDKL_GEMM_BK == 0 &&
+                    span_fits(a.a_layout, a.lda, a.a_mcols) && span_fits(a.b_layout, a.ldb, a.b_mcols);
   if (fast) {
     // the operand layouts each projection uses
     if (a.a_layout == LAYOUT_KC && a.b_layout == LAYOUT_KC) {
