@@ -15,4 +15,7 @@ from .kl import (  # noqa: F401
     dense_kl_loss,
     sampled_rows,
     dw_rows,
+    logits_forward,
+    logits_backward,
+    logits_sampled_rows,
 )

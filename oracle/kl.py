@@ -51,6 +51,9 @@ __all__ = [
     "dense_kl_loss",
     "sampled_rows",
     "dw_rows",
+    "logits_forward",
+    "logits_backward",
+    "logits_sampled_rows",
 ]
 
 
@@ -238,3 +241,91 @@ def dw_rows(H, W, ids, logits, T: float, vrows: Iterable[int], row_lse,
         dz = coef * (np.exp(z - lse) - P)
         out[j] = dz @ Hf
     return out
+
+
+# ---------------------------------------------------------------------------
+# Forward-chunked KL: the student's logit grid is given.
+# ---------------------------------------------------------------------------
+# The pages' middle variant keeps the teacher sparse (its cached top-K per
+# position, never expanded to the dense grid) and computes the loss slice by
+# slice over positions, while the student's own logits are computed in full
+# by the output layer and kept for the backward pass [P1 "Making knowledge
+# distillation cheap enough to run at scale", section "Two system changes",
+# forward-chunked KL bullet]. The loss is the same one as above, with
+# ``z_i = Z_i`` read from the given grid instead of ``W . H_i``; the caller's
+# output layer turns dZ into its own gradients.
+#
+# Written here in the arrangement ``KL_i = e_i - gamma_i + lse_i`` with
+# ``e_i = sum_k p_ik log p_ik`` and ``gamma_i = sum_k p_ik s_i[id_ik]``
+# (equal to ``sum_k p_ik (log p_ik - log q_i[id_ik])`` because the p_ik sum
+# to one), which is independent of the arithmetic of ``forward`` above.
+# An id outside [0, V) contributes nothing to gamma_i or to the scatter of
+# the gradient (its teacher mass is dropped), the convention of the library.
+
+
+def _valid_ids(ids_rows: np.ndarray, V: int) -> np.ndarray:
+    return (ids_rows >= 0) & (ids_rows < V)
+
+
+def logits_forward(Z, ids, logits, T: float, block: int = 256) -> Dict[str, object]:
+    """Loss, per-row logsumexp of Z/T and per-row KL from the logit grid
+    ``Z [N, V]``; returns dict(loss, row_lse, row_kl) in fp64."""
+    Z = _f64(Z)
+    ids = _ids(ids)
+    N, V = Z.shape
+    row_lse = np.empty(N)
+    row_kl = np.empty(N)
+    for r0 in range(0, N, block):
+        r1 = min(N, r0 + block)
+        s = Z[r0:r1] / float(T)
+        lse = _logsumexp_rows(s)
+        p, logp = teacher_distribution(logits[r0:r1], T)
+        idr = ids[r0:r1]
+        ok = _valid_ids(idr, V)
+        s_at = np.take_along_axis(s, np.where(ok, idr, 0), axis=1)
+        e = (p * logp).sum(axis=1)
+        gamma = (p * np.where(ok, s_at, 0.0)).sum(axis=1)
+        row_kl[r0:r1] = e - gamma + lse
+        row_lse[r0:r1] = lse
+    loss = math.fsum(row_kl.tolist()) / N if N else float("nan")
+    return {"loss": loss, "row_lse": row_lse, "row_kl": row_kl}
+
+
+def logits_backward(Z, ids, logits, T: float, g: float = 1.0, block: int = 256) -> np.ndarray:
+    """Gradient ``dZ [N, V]`` of ``g * loss`` with respect to the logit grid:
+    ``dZ_i = g / (N T) * (softmax(Z_i / T) - scatter_add(ids_i, p_i))``."""
+    Z = _f64(Z)
+    ids = _ids(ids)
+    N, V = Z.shape
+    scale = float(g) / (N * float(T))
+    dZ = np.empty_like(Z)
+    for r0 in range(0, N, block):
+        r1 = min(N, r0 + block)
+        s = Z[r0:r1] / float(T)
+        q = np.exp(s - _logsumexp_rows(s)[:, None])
+        p, _ = teacher_distribution(logits[r0:r1], T)
+        idr = ids[r0:r1]
+        ok = _valid_ids(idr, V)
+        P = np.zeros_like(q)
+        rr, kk = np.nonzero(ok)
+        np.add.at(P, (rr, idr[rr, kk]), p[rr, kk])
+        dZ[r0:r1] = scale * (q - P)
+    return dZ
+
+
+def logits_sampled_rows(Z, ids, logits, T: float, rows: Iterable[int], N_total: int,
+                        g: float = 1.0) -> Dict[str, np.ndarray]:
+    """``logits_forward`` / ``logits_backward`` restricted to a few rows of a
+    large grid (one row at a time); dZ rows are those of a problem with
+    ``N_total`` positions."""
+    rows = [int(r) for r in rows]
+    out_lse, out_kl, out_dz = [], [], []
+    for r in rows:
+        Zr = _f64(Z[r:r + 1])
+        f = logits_forward(Zr, ids[r:r + 1], logits[r:r + 1], T)
+        dz = logits_backward(Zr, ids[r:r + 1], logits[r:r + 1], T, g)
+        out_lse.append(f["row_lse"][0])
+        out_kl.append(f["row_kl"][0])
+        out_dz.append(dz[0] / N_total)  # logits_backward divided by N = 1
+    return {"rows": np.asarray(rows), "row_lse": np.asarray(out_lse),
+            "row_kl": np.asarray(out_kl), "dZ_rows": np.stack(out_dz) if out_dz else np.zeros((0, 0))}

@@ -248,6 +248,168 @@ def pin_row_functions(o):
            what="sampled dW rows")
 
 
+# --- forward-chunked KL (the student's logit grid is given) ------------------
+
+def _rand_logits_problem(rng, N, V, K, scale=1.0):
+    Z = rng.standard_normal((N, V)) * scale
+    ids = np.stack([rng.choice(V, size=K, replace=False) for _ in range(N)])
+    logits = rng.standard_normal((N, K)) * 1.7
+    return Z, ids, logits
+
+
+def pin_logits_cross_entropy(o):
+    """K = 1 (one-hot teacher): torch's cross-entropy of Z / T, and its
+    autograd gradient with respect to Z."""
+    if not hasattr(o, "logits_forward"):
+        return
+    rng = np.random.default_rng(21)
+    N, V, T, g = 7, 19, 1.7, 0.6
+    Z, ids, logits = _rand_logits_problem(rng, N, V, 1)
+    Zt = torch.tensor(Z, requires_grad=True)
+    ce = F.cross_entropy(Zt / T, torch.tensor(ids[:, 0]))
+    (g * ce).backward()
+    out = o.logits_forward(Z, ids, logits, T)
+    _close(out["loss"], ce.item(), 1e-13, what="logits K=1 loss vs cross_entropy")
+    _close(out["row_lse"], sps.logsumexp(Z / T, axis=1), 1e-13, what="logits lse vs scipy")
+    _close(o.logits_backward(Z, ids, logits, T, g), Zt.grad.numpy(), 1e-12, what="logits K=1 dZ")
+
+
+def pin_logits_dense_libraries(o):
+    """General K: the dense teacher grid against softmax(Z/T) through scipy's
+    rel_entr and torch's kl_div (loss), and torch autograd through kl_div
+    (gradient)."""
+    if not hasattr(o, "logits_forward"):
+        return
+    rng = np.random.default_rng(22)
+    N, V, K, T, g = 6, 15, 5, 1.3, 1.4
+    Z, ids, logits = _rand_logits_problem(rng, N, V, K)
+    P = np.zeros((N, V))
+    for i in range(N):
+        P[i, ids[i]] = sps.softmax(logits[i] / T)
+    ref = sps.rel_entr(P, sps.softmax(Z / T, axis=1)).sum(axis=1)
+    out = o.logits_forward(Z, ids, logits, T)
+    _close(out["row_kl"], ref, 1e-12, what="logits row_kl vs rel_entr")
+    Zt = torch.tensor(Z, requires_grad=True)
+    kl = F.kl_div(torch.log_softmax(Zt / T, dim=1), torch.tensor(P), reduction="sum") / N
+    (g * kl).backward()
+    _close(out["loss"], kl.item(), 1e-12, what="logits loss vs kl_div")
+    _close(o.logits_backward(Z, ids, logits, T, g), Zt.grad.numpy(), 1e-12, what="logits dZ vs autograd")
+
+
+def pin_logits_finite_differences(o):
+    """Central differences of g * loss (h = 1e-6) for every entry of Z."""
+    if not hasattr(o, "logits_forward"):
+        return
+    rng = np.random.default_rng(23)
+    N, V, K, T, g = 3, 9, 4, 0.8, 1.2
+    Z, ids, logits = _rand_logits_problem(rng, N, V, K)
+    dZ = o.logits_backward(Z, ids, logits, T, g)
+    h = 1e-6
+    fd = np.zeros_like(Z)
+    for idx in np.ndindex(Z.shape):
+        Zp = Z.copy(); Zp[idx] += h
+        Zm = Z.copy(); Zm[idx] -= h
+        fd[idx] = g * (o.logits_forward(Zp, ids, logits, T)["loss"]
+                       - o.logits_forward(Zm, ids, logits, T)["loss"]) / (2 * h)
+    _close(dZ, fd, 1e-6, what="logits finite differences")
+
+
+def pin_logits_brute_force_dropped_ids(o):
+    """Pure-Python loops (math module only) on a tiny grid where some ids are
+    outside [0, V): those entries keep their share of the teacher's
+    normalisation but add nothing to the gathered logit or to the gradient."""
+    if not hasattr(o, "logits_forward"):
+        return
+    rng = np.random.default_rng(24)
+    N, V, K, T, g = 4, 6, 3, 1.9, 0.8
+    Z = rng.standard_normal((N, V))
+    ids = np.array([[0, 5, 2], [7, 1, -1], [3, 3, 4], [6, 2, 0]])  # 7, -1, 6 dropped; row 2 repeats 3
+    logits = rng.standard_normal((N, K))
+    kl, dz = [], np.zeros((N, V))
+    for i in range(N):
+        a = [logits[i, k] / T for k in range(K)]
+        ma = max(a)
+        za = sum(math.exp(x - ma) for x in a)
+        p = [math.exp(x - ma) / za for x in a]
+        s = [Z[i, v] / T for v in range(V)]
+        ms = max(s)
+        lse = ms + math.log(sum(math.exp(x - ms) for x in s))
+        val = sum(p[k] * math.log(p[k]) for k in range(K))
+        for k in range(K):
+            if 0 <= ids[i, k] < V:
+                val -= p[k] * s[ids[i, k]]
+        kl.append(val + lse)
+        for v in range(V):
+            mass = sum(p[k] for k in range(K) if ids[i, k] == v)
+            dz[i, v] = g / (N * T) * (math.exp(s[v] - lse) - mass)
+    out = o.logits_forward(Z, ids, logits, T)
+    _close(out["row_kl"], kl, 1e-13, what="brute-force row_kl")
+    _close(o.logits_backward(Z, ids, logits, T, g), dz, 1e-13, what="brute-force dZ")
+
+
+def pin_logits_closed_forms_and_invariants(o):
+    if not hasattr(o, "logits_forward"):
+        return
+    rng = np.random.default_rng(25)
+    N, V, K, T, g = 8, 21, 5, 1.6, 0.9
+    Z, ids, logits = _rand_logits_problem(rng, N, V, K)
+    base = o.logits_forward(Z, ids, logits, T)
+    dZ = o.logits_backward(Z, ids, logits, T, g)
+    # constant rows: the student is uniform, KL = log V - entropy(p) (scipy)
+    c = rng.standard_normal((N, 1))
+    u = o.logits_forward(np.repeat(c, V, axis=1), ids, logits, T)
+    ent = np.array([sst.entropy(sps.softmax(logits[i] / T)) for i in range(N)])
+    _close(u["row_kl"], math.log(V) - ent, 1e-12, what="uniform logits row_kl")
+    _close(u["row_lse"], c[:, 0] / T + math.log(V), 1e-13, what="uniform logits lse")
+    # adding a constant to a row changes lse by c/T and nothing else
+    sh = o.logits_forward(Z + c, ids, logits, T)
+    _close(sh["row_kl"], base["row_kl"], 1e-12, what="row-shift row_kl")
+    _close(sh["row_lse"], base["row_lse"] + c[:, 0] / T, 1e-12, what="row-shift lse")
+    _close(o.logits_backward(Z + c, ids, logits, T, g), dZ, 1e-12, what="row-shift dZ")
+    # every dZ row sums to zero; only the K teacher entries can be negative
+    _close(dZ.sum(axis=1), np.zeros(N), 0.0, atol=1e-15, what="dZ row sums")
+    mask = np.ones_like(dZ, dtype=bool)
+    np.put_along_axis(mask, ids, False, axis=1)
+    assert np.all(dZ[mask] > 0.0)
+    # KL >= 0; K-pair permutation; block size; linearity in g
+    assert np.all(base["row_kl"] >= -1e-15)
+    perm = rng.permutation(K)
+    _close(o.logits_forward(Z, ids[:, perm], logits[:, perm], T)["row_kl"], base["row_kl"], 1e-13,
+           what="logits K-permutation")
+    for blk in (1, 3):
+        _close(o.logits_forward(Z, ids, logits, T, block=blk)["loss"], base["loss"], 1e-13,
+               what=f"logits block {blk}")
+        _close(o.logits_backward(Z, ids, logits, T, g, block=blk), dZ, 1e-13, what=f"logits dZ block {blk}")
+    _close(o.logits_backward(Z, ids, logits, T, 3.0 * g), 3.0 * dZ, 1e-13, what="logits dZ linear in g")
+    # temperature identity: (Z, l, T) is (Z/T, l/T, 1), dZ_T = dZ_1(Z/T) / T
+    t1 = o.logits_forward(Z / T, ids, logits / T, 1.0)
+    _close(t1["loss"], base["loss"], 1e-13, what="logits temperature identity")
+    _close(o.logits_backward(Z / T, ids, logits / T, 1.0, g) / T, dZ, 1e-12,
+           what="logits temperature identity dZ")
+
+
+def pin_logits_matches_fused(o):
+    """With Z = H W^T the forward-chunked functions give the fused loss, and
+    the output layer's chain rule (dH = dZ W, dW = dZ^T H) gives the fused
+    gradients; the two are written in different arrangements."""
+    if not hasattr(o, "logits_forward"):
+        return
+    rng = np.random.default_rng(26)
+    N, d, V, K, T, g = 6, 5, 17, 4, 1.2, 0.7
+    H, W, ids, logits = _rand_problem(rng, N, d, V, K)
+    f = o.forward(H, W, ids, logits, T)
+    lf = o.logits_forward(H @ W.T, ids, logits, T)
+    _close(lf["row_kl"], f["row_kl"], 1e-12, what="logits vs fused row_kl")
+    _close(lf["row_lse"], f["row_lse"], 1e-13, what="logits vs fused lse")
+    dH, dW = o.backward(H, W, ids, logits, T, g)
+    dZ = o.logits_backward(H @ W.T, ids, logits, T, g)
+    _close(dZ @ W, dH, 1e-12, what="chain rule dH")
+    _close(dZ.T @ H, dW, 1e-12, what="chain rule dW")
+    sr = o.logits_sampled_rows(H @ W.T, ids, logits, T, [0, 4], N, g)
+    _close(sr["dZ_rows"], dZ[[0, 4]], 1e-13, what="logits sampled dZ rows")
+    _close(sr["row_kl"], lf["row_kl"][[0, 4]], 1e-13, what="logits sampled kl")
+
+
 ALL_PINS = [
     pin_two_token_softplus,
     pin_uniform_student,
@@ -257,4 +419,10 @@ ALL_PINS = [
     pin_finite_differences,
     pin_invariants,
     pin_row_functions,
+    pin_logits_cross_entropy,
+    pin_logits_dense_libraries,
+    pin_logits_finite_differences,
+    pin_logits_brute_force_dropped_ids,
+    pin_logits_closed_forms_and_invariants,
+    pin_logits_matches_fused,
 ]

@@ -35,6 +35,16 @@ MUTANTS = [
     ("dW_wrong_operand", "dW += dZ.T @ H[r0:r1]", "dW += dZ.T @ (H[r0:r1] * 0.5)"),
     ("sum_not_mean", "loss = math.fsum(row_kl.tolist()) / N if N",
      "loss = math.fsum(row_kl.tolist()) if N"),
+    # forward-chunked KL (logit grid given)
+    ("logits_drop_entropy", "row_kl[r0:r1] = e - gamma + lse", "row_kl[r0:r1] = -gamma + lse"),
+    ("logits_gamma_sign", "row_kl[r0:r1] = e - gamma + lse", "row_kl[r0:r1] = e + gamma + lse"),
+    ("logits_gather_no_T", "s_at = np.take_along_axis(s, np.where(ok, idr, 0), axis=1)",
+     "s_at = np.take_along_axis(Z[r0:r1], np.where(ok, idr, 0), axis=1)"),
+    ("logits_keep_dropped_ids", "gamma = (p * np.where(ok, s_at, 0.0)).sum(axis=1)",
+     "gamma = (p * s_at).sum(axis=1)"),
+    ("logits_grad_no_T", "scale = float(g) / (N * float(T))", "scale = float(g) / N"),
+    ("logits_grad_no_teacher", "dZ[r0:r1] = scale * (q - P)", "dZ[r0:r1] = scale * q"),
+    ("logits_scatter_first_id_only", "rr, kk = np.nonzero(ok)", "rr, kk = np.nonzero(ok[:, :1])"),
 ]
 
 
