@@ -6,6 +6,11 @@ already resident in HBM (every kernel of the path). Prints ONE JSON line.
 
 Default workload: the gpt-oss-20b-like head at 32K tokens
 (N=32768, d=2880, V=201088, K=100, chunk=2048, bf16, T=1).
+
+--path logits measures the forward-chunked variant instead: one step =
+kdkl_logits_forward + kdkl_logits_backward on the logit grid Z = H W^T of the
+same workload (computed on the device before timing, as the caller's output
+layer would); that path is bound by HBM bandwidth.
 """
 from __future__ import annotations
 
@@ -31,7 +36,7 @@ def log(*a):
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("kdkl_kernels.hip", "kdkl_api.hip", "kdkl_internal.h"):
+    for f in ("kdkl_kernels.hip", "kdkl_logits.hip", "kdkl_api.hip", "kdkl_internal.h"):
         with open(os.path.join(ROOT, "chunked_kl_loss_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -92,6 +97,120 @@ def cpu_baseline(w, x, rows: int):
                       f"fp64 numpy forward+backward, {dt:.1f} s"}
 
 
+def cpu_baseline_logits(w, Z_rows, x, rows: int):
+    """The CPU oracle of the forward-chunked path on the first `rows` rows of
+    the logit grid (full vocabulary)."""
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    ids, lg = x["ids"][:rows], x["logits"][:rows]
+    t0 = time.perf_counter()
+    oracle.logits_forward(Z_rows, ids, lg, w.T)
+    oracle.logits_backward(Z_rows, ids, lg, w.T)
+    dt = time.perf_counter() - t0
+    return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {rows} of {w.N} rows of the {w.name} logit grid (full V={w.V}); "
+                      f"fp64 numpy forward+backward, {dt:.1f} s"}
+
+
+def kernel_table(kstats, steps):
+    kernels = {}
+    for name, s in kstats.items():
+        kernels[name] = {
+            "launches_per_step": s["launches"] / steps,
+            "avg_ms": s["total_ms"] / max(1, s["launches"]),
+            "ms_per_step": s["total_ms"] / steps,
+            "tflops": (s["flops"] / (s["total_ms"] / 1e3) / 1e12) if s["total_ms"] > 0 else 0.0,
+            "gbs": (s["bytes"] / (s["total_ms"] / 1e3) / 1e9) if s["total_ms"] > 0 else 0.0,
+        }
+    return kernels
+
+
+def bench_logits(args, w, x):
+    import torch
+
+    import chunked_kl_loss_amd as kd
+
+    dev = torch.device("cuda:0")
+    Hd, Wd = x["H"].to(dev), x["W"].to(dev)
+    Z = torch.matmul(Hd, Wd.T.contiguous())  # the output layer's logit grid [N, V]
+    del Hd, Wd
+    torch.cuda.synchronize(dev)
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats(dev)
+    ids, lg = x["ids"].to(dev), x["logits"].to(dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    row_lse = torch.empty(w.N, dtype=torch.float32, device=dev)
+    row_kl = torch.empty(w.N, dtype=torch.float32, device=dev)
+    dZ = Z if args.inplace else torch.empty_like(Z)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        kd.logits_forward(Z, ids, lg, w.T, loss=loss, row_lse=row_lse, row_kl=row_kl, stream=stream)
+        kd.logits_backward(Z, ids, lg, w.T, row_lse, None, dZ=dZ, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    log(f"bench: warmup done, loss={loss.item():.6f}")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    kd.profile_begin()
+    torch.cuda.synchronize(dev)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    kstats = kd.profile_end()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    peak_gib = torch.cuda.max_memory_allocated(dev) / 2**30
+    log(f"bench: {ms:.3f} ms/step")
+    dtype = "bf16" if w.dtype == "bf16" else "fp32"
+    es = 2 if dtype == "bf16" else 4
+    bytes_step = 3.0 * w.N * w.V * es + 2.0 * w.N * w.K * 8.0 + 12.0 * w.N
+    dom = max(kstats, key=lambda k: kstats[k]["total_ms"])
+    ds = kstats[dom]
+    achieved = ds["bytes"] / (ds["total_ms"] / 1e3) / 1e9
+    out = {
+        "metric": "forward-chunked KL fwd+bwd tokens/s (student logit grid given); HBM GB/s; peak HBM GiB",
+        "value": round(w.N / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded; logit grid = H W^T of the workload's H and W)",
+        "config": {"workload": w.name, "path": "forward-chunked (logit grid given)", "N": w.N,
+                   "V": w.V, "K": w.K, "T": w.T, "dZ_in_place": bool(args.inplace),
+                   "parallelism": "single GPU"},
+        "hbm_gbs_step": round(bytes_step / (ms / 1e3) / 1e9, 1),
+        "bytes_per_step": bytes_step,
+        "peak_hbm_gib": round(peak_gib, 3),
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic(dom, w.name),
+                     "avg_launch_ms": round(ds["total_ms"] / ds["launches"], 4),
+                     "bytes_per_launch": ds["bytes"] / ds["launches"]},
+        "kernels": kernel_table(kstats, args.steps),
+    }
+    if not args.no_cpu_baseline:
+        rows = min(args.cpu_rows, w.N)
+        log(f"bench: timing the CPU oracle on {rows} rows")
+        out["cpu_baseline"] = cpu_baseline_logits(w, Z[:rows].cpu(), x, rows)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -102,6 +221,11 @@ def main():
     ap.add_argument("--chunk", type=int, default=None, help="override the chunk size")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=("fused", "logits"), default="fused",
+                    help="fused: the fused chunked loss (default); logits: the forward-chunked "
+                         "loss on a given logit grid")
+    ap.add_argument("--inplace", action="store_true",
+                    help="logits path: write dZ over the logit grid")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -130,6 +254,10 @@ def main():
     x = wl.generate(w)
     log(f"bench: inputs generated in {time.time() - t0:.1f} s")
     torch.cuda.set_device(dev)
+    if args.path == "logits":
+        torch.zeros(1, device=dev)
+        bench_logits(args, w, x)
+        return
     torch.zeros(1, device=dev)  # initialise the device before reading memory stats
     torch.cuda.reset_peak_memory_stats(dev)
     H, W, ids, lg = (x[k].to(dev) for k in ("H", "W", "ids", "logits"))
@@ -173,15 +301,7 @@ def main():
     tok_s = w.N / (ms / 1e3)
     mfma_pct = 100.0 * flops_step / (ms / 1e3) / (peak * 1e12)
 
-    kernels = {}
-    for name, s in kstats.items():
-        kernels[name] = {
-            "launches_per_step": s["launches"] / args.steps,
-            "avg_ms": s["total_ms"] / max(1, s["launches"]),
-            "ms_per_step": s["total_ms"] / args.steps,
-            "tflops": (s["flops"] / (s["total_ms"] / 1e3) / 1e12) if s["total_ms"] > 0 else 0.0,
-            "gbs": (s["bytes"] / (s["total_ms"] / 1e3) / 1e9) if s["total_ms"] > 0 else 0.0,
-        }
+    kernels = kernel_table(kstats, args.steps)
     dom = max(kstats, key=lambda k: kstats[k]["total_ms"])
     ds = kstats[dom]
     achieved = ds["flops"] / (ds["total_ms"] / 1e3) / 1e12

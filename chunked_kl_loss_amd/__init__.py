@@ -25,6 +25,10 @@ __all__ = [
     "kdkl_backward",
     "FusedKLLoss",
     "fused_kl_loss",
+    "logits_forward",
+    "logits_backward",
+    "ForwardChunkedKLLoss",
+    "forward_chunked_kl_loss",
     "profile_begin",
     "profile_end",
     "KdklError",
@@ -144,6 +148,80 @@ class FusedKLLoss(torch.autograd.Function):
 def fused_kl_loss(H, W, ids, logits, T: float = 1.0, chunk: int = 2048):
     """Mean over positions of KL(teacher top-K || student), differentiable in H and W."""
     return FusedKLLoss.apply(H, W, ids, logits, T, chunk)
+
+
+def _check_logits_shapes(Z, ids, logits):
+    if Z.dim() != 2 or not Z.is_contiguous():
+        raise ValueError("Z must be a contiguous [N, V] tensor")
+    N, V = Z.shape
+    if ids.shape != logits.shape or ids.dim() != 2 or ids.shape[0] != N:
+        raise ValueError("shape mismatch among Z [N,V], ids/logits [N,K]")
+    if Z.dtype not in (torch.float32, torch.bfloat16) or ids.dtype != torch.int32 \
+            or logits.dtype != torch.float32:
+        raise TypeError("Z float32 or bfloat16; ids int32; logits float32")
+    return N, V, ids.shape[1]
+
+
+def logits_forward(Z, ids, logits, T: float, *, loss=None, row_lse=None, row_kl=None,
+                   stream=None):
+    """Forward-chunked KL from the student's logit grid ``Z [N, V]``
+    (``kdkl_logits_forward``); returns (loss [1] fp32, row_lse [N], row_kl [N])."""
+    _need_gpu(Z, ids, logits)
+    N, V, K = _check_logits_shapes(Z, ids, logits)
+    dev = Z.device
+    if loss is None:
+        loss = torch.empty(1, dtype=torch.float32, device=dev)
+    if row_lse is None:
+        row_lse = torch.empty(N, dtype=torch.float32, device=dev)
+    if row_kl is None:
+        row_kl = torch.empty(N, dtype=torch.float32, device=dev)
+    check(_load().kdkl_logits_forward(_ptr(Z), _ptr(ids), _ptr(logits), N, V, K, float(T),
+                                      _dtype_code(Z), _ptr(loss), _ptr(row_lse), _ptr(row_kl),
+                                      _stream(dev, stream)),
+          "kdkl_logits_forward")
+    return loss, row_lse, row_kl
+
+
+def logits_backward(Z, ids, logits, T: float, row_lse, grad_loss=None, *, dZ=None,
+                    stream=None):
+    """Gradient of the forward-chunked KL with respect to ``Z``
+    (``kdkl_logits_backward``); ``dZ=Z`` overwrites the logits in place."""
+    _need_gpu(Z, ids, logits, row_lse, grad_loss)
+    N, V, K = _check_logits_shapes(Z, ids, logits)
+    if dZ is None:
+        dZ = torch.empty_like(Z)
+    if dZ.shape != Z.shape or dZ.dtype != Z.dtype or not dZ.is_contiguous():
+        raise ValueError("dZ must be a contiguous tensor of Z's shape and dtype")
+    if grad_loss is not None and grad_loss.dtype != torch.float32:
+        raise TypeError("grad_loss must be float32")
+    check(_load().kdkl_logits_backward(_ptr(Z), _ptr(ids), _ptr(logits), N, V, K, float(T),
+                                       _dtype_code(Z), _ptr(row_lse), _ptr(grad_loss),
+                                       _ptr(dZ), _stream(Z.device, stream)),
+          "kdkl_logits_backward")
+    return dZ
+
+
+class ForwardChunkedKLLoss(torch.autograd.Function):
+    """Autograd wrapper of the forward-chunked KL: the logit grid is an input
+    (saved for the backward pass together with row_lse)."""
+
+    @staticmethod
+    def forward(ctx, Z, ids, logits, T: float):
+        loss, row_lse, _ = logits_forward(Z, ids, logits, T)
+        ctx.save_for_backward(Z, ids, logits, row_lse)
+        ctx.T = T
+        return loss[0]
+
+    @staticmethod
+    def backward(ctx, g):
+        Z, ids, logits, row_lse = ctx.saved_tensors
+        g = g.reshape(1).to(torch.float32).contiguous()
+        return logits_backward(Z, ids, logits, ctx.T, row_lse, g), None, None, None
+
+
+def forward_chunked_kl_loss(Z, ids, logits, T: float = 1.0):
+    """Mean over positions of KL(teacher top-K || softmax(Z / T)), differentiable in Z."""
+    return ForwardChunkedKLLoss.apply(Z, ids, logits, T)
 
 
 def profile_begin():

@@ -19,7 +19,8 @@ namespace kdkl {
 const char* kernel_name(int id) {
   static const char* names[K_COUNT] = {
       "teacher_prep", "fwd_gemm_lse", "split_merge", "loss_reduce", "transpose_w",
-      "transpose_h",  "dz_gemm",      "dh_gemm",     "dh_reduce",   "dw_gemm"};
+      "transpose_h",  "dz_gemm",      "dh_gemm",     "dh_reduce",   "dw_gemm",
+      "logits_fwd",   "logits_bwd"};
   return (id >= 0 && id < K_COUNT) ? names[id] : "?";
 }
 
@@ -352,6 +353,58 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
     e = timed(K_DW_GEMM, fl, ((double)V * rows + (double)rows * d) * P.es + 8.0 * V * d, s,
               [&] { return launch_gemm(dtype, EPI_DW, w, s); });
   }
+  return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
+}
+
+// ---------------------- forward-chunked KL (logit grid) --------------------
+
+static kdkl_status check_logits(const void* Z, const int32_t* ids, const float* lg, int64_t N, int64_t V,
+                                int32_t K, float T, int dtype) {
+  if (dtype != KDKL_F32 && dtype != KDKL_BF16) return KDKL_ERR_DTYPE;
+  if (N < 0 || V <= 0 || K <= 0 || K > 1024 || K > V) return KDKL_ERR_SHAPE;
+  if (V > ((int64_t)1 << 40) || N > ((int64_t)1 << 40) || N * V > ((int64_t)1 << 60)) return KDKL_ERR_OVERFLOW;
+  if (N > 0 && (!Z || !ids || !lg)) return KDKL_ERR_NULL;
+  if (!(T > 0.f) || !isfinite(T)) return KDKL_ERR_VALUE;
+  if (!aligned16(Z)) return KDKL_ERR_ALIGN;
+  return KDKL_OK;
+}
+
+kdkl_status kdkl_logits_forward(const void* Z, const int32_t* ids, const float* lg, int64_t N, int64_t V,
+                                int32_t K, float T, int dtype, float* loss, float* row_lse, float* row_kl,
+                                void* stream) {
+  kdkl_status st = check_logits(Z, ids, lg, N, V, K, T, dtype);
+  if (st != KDKL_OK) return st;
+  if (!loss || (N > 0 && (!row_lse || !row_kl))) return KDKL_ERR_NULL;
+  hipStream_t s = (hipStream_t)stream;
+  LogitsArgs a;
+  memset(&a, 0, sizeof(a));
+  a.Z = Z; a.ids = ids; a.logits = lg; a.N = N; a.V = V; a.K = K; a.inv_T = 1.0f / T;
+  a.row_lse = row_lse; a.row_kl = row_kl;
+  const double es = dtype == KDKL_BF16 ? 2.0 : 4.0;
+  hipError_t e = timed(K_LOGITS_FWD, 0.0, (double)N * (V * es + K * 8.0 + 8.0), s,
+                       [&] { return launch_logits_fwd(dtype, a, s); });
+  if (e == hipSuccess)
+    e = timed(K_LOSS, 0.0, (double)N * 4.0, s, [&] { return launch_loss(row_kl, N, loss, s); });
+  return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
+}
+
+kdkl_status kdkl_logits_backward(const void* Z, const int32_t* ids, const float* lg, int64_t N, int64_t V,
+                                 int32_t K, float T, int dtype, const float* row_lse, const float* grad_loss,
+                                 void* dZ, void* stream) {
+  kdkl_status st = check_logits(Z, ids, lg, N, V, K, T, dtype);
+  if (st != KDKL_OK) return st;
+  if (N > 0 && (!row_lse || !dZ)) return KDKL_ERR_NULL;
+  if (!aligned16(dZ)) return KDKL_ERR_ALIGN;
+  if (N == 0) return KDKL_OK;
+  hipStream_t s = (hipStream_t)stream;
+  LogitsArgs a;
+  memset(&a, 0, sizeof(a));
+  a.Z = Z; a.dZ = dZ; a.ids = ids; a.logits = lg; a.N = N; a.V = V; a.K = K; a.inv_T = 1.0f / T;
+  a.row_lse = const_cast<float*>(row_lse); a.grad = grad_loss;
+  a.coef_base = (float)(1.0 / ((double)N * (double)T));
+  const double es = dtype == KDKL_BF16 ? 2.0 : 4.0;
+  hipError_t e = timed(K_LOGITS_BWD, 0.0, (double)N * (2.0 * V * es + K * 8.0 + 4.0), s,
+                       [&] { return launch_logits_bwd(dtype, a, s); });
   return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
 }
 

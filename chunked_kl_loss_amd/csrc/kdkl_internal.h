@@ -25,6 +25,8 @@ enum KernelId {
   K_DH_GEMM,
   K_DH_REDUCE,
   K_DW_GEMM,
+  K_LOGITS_FWD,
+  K_LOGITS_BWD,
   K_COUNT
 };
 
@@ -114,5 +116,22 @@ enum Epilogue { EPI_FWD = 0, EPI_DZ = 1, EPI_DH = 2, EPI_DW = 3 };
 // dtype: 0 = fp32, 1 = bf16
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s);
 int gemm_k_step(int dtype);  // elements per k-step of the GEMM main loop
+
+// Forward-chunked KL over a given logit grid (one wavefront per row).
+struct LogitsArgs {
+  const void* Z;        // [N, V] storage dtype, row-major, 16-byte aligned base
+  void* dZ;             // [N, V] backward output (may be Z itself)
+  const int32_t* ids;   // [N, K]
+  const float* logits;  // [N, K]
+  int64_t N, V;
+  int K;                // 1..1024
+  float inv_T;
+  float* row_lse;       // [N] forward output, backward input
+  float* row_kl;        // [N] forward output
+  const float* grad;    // backward: upstream scalar g (NULL means 1)
+  float coef_base;      // backward: 1 / (N T)
+};
+hipError_t launch_logits_fwd(int dtype, const LogitsArgs& a, hipStream_t s);
+hipError_t launch_logits_bwd(int dtype, const LogitsArgs& a, hipStream_t s);
 
 }  // namespace kdkl

@@ -1,0 +1,383 @@
+// Device kernels of the forward-chunked KL loss: the student's logit grid
+// Z [N, V] is given (the output layer computed it in full and keeps it for
+// the backward pass) and the teacher stays sparse, its cached top-K per
+// position [P1 "Making knowledge distillation cheap enough to run at scale",
+// section "Two system changes", forward-chunked KL bullet].
+//
+// Both passes stream Z once and are bound by HBM bandwidth. One wavefront
+// owns one row (position): rows are independent, so the pages' slicing over
+// positions is the grid itself and no chunk buffer exists.
+//   forward : lse_i = log sum_v exp(z_iv / T) (online, base 2), and
+//             KL_i = e_i - gamma_i + lse_i with e_i = sum_k p_ik log p_ik and
+//             gamma_i = sum_k p_ik z_i[id_ik] / T.
+//   backward: dZ_iv = g/(N T) (exp(z_iv / T - lse_i) - sum_k p_ik [v = id_ik]).
+// An id outside [0, V) adds nothing to gamma or to the gradient (its teacher
+// mass is dropped) and is never dereferenced.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kdkl_internal.h"
+
+namespace kdkl {
+
+namespace {
+
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kRowsPerBlock = 4;  // one wavefront per row
+
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+template <typename T>
+__device__ __forceinline__ T wave_xor(T v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += wave_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, wave_xor(v, o));
+  return v;
+}
+
+// Element access for the two storage types. A 16-byte vector holds
+// kVec elements.
+template <typename TE>
+struct Elem;
+
+template <>
+struct Elem<uint16_t> {  // bf16 bits
+  static constexpr int kVec = 8;
+  __device__ static float load(const uint16_t* p) { return __builtin_bit_cast(float, (uint32_t)*p << 16); }
+  __device__ static void store(uint16_t* p, float v) {
+    *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+  }
+  __device__ static void unpack(const uint4& u, float (&x)[kVec]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __builtin_bit_cast(float, w[j] << 16);
+      x[2 * j + 1] = __builtin_bit_cast(float, w[j] & 0xffff0000u);
+    }
+  }
+  __device__ static uint4 pack(const float (&y)[kVec]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t lo = __builtin_bit_cast(uint16_t, static_cast<__bf16>(y[2 * j]));
+      const uint32_t hi = __builtin_bit_cast(uint16_t, static_cast<__bf16>(y[2 * j + 1]));
+      w[j] = lo | (hi << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+
+template <>
+struct Elem<float> {
+  static constexpr int kVec = 4;
+  __device__ static float load(const float* p) { return *p; }
+  __device__ static void store(float* p, float v) { *p = v; }
+  __device__ static void unpack(const uint4& u, float (&x)[kVec]) {
+    x[0] = __builtin_bit_cast(float, u.x);
+    x[1] = __builtin_bit_cast(float, u.y);
+    x[2] = __builtin_bit_cast(float, u.z);
+    x[3] = __builtin_bit_cast(float, u.w);
+  }
+  __device__ static uint4 pack(const float (&y)[kVec]) {
+    return make_uint4(__builtin_bit_cast(uint32_t, y[0]), __builtin_bit_cast(uint32_t, y[1]),
+                      __builtin_bit_cast(uint32_t, y[2]), __builtin_bit_cast(uint32_t, y[3]));
+  }
+};
+
+// A row of V elements starting at element offset `start` of a 16-byte
+// aligned buffer: `head` scalar elements up to the first 16-byte boundary,
+// `nvec` whole vectors, then `tail` scalar elements.
+struct RowSplit {
+  int head, tail;
+  int64_t nvec;
+};
+
+template <int VEC>
+__device__ __forceinline__ RowSplit split_row(int64_t start, int64_t V) {
+  RowSplit r;
+  const int64_t mis = start % VEC;
+  int64_t head = mis ? VEC - mis : 0;
+  if (head > V) head = V;
+  r.head = (int)head;
+  r.nvec = (V - head) / VEC;
+  r.tail = (int)(V - head - r.nvec * VEC);
+  return r;
+}
+
+// Teacher top-K of one row, spread over the wavefront (entry k on lane
+// k % 64, slot k / 64; KPL slots per lane hold K <= 64 KPL entries):
+// p_k = softmax_k(l_k / T), e = sum_k p_k log p_k, and the student logit z at
+// each in-range id (read before anything is written, so dZ may share storage
+// with Z).
+template <typename TE, int KPL>
+struct TeacherRow {
+  float p[KPL];
+  float z[KPL];
+  int id[KPL];
+  bool ok[KPL];
+  float e;  // wavefront total
+
+  __device__ void load(const LogitsArgs& a, int64_t row, int lane) {
+    const int K = a.K;
+    const int64_t g = row * (int64_t)K;
+    const TE* zr = (const TE*)a.Z + row * a.V;
+    float av[KPL];
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      const int k = lane + 64 * j;
+      av[j] = kNegInf;
+      id[j] = -1;
+      if (k < K) {
+        av[j] = a.logits[g + k] * a.inv_T;
+        id[j] = a.ids[g + k];
+        mx = fmaxf(mx, av[j]);
+      }
+      ok[j] = id[j] >= 0 && (int64_t)id[j] < a.V;
+      z[j] = ok[j] ? Elem<TE>::load(zr + id[j]) : 0.f;
+    }
+    mx = wave_max(mx);
+    float se = 0.f;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j)
+      if (lane + 64 * j < K) se += exp2_hw((av[j] - mx) * kLog2e);
+    const float lt = mx + log2_hw(wave_sum(se)) * kLn2;  // natural-log normaliser
+    float ent = 0.f;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      p[j] = 0.f;
+      if (lane + 64 * j < K) {
+        const float lp = av[j] - lt;
+        p[j] = exp2_hw(lp * kLog2e);
+        ent += p[j] * lp;
+      }
+    }
+    e = wave_sum(ent);
+  }
+};
+
+// Online (max, sum 2^(x - max)) over base-2 scaled logits x.
+struct OnlineLse {
+  float m = kNegInf, s = 0.f;
+  __device__ void add(float x) {
+    if (x == kNegInf) return;
+    if (x > m) {
+      s = s * exp2_hw(m - x) + 1.f;
+      m = x;
+    } else {
+      s += exp2_hw(x - m);
+    }
+  }
+  template <int N>
+  __device__ void add_vec(const float (&x)[N]) {
+    float mv = x[0];
+#pragma unroll
+    for (int j = 1; j < N; ++j) mv = fmaxf(mv, x[j]);
+    if (mv == kNegInf) return;
+    if (mv > m) {
+      s *= exp2_hw(m - mv);
+      m = mv;
+    }
+#pragma unroll
+    for (int j = 0; j < N; ++j) s += exp2_hw(x[j] - m);
+  }
+  __device__ void wave_merge() {
+    for (int o = 32; o > 0; o >>= 1) {
+      const float om = wave_xor(m, o), os = wave_xor(s, o);
+      const float nm = fmaxf(m, om);
+      if (nm > kNegInf) {
+        s = (m > kNegInf ? s * exp2_hw(m - nm) : 0.f) + (om > kNegInf ? os * exp2_hw(om - nm) : 0.f);
+        m = nm;
+      }
+    }
+  }
+};
+
+constexpr int kUnroll = 4;  // 16-byte loads in flight per lane
+
+// Streaming access to the logit grid: each byte is read once (and dZ written
+// once), so both go out with the nontemporal hint. Besides keeping the caches
+// for the reused data, it leaves no dirty dZ lines in the caches to be
+// written back while the next pass streams Z.
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const u32x4_t v = __builtin_nontemporal_load((const u32x4_t*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
+  __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, (u32x4_t*)p);
+}
+
+template <typename TE, int KPL>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void logits_fwd_kernel(LogitsArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= a.N) return;
+  constexpr int VEC = Elem<TE>::kVec;
+  TeacherRow<TE, KPL> t;
+  t.load(a, row, lane);
+  float gam = 0.f;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) gam += t.ok[j] ? t.p[j] * t.z[j] : 0.f;
+  gam = wave_sum(gam) * a.inv_T;
+
+  const float c = kLog2e * a.inv_T;
+  const int64_t start = row * a.V;
+  const TE* zr = (const TE*)a.Z + start;
+  const RowSplit rs = split_row<VEC>(start, a.V);
+  OnlineLse acc;
+  if (lane < rs.head) acc.add(Elem<TE>::load(zr + lane) * c);
+  const uint4* vp = (const uint4*)(zr + rs.head);
+  int64_t i = lane;
+  for (; i + 64 * (kUnroll - 1) < rs.nvec; i += 64 * kUnroll) {
+    uint4 u[kUnroll];
+#pragma unroll
+    for (int q = 0; q < kUnroll; ++q) u[q] = load_stream(vp + i + 64 * q);
+#pragma unroll
+    for (int q = 0; q < kUnroll; ++q) {
+      float x[VEC];
+      Elem<TE>::unpack(u[q], x);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) x[j] *= c;
+      acc.add_vec(x);
+    }
+  }
+  for (; i < rs.nvec; i += 64) {
+    float x[VEC];
+    Elem<TE>::unpack(load_stream(vp + i), x);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) x[j] *= c;
+    acc.add_vec(x);
+  }
+  if (lane < rs.tail) acc.add(Elem<TE>::load(zr + rs.head + rs.nvec * VEC + lane) * c);
+  acc.wave_merge();
+  if (lane == 0) {
+    const float lse = (acc.m + log2_hw(acc.s)) * kLn2;
+    a.row_lse[row] = lse;
+    a.row_kl[row] = t.e - gam + lse;
+  }
+}
+
+template <typename TE, int KPL>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void logits_bwd_kernel(LogitsArgs a) {
+  __shared__ int32_t s_id[kRowsPerBlock][64 * KPL];
+  __shared__ float s_p[kRowsPerBlock][64 * KPL];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + w;
+  if (row >= a.N) return;
+  constexpr int VEC = Elem<TE>::kVec;
+  TeacherRow<TE, KPL> t;
+  t.load(a, row, lane);
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int k = lane + 64 * j;
+    if (k < a.K) {
+      s_id[w][k] = t.id[j];
+      s_p[w][k] = t.p[j];
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  // The gathered logits must have been read before any store of this row
+  // (dZ may be Z).
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  const float coef = (a.grad ? a.grad[0] : 1.f) * a.coef_base;
+  const float c = kLog2e * a.inv_T;
+  const float lse2 = a.row_lse[row] * kLog2e;
+  const int64_t start = row * a.V;
+  const TE* zr = (const TE*)a.Z + start;
+  TE* dr = (TE*)a.dZ + start;
+  const RowSplit rs = split_row<VEC>(start, a.V);
+  if (lane < rs.head) Elem<TE>::store(dr + lane, coef * exp2_hw(Elem<TE>::load(zr + lane) * c - lse2));
+  const uint4* vp = (const uint4*)(zr + rs.head);
+  uint4* op = (uint4*)(dr + rs.head);
+  int64_t i = lane;
+  for (; i + 64 * (kUnroll - 1) < rs.nvec; i += 64 * kUnroll) {
+    uint4 u[kUnroll];
+#pragma unroll
+    for (int q = 0; q < kUnroll; ++q) u[q] = load_stream(vp + i + 64 * q);
+#pragma unroll
+    for (int q = 0; q < kUnroll; ++q) {
+      float x[VEC];
+      Elem<TE>::unpack(u[q], x);
+#pragma unroll
+      for (int j = 0; j < VEC; ++j) x[j] = coef * exp2_hw(x[j] * c - lse2);
+      store_stream(op + i + 64 * q, Elem<TE>::pack(x));
+    }
+  }
+  for (; i < rs.nvec; i += 64) {
+    float x[VEC];
+    Elem<TE>::unpack(load_stream(vp + i), x);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) x[j] = coef * exp2_hw(x[j] * c - lse2);
+    store_stream(op + i, Elem<TE>::pack(x));
+  }
+  if (lane < rs.tail) {
+    const int64_t v = rs.head + rs.nvec * VEC + lane;
+    Elem<TE>::store(dr + v, coef * exp2_hw(Elem<TE>::load(zr + v) * c - lse2));
+  }
+  // Teacher entries: overwrite with the full value once the dense stores of
+  // this wavefront have been performed (same addresses, written later).
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    if (lane + 64 * j < a.K && t.ok[j]) {
+      float mass = 0.f;  // duplicates of an id add their mass
+      for (int q = 0; q < a.K; ++q) mass += s_id[w][q] == t.id[j] ? s_p[w][q] : 0.f;
+      Elem<TE>::store(dr + t.id[j], coef * (exp2_hw(t.z[j] * c - lse2) - mass));
+    }
+  }
+}
+
+}  // namespace
+
+// Slots per lane for the teacher entries: the smallest of 2, 4, 16 with
+// K <= 64 * slots.
+template <template <typename, int> class Launch, typename TE>
+static hipError_t launch_k(const LogitsArgs& a, hipStream_t s) {
+  if (a.K <= 128) return Launch<TE, 2>::go(a, s);
+  if (a.K <= 256) return Launch<TE, 4>::go(a, s);
+  return Launch<TE, 16>::go(a, s);
+}
+
+template <typename TE, int KPL>
+struct FwdLaunch {
+  static hipError_t go(const LogitsArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)((a.N + kRowsPerBlock - 1) / kRowsPerBlock));
+    hipLaunchKernelGGL((logits_fwd_kernel<TE, KPL>), grid, dim3(64 * kRowsPerBlock), 0, s, a);
+    return hipGetLastError();
+  }
+};
+
+template <typename TE, int KPL>
+struct BwdLaunch {
+  static hipError_t go(const LogitsArgs& a, hipStream_t s) {
+    const dim3 grid((unsigned)((a.N + kRowsPerBlock - 1) / kRowsPerBlock));
+    hipLaunchKernelGGL((logits_bwd_kernel<TE, KPL>), grid, dim3(64 * kRowsPerBlock), 0, s, a);
+    return hipGetLastError();
+  }
+};
+
+hipError_t launch_logits_fwd(int dtype, const LogitsArgs& a, hipStream_t s) {
+  if (a.N <= 0) return hipSuccess;
+  if (a.K < 1 || a.K > 1024) return hipErrorInvalidValue;
+  return dtype == 1 ? launch_k<FwdLaunch, uint16_t>(a, s) : launch_k<FwdLaunch, float>(a, s);
+}
+
+hipError_t launch_logits_bwd(int dtype, const LogitsArgs& a, hipStream_t s) {
+  if (a.N <= 0) return hipSuccess;
+  if (a.K < 1 || a.K > 1024) return hipErrorInvalidValue;
+  return dtype == 1 ? launch_k<BwdLaunch, uint16_t>(a, s) : launch_k<BwdLaunch, float>(a, s);
+}
+
+}  // namespace kdkl

@@ -116,9 +116,41 @@ kdkl_status kdkl_backward(const void* H, const void* W,
                           void* dH, float* dW, int accumulate_dW,
                           void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- forward-chunked KL: the student's logit grid is given ----------------
+ * The pages' middle variant: the teacher stays sparse (its cached top-K per
+ * position), the loss is computed slice by slice over positions, and the
+ * student's own logits Z [N, V] are computed in full by the output layer and
+ * kept for the backward pass [P1 "Making knowledge distillation cheap enough
+ * to run at scale", section "Two system changes", forward-chunked KL bullet].
+ * Same loss, readings and id conventions as kdkl_forward with z_i = Z_i; the
+ * caller's output layer turns dZ into its own gradients. Both calls stream Z
+ * once (bound by HBM bandwidth); rows are processed independently, so no
+ * chunk size and no workspace are needed.
+ *
+ * kdkl_logits_forward:
+ *   Z [N, V] dtype (row-major, 16-byte aligned base; any V >= 1),
+ *   topk_ids [N, K] int32, topk_logits [N, K] fp32, 1 <= K <= min(V, 1024),
+ *   T > 0. Outputs (device): loss [1] fp32 (mean KL, NaN when N == 0),
+ *   row_lse [N] = logsumexp_v(Z_iv / T) (keep it for the backward),
+ *   row_kl [N] per-position KL (required: the loss is reduced from it). */
+kdkl_status kdkl_logits_forward(const void* Z, const int32_t* topk_ids,
+                                const float* topk_logits, int64_t N, int64_t V,
+                                int32_t K, float T, int dtype, float* loss,
+                                float* row_lse, float* row_kl, void* stream);
+/* kdkl_logits_backward: writes dZ [N, V] in Z's dtype,
+ *   dZ_i = g / (N T) * (softmax(Z_i / T) - scatter(ids_i, p_i)),
+ * with g read from the device scalar grad_loss (NULL means 1) and row_lse
+ * the forward's output for the same inputs. dZ may be Z itself (the gradient
+ * then overwrites the logits in place); otherwise the two must not overlap.
+ * dZ must be 16-byte aligned. */
+kdkl_status kdkl_logits_backward(const void* Z, const int32_t* topk_ids,
+                                 const float* topk_logits, int64_t N, int64_t V,
+                                 int32_t K, float T, int dtype,
+                                 const float* row_lse, const float* grad_loss,
+                                 void* dZ, void* stream);
 /* ---- measurement aid: per-kernel timing with HIP events ------------------
  * Between kdkl_profile_begin() and kdkl_profile_end(), every kernel launched
- * by kdkl_forward / kdkl_backward is bracketed by two HIP events recorded on
+ * by the compute calls is bracketed by two HIP events recorded on
  * the launch stream. kdkl_profile_end() waits for those events and returns,
  * per kernel name, the launch count, the summed event time and the summed
  * algorithmic work (flop and HBM bytes by the formulas the library states for

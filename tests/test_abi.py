@@ -169,3 +169,63 @@ def test_binding_refuses_cpu_tensors():
     lg = torch.zeros(4, 2)
     with pytest.raises(ValueError):
         kd.kdkl_forward(H, W, ids, lg, 1.0, 2)
+
+
+# --- forward-chunked KL entry points ------------------------------------------
+
+def lfwd(lib, **kw):
+    a = dict(Z=FAKE, ids=FAKE, lg=FAKE, N=64, V=1000, K=8, T=1.0, dt=L.KDKL_BF16, loss=FAKE,
+             lse=FAKE, kl=FAKE, stream=None)
+    a.update(kw)
+    return lib.kdkl_logits_forward(a["Z"], a["ids"], a["lg"], a["N"], a["V"], a["K"], a["T"],
+                                   a["dt"], a["loss"], a["lse"], a["kl"], a["stream"])
+
+
+def lbwd(lib, **kw):
+    a = dict(Z=FAKE, ids=FAKE, lg=FAKE, N=64, V=1000, K=8, T=1.0, dt=L.KDKL_BF16, lse=FAKE, g=None,
+             dZ=FAKE, stream=None)
+    a.update(kw)
+    return lib.kdkl_logits_backward(a["Z"], a["ids"], a["lg"], a["N"], a["V"], a["K"], a["T"],
+                                    a["dt"], a["lse"], a["g"], a["dZ"], a["stream"])
+
+
+@pytest.mark.parametrize("call", [lfwd, lbwd], ids=["logits_forward", "logits_backward"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(Z=None), NULL),
+    (dict(ids=None), NULL),
+    (dict(lg=None), NULL),
+    (dict(lse=None), NULL),
+    (dict(T=0.0), VALUE),
+    (dict(T=float("nan")), VALUE),
+    (dict(K=0), SHAPE),
+    (dict(K=1025), SHAPE),
+    (dict(K=1001), SHAPE),  # K > V
+    (dict(V=0), SHAPE),
+    (dict(N=-1), SHAPE),
+    (dict(N=1 << 41), OVERFLOW),
+    (dict(dt=3), DTYPE),
+    (dict(Z=FAKE + 2), ALIGN),
+])
+def test_logits_calls_reject_bad_arguments(lib, call, kw, status):
+    assert call(lib, **kw) == status
+
+
+def test_logits_output_pointers_checked(lib):
+    assert lfwd(lib, loss=None) == NULL
+    assert lfwd(lib, kl=None) == NULL
+    assert lbwd(lib, dZ=None) == NULL
+    assert lbwd(lib, dZ=FAKE + 8) == ALIGN
+    # nothing to do for N == 0 on the backward: returns before any HIP call
+    assert lbwd(lib, N=0, Z=None, ids=None, lg=None, lse=None, dZ=None) == OK
+
+
+def test_logits_binding_refuses_cpu_tensors():
+    import torch
+
+    import chunked_kl_loss_amd as kd
+
+    Z = torch.zeros(4, 16, dtype=torch.bfloat16)
+    ids = torch.zeros(4, 2, dtype=torch.int32)
+    lg = torch.zeros(4, 2)
+    with pytest.raises(ValueError):
+        kd.logits_forward(Z, ids, lg, 1.0)
