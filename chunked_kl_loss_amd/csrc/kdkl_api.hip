@@ -70,6 +70,9 @@ hipError_t timed(int kid, double flops, double bytes, hipStream_t s, F&& launch)
 // ------------------------------ planning ----------------------------------
 static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
+// Compute units of the MI355X; the dH split count is sized for them.
+constexpr int64_t kComputeUnits = 256;
+
 struct Plan {
   int64_t N, d, V, K, chunk;
   int dtype;
@@ -80,6 +83,7 @@ struct Plan {
   int dh_splits;
   int64_t dh_ksplit;
   bool fast;       // bf16 main loop: reads W, H and dZ in place (no transposes)
+  int dtile;       // N-tile width of the dH and dW products (hidden-size axis)
   // offsets into the forward workspace
   size_t f_sids, f_sp, f_erow, f_tstart, f_part, f_rowkl, f_bytes;
   // offsets into the backward workspace
@@ -112,17 +116,25 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   P->Cp = round_up(P->chunk, kTokenTile);
   P->Vp = round_up(V, kVocabTile);
   P->fast = gemm_fast_path(dtype, d, P->Vp, P->Cp);
+  P->dtile = gemm_d_tile(P->fast, d);
   P->n_vt = P->Vp / kVocabTile;
   if (P->Cp > INT32_MAX / 2) return KDKL_ERR_OVERFLOW;
-  // dH split-K: enough workgroups to cover the 256 CUs a few times over,
-  // each split at least 8 k-steps long.
-  const int64_t tiles = ((P->Cp + 255) / 256) * ((d + 255) / 256);
-  int64_t S = (768 + tiles - 1) / tiles;
+  // dH split-K: the number of splits S that makes the launch cheapest when
+  // every workgroup does 1/S of a tile's work and the 256 compute units of
+  // the device take them in rounds: minimise ceil(tiles * S / 256) / S (ties
+  // to the smaller S, fewer partials), with each split at least 8 k-steps.
+  const int64_t tiles = ((P->Cp + 255) / 256) * ((d + P->dtile - 1) / P->dtile);
   const int64_t kstep = dtype == KDKL_BF16 ? 64 : 32;
-  const int64_t smax = P->Vp / (8 * kstep);
-  if (S > smax) S = smax;
-  if (S > 16) S = 16;
-  if (S < 1) S = 1;
+  int64_t smax = P->Vp / (8 * kstep);
+  if (smax > 16) smax = 16;
+  if (smax < 1) smax = 1;
+  int64_t S = 1;
+  for (int64_t c = 2; c <= smax; ++c) {
+    // rounds(c) / c < rounds(S) / S, compared without division
+    const int64_t rc = (tiles * c + kComputeUnits - 1) / kComputeUnits;
+    const int64_t rs = (tiles * S + kComputeUnits - 1) / kComputeUnits;
+    if (rc * S < rs * c) S = c;
+  }
   P->dh_splits = (int)S;
   P->dh_ksplit = round_up((P->Vp + S - 1) / S, kstep);
 
@@ -326,7 +338,7 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
     h.A = ws + P.b_dzcv; h.lda = P.Vp; h.a_layout = LAYOUT_KC;
     h.B = ws + P.b_wt; h.ldb = P.Vp; h.b_layout = LAYOUT_KC;
     h.M = rows; h.N = (int)d; h.k_end = P.Vp; h.k_split = P.dh_ksplit;
-    h.tiles_m = (int)((rows + 255) / 256); h.tiles_n = (int)((d + 255) / 256);
+    h.tiles_m = (int)((rows + 255) / 256); h.tiles_n = (int)((d + P.dtile - 1) / P.dtile); h.bn = P.dtile;
     h.splits = (int)((P.Vp + P.dh_ksplit - 1) / P.dh_ksplit);
     h.out = (float*)(ws + P.b_dhpart); h.ldo = d; h.Cp = P.Cp;
     const int splits = h.splits;
@@ -348,7 +360,7 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
     }
     w.B = ws + P.b_ht; w.ldb = P.Cp; w.b_layout = LAYOUT_KC;
     w.M = (int)V; w.N = (int)d; w.k_end = rows_pad; w.k_split = rows_pad;
-    w.tiles_m = (int)P.n_vt; w.tiles_n = (int)((d + 255) / 256); w.splits = 1;
+    w.tiles_m = (int)P.n_vt; w.tiles_n = (int)((d + P.dtile - 1) / P.dtile); w.splits = 1; w.bn = P.dtile;
     w.out = dW; w.ldo = d; w.accumulate = (r0 > 0 || accumulate_dW) ? 1 : 0;
     e = timed(K_DW_GEMM, fl, ((double)V * rows + (double)rows * d) * P.es + 8.0 * V * d, s,
               [&] { return launch_gemm(dtype, EPI_DW, w, s); });

@@ -81,6 +81,7 @@ struct GemmArgs {
   // operand has *_krows valid rows and *_mcols valid columns; reads past
   // them are clamped (their products are zero or masked).
   int a_layout, b_layout;
+  int bn;                        // N-tile width: 256 (or 0), or 320 for dH / dW (see gemm_d_tile)
   int64_t a_krows, a_mcols, b_krows, b_mcols;
 };
 
@@ -91,6 +92,9 @@ enum { LAYOUT_KC = 0, LAYOUT_MC = 1 };
 // every operand's leading dimension (d, padded V, padded chunk) small enough
 // for 32-bit load offsets within a tile.
 bool gemm_fast_path(int dtype, int64_t d, int64_t Vp, int64_t Cp);
+// N-tile width of the products whose N axis is the hidden size d (dH, dW):
+// 320 on the fast path when it pads d less than 256 does, else 256.
+int gemm_d_tile(bool fast, int64_t d);
 
 struct MergeArgs {
   const float4* part;   // [Cp, n_vt]

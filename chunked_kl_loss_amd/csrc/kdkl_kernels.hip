@@ -293,18 +293,23 @@ hipError_t launch_dh_reduce(int dtype, const float* part, int splits, int rows, 
 // lane l holds output row 8 * (r >> 2) + 4 * (l >> 5) + (r & 3), column
 // (l & 31).
 // ---------------------------------------------------------------------------
-constexpr int BM = 256, BN = 256;      // workgroup tile
+constexpr int BM = 256, BN = 256;      // workgroup tile (the N width is a property of the grid below)
 constexpr int kDwPitch = BN + 8;       // fp32 row pitch of the dW staging tile
 constexpr int kDzPitch = BM + 8;       // bf16 row pitch of the dZ staging tile
 constexpr int kEpiSmem = 128 * kDwPitch * 4;
 
-template <int WAVES_M, int WAVES_N>
+// Wavefront grid of a BM x TN workgroup tile. TN is 256 except for the
+// products whose N axis is the hidden size, which may use 320-wide tiles
+// (a hidden size of 2880 is 9 x 320 but 11.25 x 256).
+template <int WAVES_M, int WAVES_N, int TN = 256>
 struct Grid {
   static constexpr int kWavesM = WAVES_M, kWavesN = WAVES_N;
   static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int WM = BM / WAVES_M, WN = BN / WAVES_N;
+  static constexpr int BN = TN;
+  static constexpr int WM = BM / WAVES_M, WN = TN / WAVES_N;
   static constexpr int MB = WM / 32, NB = WN / 32;
+  static_assert(WM % 32 == 0 && WN % 32 == 0, "wavefront tiles are whole 32 x 32 blocks");
   static __device__ __forceinline__ int wm() { return (int)(threadIdx.x >> 6) / WAVES_N; }
   static __device__ __forceinline__ int wn() { return (int)(threadIdx.x >> 6) % WAVES_N; }
 };
@@ -346,7 +351,7 @@ __device__ __forceinline__ void hit_ranges(const GemmArgs& p, const Tile& t, int
   const int lane = threadIdx.x & 63, wn = G::wn();
 #pragma unroll
   for (int nb = 0; nb < G::NB; ++nb) {
-    const int col = t.tn * BN + wn * G::WN + nb * 32 + (lane & 31);
+    const int col = t.tn * G::BN + wn * G::WN + nb * 32 + (lane & 31);
     if (col < p.N) {
       lo[nb] = p.tstart[(int64_t)t.tm * p.Cp + col];
       hi[nb] = p.tstart[(int64_t)(t.tm + 1) * p.Cp + col];
@@ -371,6 +376,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
                                               char* smem, const int (&hit_lo)[G::NB],
                                               const int (&hit_hi)[G::NB]) {
   constexpr int MB = G::MB, NB = G::NB, NT = G::kThreads;
+  constexpr int BN = G::BN;
+  static_assert(BN == 256 || EPI == EPI_DH || EPI == EPI_DW, "token-axis tiles are 256 wide");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wm = G::wm(), wn = G::wn();
   const int m0 = t.tm * BM, n0 = t.tn * BN;
@@ -557,57 +564,61 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
         }
     }
   } else {
-    // EPI_DW: dW[row, col] (+)= tile, staged through LDS 128 rows at a time
+    // EPI_DW: dW[row, col] (+)= tile, staged through LDS PR rows at a time
     // so the read-modify-write of dW uses 16-byte accesses on whole rows.
-    // The old values of each half are loaded into registers before that
-    // half's accumulators go through LDS, so the load latency overlaps the
-    // staging (and, for the second half, the first half's stores).
-    static_assert(128 % G::WM == 0, "dW staging takes whole wavefront tiles per 128-row half");
+    // The old values of each part are loaded into registers before that
+    // part's accumulators go through LDS, so the load latency overlaps the
+    // staging (and, after the first part, the previous part's stores).
+    constexpr int PR = BN == 256 ? 128 : 64;  // rows per staged part (fits the LDS)
+    constexpr int PITCH = BN + 8;
+    constexpr int C4 = BN / 4;                // float4 per row
+    constexpr int ITER = PR * C4 / NT;
+    static_assert(PR % G::WM == 0 && (PR * C4) % NT == 0, "dW staging takes whole wavefront tiles");
+    static_assert(PR * PITCH * 4 <= kEpiSmem, "dW staging fits the shared buffer");
     float* F = (float*)smem;
-    constexpr int ITER = (128 * BN / 4) / NT;
     float4 o[ITER];
     // Rows and columns past the edge read a clamped (valid) address; their
     // sums are never stored.
-    auto load_old = [&](int half) {
+    auto load_old = [&](int part) {
 #pragma unroll
       for (int u = 0; u < ITER; ++u) o[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (p.accumulate) {
 #pragma unroll
         for (int u = 0; u < ITER; ++u) {
           const int j = u * NT + tid;
-          const int row = min(m0 + half * 128 + (j >> 6), p.M - 1), col = min(n0 + (j & 63) * 4, p.N - 4);
+          const int row = min(m0 + part * PR + j / C4, p.M - 1), col = min(n0 + (j % C4) * 4, p.N - 4);
           o[u] = *(const float4*)(p.out + (int64_t)row * p.ldo + col);
         }
       }
     };
     load_old(0);
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int part = 0; part < BM / PR; ++part) {
       __syncthreads();
-      if ((wm * G::WM) / 128 == half) {
-        const int rb = wm * G::WM - half * 128;
+      if ((wm * G::WM) / PR == part) {
+        const int rb = wm * G::WM - part * PR;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              F[(rb + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * kDwPitch + wn * G::WN + nb * 32 +
+              F[(rb + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * PITCH + wn * G::WN + nb * 32 +
                 (lane & 31)] = acc[mb][nb][r];
       }
       __syncthreads();
 #pragma unroll
       for (int u = 0; u < ITER; ++u) {
         const int j = u * NT + tid;
-        const int r = j >> 6, c4 = j & 63;
-        const int row = m0 + half * 128 + r, col = n0 + c4 * 4;
+        const int r = j / C4, c4 = j % C4;
+        const int row = m0 + part * PR + r, col = n0 + c4 * 4;
         if (row < p.M && col < p.N) {
-          const float4 v = *(const float4*)(F + r * kDwPitch + c4 * 4);
+          const float4 v = *(const float4*)(F + r * PITCH + c4 * 4);
           *(float4*)(p.out + (int64_t)row * p.ldo + col) =
               make_float4(o[u].x + v.x, o[u].y + v.y, o[u].z + v.z, o[u].w + v.w);
         }
       }
-      if (half == 0) load_old(1);
+      if (part + 1 < BM / PR) load_old(part + 1);
     }
   }
 }
@@ -818,13 +829,16 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
   constexpr int MB = G::MB, NB = G::NB;
   constexpr int RB = BK * 2;                 // bytes of one k-contiguous LDS row
   constexpr int CPR = RB / 16;               // 16-byte chunks per such row
-  constexpr int TILE = BM * RB;              // bytes of one operand tile per stage
-  constexpr int STG = 2 * TILE;
+  constexpr int TILE = BM * RB;              // bytes of the A tile per stage
+  constexpr int TILE_B = G::BN * RB;         // bytes of the B tile per stage
+  constexpr int STG = TILE + TILE_B;
   constexpr int SMEM = NSTAGE * STG > kEpiSmem ? NSTAGE * STG : kEpiSmem;
-  constexpr int LPO = TILE / (1024 * G::kWaves);  // direct loads per wave per operand per stage
-  constexpr int LPS = 2 * LPO;
+  constexpr int LPO = TILE / (1024 * G::kWaves);     // direct loads per wave for A per stage
+  constexpr int LPO_B = TILE_B / (1024 * G::kWaves);  // and for B
+  constexpr int LPS = LPO + LPO_B;
   constexpr int KG = BK / 16;                // 16-element k-groups per step
-  static_assert(BM == BN && BM == 256, "k-major LDS rows hold 256 elements");
+  static_assert(LPO * 1024 * G::kWaves == TILE && LPO_B * 1024 * G::kWaves == TILE_B, "whole loads per wave");
+  static_assert(BM == 256 && (LB == LAYOUT_KC || G::BN == 256), "k-major LDS rows hold 256 elements");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   Tile t;
   if (!tile_of(p, t)) return;
@@ -834,7 +848,7 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid / G::kWavesN, wn = wid % G::kWavesN;
-  const int m0 = t.tm * BM, n0 = t.tn * BN;
+  const int m0 = t.tm * BM, n0 = t.tn * G::BN;
   const int64_t kb = (int64_t)t.ks * p.k_split;
   const int64_t ke = kb + p.k_split < p.k_end ? kb + p.k_split : p.k_end;
   const int nk = ke > kb ? (int)((ke - kb) / BK) : 0;
@@ -873,12 +887,11 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
     }
     return s;
   };
-  Src sa[LPO], sb[LPO];
+  Src sa[LPO], sb[LPO_B];
 #pragma unroll
-  for (int i = 0; i < LPO; ++i) {
-    sa[i] = make_src(LA, p.lda, p.M, m0, p.a_mcols, i);
-    sb[i] = make_src(LB, p.ldb, p.N, n0, p.b_mcols, i);
-  }
+  for (int i = 0; i < LPO; ++i) sa[i] = make_src(LA, p.lda, p.M, m0, p.a_mcols, i);
+#pragma unroll
+  for (int i = 0; i < LPO_B; ++i) sb[i] = make_src(LB, p.ldb, p.N, n0, p.b_mcols, i);
   // Uniform base of one operand's stage kt.
   auto stage_base = [&](int layout, const void* X, int64_t ld, int row0, int kt) -> const char* {
     const int64_t k0 = kb + (int64_t)kt * BK;
@@ -899,7 +912,7 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
     for (int i = 0; i < LPO; ++i)
       load16_lds(ba, lane_off(LA, sa[i], p.lda, p.a_krows, kt), base + (i * G::kWaves + wid) * 1024);
 #pragma unroll
-    for (int i = 0; i < LPO; ++i)
+    for (int i = 0; i < LPO_B; ++i)
       load16_lds(bb, lane_off(LB, sb[i], p.ldb, p.b_krows, kt), base + TILE + (i * G::kWaves + wid) * 1024);
   };
 
@@ -980,7 +993,7 @@ using FastGrid = typename std::conditional<
 // Byte span of one stage's direct loads from its buffer-resource base: the
 // lane offsets are 32-bit and the resource's range is 2^31 - 1 bytes.
 static bool span_fits(int layout, int64_t ld, int64_t mcols) {
-  const int64_t span = layout == LAYOUT_KC ? (256 * ld + KDKL_GEMM_BK) * 2 : (KDKL_GEMM_BK * ld + mcols) * 2;
+  const int64_t span = layout == LAYOUT_KC ? (320 * ld + KDKL_GEMM_BK) * 2 : (KDKL_GEMM_BK * ld + mcols) * 2;
   return span < ((int64_t)1 << 31);
 }
 
@@ -994,8 +1007,27 @@ bool gemm_fast_path(int dtype, int64_t d, int64_t Vp, int64_t Cp) {
 // each wave fewer dZ fragments than the 2 x 4 grid of the other products.
 using DwGrid = typename std::conditional<KDKL_GEMM_WAVES == 8 && KDKL_DW_GRID42, Grid<4, 2>, FastGrid>::type;
 
+#ifndef KDKL_D320
+#define KDKL_D320 1
+#endif
+int gemm_d_tile(bool fast, int64_t d) {
+  if (!fast || !KDKL_D320) return 256;
+  const int64_t pad256 = (d + 255) / 256 * 256, pad320 = (d + 319) / 320 * 320;
+  return pad320 < pad256 ? 320 : 256;
+}
+
 template <int EPI, int LA, int LB>
 static hipError_t launch_fast(const GemmArgs& a, dim3 grid, hipStream_t s) {
+  if constexpr (EPI == EPI_DH || EPI == EPI_DW) {
+    if (a.bn == 320) {
+      // 256 x 320 tiles on a 4 x 2 grid: wavefront tiles of 64 x 160
+      using GW = Grid<4, 2, 320>;
+      hipLaunchKernelGGL((gemm_bf16_kernel<GW, EPI, KDKL_GEMM_BK, KDKL_GEMM_STAGES, LA, LB>), grid,
+                         dim3(GW::kThreads), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  if (a.bn != 0 && a.bn != 256) return hipErrorInvalidValue;
   using GG = typename std::conditional<EPI == EPI_DW, DwGrid, FastGrid>::type;
   hipLaunchKernelGGL((gemm_bf16_kernel<GG, EPI, KDKL_GEMM_BK, KDKL_GEMM_STAGES, LA, LB>), grid,
                      dim3(GG::kThreads), 0, s, a);
@@ -1020,6 +1052,7 @@ static hipError_t launch_gemm_e(int dtype, const GemmArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   }
   if (a.a_layout != LAYOUT_KC || a.b_layout != LAYOUT_KC) return hipErrorInvalidValue;
+  if (a.bn != 0 && a.bn != 256) return hipErrorInvalidValue;
   if (dtype == 1)
     hipLaunchKernelGGL((gemm_generic_kernel<uint16_t, EPI>), grid, dim3(256), 0, s, a);
   else

@@ -23,6 +23,10 @@ CASES = [
     ("llama3b_geometry", "llama3b_8k", dict(N=96, chunk=40), None),
     ("gptoss20b_geometry", "gptoss20b_32k", dict(N=80, chunk=32), None),
     ("longctx_geometry_T2", "longctx_256k", dict(N=64, chunk=24), None),
+    # hidden sizes whose dH / dW products use 320-wide tiles: one exact, one
+    # with a partial last tile, both with ragged vocabulary and chunk tails
+    ("bf16_d_tile320_exact", "small_bf16", dict(N=130, d=960, V=2500, K=12, chunk=64, T=1.0), 11),
+    ("bf16_d_tile320_ragged", "small_bf16", dict(N=200, d=576, V=3001, K=30, chunk=96, T=1.3), 10),
 ]
 
 
