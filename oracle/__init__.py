@@ -18,4 +18,6 @@ from .kl import (  # noqa: F401
     logits_forward,
     logits_backward,
     logits_sampled_rows,
+    kept_positions,
+    IGNORE_ID,
 )

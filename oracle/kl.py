@@ -22,6 +22,14 @@ definition written out in fp64:
 * per-position forward KL ``KL_i = sum_k p_ik (log p_ik - log q_i[id_ik])``;
 * ``loss = (1/N) sum_i KL_i`` (mean over positions).
 
+Ignored positions (reading; the pages only mention ablations on sequence
+packing [P1, section "The resulting student model", last paragraphs]): a
+position whose first teacher id is ``IGNORE_ID`` (-1) has no teacher target,
+as at padding or packing boundaries. It contributes nothing: KL_i = 0, a zero
+gradient row, and the mean runs over the positions that are kept (N is their
+number below; with none kept the loss is NaN and every gradient is zero). The
+other entries of an ignored row are never used.
+
 Gradient (derived here; the pages say a closed form exists but do not print
 it [P1, section "The resulting student model", last paragraph]): with
 upstream scalar ``g``,
@@ -54,6 +62,8 @@ __all__ = [
     "logits_forward",
     "logits_backward",
     "logits_sampled_rows",
+    "kept_positions",
+    "IGNORE_ID",
 ]
 
 
@@ -78,6 +88,21 @@ def _ids(x) -> np.ndarray:
     except ImportError:  # pragma: no cover
         pass
     return np.asarray(x, dtype=np.int64)
+
+
+IGNORE_ID = -1
+
+
+def kept_positions(ids) -> np.ndarray:
+    """Boolean [N]: positions whose first teacher id is not IGNORE_ID."""
+    ids = _ids(ids)
+    return ids[:, 0] != IGNORE_ID if ids.shape[0] else np.zeros(0, dtype=bool)
+
+
+def _usable_ids(ids: np.ndarray, kept: np.ndarray) -> np.ndarray:
+    # ignored rows may hold anything; give them harmless indices (their
+    # results are discarded)
+    return np.where(kept[:, None], ids, 0)
 
 
 def _logsumexp_rows(a: np.ndarray) -> np.ndarray:
@@ -115,16 +140,20 @@ def forward(H, W, ids, logits, T: float, block: int = 256) -> Dict[str, object]:
     H = _f64(H)
     W = _f64(W)
     ids = _ids(ids)
-    N = H.shape[0]
-    row_lse = np.empty(N)
-    row_kl = np.empty(N)
-    for r0 in range(0, N, block):
-        r1 = min(N, r0 + block)
+    n_rows = H.shape[0]
+    kept = kept_positions(ids)
+    ids = _usable_ids(ids, kept)
+    row_lse = np.empty(n_rows)
+    row_kl = np.empty(n_rows)
+    for r0 in range(0, n_rows, block):
+        r1 = min(n_rows, r0 + block)
         logq, lse = student_log_softmax(H[r0:r1], W, T)
         p, logp = teacher_distribution(logits[r0:r1], T)
         logq_at = np.take_along_axis(logq, ids[r0:r1], axis=1)
         row_kl[r0:r1] = (p * (logp - logq_at)).sum(axis=1)
         row_lse[r0:r1] = lse
+    row_kl[~kept] = 0.0
+    N = int(kept.sum())  # the mean runs over the kept positions
     loss = math.fsum(row_kl.tolist()) / N if N else float("nan")
     return {"loss": loss, "row_lse": row_lse, "row_kl": row_kl}
 
@@ -145,13 +174,17 @@ def backward(H, W, ids, logits, T: float, g: float = 1.0,
     H = _f64(H)
     W = _f64(W)
     ids = _ids(ids)
-    N = H.shape[0]
-    coef = float(g) / (N * float(T))
+    n_rows = H.shape[0]
+    kept = kept_positions(ids)
+    ids = _usable_ids(ids, kept)
+    N = int(kept.sum())  # the mean runs over the kept positions
+    coef = float(g) / (N * float(T)) if N else 0.0
     dH = np.empty_like(H)
     dW = np.zeros_like(W)
-    for r0 in range(0, N, block):
-        r1 = min(N, r0 + block)
+    for r0 in range(0, n_rows, block):
+        r1 = min(n_rows, r0 + block)
         dZ = _dz_rows(H[r0:r1], W, ids[r0:r1], logits[r0:r1], T, coef)
+        dZ[~kept[r0:r1]] = 0.0
         dH[r0:r1] = dZ @ W
         dW += dZ.T @ H[r0:r1]
     return dH, dW
@@ -174,9 +207,12 @@ def dense_kl_loss(H, W, ids, logits, T: float) -> float:
     ids = _ids(ids)
     N, K = ids.shape
     V = W.shape[0]
+    kept = kept_positions(ids)
     a = _f64(logits) / float(T)
     P = np.zeros((N, V))
     for i in range(N):
+        if not kept[i]:
+            continue
         e = np.exp(a[i] - a[i].max())
         for k in range(K):
             P[i, ids[i, k]] += e[k] / e.sum()
@@ -190,7 +226,8 @@ def dense_kl_loss(H, W, ids, logits, T: float) -> float:
         for v in range(V):
             if P[i, v] > 0:
                 total += P[i, v] * (math.log(P[i, v]) - logQ[i, v])
-    return total / N
+    n_kept = int(kept.sum())
+    return total / n_kept if n_kept else float("nan")
 
 
 def sampled_rows(H, W, ids, logits, T: float, rows: Iterable[int],
@@ -198,11 +235,12 @@ def sampled_rows(H, W, ids, logits, T: float, rows: Iterable[int],
     """Per-row results for a few rows of a large problem, one row at a time.
 
     Returns dict(rows, row_lse, row_kl, dH_rows) where ``dH_rows`` are the rows
-    of the gradient of ``g * loss`` for a problem of ``N_total`` positions.
+    of the gradient of ``g * loss`` for a problem of ``N_total`` kept
+    positions.
     """
     rows = np.asarray(list(rows), dtype=np.int64)
     Wf = _f64(W)
-    coef = float(g) / (N_total * float(T))
+    coef = float(g) / (N_total * float(T)) if N_total else 0.0
     lse_out = np.empty(rows.size)
     kl_out = np.empty(rows.size)
     dh_out = np.empty((rows.size, Wf.shape[1]))
@@ -211,9 +249,13 @@ def sampled_rows(H, W, ids, logits, T: float, rows: Iterable[int],
         idr = _ids(ids[r:r + 1])
         lgr = _f64(logits[r:r + 1])
         logq, lse = student_log_softmax(Hr, Wf, T)
+        lse_out[j] = lse[0]
+        if not kept_positions(idr)[0]:
+            kl_out[j] = 0.0
+            dh_out[j] = 0.0
+            continue
         p, logp = teacher_distribution(lgr, T)
         kl_out[j] = (p * (logp - np.take_along_axis(logq, idr, axis=1))).sum()
-        lse_out[j] = lse[0]
         dz = _dz_rows(Hr, Wf, idr, lgr, T, coef)
         dh_out[j] = (dz @ Wf)[0]
     return {"rows": rows, "row_lse": lse_out, "row_kl": kl_out, "dH_rows": dh_out}
@@ -228,9 +270,10 @@ def dw_rows(H, W, ids, logits, T: float, vrows: Iterable[int], row_lse,
     ``backward``, evaluated one vocabulary row at a time)."""
     Hf = _f64(H)
     ids_ = _ids(ids)
+    kept = kept_positions(ids_)
     vrows = np.asarray(list(vrows), dtype=np.int64)
-    N = Hf.shape[0]
-    coef = float(g) / (N * float(T))
+    N = int(kept.sum())  # the mean runs over the kept positions
+    coef = float(g) / (N * float(T)) if N else 0.0
     Wv = _f64(W[vrows])  # [nv, d]
     p, _ = teacher_distribution(logits, T)
     lse = np.asarray(row_lse, dtype=np.float64)
@@ -239,6 +282,7 @@ def dw_rows(H, W, ids, logits, T: float, vrows: Iterable[int], row_lse,
         z = Hf @ Wv[j] / float(T)
         P = (p * (ids_ == v)).sum(axis=1)
         dz = coef * (np.exp(z - lse) - P)
+        dz[~kept] = 0.0
         out[j] = dz @ Hf
     return out
 
@@ -272,11 +316,13 @@ def logits_forward(Z, ids, logits, T: float, block: int = 256) -> Dict[str, obje
     ``Z [N, V]``; returns dict(loss, row_lse, row_kl) in fp64."""
     Z = _f64(Z)
     ids = _ids(ids)
-    N, V = Z.shape
-    row_lse = np.empty(N)
-    row_kl = np.empty(N)
-    for r0 in range(0, N, block):
-        r1 = min(N, r0 + block)
+    n_rows, V = Z.shape
+    kept = kept_positions(ids)
+    ids = _usable_ids(ids, kept)
+    row_lse = np.empty(n_rows)
+    row_kl = np.empty(n_rows)
+    for r0 in range(0, n_rows, block):
+        r1 = min(n_rows, r0 + block)
         s = Z[r0:r1] / float(T)
         lse = _logsumexp_rows(s)
         p, logp = teacher_distribution(logits[r0:r1], T)
@@ -287,6 +333,8 @@ def logits_forward(Z, ids, logits, T: float, block: int = 256) -> Dict[str, obje
         gamma = (p * np.where(ok, s_at, 0.0)).sum(axis=1)
         row_kl[r0:r1] = e - gamma + lse
         row_lse[r0:r1] = lse
+    row_kl[~kept] = 0.0
+    N = int(kept.sum())  # the mean runs over the kept positions
     loss = math.fsum(row_kl.tolist()) / N if N else float("nan")
     return {"loss": loss, "row_lse": row_lse, "row_kl": row_kl}
 
@@ -296,11 +344,14 @@ def logits_backward(Z, ids, logits, T: float, g: float = 1.0, block: int = 256) 
     ``dZ_i = g / (N T) * (softmax(Z_i / T) - scatter_add(ids_i, p_i))``."""
     Z = _f64(Z)
     ids = _ids(ids)
-    N, V = Z.shape
-    scale = float(g) / (N * float(T))
+    n_rows, V = Z.shape
+    kept = kept_positions(ids)
+    ids = _usable_ids(ids, kept)
+    N = int(kept.sum())  # the mean runs over the kept positions
+    scale = float(g) / (N * float(T)) if N else 0.0
     dZ = np.empty_like(Z)
-    for r0 in range(0, N, block):
-        r1 = min(N, r0 + block)
+    for r0 in range(0, n_rows, block):
+        r1 = min(n_rows, r0 + block)
         s = Z[r0:r1] / float(T)
         q = np.exp(s - _logsumexp_rows(s)[:, None])
         p, _ = teacher_distribution(logits[r0:r1], T)
@@ -310,6 +361,7 @@ def logits_backward(Z, ids, logits, T: float, g: float = 1.0, block: int = 256) 
         rr, kk = np.nonzero(ok)
         np.add.at(P, (rr, idr[rr, kk]), p[rr, kk])
         dZ[r0:r1] = scale * (q - P)
+        dZ[r0:r1][~kept[r0:r1]] = 0.0
     return dZ
 
 
@@ -317,7 +369,7 @@ def logits_sampled_rows(Z, ids, logits, T: float, rows: Iterable[int], N_total: 
                         g: float = 1.0) -> Dict[str, np.ndarray]:
     """``logits_forward`` / ``logits_backward`` restricted to a few rows of a
     large grid (one row at a time); dZ rows are those of a problem with
-    ``N_total`` positions."""
+    ``N_total`` kept positions."""
     rows = [int(r) for r in rows]
     out_lse, out_kl, out_dz = [], [], []
     for r in rows:
@@ -326,6 +378,6 @@ def logits_sampled_rows(Z, ids, logits, T: float, rows: Iterable[int], N_total: 
         dz = logits_backward(Zr, ids[r:r + 1], logits[r:r + 1], T, g)
         out_lse.append(f["row_lse"][0])
         out_kl.append(f["row_kl"][0])
-        out_dz.append(dz[0] / N_total)  # logits_backward divided by N = 1
+        out_dz.append(dz[0] / N_total if N_total else 0.0 * dz[0])  # logits_backward divided by N = 1
     return {"rows": np.asarray(rows), "row_lse": np.asarray(out_lse),
             "row_kl": np.asarray(out_kl), "dZ_rows": np.stack(out_dz) if out_dz else np.zeros((0, 0))}

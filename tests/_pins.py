@@ -410,6 +410,72 @@ def pin_logits_matches_fused(o):
     _close(sr["row_kl"], lf["row_kl"][[0, 4]], 1e-13, what="logits sampled kl")
 
 
+# --- ignored positions (first teacher id -1) -----------------------------------
+
+def pin_ignored_positions(o):
+    """Ignoring a position is deleting it: loss, dW and the kept rows' outputs
+    equal those of the problem without it (computed by the unmasked paths,
+    pinned above), its KL and gradient row are zero, its other teacher
+    entries are never used; with nothing kept the loss is NaN and every
+    gradient is zero. For the fused and the forward-chunked functions, the
+    dense-grid baseline and the one-row helpers."""
+    if not hasattr(o, "kept_positions"):
+        return
+    rng = np.random.default_rng(27)
+    N, d, V, K, T, g = 10, 5, 19, 4, 1.3, 0.8
+    H, W, ids, logits = _rand_problem(rng, N, d, V, K)
+    ign = np.array([1, 4, 5, 9])
+    keep = np.setdiff1d(np.arange(N), ign)
+    ids_m = ids.copy()
+    ids_m[ign, 0] = -1
+    ids_m[ign[0], 1:] = 10 ** 9  # never used
+    assert np.array_equal(o.kept_positions(ids_m), np.isin(np.arange(N), keep))
+    f = o.forward(H, W, ids_m, logits, T)
+    fr = o.forward(H[keep], W, ids[keep], logits[keep], T)
+    _close(f["loss"], fr["loss"], 1e-13, what="ignored: loss")
+    assert np.all(f["row_kl"][ign] == 0.0)
+    _close(f["row_kl"][keep], fr["row_kl"], 1e-13, what="ignored: kept row_kl")
+    _close(f["row_lse"], o.forward(H, W, ids, logits, T)["row_lse"], 1e-13, what="ignored: lse")
+    dH, dW = o.backward(H, W, ids_m, logits, T, g)
+    dHr, dWr = o.backward(H[keep], W, ids[keep], logits[keep], T, g)
+    assert np.all(dH[ign] == 0.0)
+    _close(dH[keep], dHr, 1e-13, what="ignored: kept dH")
+    _close(dW, dWr, 1e-13, what="ignored: dW")
+    _close(o.dense_kl_loss(H, W, ids_m, logits, T), fr["loss"], 1e-12, what="ignored: dense grid")
+    sr = o.sampled_rows(H, W, ids_m, logits, T, [0, 1, 6], len(keep), g)
+    _close(sr["dH_rows"], dH[[0, 1, 6]], 1e-13, what="ignored: sampled dH")
+    _close(sr["row_kl"], f["row_kl"][[0, 1, 6]], 1e-13, what="ignored: sampled kl")
+    _close(o.dw_rows(H, W, ids_m, logits, T, [0, 3, 18], f["row_lse"], g), dW[[0, 3, 18]], 1e-12,
+           what="ignored: dW rows")
+    Z = H @ W.T
+    lf = o.logits_forward(Z, ids_m, logits, T)
+    lfr = o.logits_forward(Z[keep], ids[keep], logits[keep], T)
+    _close(lf["loss"], lfr["loss"], 1e-13, what="ignored: logits loss")
+    assert np.all(lf["row_kl"][ign] == 0.0)
+    dZ = o.logits_backward(Z, ids_m, logits, T, g)
+    assert np.all(dZ[ign] == 0.0)
+    _close(dZ[keep], o.logits_backward(Z[keep], ids[keep], logits[keep], T, g), 1e-13,
+           what="ignored: logits dZ")
+    ls = o.logits_sampled_rows(Z, ids_m, logits, T, [1, 2], len(keep), g)
+    _close(ls["dZ_rows"], dZ[[1, 2]], 1e-13, what="ignored: logits sampled dZ")
+    # only -1 marks a position; another negative first id is an out-of-range
+    # id whose mass is dropped, and the position still counts
+    ids_n = ids.copy()
+    ids_n[2, 0] = -5
+    assert o.kept_positions(ids_n)[2]
+    ln = o.logits_forward(Z, ids_n, logits, T)
+    assert ln["row_kl"][2] != 0.0
+    _close(ln["loss"], math.fsum(ln["row_kl"].tolist()) / N, 1e-13, what="out-of-range first id counts")
+    # nothing kept
+    ids_all = ids.copy()
+    ids_all[:, 0] = -1
+    assert math.isnan(o.forward(H, W, ids_all, logits, T)["loss"])
+    dH0, dW0 = o.backward(H, W, ids_all, logits, T, g)
+    assert not dH0.any() and not dW0.any()
+    assert math.isnan(o.logits_forward(Z, ids_all, logits, T)["loss"])
+    assert not o.logits_backward(Z, ids_all, logits, T, g).any()
+
+
 ALL_PINS = [
     pin_two_token_softplus,
     pin_uniform_student,
@@ -425,4 +491,5 @@ ALL_PINS = [
     pin_logits_brute_force_dropped_ids,
     pin_logits_closed_forms_and_invariants,
     pin_logits_matches_fused,
+    pin_ignored_positions,
 ]

@@ -45,6 +45,13 @@ MUTANTS = [
     ("logits_grad_no_T", "scale = float(g) / (N * float(T))", "scale = float(g) / N"),
     ("logits_grad_no_teacher", "dZ[r0:r1] = scale * (q - P)", "dZ[r0:r1] = scale * q"),
     ("logits_scatter_first_id_only", "rr, kk = np.nonzero(ok)", "rr, kk = np.nonzero(ok[:, :1])"),
+    # ignored positions
+    ("ignored_counted_in_mean", "N = int(kept.sum())  # the mean runs over the kept positions",
+     "N = kept.size  # the mean runs over the kept positions"),
+    ("ignored_row_kl_kept", "row_kl[~kept] = 0.0", "pass"),
+    ("ignored_grad_row_kept", "dZ[~kept[r0:r1]] = 0.0", "pass"),
+    ("ignored_logits_grad_row_kept", "dZ[r0:r1][~kept[r0:r1]] = 0.0", "pass"),
+    ("ignore_marker_any_negative", "return ids[:, 0] != IGNORE_ID if", "return ids[:, 0] >= 0 if"),
 ]
 
 
