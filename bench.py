@@ -147,11 +147,12 @@ def bench_logits(args, w, x):
     row_lse = torch.empty(w.N, dtype=torch.float32, device=dev)
     row_kl = torch.empty(w.N, dtype=torch.float32, device=dev)
     dZ = Z if args.inplace else torch.empty_like(Z)
+    ws = torch.empty(kd.LOGITS_BWD_WORKSPACE, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
 
     def step():
         kd.logits_forward(Z, ids, lg, w.T, loss=loss, row_lse=row_lse, row_kl=row_kl, stream=stream)
-        kd.logits_backward(Z, ids, lg, w.T, row_lse, None, dZ=dZ, stream=stream)
+        kd.logits_backward(Z, ids, lg, w.T, row_lse, None, dZ=dZ, workspace=ws, stream=stream)
 
     for _ in range(args.warmup):
         step()

@@ -182,8 +182,11 @@ def logits_forward(Z, ids, logits, T: float, *, loss=None, row_lse=None, row_kl=
     return loss, row_lse, row_kl
 
 
+LOGITS_BWD_WORKSPACE = 256  # KDKL_LOGITS_BWD_WORKSPACE
+
+
 def logits_backward(Z, ids, logits, T: float, row_lse, grad_loss=None, *, dZ=None,
-                    stream=None):
+                    workspace=None, stream=None):
     """Gradient of the forward-chunked KL with respect to ``Z``
     (``kdkl_logits_backward``); ``dZ=Z`` overwrites the logits in place."""
     _need_gpu(Z, ids, logits, row_lse, grad_loss)
@@ -194,9 +197,12 @@ def logits_backward(Z, ids, logits, T: float, row_lse, grad_loss=None, *, dZ=Non
         raise ValueError("dZ must be a contiguous tensor of Z's shape and dtype")
     if grad_loss is not None and grad_loss.dtype != torch.float32:
         raise TypeError("grad_loss must be float32")
+    if workspace is None:
+        workspace = torch.empty(LOGITS_BWD_WORKSPACE, dtype=torch.uint8, device=Z.device)
     check(_load().kdkl_logits_backward(_ptr(Z), _ptr(ids), _ptr(logits), N, V, K, float(T),
                                        _dtype_code(Z), _ptr(row_lse), _ptr(grad_loss),
-                                       _ptr(dZ), _stream(Z.device, stream)),
+                                       _ptr(dZ), _ptr(workspace), workspace.numel(),
+                                       _stream(Z.device, stream)),
           "kdkl_logits_backward")
     return dZ
 

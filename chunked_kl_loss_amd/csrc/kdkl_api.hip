@@ -20,7 +20,7 @@ const char* kernel_name(int id) {
   static const char* names[K_COUNT] = {
       "teacher_prep", "fwd_gemm_lse", "split_merge", "loss_reduce", "transpose_w",
       "transpose_h",  "dz_gemm",      "dh_gemm",     "dh_reduce",   "dw_gemm",
-      "logits_fwd",   "logits_bwd"};
+      "logits_fwd",   "logits_bwd",   "grad_scale"};
   return (id >= 0 && id < K_COUNT) ? names[id] : "?";
 }
 
@@ -85,9 +85,9 @@ struct Plan {
   bool fast;       // bf16 main loop: reads W, H and dZ in place (no transposes)
   int dtile;       // N-tile width of the dH and dW products (hidden-size axis)
   // offsets into the forward workspace
-  size_t f_sids, f_sp, f_erow, f_tstart, f_part, f_rowkl, f_bytes;
+  size_t f_sids, f_sp, f_erow, f_keep, f_tstart, f_part, f_rowkl, f_bytes;
   // offsets into the backward workspace
-  size_t b_sids, b_sp, b_erow, b_tstart, b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart, b_bytes;
+  size_t b_sids, b_sp, b_erow, b_keep, b_scale, b_tstart, b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart, b_bytes;
 };
 
 static bool mul_ok(int64_t a, int64_t b, int64_t* out) {
@@ -143,7 +143,7 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   bool ok = true;
   ok &= mul_ok(P->Cp, K, &t0) && mul_ok(t0, 4, &t0);
   ok &= region(&cur, t0, &P->f_sids) && region(&cur, t0, &P->f_sp);
-  ok &= region(&cur, P->Cp * 4, &P->f_erow);
+  ok &= region(&cur, P->Cp * 4, &P->f_erow) && region(&cur, P->Cp * 4, &P->f_keep);
   ok &= mul_ok(P->n_vt + 1, P->Cp, &t1) && mul_ok(t1, 2, &t1);
   ok &= region(&cur, t1, &P->f_tstart);
   ok &= mul_ok(P->Cp, P->n_vt, &t2) && mul_ok(t2, 16, &t2);
@@ -153,7 +153,8 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
 
   cur = 0;
   ok &= region(&cur, t0, &P->b_sids) && region(&cur, t0, &P->b_sp);
-  ok &= region(&cur, P->Cp * 4, &P->b_erow);
+  ok &= region(&cur, P->Cp * 4, &P->b_erow) && region(&cur, P->Cp * 4, &P->b_keep);
+  ok &= region(&cur, 16, &P->b_scale);
   ok &= region(&cur, t1, &P->b_tstart);
   int64_t wt, ht, dz, dhp;
   ok &= mul_ok(d, P->Vp, &wt) && mul_ok(wt, P->es, &wt);
@@ -191,12 +192,12 @@ static kdkl_status check_common(const void* H, const void* W, const int32_t* ids
 
 static TeacherArgs teacher_args(const Plan& P, const int32_t* ids, const float* lg, float T, int64_t r0,
                                 int rows, char* ws, size_t o_sids, size_t o_sp, size_t o_erow,
-                                size_t o_tstart) {
+                                size_t o_keep, size_t o_tstart) {
   TeacherArgs t;
   t.ids = ids; t.logits = lg; t.r0 = r0; t.rows = rows; t.K = (int)P.K;
   t.inv_T = 1.0f / T; t.n_vt = (int)P.n_vt; t.Cp = P.Cp;
   t.sids = (int32_t*)(ws + o_sids); t.sp = (float*)(ws + o_sp);
-  t.erow = (float*)(ws + o_erow); t.tstart = (uint16_t*)(ws + o_tstart);
+  t.erow = (float*)(ws + o_erow); t.keep = (float*)(ws + o_keep); t.tstart = (uint16_t*)(ws + o_tstart);
   return t;
 }
 
@@ -267,7 +268,8 @@ kdkl_status kdkl_forward(const void* H, const void* W, const int32_t* ids, const
   hipError_t e = hipSuccess;
   for (int64_t r0 = 0; r0 < N && e == hipSuccess; r0 += P.chunk) {
     const int rows = (int)((N - r0) < P.chunk ? (N - r0) : P.chunk);
-    TeacherArgs ta = teacher_args(P, ids, lg, T, r0, rows, ws, P.f_sids, P.f_sp, P.f_erow, P.f_tstart);
+    TeacherArgs ta =
+        teacher_args(P, ids, lg, T, r0, rows, ws, P.f_sids, P.f_sp, P.f_erow, P.f_keep, P.f_tstart);
     e = timed(K_TEACHER, 0.0, (double)rows * P.K * 8.0 * 2.0, s, [&] { return launch_teacher(ta, s); });
     if (e != hipSuccess) break;
     GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.f_sids, P.f_sp, P.f_tstart);
@@ -278,11 +280,12 @@ kdkl_status kdkl_forward(const void* H, const void* W, const int32_t* ids, const
     if (e != hipSuccess) break;
     MergeArgs m;
     m.part = (const float4*)(ws + P.f_part); m.n_vt = (int)P.n_vt; m.rows = rows;
-    m.erow = (const float*)(ws + P.f_erow); m.row_lse = row_lse + r0; m.row_kl = kl + r0;
+    m.erow = (const float*)(ws + P.f_erow); m.keep = (const float*)(ws + P.f_keep);
+    m.row_lse = row_lse + r0; m.row_kl = kl + r0;
     e = timed(K_MERGE, 0.0, (double)rows * P.n_vt * 16.0, s, [&] { return launch_merge(m, s); });
   }
   if (e == hipSuccess)
-    e = timed(K_LOSS, 0.0, (double)N * 4.0, s, [&] { return launch_loss(kl, N, loss, s); });
+    e = timed(K_LOSS, 0.0, (double)N * 8.0, s, [&] { return launch_loss(kl, ids, K, N, loss, s); });
   return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
 }
 
@@ -309,11 +312,15 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
   e = timed(K_TRANSPOSE_W, 0.0, 2.0 * (double)V * d * P.es, s, [&] {
       return launch_transpose((int)P.es, W, V, d, d, ws + P.b_wt, P.Vp, P.Vp, s);
     });
-  const double coef_base = 1.0 / ((double)N * (double)T);
+  // g / (N_kept T): the mean runs over the positions that are not ignored
+  if (e == hipSuccess)
+    e = timed(K_GRAD_SCALE, 0.0, (double)N * 4.0, s,
+              [&] { return launch_grad_scale(ids, K, N, grad_loss, T, (float*)(ws + P.b_scale), s); });
   for (int64_t r0 = 0; r0 < N && e == hipSuccess; r0 += P.chunk) {
     const int rows = (int)((N - r0) < P.chunk ? (N - r0) : P.chunk);
     const int64_t rows_pad = round_up(rows, kTokenTile);
-    TeacherArgs ta = teacher_args(P, ids, lg, T, r0, rows, ws, P.b_sids, P.b_sp, P.b_erow, P.b_tstart);
+    TeacherArgs ta =
+        teacher_args(P, ids, lg, T, r0, rows, ws, P.b_sids, P.b_sp, P.b_erow, P.b_keep, P.b_tstart);
     e = timed(K_TEACHER, 0.0, (double)rows * P.K * 8.0 * 2.0, s, [&] { return launch_teacher(ta, s); });
     if (e != hipSuccess) break;
     // H_c^T [d, Cp], zero-padded past the chunk's rows: the dW product
@@ -326,7 +333,7 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
     // recompute the chunk's logits and form dZ (token-major; the generic
     // path also writes the vocabulary-major copy)
     GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.b_sids, P.b_sp, P.b_tstart);
-    g.row_lse = row_lse + r0; g.grad = grad_loss; g.coef_base = (float)coef_base;
+    g.row_lse = row_lse + r0; g.scale = (const float*)(ws + P.b_scale); g.keep = (const float*)(ws + P.b_keep);
     g.dz_cv = ws + P.b_dzcv; g.dz_vc = P.fast ? nullptr : ws + P.b_dzvc;
     const double fl = 2.0 * rows * (double)V * d;
     e = timed(K_DZ_GEMM, fl, ((double)V + rows) * d * P.es + (P.fast ? 1.0 : 2.0) * rows * (double)V * P.es, s,
@@ -396,26 +403,28 @@ kdkl_status kdkl_logits_forward(const void* Z, const int32_t* ids, const float* 
   hipError_t e = timed(K_LOGITS_FWD, 0.0, (double)N * (V * es + K * 8.0 + 8.0), s,
                        [&] { return launch_logits_fwd(dtype, a, s); });
   if (e == hipSuccess)
-    e = timed(K_LOSS, 0.0, (double)N * 4.0, s, [&] { return launch_loss(row_kl, N, loss, s); });
+    e = timed(K_LOSS, 0.0, (double)N * 8.0, s, [&] { return launch_loss(row_kl, ids, K, N, loss, s); });
   return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
 }
 
 kdkl_status kdkl_logits_backward(const void* Z, const int32_t* ids, const float* lg, int64_t N, int64_t V,
                                  int32_t K, float T, int dtype, const float* row_lse, const float* grad_loss,
-                                 void* dZ, void* stream) {
+                                 void* dZ, void* workspace, size_t workspace_bytes, void* stream) {
   kdkl_status st = check_logits(Z, ids, lg, N, V, K, T, dtype);
   if (st != KDKL_OK) return st;
-  if (N > 0 && (!row_lse || !dZ)) return KDKL_ERR_NULL;
-  if (!aligned16(dZ)) return KDKL_ERR_ALIGN;
+  if (N > 0 && (!row_lse || !dZ || !workspace)) return KDKL_ERR_NULL;
+  if (!aligned16(dZ) || !aligned16(workspace)) return KDKL_ERR_ALIGN;
   if (N == 0) return KDKL_OK;
+  if (workspace_bytes < KDKL_LOGITS_BWD_WORKSPACE) return KDKL_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   LogitsArgs a;
   memset(&a, 0, sizeof(a));
   a.Z = Z; a.dZ = dZ; a.ids = ids; a.logits = lg; a.N = N; a.V = V; a.K = K; a.inv_T = 1.0f / T;
-  a.row_lse = const_cast<float*>(row_lse); a.grad = grad_loss;
-  a.coef_base = (float)(1.0 / ((double)N * (double)T));
+  a.row_lse = const_cast<float*>(row_lse); a.scale = (const float*)workspace;
   const double es = dtype == KDKL_BF16 ? 2.0 : 4.0;
-  hipError_t e = timed(K_LOGITS_BWD, 0.0, (double)N * (2.0 * V * es + K * 8.0 + 4.0), s,
+  hipError_t e = timed(K_GRAD_SCALE, 0.0, (double)N * 4.0, s,
+                       [&] { return launch_grad_scale(ids, K, N, grad_loss, T, (float*)workspace, s); });
+  if (e == hipSuccess) e = timed(K_LOGITS_BWD, 0.0, (double)N * (2.0 * V * es + K * 8.0 + 4.0), s,
                        [&] { return launch_logits_bwd(dtype, a, s); });
   return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
 }

@@ -27,6 +27,7 @@ enum KernelId {
   K_DW_GEMM,
   K_LOGITS_FWD,
   K_LOGITS_BWD,
+  K_GRAD_SCALE,
   K_COUNT
 };
 
@@ -45,6 +46,7 @@ struct TeacherArgs {
   int32_t* sids;          // [Cp, K]   ids sorted ascending
   float* sp;              // [Cp, K]   teacher probabilities, same order
   float* erow;            // [Cp]      sum_k p log p
+  float* keep;            // [Cp]      1 for a kept position, 0 for an ignored one (first id -1)
   uint16_t* tstart;       // [n_vt + 1, Cp] first sorted index >= tile start
 };
 
@@ -66,8 +68,8 @@ struct GemmArgs {
   const uint16_t* tstart;
   float4* part;                  // forward: [Cp, n_vt] (max, sumexp, gamma, -)
   const float* row_lse;          // backward: lse of this chunk's rows
-  const float* grad;             // backward: upstream scalar (device) or NULL
-  float coef_base;               // 1 / (N_total * T)
+  const float* scale;            // backward: device scalar g / (N_kept * T)
+  const float* keep;             // backward: keep flags of this chunk's rows [Cp]
   void* dz_cv;                   // [Cp, Vp]
   void* dz_vc;                   // [Vp, Cp]
   int64_t Vp;
@@ -101,13 +103,21 @@ struct MergeArgs {
   int n_vt;
   int rows;
   const float* erow;
+  const float* keep;    // [Cp] keep flags
   float* row_lse;       // chunk-offset
   float* row_kl;        // chunk-offset
 };
 
 hipError_t launch_teacher(const TeacherArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
-hipError_t launch_loss(const float* row_kl, int64_t N, float* loss, hipStream_t s);
+// Ignored positions: the first teacher id of the row is kIgnoreId.
+constexpr int32_t kIgnoreId = -1;
+// loss = sum_i KL_i / (number of kept positions), fixed order; NaN if none.
+hipError_t launch_loss(const float* row_kl, const int32_t* ids, int K, int64_t N, float* loss,
+                       hipStream_t s);
+// out[0] = g / (N_kept T) with g = grad[0] (1 if grad is NULL); 0 if none kept.
+hipError_t launch_grad_scale(const int32_t* ids, int K, int64_t N, const float* grad, float T,
+                             float* out, hipStream_t s);
 // out[c, r] = in[r, c] for r < R, 0 for R <= r < Rp; c < C.
 hipError_t launch_transpose(int elem_bytes, const void* in, int64_t R, int64_t C,
                             int64_t ldi, void* out, int64_t Rp, int64_t ldo,
@@ -132,8 +142,7 @@ struct LogitsArgs {
   float inv_T;
   float* row_lse;       // [N] forward output, backward input
   float* row_kl;        // [N] forward output
-  const float* grad;    // backward: upstream scalar g (NULL means 1)
-  float coef_base;      // backward: 1 / (N T)
+  const float* scale;   // backward: device scalar g / (N_kept T)
 };
 hipError_t launch_logits_fwd(int dtype, const LogitsArgs& a, hipStream_t s);
 hipError_t launch_logits_bwd(int dtype, const LogitsArgs& a, hipStream_t s);

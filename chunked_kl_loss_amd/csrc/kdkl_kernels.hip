@@ -61,6 +61,7 @@ __global__ __launch_bounds__(64) void teacher_prep_kernel(TeacherArgs a) {
   const int lane = threadIdx.x;
   const int K = a.K;
   const int64_t g = (a.r0 + row) * (int64_t)K;
+  const bool keep = a.ids[g] != kIgnoreId;  // an ignored row's teacher is never used
   constexpr int MAXE = 1024 / 64;
   float av[MAXE];
   int32_t iv[MAXE];
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(64) void teacher_prep_kernel(TeacherArgs a) {
     const int k = lane + 64 * j;
     if (k < K) {
       const float lp = av[j] - lse;
-      const float p = fast_exp(lp);
+      const float p = keep ? fast_exp(lp) : 0.f;
       ent += p * lp;
       // rank of (id, k) in ascending id order, ties by position
       int rank = 0;
@@ -107,7 +108,10 @@ __global__ __launch_bounds__(64) void teacher_prep_kernel(TeacherArgs a) {
     }
   }
   for (int o = 32; o > 0; o >>= 1) ent += shfl_xor(ent, o);
-  if (lane == 0) a.erow[row] = ent;
+  if (lane == 0) {
+    a.erow[row] = keep ? ent : 0.f;
+    a.keep[row] = keep ? 1.f : 0.f;
+  }
   __syncthreads();
   for (int t = lane; t <= a.n_vt; t += 64) {
     const int64_t bound = (int64_t)t * kVocabTile;
@@ -159,7 +163,7 @@ __global__ __launch_bounds__(256) void merge_kernel(MergeArgs a) {
   if (lane == 0) {
     const float lse = m + fast_log(s);
     a.row_lse[row] = lse;
-    a.row_kl[row] = a.erow[row] - gsum + lse;
+    a.row_kl[row] = a.keep[row] != 0.f ? a.erow[row] - gsum + lse : 0.f;
   }
 }
 
@@ -170,23 +174,63 @@ hipError_t launch_merge(const MergeArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// Loss: (1/N) sum_i KL_i, fp64 accumulation in a fixed order.
+// Loss: sum_i KL_i / N_kept, fp64 accumulation in a fixed order (ignored
+// positions have KL 0 and are not counted); and the backward's scale
+// g / (N_kept T). One workgroup; the count reads each row's first id.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void loss_kernel(const float* row_kl, int64_t N, float* loss) {
-  __shared__ double red[1024];
-  double acc = 0.0;
-  for (int64_t i = threadIdx.x; i < N; i += 1024) acc += (double)row_kl[i];
-  red[threadIdx.x] = acc;
+__device__ __forceinline__ void block_sum2(double& a, long long& c) {
+  __shared__ double ra[1024];
+  __shared__ long long rc[1024];
+  ra[threadIdx.x] = a;
+  rc[threadIdx.x] = c;
   __syncthreads();
   for (int w = 512; w > 0; w >>= 1) {
-    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    if ((int)threadIdx.x < w) {
+      ra[threadIdx.x] += ra[threadIdx.x + w];
+      rc[threadIdx.x] += rc[threadIdx.x + w];
+    }
     __syncthreads();
   }
-  if (threadIdx.x == 0) loss[0] = (float)(red[0] / (double)N);
+  a = ra[0];
+  c = rc[0];
 }
 
-hipError_t launch_loss(const float* row_kl, int64_t N, float* loss, hipStream_t s) {
-  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(1024), 0, s, row_kl, N, loss);
+__global__ __launch_bounds__(1024) void loss_kernel(const float* row_kl, const int32_t* ids, int K, int64_t N,
+                                                    float* loss) {
+  double acc = 0.0;
+  long long kept = 0;
+  // independent strided reads: unrolled so that many are in flight at once
+#pragma unroll 8
+  for (int64_t i = threadIdx.x; i < N; i += 1024) {
+    acc += (double)row_kl[i];
+    kept += ids[i * K] != kIgnoreId;
+  }
+  block_sum2(acc, kept);
+  if (threadIdx.x == 0) loss[0] = (float)(acc / (double)kept);  // NaN when nothing is kept
+}
+
+hipError_t launch_loss(const float* row_kl, const int32_t* ids, int K, int64_t N, float* loss,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(loss_kernel, dim3(1), dim3(1024), 0, s, row_kl, ids, K, N, loss);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(1024) void grad_scale_kernel(const int32_t* ids, int K, int64_t N, const float* grad,
+                                                          float T, float* out) {
+  double unused = 0.0;
+  long long kept = 0;
+#pragma unroll 8
+  for (int64_t i = threadIdx.x; i < N; i += 1024) kept += ids[i * K] != kIgnoreId;
+  block_sum2(unused, kept);
+  if (threadIdx.x == 0) {
+    const double g = grad ? (double)grad[0] : 1.0;
+    out[0] = kept ? (float)(g / ((double)kept * (double)T)) : 0.f;
+  }
+}
+
+hipError_t launch_grad_scale(const int32_t* ids, int K, int64_t N, const float* grad, float T, float* out,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(grad_scale_kernel, dim3(1), dim3(1024), 0, s, ids, K, N, grad, T, out);
   return hipGetLastError();
 }
 
@@ -371,6 +415,33 @@ __device__ __forceinline__ int hit_slot(int id, int V, int m0, int wm, int lane)
   return (r >> 5) * 16 + ((rin >> 3) << 2) + (rin & 3);
 }
 
+#ifndef KDKL_EPI_NT
+#define KDKL_EPI_NT 1
+#endif
+// Epilogue streams written (dZ chunk, dW) or read once per launch (old dW):
+// far larger than the caches, so they go out with the nontemporal hint.
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_nt_t;
+__device__ __forceinline__ void store16_stream(void* p, uint4 v) {
+  if (KDKL_EPI_NT)
+    __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, (u32x4_t*)p);
+  else
+    *(uint4*)p = v;
+}
+__device__ __forceinline__ void store16_stream(float* p, float4 v) {
+  if (KDKL_EPI_NT)
+    __builtin_nontemporal_store(f32x4_nt_t{v.x, v.y, v.z, v.w}, (f32x4_nt_t*)p);
+  else
+    *(float4*)p = v;
+}
+__device__ __forceinline__ float4 load16_stream(const float* p) {
+  if (KDKL_EPI_NT) {
+    const f32x4_nt_t v = __builtin_nontemporal_load((const f32x4_nt_t*)p);
+    return make_float4(v.x, v.y, v.z, v.w);
+  }
+  return *(const float4*)p;
+}
+
 template <class G, int ES, int EPI>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)[G::MB][G::NB], const Tile& t,
                                               char* smem, const int (&hit_lo)[G::NB],
@@ -450,20 +521,22 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
   } else if constexpr (EPI == EPI_DZ) {
     // dZ = coef * (softmax(s) - teacher) for the tile, written to the chunk
     // buffers token-major (dz_cv [Cp, Vp]) and vocabulary-major (dz_vc [Vp, Cp]).
-    const float g = p.grad ? p.grad[0] : 1.0f;
-    const float coef = g * p.coef_base;
+    // coef = g / (N_kept T); an ignored position's column is zero (its
+    // teacher mass is zero as well).
+    const float coef = p.scale[0];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int col = n0 + wn * G::WN + nb * 32 + (lane & 31);
       const bool cval = col < p.N;
       const float lse = cval ? p.row_lse[col] : 0.f;
+      const float kc = cval ? p.keep[col] : 0.f;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + acc_row<G>(wm, mb, r, lane);
           const float q = fast_exp(acc[mb][nb][r] * p.inv_T - lse);
-          acc[mb][nb][r] = (row < p.V && cval) ? q : 0.f;
+          acc[mb][nb][r] = (row < p.V && cval) ? q * kc : 0.f;
         }
       for (int h = hit_lo[nb]; h < hit_hi[nb]; ++h) {
         const int slot = hit_slot<G>(p.sids[(int64_t)col * p.K + h], p.V, m0, wm, lane);
@@ -508,7 +581,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
 #pragma unroll 4
         for (int j = tid; j < 128 * 32; j += NT) {
           const int i = j >> 5, c = j & 31;
-          *(uint4*)(cv + (int64_t)(nb0 + i) * p.Vp + m0 + c * 8) = *(const uint4*)(T + i * kDzPitch + c * 8);
+          store16_stream(cv + (int64_t)(nb0 + i) * p.Vp + m0 + c * 8, *(const uint4*)(T + i * kDzPitch + c * 8));
         }
         // vocabulary-major rows: 256 bytes of tokens each (only for the
         // generic path, whose dW product needs K-contiguous operands)
@@ -587,7 +660,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
         for (int u = 0; u < ITER; ++u) {
           const int j = u * NT + tid;
           const int row = min(m0 + part * PR + j / C4, p.M - 1), col = min(n0 + (j % C4) * 4, p.N - 4);
-          o[u] = *(const float4*)(p.out + (int64_t)row * p.ldo + col);
+          o[u] = load16_stream(p.out + (int64_t)row * p.ldo + col);
         }
       }
     };
@@ -614,8 +687,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
         const int row = m0 + part * PR + r, col = n0 + c4 * 4;
         if (row < p.M && col < p.N) {
           const float4 v = *(const float4*)(F + r * PITCH + c4 * 4);
-          *(float4*)(p.out + (int64_t)row * p.ldo + col) =
-              make_float4(o[u].x + v.x, o[u].y + v.y, o[u].z + v.z, o[u].w + v.w);
+          store16_stream(p.out + (int64_t)row * p.ldo + col,
+                         make_float4(o[u].x + v.x, o[u].y + v.y, o[u].z + v.z, o[u].w + v.w));
         }
       }
       if (part + 1 < BM / PR) load_old(part + 1);

@@ -12,7 +12,9 @@
 //             gamma_i = sum_k p_ik z_i[id_ik] / T.
 //   backward: dZ_iv = g/(N T) (exp(z_iv / T - lse_i) - sum_k p_ik [v = id_ik]).
 // An id outside [0, V) adds nothing to gamma or to the gradient (its teacher
-// mass is dropped) and is never dereferenced.
+// mass is dropped) and is never dereferenced. A position whose first teacher
+// id is -1 is ignored: KL 0 and a zero gradient row; the mean and the
+// gradient scale count only kept positions.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -226,6 +228,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void logits_fwd_kernel(LogitsAr
   constexpr int VEC = Elem<TE>::kVec;
   TeacherRow<TE, KPL> t;
   t.load(a, row, lane);
+  const bool keep = a.ids[row * a.K] != kIgnoreId;
   float gam = 0.f;
 #pragma unroll
   for (int j = 0; j < KPL; ++j) gam += t.ok[j] ? t.p[j] * t.z[j] : 0.f;
@@ -264,7 +267,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void logits_fwd_kernel(LogitsAr
   if (lane == 0) {
     const float lse = (acc.m + log2_hw(acc.s)) * kLn2;
     a.row_lse[row] = lse;
-    a.row_kl[row] = t.e - gam + lse;
+    a.row_kl[row] = keep ? t.e - gam + lse : 0.f;
   }
 }
 
@@ -291,7 +294,8 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void logits_bwd_kernel(LogitsAr
   // (dZ may be Z).
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  const float coef = (a.grad ? a.grad[0] : 1.f) * a.coef_base;
+  const bool keep = a.ids[row * a.K] != kIgnoreId;
+  const float coef = keep ? a.scale[0] : 0.f;  // an ignored row's gradient is zero
   const float c = kLog2e * a.inv_T;
   const float lse2 = a.row_lse[row] * kLog2e;
   const int64_t start = row * a.V;
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void logits_bwd_kernel(LogitsAr
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
   for (int j = 0; j < KPL; ++j) {
-    if (lane + 64 * j < a.K && t.ok[j]) {
+    if (keep && lane + 64 * j < a.K && t.ok[j]) {
       float mass = 0.f;  // duplicates of an id add their mass
       for (int q = 0; q < a.K; ++q) mass += s_id[w][q] == t.id[j] ? s_p[w][q] : 0.f;
       Elem<TE>::store(dr + t.id[j], coef * (exp2_hw(t.z[j] * c - lse2) - mass));

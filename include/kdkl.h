@@ -27,7 +27,8 @@
  * temperature divides both teacher and student logits, and no T^2 factor is
  * applied; the reduction is the mean over the N positions.
  *
- * Gradient (with upstream scalar g = dL_total/dloss):
+ * Gradient (with upstream scalar g = dL_total/dloss; N counts the kept
+ * positions, see "Ignored positions" below):
  *     dZ_i = g / (N T) * (q_i - scatter(ids_i, p_i))     [V]
  *     dH   = dZ W        dW = dZ^T H
  *
@@ -45,6 +46,15 @@
  *   - Preconditions not checked: ids of a row distinct (duplicates add their
  *     mass) and in [0, V). An id outside [0, V) never faults; its teacher mass
  *     is dropped from the loss and gradient.
+ *   - Ignored positions: a position whose FIRST teacher id is -1 has no
+ *     teacher target (padding, packing boundaries). It adds nothing: its
+ *     per-row KL is 0, its gradient row (dZ, hence dH) is 0, and the mean
+ *     and the gradient scale count only the kept positions. With no kept
+ *     position the loss is NaN and every gradient is 0. The rest of an
+ *     ignored row's ids and logits are never used. This is a reading: the
+ *     pages only mention that sequence packing was studied [P1 "Making
+ *     knowledge distillation cheap enough to run at scale", section "The
+ *     resulting student model"].
  *   - Results are bitwise reproducible run to run (fixed reduction orders, no
  *     floating-point atomics).
  */
@@ -59,6 +69,8 @@ extern "C" {
 #endif
 
 #define KDKL_ABI_VERSION 1
+/* Bytes of device workspace kdkl_logits_backward needs (any N, V, K). */
+#define KDKL_LOGITS_BWD_WORKSPACE 256
 
 typedef enum {
   KDKL_OK = 0,
@@ -91,7 +103,8 @@ kdkl_status kdkl_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K,
  *   H [N, d] dtype, W [V, d] dtype, topk_ids [N, K] int32, topk_logits
  *   [N, K] fp32; T > 0; chunk = positions per slice (>= 1; the last slice may
  *   be short); 1 <= K <= min(V, 1024).
- * Outputs (device): loss [1] fp32 (mean KL; NaN when N == 0),
+ * Outputs (device): loss [1] fp32 (mean KL over kept positions; NaN when
+ *   none, e.g. N == 0),
  *   row_lse [N] fp32 = logsumexp_v(s_iv) (keep it for kdkl_backward),
  *   row_kl [N] fp32 per-position KL, or NULL if not wanted.
  * Workspace: >= *fwd_bytes from kdkl_workspace_size. */
@@ -130,7 +143,8 @@ kdkl_status kdkl_backward(const void* H, const void* W,
  * kdkl_logits_forward:
  *   Z [N, V] dtype (row-major, 16-byte aligned base; any V >= 1),
  *   topk_ids [N, K] int32, topk_logits [N, K] fp32, 1 <= K <= min(V, 1024),
- *   T > 0. Outputs (device): loss [1] fp32 (mean KL, NaN when N == 0),
+ *   T > 0. Outputs (device): loss [1] fp32 (mean KL over kept positions,
+ *   NaN when none),
  *   row_lse [N] = logsumexp_v(Z_iv / T) (keep it for the backward),
  *   row_kl [N] per-position KL (required: the loss is reduced from it). */
 kdkl_status kdkl_logits_forward(const void* Z, const int32_t* topk_ids,
@@ -138,16 +152,18 @@ kdkl_status kdkl_logits_forward(const void* Z, const int32_t* topk_ids,
                                 int32_t K, float T, int dtype, float* loss,
                                 float* row_lse, float* row_kl, void* stream);
 /* kdkl_logits_backward: writes dZ [N, V] in Z's dtype,
- *   dZ_i = g / (N T) * (softmax(Z_i / T) - scatter(ids_i, p_i)),
- * with g read from the device scalar grad_loss (NULL means 1) and row_lse
- * the forward's output for the same inputs. dZ may be Z itself (the gradient
- * then overwrites the logits in place); otherwise the two must not overlap.
- * dZ must be 16-byte aligned. */
+ *   dZ_i = g / (N_kept T) * (softmax(Z_i / T) - scatter(ids_i, p_i))
+ * (zero rows for ignored positions), with g read from the device scalar
+ * grad_loss (NULL means 1) and row_lse the forward's output for the same
+ * inputs. dZ may be Z itself (the gradient then overwrites the logits in
+ * place); otherwise the two must not overlap. dZ and the workspace (at least
+ * KDKL_LOGITS_BWD_WORKSPACE bytes, caller-owned) must be 16-byte aligned. */
 kdkl_status kdkl_logits_backward(const void* Z, const int32_t* topk_ids,
                                  const float* topk_logits, int64_t N, int64_t V,
                                  int32_t K, float T, int dtype,
                                  const float* row_lse, const float* grad_loss,
-                                 void* dZ, void* stream);
+                                 void* dZ, void* workspace, size_t workspace_bytes,
+                                 void* stream);
 /* ---- measurement aid: per-kernel timing with HIP events ------------------
  * Between kdkl_profile_begin() and kdkl_profile_end(), every kernel launched
  * by the compute calls is bracketed by two HIP events recorded on

@@ -183,10 +183,10 @@ def lfwd(lib, **kw):
 
 def lbwd(lib, **kw):
     a = dict(Z=FAKE, ids=FAKE, lg=FAKE, N=64, V=1000, K=8, T=1.0, dt=L.KDKL_BF16, lse=FAKE, g=None,
-             dZ=FAKE, stream=None)
+             dZ=FAKE, ws=FAKE, wsb=256, stream=None)
     a.update(kw)
     return lib.kdkl_logits_backward(a["Z"], a["ids"], a["lg"], a["N"], a["V"], a["K"], a["T"],
-                                    a["dt"], a["lse"], a["g"], a["dZ"], a["stream"])
+                                    a["dt"], a["lse"], a["g"], a["dZ"], a["ws"], a["wsb"], a["stream"])
 
 
 @pytest.mark.parametrize("call", [lfwd, lbwd], ids=["logits_forward", "logits_backward"])
@@ -215,8 +215,11 @@ def test_logits_output_pointers_checked(lib):
     assert lfwd(lib, kl=None) == NULL
     assert lbwd(lib, dZ=None) == NULL
     assert lbwd(lib, dZ=FAKE + 8) == ALIGN
+    assert lbwd(lib, ws=None) == NULL
+    assert lbwd(lib, ws=FAKE + 4) == ALIGN
+    assert lbwd(lib, wsb=255) == WORKSPACE
     # nothing to do for N == 0 on the backward: returns before any HIP call
-    assert lbwd(lib, N=0, Z=None, ids=None, lg=None, lse=None, dZ=None) == OK
+    assert lbwd(lib, N=0, Z=None, ids=None, lg=None, lse=None, dZ=None, ws=None, wsb=0) == OK
 
 
 def test_logits_binding_refuses_cpu_tensors():

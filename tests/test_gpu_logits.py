@@ -148,6 +148,22 @@ def test_logits_autograd_function():
     assert abs(loss.item() - oracle.logits_forward(Z, ids, lg, 1.5)["loss"]) <= 1e-4
 
 
+def test_logits_ignored_positions():
+    print("case logits ignored positions", flush=True)
+    Z, ids, lg = _problem(torch.bfloat16, 150, 3003, 50, seed=8)
+    rows = np.arange(0, 150, 4)
+    ids[rows, 0] = -1
+    ids[rows[0], 1:] = 10 ** 9  # never used
+    lg[rows[1]] = float("nan")  # never used
+    got = _run(Z, ids, lg, 1.2, 0.8)
+    assert np.all(got["row_kl"][rows] == 0.0) and np.all(got["dZ"][rows] == 0.0)
+    _check(got, Z, ids, lg, 1.2, 0.8, "bf16", "logits ignored positions")
+    ids_all = ids.clone()
+    ids_all[:, 0] = -1
+    got = _run(Z, ids_all, lg, 1.0)
+    assert math.isnan(got["loss"]) and not np.any(got["dZ"])
+
+
 def test_logits_full_size_gptoss20b_32k():
     """The 32K-position gpt-oss-like workload (N=32768, V=201088, K=100, bf16)
     with Z = H W^T computed on the device: sampled rows against the oracle and

@@ -172,3 +172,39 @@ def test_temperature_identity_exact_for_T2():
     b = run_gpu(x1, 1.0, w.chunk)
     assert abs(a["loss"] - b["loss"]) <= 1e-6 * abs(a["loss"])
     assert maxrel(a["dH"], b["dH"] / 2.0) <= 1e-2
+
+
+def _mark_ignored(x, rows):
+    """First id -1 marks an ignored position; the rest of such a row is
+    garbage that must never be used."""
+    ids = x["ids"].clone()
+    lg = x["logits"].clone()
+    ids[rows, 0] = -1
+    ids[rows[0], 1:] = 10 ** 9
+    lg[rows[1]] = float("nan")
+    return dict(x, ids=ids, logits=lg)
+
+
+@pytest.mark.parametrize("name,over,seed", [
+    ("tiny_fp32", dict(N=90, chunk=32), 31),
+    ("small_bf16", dict(N=300, d=576, V=3001, K=20, chunk=128, T=1.3), 32),
+])
+def test_ignored_positions(name, over, seed):
+    w, x = _inputs(name, over, seed)
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(w.N, size=w.N // 4, replace=False))
+    xm = _mark_ignored(x, rows)
+    print(f"case ignored positions {name}: N={w.N} ignored={len(rows)}", flush=True)
+    got = run_gpu(xm, w.T, w.chunk, g=0.9)
+    ref = oracle.loss_and_grads(xm["H"], xm["W"], xm["ids"], xm["logits"], w.T, g=0.9)
+    assert np.all(got["row_kl"][rows] == 0.0) and np.all(got["dH"][rows] == 0.0)
+    assert_parity(got, ref, w.dtype, f"ignored {name}")
+
+
+def test_all_positions_ignored():
+    w, x = _inputs("small_bf16", dict(N=64, d=256, V=2000, K=8, chunk=32), 33)
+    xm = _mark_ignored(x, np.arange(w.N))
+    print("case all positions ignored", flush=True)
+    got = run_gpu(xm, w.T, w.chunk)
+    assert math.isnan(got["loss"])
+    assert not np.any(got["dH"]) and not np.any(got["dW"])
