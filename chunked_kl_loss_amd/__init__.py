@@ -29,6 +29,9 @@ __all__ = [
     "logits_backward",
     "ForwardChunkedKLLoss",
     "forward_chunked_kl_loss",
+    "dense_sizes",
+    "dense_forward",
+    "dense_backward",
     "profile_begin",
     "profile_end",
     "KdklError",
@@ -228,6 +231,56 @@ class ForwardChunkedKLLoss(torch.autograd.Function):
 def forward_chunked_kl_loss(Z, ids, logits, T: float = 1.0):
     """Mean over positions of KL(teacher top-K || softmax(Z / T)), differentiable in Z."""
     return ForwardChunkedKLLoss.apply(Z, ids, logits, T)
+
+
+def dense_sizes(N: int, d: int, V: int, K: int, dtype: torch.dtype) -> Tuple[int, int, int]:
+    """(forward workspace, saved grids, backward workspace) bytes of the dense path."""
+    f, sv, b = C.c_size_t(), C.c_size_t(), C.c_size_t()
+    code = KDKL_BF16 if dtype == torch.bfloat16 else KDKL_F32
+    check(_load().kdkl_dense_sizes(N, d, V, K, code, C.byref(f), C.byref(sv), C.byref(b)),
+          "kdkl_dense_sizes")
+    return f.value, sv.value, b.value
+
+
+def dense_forward(H, W, ids, logits, T: float, *, saved=None, loss=None, row_lse=None,
+                  row_kl=None, workspace=None, stream=None):
+    """The pages' dense baseline (``kdkl_dense_forward``); returns (loss, row_lse,
+    row_kl, saved) where ``saved`` holds the two full grids for the backward."""
+    _need_gpu(H, W, ids, logits)
+    N, d, V, K = _check_shapes(H, W, ids, logits)
+    dev = H.device
+    fb, sb, _ = dense_sizes(N, d, V, K, H.dtype)
+    loss = torch.empty(1, dtype=torch.float32, device=dev) if loss is None else loss
+    row_lse = torch.empty(N, dtype=torch.float32, device=dev) if row_lse is None else row_lse
+    row_kl = torch.empty(N, dtype=torch.float32, device=dev) if row_kl is None else row_kl
+    saved = torch.empty(sb, dtype=torch.uint8, device=dev) if saved is None else saved
+    workspace = torch.empty(fb, dtype=torch.uint8, device=dev) if workspace is None else workspace
+    check(_load().kdkl_dense_forward(_ptr(H), _ptr(W), _ptr(ids), _ptr(logits), N, d, V, K, float(T),
+                                     _dtype_code(H), _ptr(loss), _ptr(row_lse), _ptr(row_kl),
+                                     _ptr(saved), saved.numel(), _ptr(workspace), workspace.numel(),
+                                     _stream(dev, stream)),
+          "kdkl_dense_forward")
+    return loss, row_lse, row_kl, saved
+
+
+def dense_backward(H, W, ids, logits, T: float, saved, grad_loss=None, *, dH=None, dW=None,
+                   accumulate_dW: bool = False, workspace=None, stream=None):
+    """Gradients of the dense baseline from its saved grids (``kdkl_dense_backward``)."""
+    _need_gpu(H, W, ids, logits, saved, grad_loss)
+    N, d, V, K = _check_shapes(H, W, ids, logits)
+    dev = H.device
+    _, _, bb = dense_sizes(N, d, V, K, H.dtype)
+    dH = torch.empty_like(H) if dH is None else dH
+    dW = torch.empty((V, d), dtype=torch.float32, device=dev) if dW is None else dW
+    if grad_loss is not None and grad_loss.dtype != torch.float32:
+        raise TypeError("grad_loss must be float32")
+    workspace = torch.empty(bb, dtype=torch.uint8, device=dev) if workspace is None else workspace
+    check(_load().kdkl_dense_backward(_ptr(H), _ptr(W), _ptr(ids), _ptr(logits), N, d, V, K,
+                                      float(T), _dtype_code(H), _ptr(saved), saved.numel(),
+                                      _ptr(grad_loss), _ptr(dH), _ptr(dW), int(bool(accumulate_dW)),
+                                      _ptr(workspace), workspace.numel(), _stream(dev, stream)),
+          "kdkl_dense_backward")
+    return dH, dW
 
 
 def profile_begin():

@@ -53,6 +53,12 @@ SIGNATURES = {
                                       _P, _P, _P, _P]),
     "kdkl_logits_backward": (C.c_int, [_P, _P, _P, _I64, _I64, _I32, C.c_float, C.c_int,
                                        _P, _P, _P, _P, C.c_size_t, _P]),
+    "kdkl_dense_sizes": (C.c_int, [_I64, _I64, _I64, _I32, C.c_int, C.POINTER(C.c_size_t),
+                                   C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
+    "kdkl_dense_forward": (C.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, C.c_float, C.c_int,
+                                     _P, _P, _P, _P, C.c_size_t, _P, C.c_size_t, _P]),
+    "kdkl_dense_backward": (C.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, C.c_float, C.c_int,
+                                      _P, C.c_size_t, _P, _P, _P, C.c_int, _P, C.c_size_t, _P]),
     "kdkl_profile_begin": (C.c_int, []),
     "kdkl_profile_end": (C.c_int, [C.POINTER(KernelStat), C.c_int, C.POINTER(C.c_int)]),
 }

@@ -20,7 +20,8 @@ const char* kernel_name(int id) {
   static const char* names[K_COUNT] = {
       "teacher_prep", "fwd_gemm_lse", "split_merge", "loss_reduce", "transpose_w",
       "transpose_h",  "dz_gemm",      "dh_gemm",     "dh_reduce",   "dw_gemm",
-      "logits_fwd",   "logits_bwd",   "grad_scale"};
+      "logits_fwd",   "logits_bwd",   "grad_scale",  "dense_gemm",  "dense_student",
+      "dense_teacher", "dense_kl",    "dense_grad"};
   return (id >= 0 && id < K_COUNT) ? names[id] : "?";
 }
 
@@ -289,6 +290,49 @@ kdkl_status kdkl_forward(const void* H, const void* W, const int32_t* ids, const
   return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
 }
 
+// dH and dW (+)= of one chunk of rows [r0, r0 + rows) from its dZ in the
+// backward workspace (token-major; vocabulary-major too on the generic path),
+// W^T and H_c^T: dH_c = dZ_c W split over the vocabulary and summed in a fixed
+// order, dW (+)= dZ_c^T H_c.
+static hipError_t chunk_products(const Plan& P, int dtype, char* ws, int64_t r0, int rows, void* dH, float* dW,
+                               bool accumulate, hipStream_t s) {
+  const int64_t d = P.d, V = P.V;
+  const int64_t rows_pad = round_up(rows, kTokenTile);
+  const double fl = 2.0 * rows * (double)V * d;
+  // dH_c = dZ_c W  (split over the vocabulary, then a fixed-order sum)
+  GemmArgs h;
+  memset(&h, 0, sizeof(h));
+  h.A = ws + P.b_dzcv; h.lda = P.Vp; h.a_layout = LAYOUT_KC;
+  h.B = ws + P.b_wt; h.ldb = P.Vp; h.b_layout = LAYOUT_KC;
+  h.M = rows; h.N = (int)d; h.k_end = P.Vp; h.k_split = P.dh_ksplit;
+  h.tiles_m = (int)((rows + 255) / 256); h.tiles_n = (int)((d + P.dtile - 1) / P.dtile); h.bn = P.dtile;
+  h.splits = (int)((P.Vp + P.dh_ksplit - 1) / P.dh_ksplit);
+  h.out = (float*)(ws + P.b_dhpart); h.ldo = d; h.Cp = P.Cp;
+  const int splits = h.splits;
+  hipError_t e = timed(K_DH_GEMM, fl, ((double)V * rows + (double)V * d) * P.es + 4.0 * splits * rows * d, s,
+            [&] { return launch_gemm(dtype, EPI_DH, h, s); });
+  if (e != hipSuccess) return e;
+  void* dHc = (char*)dH + r0 * d * P.es;
+  e = timed(K_DH_REDUCE, 0.0, 4.0 * splits * rows * d + (double)rows * d * P.es, s, [&] {
+    return launch_dh_reduce(dtype, (const float*)(ws + P.b_dhpart), splits, rows, d, P.Cp, dHc, s);
+  });
+  if (e != hipSuccess) return e;
+  // dW (+)= dZ_c^T H_c
+  GemmArgs w;
+  memset(&w, 0, sizeof(w));
+  if (P.fast) {
+    w.A = ws + P.b_dzcv; w.lda = P.Vp; w.a_layout = LAYOUT_MC; w.a_krows = P.Cp; w.a_mcols = P.Vp;
+  } else {
+    w.A = ws + P.b_dzvc; w.lda = P.Cp; w.a_layout = LAYOUT_KC;
+  }
+  w.B = ws + P.b_ht; w.ldb = P.Cp; w.b_layout = LAYOUT_KC;
+  w.M = (int)V; w.N = (int)d; w.k_end = rows_pad; w.k_split = rows_pad;
+  w.tiles_m = (int)P.n_vt; w.tiles_n = (int)((d + P.dtile - 1) / P.dtile); w.splits = 1; w.bn = P.dtile;
+  w.out = dW; w.ldo = d; w.accumulate = accumulate ? 1 : 0;
+  return timed(K_DW_GEMM, fl, ((double)V * rows + (double)rows * d) * P.es + 8.0 * V * d, s,
+            [&] { return launch_gemm(dtype, EPI_DW, w, s); });
+}
+
 kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, const float* lg, int64_t N,
                           int64_t d, int64_t V, int32_t K, float T, int64_t chunk, int dtype,
                           const float* row_lse, const float* grad_loss, void* dH, float* dW,
@@ -339,38 +383,7 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
     e = timed(K_DZ_GEMM, fl, ((double)V + rows) * d * P.es + (P.fast ? 1.0 : 2.0) * rows * (double)V * P.es, s,
               [&] { return launch_gemm(dtype, EPI_DZ, g, s); });
     if (e != hipSuccess) break;
-    // dH_c = dZ_c W  (split over the vocabulary, then a fixed-order sum)
-    GemmArgs h;
-    memset(&h, 0, sizeof(h));
-    h.A = ws + P.b_dzcv; h.lda = P.Vp; h.a_layout = LAYOUT_KC;
-    h.B = ws + P.b_wt; h.ldb = P.Vp; h.b_layout = LAYOUT_KC;
-    h.M = rows; h.N = (int)d; h.k_end = P.Vp; h.k_split = P.dh_ksplit;
-    h.tiles_m = (int)((rows + 255) / 256); h.tiles_n = (int)((d + P.dtile - 1) / P.dtile); h.bn = P.dtile;
-    h.splits = (int)((P.Vp + P.dh_ksplit - 1) / P.dh_ksplit);
-    h.out = (float*)(ws + P.b_dhpart); h.ldo = d; h.Cp = P.Cp;
-    const int splits = h.splits;
-    e = timed(K_DH_GEMM, fl, ((double)V * rows + (double)V * d) * P.es + 4.0 * splits * rows * d, s,
-              [&] { return launch_gemm(dtype, EPI_DH, h, s); });
-    if (e != hipSuccess) break;
-    void* dHc = (char*)dH + r0 * d * P.es;
-    e = timed(K_DH_REDUCE, 0.0, 4.0 * splits * rows * d + (double)rows * d * P.es, s, [&] {
-      return launch_dh_reduce(dtype, (const float*)(ws + P.b_dhpart), splits, rows, d, P.Cp, dHc, s);
-    });
-    if (e != hipSuccess) break;
-    // dW (+)= dZ_c^T H_c
-    GemmArgs w;
-    memset(&w, 0, sizeof(w));
-    if (P.fast) {
-      w.A = ws + P.b_dzcv; w.lda = P.Vp; w.a_layout = LAYOUT_MC; w.a_krows = P.Cp; w.a_mcols = P.Vp;
-    } else {
-      w.A = ws + P.b_dzvc; w.lda = P.Cp; w.a_layout = LAYOUT_KC;
-    }
-    w.B = ws + P.b_ht; w.ldb = P.Cp; w.b_layout = LAYOUT_KC;
-    w.M = (int)V; w.N = (int)d; w.k_end = rows_pad; w.k_split = rows_pad;
-    w.tiles_m = (int)P.n_vt; w.tiles_n = (int)((d + P.dtile - 1) / P.dtile); w.splits = 1; w.bn = P.dtile;
-    w.out = dW; w.ldo = d; w.accumulate = (r0 > 0 || accumulate_dW) ? 1 : 0;
-    e = timed(K_DW_GEMM, fl, ((double)V * rows + (double)rows * d) * P.es + 8.0 * V * d, s,
-              [&] { return launch_gemm(dtype, EPI_DW, w, s); });
+    e = chunk_products(P, dtype, ws, r0, rows, dH, dW, r0 > 0 || accumulate_dW, s);
   }
   return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
 }
@@ -426,6 +439,134 @@ kdkl_status kdkl_logits_backward(const void* Z, const int32_t* ids, const float*
                        [&] { return launch_grad_scale(ids, K, N, grad_loss, T, (float*)workspace, s); });
   if (e == hipSuccess) e = timed(K_LOGITS_BWD, 0.0, (double)N * (2.0 * V * es + K * 8.0 + 4.0), s,
                        [&] { return launch_logits_bwd(dtype, a, s); });
+  return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
+}
+
+// ------------------------------ dense KL ------------------------------------
+// The pages' correctness baseline: the full student log-probability grid and
+// the full teacher probability grid are built, compared grid-wide and kept
+// for the backward pass. The GEMMs are those of the fused path run over one
+// chunk of all N rows (the projection in raw-store mode).
+
+struct DensePlan {
+  Plan P;                      // chunk = N
+  size_t f_z, f_rowkl, f_bytes;  // forward workspace: the logits [Cp, Vp]
+  size_t s_logq, s_p, s_bytes;   // saved grids: logq and P, [N, Vp] fp32 each
+};
+
+static kdkl_status make_dense_plan(int64_t N, int64_t d, int64_t V, int32_t K, int dtype, DensePlan* D) {
+  kdkl_status st = make_plan(N, d, V, K, N > 0 ? N : 1, dtype, &D->P);
+  if (st != KDKL_OK) return st;
+  const Plan& P = D->P;
+  int64_t z, g;
+  size_t cur = 0;
+  bool ok = mul_ok(P.Cp, P.Vp, &z) && mul_ok(z, P.es, &z);
+  ok &= region(&cur, z, &D->f_z) && region(&cur, (N > 0 ? N : 1) * 4, &D->f_rowkl);
+  D->f_bytes = cur;
+  cur = 0;
+  ok &= mul_ok(N > 0 ? N : 1, P.Vp, &g) && mul_ok(g, 4, &g);
+  ok &= region(&cur, g, &D->s_logq) && region(&cur, g, &D->s_p);
+  D->s_bytes = cur;
+  return ok ? KDKL_OK : KDKL_ERR_OVERFLOW;
+}
+
+static DenseArgs dense_args(const DensePlan& D, const int32_t* ids, const float* lg, float T, char* saved) {
+  DenseArgs a;
+  memset(&a, 0, sizeof(a));
+  a.logq = (float*)(saved + D.s_logq); a.P = (float*)(saved + D.s_p);
+  a.ids = ids; a.logits = lg; a.N = D.P.N; a.V = D.P.V; a.ldv = D.P.Vp; a.rows_pad = D.P.Cp;
+  a.K = (int)D.P.K; a.inv_T = 1.0f / T;
+  return a;
+}
+
+kdkl_status kdkl_dense_sizes(int64_t N, int64_t d, int64_t V, int32_t K, int dtype, size_t* fwd_bytes,
+                             size_t* saved_bytes, size_t* bwd_bytes) {
+  DensePlan D;
+  kdkl_status st = make_dense_plan(N, d, V, K, dtype, &D);
+  if (st != KDKL_OK) return st;
+  if (fwd_bytes) *fwd_bytes = D.f_bytes;
+  if (saved_bytes) *saved_bytes = D.s_bytes;
+  if (bwd_bytes) *bwd_bytes = D.P.b_bytes;
+  return KDKL_OK;
+}
+
+kdkl_status kdkl_dense_forward(const void* H, const void* W, const int32_t* ids, const float* lg, int64_t N,
+                               int64_t d, int64_t V, int32_t K, float T, int dtype, float* loss, float* row_lse,
+                               float* row_kl, void* saved, size_t saved_bytes, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  DensePlan D;
+  kdkl_status st = make_dense_plan(N, d, V, K, dtype, &D);
+  if (st != KDKL_OK) return st;
+  if ((st = check_common(H, W, ids, lg, N, T)) != KDKL_OK) return st;
+  if (!loss || !saved || !workspace || (N > 0 && !row_lse)) return KDKL_ERR_NULL;
+  if (workspace_bytes < D.f_bytes || saved_bytes < D.s_bytes) return KDKL_ERR_WORKSPACE;
+  if (!aligned16(workspace) || !aligned16(saved)) return KDKL_ERR_ALIGN;
+  const Plan& P = D.P;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  float* kl = row_kl ? row_kl : (float*)(ws + D.f_rowkl);
+  hipError_t e = hipSuccess;
+  if (N > 0) {
+    // the logit grid Z = H W^T [Cp, Vp] (zero past V)
+    GemmArgs g = projection_args(P, H, W, T, 0, (int)N, ws, 0, 0, 0);
+    g.sids = nullptr; g.sp = nullptr; g.tstart = nullptr;
+    g.raw = 1; g.dz_cv = ws + D.f_z; g.dz_vc = nullptr;
+    e = timed(K_DENSE_GEMM, 2.0 * N * (double)V * d, ((double)V + N) * d * P.es + (double)N * V * P.es, s,
+              [&] { return launch_gemm(dtype, EPI_DZ, g, s); });
+    DenseArgs a = dense_args(D, ids, lg, T, (char*)saved);
+    a.Z = ws + D.f_z; a.row_lse = row_lse; a.row_kl = kl;
+    const double grid4 = (double)N * V * 4.0;
+    if (e == hipSuccess)
+      e = timed(K_DENSE_STUDENT, 0.0, 2.0 * N * (double)V * P.es + grid4, s,
+                [&] { return launch_dense_student(dtype, a, s); });
+    if (e == hipSuccess)
+      e = timed(K_DENSE_TEACHER, 0.0, grid4 + (double)N * K * 8.0, s, [&] { return launch_dense_teacher(a, s); });
+    if (e == hipSuccess)
+      e = timed(K_DENSE_KL, 0.0, 2.0 * grid4, s, [&] { return launch_dense_kl(a, s); });
+  }
+  if (e == hipSuccess)
+    e = timed(K_LOSS, 0.0, (double)N * 8.0, s, [&] { return launch_loss(kl, ids, K, N, loss, s); });
+  return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
+}
+
+kdkl_status kdkl_dense_backward(const void* H, const void* W, const int32_t* ids, const float* lg, int64_t N,
+                                int64_t d, int64_t V, int32_t K, float T, int dtype, const void* saved,
+                                size_t saved_bytes, const float* grad_loss, void* dH, float* dW,
+                                int accumulate_dW, void* workspace, size_t workspace_bytes, void* stream) {
+  DensePlan D;
+  kdkl_status st = make_dense_plan(N, d, V, K, dtype, &D);
+  if (st != KDKL_OK) return st;
+  if ((st = check_common(H, W, ids, lg, N, T)) != KDKL_OK) return st;
+  if (!dW || !workspace || !saved || (N > 0 && !dH)) return KDKL_ERR_NULL;
+  const Plan& P = D.P;
+  if (workspace_bytes < P.b_bytes || saved_bytes < D.s_bytes) return KDKL_ERR_WORKSPACE;
+  if (!aligned16(workspace) || !aligned16(saved) || !aligned16(dW) || !aligned16(dH)) return KDKL_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  hipError_t e = hipSuccess;
+  if (N == 0) {
+    if (!accumulate_dW) e = launch_zero(dW, V * d, s);
+    return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
+  }
+  e = timed(K_TRANSPOSE_W, 0.0, 2.0 * (double)V * d * P.es, s, [&] {
+      return launch_transpose((int)P.es, W, V, d, d, ws + P.b_wt, P.Vp, P.Vp, s);
+    });
+  if (e == hipSuccess)
+    e = timed(K_GRAD_SCALE, 0.0, (double)N * 4.0, s,
+              [&] { return launch_grad_scale(ids, K, N, grad_loss, T, (float*)(ws + P.b_scale), s); });
+  if (e == hipSuccess)
+    e = timed(K_TRANSPOSE_H, 0.0, 2.0 * (double)N * d * P.es, s, [&] {
+      return launch_transpose((int)P.es, H, N, d, d, ws + P.b_ht, P.Cp, P.Cp, s);
+    });
+  // dZ = g/(N_kept T) (exp(logq) - P), token-major [Cp, Vp], from the saved grids
+  DenseArgs a = dense_args(D, ids, lg, T, (char*)const_cast<void*>(saved));
+  a.dZ = ws + P.b_dzcv; a.scale = (const float*)(ws + P.b_scale);
+  if (e == hipSuccess)
+    e = timed(K_DENSE_GRAD, 0.0, 2.0 * N * (double)V * 4.0 + (double)P.Cp * P.Vp * P.es, s,
+              [&] { return launch_dense_grad(dtype, a, s); });
+  if (e == hipSuccess && !P.fast)  // the generic dW product reads dZ vocabulary-major
+    e = launch_transpose((int)P.es, ws + P.b_dzcv, P.Cp, P.Vp, P.Vp, ws + P.b_dzvc, P.Cp, P.Cp, s);
+  if (e == hipSuccess) e = chunk_products(P, dtype, ws, 0, (int)N, dH, dW, accumulate_dW != 0, s);
   return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
 }
 

@@ -28,6 +28,11 @@ enum KernelId {
   K_LOGITS_FWD,
   K_LOGITS_BWD,
   K_GRAD_SCALE,
+  K_DENSE_GEMM,
+  K_DENSE_STUDENT,
+  K_DENSE_TEACHER,
+  K_DENSE_KL,
+  K_DENSE_GRAD,
   K_COUNT
 };
 
@@ -70,6 +75,7 @@ struct GemmArgs {
   const float* row_lse;          // backward: lse of this chunk's rows
   const float* scale;            // backward: device scalar g / (N_kept * T)
   const float* keep;             // backward: keep flags of this chunk's rows [Cp]
+  int raw;                       // EPI_DZ only: store the logits z themselves (dense path)
   void* dz_cv;                   // [Cp, Vp]
   void* dz_vc;                   // [Vp, Cp]
   int64_t Vp;
@@ -145,6 +151,28 @@ struct LogitsArgs {
   const float* scale;   // backward: device scalar g / (N_kept T)
 };
 hipError_t launch_logits_fwd(int dtype, const LogitsArgs& a, hipStream_t s);
+
+// Dense KL (the pages' baseline): full student log-probability and teacher
+// probability grids, row pitch ldv (the padded vocabulary), one wavefront
+// per row.
+struct DenseArgs {
+  const void* Z;        // [rows_pad, ldv] storage dtype: the projected logits
+  float* logq;          // [N, ldv] fp32 student log-probabilities
+  float* P;             // [N, ldv] fp32 teacher probabilities, zero off the top-K
+  void* dZ;             // [rows_pad, ldv] storage dtype (backward; zero past N rows and V columns)
+  const int32_t* ids;   // [N, K]
+  const float* logits;  // [N, K]
+  int64_t N, V, ldv, rows_pad;
+  int K;
+  float inv_T;
+  float* row_lse;       // [N]
+  float* row_kl;        // [N]
+  const float* scale;   // backward: device scalar g / (N_kept T)
+};
+hipError_t launch_dense_student(int dtype, const DenseArgs& a, hipStream_t s);
+hipError_t launch_dense_teacher(const DenseArgs& a, hipStream_t s);
+hipError_t launch_dense_kl(const DenseArgs& a, hipStream_t s);
+hipError_t launch_dense_grad(int dtype, const DenseArgs& a, hipStream_t s);
 hipError_t launch_logits_bwd(int dtype, const LogitsArgs& a, hipStream_t s);
 
 }  // namespace kdkl

@@ -396,7 +396,7 @@ __device__ __forceinline__ void hit_ranges(const GemmArgs& p, const Tile& t, int
 #pragma unroll
   for (int nb = 0; nb < G::NB; ++nb) {
     const int col = t.tn * G::BN + wn * G::WN + nb * 32 + (lane & 31);
-    if (col < p.N) {
+    if (col < p.N && !p.raw) {  // raw logits (dense path): no teacher index
       lo[nb] = p.tstart[(int64_t)t.tm * p.Cp + col];
       hi[nb] = p.tstart[(int64_t)(t.tm + 1) * p.Cp + col];
     } else {
@@ -522,12 +522,23 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
     // dZ = coef * (softmax(s) - teacher) for the tile, written to the chunk
     // buffers token-major (dz_cv [Cp, Vp]) and vocabulary-major (dz_vc [Vp, Cp]).
     // coef = g / (N_kept T); an ignored position's column is zero (its
-    // teacher mass is zero as well).
-    const float coef = p.scale[0];
+    // teacher mass is zero as well). In raw mode (the dense path) the tile of
+    // logits z itself is stored (coef 1, zero outside the valid rows).
+    const float coef = p.raw ? 1.f : p.scale[0];
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int col = n0 + wn * G::WN + nb * 32 + (lane & 31);
       const bool cval = col < p.N;
+      if (p.raw) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = m0 + acc_row<G>(wm, mb, r, lane);
+            acc[mb][nb][r] = (row < p.V && cval) ? acc[mb][nb][r] : 0.f;
+          }
+        continue;
+      }
       const float lse = cval ? p.row_lse[col] : 0.f;
       const float kc = cval ? p.keep[col] : 0.f;
 #pragma unroll
@@ -614,6 +625,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
             const float v0 = acc[mb][nb][r4 * 4 + 0] * coef, v1 = acc[mb][nb][r4 * 4 + 1] * coef;
             const float v2 = acc[mb][nb][r4 * 4 + 2] * coef, v3 = acc[mb][nb][r4 * 4 + 3] * coef;
             *(float4*)(cv + (int64_t)col * p.Vp + row) = make_float4(v0, v1, v2, v3);
+            if (vc == nullptr) continue;
             vc[(int64_t)(row + 0) * p.Cp + col] = v0;
             vc[(int64_t)(row + 1) * p.Cp + col] = v1;
             vc[(int64_t)(row + 2) * p.Cp + col] = v2;

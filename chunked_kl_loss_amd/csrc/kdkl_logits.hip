@@ -129,7 +129,8 @@ struct TeacherRow {
   bool ok[KPL];
   float e;  // wavefront total
 
-  __device__ void load(const LogitsArgs& a, int64_t row, int lane) {
+  // gather = false skips reading the student logits (z stays 0)
+  __device__ void load(const LogitsArgs& a, int64_t row, int lane, bool gather = true) {
     const int K = a.K;
     const int64_t g = row * (int64_t)K;
     const TE* zr = (const TE*)a.Z + row * a.V;
@@ -146,7 +147,7 @@ struct TeacherRow {
         mx = fmaxf(mx, av[j]);
       }
       ok[j] = id[j] >= 0 && (int64_t)id[j] < a.V;
-      z[j] = ok[j] ? Elem<TE>::load(zr + id[j]) : 0.f;
+      z[j] = (gather && ok[j]) ? Elem<TE>::load(zr + id[j]) : 0.f;
     }
     mx = wave_max(mx);
     float se = 0.f;
@@ -343,6 +344,144 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void logits_bwd_kernel(LogitsAr
   }
 }
 
+// ------------------------------ dense KL ------------------------------------
+// The pages' dense baseline builds the full teacher probability grid from the
+// cached top-K and compares it with the student's full log-probability grid
+// [P1, section "Two system changes", dense KL bullet]; both grids are kept for
+// the backward pass. Rows are 16-byte aligned (pitch ldv, a multiple of 256
+// elements), so every pass streams whole vectors plus a scalar tail.
+
+template <typename TE>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void dense_student_kernel(DenseArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= a.N) return;
+  constexpr int VEC = Elem<TE>::kVec;
+  const TE* zr = (const TE*)a.Z + row * a.ldv;
+  float* lq = a.logq + row * a.ldv;
+  const int64_t nvec = a.V / VEC;
+  const int tail = (int)(a.V - nvec * VEC);
+  const float c = kLog2e * a.inv_T;
+  const uint4* vp = (const uint4*)zr;
+  OnlineLse acc;
+  for (int64_t i = lane; i < nvec; i += 64) {
+    float x[VEC];
+    Elem<TE>::unpack(load_stream(vp + i), x);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) x[j] *= c;
+    acc.add_vec(x);
+  }
+  if (lane < tail) acc.add(Elem<TE>::load(zr + nvec * VEC + lane) * c);
+  acc.wave_merge();
+  const float lse = (acc.m + log2_hw(acc.s)) * kLn2;
+  for (int64_t i = lane; i < nvec; i += 64) {
+    float x[VEC];
+    Elem<TE>::unpack(load_stream(vp + i), x);
+#pragma unroll
+    for (int q = 0; q < VEC / 4; ++q)
+      store_stream((uint4*)(lq + i * VEC) + q,
+                   make_uint4(__builtin_bit_cast(uint32_t, x[4 * q] * a.inv_T - lse),
+                              __builtin_bit_cast(uint32_t, x[4 * q + 1] * a.inv_T - lse),
+                              __builtin_bit_cast(uint32_t, x[4 * q + 2] * a.inv_T - lse),
+                              __builtin_bit_cast(uint32_t, x[4 * q + 3] * a.inv_T - lse)));
+  }
+  if (lane < tail) lq[nvec * VEC + lane] = Elem<TE>::load(zr + nvec * VEC + lane) * a.inv_T - lse;
+  if (lane == 0) a.row_lse[row] = lse;
+}
+
+template <int KPL>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void dense_teacher_kernel(DenseArgs a) {
+  __shared__ int32_t s_id[kRowsPerBlock][64 * KPL];
+  __shared__ float s_p[kRowsPerBlock][64 * KPL];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + w;
+  if (row >= a.N) return;
+  LogitsArgs la;
+  la.Z = nullptr; la.ids = a.ids; la.logits = a.logits; la.V = a.V; la.K = a.K; la.inv_T = a.inv_T;
+  TeacherRow<float, KPL> t;
+  t.load(la, row, lane, false);
+  const bool keep = a.ids[row * a.K] != kIgnoreId;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    const int k = lane + 64 * j;
+    if (k < a.K) {
+      s_id[w][k] = t.id[j];
+      s_p[w][k] = t.p[j];
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  float* pr = a.P + row * a.ldv;
+  const int64_t nvec = a.V / 4;
+  for (int64_t i = lane; i < nvec; i += 64) store_stream((uint4*)pr + i, make_uint4(0u, 0u, 0u, 0u));
+  if (lane < (int)(a.V - nvec * 4)) pr[nvec * 4 + lane] = 0.f;
+  // teacher entries after the zeros of this wavefront have been performed
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) {
+    if (keep && lane + 64 * j < a.K && t.ok[j]) {
+      float mass = 0.f;  // duplicates of an id add their mass
+      for (int q = 0; q < a.K; ++q) mass += s_id[w][q] == t.id[j] ? s_p[w][q] : 0.f;
+      pr[t.id[j]] = mass;
+    }
+  }
+}
+
+__global__ __launch_bounds__(64 * kRowsPerBlock) void dense_kl_kernel(DenseArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= a.N) return;
+  const float* pr = a.P + row * a.ldv;
+  const float* lq = a.logq + row * a.ldv;
+  const int64_t nvec = a.V / 4;
+  auto term = [](float p, float l) { return p > 0.f ? p * (log2_hw(p) * kLn2 - l) : 0.f; };
+  float kl = 0.f;
+  for (int64_t i = lane; i < nvec; i += 64) {
+    const uint4 pu = load_stream((const uint4*)pr + i), lu = load_stream((const uint4*)lq + i);
+    kl += term(__builtin_bit_cast(float, pu.x), __builtin_bit_cast(float, lu.x)) +
+          term(__builtin_bit_cast(float, pu.y), __builtin_bit_cast(float, lu.y)) +
+          term(__builtin_bit_cast(float, pu.z), __builtin_bit_cast(float, lu.z)) +
+          term(__builtin_bit_cast(float, pu.w), __builtin_bit_cast(float, lu.w));
+  }
+  if (lane < (int)(a.V - nvec * 4)) kl += term(pr[nvec * 4 + lane], lq[nvec * 4 + lane]);
+  kl = wave_sum(kl);
+  if (lane == 0) a.row_kl[row] = kl;  // an ignored row's P is zero, so its KL is 0
+}
+
+template <typename TE>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void dense_grad_kernel(DenseArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  if (row >= a.rows_pad) return;
+  constexpr int VEC = Elem<TE>::kVec;
+  uint4* out = (uint4*)((TE*)a.dZ + row * a.ldv);
+  const int64_t nvec = a.ldv / VEC;  // whole row including the zero padding
+  if (row >= a.N) {
+    for (int64_t i = lane; i < nvec; i += 64) store_stream(out + i, make_uint4(0u, 0u, 0u, 0u));
+    return;
+  }
+  const bool keep = a.ids[row * a.K] != kIgnoreId;
+  const float coef = keep ? a.scale[0] : 0.f;
+  const uint4* pr = (const uint4*)(a.P + row * a.ldv);
+  const uint4* lq = (const uint4*)(a.logq + row * a.ldv);
+  for (int64_t i = lane; i < nvec; i += 64) {
+    float y[VEC];
+#pragma unroll
+    for (int q = 0; q < VEC / 4; ++q) {
+      const uint4 pu = load_stream(pr + i * (VEC / 4) + q), lu = load_stream(lq + i * (VEC / 4) + q);
+      const float pv[4] = {__builtin_bit_cast(float, pu.x), __builtin_bit_cast(float, pu.y),
+                           __builtin_bit_cast(float, pu.z), __builtin_bit_cast(float, pu.w)};
+      const float lv[4] = {__builtin_bit_cast(float, lu.x), __builtin_bit_cast(float, lu.y),
+                           __builtin_bit_cast(float, lu.z), __builtin_bit_cast(float, lu.w)};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t v = i * VEC + 4 * q + j;
+        y[4 * q + j] = v < a.V ? coef * (exp2_hw(lv[j] * kLog2e) - pv[j]) : 0.f;
+      }
+    }
+    store_stream(out + i, Elem<TE>::pack(y));
+  }
+}
+
 }  // namespace
 
 // Slots per lane for the teacher entries: the smallest of 2, 4, 16 with
@@ -382,6 +521,48 @@ hipError_t launch_logits_bwd(int dtype, const LogitsArgs& a, hipStream_t s) {
   if (a.N <= 0) return hipSuccess;
   if (a.K < 1 || a.K > 1024) return hipErrorInvalidValue;
   return dtype == 1 ? launch_k<BwdLaunch, uint16_t>(a, s) : launch_k<BwdLaunch, float>(a, s);
+}
+
+static dim3 dense_grid(int64_t rows) { return dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)); }
+
+hipError_t launch_dense_student(int dtype, const DenseArgs& a, hipStream_t s) {
+  if (a.N <= 0) return hipSuccess;
+  if (a.ldv % 256 != 0) return hipErrorInvalidValue;
+  if (dtype == 1)
+    hipLaunchKernelGGL(dense_student_kernel<uint16_t>, dense_grid(a.N), dim3(64 * kRowsPerBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL(dense_student_kernel<float>, dense_grid(a.N), dim3(64 * kRowsPerBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_teacher(const DenseArgs& a, hipStream_t s) {
+  if (a.N <= 0) return hipSuccess;
+  if (a.K < 1 || a.K > 1024 || a.ldv % 256 != 0) return hipErrorInvalidValue;
+  const dim3 g = dense_grid(a.N), b(64 * kRowsPerBlock);
+  if (a.K <= 128)
+    hipLaunchKernelGGL(dense_teacher_kernel<2>, g, b, 0, s, a);
+  else if (a.K <= 256)
+    hipLaunchKernelGGL(dense_teacher_kernel<4>, g, b, 0, s, a);
+  else
+    hipLaunchKernelGGL(dense_teacher_kernel<16>, g, b, 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_kl(const DenseArgs& a, hipStream_t s) {
+  if (a.N <= 0) return hipSuccess;
+  if (a.ldv % 256 != 0) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(dense_kl_kernel, dense_grid(a.N), dim3(64 * kRowsPerBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_dense_grad(int dtype, const DenseArgs& a, hipStream_t s) {
+  if (a.rows_pad <= 0) return hipSuccess;
+  if (a.ldv % 256 != 0 || a.rows_pad < a.N) return hipErrorInvalidValue;
+  if (dtype == 1)
+    hipLaunchKernelGGL(dense_grad_kernel<uint16_t>, dense_grid(a.rows_pad), dim3(64 * kRowsPerBlock), 0, s, a);
+  else
+    hipLaunchKernelGGL(dense_grad_kernel<float>, dense_grid(a.rows_pad), dim3(64 * kRowsPerBlock), 0, s, a);
+  return hipGetLastError();
 }
 
 }  // namespace kdkl

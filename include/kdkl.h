@@ -164,6 +164,39 @@ kdkl_status kdkl_logits_backward(const void* Z, const int32_t* topk_ids,
                                  const float* row_lse, const float* grad_loss,
                                  void* dZ, void* workspace, size_t workspace_bytes,
                                  void* stream);
+/* ---- dense KL: the pages' correctness baseline ------------------------------
+ * The textbook computation the pages use as their correctness baseline: the
+ * full teacher probability grid is rebuilt from the cached top-K (zero
+ * elsewhere) and compared with the student's full log-probability grid; both
+ * vocabulary x position grids are kept for the backward pass [P1 "Making
+ * knowledge distillation cheap enough to run at scale", section "Two system
+ * changes", dense KL bullet]. Same loss, gradient and conventions as
+ * kdkl_forward / kdkl_backward; what differs is memory: the caller owns a
+ * `saved` buffer holding both grids in fp32 (about 8 N V bytes), plus one
+ * logit grid of workspace in each call. Useful to reproduce the pages'
+ * memory comparison, not for training.
+ *
+ * kdkl_dense_sizes: bytes of the forward workspace, of the saved grids
+ *   (written by the forward, read by the backward) and of the backward
+ *   workspace. Host-only. */
+kdkl_status kdkl_dense_sizes(int64_t N, int64_t d, int64_t V, int32_t K, int dtype,
+                             size_t* fwd_bytes, size_t* saved_bytes, size_t* bwd_bytes);
+/* kdkl_dense_forward: arguments and outputs as kdkl_forward (no chunk);
+ * fills `saved` (>= *saved_bytes, 16-byte aligned) for the backward. */
+kdkl_status kdkl_dense_forward(const void* H, const void* W,
+                               const int32_t* topk_ids, const float* topk_logits,
+                               int64_t N, int64_t d, int64_t V, int32_t K, float T,
+                               int dtype, float* loss, float* row_lse, float* row_kl,
+                               void* saved, size_t saved_bytes,
+                               void* workspace, size_t workspace_bytes, void* stream);
+/* kdkl_dense_backward: as kdkl_backward, from the grids the forward saved. */
+kdkl_status kdkl_dense_backward(const void* H, const void* W,
+                                const int32_t* topk_ids, const float* topk_logits,
+                                int64_t N, int64_t d, int64_t V, int32_t K, float T,
+                                int dtype, const void* saved, size_t saved_bytes,
+                                const float* grad_loss, void* dH, float* dW,
+                                int accumulate_dW, void* workspace,
+                                size_t workspace_bytes, void* stream);
 /* ---- measurement aid: per-kernel timing with HIP events ------------------
  * Between kdkl_profile_begin() and kdkl_profile_end(), every kernel launched
  * by the compute calls is bracketed by two HIP events recorded on

@@ -232,3 +232,53 @@ def test_logits_binding_refuses_cpu_tensors():
     lg = torch.zeros(4, 2)
     with pytest.raises(ValueError):
         kd.logits_forward(Z, ids, lg, 1.0)
+
+
+# --- dense baseline entry points ------------------------------------------------
+
+def test_dense_sizes(lib):
+    f, sv, b = C.c_size_t(), C.c_size_t(), C.c_size_t()
+    N, d, V, K = 32768, 2880, 201088, 100
+    assert lib.kdkl_dense_sizes(N, d, V, K, L.KDKL_BF16, C.byref(f), C.byref(sv), C.byref(b)) == OK
+    Vp = (V + 255) // 256 * 256
+    assert sv.value >= 2 * N * Vp * 4 and sv.value < 2 * N * Vp * 4 + 4096  # both grids, fp32
+    assert f.value >= N * Vp * 2                                            # the logit grid
+    assert b.value >= N * Vp * 2 + d * Vp * 2                               # dZ grid and W^T
+    assert lib.kdkl_dense_sizes(N, d, V, 0, L.KDKL_BF16, None, None, None) == SHAPE
+
+
+def dfwd(lib, **kw):
+    a = dict(H=FAKE, W=FAKE, ids=FAKE, lg=FAKE, N=64, d=64, V=1000, K=8, T=1.0, dt=L.KDKL_BF16,
+             loss=FAKE, lse=FAKE, kl=None, sv=FAKE, svb=1 << 40, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.kdkl_dense_forward(a["H"], a["W"], a["ids"], a["lg"], a["N"], a["d"], a["V"], a["K"],
+                                  a["T"], a["dt"], a["loss"], a["lse"], a["kl"], a["sv"], a["svb"],
+                                  a["ws"], a["wsb"], a["stream"])
+
+
+def dbwd(lib, **kw):
+    a = dict(H=FAKE, W=FAKE, ids=FAKE, lg=FAKE, N=64, d=64, V=1000, K=8, T=1.0, dt=L.KDKL_BF16,
+             sv=FAKE, svb=1 << 40, g=None, dH=FAKE, dW=FAKE, acc=0, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.kdkl_dense_backward(a["H"], a["W"], a["ids"], a["lg"], a["N"], a["d"], a["V"], a["K"],
+                                   a["T"], a["dt"], a["sv"], a["svb"], a["g"], a["dH"], a["dW"], a["acc"],
+                                   a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("call", [dfwd, dbwd], ids=["dense_forward", "dense_backward"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), NULL),
+    (dict(ids=None), NULL),
+    (dict(sv=None), NULL),
+    (dict(ws=None), NULL),
+    (dict(T=0.0), VALUE),
+    (dict(d=60), SHAPE),
+    (dict(K=0), SHAPE),
+    (dict(dt=5), DTYPE),
+    (dict(svb=16), WORKSPACE),
+    (dict(wsb=16), WORKSPACE),
+    (dict(sv=FAKE + 4), ALIGN),
+    (dict(H=FAKE + 8), ALIGN),
+])
+def test_dense_calls_reject_bad_arguments(lib, call, kw, status):
+    assert call(lib, **kw) == status
