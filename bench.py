@@ -10,7 +10,8 @@ Default workload: the gpt-oss-20b-like head at 32K tokens
 --path logits measures the forward-chunked variant instead: one step =
 kdkl_logits_forward + kdkl_logits_backward on the logit grid Z = H W^T of the
 same workload (computed on the device before timing, as the caller's output
-layer would); that path is bound by HBM bandwidth.
+layer would); that path is bound by HBM bandwidth. --path dense measures the
+dense baseline (full grids kept for the backward).
 """
 from __future__ import annotations
 
@@ -212,6 +213,95 @@ def bench_logits(args, w, x):
     print(json.dumps(out), flush=True)
 
 
+def bench_dense(args, w, x):
+    """The pages' dense baseline: full student and teacher grids kept for the
+    backward pass (no recompute: 6 N V d flop per step)."""
+    import torch
+
+    import chunked_kl_loss_amd as kd
+
+    dev = torch.device("cuda:0")
+    torch.cuda.reset_peak_memory_stats(dev)
+    H, W, ids, lg = (x[k].to(dev) for k in ("H", "W", "ids", "logits"))
+    fb, sb, bb = kd.dense_sizes(w.N, w.d, w.V, w.K, H.dtype)
+    saved = torch.empty(sb, dtype=torch.uint8, device=dev)
+    ws_f = torch.empty(fb, dtype=torch.uint8, device=dev)
+    loss = torch.empty(1, dtype=torch.float32, device=dev)
+    row_lse = torch.empty(w.N, dtype=torch.float32, device=dev)
+    row_kl = torch.empty(w.N, dtype=torch.float32, device=dev)
+    dH = torch.empty_like(H)
+    dW = torch.empty((w.V, w.d), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        # the forward's logit-grid workspace is released before the backward's
+        # is taken, as an autograd framework would
+        wf = torch.empty(fb, dtype=torch.uint8, device=dev)
+        kd.dense_forward(H, W, ids, lg, w.T, saved=saved, loss=loss, row_lse=row_lse, row_kl=row_kl,
+                         workspace=wf, stream=stream)
+        del wf
+        wb = torch.empty(bb, dtype=torch.uint8, device=dev)
+        kd.dense_backward(H, W, ids, lg, w.T, saved, None, dH=dH, dW=dW, workspace=wb, stream=stream)
+        del wb
+
+    del ws_f
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    log(f"bench: warmup done, loss={loss.item():.6f}")
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    kd.profile_begin()
+    torch.cuda.synchronize(dev)
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    kstats = kd.profile_end()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    peak_gib = torch.cuda.max_memory_allocated(dev) / 2**30
+    log(f"bench: {ms:.2f} ms/step, peak {peak_gib:.2f} GiB")
+    dtype = "bf16" if w.dtype == "bf16" else "fp32"
+    flops_step = 6.0 * w.N * w.V * w.d
+    peak = PEAK_TFLOPS[dtype]
+    dom = max(kstats, key=lambda k: kstats[k]["total_ms"])
+    ds = kstats[dom]
+    t = ds["total_ms"] / 1e3
+    if ds["flops"] > 0:
+        roof = {"bound": "mfma", "achieved": round(ds["flops"] / t / 1e12, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(ds["flops"] / t / 1e12 / peak, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(ds["bytes"] / t / 1e9, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ds["bytes"] / t / 1e9 / HBM_PEAK_GBS, 4)}
+    roof.update({"kernel": dom, "traffic": load_traffic(dom, w.name),
+                 "avg_launch_ms": round(ds["total_ms"] / ds["launches"], 4)})
+    out = {
+        "metric": "dense KL (full grids) fwd+bwd tokens/s; MFMA util % of bf16 peak; peak HBM GiB",
+        "value": round(w.N / (ms / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": w.name, "path": "dense (full grids kept)", "N": w.N, "d": w.d, "V": w.V,
+                   "K": w.K, "T": w.T, "parallelism": "single GPU"},
+        "mfma_util_pct": round(100.0 * flops_step / (ms / 1e3) / (peak * 1e12), 2),
+        "flop_per_step": flops_step,
+        "peak_hbm_gib": round(peak_gib, 3),
+        "saved_grids_gib": round(sb / 2**30, 3),
+        "roofline": roof,
+        "kernels": kernel_table(kstats, args.steps),
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,9 +312,9 @@ def main():
     ap.add_argument("--chunk", type=int, default=None, help="override the chunk size")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=("fused", "logits"), default="fused",
+    ap.add_argument("--path", choices=("fused", "logits", "dense"), default="fused",
                     help="fused: the fused chunked loss (default); logits: the forward-chunked "
-                         "loss on a given logit grid")
+                         "loss on a given logit grid; dense: the dense baseline (full grids)")
     ap.add_argument("--inplace", action="store_true",
                     help="logits path: write dZ over the logit grid")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -258,6 +348,10 @@ def main():
     if args.path == "logits":
         torch.zeros(1, device=dev)
         bench_logits(args, w, x)
+        return
+    if args.path == "dense":
+        torch.zeros(1, device=dev)
+        bench_dense(args, w, x)
         return
     torch.zeros(1, device=dev)  # initialise the device before reading memory stats
     torch.cuda.reset_peak_memory_stats(dev)
