@@ -906,6 +906,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 #ifndef KDKL_GEMM_STAGES
 #define KDKL_GEMM_STAGES 2
 #endif
+#ifndef KDKL_DMA_SPREAD
+#define KDKL_DMA_SPREAD 2
+#endif
 #ifndef KDKL_DW_GRID42
 #define KDKL_DW_GRID42 1
 #endif
@@ -1000,6 +1003,25 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
     for (int i = 0; i < LPO_B; ++i)
       load16_lds(bb, lane_off(LB, sb[i], p.ldb, p.b_krows, kt), base + TILE + (i * G::kWaves + wid) * 1024);
   };
+  // Part `part` of NPART of a stage's loads (A loads first, then B): the
+  // loads of the next stage are spread over the k-groups of the current step
+  // so that their LDS writes do not arrive as one burst against the fragment
+  // reads.
+  constexpr int NPART = KDKL_DMA_SPREAD < KG ? KDKL_DMA_SPREAD : KG;
+  auto issue_part = [&](int kt, int part) {
+    char* base = smem + (kt % NSTAGE) * STG;
+    const char* ba = stage_base(LA, p.A, p.lda, m0, kt);
+    const char* bb = stage_base(LB, p.B, p.ldb, n0, kt);
+#pragma unroll
+    for (int q = 0; q < LPS; ++q) {
+      if (q * NPART / LPS != part) continue;
+      if (q < LPO)
+        load16_lds(ba, lane_off(LA, sa[q], p.lda, p.a_krows, kt), base + (q * G::kWaves + wid) * 1024);
+      else
+        load16_lds(bb, lane_off(LB, sb[q - LPO], p.ldb, p.b_krows, kt),
+                   base + TILE + ((q - LPO) * G::kWaves + wid) * 1024);
+    }
+  };
 
   f32x16_t acc[MB][NB];
   zero_acc<G>(acc);
@@ -1049,9 +1071,13 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
     load_frags(0, 0, 0);
     for (int kt = 0; kt < nk; ++kt) {
       const bool more = kt + NSTAGE - 1 < nk;
-      if (more) issue(kt + NSTAGE - 1);
 #pragma unroll
       for (int kk = 0; kk < KG; ++kk) {
+        if (more) {
+#pragma unroll
+          for (int part = 0; part < NPART; ++part)
+            if (part * KG / NPART == kk) issue_part(kt + NSTAGE - 1, part);
+        }
         if (kk + 1 < KG) load_frags(kt, kk + 1, (kk + 1) & 1);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
