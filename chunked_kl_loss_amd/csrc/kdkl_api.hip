@@ -80,6 +80,7 @@ struct Plan {
   int64_t es;      // element bytes of H, W, dZ, dH
   int64_t Cp;      // chunk capacity (multiple of the token tile)
   int64_t Vp;      // padded vocabulary (multiple of the vocabulary tile)
+  int vt;          // vocabulary tile: rows per workgroup of the forward and dZ products
   int64_t n_vt;    // vocabulary tiles
   int dh_splits;
   int64_t dh_ksplit;
@@ -115,10 +116,18 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   P->es = dtype == KDKL_BF16 ? 2 : 4;
   P->chunk = chunk < N ? chunk : (N > 0 ? N : 1);
   P->Cp = round_up(P->chunk, kTokenTile);
-  P->Vp = round_up(V, kVocabTile);
+  P->vt = kVocabTile;
+  P->Vp = round_up(V, P->vt);
   P->fast = gemm_fast_path(dtype, d, P->Vp, P->Cp);
+  if (P->fast && gemm_vocab_tile(true) != P->vt) {
+    const int64_t vp = round_up(V, gemm_vocab_tile(true));
+    if (gemm_fast_path(dtype, d, vp, P->Cp)) {
+      P->vt = gemm_vocab_tile(true);
+      P->Vp = vp;
+    }
+  }
   P->dtile = gemm_d_tile(P->fast, d);
-  P->n_vt = P->Vp / kVocabTile;
+  P->n_vt = P->Vp / P->vt;
   if (P->Cp > INT32_MAX / 2) return KDKL_ERR_OVERFLOW;
   // dH split-K: the number of splits S that makes the launch cheapest when
   // every workgroup does 1/S of a tile's work and the 256 compute units of
@@ -196,7 +205,7 @@ static TeacherArgs teacher_args(const Plan& P, const int32_t* ids, const float* 
                                 size_t o_keep, size_t o_tstart) {
   TeacherArgs t;
   t.ids = ids; t.logits = lg; t.r0 = r0; t.rows = rows; t.K = (int)P.K;
-  t.inv_T = 1.0f / T; t.n_vt = (int)P.n_vt; t.Cp = P.Cp;
+  t.inv_T = 1.0f / T; t.vt = P.vt; t.n_vt = (int)P.n_vt; t.Cp = P.Cp;
   t.sids = (int32_t*)(ws + o_sids); t.sp = (float*)(ws + o_sp);
   t.erow = (float*)(ws + o_erow); t.keep = (float*)(ws + o_keep); t.tstart = (uint16_t*)(ws + o_tstart);
   return t;
@@ -211,6 +220,7 @@ static GemmArgs projection_args(const Plan& P, const void* H, const void* W, flo
   g.M = (int)P.V; g.N = rows;
   g.k_end = P.d; g.k_split = P.d;
   g.tiles_m = (int)P.n_vt; g.tiles_n = (int)((rows + kTokenTile - 1) / kTokenTile); g.splits = 1;
+  g.bm = P.vt;
   g.inv_T = 1.0f / T; g.V = (int)P.V; g.K = (int)P.K; g.Cp = P.Cp; g.n_vt = (int)P.n_vt;
   g.sids = (const int32_t*)(ws + o_sids); g.sp = (const float*)(ws + o_sp);
   g.tstart = (const uint16_t*)(ws + o_tstart);
@@ -327,7 +337,7 @@ static hipError_t chunk_products(const Plan& P, int dtype, char* ws, int64_t r0,
   }
   w.B = ws + P.b_ht; w.ldb = P.Cp; w.b_layout = LAYOUT_KC;
   w.M = (int)V; w.N = (int)d; w.k_end = rows_pad; w.k_split = rows_pad;
-  w.tiles_m = (int)P.n_vt; w.tiles_n = (int)((d + P.dtile - 1) / P.dtile); w.splits = 1; w.bn = P.dtile;
+  w.tiles_m = (int)((V + 255) / 256); w.tiles_n = (int)((d + P.dtile - 1) / P.dtile); w.splits = 1; w.bn = P.dtile;
   w.out = dW; w.ldo = d; w.accumulate = accumulate ? 1 : 0;
   return timed(K_DW_GEMM, fl, ((double)V * rows + (double)rows * d) * P.es + 8.0 * V * d, s,
             [&] { return launch_gemm(dtype, EPI_DW, w, s); });

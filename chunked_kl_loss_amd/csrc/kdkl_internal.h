@@ -8,8 +8,10 @@
 
 namespace kdkl {
 
-// Tile of the vocabulary handled by one workgroup of the projection GEMMs.
-// The teacher preparation builds its per-tile index with the same width.
+// Tile of the vocabulary handled by one workgroup of the projection GEMMs
+// (the forward and dZ products): 256 rows, or 384 on the bf16 main loop (see
+// gemm_vocab_tile). The teacher preparation builds its per-tile index with
+// the same width.
 constexpr int kVocabTile = 256;
 // Token-axis tile of the projection GEMMs; chunk buffers are padded to it.
 constexpr int kTokenTile = 256;
@@ -46,7 +48,8 @@ struct TeacherArgs {
   int rows;
   int K;
   float inv_T;
-  int n_vt;               // vocabulary tiles (ceil(V / kVocabTile))
+  int vt;                 // rows per vocabulary tile
+  int n_vt;               // vocabulary tiles (ceil(V / vt))
   int64_t Cp;             // padded chunk capacity (row pitch of tstart)
   int32_t* sids;          // [Cp, K]   ids sorted ascending
   float* sp;              // [Cp, K]   teacher probabilities, same order
@@ -90,6 +93,7 @@ struct GemmArgs {
   // them are clamped (their products are zero or masked).
   int a_layout, b_layout;
   int bn;                        // N-tile width: 256 (or 0), or 320 for dH / dW (see gemm_d_tile)
+  int bm;                        // M-tile height: 256 (or 0), or 384 for the forward / dZ products (see gemm_vocab_tile)
   int64_t a_krows, a_mcols, b_krows, b_mcols;
 };
 
@@ -103,6 +107,10 @@ bool gemm_fast_path(int dtype, int64_t d, int64_t Vp, int64_t Cp);
 // N-tile width of the products whose N axis is the hidden size d (dH, dW):
 // 320 on the fast path when it pads d less than 256 does, else 256.
 int gemm_d_tile(bool fast, int64_t d);
+// Vocabulary tile (M-tile height) of the forward and dZ products: 384 on the
+// bf16 main loop (a 384 x 256 tile reads fewer operand bytes through LDS per
+// flop than 256 x 256), else 256.
+int gemm_vocab_tile(bool fast);
 
 struct MergeArgs {
   const float4* part;   // [Cp, n_vt]

@@ -10,7 +10,8 @@
 //   EPI_FWD  Z^T tile = W_tile . H_tile^T; per token: max, sum exp, and the
 //            teacher-weighted logit sum over the tile's vocabulary rows.
 //   EPI_DZ   same product; dZ = coef * (softmax - teacher) written to the
-//            chunk buffers in two layouts (token-major and vocab-major).
+//            token-major chunk buffer (and a vocab-major copy on the generic
+//            path).
 //   EPI_DH   dH partial = dZ . W over a split of the vocabulary (split-K).
 //   EPI_DW   dW (+)= dZ^T . H over the chunk's tokens.
 #include <hip/hip_runtime.h>
@@ -51,7 +52,7 @@ __device__ __forceinline__ T shfl_xor(T v, int mask) {
 // Teacher preparation (one wavefront per position of the chunk):
 //   p_k = softmax_k(l_k / T), e = sum_k p_k log p_k,
 //   (id, p) pairs sorted by id, and for each vocabulary tile t the number of
-//   sorted ids below t * kVocabTile (so a tile's teacher entries are the
+//   sorted ids below t * vt (so a tile's teacher entries are the
 //   contiguous range [tstart[t], tstart[t+1])).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void teacher_prep_kernel(TeacherArgs a) {
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(64) void teacher_prep_kernel(TeacherArgs a) {
   }
   __syncthreads();
   for (int t = lane; t <= a.n_vt; t += 64) {
-    const int64_t bound = (int64_t)t * kVocabTile;
+    const int64_t bound = (int64_t)t * a.vt;
     int lo = 0, hi = K;  // first index with sorted id >= bound
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
@@ -337,22 +338,26 @@ hipError_t launch_dh_reduce(int dtype, const float* part, int splits, int rows, 
 // lane l holds output row 8 * (r >> 2) + 4 * (l >> 5) + (r & 3), column
 // (l & 31).
 // ---------------------------------------------------------------------------
-constexpr int BM = 256, BN = 256;      // workgroup tile (the N width is a property of the grid below)
+constexpr int BM = 256, BN = 256;      // workgroup tile of the generic main loop
 constexpr int kDwPitch = BN + 8;       // fp32 row pitch of the dW staging tile
-constexpr int kDzPitch = BM + 8;       // bf16 row pitch of the dZ staging tile
 constexpr int kEpiSmem = 128 * kDwPitch * 4;
 
-// Wavefront grid of a BM x TN workgroup tile. TN is 256 except for the
-// products whose N axis is the hidden size, which may use 320-wide tiles
-// (a hidden size of 2880 is 9 x 320 but 11.25 x 256).
-template <int WAVES_M, int WAVES_N, int TN = 256>
+// Wavefront grid of a TM x TN workgroup tile. TM x TN is 256 x 256 except
+// for the products whose N axis is the hidden size, which may use 320-wide
+// tiles (a hidden size of 2880 is 9 x 320 but 11.25 x 256), and the forward
+// and dZ products on the bf16 main loop, which use 384 x 256.
+template <int WAVES_M, int WAVES_N, int TN = 256, int TM = 256>
 struct Grid {
   static constexpr int kWavesM = WAVES_M, kWavesN = WAVES_N;
   static constexpr int kWaves = WAVES_M * WAVES_N;
   static constexpr int kThreads = 64 * kWaves;
-  static constexpr int BN = TN;
-  static constexpr int WM = BM / WAVES_M, WN = TN / WAVES_N;
+  static constexpr int BM = TM, BN = TN;
+  static constexpr int WM = TM / WAVES_M, WN = TN / WAVES_N;
   static constexpr int MB = WM / 32, NB = WN / 32;
+  // Above 160 accumulator registers per lane (two wavefronts per SIMD share
+  // 512), the B fragments of the next k-group are read into the registers
+  // of the current one as each is consumed instead of a second buffer.
+  static constexpr bool kSingleB = MB * NB * 16 > 160;
   static_assert(WM % 32 == 0 && WN % 32 == 0, "wavefront tiles are whole 32 x 32 blocks");
   static __device__ __forceinline__ int wm() { return (int)(threadIdx.x >> 6) / WAVES_N; }
   static __device__ __forceinline__ int wn() { return (int)(threadIdx.x >> 6) % WAVES_N; }
@@ -447,39 +452,61 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
                                               char* smem, const int (&hit_lo)[G::NB],
                                               const int (&hit_hi)[G::NB]) {
   constexpr int MB = G::MB, NB = G::NB, NT = G::kThreads;
-  constexpr int BN = G::BN;
+  constexpr int BM = G::BM, BN = G::BN;
+  constexpr int kDzPitch = BM + 8;  // bf16 row pitch of the dZ staging tile
+  static_assert(BM == 256 || EPI == EPI_FWD || EPI == EPI_DZ, "vocabulary-row tiles of dH / dW are 256 high");
   static_assert(BN == 256 || EPI == EPI_DH || EPI == EPI_DW, "token-axis tiles are 256 wide");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wm = G::wm(), wn = G::wn();
   const int m0 = t.tm * BM, n0 = t.tn * BN;
+  // Rows past V exist only in the last vocabulary tile; the others skip the mask.
+  const bool full_rows = m0 + BM <= p.V;
+  auto row_ok = [&](int mb, int r) { return m0 + acc_row<G>(wm, mb, r, lane) < p.V; };
+  // exp(s - m) with s = z / T as exp2(z * c2 - m2): one fused multiply-add per element
+  const float c2 = p.inv_T * kLog2e;
   if constexpr (EPI == EPI_FWD) {
     // s = z / T over the tile's vocabulary rows (A rows), per token column:
     // max, sum of exp(s - max), and sum of p * s over the teacher ids here.
+    // The max is taken over z (T > 0 preserves order) and scaled once.
     float* red = (float*)smem;  // [WAVES_M][BN][3]
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int ct = wn * G::WN + nb * 32 + (lane & 31);
       const int col = n0 + ct;
-      float mx = kNegInf;
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + acc_row<G>(wm, mb, r, lane);
-          const float s = row < p.V ? acc[mb][nb][r] * p.inv_T : kNegInf;
-          acc[mb][nb][r] = s;
-          mx = fmaxf(mx, s);
-        }
-      mx = fmaxf(mx, shfl_xor(mx, 32));
-      float se = 0.f;
-      if (mx > kNegInf) {
+      float zmax = kNegInf;
+      if (full_rows) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) se += fast_exp(acc[mb][nb][r] - mx);
+          for (int r = 0; r < 16; ++r) zmax = fmaxf(zmax, acc[mb][nb][r]);
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) zmax = fmaxf(zmax, row_ok(mb, r) ? acc[mb][nb][r] : kNegInf);
+      }
+      zmax = fmaxf(zmax, shfl_xor(zmax, 32));
+      float se = 0.f;
+      if (zmax > kNegInf) {
+        const float off = zmax * c2;
+        if (full_rows) {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) se += __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mb][nb][r], c2, -off));
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mb][nb][r], c2, -off));
+              se += row_ok(mb, r) ? e : 0.f;
+            }
+        }
       }
       se += shfl_xor(se, 32);
-      float gam = 0.f;
+      const float mx = zmax * p.inv_T;
+      float gz = 0.f;  // sum of p * z; times 1/T below
       for (int h = hit_lo[nb]; h < hit_hi[nb]; ++h) {
         const int slot = hit_slot<G>(p.sids[(int64_t)col * p.K + h], p.V, m0, wm, lane);
         if (slot < 0) continue;
@@ -488,9 +515,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) v = (mb * 16 + rr == slot) ? acc[mb][nb][rr] : v;
-        gam += p.sp[(int64_t)col * p.K + h] * v;
+        gz += p.sp[(int64_t)col * p.K + h] * v;
       }
-      gam += shfl_xor(gam, 32);
+      gz += shfl_xor(gz, 32);
+      const float gam = gz * p.inv_T;
       if (lane < 32) {
         float* e = red + (wm * BN + ct) * 3;
         e[0] = mx;
@@ -539,20 +567,26 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
           }
         continue;
       }
-      const float lse = cval ? p.row_lse[col] : 0.f;
-      const float kc = cval ? p.keep[col] : 0.f;
+      // coef * q = coef * exp2(z * c2 - lse * log2 e); a column past the
+      // chunk or of an ignored position gets lse2 = +inf, so its q is 0
+      const bool use = cval && p.keep[col] != 0.f;
+      const float lse2 = use ? p.row_lse[col] * kLog2e : __builtin_huge_valf();
+      const float qs = use ? coef : 0.f;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + acc_row<G>(wm, mb, r, lane);
-          const float q = fast_exp(acc[mb][nb][r] * p.inv_T - lse);
-          acc[mb][nb][r] = (row < p.V && cval) ? q * kc : 0.f;
-        }
+        for (int r = 0; r < 16; ++r)
+          acc[mb][nb][r] = qs * __builtin_amdgcn_exp2f(__builtin_fmaf(acc[mb][nb][r], c2, -lse2));
+      if (!full_rows) {
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[mb][nb][r] = row_ok(mb, r) ? acc[mb][nb][r] : 0.f;
+      }
       for (int h = hit_lo[nb]; h < hit_hi[nb]; ++h) {
         const int slot = hit_slot<G>(p.sids[(int64_t)col * p.K + h], p.V, m0, wm, lane);
         if (slot < 0) continue;
-        const float pk = p.sp[(int64_t)col * p.K + h];
+        const float pk = coef * p.sp[(int64_t)col * p.K + h];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -561,7 +595,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
       }
     }
     if constexpr (ES == 2) {
-      // Stage 128 token columns at a time as bf16 [128 n][256 v] in LDS, then
+      // Stage 128 token columns at a time as bf16 [128 n][BM v] in LDS, then
       // write both layouts with 16-byte stores.
       uint16_t* T = (uint16_t*)smem;
       uint16_t* cv = (uint16_t*)p.dz_cv;
@@ -579,19 +613,20 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
                 const int nl = wn * G::WN + nb * 32 + (lane & 31) - half * 128;
                 const int vl = acc_row<G>(wm, mb, r4 * 4, lane);
                 ushort4 o;
-                o.x = f32_to_bf16_bits(acc[mb][nb][r4 * 4 + 0] * coef);
-                o.y = f32_to_bf16_bits(acc[mb][nb][r4 * 4 + 1] * coef);
-                o.z = f32_to_bf16_bits(acc[mb][nb][r4 * 4 + 2] * coef);
-                o.w = f32_to_bf16_bits(acc[mb][nb][r4 * 4 + 3] * coef);
+                o.x = f32_to_bf16_bits(acc[mb][nb][r4 * 4 + 0]);
+                o.y = f32_to_bf16_bits(acc[mb][nb][r4 * 4 + 1]);
+                o.z = f32_to_bf16_bits(acc[mb][nb][r4 * 4 + 2]);
+                o.w = f32_to_bf16_bits(acc[mb][nb][r4 * 4 + 3]);
                 *(ushort4*)(T + nl * kDzPitch + vl) = o;
               }
         }
         __syncthreads();
         const int nb0 = n0 + half * 128;
-        // token-major rows: 512 bytes of vocabulary each
+        // token-major rows: BM * 2 bytes of vocabulary each
+        constexpr int CV = BM / 8;  // 16-byte chunks per row
 #pragma unroll 4
-        for (int j = tid; j < 128 * 32; j += NT) {
-          const int i = j >> 5, c = j & 31;
+        for (int j = tid; j < 128 * CV; j += NT) {
+          const int i = j / CV, c = j % CV;
           store16_stream(cv + (int64_t)(nb0 + i) * p.Vp + m0 + c * 8, *(const uint4*)(T + i * kDzPitch + c * 8));
         }
         // vocabulary-major rows: 256 bytes of tokens each (only for the
@@ -599,7 +634,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
         if (vc == nullptr) continue;
 #pragma unroll 4
         for (int j = tid; j < BM * 16; j += NT) {
-          const int v = j & (BM - 1), c = j >> 8;
+          const int v = j % BM, c = j / BM;
           uint16_t e[8];
 #pragma unroll
           for (int q = 0; q < 8; ++q) e[q] = T[(c * 8 + q) * kDzPitch + v];
@@ -622,8 +657,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
             const int row = m0 + acc_row<G>(wm, mb, r4 * 4, lane);
-            const float v0 = acc[mb][nb][r4 * 4 + 0] * coef, v1 = acc[mb][nb][r4 * 4 + 1] * coef;
-            const float v2 = acc[mb][nb][r4 * 4 + 2] * coef, v3 = acc[mb][nb][r4 * 4 + 3] * coef;
+            const float v0 = acc[mb][nb][r4 * 4 + 0], v1 = acc[mb][nb][r4 * 4 + 1];
+            const float v2 = acc[mb][nb][r4 * 4 + 2], v3 = acc[mb][nb][r4 * 4 + 3];
             *(float4*)(cv + (int64_t)col * p.Vp + row) = make_float4(v0, v1, v2, v3);
             if (vc == nullptr) continue;
             vc[(int64_t)(row + 0) * p.Cp + col] = v0;
@@ -917,7 +952,7 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
   constexpr int MB = G::MB, NB = G::NB;
   constexpr int RB = BK * 2;                 // bytes of one k-contiguous LDS row
   constexpr int CPR = RB / 16;               // 16-byte chunks per such row
-  constexpr int TILE = BM * RB;              // bytes of the A tile per stage
+  constexpr int TILE = G::BM * RB;           // bytes of the A tile per stage
   constexpr int TILE_B = G::BN * RB;         // bytes of the B tile per stage
   constexpr int STG = TILE + TILE_B;
   constexpr int SMEM = NSTAGE * STG > kEpiSmem ? NSTAGE * STG : kEpiSmem;
@@ -926,7 +961,8 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
   constexpr int LPS = LPO + LPO_B;
   constexpr int KG = BK / 16;                // 16-element k-groups per step
   static_assert(LPO * 1024 * G::kWaves == TILE && LPO_B * 1024 * G::kWaves == TILE_B, "whole loads per wave");
-  static_assert(BM == 256 && (LB == LAYOUT_KC || G::BN == 256), "k-major LDS rows hold 256 elements");
+  static_assert((LA == LAYOUT_KC || G::BM == 256) && (LB == LAYOUT_KC || G::BN == 256),
+                "k-major LDS rows hold 256 elements");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   Tile t;
   if (!tile_of(p, t)) return;
@@ -936,7 +972,7 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid / G::kWavesN, wn = wid % G::kWavesN;
-  const int m0 = t.tm * BM, n0 = t.tn * G::BN;
+  const int m0 = t.tm * G::BM, n0 = t.tn * G::BN;
   const int64_t kb = (int64_t)t.ks * p.k_split;
   const int64_t ke = kb + p.k_split < p.k_end ? kb + p.k_split : p.k_end;
   const int nk = ke > kb ? (int)((ke - kb) / BK) : 0;
@@ -1025,7 +1061,8 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
 
   f32x16_t acc[MB][NB];
   zero_acc<G>(acc);
-  bf16x8_t fa[2][MB], fb[2][NB];
+  constexpr bool SB = G::kSingleB;
+  bf16x8_t fa[2][MB], fb[SB ? 1 : 2][NB];
   // One MFMA operand fragment (8 consecutive k of output row/column `r0 +
   // (lane & 31)`) from an operand tile in either layout.
   auto frag = [&](int layout, const char* s, int r0, int kk) -> bf16x8_t {
@@ -1050,13 +1087,14 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
       return v;
     }
   };
-  auto load_frags = [&](int kt, int kk, int buf) {
+  auto load_frags = [&](int kt, int kk, int buf, bool with_b) {
     const char* sA = smem + (kt % NSTAGE) * STG;
     const char* sB = sA + TILE;
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) fa[buf][mb] = frag(LA, sA, wm * G::WM + mb * 32, kk);
+    if (with_b)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) fb[buf][nb] = frag(LB, sB, wn * G::WN + nb * 32, kk);
+      for (int nb = 0; nb < NB; ++nb) fb[SB ? 0 : buf][nb] = frag(LB, sB, wn * G::WN + nb * 32, kk);
   };
 
   if (nk > 0) {
@@ -1068,7 +1106,7 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
     else
       wait_vmcnt<0>();
     phase_barrier();
-    load_frags(0, 0, 0);
+    load_frags(0, 0, 0, true);
     for (int kt = 0; kt < nk; ++kt) {
       const bool more = kt + NSTAGE - 1 < nk;
 #pragma unroll
@@ -1078,13 +1116,25 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
           for (int part = 0; part < NPART; ++part)
             if (part * KG / NPART == kk) issue_part(kt + NSTAGE - 1, part);
         }
-        if (kk + 1 < KG) load_frags(kt, kk + 1, (kk + 1) & 1);
+        if (kk + 1 < KG) load_frags(kt, kk + 1, (kk + 1) & 1, !SB);
+        if constexpr (SB) {
+          // each B fragment is replaced by the next k-group's once its MFMAs are issued
+          const char* sB = smem + (kt % NSTAGE) * STG + TILE;
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+          for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
-          for (int nb = 0; nb < NB; ++nb)
-            acc[mb][nb] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][mb], fb[kk & 1][nb], acc[mb][nb], 0, 0, 0);
+            for (int mb = 0; mb < MB; ++mb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][mb], fb[0][nb], acc[mb][nb], 0, 0, 0);
+            if (kk + 1 < KG) fb[0][nb] = frag(LB, sB, wn * G::WN + nb * 32, kk + 1);
+          }
+        } else {
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+              acc[mb][nb] =
+                  __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][mb], fb[kk & 1][nb], acc[mb][nb], 0, 0, 0);
+        }
       }
       // stage kt + 1 must have landed; later stages may still be in flight
       if (more)
@@ -1092,7 +1142,7 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
       else
         wait_vmcnt<0>();
       phase_barrier();
-      if (kt + 1 < nk) load_frags(kt + 1, 0, 0);
+      if (kt + 1 < nk) load_frags(kt + 1, 0, 0, true);
     }
   }
   gemm_epilogue<G, 2, EPI>(p, acc, t, smem, hit_lo, hit_hi);
@@ -1104,7 +1154,7 @@ using FastGrid = typename std::conditional<
 // Byte span of one stage's direct loads from its buffer-resource base: the
 // lane offsets are 32-bit and the resource's range is 2^31 - 1 bytes.
 static bool span_fits(int layout, int64_t ld, int64_t mcols) {
-  const int64_t span = layout == LAYOUT_KC ? (320 * ld + KDKL_GEMM_BK) * 2 : (KDKL_GEMM_BK * ld + mcols) * 2;
+  const int64_t span = layout == LAYOUT_KC ? (384 * ld + KDKL_GEMM_BK) * 2 : (KDKL_GEMM_BK * ld + mcols) * 2;
   return span < ((int64_t)1 << 31);
 }
 
@@ -1121,6 +1171,11 @@ using DwGrid = typename std::conditional<KDKL_GEMM_WAVES == 8 && KDKL_DW_GRID42,
 #ifndef KDKL_D320
 #define KDKL_D320 1
 #endif
+#ifndef KDKL_V384
+#define KDKL_V384 1
+#endif
+int gemm_vocab_tile(bool fast) { return fast && KDKL_V384 ? 384 : 256; }
+
 int gemm_d_tile(bool fast, int64_t d) {
   if (!fast || !KDKL_D320) return 256;
   const int64_t pad256 = (d + 255) / 256 * 256, pad320 = (d + 319) / 320 * 320;
@@ -1129,6 +1184,16 @@ int gemm_d_tile(bool fast, int64_t d) {
 
 template <int EPI, int LA, int LB>
 static hipError_t launch_fast(const GemmArgs& a, dim3 grid, hipStream_t s) {
+  if constexpr (EPI == EPI_FWD || EPI == EPI_DZ) {
+    if (a.bm == 384) {
+      // 384 x 256 tiles on a 4 x 2 grid: wavefront tiles of 96 x 128
+      using GV = Grid<4, 2, 256, 384>;
+      hipLaunchKernelGGL((gemm_bf16_kernel<GV, EPI, KDKL_GEMM_BK, KDKL_GEMM_STAGES, LA, LB>), grid,
+                         dim3(GV::kThreads), 0, s, a);
+      return hipGetLastError();
+    }
+  }
+  if (a.bm != 0 && a.bm != 256) return hipErrorInvalidValue;
   if constexpr (EPI == EPI_DH || EPI == EPI_DW) {
     if (a.bn == 320) {
       // 256 x 320 tiles on a 4 x 2 grid: wavefront tiles of 64 x 160
@@ -1163,7 +1228,7 @@ static hipError_t launch_gemm_e(int dtype, const GemmArgs& a, hipStream_t s) {
     return hipErrorInvalidValue;
   }
   if (a.a_layout != LAYOUT_KC || a.b_layout != LAYOUT_KC) return hipErrorInvalidValue;
-  if (a.bn != 0 && a.bn != 256) return hipErrorInvalidValue;
+  if ((a.bn != 0 && a.bn != 256) || (a.bm != 0 && a.bm != 256)) return hipErrorInvalidValue;
   if (dtype == 1)
     hipLaunchKernelGGL((gemm_generic_kernel<uint16_t, EPI>), grid, dim3(256), 0, s, a);
   else

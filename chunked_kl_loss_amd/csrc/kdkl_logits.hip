@@ -348,7 +348,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void logits_bwd_kernel(LogitsAr
 // The pages' dense baseline builds the full teacher probability grid from the
 // cached top-K and compares it with the student's full log-probability grid
 // [P1, section "Two system changes", dense KL bullet]; both grids are kept for
-// the backward pass. Rows are 16-byte aligned (pitch ldv, a multiple of 256
+// the backward pass. Rows are 16-byte aligned (pitch ldv, a multiple of 8
 // elements), so every pass streams whole vectors plus a scalar tail.
 
 template <typename TE>
@@ -527,7 +527,7 @@ static dim3 dense_grid(int64_t rows) { return dim3((unsigned)((rows + kRowsPerBl
 
 hipError_t launch_dense_student(int dtype, const DenseArgs& a, hipStream_t s) {
   if (a.N <= 0) return hipSuccess;
-  if (a.ldv % 256 != 0) return hipErrorInvalidValue;
+  if (a.ldv % 8 != 0) return hipErrorInvalidValue;
   if (dtype == 1)
     hipLaunchKernelGGL(dense_student_kernel<uint16_t>, dense_grid(a.N), dim3(64 * kRowsPerBlock), 0, s, a);
   else
@@ -537,7 +537,7 @@ hipError_t launch_dense_student(int dtype, const DenseArgs& a, hipStream_t s) {
 
 hipError_t launch_dense_teacher(const DenseArgs& a, hipStream_t s) {
   if (a.N <= 0) return hipSuccess;
-  if (a.K < 1 || a.K > 1024 || a.ldv % 256 != 0) return hipErrorInvalidValue;
+  if (a.K < 1 || a.K > 1024 || a.ldv % 8 != 0) return hipErrorInvalidValue;
   const dim3 g = dense_grid(a.N), b(64 * kRowsPerBlock);
   if (a.K <= 128)
     hipLaunchKernelGGL(dense_teacher_kernel<2>, g, b, 0, s, a);
@@ -550,14 +550,14 @@ hipError_t launch_dense_teacher(const DenseArgs& a, hipStream_t s) {
 
 hipError_t launch_dense_kl(const DenseArgs& a, hipStream_t s) {
   if (a.N <= 0) return hipSuccess;
-  if (a.ldv % 256 != 0) return hipErrorInvalidValue;
+  if (a.ldv % 8 != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(dense_kl_kernel, dense_grid(a.N), dim3(64 * kRowsPerBlock), 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_dense_grad(int dtype, const DenseArgs& a, hipStream_t s) {
   if (a.rows_pad <= 0) return hipSuccess;
-  if (a.ldv % 256 != 0 || a.rows_pad < a.N) return hipErrorInvalidValue;
+  if (a.ldv % 8 != 0 || a.rows_pad < a.N) return hipErrorInvalidValue;
   if (dtype == 1)
     hipLaunchKernelGGL(dense_grad_kernel<uint16_t>, dense_grid(a.rows_pad), dim3(64 * kRowsPerBlock), 0, s, a);
   else
