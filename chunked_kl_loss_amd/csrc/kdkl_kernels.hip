@@ -257,10 +257,55 @@ __global__ __launch_bounds__(256) void transpose_kernel(const E* __restrict__ in
   }
 }
 
+// 16-bit transpose with 16-byte accesses on both sides: a 64 x 64 tile is
+// read as rows of 8-element vectors, and each output vector gathers 8 rows
+// of one column from LDS. Needs C, ldi, ldo and Rp multiples of 8 and
+// 16-byte aligned rows.
+__global__ __launch_bounds__(256) void transpose16_kernel(const uint16_t* __restrict__ in, int64_t R, int64_t C,
+                                                          int64_t ldi, uint16_t* __restrict__ out, int64_t Rp,
+                                                          int64_t ldo) {
+  constexpr int P = 72;  // row pitch in elements (144 bytes: 16-byte aligned rows)
+  __shared__ __attribute__((aligned(16))) uint16_t tile[64 * P];
+  const int64_t r0 = (int64_t)blockIdx.x * 64;
+  const int64_t c0 = (int64_t)blockIdx.y * 64;
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int idx = q * 256 + t, row = idx >> 3, ch = idx & 7;
+    const int64_t r = r0 + row, c = c0 + ch * 8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < R && c < C) v = *(const uint4*)(in + r * ldi + c);
+    *(uint4*)(tile + row * P + ch * 8) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int idx = q * 256 + t, oc = idx >> 3, orr = idx & 7;
+    const int64_t c = c0 + oc, r = r0 + orr * 8;
+    if (c >= C || r >= Rp) continue;
+    uint16_t e[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) e[j] = tile[(orr * 8 + j) * P + oc];
+    uint4 o;
+    o.x = e[0] | ((uint32_t)e[1] << 16);
+    o.y = e[2] | ((uint32_t)e[3] << 16);
+    o.z = e[4] | ((uint32_t)e[5] << 16);
+    o.w = e[6] | ((uint32_t)e[7] << 16);
+    *(uint4*)(out + c * ldo + r) = o;
+  }
+}
+
 hipError_t launch_transpose(int elem_bytes, const void* in, int64_t R, int64_t C, int64_t ldi,
                             void* out, int64_t Rp, int64_t ldo, hipStream_t s) {
   if (Rp <= 0 || C <= 0) return hipSuccess;
   dim3 grid((unsigned)((Rp + 63) / 64), (unsigned)((C + 63) / 64));
+  const bool vec = elem_bytes == 2 && C % 8 == 0 && ldi % 8 == 0 && ldo % 8 == 0 && Rp % 8 == 0 &&
+                   ((uintptr_t)in & 15u) == 0 && ((uintptr_t)out & 15u) == 0;
+  if (vec) {
+    hipLaunchKernelGGL(transpose16_kernel, grid, dim3(256), 0, s, (const uint16_t*)in, R, C, ldi,
+                       (uint16_t*)out, Rp, ldo);
+    return hipGetLastError();
+  }
   if (elem_bytes == 2)
     hipLaunchKernelGGL(transpose_kernel<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)in, R, C,
                        ldi, (uint16_t*)out, Rp, ldo);
