@@ -119,12 +119,10 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   P->vt = kVocabTile;
   P->Vp = round_up(V, P->vt);
   P->fast = gemm_fast_path(dtype, d, P->Vp, P->Cp);
-  if (P->fast && gemm_vocab_tile(true) != P->vt) {
-    const int64_t vp = round_up(V, gemm_vocab_tile(true));
-    if (gemm_fast_path(dtype, d, vp, P->Cp)) {
-      P->vt = gemm_vocab_tile(true);
-      P->Vp = vp;
-    }
+  const int vt = gemm_vocab_tile(P->fast, V, P->Cp / kTokenTile);
+  if (vt != P->vt && gemm_fast_path(dtype, d, round_up(V, vt), P->Cp)) {
+    P->vt = vt;
+    P->Vp = round_up(V, vt);
   }
   P->dtile = gemm_d_tile(P->fast, d);
   P->n_vt = P->Vp / P->vt;

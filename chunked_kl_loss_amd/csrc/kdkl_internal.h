@@ -107,10 +107,11 @@ bool gemm_fast_path(int dtype, int64_t d, int64_t Vp, int64_t Cp);
 // N-tile width of the products whose N axis is the hidden size d (dH, dW):
 // 320 on the fast path when it pads d less than 256 does, else 256.
 int gemm_d_tile(bool fast, int64_t d);
-// Vocabulary tile (M-tile height) of the forward and dZ products: 384 on the
-// bf16 main loop (a 384 x 256 tile reads fewer operand bytes through LDS per
-// flop than 256 x 256), else 256.
-int gemm_vocab_tile(bool fast);
+// Vocabulary tile (M-tile height) of the forward and dZ products for V rows
+// and `token_tiles` 256-wide token tiles per launch: 384 on the bf16 main loop
+// when that takes fewer workgroup rounds' time (a 384 x 256 tile reads fewer
+// operand bytes through LDS per flop than 256 x 256), else 256.
+int gemm_vocab_tile(bool fast, int64_t V, int64_t token_tiles);
 
 struct MergeArgs {
   const float4* part;   // [Cp, n_vt]

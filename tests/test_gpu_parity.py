@@ -27,12 +27,14 @@ CASES = [
     # with a partial last tile, both with ragged vocabulary and chunk tails
     ("bf16_d_tile320_exact", "small_bf16", dict(N=130, d=960, V=2500, K=12, chunk=64, T=1.0), 11),
     ("bf16_d_tile320_ragged", "small_bf16", dict(N=200, d=576, V=3001, K=30, chunk=96, T=1.3), 10),
-    # the forward / dZ products tile the vocabulary by 384 rows on the bf16
-    # path: fewer rows than one tile, an exact multiple, and a last tile
-    # holding a single row
-    ("bf16_vtile384_small_V", "small_bf16", dict(N=90, d=128, V=300, K=10, chunk=64, T=1.0), 12),
-    ("bf16_vtile384_exact", "small_bf16", dict(N=150, d=192, V=1536, K=16, chunk=80, T=1.1), 13),
-    ("bf16_vtile384_one_row", "small_bf16", dict(N=120, d=256, V=1153, K=8, chunk=100, T=0.9), 14),
+    # bf16 main loop with a vocabulary smaller than one tile
+    ("bf16_fast_small_V", "small_bf16", dict(N=90, d=128, V=300, K=10, chunk=64, T=1.0), 12),
+    # launches large enough for 384-row vocabulary tiles on the forward / dZ
+    # products (one workgroup round of 384-row tiles against two of 256):
+    # an exact multiple of 384, and a last tile holding a single row with a
+    # ragged second chunk
+    ("bf16_vtile384_exact", "small_bf16", dict(N=2048, d=128, V=12288, K=16, chunk=2048, T=1.1), 13),
+    ("bf16_vtile384_one_row", "small_bf16", dict(N=2100, d=192, V=11905, K=8, chunk=2048, T=0.9), 14),
 ]
 
 
