@@ -317,6 +317,9 @@ def main():
                          "loss on a given logit grid; dense: the dense baseline (full grids)")
     ap.add_argument("--inplace", action="store_true",
                     help="logits path: write dZ over the logit grid")
+    ap.add_argument("--gen-reading", choices=("1based", "0based"), default="1based",
+                    help="reading of the workload list's cross-references for the teacher "
+                         "generator of the 8K and 256K workloads (1based: uniform ids, N(0, 2))")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -339,6 +342,8 @@ def main():
         w = w.with_(N=args.N)
     if args.chunk is not None:
         w = w.with_(chunk=args.chunk)
+    if args.gen_reading == "0based":
+        w = wl.other_reading(w)
     dev = torch.device("cuda:0")
     log(f"bench: generating {w.name} N={w.N} d={w.d} V={w.V} K={w.K} chunk={w.chunk} T={w.T}")
     t0 = time.time()
@@ -422,7 +427,7 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": w.name, "N": w.N, "d": w.d, "V": w.V, "K": w.K, "chunk": w.chunk,
                    "T": w.T, "teacher_ids": w.id_dist, "teacher_logit_var": w.logit_var,
-                   "parallelism": "single GPU"},
+                   "gen_reading": args.gen_reading, "parallelism": "single GPU"},
         "mfma_util_pct": round(mfma_pct, 2),
         "flop_per_step": flops_step,
         "peak_hbm_gib": round(peak_gib, 3),

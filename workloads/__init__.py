@@ -33,7 +33,7 @@ from typing import Dict, Optional
 import numpy as np
 import torch
 
-__all__ = ["Workload", "CONFIGS", "get_config", "generate", "seed_for"]
+__all__ = ["Workload", "CONFIGS", "get_config", "other_reading", "generate", "seed_for"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -75,6 +75,18 @@ CONFIGS: Dict[str, Workload] = {
     "longctx_256k": Workload("longctx_256k", 262144, 2880, 201088, 100, 4096,
                              2.0, "bf16", "uniform", 2.0, index=5),
 }
+
+
+def other_reading(w: Workload) -> Workload:
+    """The same workload under the 0-based reading of the cross-references
+    (the third workload takes the second one's teacher generator, Zipf ids
+    with logits N(0, 3); the fifth takes the fourth one's, Zipf with N(0, 4)).
+    Shapes and flops are unchanged; only the value distributions differ."""
+    if w.index == 3:
+        return w.with_(id_dist="zipf", logit_var=3.0)
+    if w.index == 5:
+        return w.with_(id_dist="zipf", logit_var=4.0)
+    return w
 
 
 def get_config(name: str) -> Workload:
