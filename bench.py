@@ -429,6 +429,9 @@ def main():
                    "T": w.T, "teacher_ids": w.id_dist, "teacher_logit_var": w.logit_var,
                    "gen_reading": args.gen_reading, "parallelism": "single GPU"},
         "mfma_util_pct": round(mfma_pct, 2),
+        # the same time against the 6 N V d flop of forward + dH + dW alone
+        # (the recompute is part of the method and counted above)
+        "mfma_util_pct_without_recompute": round(mfma_pct * 0.75, 2),
         "flop_per_step": flops_step,
         "peak_hbm_gib": round(peak_gib, 3),
         "workspace_gib": {"forward": round(fb / 2**30, 3), "backward": round(bb / 2**30, 3)},
