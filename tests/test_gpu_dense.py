@@ -36,6 +36,8 @@ CASES = [
     ("dense_tiny_fp32", "tiny_fp32", dict(N=70, d=72, V=1000, K=7, T=0.7), 41),
     ("dense_bf16_ragged", "small_bf16", dict(N=300, d=576, V=3001, K=20, T=1.3), 42),
     ("dense_bf16_tile256", "small_bf16", dict(N=257, d=256, V=4096, K=100, T=1.0), 43),
+    # large enough for 384-row vocabulary tiles on the projection
+    ("dense_bf16_vtile384", "small_bf16", dict(N=2048, d=128, V=11905, K=16, T=1.2), 45),
 ]
 
 
