@@ -32,6 +32,7 @@ __all__ = [
     "dense_sizes",
     "dense_forward",
     "dense_backward",
+    "check_ids",
     "profile_begin",
     "profile_end",
     "KdklError",
@@ -231,6 +232,25 @@ class ForwardChunkedKLLoss(torch.autograd.Function):
 def forward_chunked_kl_loss(Z, ids, logits, T: float = 1.0):
     """Mean over positions of KL(teacher top-K || softmax(Z / T)), differentiable in Z."""
     return ForwardChunkedKLLoss.apply(Z, ids, logits, T)
+
+
+CHECK_IDS_WORKSPACE = 16384  # KDKL_CHECK_IDS_WORKSPACE
+
+
+def check_ids(ids, V: int, *, stream=None) -> Tuple[int, int]:
+    """``kdkl_check_ids``: (ids outside [0, V), positions holding a repeated
+    id), both over the kept positions; synchronises the stream to read them."""
+    _need_gpu(ids)
+    if ids.dim() != 2 or ids.dtype != torch.int32 or not ids.is_contiguous():
+        raise ValueError("ids must be a contiguous int32 [N, K] tensor")
+    N, K = ids.shape
+    counts = torch.zeros(2, dtype=torch.int64, device=ids.device)
+    ws = torch.empty(CHECK_IDS_WORKSPACE, dtype=torch.uint8, device=ids.device)
+    check(_load().kdkl_check_ids(_ptr(ids), N, K, int(V), _ptr(counts), _ptr(ws), ws.numel(),
+                                 _stream(ids.device, stream)),
+          "kdkl_check_ids")
+    c = counts.cpu()
+    return int(c[0]), int(c[1])
 
 
 def dense_sizes(N: int, d: int, V: int, K: int, dtype: torch.dtype) -> Tuple[int, int, int]:

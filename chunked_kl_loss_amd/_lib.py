@@ -59,6 +59,7 @@ SIGNATURES = {
                                      _P, _P, _P, _P, C.c_size_t, _P, C.c_size_t, _P]),
     "kdkl_dense_backward": (C.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, C.c_float, C.c_int,
                                       _P, C.c_size_t, _P, _P, _P, C.c_int, _P, C.c_size_t, _P]),
+    "kdkl_check_ids": (C.c_int, [_P, _I64, _I32, _I64, _P, _P, C.c_size_t, _P]),
     "kdkl_profile_begin": (C.c_int, []),
     "kdkl_profile_end": (C.c_int, [C.POINTER(KernelStat), C.c_int, C.POINTER(C.c_int)]),
 }

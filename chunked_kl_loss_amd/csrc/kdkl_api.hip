@@ -450,6 +450,21 @@ kdkl_status kdkl_logits_backward(const void* Z, const int32_t* ids, const float*
   return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
 }
 
+// --------------------------- teacher-id check ------------------------------
+
+kdkl_status kdkl_check_ids(const int32_t* ids, int64_t N, int32_t K, int64_t V, int64_t* counts,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (N < 0 || K < 1 || K > 1024 || V <= 0) return KDKL_ERR_SHAPE;
+  if (N > ((int64_t)1 << 40) || V > ((int64_t)1 << 40)) return KDKL_ERR_OVERFLOW;
+  if (!counts || !workspace || (N > 0 && !ids)) return KDKL_ERR_NULL;
+  if (((uintptr_t)counts & 7u) || ((uintptr_t)workspace & 7u)) return KDKL_ERR_ALIGN;
+  if (workspace_bytes < (size_t)KDKL_CHECK_IDS_WORKSPACE) return KDKL_ERR_WORKSPACE;
+  static_assert(KDKL_CHECK_IDS_WORKSPACE >= kCheckIdsMaxBlocks * 2 * 8, "workspace holds every partial");
+  hipStream_t s = (hipStream_t)stream;
+  const hipError_t e = launch_check_ids(N > 0 ? ids : nullptr, N, K, V, workspace, counts, s);
+  return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
+}
+
 // ------------------------------ dense KL ------------------------------------
 // The pages' correctness baseline: the full student log-probability grid and
 // the full teacher probability grid are built, compared grid-wide and kept

@@ -138,6 +138,13 @@ hipError_t launch_transpose(int elem_bytes, const void* in, int64_t R, int64_t C
                             int64_t ldi, void* out, int64_t Rp, int64_t ldo,
                             hipStream_t s);
 hipError_t launch_zero(float* p, int64_t n, hipStream_t s);
+// Teacher-id validation (kdkl_check_ids): at most kCheckIdsMaxBlocks blocks
+// write two int64 partial counts each into `partial`, then one block sums
+// them in a fixed order into out[0..1].
+constexpr int kCheckIdsMaxBlocks = 1024;
+int check_ids_blocks(int64_t N);
+hipError_t launch_check_ids(const int32_t* ids, int64_t N, int K, int64_t V, void* partial, int64_t* out,
+                            hipStream_t s);
 hipError_t launch_dh_reduce(int dtype, const float* part, int splits, int rows,
                             int64_t d, int64_t Cp, void* dH, hipStream_t s);
 

@@ -71,6 +71,8 @@ extern "C" {
 #define KDKL_ABI_VERSION 1
 /* Bytes of device workspace kdkl_logits_backward needs (any N, V, K). */
 #define KDKL_LOGITS_BWD_WORKSPACE 256
+/* Bytes of device workspace kdkl_check_ids needs (any N, V, K). */
+#define KDKL_CHECK_IDS_WORKSPACE 16384
 
 typedef enum {
   KDKL_OK = 0,
@@ -197,6 +199,19 @@ kdkl_status kdkl_dense_backward(const void* H, const void* W,
                                 const float* grad_loss, void* dH, float* dW,
                                 int accumulate_dW, void* workspace,
                                 size_t workspace_bytes, void* stream);
+/* ---- optional validation of the teacher ids --------------------------------
+ * kdkl_check_ids: counts, over the kept positions (first id not -1), the ids
+ * outside [0, V) and the positions holding some id more than once, and writes
+ * them to counts[0] and counts[1] (int64, DEVICE memory). The loss does not
+ * need this: it drops out-of-range ids and adds the mass of repeated ones
+ * (see the preconditions above); the check tells a caller whether its cache
+ * breaks the pages' setting of K distinct in-vocabulary ids per position.
+ * The workspace (>= KDKL_CHECK_IDS_WORKSPACE bytes, caller-owned) and counts
+ * must be 8-byte aligned. K in [1, 1024]; N = 0 writes zero counts. Enqueued
+ * on `stream`, deterministic; the host reads the counts after synchronising. */
+kdkl_status kdkl_check_ids(const int32_t* topk_ids, int64_t N, int32_t K, int64_t V,
+                           int64_t* counts, void* workspace, size_t workspace_bytes,
+                           void* stream);
 /* ---- measurement aid: per-kernel timing with HIP events ------------------
  * Between kdkl_profile_begin() and kdkl_profile_end(), every kernel launched
  * by the compute calls is bracketed by two HIP events recorded on

@@ -282,3 +282,38 @@ def dbwd(lib, **kw):
 ])
 def test_dense_calls_reject_bad_arguments(lib, call, kw, status):
     assert call(lib, **kw) == status
+
+
+# --- teacher-id validation entry point -------------------------------------------
+
+def chk(lib, **kw):
+    a = dict(ids=FAKE, N=64, K=8, V=1000, counts=FAKE, ws=FAKE, wsb=16384, stream=None)
+    a.update(kw)
+    return lib.kdkl_check_ids(a["ids"], a["N"], a["K"], a["V"], a["counts"], a["ws"], a["wsb"],
+                              a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ids=None), NULL),
+    (dict(counts=None), NULL),
+    (dict(ws=None), NULL),
+    (dict(K=0), SHAPE),
+    (dict(K=1025), SHAPE),
+    (dict(V=0), SHAPE),
+    (dict(N=-1), SHAPE),
+    (dict(N=1 << 41), OVERFLOW),
+    (dict(counts=FAKE + 4), ALIGN),
+    (dict(ws=FAKE + 4), ALIGN),
+    (dict(wsb=16383), WORKSPACE),
+])
+def test_check_ids_rejects_bad_arguments(lib, kw, status):
+    assert chk(lib, **kw) == status
+
+
+def test_check_ids_binding_refuses_cpu_tensors():
+    import torch
+
+    import chunked_kl_loss_amd as kd
+
+    with pytest.raises(ValueError):
+        kd.check_ids(torch.zeros(4, 2, dtype=torch.int32), 16)
