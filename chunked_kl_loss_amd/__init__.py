@@ -63,6 +63,18 @@ def _need_gpu(*ts):
             raise ValueError("inputs must be contiguous tensors on a ROCm device")
 
 
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
+def _want(t, shape, dtype, device, name):
+    """A caller-provided output must match exactly: the library writes it
+    through a raw pointer."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} on {device}, "
+                         f"got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
 def workspace_size(N: int, d: int, V: int, K: int, chunk: int, dtype: torch.dtype) -> Tuple[int, int]:
     """(forward bytes, backward bytes) of device workspace."""
     f = C.c_size_t()
@@ -95,12 +107,17 @@ def kdkl_forward(H, W, ids, logits, T: float, chunk: int, *, loss=None, row_lse=
         row_lse = torch.empty(N, dtype=torch.float32, device=dev)
     if row_kl is None and want_row_kl:
         row_kl = torch.empty(N, dtype=torch.float32, device=dev)
+    _want(loss, (1,), torch.float32, dev, "loss")
+    _want(row_lse, (N,), torch.float32, dev, "row_lse")
+    if row_kl is not None:
+        _want(row_kl, (N,), torch.float32, dev, "row_kl")
     fb, _ = workspace_size(N, d, V, K, chunk, H.dtype)
     if workspace is None:
         workspace = torch.empty(fb, dtype=torch.uint8, device=dev)
+    _need_gpu(workspace)
     check(_load().kdkl_forward(_ptr(H), _ptr(W), _ptr(ids), _ptr(logits), N, d, V, K,
                               float(T), chunk, _dtype_code(H), _ptr(loss), _ptr(row_lse),
-                              _ptr(row_kl), _ptr(workspace), workspace.numel(),
+                              _ptr(row_kl), _ptr(workspace), _nbytes(workspace),
                               _stream(dev, stream)),
           "kdkl_forward")
     return loss, row_lse, row_kl
@@ -118,13 +135,19 @@ def kdkl_backward(H, W, ids, logits, T: float, chunk: int, row_lse, grad_loss=No
         dW = torch.empty((V, d), dtype=torch.float32, device=dev)
     if grad_loss is not None and grad_loss.dtype != torch.float32:
         raise TypeError("grad_loss must be float32")
+    _want(row_lse, (N,), torch.float32, dev, "row_lse")
+    _want(dH, tuple(H.shape), H.dtype, dev, "dH")
+    _want(dW, (V, d), torch.float32, dev, "dW")
+    if grad_loss is not None:
+        _want(grad_loss, (1,), torch.float32, dev, "grad_loss")
     _, bb = workspace_size(N, d, V, K, chunk, H.dtype)
     if workspace is None:
         workspace = torch.empty(bb, dtype=torch.uint8, device=dev)
+    _need_gpu(workspace)
     check(_load().kdkl_backward(_ptr(H), _ptr(W), _ptr(ids), _ptr(logits), N, d, V, K,
                                float(T), chunk, _dtype_code(H), _ptr(row_lse),
                                _ptr(grad_loss), _ptr(dH), _ptr(dW), int(bool(accumulate_dW)),
-                               _ptr(workspace), workspace.numel(), _stream(dev, stream)),
+                               _ptr(workspace), _nbytes(workspace), _stream(dev, stream)),
           "kdkl_backward")
     return dH, dW
 
@@ -179,6 +202,9 @@ def logits_forward(Z, ids, logits, T: float, *, loss=None, row_lse=None, row_kl=
         row_lse = torch.empty(N, dtype=torch.float32, device=dev)
     if row_kl is None:
         row_kl = torch.empty(N, dtype=torch.float32, device=dev)
+    _want(loss, (1,), torch.float32, dev, "loss")
+    _want(row_lse, (N,), torch.float32, dev, "row_lse")
+    _want(row_kl, (N,), torch.float32, dev, "row_kl")
     check(_load().kdkl_logits_forward(_ptr(Z), _ptr(ids), _ptr(logits), N, V, K, float(T),
                                       _dtype_code(Z), _ptr(loss), _ptr(row_lse), _ptr(row_kl),
                                       _stream(dev, stream)),
@@ -201,11 +227,15 @@ def logits_backward(Z, ids, logits, T: float, row_lse, grad_loss=None, *, dZ=Non
         raise ValueError("dZ must be a contiguous tensor of Z's shape and dtype")
     if grad_loss is not None and grad_loss.dtype != torch.float32:
         raise TypeError("grad_loss must be float32")
+    _want(row_lse, (N,), torch.float32, Z.device, "row_lse")
+    if grad_loss is not None:
+        _want(grad_loss, (1,), torch.float32, Z.device, "grad_loss")
     if workspace is None:
         workspace = torch.empty(LOGITS_BWD_WORKSPACE, dtype=torch.uint8, device=Z.device)
+    _need_gpu(workspace)
     check(_load().kdkl_logits_backward(_ptr(Z), _ptr(ids), _ptr(logits), N, V, K, float(T),
                                        _dtype_code(Z), _ptr(row_lse), _ptr(grad_loss),
-                                       _ptr(dZ), _ptr(workspace), workspace.numel(),
+                                       _ptr(dZ), _ptr(workspace), _nbytes(workspace),
                                        _stream(Z.device, stream)),
           "kdkl_logits_backward")
     return dZ
@@ -246,7 +276,7 @@ def check_ids(ids, V: int, *, stream=None) -> Tuple[int, int]:
     N, K = ids.shape
     counts = torch.zeros(2, dtype=torch.int64, device=ids.device)
     ws = torch.empty(CHECK_IDS_WORKSPACE, dtype=torch.uint8, device=ids.device)
-    check(_load().kdkl_check_ids(_ptr(ids), N, K, int(V), _ptr(counts), _ptr(ws), ws.numel(),
+    check(_load().kdkl_check_ids(_ptr(ids), N, K, int(V), _ptr(counts), _ptr(ws), _nbytes(ws),
                                  _stream(ids.device, stream)),
           "kdkl_check_ids")
     c = counts.cpu()
@@ -275,9 +305,13 @@ def dense_forward(H, W, ids, logits, T: float, *, saved=None, loss=None, row_lse
     row_kl = torch.empty(N, dtype=torch.float32, device=dev) if row_kl is None else row_kl
     saved = torch.empty(sb, dtype=torch.uint8, device=dev) if saved is None else saved
     workspace = torch.empty(fb, dtype=torch.uint8, device=dev) if workspace is None else workspace
+    _want(loss, (1,), torch.float32, dev, "loss")
+    _want(row_lse, (N,), torch.float32, dev, "row_lse")
+    _want(row_kl, (N,), torch.float32, dev, "row_kl")
+    _need_gpu(saved, workspace)
     check(_load().kdkl_dense_forward(_ptr(H), _ptr(W), _ptr(ids), _ptr(logits), N, d, V, K, float(T),
                                      _dtype_code(H), _ptr(loss), _ptr(row_lse), _ptr(row_kl),
-                                     _ptr(saved), saved.numel(), _ptr(workspace), workspace.numel(),
+                                     _ptr(saved), _nbytes(saved), _ptr(workspace), _nbytes(workspace),
                                      _stream(dev, stream)),
           "kdkl_dense_forward")
     return loss, row_lse, row_kl, saved
@@ -295,10 +329,15 @@ def dense_backward(H, W, ids, logits, T: float, saved, grad_loss=None, *, dH=Non
     if grad_loss is not None and grad_loss.dtype != torch.float32:
         raise TypeError("grad_loss must be float32")
     workspace = torch.empty(bb, dtype=torch.uint8, device=dev) if workspace is None else workspace
+    _want(dH, tuple(H.shape), H.dtype, dev, "dH")
+    _want(dW, (V, d), torch.float32, dev, "dW")
+    if grad_loss is not None:
+        _want(grad_loss, (1,), torch.float32, dev, "grad_loss")
+    _need_gpu(workspace)
     check(_load().kdkl_dense_backward(_ptr(H), _ptr(W), _ptr(ids), _ptr(logits), N, d, V, K,
-                                      float(T), _dtype_code(H), _ptr(saved), saved.numel(),
+                                      float(T), _dtype_code(H), _ptr(saved), _nbytes(saved),
                                       _ptr(grad_loss), _ptr(dH), _ptr(dW), int(bool(accumulate_dW)),
-                                      _ptr(workspace), workspace.numel(), _stream(dev, stream)),
+                                      _ptr(workspace), _nbytes(workspace), _stream(dev, stream)),
           "kdkl_dense_backward")
     return dH, dW
 

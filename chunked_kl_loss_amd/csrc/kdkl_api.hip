@@ -56,13 +56,21 @@ hipError_t timed(int kid, double flops, double bytes, hipStream_t s, F&& launch)
   if (!g_prof.on) return launch();
   std::lock_guard<std::mutex> lk(g_prof.mu);
   hipEvent_t a = prof_event(), b = prof_event();
-  if (!a || !b) return hipErrorOutOfMemory;
+  auto give_back = [&] {  // events not recorded go back to the pool
+    if (a) g_prof.pool.push_back(a);
+    if (b) g_prof.pool.push_back(b);
+  };
+  if (!a || !b) {
+    give_back();
+    return hipErrorOutOfMemory;
+  }
   hipError_t e = hipEventRecord(a, s);
-  if (e != hipSuccess) return e;
-  e = launch();
-  if (e != hipSuccess) return e;
-  e = hipEventRecord(b, s);
-  if (e != hipSuccess) return e;
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(b, s);
+  if (e != hipSuccess) {
+    give_back();
+    return e;
+  }
   g_prof.recs.push_back({kid, a, b, flops, bytes});
   return hipSuccess;
 }
