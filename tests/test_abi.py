@@ -317,3 +317,19 @@ def test_check_ids_binding_refuses_cpu_tensors():
 
     with pytest.raises(ValueError):
         kd.check_ids(torch.zeros(4, 2, dtype=torch.int32), 16)
+
+
+def test_binding_output_checks():
+    """Caller-provided outputs are written through raw pointers: the binding
+    refuses any whose shape, dtype or layout differs from what the call
+    writes (host-side check, no device needed)."""
+    import torch
+
+    import chunked_kl_loss_amd as kd
+
+    cpu = torch.device("cpu")
+    kd._want(torch.zeros(4, 3), (4, 3), torch.float32, cpu, "ok")
+    for bad in (torch.zeros(3, 4), torch.zeros(4, 3, dtype=torch.bfloat16), torch.zeros(3, 4).t()):
+        with pytest.raises(ValueError):
+            kd._want(bad, (4, 3), torch.float32, cpu, "dW")
+    assert kd._nbytes(torch.zeros(5, dtype=torch.float32)) == 20
