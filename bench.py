@@ -317,6 +317,8 @@ def main():
                          "loss on a given logit grid; dense: the dense baseline (full grids)")
     ap.add_argument("--inplace", action="store_true",
                     help="logits path: write dZ over the logit grid")
+    ap.add_argument("--seed", type=int, default=None,
+                    help="seed of the synthetic inputs (default: the workload's own, 1000 + its number)")
     ap.add_argument("--gen-reading", choices=("1based", "0based"), default="1based",
                     help="reading of the workload list's cross-references for the teacher "
                          "generator of the 8K and 256K workloads (1based: uniform ids, N(0, 2))")
@@ -347,7 +349,7 @@ def main():
     dev = torch.device("cuda:0")
     log(f"bench: generating {w.name} N={w.N} d={w.d} V={w.V} K={w.K} chunk={w.chunk} T={w.T}")
     t0 = time.time()
-    x = wl.generate(w)
+    x = wl.generate(w, seed=args.seed)
     log(f"bench: inputs generated in {time.time() - t0:.1f} s")
     torch.cuda.set_device(dev)
     if args.path == "logits":
@@ -427,7 +429,9 @@ def main():
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": w.name, "N": w.N, "d": w.d, "V": w.V, "K": w.K, "chunk": w.chunk,
                    "T": w.T, "teacher_ids": w.id_dist, "teacher_logit_var": w.logit_var,
-                   "gen_reading": args.gen_reading, "parallelism": "single GPU"},
+                   "gen_reading": args.gen_reading,
+                   "seed": args.seed if args.seed is not None else wl.seed_for(w),
+                   "parallelism": "single GPU"},
         "mfma_util_pct": round(mfma_pct, 2),
         # the same time against the 6 N V d flop of forward + dH + dW alone
         # (the recompute is part of the method and counted above)
