@@ -970,6 +970,28 @@ __device__ __forceinline__ void phase_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// ds_read_b64_tr_b16 as assembly. For the builtin form the compiler's
+// wait-count pass knows no address, so it waits for every outstanding
+// direct-to-LDS stage load (vmcnt(0)) before each such read, twice per
+// k-step, although a stage being read is never the one in flight. Issued
+// here as plain assembly, the reads' results are waited for explicitly by
+// lds_ready before the MFMAs that use them.
+__device__ __forceinline__ s16x4_t ds_read_tr16(const char* p) {
+  const uint32_t a = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+  s16x4_t v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(v) : "v"(a) : "memory");
+  return v;
+}
+
+// Waits for every outstanding LDS access, then ties the fragments to the
+// wait so that their uses stay after it.
+template <int N>
+__device__ __forceinline__ void lds_ready(bf16x8_t (&f)[N]) {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(f[i]));
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -1122,7 +1144,7 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
       for (int j2 = 0; j2 < 2; ++j2) {
         const int k = kk * 16 + 8 * (lane >> 5) + 4 * j2 + ((lane & 15) >> 2);
         const int pq = q ^ (8 * (k & 3));
-        const s16x4_t h = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(s + k * 512 + pq * 8));
+        const s16x4_t h = ds_read_tr16(s + k * 512 + pq * 8);
         const bf16x4_t hb = __builtin_bit_cast(bf16x4_t, h);
         v[4 * j2 + 0] = hb[0];
         v[4 * j2 + 1] = hb[1];
@@ -1156,6 +1178,12 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
       const bool more = kt + NSTAGE - 1 < nk;
 #pragma unroll
       for (int kk = 0; kk < KG; ++kk) {
+        // fragments of this k-group read through the transpose (assembly,
+        // issued one k-group earlier) are waited for before anything else;
+        // the fence keeps the previous k-group's MFMAs ahead of that wait
+        if constexpr (LA == LAYOUT_MC || LB == LAYOUT_MC) __builtin_amdgcn_sched_barrier(0);
+        if constexpr (LA == LAYOUT_MC) lds_ready(fa[kk & 1]);
+        if constexpr (LB == LAYOUT_MC) lds_ready(fb[SB ? 0 : (kk & 1)]);
         if (more) {
 #pragma unroll
           for (int part = 0; part < NPART; ++part)
