@@ -92,13 +92,42 @@ struct Plan {
   int64_t n_vt;    // vocabulary tiles
   int dh_splits;
   int64_t dh_ksplit;
+  // The backward visits `bg` consecutive chunks at a time ("group", token
+  // capacity Cg) in n_parts slices of the vocabulary, vpart rows each: the dZ
+  // buffer [Cg, vpart] holds as many elements as one chunk's [Cp, Vp], and dW
+  // takes one read-modify-write per group and slice instead of one per chunk.
+  int bg;
+  int64_t Cg;
+  int64_t vpart;
+  int n_parts;
   bool fast;       // bf16 main loop: reads W, H and dZ in place (no transposes)
   int dtile;       // N-tile width of the dH and dW products (hidden-size axis)
   // offsets into the forward workspace
   size_t f_sids, f_sp, f_erow, f_keep, f_tstart, f_part, f_rowkl, f_bytes;
   // offsets into the backward workspace
-  size_t b_sids, b_sp, b_erow, b_keep, b_scale, b_tstart, b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart, b_bytes;
+  size_t b_sids, b_sp, b_erow, b_keep, b_scale, b_tstart, b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart, b_dhacc, b_bytes;
 };
+
+#ifndef KDKL_DH_BUSY
+#define KDKL_DH_BUSY 0.97
+#endif
+#ifndef KDKL_BWD_GROUP
+#define KDKL_BWD_GROUP 4
+#endif
+
+// Chunks per backward group on the bf16 main loop. Each vocabulary slice of a
+// group must still give the dW product at least two rounds of workgroups
+// (one per compute unit), or the partial last round costs more than the
+// read-modify-writes saved; and a group never spans more rows than there are.
+static int backward_group(const Plan& P, int64_t N) {
+  int bg = KDKL_BWD_GROUP;
+  if (!P.fast || bg < 2) return 1;
+  const int64_t chunks = (N + P.chunk - 1) / P.chunk;
+  while (bg > 1 && (bg > chunks || (P.V / bg / 256) * ((P.d + P.dtile - 1) / P.dtile) < 2 * kComputeUnits ||
+                    !gemm_fast_path(P.dtype, P.d, P.Vp, round_up(bg * P.chunk, kTokenTile))))
+    bg >>= 1;
+  return bg;
+}
 
 static bool mul_ok(int64_t a, int64_t b, int64_t* out) {
   return !__builtin_mul_overflow(a, b, out) && *out >= 0;
@@ -134,25 +163,38 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   }
   P->dtile = gemm_d_tile(P->fast, d);
   P->n_vt = P->Vp / P->vt;
-  if (P->Cp > INT32_MAX / 2) return KDKL_ERR_OVERFLOW;
-  // dH split-K: the number of splits S that makes the launch cheapest when
-  // every workgroup does 1/S of a tile's work and the 256 compute units of
-  // the device take them in rounds: minimise ceil(tiles * S / 256) / S (ties
-  // to the smaller S, fewer partials), with each split at least 8 k-steps.
-  const int64_t tiles = ((P->Cp + 255) / 256) * ((d + P->dtile - 1) / P->dtile);
+  if (P->Cp > INT32_MAX / 4) return KDKL_ERR_OVERFLOW;
+  P->bg = backward_group(*P, N);
+  P->Cg = round_up(P->bg * P->chunk, kTokenTile);
+  if (P->bg == 1) {
+    P->Cg = P->Cp;
+    P->vpart = P->Vp;
+  } else {
+    // slices start on a tile boundary of both the dZ product (vt rows) and
+    // the dW product (256 rows)
+    const int64_t align = P->vt % 256 == 0 ? P->vt : P->vt * 2;
+    P->vpart = round_up((V + P->bg - 1) / P->bg, align);
+  }
+  P->n_parts = (int)((V + P->vpart - 1) / P->vpart);
+  // dH split-K: the fewest splits S whose launch keeps the 256 compute units
+  // within 3% as busy as the best S does, when every workgroup does 1/S of a
+  // tile's work and the units take them in rounds (fewer splits, fewer fp32
+  // partials), with each split at least 8 k-steps.
+  const int64_t tiles = ((P->Cg + 255) / 256) * ((d + P->dtile - 1) / P->dtile);
   const int64_t kstep = dtype == KDKL_BF16 ? 64 : 32;
-  int64_t smax = P->Vp / (8 * kstep);
+  int64_t smax = P->vpart / (8 * kstep);
   if (smax > 16) smax = 16;
   if (smax < 1) smax = 1;
+  auto busy = [&](int64_t c) {  // share of the rounds' workgroup slots in use
+    const int64_t r = (tiles * c + kComputeUnits - 1) / kComputeUnits;
+    return (double)(tiles * c) / (double)(r * kComputeUnits);
+  };
+  double best = 0.0;
+  for (int64_t c = 1; c <= smax; ++c) best = busy(c) > best ? busy(c) : best;
   int64_t S = 1;
-  for (int64_t c = 2; c <= smax; ++c) {
-    // rounds(c) / c < rounds(S) / S, compared without division
-    const int64_t rc = (tiles * c + kComputeUnits - 1) / kComputeUnits;
-    const int64_t rs = (tiles * S + kComputeUnits - 1) / kComputeUnits;
-    if (rc * S < rs * c) S = c;
-  }
+  while (S < smax && busy(S) < KDKL_DH_BUSY * best) ++S;
   P->dh_splits = (int)S;
-  P->dh_ksplit = round_up((P->Vp + S - 1) / S, kstep);
+  P->dh_ksplit = round_up((P->vpart + S - 1) / S, kstep);
 
   int64_t t0, t1, t2;
   size_t cur = 0;
@@ -168,14 +210,17 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   P->f_bytes = cur;
 
   cur = 0;
-  ok &= region(&cur, t0, &P->b_sids) && region(&cur, t0, &P->b_sp);
-  ok &= region(&cur, P->Cp * 4, &P->b_erow) && region(&cur, P->Cp * 4, &P->b_keep);
+  int64_t g0, g1;
+  ok &= mul_ok(P->Cg, K, &g0) && mul_ok(g0, 4, &g0);
+  ok &= mul_ok(P->n_vt + 1, P->Cg, &g1) && mul_ok(g1, 2, &g1);
+  ok &= region(&cur, g0, &P->b_sids) && region(&cur, g0, &P->b_sp);
+  ok &= region(&cur, P->Cg * 4, &P->b_erow) && region(&cur, P->Cg * 4, &P->b_keep);
   ok &= region(&cur, 16, &P->b_scale);
-  ok &= region(&cur, t1, &P->b_tstart);
+  ok &= region(&cur, g1, &P->b_tstart);
   int64_t wt, ht, dz, dhp;
   ok &= mul_ok(d, P->Vp, &wt) && mul_ok(wt, P->es, &wt);
-  ok &= mul_ok(d, P->Cp, &ht) && mul_ok(ht, P->es, &ht);
-  ok &= mul_ok(P->Cp, P->Vp, &dz) && mul_ok(dz, P->es, &dz);
+  ok &= mul_ok(d, P->Cg, &ht) && mul_ok(ht, P->es, &ht);
+  ok &= mul_ok(P->Cg, P->vpart, &dz) && mul_ok(dz, P->es, &dz);
   if (P->fast) {
     // dW reads the token-major dZ in place through the LDS transpose and
     // H_c^T (one small transpose per chunk); dH reads W^T, transposed once
@@ -189,8 +234,14 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
     ok &= region(&cur, ht, &P->b_ht);
     ok &= region(&cur, dz, &P->b_dzcv) && region(&cur, dz, &P->b_dzvc);
   }
-  ok &= mul_ok(S * P->Cp, d, &dhp) && mul_ok(dhp, 4, &dhp);
+  ok &= mul_ok(S * P->Cg, d, &dhp) && mul_ok(dhp, 4, &dhp);
   ok &= region(&cur, dhp, &P->b_dhpart);
+  P->b_dhacc = 0;
+  if (P->n_parts > 1) {
+    int64_t acc;
+    ok &= mul_ok(P->Cg, d, &acc) && mul_ok(acc, 4, &acc);
+    ok &= region(&cur, acc, &P->b_dhacc);
+  }
   P->b_bytes = cur;
   return ok ? KDKL_OK : KDKL_ERR_OVERFLOW;
 }
@@ -207,11 +258,11 @@ static kdkl_status check_common(const void* H, const void* W, const int32_t* ids
 }
 
 static TeacherArgs teacher_args(const Plan& P, const int32_t* ids, const float* lg, float T, int64_t r0,
-                                int rows, char* ws, size_t o_sids, size_t o_sp, size_t o_erow,
+                                int rows, int64_t pitch, char* ws, size_t o_sids, size_t o_sp, size_t o_erow,
                                 size_t o_keep, size_t o_tstart) {
   TeacherArgs t;
   t.ids = ids; t.logits = lg; t.r0 = r0; t.rows = rows; t.K = (int)P.K;
-  t.inv_T = 1.0f / T; t.vt = P.vt; t.n_vt = (int)P.n_vt; t.Cp = P.Cp;
+  t.inv_T = 1.0f / T; t.vt = P.vt; t.n_vt = (int)P.n_vt; t.Cp = pitch;
   t.sids = (int32_t*)(ws + o_sids); t.sp = (float*)(ws + o_sp);
   t.erow = (float*)(ws + o_erow); t.keep = (float*)(ws + o_keep); t.tstart = (uint16_t*)(ws + o_tstart);
   return t;
@@ -286,7 +337,7 @@ kdkl_status kdkl_forward(const void* H, const void* W, const int32_t* ids, const
   for (int64_t r0 = 0; r0 < N && e == hipSuccess; r0 += P.chunk) {
     const int rows = (int)((N - r0) < P.chunk ? (N - r0) : P.chunk);
     TeacherArgs ta =
-        teacher_args(P, ids, lg, T, r0, rows, ws, P.f_sids, P.f_sp, P.f_erow, P.f_keep, P.f_tstart);
+        teacher_args(P, ids, lg, T, r0, rows, P.Cp, ws, P.f_sids, P.f_sp, P.f_erow, P.f_keep, P.f_tstart);
     e = timed(K_TEACHER, 0.0, (double)rows * P.K * 8.0 * 2.0, s, [&] { return launch_teacher(ta, s); });
     if (e != hipSuccess) break;
     GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.f_sids, P.f_sp, P.f_tstart);
@@ -306,47 +357,66 @@ kdkl_status kdkl_forward(const void* H, const void* W, const int32_t* ids, const
   return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
 }
 
-// dH and dW (+)= of one chunk of rows [r0, r0 + rows) from its dZ in the
-// backward workspace (token-major; vocabulary-major too on the generic path),
-// W^T and H_c^T: dH_c = dZ_c W split over the vocabulary and summed in a fixed
-// order, dW (+)= dZ_c^T H_c.
-static hipError_t chunk_products(const Plan& P, int dtype, char* ws, int64_t r0, int rows, void* dH, float* dW,
-                               bool accumulate, hipStream_t s) {
-  const int64_t d = P.d, V = P.V;
+// dW_slice (+)= dZ^T H_g for vocabulary slice `part` of one group of rows.
+static hipError_t dw_product(const Plan& P, int dtype, char* ws, int rows, int part, float* dW, bool accumulate,
+                             hipStream_t s) {
+  const int64_t d = P.d;
+  const int64_t v0 = part * P.vpart;
+  const int64_t vlen = P.V - v0 < P.vpart ? P.V - v0 : P.vpart;
   const int64_t rows_pad = round_up(rows, kTokenTile);
-  const double fl = 2.0 * rows * (double)V * d;
-  // dH_c = dZ_c W  (split over the vocabulary, then a fixed-order sum)
-  GemmArgs h;
-  memset(&h, 0, sizeof(h));
-  h.A = ws + P.b_dzcv; h.lda = P.Vp; h.a_layout = LAYOUT_KC;
-  h.B = ws + P.b_wt; h.ldb = P.Vp; h.b_layout = LAYOUT_KC;
-  h.M = rows; h.N = (int)d; h.k_end = P.Vp; h.k_split = P.dh_ksplit;
-  h.tiles_m = (int)((rows + 255) / 256); h.tiles_n = (int)((d + P.dtile - 1) / P.dtile); h.bn = P.dtile;
-  h.splits = (int)((P.Vp + P.dh_ksplit - 1) / P.dh_ksplit);
-  h.out = (float*)(ws + P.b_dhpart); h.ldo = d; h.Cp = P.Cp;
-  const int splits = h.splits;
-  hipError_t e = timed(K_DH_GEMM, fl, ((double)V * rows + (double)V * d) * P.es + 4.0 * splits * rows * d, s,
-            [&] { return launch_gemm(dtype, EPI_DH, h, s); });
-  if (e != hipSuccess) return e;
-  void* dHc = (char*)dH + r0 * d * P.es;
-  e = timed(K_DH_REDUCE, 0.0, 4.0 * splits * rows * d + (double)rows * d * P.es, s, [&] {
-    return launch_dh_reduce(dtype, (const float*)(ws + P.b_dhpart), splits, rows, d, P.Cp, dHc, s);
-  });
-  if (e != hipSuccess) return e;
-  // dW (+)= dZ_c^T H_c
+  const double fl = 2.0 * rows * (double)vlen * d;
   GemmArgs w;
   memset(&w, 0, sizeof(w));
   if (P.fast) {
-    w.A = ws + P.b_dzcv; w.lda = P.Vp; w.a_layout = LAYOUT_MC; w.a_krows = P.Cp; w.a_mcols = P.Vp;
+    w.A = ws + P.b_dzcv; w.lda = P.vpart; w.a_layout = LAYOUT_MC; w.a_krows = P.Cg; w.a_mcols = P.vpart;
   } else {
-    w.A = ws + P.b_dzvc; w.lda = P.Cp; w.a_layout = LAYOUT_KC;
+    w.A = ws + P.b_dzvc; w.lda = P.Cg; w.a_layout = LAYOUT_KC;
   }
-  w.B = ws + P.b_ht; w.ldb = P.Cp; w.b_layout = LAYOUT_KC;
-  w.M = (int)V; w.N = (int)d; w.k_end = rows_pad; w.k_split = rows_pad;
-  w.tiles_m = (int)((V + 255) / 256); w.tiles_n = (int)((d + P.dtile - 1) / P.dtile); w.splits = 1; w.bn = P.dtile;
-  w.out = dW; w.ldo = d; w.accumulate = accumulate ? 1 : 0;
-  return timed(K_DW_GEMM, fl, ((double)V * rows + (double)rows * d) * P.es + 8.0 * V * d, s,
+  w.B = ws + P.b_ht; w.ldb = P.Cg; w.b_layout = LAYOUT_KC;
+  w.M = (int)vlen; w.N = (int)d; w.k_end = rows_pad; w.k_split = rows_pad;
+  w.tiles_m = (int)((vlen + 255) / 256); w.tiles_n = (int)((d + P.dtile - 1) / P.dtile); w.splits = 1;
+  w.bn = P.dtile;
+  w.out = dW + v0 * d; w.ldo = d; w.accumulate = accumulate ? 1 : 0;
+  return timed(K_DW_GEMM, fl, ((double)vlen * rows + (double)rows * d) * P.es + 8.0 * vlen * d, s,
             [&] { return launch_gemm(dtype, EPI_DW, w, s); });
+}
+
+// dH and dW (+)= of one group of rows [r0, r0 + rows) and vocabulary slice
+// `part` from its dZ in the backward workspace (token-major [Cg, vpart]; the
+// generic path, which has a single slice, also vocabulary-major), W^T and the
+// group's H^T: dH_g (+)= dZ W_slice split over the slice's vocabulary and
+// summed in a fixed order (slices in order, each slice's splits in order),
+// dW_slice (+)= dZ^T H_g.
+static hipError_t part_products(const Plan& P, int dtype, char* ws, int64_t r0, int rows, int part, void* dH,
+                                float* dW, bool accumulate, hipStream_t s) {
+  const int64_t d = P.d;
+  const int64_t v0 = part * P.vpart;
+  const int64_t vlen = P.V - v0 < P.vpart ? P.V - v0 : P.vpart;  // valid vocabulary rows
+  const int64_t kv = P.Vp - v0 < P.vpart ? P.Vp - v0 : P.vpart;  // padded: zero past vlen
+  const double fl = 2.0 * rows * (double)vlen * d;
+  GemmArgs h;
+  memset(&h, 0, sizeof(h));
+  h.A = ws + P.b_dzcv; h.lda = P.vpart; h.a_layout = LAYOUT_KC;
+  h.B = ws + P.b_wt + v0 * P.es; h.ldb = P.Vp; h.b_layout = LAYOUT_KC;
+  h.M = rows; h.N = (int)d; h.k_end = kv; h.k_split = P.dh_ksplit;
+  h.tiles_m = (int)((rows + 255) / 256); h.tiles_n = (int)((d + P.dtile - 1) / P.dtile); h.bn = P.dtile;
+  h.splits = (int)((kv + P.dh_ksplit - 1) / P.dh_ksplit);
+  h.out = (float*)(ws + P.b_dhpart); h.ldo = d; h.Cp = P.Cg;
+  const int splits = h.splits;
+  // the first slice starts the fp32 sum, the last one writes dH in its dtype
+  const bool first = part == 0, last = part == P.n_parts - 1;
+  const float* acc_in = first ? nullptr : (const float*)(ws + P.b_dhacc);
+  void* out = last ? (void*)((char*)dH + r0 * d * P.es) : (void*)(ws + P.b_dhacc);
+  const int out_dtype = last ? dtype : (int)KDKL_F32;
+  const double sum_bytes = (first ? 0.0 : 4.0 * rows * d) + (double)rows * d * (last ? P.es : 4);
+  hipError_t e = timed(K_DH_GEMM, fl, ((double)vlen * rows + (double)vlen * d) * P.es + 4.0 * splits * rows * d,
+                       s, [&] { return launch_gemm(dtype, EPI_DH, h, s); });
+  if (e == hipSuccess)
+    e = timed(K_DH_REDUCE, 0.0, 4.0 * splits * rows * d + sum_bytes, s, [&] {
+      return launch_dh_reduce(out_dtype, (const float*)(ws + P.b_dhpart), splits, rows, d, P.Cg, acc_in, out, s);
+    });
+  if (e != hipSuccess) return e;
+  return dw_product(P, dtype, ws, rows, part, dW, accumulate, s);
 }
 
 kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, const float* lg, int64_t N,
@@ -376,30 +446,40 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
   if (e == hipSuccess)
     e = timed(K_GRAD_SCALE, 0.0, (double)N * 4.0, s,
               [&] { return launch_grad_scale(ids, K, N, grad_loss, T, (float*)(ws + P.b_scale), s); });
-  for (int64_t r0 = 0; r0 < N && e == hipSuccess; r0 += P.chunk) {
-    const int rows = (int)((N - r0) < P.chunk ? (N - r0) : P.chunk);
+  const int64_t group = P.bg * P.chunk;
+  for (int64_t r0 = 0; r0 < N && e == hipSuccess; r0 += group) {
+    const int rows = (int)((N - r0) < group ? (N - r0) : group);
     const int64_t rows_pad = round_up(rows, kTokenTile);
-    TeacherArgs ta =
-        teacher_args(P, ids, lg, T, r0, rows, ws, P.b_sids, P.b_sp, P.b_erow, P.b_keep, P.b_tstart);
+    TeacherArgs ta = teacher_args(P, ids, lg, T, r0, rows, P.Cg, ws, P.b_sids, P.b_sp, P.b_erow, P.b_keep,
+                                  P.b_tstart);
     e = timed(K_TEACHER, 0.0, (double)rows * P.K * 8.0 * 2.0, s, [&] { return launch_teacher(ta, s); });
     if (e != hipSuccess) break;
-    // H_c^T [d, Cp], zero-padded past the chunk's rows: the dW product
-    // contracts over the chunk's tokens.
-    const char* Hc = (const char*)H + r0 * d * P.es;
+    // H_g^T [d, Cg], zero-padded past the group's rows: the dW product
+    // contracts over the group's tokens.
+    const char* Hg = (const char*)H + r0 * d * P.es;
     e = timed(K_TRANSPOSE_H, 0.0, 2.0 * (double)rows * d * P.es, s, [&] {
-      return launch_transpose((int)P.es, Hc, rows, d, d, ws + P.b_ht, rows_pad, P.Cp, s);
+      return launch_transpose((int)P.es, Hg, rows, d, d, ws + P.b_ht, rows_pad, P.Cg, s);
     });
-    if (e != hipSuccess) break;
-    // recompute the chunk's logits and form dZ (token-major; the generic
-    // path also writes the vocabulary-major copy)
-    GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.b_sids, P.b_sp, P.b_tstart);
-    g.row_lse = row_lse + r0; g.scale = (const float*)(ws + P.b_scale); g.keep = (const float*)(ws + P.b_keep);
-    g.dz_cv = ws + P.b_dzcv; g.dz_vc = P.fast ? nullptr : ws + P.b_dzvc;
-    const double fl = 2.0 * rows * (double)V * d;
-    e = timed(K_DZ_GEMM, fl, ((double)V + rows) * d * P.es + (P.fast ? 1.0 : 2.0) * rows * (double)V * P.es, s,
-              [&] { return launch_gemm(dtype, EPI_DZ, g, s); });
-    if (e != hipSuccess) break;
-    e = chunk_products(P, dtype, ws, r0, rows, dH, dW, r0 > 0 || accumulate_dW, s);
+    for (int part = 0; part < P.n_parts && e == hipSuccess; ++part) {
+      // recompute the group's logits over the slice's vocabulary rows and
+      // form dZ (token-major; the generic path also writes the
+      // vocabulary-major copy)
+      const int64_t v0 = part * P.vpart;
+      const int64_t vlen = V - v0 < P.vpart ? V - v0 : P.vpart;
+      GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.b_sids, P.b_sp, P.b_tstart);
+      g.A = (const char*)W + v0 * d * P.es;
+      g.M = (int)vlen; g.V = (int)vlen; g.v0 = (int)v0; g.tm0 = (int)(v0 / P.vt);
+      g.tiles_m = (int)((vlen + P.vt - 1) / P.vt);
+      g.Cp = P.Cg; g.Vp = P.vpart;
+      g.row_lse = row_lse + r0; g.scale = (const float*)(ws + P.b_scale); g.keep = (const float*)(ws + P.b_keep);
+      g.dz_cv = ws + P.b_dzcv; g.dz_vc = P.fast ? nullptr : ws + P.b_dzvc;
+      const double fl = 2.0 * rows * (double)vlen * d;
+      e = timed(K_DZ_GEMM, fl,
+                ((double)vlen + rows) * d * P.es + (P.fast ? 1.0 : 2.0) * rows * (double)vlen * P.es, s,
+                [&] { return launch_gemm(dtype, EPI_DZ, g, s); });
+      if (e != hipSuccess) break;
+      e = part_products(P, dtype, ws, r0, rows, part, dH, dW, r0 > 0 || accumulate_dW, s);
+    }
   }
   return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
 }
@@ -589,6 +669,7 @@ kdkl_status kdkl_dense_backward(const void* H, const void* W, const int32_t* ids
     e = timed(K_TRANSPOSE_H, 0.0, 2.0 * (double)N * d * P.es, s, [&] {
       return launch_transpose((int)P.es, H, N, d, d, ws + P.b_ht, P.Cp, P.Cp, s);
     });
+
   // dZ = g/(N_kept T) (exp(logq) - P), token-major [Cp, Vp], from the saved grids
   DenseArgs a = dense_args(D, ids, lg, T, (char*)const_cast<void*>(saved));
   a.dZ = ws + P.b_dzcv; a.scale = (const float*)(ws + P.b_scale);
@@ -597,7 +678,7 @@ kdkl_status kdkl_dense_backward(const void* H, const void* W, const int32_t* ids
               [&] { return launch_dense_grad(dtype, a, s); });
   if (e == hipSuccess && !P.fast)  // the generic dW product reads dZ vocabulary-major
     e = launch_transpose((int)P.es, ws + P.b_dzcv, P.Cp, P.Vp, P.Vp, ws + P.b_dzvc, P.Cp, P.Cp, s);
-  if (e == hipSuccess) e = chunk_products(P, dtype, ws, 0, (int)N, dH, dW, accumulate_dW != 0, s);
+  if (e == hipSuccess) e = part_products(P, dtype, ws, 0, (int)N, 0, dH, dW, accumulate_dW != 0, s);
   return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
 }
 

@@ -67,9 +67,11 @@ struct GemmArgs {
   int tiles_m, tiles_n, splits;
   // projection epilogues (A = W rows = vocabulary, B = H rows = tokens)
   float inv_T;
-  int V;                         // vocabulary size (rows >= V are padding)
+  int V;                         // valid A rows (vocabulary rows of this launch; rows >= V are padding)
+  int v0;                        // vocabulary row of A's first row (a slice of W in the backward)
+  int tm0;                       // its vocabulary tile: v0 / vocabulary tile
   int K;                         // teacher top-K
-  int64_t Cp;                    // chunk capacity
+  int64_t Cp;                    // token capacity: row pitch of tstart, dz_vc and the dH partials
   int n_vt;
   const int32_t* sids;
   const float* sp;
@@ -81,7 +83,7 @@ struct GemmArgs {
   int raw;                       // EPI_DZ only: store the logits z themselves (dense path)
   void* dz_cv;                   // [Cp, Vp]
   void* dz_vc;                   // [Vp, Cp]
-  int64_t Vp;
+  int64_t Vp;                    // row pitch of dz_cv (vocabulary columns held)
   // dH split-K partials [splits, Cp, d] and dW [V, d]
   float* out;
   int64_t ldo;
@@ -145,8 +147,11 @@ constexpr int kCheckIdsMaxBlocks = 1024;
 int check_ids_blocks(int64_t N);
 hipError_t launch_check_ids(const int32_t* ids, int64_t N, int K, int64_t V, void* partial, int64_t* out,
                             hipStream_t s);
+// out[r, c] = acc_in[r, c] (if not NULL) + sum over s of part[s, r, c], in
+// split order, for r < rows; out in dtype (fp32 or bf16), acc_in fp32 and
+// out may alias it. The partials have row pitch d and split pitch Cp * d.
 hipError_t launch_dh_reduce(int dtype, const float* part, int splits, int rows,
-                            int64_t d, int64_t Cp, void* dH, hipStream_t s);
+                            int64_t d, int64_t Cp, const float* acc_in, void* out, hipStream_t s);
 
 enum Epilogue { EPI_FWD = 0, EPI_DZ = 1, EPI_DH = 2, EPI_DW = 3 };
 // dtype: 0 = fp32, 1 = bf16

@@ -330,16 +330,17 @@ hipError_t launch_zero(float* p, int64_t n, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------
-// dH = sum over splits of the fp32 partials, in split order.
+// dH = sum over splits of the fp32 partials, in split order, added to the
+// sum of the earlier vocabulary slices when the backward runs in slices.
 // ---------------------------------------------------------------------------
 template <int BF16>
 __global__ __launch_bounds__(256) void dh_reduce_kernel(const float* __restrict__ part, int splits,
                                                         int64_t n_elems, int64_t stride,
-                                                        void* __restrict__ dH) {
+                                                        const float* acc_in, void* dH) {
   const int64_t i4 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i4 >= n_elems) return;
-  float4 acc = *(const float4*)(part + i4);
-  for (int s = 1; s < splits; ++s) {
+  float4 acc = acc_in ? *(const float4*)(acc_in + i4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s = 0; s < splits; ++s) {
     const float4 v = *(const float4*)(part + (int64_t)s * stride + i4);
     acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
   }
@@ -354,14 +355,14 @@ __global__ __launch_bounds__(256) void dh_reduce_kernel(const float* __restrict_
 }
 
 hipError_t launch_dh_reduce(int dtype, const float* part, int splits, int rows, int64_t d, int64_t Cp,
-                            void* dH, hipStream_t s) {
+                            const float* acc_in, void* dH, hipStream_t s) {
   const int64_t n = (int64_t)rows * d;  // d is a multiple of 4
   if (n <= 0) return hipSuccess;
   const unsigned blocks = (unsigned)((n / 4 + 255) / 256);
   if (dtype == 1)
-    hipLaunchKernelGGL(dh_reduce_kernel<1>, dim3(blocks), dim3(256), 0, s, part, splits, n, Cp * d, dH);
+    hipLaunchKernelGGL(dh_reduce_kernel<1>, dim3(blocks), dim3(256), 0, s, part, splits, n, Cp * d, acc_in, dH);
   else
-    hipLaunchKernelGGL(dh_reduce_kernel<0>, dim3(blocks), dim3(256), 0, s, part, splits, n, Cp * d, dH);
+    hipLaunchKernelGGL(dh_reduce_kernel<0>, dim3(blocks), dim3(256), 0, s, part, splits, n, Cp * d, acc_in, dH);
   return hipGetLastError();
 }
 
@@ -447,15 +448,16 @@ __device__ __forceinline__ void hit_ranges(const GemmArgs& p, const Tile& t, int
   for (int nb = 0; nb < G::NB; ++nb) {
     const int col = t.tn * G::BN + wn * G::WN + nb * 32 + (lane & 31);
     if (col < p.N && !p.raw) {  // raw logits (dense path): no teacher index
-      lo[nb] = p.tstart[(int64_t)t.tm * p.Cp + col];
-      hi[nb] = p.tstart[(int64_t)(t.tm + 1) * p.Cp + col];
+      lo[nb] = p.tstart[(int64_t)(p.tm0 + t.tm) * p.Cp + col];
+      hi[nb] = p.tstart[(int64_t)(p.tm0 + t.tm + 1) * p.Cp + col];
     } else {
       lo[nb] = hi[nb] = 0;
     }
   }
 }
 
-// Accumulator slot (mb * 16 + r) of vocabulary row `id` in this lane, or -1.
+// Accumulator slot (mb * 16 + r) of launch-relative vocabulary row `id` in
+// this lane, or -1.
 template <class G>
 __device__ __forceinline__ int hit_slot(int id, int V, int m0, int wm, int lane) {
   const int r = id - m0 - wm * G::WM;
@@ -553,7 +555,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
       const float mx = zmax * p.inv_T;
       float gz = 0.f;  // sum of p * z; times 1/T below
       for (int h = hit_lo[nb]; h < hit_hi[nb]; ++h) {
-        const int slot = hit_slot<G>(p.sids[(int64_t)col * p.K + h], p.V, m0, wm, lane);
+        const int slot = hit_slot<G>(p.sids[(int64_t)col * p.K + h] - p.v0, p.V, m0, wm, lane);
         if (slot < 0) continue;
         float v = 0.f;
 #pragma unroll
@@ -629,7 +631,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
           for (int r = 0; r < 16; ++r) acc[mb][nb][r] = row_ok(mb, r) ? acc[mb][nb][r] : 0.f;
       }
       for (int h = hit_lo[nb]; h < hit_hi[nb]; ++h) {
-        const int slot = hit_slot<G>(p.sids[(int64_t)col * p.K + h], p.V, m0, wm, lane);
+        const int slot = hit_slot<G>(p.sids[(int64_t)col * p.K + h] - p.v0, p.V, m0, wm, lane);
         if (slot < 0) continue;
         const float pk = coef * p.sp[(int64_t)col * p.K + h];
 #pragma unroll

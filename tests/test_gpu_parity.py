@@ -35,6 +35,12 @@ CASES = [
     # ragged second chunk
     ("bf16_vtile384_exact", "small_bf16", dict(N=2048, d=128, V=12288, K=16, chunk=2048, T=1.1), 13),
     ("bf16_vtile384_one_row", "small_bf16", dict(N=2100, d=192, V=11905, K=8, chunk=2048, T=0.9), 14),
+    # vocabularies large enough for the backward to take several chunks at a
+    # time in as many vocabulary slices, each last slice ending in a partial
+    # tile: three chunks (groups of two: a full group, then one partial
+    # chunk), and five (a full group of four, then one partial chunk)
+    ("bf16_backward_groups2", "small_bf16", dict(N=150, d=64, V=270001, K=16, chunk=64, T=1.2), 15),
+    ("bf16_backward_groups4", "small_bf16", dict(N=148, d=64, V=530001, K=12, chunk=32, T=0.8), 16),
 ]
 
 
