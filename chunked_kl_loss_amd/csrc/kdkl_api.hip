@@ -103,9 +103,9 @@ struct Plan {
   bool fast;       // bf16 main loop: reads W, H and dZ in place (no transposes)
   int dtile;       // N-tile width of the dH and dW products (hidden-size axis)
   // offsets into the forward workspace
-  size_t f_sids, f_sp, f_erow, f_keep, f_tstart, f_part, f_rowkl, f_bytes;
+  size_t f_ent, f_erow, f_keep, f_tstart, f_part, f_rowkl, f_bytes;
   // offsets into the backward workspace
-  size_t b_sids, b_sp, b_erow, b_keep, b_scale, b_tstart, b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart, b_dhacc, b_bytes;
+  size_t b_ent, b_erow, b_keep, b_scale, b_tstart, b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart, b_dhacc, b_bytes;
 };
 
 #ifndef KDKL_DH_BUSY
@@ -199,8 +199,8 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   int64_t t0, t1, t2;
   size_t cur = 0;
   bool ok = true;
-  ok &= mul_ok(P->Cp, K, &t0) && mul_ok(t0, 4, &t0);
-  ok &= region(&cur, t0, &P->f_sids) && region(&cur, t0, &P->f_sp);
+  ok &= mul_ok(P->Cp, K, &t0) && mul_ok(t0, 8, &t0);
+  ok &= region(&cur, t0, &P->f_ent);
   ok &= region(&cur, P->Cp * 4, &P->f_erow) && region(&cur, P->Cp * 4, &P->f_keep);
   ok &= mul_ok(P->n_vt + 1, P->Cp, &t1) && mul_ok(t1, 2, &t1);
   ok &= region(&cur, t1, &P->f_tstart);
@@ -211,9 +211,9 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
 
   cur = 0;
   int64_t g0, g1;
-  ok &= mul_ok(P->Cg, K, &g0) && mul_ok(g0, 4, &g0);
+  ok &= mul_ok(P->Cg, K, &g0) && mul_ok(g0, 8, &g0);
   ok &= mul_ok(P->n_vt + 1, P->Cg, &g1) && mul_ok(g1, 2, &g1);
-  ok &= region(&cur, g0, &P->b_sids) && region(&cur, g0, &P->b_sp);
+  ok &= region(&cur, g0, &P->b_ent);
   ok &= region(&cur, P->Cg * 4, &P->b_erow) && region(&cur, P->Cg * 4, &P->b_keep);
   ok &= region(&cur, 16, &P->b_scale);
   ok &= region(&cur, g1, &P->b_tstart);
@@ -258,18 +258,18 @@ static kdkl_status check_common(const void* H, const void* W, const int32_t* ids
 }
 
 static TeacherArgs teacher_args(const Plan& P, const int32_t* ids, const float* lg, float T, int64_t r0,
-                                int rows, int64_t pitch, char* ws, size_t o_sids, size_t o_sp, size_t o_erow,
+                                int rows, int64_t pitch, char* ws, size_t o_ent, size_t o_erow,
                                 size_t o_keep, size_t o_tstart) {
   TeacherArgs t;
   t.ids = ids; t.logits = lg; t.r0 = r0; t.rows = rows; t.K = (int)P.K;
   t.inv_T = 1.0f / T; t.vt = P.vt; t.n_vt = (int)P.n_vt; t.Cp = pitch;
-  t.sids = (int32_t*)(ws + o_sids); t.sp = (float*)(ws + o_sp);
+  t.ent = (int2*)(ws + o_ent);
   t.erow = (float*)(ws + o_erow); t.keep = (float*)(ws + o_keep); t.tstart = (uint16_t*)(ws + o_tstart);
   return t;
 }
 
 static GemmArgs projection_args(const Plan& P, const void* H, const void* W, float T, int64_t r0,
-                                int rows, char* ws, size_t o_sids, size_t o_sp, size_t o_tstart) {
+                                int rows, char* ws, size_t o_ent, size_t o_tstart) {
   GemmArgs g;
   memset(&g, 0, sizeof(g));
   g.A = W; g.lda = P.d;
@@ -279,7 +279,7 @@ static GemmArgs projection_args(const Plan& P, const void* H, const void* W, flo
   g.tiles_m = (int)P.n_vt; g.tiles_n = (int)((rows + kTokenTile - 1) / kTokenTile); g.splits = 1;
   g.bm = P.vt;
   g.inv_T = 1.0f / T; g.V = (int)P.V; g.K = (int)P.K; g.Cp = P.Cp; g.n_vt = (int)P.n_vt;
-  g.sids = (const int32_t*)(ws + o_sids); g.sp = (const float*)(ws + o_sp);
+  g.ent = (const int2*)(ws + o_ent);
   g.tstart = (const uint16_t*)(ws + o_tstart);
   g.Vp = P.Vp;
   g.a_layout = g.b_layout = LAYOUT_KC;
@@ -337,10 +337,10 @@ kdkl_status kdkl_forward(const void* H, const void* W, const int32_t* ids, const
   for (int64_t r0 = 0; r0 < N && e == hipSuccess; r0 += P.chunk) {
     const int rows = (int)((N - r0) < P.chunk ? (N - r0) : P.chunk);
     TeacherArgs ta =
-        teacher_args(P, ids, lg, T, r0, rows, P.Cp, ws, P.f_sids, P.f_sp, P.f_erow, P.f_keep, P.f_tstart);
+        teacher_args(P, ids, lg, T, r0, rows, P.Cp, ws, P.f_ent, P.f_erow, P.f_keep, P.f_tstart);
     e = timed(K_TEACHER, 0.0, (double)rows * P.K * 8.0 * 2.0, s, [&] { return launch_teacher(ta, s); });
     if (e != hipSuccess) break;
-    GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.f_sids, P.f_sp, P.f_tstart);
+    GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.f_ent, P.f_tstart);
     g.part = (float4*)(ws + P.f_part);
     const double fl = 2.0 * rows * (double)V * d;
     const double by = ((double)V + rows) * d * P.es + (double)rows * P.n_vt * 16.0;
@@ -450,7 +450,7 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
   for (int64_t r0 = 0; r0 < N && e == hipSuccess; r0 += group) {
     const int rows = (int)((N - r0) < group ? (N - r0) : group);
     const int64_t rows_pad = round_up(rows, kTokenTile);
-    TeacherArgs ta = teacher_args(P, ids, lg, T, r0, rows, P.Cg, ws, P.b_sids, P.b_sp, P.b_erow, P.b_keep,
+    TeacherArgs ta = teacher_args(P, ids, lg, T, r0, rows, P.Cg, ws, P.b_ent, P.b_erow, P.b_keep,
                                   P.b_tstart);
     e = timed(K_TEACHER, 0.0, (double)rows * P.K * 8.0 * 2.0, s, [&] { return launch_teacher(ta, s); });
     if (e != hipSuccess) break;
@@ -466,7 +466,7 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
       // vocabulary-major copy)
       const int64_t v0 = part * P.vpart;
       const int64_t vlen = V - v0 < P.vpart ? V - v0 : P.vpart;
-      GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.b_sids, P.b_sp, P.b_tstart);
+      GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.b_ent, P.b_tstart);
       g.A = (const char*)W + v0 * d * P.es;
       g.M = (int)vlen; g.V = (int)vlen; g.v0 = (int)v0; g.tm0 = (int)(v0 / P.vt);
       g.tiles_m = (int)((vlen + P.vt - 1) / P.vt);
@@ -619,8 +619,8 @@ kdkl_status kdkl_dense_forward(const void* H, const void* W, const int32_t* ids,
   hipError_t e = hipSuccess;
   if (N > 0) {
     // the logit grid Z = H W^T [Cp, Vp] (zero past V)
-    GemmArgs g = projection_args(P, H, W, T, 0, (int)N, ws, 0, 0, 0);
-    g.sids = nullptr; g.sp = nullptr; g.tstart = nullptr;
+    GemmArgs g = projection_args(P, H, W, T, 0, (int)N, ws, 0, 0);
+    g.ent = nullptr; g.tstart = nullptr;
     g.raw = 1; g.dz_cv = ws + D.f_z; g.dz_vc = nullptr;
     e = timed(K_DENSE_GEMM, 2.0 * N * (double)V * d, ((double)V + N) * d * P.es + (double)N * V * P.es, s,
               [&] { return launch_gemm(dtype, EPI_DZ, g, s); });

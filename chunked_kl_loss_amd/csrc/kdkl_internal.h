@@ -51,8 +51,7 @@ struct TeacherArgs {
   int vt;                 // rows per vocabulary tile
   int n_vt;               // vocabulary tiles (ceil(V / vt))
   int64_t Cp;             // padded chunk capacity (row pitch of tstart)
-  int32_t* sids;          // [Cp, K]   ids sorted ascending
-  float* sp;              // [Cp, K]   teacher probabilities, same order
+  int2* ent;              // [Cp, K]   (id, bits of its teacher probability), ids ascending
   float* erow;            // [Cp]      sum_k p log p
   float* keep;            // [Cp]      1 for a kept position, 0 for an ignored one (first id -1)
   uint16_t* tstart;       // [n_vt + 1, Cp] first sorted index >= tile start
@@ -73,8 +72,7 @@ struct GemmArgs {
   int K;                         // teacher top-K
   int64_t Cp;                    // token capacity: row pitch of tstart, dz_vc and the dH partials
   int n_vt;
-  const int32_t* sids;
-  const float* sp;
+  const int2* ent;               // [Cp, K] teacher entries (id, bits of p), ids ascending per row
   const uint16_t* tstart;
   float4* part;                  // forward: [Cp, n_vt] (max, sumexp, gamma, -)
   const float* row_lse;          // backward: lse of this chunk's rows

@@ -103,8 +103,7 @@ __global__ __launch_bounds__(64) void teacher_prep_kernel(TeacherArgs a) {
         const int o = s_ids[q];
         rank += (o < id) | ((o == id) & (q < k));
       }
-      a.sids[(int64_t)row * K + rank] = id;
-      a.sp[(int64_t)row * K + rank] = p;
+      a.ent[(int64_t)row * K + rank] = make_int2(id, __float_as_int(p));
       s_sorted[rank] = id;
     }
   }
@@ -439,23 +438,6 @@ __device__ __forceinline__ bool tile_of(const GemmArgs& p, Tile& t) {
   return true;
 }
 
-// Teacher entries of this lane's token columns: [lo, hi) into the sorted list.
-template <class G>
-__device__ __forceinline__ void hit_ranges(const GemmArgs& p, const Tile& t, int (&lo)[G::NB],
-                                           int (&hi)[G::NB]) {
-  const int lane = threadIdx.x & 63, wn = G::wn();
-#pragma unroll
-  for (int nb = 0; nb < G::NB; ++nb) {
-    const int col = t.tn * G::BN + wn * G::WN + nb * 32 + (lane & 31);
-    if (col < p.N && !p.raw) {  // raw logits (dense path): no teacher index
-      lo[nb] = p.tstart[(int64_t)(p.tm0 + t.tm) * p.Cp + col];
-      hi[nb] = p.tstart[(int64_t)(p.tm0 + t.tm + 1) * p.Cp + col];
-    } else {
-      lo[nb] = hi[nb] = 0;
-    }
-  }
-}
-
 // Accumulator slot (mb * 16 + r) of launch-relative vocabulary row `id` in
 // this lane, or -1.
 template <class G>
@@ -496,8 +478,7 @@ __device__ __forceinline__ float4 load16_stream(const float* p) {
 
 template <class G, int ES, int EPI>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)[G::MB][G::NB], const Tile& t,
-                                              char* smem, const int (&hit_lo)[G::NB],
-                                              const int (&hit_hi)[G::NB]) {
+                                              char* smem) {
   constexpr int MB = G::MB, NB = G::NB, NT = G::kThreads;
   constexpr int BM = G::BM, BN = G::BN;
   constexpr int kDzPitch = BM + 8;  // bf16 row pitch of the dZ staging tile
@@ -511,6 +492,39 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
   auto row_ok = [&](int mb, int r) { return m0 + acc_row<G>(wm, mb, r, lane) < p.V; };
   // exp(s - m) with s = z / T as exp2(z * c2 - m2): one fused multiply-add per element
   const float c2 = p.inv_T * kLog2e;
+  // Per-column inputs of the forward and dZ epilogues: the column's teacher
+  // entries in this tile ([lo, hi) into its sorted list) and, for dZ, the
+  // scale qs and base-2 lse of its softmax (qs = 0 and lse2 = +inf for a
+  // column past the chunk or of an ignored position, so q = 0). One thread
+  // per column loads them into an LDS table past the epilogue's other LDS
+  // use: all columns' loads are in flight together, and the column blocks
+  // below keep no per-column registers (which would spill next to the
+  // accumulators).
+  constexpr int kRedBytes = G::kWavesM * BN * 3 * 4;
+  constexpr int kStageBytes = (EPI == EPI_DZ && ES == 2) ? 128 * kDzPitch * 2 : 0;
+  constexpr int kInfoOff = ((kRedBytes > kStageBytes ? kRedBytes : kStageBytes) + 255) / 256 * 256;
+  static_assert(kInfoOff + BN * 16 <= 128 * 1024, "the column table fits every projection kernel's LDS");
+  const int4* info = (const int4*)(smem + kInfoOff);
+  if constexpr (EPI == EPI_FWD || EPI == EPI_DZ) {
+    if (!p.raw) {
+      for (int c = tid; c < BN; c += NT) {
+        const int col = n0 + c;
+        int4 v = make_int4(0, 0, 0, __float_as_int(__builtin_huge_valf()));
+        if (col < p.N) {
+          v.x = p.tstart[(int64_t)(p.tm0 + t.tm) * p.Cp + col];
+          v.y = p.tstart[(int64_t)(p.tm0 + t.tm + 1) * p.Cp + col];
+          if constexpr (EPI == EPI_DZ) {
+            if (p.keep[col] != 0.f) {
+              v.z = __float_as_int(p.scale[0]);
+              v.w = __float_as_int(p.row_lse[col] * kLog2e);
+            }
+          }
+        }
+        ((int4*)(smem + kInfoOff))[c] = v;
+      }
+      __syncthreads();
+    }
+  }
   if constexpr (EPI == EPI_FWD) {
     // s = z / T over the tile's vocabulary rows (A rows), per token column:
     // max, sum of exp(s - max), and sum of p * s over the teacher ids here.
@@ -554,15 +568,17 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
       se += shfl_xor(se, 32);
       const float mx = zmax * p.inv_T;
       float gz = 0.f;  // sum of p * z; times 1/T below
-      for (int h = hit_lo[nb]; h < hit_hi[nb]; ++h) {
-        const int slot = hit_slot<G>(p.sids[(int64_t)col * p.K + h] - p.v0, p.V, m0, wm, lane);
+      const int4 ci = p.raw ? make_int4(0, 0, 0, 0) : info[ct];
+      for (int h = ci.x; h < ci.y; ++h) {
+        const int2 e = p.ent[(int64_t)col * p.K + h];
+        const int slot = hit_slot<G>(e.x - p.v0, p.V, m0, wm, lane);
         if (slot < 0) continue;
         float v = 0.f;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) v = (mb * 16 + rr == slot) ? acc[mb][nb][rr] : v;
-        gz += p.sp[(int64_t)col * p.K + h] * v;
+        gz += __int_as_float(e.y) * v;
       }
       gz += shfl_xor(gz, 32);
       const float gam = gz * p.inv_T;
@@ -614,11 +630,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
           }
         continue;
       }
-      // coef * q = coef * exp2(z * c2 - lse * log2 e); a column past the
-      // chunk or of an ignored position gets lse2 = +inf, so its q is 0
-      const bool use = cval && p.keep[col] != 0.f;
-      const float lse2 = use ? p.row_lse[col] * kLog2e : __builtin_huge_valf();
-      const float qs = use ? coef : 0.f;
+      // coef * q = qs * exp2(z * c2 - lse2)
+      const int4 ci = info[wn * G::WN + nb * 32 + (lane & 31)];
+      const float qs = __int_as_float(ci.z), lse2 = __int_as_float(ci.w);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -630,10 +644,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[mb][nb][r] = row_ok(mb, r) ? acc[mb][nb][r] : 0.f;
       }
-      for (int h = hit_lo[nb]; h < hit_hi[nb]; ++h) {
-        const int slot = hit_slot<G>(p.sids[(int64_t)col * p.K + h] - p.v0, p.V, m0, wm, lane);
+      for (int h = ci.x; h < ci.y; ++h) {
+        const int2 e = p.ent[(int64_t)col * p.K + h];
+        const int slot = hit_slot<G>(e.x - p.v0, p.V, m0, wm, lane);
         if (slot < 0) continue;
-        const float pk = coef * p.sp[(int64_t)col * p.K + h];
+        const float pk = coef * __int_as_float(e.y);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -886,8 +901,6 @@ __global__ __launch_bounds__(256, 1) void gemm_generic_kernel(const GemmArgs p) 
   const int64_t ke = kb + p.k_split < p.k_end ? kb + p.k_split : p.k_end;
   const int nk = ke > kb ? (int)((ke - kb + BK - 1) / BK) : 0;
 
-  int hit_lo[G::NB], hit_hi[G::NB];
-  if constexpr (EPI == EPI_FWD || EPI == EPI_DZ) hit_ranges<G>(p, t, hit_lo, hit_hi);
   f32x16_t acc[G::MB][G::NB];
   zero_acc<G>(acc);
 
@@ -932,7 +945,7 @@ __global__ __launch_bounds__(256, 1) void gemm_generic_kernel(const GemmArgs p) 
       __syncthreads();
     }
   }
-  gemm_epilogue<G, ES, EPI>(p, acc, t, smem, hit_lo, hit_hi);
+  gemm_epilogue<G, ES, EPI>(p, acc, t, smem);
 }
 
 // ----------------------------- bf16 main loop -------------------------------
@@ -1045,9 +1058,6 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
   const int64_t kb = (int64_t)t.ks * p.k_split;
   const int64_t ke = kb + p.k_split < p.k_end ? kb + p.k_split : p.k_end;
   const int nk = ke > kb ? (int)((ke - kb) / BK) : 0;
-
-  int hit_lo[NB], hit_hi[NB];
-  if constexpr (EPI == EPI_FWD || EPI == EPI_DZ) hit_ranges<G>(p, t, hit_lo, hit_hi);
 
   auto swz = [](int row) { return CPR == 8 ? swz8(row) : swz4(row); };
 
@@ -1220,7 +1230,7 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
       if (kt + 1 < nk) load_frags(kt + 1, 0, 0, true);
     }
   }
-  gemm_epilogue<G, 2, EPI>(p, acc, t, smem, hit_lo, hit_hi);
+  gemm_epilogue<G, 2, EPI>(p, acc, t, smem);
 }
 
 using FastGrid = typename std::conditional<
