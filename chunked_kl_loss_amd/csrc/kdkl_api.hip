@@ -223,8 +223,8 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   ok &= mul_ok(P->Cg, P->vpart, &dz) && mul_ok(dz, P->es, &dz);
   if (P->fast) {
     // dW reads the token-major dZ in place through the LDS transpose and
-    // H_c^T (one small transpose per chunk); dH reads W^T, transposed once
-    // per call (cheaper than transposed reads of W in every chunk).
+    // H_g^T (one small transpose per group); dH reads W^T, transposed once
+    // per call (cheaper than transposed reads of W in every launch).
     P->b_dzvc = 0;
     ok &= region(&cur, wt, &P->b_wt);
     ok &= region(&cur, ht, &P->b_ht);

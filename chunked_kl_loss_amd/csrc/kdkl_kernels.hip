@@ -426,15 +426,26 @@ struct Tile {
 
 // XCD-aware tile order: workgroups are dealt round-robin to the 8 XCDs, so
 // each XCD gets a contiguous run of tiles (neighbours share an A tile and
-// stay in that XCD's L2). Returns false for the padding workgroups.
+// stay in that XCD's L2). An N axis of 16 tiles or more is taken in bands of
+// kNBand tiles: an XCD's 32 concurrent workgroups then cover a few A tiles
+// by one band of B tiles, instead of one A tile by all the B tiles, whose
+// bytes would be fetched again in every round. Returns false for the
+// padding workgroups.
+constexpr int kNBand = 8;
 __device__ __forceinline__ bool tile_of(const GemmArgs& p, Tile& t) {
   const int total = p.tiles_m * p.tiles_n * p.splits;
   const int per = (total + 7) >> 3;
   const int L = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
   if (L >= total) return false;
-  t.tn = L % p.tiles_n;
-  t.tm = (L / p.tiles_n) % p.tiles_m;
-  t.ks = L / (p.tiles_n * p.tiles_m);
+  const int mn = p.tiles_m * p.tiles_n;
+  t.ks = L / mn;
+  const int l = L - t.ks * mn;
+  const int nb = p.tiles_n >= 2 * kNBand ? kNBand : p.tiles_n;  // band width
+  const int band = l / (nb * p.tiles_m);  // every band before the last is full
+  const int w = min(nb, p.tiles_n - band * nb);
+  const int r = l - band * nb * p.tiles_m;
+  t.tm = r / w;
+  t.tn = band * nb + r % w;
   return true;
 }
 
