@@ -5,6 +5,7 @@
 // scale", section "Two system changes", fused chunked KL bullet].
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <stdlib.h>
 #include <stdint.h>
 #include <string.h>
 
@@ -101,6 +102,7 @@ struct Plan {
   int64_t vpart;
   int n_parts;
   bool fast;       // bf16 main loop: reads W, H and dZ in place (no transposes)
+  bool wt;         // the dH product reads W^T written once per backward call (else W in place)
   int dtile;       // N-tile width of the dH and dW products (hidden-size axis)
   // offsets into the forward workspace
   size_t f_ent, f_erow, f_keep, f_tstart, f_part, f_rowkl, f_bytes;
@@ -108,6 +110,16 @@ struct Plan {
   size_t b_ent, b_erow, b_keep, b_scale, b_tstart, b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart, b_dhacc, b_bytes;
 };
 
+// The dH product on the bf16 main loop reads a W^T copy written once per
+// backward call. With KDKL_DH_W_INPLACE=1 in the environment (read when the
+// plan is made, so the workspace size and the call must see the same value)
+// it reads W in place through the LDS transpose read instead: V * d * 2
+// fewer bytes of workspace, no transpose, for dH products ~7% slower (twice
+// the LDS instructions per MFMA).
+static bool dh_reads_w_in_place() {
+  const char* e = getenv("KDKL_DH_W_INPLACE");
+  return e != nullptr && e[0] == '1' && e[1] == 0;
+}
 #ifndef KDKL_DH_BUSY
 #define KDKL_DH_BUSY 0.97
 #endif
@@ -162,6 +174,7 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
     P->Vp = round_up(V, vt);
   }
   P->dtile = gemm_d_tile(P->fast, d);
+  P->wt = !P->fast || !dh_reads_w_in_place();
   P->n_vt = P->Vp / P->vt;
   if (P->Cp > INT32_MAX / 4) return KDKL_ERR_OVERFLOW;
   P->bg = backward_group(*P, N);
@@ -221,16 +234,16 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   ok &= mul_ok(d, P->Vp, &wt) && mul_ok(wt, P->es, &wt);
   ok &= mul_ok(d, P->Cg, &ht) && mul_ok(ht, P->es, &ht);
   ok &= mul_ok(P->Cg, P->vpart, &dz) && mul_ok(dz, P->es, &dz);
+  P->b_wt = 0;
+  if (P->wt) ok &= region(&cur, wt, &P->b_wt);
   if (P->fast) {
-    // dW reads the token-major dZ in place through the LDS transpose and
-    // H_g^T (one small transpose per group); dH reads W^T, transposed once
-    // per call (cheaper than transposed reads of W in every launch).
+    // dW reads the token-major dZ in place through the LDS transpose read and
+    // H_g^T (one small transpose per group); dH reads W in place the same
+    // way unless the plan keeps W^T.
     P->b_dzvc = 0;
-    ok &= region(&cur, wt, &P->b_wt);
     ok &= region(&cur, ht, &P->b_ht);
     ok &= region(&cur, dz, &P->b_dzcv);
   } else {
-    ok &= region(&cur, wt, &P->b_wt);
     ok &= region(&cur, ht, &P->b_ht);
     ok &= region(&cur, dz, &P->b_dzcv) && region(&cur, dz, &P->b_dzvc);
   }
@@ -383,12 +396,13 @@ static hipError_t dw_product(const Plan& P, int dtype, char* ws, int rows, int p
 
 // dH and dW (+)= of one group of rows [r0, r0 + rows) and vocabulary slice
 // `part` from its dZ in the backward workspace (token-major [Cg, vpart]; the
-// generic path, which has a single slice, also vocabulary-major), W^T and the
-// group's H^T: dH_g (+)= dZ W_slice split over the slice's vocabulary and
-// summed in a fixed order (slices in order, each slice's splits in order),
-// dW_slice (+)= dZ^T H_g.
-static hipError_t part_products(const Plan& P, int dtype, char* ws, int64_t r0, int rows, int part, void* dH,
-                                float* dW, bool accumulate, hipStream_t s) {
+// generic path, which has a single slice, also vocabulary-major), W (read in
+// place through the LDS transpose read on the bf16 main loop, else as the
+// W^T the call wrote) and the group's H^T: dH_g (+)= dZ W_slice split over
+// the slice's vocabulary and summed in a fixed order (slices in order, each
+// slice's splits in order), dW_slice (+)= dZ^T H_g.
+static hipError_t part_products(const Plan& P, int dtype, const void* W, char* ws, int64_t r0, int rows, int part,
+                                void* dH, float* dW, bool accumulate, hipStream_t s) {
   const int64_t d = P.d;
   const int64_t v0 = part * P.vpart;
   const int64_t vlen = P.V - v0 < P.vpart ? P.V - v0 : P.vpart;  // valid vocabulary rows
@@ -397,7 +411,14 @@ static hipError_t part_products(const Plan& P, int dtype, char* ws, int64_t r0, 
   GemmArgs h;
   memset(&h, 0, sizeof(h));
   h.A = ws + P.b_dzcv; h.lda = P.vpart; h.a_layout = LAYOUT_KC;
-  h.B = ws + P.b_wt + v0 * P.es; h.ldb = P.Vp; h.b_layout = LAYOUT_KC;
+  if (!P.wt) {
+    // W rows v0.. as k rows (the hidden size contiguous); rows past the
+    // slice's vocabulary are clamped to its last row (dZ is zero there)
+    h.B = (const char*)W + v0 * P.d * P.es; h.ldb = P.d; h.b_layout = LAYOUT_MC;
+    h.b_krows = vlen; h.b_mcols = P.d;
+  } else {
+    h.B = ws + P.b_wt + v0 * P.es; h.ldb = P.Vp; h.b_layout = LAYOUT_KC;
+  }
   h.M = rows; h.N = (int)d; h.k_end = kv; h.k_split = P.dh_ksplit;
   h.tiles_m = (int)((rows + 255) / 256); h.tiles_n = (int)((d + P.dtile - 1) / P.dtile); h.bn = P.dtile;
   h.splits = (int)((kv + P.dh_ksplit - 1) / P.dh_ksplit);
@@ -437,11 +458,12 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
     if (!accumulate_dW) e = launch_zero(dW, V * d, s);
     return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
   }
-  // W^T [d, Vp], zero-padded, once per call: the dH product contracts over
-  // V and reads both operands K-contiguous.
-  e = timed(K_TRANSPOSE_W, 0.0, 2.0 * (double)V * d * P.es, s, [&] {
-      return launch_transpose((int)P.es, W, V, d, d, ws + P.b_wt, P.Vp, P.Vp, s);
-    });
+  // W^T [d, Vp], zero-padded, once per call when the dH product reads both
+  // operands K-contiguous (the generic path, or a build that keeps W^T)
+  if (P.wt)
+    e = timed(K_TRANSPOSE_W, 0.0, 2.0 * (double)V * d * P.es, s, [&] {
+        return launch_transpose((int)P.es, W, V, d, d, ws + P.b_wt, P.Vp, P.Vp, s);
+      });
   // g / (N_kept T): the mean runs over the positions that are not ignored
   if (e == hipSuccess)
     e = timed(K_GRAD_SCALE, 0.0, (double)N * 4.0, s,
@@ -478,7 +500,7 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
                 ((double)vlen + rows) * d * P.es + (P.fast ? 1.0 : 2.0) * rows * (double)vlen * P.es, s,
                 [&] { return launch_gemm(dtype, EPI_DZ, g, s); });
       if (e != hipSuccess) break;
-      e = part_products(P, dtype, ws, r0, rows, part, dH, dW, r0 > 0 || accumulate_dW, s);
+      e = part_products(P, dtype, W, ws, r0, rows, part, dH, dW, r0 > 0 || accumulate_dW, s);
     }
   }
   return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
@@ -659,9 +681,10 @@ kdkl_status kdkl_dense_backward(const void* H, const void* W, const int32_t* ids
     if (!accumulate_dW) e = launch_zero(dW, V * d, s);
     return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
   }
-  e = timed(K_TRANSPOSE_W, 0.0, 2.0 * (double)V * d * P.es, s, [&] {
-      return launch_transpose((int)P.es, W, V, d, d, ws + P.b_wt, P.Vp, P.Vp, s);
-    });
+  if (P.wt)
+    e = timed(K_TRANSPOSE_W, 0.0, 2.0 * (double)V * d * P.es, s, [&] {
+        return launch_transpose((int)P.es, W, V, d, d, ws + P.b_wt, P.Vp, P.Vp, s);
+      });
   if (e == hipSuccess)
     e = timed(K_GRAD_SCALE, 0.0, (double)N * 4.0, s,
               [&] { return launch_grad_scale(ids, K, N, grad_loss, T, (float*)(ws + P.b_scale), s); });
@@ -678,7 +701,7 @@ kdkl_status kdkl_dense_backward(const void* H, const void* W, const int32_t* ids
               [&] { return launch_dense_grad(dtype, a, s); });
   if (e == hipSuccess && !P.fast)  // the generic dW product reads dZ vocabulary-major
     e = launch_transpose((int)P.es, ws + P.b_dzcv, P.Cp, P.Vp, P.Vp, ws + P.b_dzvc, P.Cp, P.Cp, s);
-  if (e == hipSuccess) e = part_products(P, dtype, ws, 0, (int)N, 0, dH, dW, accumulate_dW != 0, s);
+  if (e == hipSuccess) e = part_products(P, dtype, W, ws, 0, (int)N, 0, dH, dW, accumulate_dW != 0, s);
   return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
 }
 

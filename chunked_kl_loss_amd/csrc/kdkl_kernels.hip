@@ -1054,8 +1054,9 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
   constexpr int LPS = LPO + LPO_B;
   constexpr int KG = BK / 16;                // 16-element k-groups per step
   static_assert(LPO * 1024 * G::kWaves == TILE && LPO_B * 1024 * G::kWaves == TILE_B, "whole loads per wave");
-  static_assert((LA == LAYOUT_KC || G::BM == 256) && (LB == LAYOUT_KC || G::BN == 256),
-                "k-major LDS rows hold 256 elements");
+  static_assert((LA == LAYOUT_KC || G::BM == 256 || G::BM == 320) &&
+                    (LB == LAYOUT_KC || G::BN == 256 || G::BN == 320),
+                "k-major LDS rows hold 256 or 320 elements");
   __shared__ __attribute__((aligned(1024))) char smem[SMEM];
   Tile t;
   if (!tile_of(p, t)) return;
@@ -1080,12 +1081,17 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
   // adds a 32-bit byte offset (the host keeps a tile's span below 2 GiB).
   // KC: lane offset = 16-byte chunk of an output-axis row, fixed over the
   // k-steps (the base advances RB bytes per step). MC: 16-byte unit of a k
-  // row; the k row is clamped to the last one per step.
+  // row; the k row is clamped to the last one per step. An MC stage holds
+  // BK rows of W_ (256 or 320) elements; global unit u of row k sits at LDS
+  // unit mc_unit(k, u) of that row: rows of 512 bytes are XORed by 4 units
+  // per k mod 4, rows of 640 bytes (128 bytes mod the 256-byte bank span)
+  // rotated by 4 units when bit 1 of k is set, so that the four rows a
+  // transposed read touches fall in four distinct 64-byte bank quarters.
   struct Src {
     uint32_t off;  // KC: byte offset from the tile base; MC: column byte offset
     int krow;      // MC: k row within the stage
   };
-  auto make_src = [&](int layout, int64_t ld, int rows, int row0, int64_t mcols, int i) {
+  auto make_src = [&](int layout, int64_t ld, int rows, int row0, int64_t mcols, int i, int W_) {
     Src s;
     const int slot = (i * G::kWaves + wid) * 64 + lane;
     if (layout == LAYOUT_KC) {
@@ -1094,7 +1100,9 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
       s.off = (uint32_t)(((int64_t)(g - row0) * ld) * 2 + c * 16);
       s.krow = 0;
     } else {
-      const int kr = slot >> 5, u = (slot & 31) ^ (4 * (kr & 3));
+      const int U = W_ / 8;  // 16-byte units per k row
+      const int kr = slot / U, su = slot % U;
+      const int u = W_ == 256 ? su ^ (4 * (kr & 3)) : (su + U - 4 * ((kr >> 1) & 1)) % U;
       const int64_t col = min((int64_t)row0 + u * 8, mcols - 8);
       s.off = (uint32_t)(col * 2);
       s.krow = kr;
@@ -1103,9 +1111,9 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
   };
   Src sa[LPO], sb[LPO_B];
 #pragma unroll
-  for (int i = 0; i < LPO; ++i) sa[i] = make_src(LA, p.lda, p.M, m0, p.a_mcols, i);
+  for (int i = 0; i < LPO; ++i) sa[i] = make_src(LA, p.lda, p.M, m0, p.a_mcols, i, G::BM);
 #pragma unroll
-  for (int i = 0; i < LPO_B; ++i) sb[i] = make_src(LB, p.ldb, p.N, n0, p.b_mcols, i);
+  for (int i = 0; i < LPO_B; ++i) sb[i] = make_src(LB, p.ldb, p.N, n0, p.b_mcols, i, G::BN);
   // Uniform base of one operand's stage kt.
   auto stage_base = [&](int layout, const void* X, int64_t ld, int row0, int kt) -> const char* {
     const int64_t k0 = kb + (int64_t)kt * BK;
@@ -1155,19 +1163,20 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
   bf16x8_t fa[2][MB], fb[SB ? 1 : 2][NB];
   // One MFMA operand fragment (8 consecutive k of output row/column `r0 +
   // (lane & 31)`) from an operand tile in either layout.
-  auto frag = [&](int layout, const char* s, int r0, int kk) -> bf16x8_t {
+  auto frag = [&](int layout, const char* s, int r0, int kk, int W_) -> bf16x8_t {
     if (layout == LAYOUT_KC) {
       const int row = r0 + (lane & 31);
       const int c = kk * 2 + (lane >> 5);
       return *(const bf16x8_t*)(s + row * RB + ((c ^ swz(row)) << 4));
     } else {
+      // 8-byte item q of k row k sits at item mc_unit(k, q / 2) * 2 + q % 2
       const int q = ((r0 + 16 * ((lane >> 4) & 1)) >> 2) + (lane & 3);
       bf16x8_t v;
 #pragma unroll
       for (int j2 = 0; j2 < 2; ++j2) {
         const int k = kk * 16 + 8 * (lane >> 5) + 4 * j2 + ((lane & 15) >> 2);
-        const int pq = q ^ (8 * (k & 3));
-        const s16x4_t h = ds_read_tr16(s + k * 512 + pq * 8);
+        const int pq = W_ == 256 ? q ^ (8 * (k & 3)) : (q + 8 * ((k >> 1) & 1)) % (W_ / 4);
+        const s16x4_t h = ds_read_tr16(s + k * (W_ * 2) + pq * 8);
         const bf16x4_t hb = __builtin_bit_cast(bf16x4_t, h);
         v[4 * j2 + 0] = hb[0];
         v[4 * j2 + 1] = hb[1];
@@ -1181,10 +1190,10 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
     const char* sA = smem + (kt % NSTAGE) * STG;
     const char* sB = sA + TILE;
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) fa[buf][mb] = frag(LA, sA, wm * G::WM + mb * 32, kk);
+    for (int mb = 0; mb < MB; ++mb) fa[buf][mb] = frag(LA, sA, wm * G::WM + mb * 32, kk, G::BM);
     if (with_b)
 #pragma unroll
-      for (int nb = 0; nb < NB; ++nb) fb[SB ? 0 : buf][nb] = frag(LB, sB, wn * G::WN + nb * 32, kk);
+      for (int nb = 0; nb < NB; ++nb) fb[SB ? 0 : buf][nb] = frag(LB, sB, wn * G::WN + nb * 32, kk, G::BN);
   };
 
   if (nk > 0) {
@@ -1221,7 +1230,7 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
               acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][mb], fb[0][nb], acc[mb][nb], 0, 0, 0);
-            if (kk + 1 < KG) fb[0][nb] = frag(LB, sB, wn * G::WN + nb * 32, kk + 1);
+            if (kk + 1 < KG) fb[0][nb] = frag(LB, sB, wn * G::WN + nb * 32, kk + 1, G::BN);
           }
         } else {
 #pragma unroll
@@ -1329,6 +1338,8 @@ static hipError_t launch_gemm_e(int dtype, const GemmArgs& a, hipStream_t s) {
     }
     if constexpr (EPI == EPI_DW)
       if (a.a_layout == LAYOUT_MC && a.b_layout == LAYOUT_KC) return launch_fast<EPI, LAYOUT_MC, LAYOUT_KC>(a, grid, s);
+    if constexpr (EPI == EPI_DH)
+      if (a.a_layout == LAYOUT_KC && a.b_layout == LAYOUT_MC) return launch_fast<EPI, LAYOUT_KC, LAYOUT_MC>(a, grid, s);
     return hipErrorInvalidValue;
   }
   if (a.a_layout != LAYOUT_KC || a.b_layout != LAYOUT_KC) return hipErrorInvalidValue;

@@ -54,17 +54,18 @@ def ws(lib, N, d, V, K, chunk, dt):
 
 
 def test_workspace_size_arithmetic(lib):
-    # gpt-oss-like head at 32K: the bf16 backward workspace holds W^T, the
+    # gpt-oss-like head at 32K: the bf16 backward workspace holds the
     # token-major dZ of one group of chunks over one vocabulary slice (about
-    # as many elements as one chunk over the whole vocabulary), the dH split
-    # partials and the group's fp32 dH sum; nothing scales with N except the
+    # as many elements as one chunk over the whole vocabulary), the group's
+    # H^T, the dH split partials, the group's fp32 dH sum and (unless the
+    # build reads W in place) W^T; nothing scales with N except the
     # forward's per-row KL scratch.
     st, f, b = ws(lib, 32768, 2880, 201088, 100, 2048, L.KDKL_BF16)
     assert st == OK
     Vp = (201088 + 255) // 256 * 256
-    assert b >= 2048 * Vp * 2 + 2880 * Vp * 2
+    assert b >= 2048 * Vp * 2
     assert b < 2048 * Vp * 2 + 2880 * Vp * 2 + 2**30
-    # d not a multiple of 64: the generic path also keeps H_c^T and a
+    # d not a multiple of 64: the generic path also keeps W^T, H_c^T and a
     # vocabulary-major copy of dZ
     _, _, bg = ws(lib, 32768, 2888, 201088, 100, 2048, L.KDKL_BF16)
     assert bg >= 2 * 2048 * Vp * 2 + 2888 * Vp * 2
@@ -245,7 +246,7 @@ def test_dense_sizes(lib):
     Vp = (V + 255) // 256 * 256
     assert sv.value >= 2 * N * Vp * 4 and sv.value < 2 * N * Vp * 4 + 4096  # both grids, fp32
     assert f.value >= N * Vp * 2                                            # the logit grid
-    assert b.value >= N * Vp * 2 + d * Vp * 2                               # dZ grid and W^T
+    assert b.value >= N * Vp * 2                                            # the dZ grid
     assert lib.kdkl_dense_sizes(N, d, V, 0, L.KDKL_BF16, None, None, None) == SHAPE
 
 
@@ -335,3 +336,21 @@ def test_binding_output_checks():
         with pytest.raises(ValueError):
             kd._want(bad, (4, 3), torch.float32, cpu, "dW")
     assert kd._nbytes(torch.zeros(5, dtype=torch.float32)) == 20
+
+
+def test_dh_reading_w_in_place_drops_the_transposed_copy(lib, monkeypatch):
+    # the bf16 backward normally keeps W^T [d, Vp]; with KDKL_DH_W_INPLACE=1
+    # its dH product reads W in place and the workspace shrinks by that copy
+    N, d, V, K, chunk = 32768, 2880, 201088, 100, 2048
+    monkeypatch.delenv("KDKL_DH_W_INPLACE", raising=False)
+    _, f0, b0 = ws(lib, N, d, V, K, chunk, L.KDKL_BF16)
+    monkeypatch.setenv("KDKL_DH_W_INPLACE", "1")
+    _, f1, b1 = ws(lib, N, d, V, K, chunk, L.KDKL_BF16)
+    Vp = (V + 383) // 384 * 384
+    assert f1 == f0
+    assert b0 - b1 >= d * Vp * 2 and b0 - b1 < d * Vp * 2 + 512
+    # the generic path (d not a multiple of 64) always keeps W^T
+    _, _, g1 = ws(lib, N, 2888, V, K, chunk, L.KDKL_BF16)
+    monkeypatch.delenv("KDKL_DH_W_INPLACE")
+    _, _, g0 = ws(lib, N, 2888, V, K, chunk, L.KDKL_BF16)
+    assert g1 == g0

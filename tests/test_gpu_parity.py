@@ -62,6 +62,20 @@ def test_parity_vs_oracle(case, name, over, seed):
     assert maxrel(got["row_kl"], ref["row_kl"]) <= TOL[w.dtype]["loss"] * 10
 
 
+@pytest.mark.parametrize("name,over", [
+    ("gptoss20b_32k", dict(N=80, chunk=32)),  # 320-wide hidden-size tiles, backward groups
+    ("llama3b_8k", dict(N=96, chunk=40)),     # 256-wide hidden-size tiles
+], ids=["d_tile320", "d_tile256"])
+def test_dh_reading_w_in_place(name, over, monkeypatch):
+    # the dH product reading W through the LDS transpose read instead of a W^T copy
+    monkeypatch.setenv("KDKL_DH_W_INPLACE", "1")
+    w, x = _inputs(name, over, None)
+    print(f"case dh_w_in_place {name}: N={w.N} d={w.d} V={w.V} chunk={w.chunk}", flush=True)
+    got = run_gpu(x, w.T, w.chunk)
+    ref = oracle.loss_and_grads(x["H"], x["W"], x["ids"], x["logits"], w.T)
+    assert_parity(got, ref, w.dtype, f"{name} dH reading W in place")
+
+
 def test_chunk_size_independence():
     w, x = _inputs("tiny_fp32", dict(N=64, V=1000, K=5), 21)
     ref = oracle.loss_and_grads(x["H"], x["W"], x["ids"], x["logits"], w.T)
