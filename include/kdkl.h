@@ -96,7 +96,12 @@ const char* kdkl_status_string(int status);
 
 /* Bytes of device workspace needed by kdkl_forward (*fwd_bytes) and by
  * kdkl_backward (*bwd_bytes) for these sizes. Either output may be NULL.
- * Host-only; the same validation as the compute calls. */
+ * Host-only; the same validation as the compute calls. On the bf16 path the
+ * backward workspace holds a transposed copy of W (V * d elements) unless
+ * the environment sets KDKL_DH_W_INPLACE=1, which makes the dH product read
+ * W in place (less memory, slightly slower); ask for the size and call
+ * kdkl_backward under the same setting (a smaller workspace is rejected with
+ * KDKL_ERR_WORKSPACE). */
 kdkl_status kdkl_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K,
                                 int64_t chunk, int dtype,
                                 size_t* fwd_bytes, size_t* bwd_bytes);
