@@ -102,6 +102,21 @@ def test_upstream_gradient_and_accumulate():
     assert err <= 2 * np.finfo(np.float32).eps * np.abs(expect).max() + 1e-5 * np.abs(ref["dW"]).max()
 
 
+def test_upstream_gradient_and_accumulate_in_backward_groups():
+    # the bf16 path taking its chunks in groups over vocabulary slices: each
+    # group's dW read-modify-write adds to the caller's dW, and the upstream
+    # gradient scales both products
+    w, x = _inputs("small_bf16", dict(N=150, d=64, V=270001, K=16, chunk=64, T=1.2), 15)
+    ref = oracle.loss_and_grads(x["H"], x["W"], x["ids"], x["logits"], w.T, g=0.37)
+    scale = float(np.abs(ref["dW"]).max())
+    init = torch.randn(w.V, w.d, dtype=torch.float32) * scale
+    got = run_gpu(x, w.T, w.chunk, g=0.37, accumulate_dW=True, dW_init=init)
+    eh = maxrel(got["dH"], ref["dH"])
+    ew = maxrel(got["dW"] - init.double().numpy(), ref["dW"])
+    print(f"groups g=0.37 accumulate: dH {eh:.2e} dW {ew:.2e}", flush=True)
+    assert eh <= TOL["bf16"]["grad"] and ew <= TOL["bf16"]["grad"]
+
+
 def test_bitwise_determinism():
     w, x = _inputs("small_bf16", dict(N=512, V=8000, chunk=200), 23)
     a = run_gpu(x, w.T, w.chunk)
