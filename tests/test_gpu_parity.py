@@ -41,6 +41,10 @@ CASES = [
     # chunk), and five (a full group of four, then one partial chunk)
     ("bf16_backward_groups2", "small_bf16", dict(N=150, d=64, V=270001, K=16, chunk=64, T=1.2), 15),
     ("bf16_backward_groups4", "small_bf16", dict(N=148, d=64, V=530001, K=12, chunk=32, T=0.8), 16),
+    # the largest teacher top-K the boundary takes, over a small vocabulary:
+    # dozens of teacher entries per column in every vocabulary tile
+    ("bf16_max_K", "small_bf16", dict(N=100, d=128, V=6000, K=1024, chunk=64, T=1.0), 17),
+    ("fp32_max_K", "tiny_fp32", dict(N=40, d=64, V=1500, K=1024, chunk=16, T=0.9), 18),
 ]
 
 
