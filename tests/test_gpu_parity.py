@@ -45,6 +45,9 @@ CASES = [
     # dozens of teacher entries per column in every vocabulary tile
     ("bf16_max_K", "small_bf16", dict(N=100, d=128, V=6000, K=1024, chunk=64, T=1.0), 17),
     ("fp32_max_K", "tiny_fp32", dict(N=40, d=64, V=1500, K=1024, chunk=16, T=0.9), 18),
+    # a single position (one partial token tile)
+    ("bf16_one_position", "small_bf16", dict(N=1, d=128, V=3000, K=10, chunk=64, T=1.0), 19),
+    ("fp32_one_position", "tiny_fp32", dict(N=1, d=64, V=700, K=5, chunk=8, T=1.0), 20),
 ]
 
 
