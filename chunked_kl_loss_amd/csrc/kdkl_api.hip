@@ -212,12 +212,14 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   int64_t t0, t1, t2;
   size_t cur = 0;
   bool ok = true;
-  ok &= mul_ok(P->Cp, K, &t0) && mul_ok(t0, 8, &t0);
+  // the forward takes the backward's groups too (bigger launches fill the
+  // device's rounds better; results per row do not depend on it)
+  ok &= mul_ok(P->Cg, K, &t0) && mul_ok(t0, 8, &t0);
   ok &= region(&cur, t0, &P->f_ent);
-  ok &= region(&cur, P->Cp * 4, &P->f_erow) && region(&cur, P->Cp * 4, &P->f_keep);
-  ok &= mul_ok(P->n_vt + 1, P->Cp, &t1) && mul_ok(t1, 2, &t1);
+  ok &= region(&cur, P->Cg * 4, &P->f_erow) && region(&cur, P->Cg * 4, &P->f_keep);
+  ok &= mul_ok(P->n_vt + 1, P->Cg, &t1) && mul_ok(t1, 2, &t1);
   ok &= region(&cur, t1, &P->f_tstart);
-  ok &= mul_ok(P->Cp, P->n_vt, &t2) && mul_ok(t2, 16, &t2);
+  ok &= mul_ok(P->Cg, P->n_vt, &t2) && mul_ok(t2, 16, &t2);
   ok &= region(&cur, t2, &P->f_part);
   ok &= region(&cur, (N > 0 ? N : 1) * 4, &P->f_rowkl);
   P->f_bytes = cur;
@@ -347,13 +349,15 @@ kdkl_status kdkl_forward(const void* H, const void* W, const int32_t* ids, const
   char* ws = (char*)workspace;
   float* kl = row_kl ? row_kl : (float*)(ws + P.f_rowkl);
   hipError_t e = hipSuccess;
-  for (int64_t r0 = 0; r0 < N && e == hipSuccess; r0 += P.chunk) {
-    const int rows = (int)((N - r0) < P.chunk ? (N - r0) : P.chunk);
+  const int64_t group = P.bg * P.chunk;  // rows per launch: the backward's group
+  for (int64_t r0 = 0; r0 < N && e == hipSuccess; r0 += group) {
+    const int rows = (int)((N - r0) < group ? (N - r0) : group);
     TeacherArgs ta =
-        teacher_args(P, ids, lg, T, r0, rows, P.Cp, ws, P.f_ent, P.f_erow, P.f_keep, P.f_tstart);
+        teacher_args(P, ids, lg, T, r0, rows, P.Cg, ws, P.f_ent, P.f_erow, P.f_keep, P.f_tstart);
     e = timed(K_TEACHER, 0.0, (double)rows * P.K * 8.0 * 2.0, s, [&] { return launch_teacher(ta, s); });
     if (e != hipSuccess) break;
     GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.f_ent, P.f_tstart);
+    g.Cp = P.Cg;
     g.part = (float4*)(ws + P.f_part);
     const double fl = 2.0 * rows * (double)V * d;
     const double by = ((double)V + rows) * d * P.es + (double)rows * P.n_vt * 16.0;

@@ -69,7 +69,7 @@ def test_workspace_size_arithmetic(lib):
     # vocabulary-major copy of dZ
     _, _, bg = ws(lib, 32768, 2888, 201088, 100, 2048, L.KDKL_BF16)
     assert bg >= 2 * 2048 * Vp * 2 + 2888 * Vp * 2
-    assert f < 64 * 2**20
+    assert f < 128 * 2**20  # per-group teacher products and split partials
     # memory is independent of N apart from O(N) scratch
     _, f2, b2 = ws(lib, 262144, 2880, 201088, 100, 2048, L.KDKL_BF16)
     assert b2 == b and f2 - f == (262144 - 32768) * 4
