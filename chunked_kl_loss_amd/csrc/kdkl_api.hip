@@ -124,20 +124,27 @@ static bool dh_reads_w_in_place() {
 #define KDKL_DH_BUSY 0.97
 #endif
 #ifndef KDKL_BWD_GROUP
-#define KDKL_BWD_GROUP 4
+#define KDKL_BWD_GROUP 8
 #endif
 
-// Chunks per backward group on the bf16 main loop. Each vocabulary slice of a
-// group must still give the dW product at least two rounds of workgroups
-// (one per compute unit), or the partial last round costs more than the
-// read-modify-writes saved; and a group never spans more rows than there are.
+// Chunks per group (both calls) on the bf16 main loop: the largest of 8, 4,
+// 2 whose vocabulary slice still gives the dW product a full round of
+// workgroups (one per compute unit) and fills its rounds to 95% or more (a
+// partial last round costs more than the read-modify-writes saved), over no
+// more chunks than there are.
 static int backward_group(const Plan& P, int64_t N) {
   int bg = KDKL_BWD_GROUP;
   if (!P.fast || bg < 2) return 1;
   const int64_t chunks = (N + P.chunk - 1) / P.chunk;
-  while (bg > 1 && (bg > chunks || (P.V / bg / 256) * ((P.d + P.dtile - 1) / P.dtile) < 2 * kComputeUnits ||
-                    !gemm_fast_path(P.dtype, P.d, P.Vp, round_up(bg * P.chunk, kTokenTile))))
-    bg >>= 1;
+  const int64_t dtiles = (P.d + P.dtile - 1) / P.dtile;
+  for (; bg > 1; bg >>= 1) {
+    if (bg > chunks || !gemm_fast_path(P.dtype, P.d, P.Vp, round_up(bg * P.chunk, kTokenTile))) continue;
+    const int64_t align = P.vt % 256 == 0 ? P.vt : P.vt * 2;  // slice starts, as make_plan sets them
+    const int64_t vpart = round_up((P.V + bg - 1) / bg, align);
+    const int64_t tiles = (vpart + 255) / 256 * dtiles;
+    const int64_t rounds = (tiles + kComputeUnits - 1) / kComputeUnits;
+    if (tiles >= kComputeUnits && tiles * 100 >= rounds * kComputeUnits * 95) break;
+  }
   return bg;
 }
 
