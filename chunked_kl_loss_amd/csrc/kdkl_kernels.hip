@@ -1040,6 +1040,9 @@ __device__ __forceinline__ void wait_vmcnt() {
 #ifndef KDKL_DW_GRID42
 #define KDKL_DW_GRID42 1
 #endif
+#ifndef KDKL_EARLY_BARRIER
+#define KDKL_EARLY_BARRIER 1
+#endif
 template <class G, int EPI, int BK, int NSTAGE, int LA, int LB>
 __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArgs p) {
   constexpr int MB = G::MB, NB = G::NB;
@@ -1141,7 +1144,18 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
   // loads of the next stage are spread over the k-groups of the current step
   // so that their LDS writes do not arrive as one burst against the fragment
   // reads.
-  constexpr int NPART = KDKL_DMA_SPREAD < KG ? KDKL_DMA_SPREAD : KG;
+  // With two stages the k-step barrier can sit before the last k-group's
+  // MFMAs instead of after them (EB): by then every fragment of the stage is
+  // in registers, so the next stage's first fragments are read while those
+  // MFMAs run rather than after the barrier, when all wavefronts would read
+  // at once with the matrix cores idle. The next stage's loads then go out
+  // over the k-groups before the last one. Measured per product, this pays
+  // only for dW (about 5% per launch); dH and the 256 x 256 tiles ran 3-6%
+  // slower with it, and the forward and dZ tiles (single-buffered B
+  // fragments) no longer fit their registers.
+  constexpr bool EB = KDKL_EARLY_BARRIER && EPI == EPI_DW && NSTAGE == 2 && KG >= 2 && !G::kSingleB;
+  constexpr int KGI = EB ? KG - 1 : KG;  // k-groups that issue loads
+  constexpr int NPART = KDKL_DMA_SPREAD < KGI ? KDKL_DMA_SPREAD : KGI;
   auto issue_part = [&](int kt, int part) {
     char* base = smem + (kt % NSTAGE) * STG;
     const char* ba = stage_base(LA, p.A, p.lda, m0, kt);
@@ -1208,6 +1222,7 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
     load_frags(0, 0, 0, true);
     for (int kt = 0; kt < nk; ++kt) {
       const bool more = kt + NSTAGE - 1 < nk;
+      const bool next = kt + 1 < nk;
 #pragma unroll
       for (int kk = 0; kk < KG; ++kk) {
         // fragments of this k-group read through the transpose (assembly,
@@ -1219,18 +1234,34 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
         if (more) {
 #pragma unroll
           for (int part = 0; part < NPART; ++part)
-            if (part * KG / NPART == kk) issue_part(kt + NSTAGE - 1, part);
+            if (part * KGI / NPART == kk) issue_part(kt + NSTAGE - 1, part);
         }
-        if (kk + 1 < KG) load_frags(kt, kk + 1, (kk + 1) & 1, !SB);
+        if (EB && kk == KG - 1) {
+          // this wavefront's fragment reads and stage loads are complete;
+          // after the barrier so are everyone's (the stage may be reused and
+          // the next one has landed)
+          asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+          wait_vmcnt<0>();
+          phase_barrier();
+        }
+        if (kk + 1 < KG)
+          load_frags(kt, kk + 1, (kk + 1) & 1, !SB);
+        else if (EB && next)
+          load_frags(kt + 1, 0, 0, !SB);
         if constexpr (SB) {
-          // each B fragment is replaced by the next k-group's once its MFMAs are issued
+          // each B fragment is replaced by the next k-group's once its MFMAs
+          // are issued (with EB, after the last k-group: the next stage's first)
           const char* sB = smem + (kt % NSTAGE) * STG + TILE;
+          const char* sBn = smem + ((kt + 1) % NSTAGE) * STG + TILE;
 #pragma unroll
           for (int nb = 0; nb < NB; ++nb) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
               acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][mb], fb[0][nb], acc[mb][nb], 0, 0, 0);
-            if (kk + 1 < KG) fb[0][nb] = frag(LB, sB, wn * G::WN + nb * 32, kk + 1, G::BN);
+            if (kk + 1 < KG)
+              fb[0][nb] = frag(LB, sB, wn * G::WN + nb * 32, kk + 1, G::BN);
+            else if (EB && next)
+              fb[0][nb] = frag(LB, sBn, wn * G::WN + nb * 32, 0, G::BN);
           }
         } else {
 #pragma unroll
@@ -1241,13 +1272,15 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
                   __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][mb], fb[kk & 1][nb], acc[mb][nb], 0, 0, 0);
         }
       }
-      // stage kt + 1 must have landed; later stages may still be in flight
-      if (more)
-        wait_vmcnt<LPS * (NSTAGE - 2)>();
-      else
-        wait_vmcnt<0>();
-      phase_barrier();
-      if (kt + 1 < nk) load_frags(kt + 1, 0, 0, true);
+      if constexpr (!EB) {
+        // stage kt + 1 must have landed; later stages may still be in flight
+        if (more)
+          wait_vmcnt<LPS * (NSTAGE - 2)>();
+        else
+          wait_vmcnt<0>();
+        phase_barrier();
+        if (next) load_frags(kt + 1, 0, 0, true);
+      }
     }
   }
   gemm_epilogue<G, 2, EPI>(p, acc, t, smem);
