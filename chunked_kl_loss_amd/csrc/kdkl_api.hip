@@ -121,7 +121,7 @@ static bool dh_reads_w_in_place() {
   return e != nullptr && e[0] == '1' && e[1] == 0;
 }
 #ifndef KDKL_DH_BUSY
-#define KDKL_DH_BUSY 0.97
+#define KDKL_DH_BUSY 0.96
 #endif
 #ifndef KDKL_BWD_GROUP
 #define KDKL_BWD_GROUP 8
@@ -197,7 +197,7 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   }
   P->n_parts = (int)((V + P->vpart - 1) / P->vpart);
   // dH split-K: the fewest splits S whose launch keeps the 256 compute units
-  // within 3% as busy as the best S does, when every workgroup does 1/S of a
+  // within 4% as busy as the best S does, when every workgroup does 1/S of a
   // tile's work and the units take them in rounds (fewer splits, fewer fp32
   // partials), with each split at least 8 k-steps.
   const int64_t tiles = ((P->Cg + 255) / 256) * ((d + P->dtile - 1) / P->dtile);
