@@ -21,6 +21,7 @@ from ._lib import KDKL_BF16, KDKL_F32, KdklError, KernelStat, check, load as _lo
 
 __all__ = [
     "workspace_size",
+    "plan_info",
     "kdkl_forward",
     "kdkl_backward",
     "FusedKLLoss",
@@ -83,6 +84,15 @@ def workspace_size(N: int, d: int, V: int, K: int, chunk: int, dtype: torch.dtyp
     check(_load().kdkl_workspace_size(N, d, V, K, chunk, code, C.byref(f), C.byref(b)),
           "kdkl_workspace_size")
     return f.value, b.value
+
+
+def plan_info(N: int, d: int, V: int, K: int, chunk: int, dtype: torch.dtype) -> Tuple[int, int, int]:
+    """(chunks per group, vocabulary slices per group, dH splits) the calls use."""
+    g, v, s = C.c_int(), C.c_int(), C.c_int()
+    code = KDKL_BF16 if dtype == torch.bfloat16 else KDKL_F32
+    check(_load().kdkl_plan_info(N, d, V, K, chunk, code, C.byref(g), C.byref(v), C.byref(s)),
+          "kdkl_plan_info")
+    return g.value, v.value, s.value
 
 
 def _check_shapes(H, W, ids, logits):

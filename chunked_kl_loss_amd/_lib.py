@@ -45,6 +45,8 @@ SIGNATURES = {
     "kdkl_status_string": (C.c_char_p, [C.c_int]),
     "kdkl_workspace_size": (C.c_int, [_I64, _I64, _I64, _I32, _I64, C.c_int,
                                       C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
+    "kdkl_plan_info": (C.c_int, [_I64, _I64, _I64, _I32, _I64, C.c_int, C.POINTER(C.c_int),
+                                 C.POINTER(C.c_int), C.POINTER(C.c_int)]),
     "kdkl_forward": (C.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, C.c_float, _I64,
                                C.c_int, _P, _P, _P, _P, C.c_size_t, _P]),
     "kdkl_backward": (C.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, C.c_float, _I64,

@@ -341,6 +341,17 @@ kdkl_status kdkl_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K, int6
   return KDKL_OK;
 }
 
+kdkl_status kdkl_plan_info(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int dtype,
+                           int* chunks_per_group, int* vocab_slices, int* dh_splits) {
+  Plan P;
+  kdkl_status st = make_plan(N, d, V, K, chunk, dtype, &P);
+  if (st != KDKL_OK) return st;
+  if (chunks_per_group) *chunks_per_group = P.bg;
+  if (vocab_slices) *vocab_slices = P.n_parts;
+  if (dh_splits) *dh_splits = P.dh_splits;
+  return KDKL_OK;
+}
+
 kdkl_status kdkl_forward(const void* H, const void* W, const int32_t* ids, const float* lg, int64_t N,
                          int64_t d, int64_t V, int32_t K, float T, int64_t chunk, int dtype, float* loss,
                          float* row_lse, float* row_kl, void* workspace, size_t workspace_bytes,

@@ -106,6 +106,23 @@ kdkl_status kdkl_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K,
                                 int64_t chunk, int dtype,
                                 size_t* fwd_bytes, size_t* bwd_bytes);
 
+/* How the calls will block the work for these sizes (host-only, the same
+ * validation as kdkl_workspace_size; each output may be NULL):
+ *   *chunks_per_group: slices of `chunk` positions taken together per launch
+ *     (1 = one slice at a time); the backward covers the vocabulary of a
+ *     group in *vocab_slices consecutive slices, so dW's fp32
+ *     read-modify-write happens once per group and slice;
+ *   *dh_splits: split-K count of the dH product per launch (fp32 partials
+ *     summed in a fixed order).
+ * The blocking never changes the results beyond rounding order; it is
+ * reported so that callers and tests can tell which launch shapes a size
+ * exercises. The slices themselves are the chunks over positions that the
+ * loss is computed in [P1 "Making knowledge distillation cheap enough to
+ * run at scale", section "Fused chunked KL loss"]. */
+kdkl_status kdkl_plan_info(int64_t N, int64_t d, int64_t V, int32_t K,
+                           int64_t chunk, int dtype, int* chunks_per_group,
+                           int* vocab_slices, int* dh_splits);
+
 /* Forward pass of the fused chunked KL loss.
  *   H [N, d] dtype, W [V, d] dtype, topk_ids [N, K] int32, topk_logits
  *   [N, K] fp32; T > 0; chunk = positions per slice (>= 1; the last slice may

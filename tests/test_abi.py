@@ -354,3 +354,56 @@ def test_dh_reading_w_in_place_drops_the_transposed_copy(lib, monkeypatch):
     monkeypatch.delenv("KDKL_DH_W_INPLACE")
     _, _, g0 = ws(lib, N, 2888, V, K, chunk, L.KDKL_BF16)
     assert g1 == g0
+
+
+def plan(lib, N, d, V, K, chunk, dt):
+    g, v, s = C.c_int(), C.c_int(), C.c_int()
+    st = lib.kdkl_plan_info(N, d, V, K, chunk, dt, C.byref(g), C.byref(v), C.byref(s))
+    assert st == OK, L_status(lib, st)
+    return g.value, v.value, s.value
+
+
+def L_status(lib, st):
+    return lib.kdkl_status_string(st).decode()
+
+
+@pytest.mark.parametrize("sizes,groups", [
+    # the GPU parity cases for backward groups: each must exercise its size
+    ((150, 64, 131001, 16, 64), 2),
+    ((148, 64, 262001, 12, 32), 4),
+    ((133, 64, 524001, 20, 16), 8),
+    # the named workloads (N, d, V, K, chunk): an eighth of gpt-oss's
+    # vocabulary would leave dW's last round of workgroups about half empty,
+    # an eighth of Llama's fills 98% of three rounds; the 2K workload's
+    # slices are too small for a full round
+    ((32768, 2880, 201088, 100, 2048), 4),
+    ((262144, 2880, 201088, 100, 4096), 4),
+    ((8192, 3072, 128256, 100, 1024), 8),
+    ((2048, 1024, 32000, 100, 256), 1),
+])
+def test_plan_groups(lib, sizes, groups):
+    g, v, s = plan(lib, *sizes, L.KDKL_BF16)
+    assert g == groups
+    assert v == groups  # as many vocabulary slices as chunks per group
+    assert s >= 1
+
+
+def test_plan_groups_never_exceed_the_chunks(lib):
+    # two chunks only: a group never spans more chunks than there are
+    g, v, _ = plan(lib, 128, 64, 524001, 20, 64, L.KDKL_BF16)
+    assert g <= 2 and v == g
+
+
+def test_plan_fp32_takes_one_chunk_at_a_time(lib):
+    assert plan(lib, 128, 256, 4096, 16, 32, L.KDKL_F32)[:2] == (1, 1)
+
+
+def test_plan_dh_splits_fill_the_rounds(lib):
+    # gpt-oss at 32K: 8192-row groups by 2880 columns on 256 x 320 tiles is
+    # 288 tiles; six splits fill 96.4% of seven rounds of 256 workgroups
+    assert plan(lib, 32768, 2880, 201088, 100, 2048, L.KDKL_BF16)[2] == 6
+
+
+def test_plan_info_validates_like_the_compute_calls(lib):
+    assert lib.kdkl_plan_info(10, 8, 16, 0, 4, L.KDKL_BF16, None, None, None) != OK
+    assert lib.kdkl_plan_info(10, 8, 16, 2, 4, L.KDKL_BF16, None, None, None) == OK
