@@ -126,6 +126,9 @@ static bool dh_reads_w_in_place() {
 #ifndef KDKL_BWD_GROUP
 #define KDKL_BWD_GROUP 8
 #endif
+#ifndef KDKL_GROUP_FILL
+#define KDKL_GROUP_FILL 95
+#endif
 
 // Chunks per group (both calls) on the bf16 main loop: the largest of 8, 4,
 // 2 whose vocabulary slice still gives the dW product a full round of
@@ -143,7 +146,7 @@ static int backward_group(const Plan& P, int64_t N) {
     const int64_t vpart = round_up((P.V + bg - 1) / bg, align);
     const int64_t tiles = (vpart + 255) / 256 * dtiles;
     const int64_t rounds = (tiles + kComputeUnits - 1) / kComputeUnits;
-    if (tiles >= kComputeUnits && tiles * 100 >= rounds * kComputeUnits * 95) break;
+    if (tiles >= kComputeUnits && tiles * 100 >= rounds * kComputeUnits * KDKL_GROUP_FILL) break;
   }
   return bg;
 }
