@@ -118,7 +118,7 @@ kdkl_status kdkl_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K,
  * reported so that callers and tests can tell which launch shapes a size
  * exercises. The slices themselves are the chunks over positions that the
  * loss is computed in [P1 "Making knowledge distillation cheap enough to
- * run at scale", section "Fused chunked KL loss"]. */
+ * run at scale", section "Two system changes", fused chunked KL bullet]. */
 kdkl_status kdkl_plan_info(int64_t N, int64_t d, int64_t V, int32_t K,
                            int64_t chunk, int dtype, int* chunks_per_group,
                            int* vocab_slices, int* dh_splits);
