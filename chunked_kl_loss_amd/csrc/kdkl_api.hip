@@ -110,15 +110,25 @@ struct Plan {
   size_t b_ent, b_erow, b_keep, b_scale, b_tstart, b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart, b_dhacc, b_bytes;
 };
 
-// The dH product on the bf16 main loop reads a W^T copy written once per
-// backward call. With KDKL_DH_W_INPLACE=1 in the environment (read when the
-// plan is made, so the workspace size and the call must see the same value)
-// it reads W in place through the LDS transpose read instead: V * d * 2
-// fewer bytes of workspace, no transpose, for dH products ~7% slower (twice
-// the LDS instructions per MFMA).
-static bool dh_reads_w_in_place() {
+// The dH product on the bf16 main loop reads either a W^T copy written once
+// per backward call or W in place through the LDS transpose read (V * d * 2
+// fewer bytes of workspace, no transpose, but each dH launch measured about
+// 2% slower on 256-wide hidden-size tiles and 4% on 320-wide ones). The plan
+// reads W in place when the modelled extra time of one call's dH launches
+// (at about 1.2 PFLOP/s) is below that of the transpose (W read and written
+// at about 5 TB/s): Llama-like heads at 8K positions, not gpt-oss-like ones
+// at 32K or more. KDKL_DH_W_INPLACE=1 or 0 in the environment forces either
+// (read when the plan is made, so the workspace size and the call must see
+// the same value).
+static bool dh_reads_w_in_place(const Plan& P, int64_t N) {
   const char* e = getenv("KDKL_DH_W_INPLACE");
-  return e != nullptr && e[0] == '1' && e[1] == 0;
+  if (e != nullptr && (e[0] == '0' || e[0] == '1') && e[1] == 0) return e[0] == '1';
+  const int64_t group = P.bg * P.chunk;
+  const double launches = (double)((N + group - 1) / group) * (double)P.n_parts;
+  const double dh_ms = 2.0 * (double)P.Cg * (double)P.vpart * (double)P.d / 1.2e12;
+  const double penalty = P.dtile == 256 ? 0.02 : 0.04;
+  const double transpose_ms = 4.0 * (double)P.V * (double)P.d / 5.0e9;
+  return launches * dh_ms * penalty < transpose_ms;
 }
 #ifndef KDKL_DH_BUSY
 #define KDKL_DH_BUSY 0.96
@@ -184,7 +194,6 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
     P->Vp = round_up(V, vt);
   }
   P->dtile = gemm_d_tile(P->fast, d);
-  P->wt = !P->fast || !dh_reads_w_in_place();
   P->n_vt = P->Vp / P->vt;
   if (P->Cp > INT32_MAX / 4) return KDKL_ERR_OVERFLOW;
   P->bg = backward_group(*P, N);
@@ -199,6 +208,7 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
     P->vpart = round_up((V + P->bg - 1) / P->bg, align);
   }
   P->n_parts = (int)((V + P->vpart - 1) / P->vpart);
+  P->wt = !P->fast || !dh_reads_w_in_place(*P, N);
   // dH split-K: the fewest splits S whose launch keeps the 256 compute units
   // within 4% as busy as the best S does, when every workgroup does 1/S of a
   // tile's work and the units take them in rounds (fewer splits, fewer fp32

@@ -97,10 +97,13 @@ const char* kdkl_status_string(int status);
 /* Bytes of device workspace needed by kdkl_forward (*fwd_bytes) and by
  * kdkl_backward (*bwd_bytes) for these sizes. Either output may be NULL.
  * Host-only; the same validation as the compute calls. On the bf16 path the
- * backward workspace holds a transposed copy of W (V * d elements) unless
- * the environment sets KDKL_DH_W_INPLACE=1, which makes the dH product read
- * W in place (less memory, slightly slower); ask for the size and call
- * kdkl_backward under the same setting (a smaller workspace is rejected with
+ * backward workspace may hold a transposed copy of W (V * d elements) for
+ * the dH product: the plan leaves it out, and reads W in place, where that
+ * costs less time for these sizes (few dH launches per call, e.g. 8K
+ * positions of a Llama-like head); KDKL_DH_W_INPLACE=1 in the environment
+ * forces the in-place read (less memory, slightly slower on large calls),
+ * KDKL_DH_W_INPLACE=0 the copy. Ask for the size and call kdkl_backward
+ * under the same setting (a smaller workspace is rejected with
  * KDKL_ERR_WORKSPACE). */
 kdkl_status kdkl_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K,
                                 int64_t chunk, int dtype,

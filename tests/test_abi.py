@@ -407,3 +407,22 @@ def test_plan_dh_splits_fill_the_rounds(lib):
 def test_plan_info_validates_like_the_compute_calls(lib):
     assert lib.kdkl_plan_info(10, 8, 16, 0, 4, L.KDKL_BF16, None, None, None) != OK
     assert lib.kdkl_plan_info(10, 8, 16, 2, 4, L.KDKL_BF16, None, None, None) == OK
+
+
+@pytest.mark.parametrize("sizes,in_place", [
+    ((8192, 3072, 128256, 100, 1024), True),     # Llama-like head, 8K: 8 dH launches per call
+    ((32768, 2880, 201088, 100, 2048), False),   # gpt-oss-like head, 32K: 16 launches
+    ((262144, 2880, 201088, 100, 4096), False),  # the same head at 256K: 64 launches
+])
+def test_w_copy_chosen_per_shape(lib, monkeypatch, sizes, in_place):
+    # by default the dH product reads W in place only where one call's slower
+    # dH launches cost less than writing the W^T copy; the environment forces either
+    monkeypatch.delenv("KDKL_DH_W_INPLACE", raising=False)
+    _, _, b_default = ws(lib, *sizes, L.KDKL_BF16)
+    monkeypatch.setenv("KDKL_DH_W_INPLACE", "1")
+    _, _, b_in_place = ws(lib, *sizes, L.KDKL_BF16)
+    monkeypatch.setenv("KDKL_DH_W_INPLACE", "0")
+    _, _, b_copy = ws(lib, *sizes, L.KDKL_BF16)
+    d, V = sizes[1], sizes[2]
+    assert b_copy - b_in_place >= d * V * 2
+    assert b_default == (b_in_place if in_place else b_copy)

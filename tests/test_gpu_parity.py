@@ -76,11 +76,13 @@ def test_parity_vs_oracle(case, name, over, seed):
     ("gptoss20b_32k", dict(N=80, chunk=32)),  # 320-wide hidden-size tiles, backward groups
     ("llama3b_8k", dict(N=96, chunk=40)),     # 256-wide hidden-size tiles
 ], ids=["d_tile320", "d_tile256"])
-def test_dh_reading_w_in_place(name, over, monkeypatch):
-    # the dH product reading W through the LDS transpose read instead of a W^T copy
-    monkeypatch.setenv("KDKL_DH_W_INPLACE", "1")
+@pytest.mark.parametrize("in_place", ["1", "0"])
+def test_dh_reading_w_in_place(name, over, in_place, monkeypatch):
+    # the dH product reading W through the LDS transpose read ("1") or a W^T
+    # copy ("0"), whichever the plan would pick for these sizes
+    monkeypatch.setenv("KDKL_DH_W_INPLACE", in_place)
     w, x = _inputs(name, over, None)
-    print(f"case dh_w_in_place {name}: N={w.N} d={w.d} V={w.V} chunk={w.chunk}", flush=True)
+    print(f"case dh_w_in_place={in_place} {name}: N={w.N} d={w.d} V={w.V} chunk={w.chunk}", flush=True)
     got = run_gpu(x, w.T, w.chunk)
     ref = oracle.loss_and_grads(x["H"], x["W"], x["ids"], x["logits"], w.T)
     assert_parity(got, ref, w.dtype, f"{name} dH reading W in place")
