@@ -30,6 +30,24 @@ gradient row, and the mean runs over the positions that are kept (N is their
 number below; with none kept the loss is NaN and every gradient is zero). The
 other entries of an ignored row are never used.
 
+Teacher ids that break the pages' setting of K distinct in-vocabulary ids per
+position (readings; the pages only describe a cache of the teacher's top 100
+tokens per position [P1, "Two system changes", offline distillation
+paragraph]):
+
+* an id outside [0, V) keeps its share of the teacher's softmax over K, but
+  the student has no entry for it: its gathered student logit reads as 0 and
+  it is not part of the student's normalisation, so its term is
+  ``p_k (log p_k + lse_i)``, and it adds nothing to the gradient's scatter;
+* a repeated id is gathered once per entry (the loss is read entry by entry:
+  ``sum_k p_k (log p_k - log q_i[id_k])``) and the scatter adds its masses.
+
+The dense-grid baseline (``dense_kl_loss``) cannot hold either case the same
+way: its grid merges repeated ids into one probability ``P_v`` and has no
+cell for an id outside [0, V), so it computes ``sum_v P_v (log P_v - log
+q_v)`` over the grid. The two agree whenever a position's ids are distinct and
+in range; the gradients agree always.
+
 Gradient (derived here; the pages say a closed form exists but do not print
 it [P1, section "The resulting student model", last paragraph]): with
 upstream scalar ``g``,
@@ -105,6 +123,19 @@ def _usable_ids(ids: np.ndarray, kept: np.ndarray) -> np.ndarray:
     return np.where(kept[:, None], ids, 0)
 
 
+def _in_vocab(ids_rows: np.ndarray, V: int) -> np.ndarray:
+    """Boolean mask of the ids that name a vocabulary entry."""
+    return (ids_rows >= 0) & (ids_rows < V)
+
+
+def _logq_at(logq: np.ndarray, lse: np.ndarray, ids_rows: np.ndarray) -> np.ndarray:
+    """log q_i[id_ik] for each teacher entry; an id outside [0, V) has no
+    student entry, its tempered logit reads as 0, so its value is -lse_i."""
+    ok = _in_vocab(ids_rows, logq.shape[1])
+    at = np.take_along_axis(logq, np.where(ok, ids_rows, 0), axis=1)
+    return np.where(ok, at, -lse[:, None])
+
+
 def _logsumexp_rows(a: np.ndarray) -> np.ndarray:
     m = a.max(axis=1, keepdims=True)
     return m[:, 0] + np.log(np.exp(a - m).sum(axis=1))
@@ -149,7 +180,7 @@ def forward(H, W, ids, logits, T: float, block: int = 256) -> Dict[str, object]:
         r1 = min(n_rows, r0 + block)
         logq, lse = student_log_softmax(H[r0:r1], W, T)
         p, logp = teacher_distribution(logits[r0:r1], T)
-        logq_at = np.take_along_axis(logq, ids[r0:r1], axis=1)
+        logq_at = _logq_at(logq, lse, ids[r0:r1])
         row_kl[r0:r1] = (p * (logp - logq_at)).sum(axis=1)
         row_lse[r0:r1] = lse
     row_kl[~kept] = 0.0
@@ -163,8 +194,11 @@ def _dz_rows(H_rows, W, ids_rows, logits_rows, T, coef):
     q = np.exp(logq)
     p, _ = teacher_distribution(logits_rows, T)
     target = np.zeros_like(q)
+    # scatter-add of the teacher mass onto the ids that name a vocabulary
+    # entry (repeated ids add up; an id outside [0, V) adds nothing)
     rows = np.repeat(np.arange(q.shape[0]), p.shape[1])
-    np.add.at(target, (rows, ids_rows.reshape(-1)), p.reshape(-1))
+    ok = _in_vocab(ids_rows, q.shape[1]).reshape(-1)
+    np.add.at(target, (rows[ok], ids_rows.reshape(-1)[ok]), p.reshape(-1)[ok])
     return coef * (q - target)
 
 
@@ -201,7 +235,8 @@ def dense_kl_loss(H, W, ids, logits, T: float) -> float:
     """The pages' dense baseline on a tiny problem: build the full teacher
     probability grid (zeros off the top-K) and the full student log-prob grid,
     then sum ``P (log P - log Q)`` over the grid where P > 0, divided by N
-    [P1, "Two system changes", dense KL bullet]."""
+    [P1, "Two system changes", dense KL bullet]. Repeated ids share one grid
+    cell (their masses add); ids outside [0, V) have no cell."""
     H = _f64(H)
     W = _f64(W)
     ids = _ids(ids)
@@ -215,7 +250,8 @@ def dense_kl_loss(H, W, ids, logits, T: float) -> float:
             continue
         e = np.exp(a[i] - a[i].max())
         for k in range(K):
-            P[i, ids[i, k]] += e[k] / e.sum()
+            if 0 <= ids[i, k] < V:  # the grid has no cell for other ids
+                P[i, ids[i, k]] += e[k] / e.sum()
     Z = H @ W.T / float(T)
     logQ = np.empty_like(Z)
     for i in range(N):
@@ -255,7 +291,7 @@ def sampled_rows(H, W, ids, logits, T: float, rows: Iterable[int],
             dh_out[j] = 0.0
             continue
         p, logp = teacher_distribution(lgr, T)
-        kl_out[j] = (p * (logp - np.take_along_axis(logq, idr, axis=1))).sum()
+        kl_out[j] = (p * (logp - _logq_at(logq, lse, idr))).sum()
         dz = _dz_rows(Hr, Wf, idr, lgr, T, coef)
         dh_out[j] = (dz @ Wf)[0]
     return {"rows": rows, "row_lse": lse_out, "row_kl": kl_out, "dH_rows": dh_out}

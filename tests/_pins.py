@@ -248,6 +248,84 @@ def pin_row_functions(o):
            what="sampled dW rows")
 
 
+def pin_fused_brute_force_dropped_and_repeated_ids(o):
+    """Pure-Python loops (math module only) on a tiny problem whose teacher
+    ids break the pages' setting: ids outside [0, V) (7, 6, -2, -5 with V = 6)
+    keep their share of the teacher's normalisation but gather nothing and
+    scatter nothing, and a repeated id is gathered per entry and scatters
+    the sum of its masses. Written as KL = sum p log p - sum_valid p s[id] +
+    lse (the oracle uses sum p (log p - log q[id])); the loss is checked
+    against central finite differences too, and the dense grid (repeated ids
+    merged into one cell, no cell for the others) against a loop over the
+    grid."""
+    rng = np.random.default_rng(28)
+    N, d, V, K, T, g = 4, 3, 6, 3, 1.9, 0.8
+    H = rng.standard_normal((N, d))
+    W = rng.standard_normal((V, d))
+    ids = np.array([[0, 5, 2], [7, 1, -2], [3, 3, 4], [6, -5, 0]])
+    logits = rng.standard_normal((N, K))
+    kl, lses, dz = [], [], np.zeros((N, V))
+    for i in range(N):
+        a = [logits[i, k] / T for k in range(K)]
+        ma = max(a)
+        za = sum(math.exp(x - ma) for x in a)
+        p = [math.exp(x - ma) / za for x in a]
+        s = [sum(H[i, j] * W[v, j] for j in range(d)) / T for v in range(V)]
+        ms = max(s)
+        lse = ms + math.log(sum(math.exp(x - ms) for x in s))
+        val = sum(p[k] * math.log(p[k]) for k in range(K)) + lse
+        for k in range(K):
+            if 0 <= ids[i, k] < V:
+                val -= p[k] * s[ids[i, k]]
+        kl.append(val)
+        lses.append(lse)
+        for v in range(V):
+            mass = sum(p[k] for k in range(K) if ids[i, k] == v)
+            dz[i, v] = g / (N * T) * (math.exp(s[v] - lse) - mass)
+    dH = [[sum(dz[i, v] * W[v, j] for v in range(V)) for j in range(d)] for i in range(N)]
+    dW = [[sum(dz[i, v] * H[i, j] for i in range(N)) for j in range(d)] for v in range(V)]
+    out = o.forward(H, W, ids, logits, T)
+    _close(out["row_kl"], kl, 1e-13, what="bad ids: row_kl")
+    _close(out["row_lse"], lses, 1e-13, what="bad ids: row_lse")
+    _close(out["loss"], sum(kl) / N, 1e-13, what="bad ids: loss")
+    gdH, gdW = o.backward(H, W, ids, logits, T, g)
+    _close(gdH, dH, 1e-13, what="bad ids: dH")
+    _close(gdW, dW, 1e-13, what="bad ids: dW")
+    sr = o.sampled_rows(H, W, ids, logits, T, [1, 2, 3], N, g)
+    _close(sr["row_kl"], [kl[1], kl[2], kl[3]], 1e-13, what="bad ids: sampled kl")
+    _close(sr["dH_rows"], [dH[1], dH[2], dH[3]], 1e-13, what="bad ids: sampled dH")
+    _close(o.dw_rows(H, W, ids, logits, T, [0, 3, 5], out["row_lse"], g), [dW[0], dW[3], dW[5]], 1e-12,
+           what="bad ids: dW rows")
+    # the gradient is the exact gradient of this loss: central differences
+    h = 1e-6
+    fH = np.zeros_like(H)
+    for idx in np.ndindex(H.shape):
+        Hp = H.copy(); Hp[idx] += h
+        Hm = H.copy(); Hm[idx] -= h
+        fH[idx] = g * (o.forward(Hp, W, ids, logits, T)["loss"] - o.forward(Hm, W, ids, logits, T)["loss"]) / (2 * h)
+    _close(gdH, fH, 1e-6, what="bad ids: finite differences dH")
+    # the dense grid: one cell per vocabulary entry
+    grid = 0.0
+    for i in range(N):
+        a = [logits[i, k] / T for k in range(K)]
+        ma = max(a)
+        za = sum(math.exp(x - ma) for x in a)
+        for v in range(V):
+            P = sum(math.exp(a[k] - ma) / za for k in range(K) if ids[i, k] == v)
+            if P > 0:
+                s = [sum(H[i, j] * W[u, j] for j in range(d)) / T for u in range(V)]
+                grid += P * (math.log(P) - (s[v] - lses[i]))
+    _close(o.dense_kl_loss(H, W, ids, logits, T), grid / N, 1e-13, what="bad ids: dense grid")
+    # the forward-chunked functions on Z = H W^T give the same loss and, by
+    # the chain rule, the same gradients
+    if hasattr(o, "logits_forward"):
+        Z = H @ W.T
+        _close(o.logits_forward(Z, ids, logits, T)["row_kl"], kl, 1e-13, what="bad ids: logits row_kl")
+        dZ = o.logits_backward(Z, ids, logits, T, g)
+        _close(dZ @ W, dH, 1e-13, what="bad ids: chain rule dH")
+        _close(dZ.T @ H, dW, 1e-13, what="bad ids: chain rule dW")
+
+
 # --- forward-chunked KL (the student's logit grid is given) ------------------
 
 def _rand_logits_problem(rng, N, V, K, scale=1.0):
@@ -485,6 +563,7 @@ ALL_PINS = [
     pin_finite_differences,
     pin_invariants,
     pin_row_functions,
+    pin_fused_brute_force_dropped_and_repeated_ids,
     pin_logits_cross_entropy,
     pin_logits_dense_libraries,
     pin_logits_finite_differences,

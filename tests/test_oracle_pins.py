@@ -30,11 +30,20 @@ MUTANTS = [
      "s = (_f64(H_rows) @ _f64(W).T)"),
     ("teacher_not_renormalised", "logp = a - _logsumexp_rows(a)[:, None]", "logp = a - a.max()"),
     ("grad_missing_T", "coef = float(g) / (N * float(T))", "coef = float(g) / N"),
-    ("gather_sorted_ids", "np.add.at(target, (rows, ids_rows.reshape(-1)), p.reshape(-1))",
-     "np.add.at(target, (rows, np.sort(ids_rows, axis=1).reshape(-1)), p.reshape(-1))"),
+    ("gather_sorted_ids", "np.add.at(target, (rows[ok], ids_rows.reshape(-1)[ok]), p.reshape(-1)[ok])",
+     "np.add.at(target, (rows[ok], np.sort(ids_rows, axis=1).reshape(-1)[ok]), p.reshape(-1)[ok])"),
     ("dW_wrong_operand", "dW += dZ.T @ H[r0:r1]", "dW += dZ.T @ (H[r0:r1] * 0.5)"),
     ("sum_not_mean", "loss = math.fsum(row_kl.tolist()) / N if N",
      "loss = math.fsum(row_kl.tolist()) if N"),
+    # teacher ids outside [0, V) and repeated ids (fused functions)
+    ("fused_gather_wraps_ids",
+     "at = np.take_along_axis(logq, np.where(ok, ids_rows, 0), axis=1)\n    return np.where(ok, at, -lse[:, None])",
+     "return np.take_along_axis(logq, ids_rows % logq.shape[1], axis=1)"),
+    ("fused_dropped_entry_without_lse", "return np.where(ok, at, -lse[:, None])", "return np.where(ok, at, 0.0)"),
+    ("fused_scatter_clips_ids",
+     "np.add.at(target, (rows[ok], ids_rows.reshape(-1)[ok]), p.reshape(-1)[ok])",
+     "np.add.at(target, (rows, np.clip(ids_rows, 0, q.shape[1] - 1).reshape(-1)), p.reshape(-1))"),
+    ("dense_grid_wraps_negative_ids", "if 0 <= ids[i, k] < V:  # the grid", "if ids[i, k] < V:  # the grid"),
     # forward-chunked KL (logit grid given)
     ("logits_drop_entropy", "row_kl[r0:r1] = e - gamma + lse", "row_kl[r0:r1] = -gamma + lse"),
     ("logits_gamma_sign", "row_kl[r0:r1] = e - gamma + lse", "row_kl[r0:r1] = e + gamma + lse"),
@@ -70,6 +79,6 @@ def test_mutant_is_caught(name, orig, new):
     for pin in _pins.ALL_PINS:
         try:
             pin(mod)
-        except AssertionError:
+        except (AssertionError, IndexError, ValueError):  # a wrong value or an invalid index
             failed.append(pin.__name__)
     assert failed, f"mutant {name} passed every pin"
