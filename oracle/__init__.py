@@ -20,4 +20,7 @@ from .kl import (  # noqa: F401
     logits_sampled_rows,
     kept_positions,
     IGNORE_ID,
+    jsd_forward,
+    jsd_backward,
+    jsd_loss_and_grads,
 )

@@ -82,6 +82,9 @@ __all__ = [
     "logits_sampled_rows",
     "kept_positions",
     "IGNORE_ID",
+    "jsd_forward",
+    "jsd_backward",
+    "jsd_loss_and_grads",
 ]
 
 
@@ -417,3 +420,119 @@ def logits_sampled_rows(Z, ids, logits, T: float, rows: Iterable[int], N_total: 
         out_dz.append(dz[0] / N_total if N_total else 0.0 * dz[0])  # logits_backward divided by N = 1
     return {"rows": np.asarray(rows), "row_lse": np.asarray(out_lse),
             "row_kl": np.asarray(out_kl), "dZ_rows": np.stack(out_dz) if out_dz else np.zeros((0, 0))}
+
+
+# ---------------------------------------------------------------------------
+# An alternative loss on the same inputs: the generalised Jensen-Shannon
+# divergence between the teacher's top-K distribution and the student.
+# ---------------------------------------------------------------------------
+# The pages report ablations on the choice of loss function for the
+# distilled student without naming the losses [P1 "Making knowledge
+# distillation cheap enough to run at scale", section "The resulting student
+# model"]. The loss taken here (a reading) is the generalised Jensen-Shannon
+# divergence with weight beta in (0, 1), with the same teacher and student
+# distributions as the KL above:
+#
+#   P_i  = the teacher's top-K probabilities softmax(l_i / T) placed on the
+#          vocabulary (repeated ids add their mass; ids outside [0, V) have
+#          no vocabulary entry and their mass is left out),
+#   q_i  = softmax(z_i / T) over the full vocabulary,
+#   M_i  = beta P_i + (1 - beta) q_i,
+#   JSD_i = beta KL(P_i || M_i) + (1 - beta) KL(q_i || M_i),
+#
+# beta = 1/2 being the symmetric Jensen-Shannon divergence; for small beta,
+# JSD_i / beta tends to the forward KL above. The loss is the mean over the
+# kept positions, and ignored positions (first id IGNORE_ID) are treated as
+# above. Gradient (derived here): with g_v = (1 - beta) log(q_v / M_v) and
+# gbar = sum_v q_v g_v, d JSD_i / d s_v = q_v (g_v - gbar), hence
+# dZ_i = g / (N T) * q_i * (g_i - gbar_i), dH = dZ W, dW = dZ^T H.
+
+
+def _teacher_grid(ids_rows: np.ndarray, logits_rows, T: float, V: int) -> np.ndarray:
+    """Teacher probabilities on the vocabulary, [rows, V]."""
+    p, _ = teacher_distribution(logits_rows, T)
+    P = np.zeros((ids_rows.shape[0], V))
+    ok = _in_vocab(ids_rows, V)
+    rr, kk = np.nonzero(ok)
+    np.add.at(P, (rr, ids_rows[rr, kk]), p[rr, kk])
+    return P
+
+
+def _jsd_parts(logq: np.ndarray, P: np.ndarray, beta: float):
+    """Per row: (JSD, q, g) with log M formed in the log domain (exact zeros
+    of P stay out of the teacher term)."""
+    with np.errstate(divide="ignore"):
+        logP = np.log(P)
+    logM = np.logaddexp(math.log(beta) + logP, math.log1p(-beta) + logq)
+    q = np.exp(logq)
+    on = P > 0
+    kl_p = np.where(on, P * (np.where(on, logP, 0.0) - logM), 0.0).sum(axis=1)
+    g = (1.0 - beta) * (logq - logM)
+    kl_q = (q * (logq - logM)).sum(axis=1)
+    return beta * kl_p + (1.0 - beta) * kl_q, q, g
+
+
+def _check_beta(beta: float) -> float:
+    beta = float(beta)
+    if not 0.0 < beta < 1.0:
+        raise ValueError("beta must lie in (0, 1)")
+    return beta
+
+
+def jsd_forward(H, W, ids, logits, T: float, beta: float = 0.5, block: int = 256) -> Dict[str, object]:
+    """Loss, per-row logsumexp of z/T and per-row JSD_beta; fp64."""
+    beta = _check_beta(beta)
+    H = _f64(H)
+    W = _f64(W)
+    ids = _ids(ids)
+    lg = _f64(logits)
+    n_rows, V = H.shape[0], W.shape[0]
+    kept = kept_positions(ids)
+    ids = _usable_ids(ids, kept)
+    row_lse = np.empty(n_rows)
+    row_kl = np.empty(n_rows)
+    for r0 in range(0, n_rows, block):
+        r1 = min(n_rows, r0 + block)
+        logq, lse = student_log_softmax(H[r0:r1], W, T)
+        P = _teacher_grid(ids[r0:r1], lg[r0:r1], T, V)
+        row_kl[r0:r1], _, _ = _jsd_parts(logq, P, beta)
+        row_lse[r0:r1] = lse
+    row_kl[~kept] = 0.0
+    N = int(kept.sum())  # the mean runs over the kept positions
+    loss = math.fsum(row_kl.tolist()) / N if N else float("nan")
+    return {"loss": loss, "row_lse": row_lse, "row_kl": row_kl}
+
+
+def jsd_backward(H, W, ids, logits, T: float, beta: float = 0.5, g: float = 1.0,
+                 block: int = 256) -> Tuple[np.ndarray, np.ndarray]:
+    """Gradients (dH [N, d], dW [V, d]) of ``g * loss`` for JSD_beta; fp64."""
+    beta = _check_beta(beta)
+    H = _f64(H)
+    W = _f64(W)
+    ids = _ids(ids)
+    lg = _f64(logits)
+    n_rows, V = H.shape[0], W.shape[0]
+    kept = kept_positions(ids)
+    ids = _usable_ids(ids, kept)
+    N = int(kept.sum())
+    coef = float(g) / (N * float(T)) if N else 0.0
+    dH = np.empty_like(H)
+    dW = np.zeros_like(W)
+    for r0 in range(0, n_rows, block):
+        r1 = min(n_rows, r0 + block)
+        logq, _ = student_log_softmax(H[r0:r1], W, T)
+        P = _teacher_grid(ids[r0:r1], lg[r0:r1], T, V)
+        _, q, gv = _jsd_parts(logq, P, beta)
+        gbar = (q * gv).sum(axis=1)
+        dZ = coef * q * (gv - gbar[:, None])
+        dZ[~kept[r0:r1]] = 0.0
+        dH[r0:r1] = dZ @ W
+        dW += dZ.T @ H[r0:r1]
+    return dH, dW
+
+
+def jsd_loss_and_grads(H, W, ids, logits, T: float, beta: float = 0.5, g: float = 1.0,
+                       block: int = 256) -> Dict[str, object]:
+    out = jsd_forward(H, W, ids, logits, T, beta, block)
+    out["dH"], out["dW"] = jsd_backward(H, W, ids, logits, T, beta, g, block)
+    return out

@@ -554,6 +554,177 @@ def pin_ignored_positions(o):
     assert not o.logits_backward(Z, ids_all, logits, T, g).any()
 
 
+# --- the alternative loss: generalised Jensen-Shannon divergence ---------------
+
+def pin_jsd_scipy_jensenshannon(o):
+    """beta = 1/2: per row, scipy's Jensen-Shannon distance squared between
+    the teacher's top-K distribution on the vocabulary and softmax(Z / T)."""
+    if not hasattr(o, "jsd_forward"):
+        return
+    from scipy.spatial.distance import jensenshannon
+    rng = np.random.default_rng(31)
+    N, d, V, K, T = 6, 5, 19, 5, 1.3
+    H, W, ids, logits = _rand_problem(rng, N, d, V, K)
+    q = sps.softmax(H @ W.T / T, axis=1)
+    ref = []
+    for i in range(N):
+        P = np.zeros(V)
+        P[ids[i]] = sps.softmax(logits[i] / T)
+        ref.append(jensenshannon(P, q[i]) ** 2)
+    out = o.jsd_forward(H, W, ids, logits, T, 0.5)
+    _close(out["row_kl"], ref, 1e-12, what="JSD 1/2 vs scipy jensenshannon")
+    _close(out["loss"], np.mean(ref), 1e-12, what="JSD 1/2 loss")
+    assert np.all(out["row_kl"] >= 0.0) and np.all(out["row_kl"] <= math.log(2.0))
+
+
+def pin_jsd_small_beta_is_forward_kl(o):
+    """JSD_beta / beta tends to the forward KL (pinned above) as beta -> 0,
+    loss and gradients, with an O(beta) remainder."""
+    if not hasattr(o, "jsd_forward"):
+        return
+    rng = np.random.default_rng(32)
+    N, d, V, K, T, g, beta = 5, 4, 17, 4, 1.4, 0.9, 1e-7
+    H, W, ids, logits = _rand_problem(rng, N, d, V, K)
+    f = o.forward(H, W, ids, logits, T)
+    j = o.jsd_forward(H, W, ids, logits, T, beta)
+    _close(j["row_kl"] / beta, f["row_kl"], 1e-5, what="JSD/beta vs KL")
+    _close(j["row_lse"], f["row_lse"], 1e-14, what="JSD lse")
+    dH, dW = o.backward(H, W, ids, logits, T, g)
+    jH, jW = o.jsd_backward(H, W, ids, logits, T, beta, g)
+    _close(jH / beta, dH, 1e-5, what="JSD/beta dH vs KL dH")
+    _close(jW / beta, dW, 1e-5, what="JSD/beta dW vs KL dW")
+
+
+def pin_jsd_torch_autograd(o):
+    """General beta: the loss through torch's kl_div (KL(P || M) and
+    KL(q || M) with M = beta P + (1 - beta) q, P with zeros off the top-K)
+    and its gradients by torch autograd."""
+    if not hasattr(o, "jsd_forward"):
+        return
+    rng = np.random.default_rng(33)
+    N, d, V, K, T, g, beta = 5, 4, 15, 4, 0.8, 1.3, 0.3
+    H, W, ids, logits = _rand_problem(rng, N, d, V, K)
+    P = np.zeros((N, V))
+    for i in range(N):
+        P[i, ids[i]] = sps.softmax(logits[i] / T)
+    Ht = torch.tensor(H, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    Pt = torch.tensor(P)
+    q = torch.softmax(Ht @ Wt.T / T, dim=1)
+    logM = torch.log(beta * Pt + (1 - beta) * q)
+    jsd = (beta * F.kl_div(logM, Pt, reduction="sum") + (1 - beta) * F.kl_div(logM, q, reduction="sum")) / N
+    (g * jsd).backward()
+    out = o.jsd_forward(H, W, ids, logits, T, beta)
+    _close(out["loss"], jsd.item(), 1e-12, what="JSD loss vs kl_div")
+    jH, jW = o.jsd_backward(H, W, ids, logits, T, beta, g)
+    _close(jH, Ht.grad.numpy(), 1e-11, what="JSD dH vs autograd")
+    _close(jW, Wt.grad.numpy(), 1e-11, what="JSD dW vs autograd")
+
+
+def pin_jsd_brute_force_and_finite_differences(o):
+    """Pure-Python loops (math module only) with ids outside [0, V) and a
+    repeated id, written over the teacher's support only (the off-support
+    entries contribute -(1 - beta) log(1 - beta) times the student's mass
+    there); central differences of the loss for every entry of H and W."""
+    if not hasattr(o, "jsd_forward"):
+        return
+    rng = np.random.default_rng(34)
+    N, d, V, K, T, g, beta = 4, 3, 6, 3, 1.6, 0.7, 0.35
+    H = rng.standard_normal((N, d))
+    W = rng.standard_normal((V, d))
+    ids = np.array([[0, 5, 2], [7, 1, -2], [3, 3, 4], [6, -5, 0]])
+    logits = rng.standard_normal((N, K))
+    ref = []
+    for i in range(N):
+        a = [logits[i, k] / T for k in range(K)]
+        ma = max(a)
+        za = sum(math.exp(x - ma) for x in a)
+        p = [math.exp(x - ma) / za for x in a]
+        s = [sum(H[i, j] * W[v, j] for j in range(d)) / T for v in range(V)]
+        ms = max(s)
+        lse = ms + math.log(sum(math.exp(x - ms) for x in s))
+        support = sorted({int(v) for v in ids[i] if 0 <= v < V})
+        val, qs = 0.0, 0.0
+        for v in support:
+            Pv = sum(p[k] for k in range(K) if ids[i, k] == v)
+            qv = math.exp(s[v] - lse)
+            Mv = beta * Pv + (1 - beta) * qv
+            val += beta * Pv * math.log(Pv / Mv) + (1 - beta) * qv * math.log(qv / Mv)
+            qs += qv
+        val += -(1 - beta) * math.log(1 - beta) * (1 - qs)
+        ref.append(val)
+    out = o.jsd_forward(H, W, ids, logits, T, beta)
+    _close(out["row_kl"], ref, 1e-13, what="JSD brute force")
+    dH, dW = o.jsd_backward(H, W, ids, logits, T, beta, g)
+    h = 1e-6
+
+    def L(Hx, Wx):
+        return g * o.jsd_forward(Hx, Wx, ids, logits, T, beta)["loss"]
+
+    for X, dX, name in ((H, dH, "dH"), (W, dW, "dW")):
+        fd = np.zeros_like(X)
+        for idx in np.ndindex(X.shape):
+            Xp = X.copy(); Xp[idx] += h
+            Xm = X.copy(); Xm[idx] -= h
+            fd[idx] = (L(Xp, W) - L(Xm, W)) / (2 * h) if X is H else (L(H, Xp) - L(H, Xm)) / (2 * h)
+        _close(dX, fd, 1e-6, what=f"JSD finite differences {name}")
+
+
+def pin_jsd_invariants(o):
+    if not hasattr(o, "jsd_forward"):
+        return
+    rng = np.random.default_rng(35)
+    N, d, V, K, T, g, beta = 8, 5, 21, 5, 1.5, 1.1, 0.4
+    H, W, ids, logits = _rand_problem(rng, N, d, V, K)
+    base = o.jsd_forward(H, W, ids, logits, T, beta)
+    dH, dW = o.jsd_backward(H, W, ids, logits, T, beta, g)
+    assert np.all(base["row_kl"] >= 0.0)
+    # teacher equal to the student over the whole vocabulary: zero loss, zero gradients
+    ide = np.stack([rng.permutation(V) for _ in range(N)])
+    eq = np.take_along_axis(H @ W.T, ide, axis=1)
+    e = o.jsd_forward(H, W, ide, eq, T, beta)
+    assert np.max(np.abs(e["row_kl"])) < 1e-13
+    eH, eW = o.jsd_backward(H, W, ide, eq, T, beta, g)
+    assert np.max(np.abs(eH)) < 1e-13 and np.max(np.abs(eW)) < 1e-13
+    # K-pair permutation, block size, linearity in g, W row shift
+    perm = rng.permutation(K)
+    _close(o.jsd_forward(H, W, ids[:, perm], logits[:, perm], T, beta)["row_kl"], base["row_kl"], 1e-13,
+           what="JSD K-permutation")
+    for blk in (1, 3):
+        _close(o.jsd_forward(H, W, ids, logits, T, beta, block=blk)["loss"], base["loss"], 1e-13,
+               what=f"JSD block {blk}")
+        bH, bW = o.jsd_backward(H, W, ids, logits, T, beta, g, block=blk)
+        _close(bH, dH, 1e-13, what=f"JSD block {blk} dH")
+        _close(bW, dW, 1e-12, what=f"JSD block {blk} dW")
+    lH, lW = o.jsd_backward(H, W, ids, logits, T, beta, 2.5 * g)
+    _close(lH, 2.5 * dH, 1e-13, what="JSD linear in g")
+    c = rng.standard_normal(d)
+    _close(o.jsd_forward(H, W + c, ids, logits, T, beta)["row_kl"], base["row_kl"], 1e-11, what="JSD W shift")
+    # every dZ row sums to zero: the columns of dW sum to zero
+    _close(dW.sum(axis=0), np.zeros(d), 0.0, atol=1e-14 * max(1.0, np.abs(dW).max() * V),
+           what="JSD column sums of dW")
+    # temperature identity
+    t1 = o.jsd_forward(H / T, W, ids, logits / T, 1.0, beta)
+    _close(t1["loss"], base["loss"], 1e-13, what="JSD temperature identity")
+    tH, tW = o.jsd_backward(H / T, W, ids, logits / T, 1.0, beta, g)
+    _close(tH / T, dH, 1e-12, what="JSD temperature identity dH")
+    _close(tW, dW, 1e-12, what="JSD temperature identity dW")
+    # ignoring a position is deleting it
+    ign = np.array([2, 5])
+    keep = np.setdiff1d(np.arange(N), ign)
+    ids_m = ids.copy()
+    ids_m[ign, 0] = -1
+    m = o.jsd_forward(H, W, ids_m, logits, T, beta)
+    _close(m["loss"], o.jsd_forward(H[keep], W, ids[keep], logits[keep], T, beta)["loss"], 1e-13,
+           what="JSD ignored: loss")
+    assert np.all(m["row_kl"][ign] == 0.0)
+    mH, mW = o.jsd_backward(H, W, ids_m, logits, T, beta, g)
+    rH, rW = o.jsd_backward(H[keep], W, ids[keep], logits[keep], T, beta, g)
+    assert np.all(mH[ign] == 0.0)
+    _close(mH[keep], rH, 1e-13, what="JSD ignored: dH")
+    _close(mW, rW, 1e-13, what="JSD ignored: dW")
+
+
 ALL_PINS = [
     pin_two_token_softplus,
     pin_uniform_student,
@@ -571,4 +742,9 @@ ALL_PINS = [
     pin_logits_closed_forms_and_invariants,
     pin_logits_matches_fused,
     pin_ignored_positions,
+    pin_jsd_scipy_jensenshannon,
+    pin_jsd_small_beta_is_forward_kl,
+    pin_jsd_torch_autograd,
+    pin_jsd_brute_force_and_finite_differences,
+    pin_jsd_invariants,
 ]

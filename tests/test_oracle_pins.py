@@ -54,6 +54,15 @@ MUTANTS = [
     ("logits_grad_no_T", "scale = float(g) / (N * float(T))", "scale = float(g) / N"),
     ("logits_grad_no_teacher", "dZ[r0:r1] = scale * (q - P)", "dZ[r0:r1] = scale * q"),
     ("logits_scatter_first_id_only", "rr, kk = np.nonzero(ok)", "rr, kk = np.nonzero(ok[:, :1])"),
+    # the alternative loss (generalised Jensen-Shannon divergence)
+    ("jsd_beta_swapped", "return beta * kl_p + (1.0 - beta) * kl_q", "return (1.0 - beta) * kl_p + beta * kl_q"),
+    ("jsd_mixture_ignores_beta", "logM = np.logaddexp(math.log(beta) + logP, math.log1p(-beta) + logq)",
+     "logM = np.logaddexp(math.log(0.5) + logP, math.log(0.5) + logq)"),
+    ("jsd_gradient_without_mean", "dZ = coef * q * (gv - gbar[:, None])", "dZ = coef * q * gv"),
+    ("jsd_gradient_without_weight", "g = (1.0 - beta) * (logq - logM)", "g = (logq - logM)"),
+    ("jsd_grid_wraps_negative_ids", "    ok = _in_vocab(ids_rows, V)\n    rr, kk", "    ok = ids_rows < V\n    rr, kk"),
+    ("jsd_teacher_term_sign", "kl_p = np.where(on, P * (np.where(on, logP, 0.0) - logM), 0.0)",
+     "kl_p = np.where(on, P * (logM - np.where(on, logP, 0.0)), 0.0)"),
     # ignored positions
     ("ignored_counted_in_mean", "N = int(kept.sum())  # the mean runs over the kept positions",
      "N = kept.size  # the mean runs over the kept positions"),
