@@ -4,8 +4,10 @@
 One step = kdkl_forward + kdkl_backward over one batch of synthetic inputs
 already resident in HBM (every kernel of the path). Prints ONE JSON line.
 
-Default workload: the gpt-oss-20b-like head at 32K tokens
-(N=32768, d=2880, V=201088, K=100, chunk=2048, bf16, T=1).
+Default workload: the long-context case, the gpt-oss-20b-like head at 256K
+tokens (N=262144, d=2880, V=201088, K=100, chunk=4096, bf16, T=2), the
+largest single-GPU configuration; --config gptoss20b_32k times the same head
+at 32K tokens (chunk 2048, T=1).
 
 --path logits measures the forward-chunked variant instead: one step =
 kdkl_logits_forward + kdkl_logits_backward on the logit grid Z = H W^T of the
@@ -307,7 +309,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="gptoss20b_32k")
+    ap.add_argument("--config", default="longctx_256k")
     ap.add_argument("--N", type=int, default=None, help="override the number of positions")
     ap.add_argument("--chunk", type=int, default=None, help="override the chunk size")
     ap.add_argument("--cpu-rows", type=int, default=2048)
@@ -322,6 +324,12 @@ def main():
     ap.add_argument("--gen-reading", choices=("1based", "0based"), default="1based",
                     help="reading of the workload list's cross-references for the teacher "
                          "generator of the 8K and 256K workloads (1based: uniform ids, N(0, 2))")
+    ap.add_argument("--chunks-per-group", type=int, default=0,
+                    help="kdkl_options.chunks_per_group (0: the library's choice)")
+    ap.add_argument("--vocab-slices", type=int, default=0,
+                    help="kdkl_options.vocab_slices (0: as many as chunks per group)")
+    ap.add_argument("--dh-w-in-place", type=int, default=0, choices=(0, 1, 2),
+                    help="kdkl_options.dh_w_in_place (0: the library's choice, 1: in place, 2: W^T copy)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -363,7 +371,11 @@ def main():
     torch.zeros(1, device=dev)  # initialise the device before reading memory stats
     torch.cuda.reset_peak_memory_stats(dev)
     H, W, ids, lg = (x[k].to(dev) for k in ("H", "W", "ids", "logits"))
-    fb, bb = kd.workspace_size(w.N, w.d, w.V, w.K, w.chunk, H.dtype)
+    opts = {"chunks_per_group": args.chunks_per_group, "vocab_slices": args.vocab_slices,
+            "dh_w_in_place": args.dh_w_in_place}
+    plan = kd.plan_info(w.N, w.d, w.V, w.K, w.chunk, H.dtype, opts)
+    log(f"bench: plan {plan}")
+    fb, bb = kd.workspace_size(w.N, w.d, w.V, w.K, w.chunk, H.dtype, opts)
     ws_f = torch.empty(fb, dtype=torch.uint8, device=dev)
     ws_b = torch.empty(bb, dtype=torch.uint8, device=dev)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
@@ -374,9 +386,9 @@ def main():
 
     def step():
         kd.kdkl_forward(H, W, ids, lg, w.T, w.chunk, loss=loss, row_lse=row_lse,
-                        workspace=ws_f, stream=stream, want_row_kl=False)
+                        workspace=ws_f, stream=stream, want_row_kl=False, options=opts)
         kd.kdkl_backward(H, W, ids, lg, w.T, w.chunk, row_lse, None, dH=dH, dW=dW,
-                         workspace=ws_b, stream=stream)
+                         workspace=ws_b, stream=stream, options=opts)
 
     for _ in range(args.warmup):
         step()
@@ -431,6 +443,7 @@ def main():
                    "T": w.T, "teacher_ids": w.id_dist, "teacher_logit_var": w.logit_var,
                    "gen_reading": args.gen_reading,
                    "seed": args.seed if args.seed is not None else wl.seed_for(w),
+                   "plan": plan,
                    "parallelism": "single GPU"},
         "mfma_util_pct": round(mfma_pct, 2),
         # the same time against the 6 N V d flop of forward + dH + dW alone

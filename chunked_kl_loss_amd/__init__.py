@@ -17,7 +17,7 @@ from typing import Optional, Tuple
 
 import torch
 
-from ._lib import KDKL_BF16, KDKL_F32, KdklError, KernelStat, check, load as _load
+from ._lib import KDKL_BF16, KDKL_F32, KdklError, KernelStat, Options, Plan, check, load as _load
 
 __all__ = [
     "workspace_size",
@@ -76,23 +76,41 @@ def _want(t, shape, dtype, device, name):
                          f"got {t.dtype} {tuple(t.shape)} on {t.device}")
 
 
-def workspace_size(N: int, d: int, V: int, K: int, chunk: int, dtype: torch.dtype) -> Tuple[int, int]:
+OPTION_FIELDS = ("loss", "chunks_per_group", "vocab_slices", "dh_w_in_place", "beta")
+
+
+def _options(options):
+    """kdkl_options from None (defaults) or a dict with any of OPTION_FIELDS."""
+    if options is None:
+        return None
+    unknown = set(options) - set(OPTION_FIELDS)
+    if unknown:
+        raise ValueError(f"unknown options {sorted(unknown)}; known: {OPTION_FIELDS}")
+    o = Options()
+    for k, v in options.items():
+        setattr(o, k, float(v) if k == "beta" else int(v))
+    return C.byref(o)
+
+
+def workspace_size(N: int, d: int, V: int, K: int, chunk: int, dtype: torch.dtype,
+                   options=None) -> Tuple[int, int]:
     """(forward bytes, backward bytes) of device workspace."""
     f = C.c_size_t()
     b = C.c_size_t()
     code = KDKL_BF16 if dtype == torch.bfloat16 else KDKL_F32
-    check(_load().kdkl_workspace_size(N, d, V, K, chunk, code, C.byref(f), C.byref(b)),
+    check(_load().kdkl_workspace_size(N, d, V, K, chunk, code, _options(options), C.byref(f),
+                                      C.byref(b)),
           "kdkl_workspace_size")
     return f.value, b.value
 
 
-def plan_info(N: int, d: int, V: int, K: int, chunk: int, dtype: torch.dtype) -> Tuple[int, int, int]:
-    """(chunks per group, vocabulary slices per group, dH splits) the calls use."""
-    g, v, s = C.c_int(), C.c_int(), C.c_int()
+def plan_info(N: int, d: int, V: int, K: int, chunk: int, dtype: torch.dtype, options=None) -> dict:
+    """The blocking the calls use (``kdkl_plan``) as a dict."""
+    p = Plan()
     code = KDKL_BF16 if dtype == torch.bfloat16 else KDKL_F32
-    check(_load().kdkl_plan_info(N, d, V, K, chunk, code, C.byref(g), C.byref(v), C.byref(s)),
+    check(_load().kdkl_plan_info(N, d, V, K, chunk, code, _options(options), C.byref(p)),
           "kdkl_plan_info")
-    return g.value, v.value, s.value
+    return {name: getattr(p, name) for name, _ in Plan._fields_ if name != "reserved"}
 
 
 def _check_shapes(H, W, ids, logits):
@@ -106,7 +124,7 @@ def _check_shapes(H, W, ids, logits):
 
 
 def kdkl_forward(H, W, ids, logits, T: float, chunk: int, *, loss=None, row_lse=None,
-                 row_kl=None, workspace=None, stream=None, want_row_kl: bool = True):
+                 row_kl=None, workspace=None, stream=None, want_row_kl: bool = True, options=None):
     """Run ``kdkl_forward``; returns (loss [1] fp32, row_lse [N], row_kl [N] or None)."""
     _need_gpu(H, W, ids, logits)
     N, d, V, K = _check_shapes(H, W, ids, logits)
@@ -121,12 +139,13 @@ def kdkl_forward(H, W, ids, logits, T: float, chunk: int, *, loss=None, row_lse=
     _want(row_lse, (N,), torch.float32, dev, "row_lse")
     if row_kl is not None:
         _want(row_kl, (N,), torch.float32, dev, "row_kl")
-    fb, _ = workspace_size(N, d, V, K, chunk, H.dtype)
+    fb, _ = workspace_size(N, d, V, K, chunk, H.dtype, options)
     if workspace is None:
         workspace = torch.empty(fb, dtype=torch.uint8, device=dev)
     _need_gpu(workspace)
     check(_load().kdkl_forward(_ptr(H), _ptr(W), _ptr(ids), _ptr(logits), N, d, V, K,
-                              float(T), chunk, _dtype_code(H), _ptr(loss), _ptr(row_lse),
+                              float(T), chunk, _dtype_code(H), _options(options), _ptr(loss),
+                              _ptr(row_lse),
                               _ptr(row_kl), _ptr(workspace), _nbytes(workspace),
                               _stream(dev, stream)),
           "kdkl_forward")
@@ -134,7 +153,8 @@ def kdkl_forward(H, W, ids, logits, T: float, chunk: int, *, loss=None, row_lse=
 
 
 def kdkl_backward(H, W, ids, logits, T: float, chunk: int, row_lse, grad_loss=None, *,
-                  dH=None, dW=None, accumulate_dW: bool = False, workspace=None, stream=None):
+                  dH=None, dW=None, accumulate_dW: bool = False, workspace=None, stream=None,
+                  options=None):
     """Run ``kdkl_backward``; returns (dH [N,d] in H's dtype, dW [V,d] fp32)."""
     _need_gpu(H, W, ids, logits, row_lse, grad_loss)
     N, d, V, K = _check_shapes(H, W, ids, logits)
@@ -150,12 +170,12 @@ def kdkl_backward(H, W, ids, logits, T: float, chunk: int, row_lse, grad_loss=No
     _want(dW, (V, d), torch.float32, dev, "dW")
     if grad_loss is not None:
         _want(grad_loss, (1,), torch.float32, dev, "grad_loss")
-    _, bb = workspace_size(N, d, V, K, chunk, H.dtype)
+    _, bb = workspace_size(N, d, V, K, chunk, H.dtype, options)
     if workspace is None:
         workspace = torch.empty(bb, dtype=torch.uint8, device=dev)
     _need_gpu(workspace)
     check(_load().kdkl_backward(_ptr(H), _ptr(W), _ptr(ids), _ptr(logits), N, d, V, K,
-                               float(T), chunk, _dtype_code(H), _ptr(row_lse),
+                               float(T), chunk, _dtype_code(H), _options(options), _ptr(row_lse),
                                _ptr(grad_loss), _ptr(dH), _ptr(dW), int(bool(accumulate_dW)),
                                _ptr(workspace), _nbytes(workspace), _stream(dev, stream)),
           "kdkl_backward")
@@ -167,24 +187,26 @@ class FusedKLLoss(torch.autograd.Function):
     recomputes each chunk's logits inside the library."""
 
     @staticmethod
-    def forward(ctx, H, W, ids, logits, T: float, chunk: int):
-        loss, row_lse, _ = kdkl_forward(H, W, ids, logits, T, chunk, want_row_kl=False)
+    def forward(ctx, H, W, ids, logits, T: float, chunk: int, options=None):
+        loss, row_lse, _ = kdkl_forward(H, W, ids, logits, T, chunk, want_row_kl=False,
+                                        options=options)
         ctx.save_for_backward(H, W, ids, logits, row_lse)
         ctx.T = T
         ctx.chunk = chunk
+        ctx.options = options
         return loss[0]
 
     @staticmethod
     def backward(ctx, g):
         H, W, ids, logits, row_lse = ctx.saved_tensors
         g = g.reshape(1).to(torch.float32).contiguous()
-        dH, dW = kdkl_backward(H, W, ids, logits, ctx.T, ctx.chunk, row_lse, g)
-        return dH, dW.to(W.dtype), None, None, None, None
+        dH, dW = kdkl_backward(H, W, ids, logits, ctx.T, ctx.chunk, row_lse, g, options=ctx.options)
+        return dH, dW.to(W.dtype), None, None, None, None, None
 
 
-def fused_kl_loss(H, W, ids, logits, T: float = 1.0, chunk: int = 2048):
+def fused_kl_loss(H, W, ids, logits, T: float = 1.0, chunk: int = 2048, options=None):
     """Mean over positions of KL(teacher top-K || student), differentiable in H and W."""
-    return FusedKLLoss.apply(H, W, ids, logits, T, chunk)
+    return FusedKLLoss.apply(H, W, ids, logits, T, chunk, options)
 
 
 def _check_logits_shapes(Z, ids, logits):

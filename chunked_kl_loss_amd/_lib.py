@@ -15,8 +15,10 @@ KDKL_BF16 = 1
 STATUS = {
     0: "KDKL_OK", 1: "KDKL_ERR_NULL", 2: "KDKL_ERR_SHAPE", 3: "KDKL_ERR_VALUE",
     4: "KDKL_ERR_DTYPE", 5: "KDKL_ERR_WORKSPACE", 6: "KDKL_ERR_OVERFLOW",
-    7: "KDKL_ERR_HIP", 8: "KDKL_ERR_ALIGN",
+    7: "KDKL_ERR_HIP", 8: "KDKL_ERR_ALIGN", 9: "KDKL_ERR_OPTION",
 }
+ABI_VERSION = 2
+KDKL_LOSS_KL = 0
 
 
 class KdklError(RuntimeError):
@@ -35,6 +37,34 @@ class KernelStat(C.Structure):
     ]
 
 
+class Options(C.Structure):
+    """kdkl_options: per-call options of the fused calls (zero = defaults)."""
+    _fields_ = [
+        ("loss", C.c_int32),
+        ("chunks_per_group", C.c_int32),
+        ("vocab_slices", C.c_int32),
+        ("dh_w_in_place", C.c_int32),
+        ("beta", C.c_float),
+        ("reserved", C.c_int32 * 3),
+    ]
+
+
+class Plan(C.Structure):
+    """kdkl_plan: the blocking the fused calls use."""
+    _fields_ = [
+        ("chunks_per_group", C.c_int32),
+        ("vocab_slices", C.c_int32),
+        ("dh_splits", C.c_int32),
+        ("dh_w_in_place", C.c_int32),
+        ("vocab_tile", C.c_int32),
+        ("hidden_tile", C.c_int32),
+        ("bf16_main_loop", C.c_int32),
+        ("reserved", C.c_int32),
+        ("fwd_bytes", C.c_uint64),
+        ("bwd_bytes", C.c_uint64),
+    ]
+
+
 _LIB = None
 _P = C.c_void_p
 _I64 = C.c_int64
@@ -43,14 +73,15 @@ _I32 = C.c_int32
 SIGNATURES = {
     "kdkl_abi_version": (C.c_int, []),
     "kdkl_status_string": (C.c_char_p, [C.c_int]),
-    "kdkl_workspace_size": (C.c_int, [_I64, _I64, _I64, _I32, _I64, C.c_int,
+    "kdkl_workspace_size": (C.c_int, [_I64, _I64, _I64, _I32, _I64, C.c_int, C.POINTER(Options),
                                       C.POINTER(C.c_size_t), C.POINTER(C.c_size_t)]),
-    "kdkl_plan_info": (C.c_int, [_I64, _I64, _I64, _I32, _I64, C.c_int, C.POINTER(C.c_int),
-                                 C.POINTER(C.c_int), C.POINTER(C.c_int)]),
+    "kdkl_plan_info": (C.c_int, [_I64, _I64, _I64, _I32, _I64, C.c_int, C.POINTER(Options),
+                                 C.POINTER(Plan)]),
     "kdkl_forward": (C.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, C.c_float, _I64,
-                               C.c_int, _P, _P, _P, _P, C.c_size_t, _P]),
+                               C.c_int, C.POINTER(Options), _P, _P, _P, _P, C.c_size_t, _P]),
     "kdkl_backward": (C.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, C.c_float, _I64,
-                                C.c_int, _P, _P, _P, _P, C.c_int, _P, C.c_size_t, _P]),
+                                C.c_int, C.POINTER(Options), _P, _P, _P, _P, C.c_int, _P,
+                                C.c_size_t, _P]),
     "kdkl_logits_forward": (C.c_int, [_P, _P, _P, _I64, _I64, _I32, C.c_float, C.c_int,
                                       _P, _P, _P, _P]),
     "kdkl_logits_backward": (C.c_int, [_P, _P, _P, _I64, _I64, _I32, C.c_float, C.c_int,
@@ -80,7 +111,7 @@ def load():
             fn = getattr(lib, name)
             fn.restype = res
             fn.argtypes = args
-        if lib.kdkl_abi_version() != 1:
+        if lib.kdkl_abi_version() != ABI_VERSION:
             raise ImportError("libkdkl.so ABI version mismatch")
         _LIB = lib
     return _LIB

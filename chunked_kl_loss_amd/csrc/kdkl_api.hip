@@ -5,10 +5,10 @@
 // scale", section "Two system changes", fused chunked KL bullet].
 #include <hip/hip_runtime.h>
 #include <math.h>
-#include <stdlib.h>
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -33,9 +33,12 @@ struct Rec {
   hipEvent_t a, b;
   double flops, bytes;
 };
+// The library's only process-wide mutable state: the timing table. `on` is
+// read without the lock on every launch (atomically) and re-read under the
+// lock before anything is recorded.
 struct Prof {
   std::mutex mu;
-  bool on = false;
+  std::atomic<bool> on{false};
   std::vector<Rec> recs;
   std::vector<hipEvent_t> pool;
 } g_prof;
@@ -54,8 +57,9 @@ hipEvent_t prof_event() {
 // Runs `launch` bracketed by events when profiling is on.
 template <class F>
 hipError_t timed(int kid, double flops, double bytes, hipStream_t s, F&& launch) {
-  if (!g_prof.on) return launch();
+  if (!g_prof.on.load(std::memory_order_acquire)) return launch();
   std::lock_guard<std::mutex> lk(g_prof.mu);
+  if (!g_prof.on.load(std::memory_order_relaxed)) return launch();
   hipEvent_t a = prof_event(), b = prof_event();
   auto give_back = [&] {  // events not recorded go back to the pool
     if (a) g_prof.pool.push_back(a);
@@ -114,21 +118,19 @@ struct Plan {
 // per backward call or W in place through the LDS transpose read (V * d * 2
 // fewer bytes of workspace, no transpose, but each dH launch measured about
 // 2% slower on 256-wide hidden-size tiles and 4% on 320-wide ones). The plan
-// reads W in place when the modelled extra time of one call's dH launches
-// (at about 1.2 PFLOP/s) is below that of the transpose (W read and written
-// at about 5 TB/s): Llama-like heads at 8K positions, not gpt-oss-like ones
-// at 32K or more. KDKL_DH_W_INPLACE=1 or 0 in the environment forces either
-// (read when the plan is made, so the workspace size and the call must see
-// the same value).
+// keeps the copy only when the modelled extra time of one call's dH launches
+// read in place (at about 1.2 PFLOP/s) exceeds the transpose (W read and
+// written at about 5 TB/s) by at least 0.3 ms: Llama-like heads at 8K
+// positions and gpt-oss-like heads up to 16K read W in place, gpt-oss-like
+// heads beyond keep the copy (a 1.2 GB step of the workspace at that N, paid
+// only where the copy saves time).
 static bool dh_reads_w_in_place(const Plan& P, int64_t N) {
-  const char* e = getenv("KDKL_DH_W_INPLACE");
-  if (e != nullptr && (e[0] == '0' || e[0] == '1') && e[1] == 0) return e[0] == '1';
   const int64_t group = P.bg * P.chunk;
   const double launches = (double)((N + group - 1) / group) * (double)P.n_parts;
   const double dh_ms = 2.0 * (double)P.Cg * (double)P.vpart * (double)P.d / 1.2e12;
   const double penalty = P.dtile == 256 ? 0.02 : 0.04;
   const double transpose_ms = 4.0 * (double)P.V * (double)P.d / 5.0e9;
-  return launches * dh_ms * penalty < transpose_ms;
+  return launches * dh_ms * penalty < transpose_ms + 0.3;
 }
 #ifndef KDKL_DH_BUSY
 #define KDKL_DH_BUSY 0.96
@@ -174,8 +176,23 @@ static bool region(size_t* cursor, int64_t bytes, size_t* off) {
   return true;
 }
 
+// Largest accepted kdkl_options.vocab_slices and chunks_per_group.
+constexpr int kMaxVocabSlices = 1024;
+constexpr int kMaxChunksPerGroup = 64;
+
+static kdkl_status check_options(const kdkl_options* o) {
+  if (o == nullptr) return KDKL_OK;
+  if (o->loss != KDKL_LOSS_KL) return KDKL_ERR_OPTION;
+  if (o->chunks_per_group < 0 || o->chunks_per_group > kMaxChunksPerGroup) return KDKL_ERR_OPTION;
+  if (o->vocab_slices < 0 || o->vocab_slices > kMaxVocabSlices) return KDKL_ERR_OPTION;
+  if (o->dh_w_in_place < 0 || o->dh_w_in_place > 2) return KDKL_ERR_OPTION;
+  for (int i = 0; i < 3; ++i)
+    if (o->reserved[i] != 0) return KDKL_ERR_OPTION;
+  return KDKL_OK;
+}
+
 static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int dtype,
-                             Plan* P) {
+                             const kdkl_options* opts, Plan* P) {
   if (dtype != KDKL_F32 && dtype != KDKL_BF16) return KDKL_ERR_DTYPE;
   const int64_t dmul = dtype == KDKL_BF16 ? 8 : 4;
   if (N < 0 || d <= 0 || V <= 0 || K <= 0 || chunk <= 0) return KDKL_ERR_SHAPE;
@@ -196,19 +213,33 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   P->dtile = gemm_d_tile(P->fast, d);
   P->n_vt = P->Vp / P->vt;
   if (P->Cp > INT32_MAX / 4) return KDKL_ERR_OVERFLOW;
-  P->bg = backward_group(*P, N);
+  kdkl_status ost = check_options(opts);
+  if (ost != KDKL_OK) return ost;
+  const kdkl_options o = opts ? *opts : kdkl_options{};
+  if (o.chunks_per_group > 0) {
+    // more than one chunk per launch needs the bf16 main loop, whose 32-bit
+    // load offsets must still cover the group's operands
+    P->bg = o.chunks_per_group;
+    if (P->bg > 1 && (!P->fast || !gemm_fast_path(dtype, d, P->Vp, round_up(P->bg * P->chunk, kTokenTile))))
+      return KDKL_ERR_OPTION;
+  } else {
+    P->bg = backward_group(*P, N);
+  }
   P->Cg = round_up(P->bg * P->chunk, kTokenTile);
-  if (P->bg == 1) {
-    P->Cg = P->Cp;
+  if (P->Cg > INT32_MAX / 4) return KDKL_ERR_OVERFLOW;
+  // vocabulary slices of a group: as many as chunks per group unless set
+  const int64_t slices = o.vocab_slices > 0 ? o.vocab_slices : P->bg;
+  if (slices <= 1) {
     P->vpart = P->Vp;
   } else {
     // slices start on a tile boundary of both the dZ product (vt rows) and
     // the dW product (256 rows)
     const int64_t align = P->vt % 256 == 0 ? P->vt : P->vt * 2;
-    P->vpart = round_up((V + P->bg - 1) / P->bg, align);
+    P->vpart = round_up((V + slices - 1) / slices, align);
   }
   P->n_parts = (int)((V + P->vpart - 1) / P->vpart);
-  P->wt = !P->fast || !dh_reads_w_in_place(*P, N);
+  if (o.dh_w_in_place == 1 && !P->fast) return KDKL_ERR_OPTION;
+  P->wt = !P->fast || (o.dh_w_in_place == 2) || (o.dh_w_in_place == 0 && !dh_reads_w_in_place(*P, N));
   // dH split-K: the fewest splits S whose launch keeps the 256 compute units
   // within 4% as busy as the best S does, when every workgroup does 1/S of a
   // tile's work and the units take them in rounds (fewer splits, fewer fp32
@@ -340,14 +371,15 @@ const char* kdkl_status_string(int s) {
     case KDKL_ERR_OVERFLOW: return "KDKL_ERR_OVERFLOW: size overflow";
     case KDKL_ERR_HIP: return "KDKL_ERR_HIP: HIP launch or runtime failure";
     case KDKL_ERR_ALIGN: return "KDKL_ERR_ALIGN: pointer not 16-byte aligned";
+    case KDKL_ERR_OPTION: return "KDKL_ERR_OPTION: an option is out of range or not available for these sizes";
     default: return "KDKL_ERR_UNKNOWN";
   }
 }
 
 kdkl_status kdkl_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int dtype,
-                                size_t* fwd_bytes, size_t* bwd_bytes) {
+                                const kdkl_options* opts, size_t* fwd_bytes, size_t* bwd_bytes) {
   Plan P;
-  kdkl_status st = make_plan(N, d, V, K, chunk, dtype, &P);
+  kdkl_status st = make_plan(N, d, V, K, chunk, dtype, opts, &P);
   if (st != KDKL_OK) return st;
   if (fwd_bytes) *fwd_bytes = P.f_bytes;
   if (bwd_bytes) *bwd_bytes = P.b_bytes;
@@ -355,22 +387,30 @@ kdkl_status kdkl_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K, int6
 }
 
 kdkl_status kdkl_plan_info(int64_t N, int64_t d, int64_t V, int32_t K, int64_t chunk, int dtype,
-                           int* chunks_per_group, int* vocab_slices, int* dh_splits) {
+                           const kdkl_options* opts, kdkl_plan* out) {
+  if (!out) return KDKL_ERR_NULL;
   Plan P;
-  kdkl_status st = make_plan(N, d, V, K, chunk, dtype, &P);
+  kdkl_status st = make_plan(N, d, V, K, chunk, dtype, opts, &P);
   if (st != KDKL_OK) return st;
-  if (chunks_per_group) *chunks_per_group = P.bg;
-  if (vocab_slices) *vocab_slices = P.n_parts;
-  if (dh_splits) *dh_splits = P.dh_splits;
+  memset(out, 0, sizeof(*out));
+  out->chunks_per_group = P.bg;
+  out->vocab_slices = P.n_parts;
+  out->dh_splits = P.dh_splits;
+  out->dh_w_in_place = P.wt ? 0 : 1;
+  out->vocab_tile = P.vt;
+  out->hidden_tile = P.dtile;
+  out->bf16_main_loop = P.fast ? 1 : 0;
+  out->fwd_bytes = P.f_bytes;
+  out->bwd_bytes = P.b_bytes;
   return KDKL_OK;
 }
 
 kdkl_status kdkl_forward(const void* H, const void* W, const int32_t* ids, const float* lg, int64_t N,
-                         int64_t d, int64_t V, int32_t K, float T, int64_t chunk, int dtype, float* loss,
-                         float* row_lse, float* row_kl, void* workspace, size_t workspace_bytes,
-                         void* stream) {
+                         int64_t d, int64_t V, int32_t K, float T, int64_t chunk, int dtype,
+                         const kdkl_options* opts, float* loss, float* row_lse, float* row_kl, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   Plan P;
-  kdkl_status st = make_plan(N, d, V, K, chunk, dtype, &P);
+  kdkl_status st = make_plan(N, d, V, K, chunk, dtype, opts, &P);
   if (st != KDKL_OK) return st;
   if ((st = check_common(H, W, ids, lg, N, T)) != KDKL_OK) return st;
   if (!loss || (N > 0 && !row_lse) || !workspace) return KDKL_ERR_NULL;
@@ -477,10 +517,11 @@ static hipError_t part_products(const Plan& P, int dtype, const void* W, char* w
 
 kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, const float* lg, int64_t N,
                           int64_t d, int64_t V, int32_t K, float T, int64_t chunk, int dtype,
-                          const float* row_lse, const float* grad_loss, void* dH, float* dW,
-                          int accumulate_dW, void* workspace, size_t workspace_bytes, void* stream) {
+                          const kdkl_options* opts, const float* row_lse, const float* grad_loss, void* dH,
+                          float* dW, int accumulate_dW, void* workspace, size_t workspace_bytes,
+                          void* stream) {
   Plan P;
-  kdkl_status st = make_plan(N, d, V, K, chunk, dtype, &P);
+  kdkl_status st = make_plan(N, d, V, K, chunk, dtype, opts, &P);
   if (st != KDKL_OK) return st;
   if ((st = check_common(H, W, ids, lg, N, T)) != KDKL_OK) return st;
   if (!dW || !workspace || (N > 0 && (!row_lse || !dH))) return KDKL_ERR_NULL;
@@ -623,7 +664,7 @@ struct DensePlan {
 };
 
 static kdkl_status make_dense_plan(int64_t N, int64_t d, int64_t V, int32_t K, int dtype, DensePlan* D) {
-  kdkl_status st = make_plan(N, d, V, K, N > 0 ? N : 1, dtype, &D->P);
+  kdkl_status st = make_plan(N, d, V, K, N > 0 ? N : 1, dtype, nullptr, &D->P);
   if (st != KDKL_OK) return st;
   const Plan& P = D->P;
   int64_t z, g;

@@ -43,9 +43,13 @@
  *     Buffers must stay alive until the stream has passed the call.
  *   - Arguments are checked before any HIP call; a failed check returns a
  *     status and touches nothing. A failed launch returns KDKL_ERR_HIP.
- *   - Preconditions not checked: ids of a row distinct (duplicates add their
- *     mass) and in [0, V). An id outside [0, V) never faults; its teacher mass
- *     is dropped from the loss and gradient.
+ *   - Preconditions not checked: ids of a row distinct and in [0, V). A
+ *     repeated id is gathered once per entry (KL_i above, entry by entry) and
+ *     the gradient adds its masses. An id outside [0, V) never faults: it
+ *     keeps its share of the teacher's softmax over K (so of sum p log p),
+ *     but the student has no entry for it: its gathered logit reads as 0,
+ *     outside the student's normalisation (its term is p_k (log p_k +
+ *     logsumexp_v s_iv)), and it adds nothing to the gradient.
  *   - Ignored positions: a position whose FIRST teacher id is -1 has no
  *     teacher target (padding, packing boundaries). It adds nothing: its
  *     per-row KL is 0, its gradient row (dZ, hence dH) is 0, and the mean
@@ -68,7 +72,7 @@
 extern "C" {
 #endif
 
-#define KDKL_ABI_VERSION 1
+#define KDKL_ABI_VERSION 2
 /* Bytes of device workspace kdkl_logits_backward needs (any N, V, K). */
 #define KDKL_LOGITS_BWD_WORKSPACE 256
 /* Bytes of device workspace kdkl_check_ids needs (any N, V, K). */
@@ -83,10 +87,67 @@ typedef enum {
   KDKL_ERR_WORKSPACE = 5, /* workspace smaller than kdkl_workspace_size() */
   KDKL_ERR_OVERFLOW = 6,  /* a size product overflows */
   KDKL_ERR_HIP = 7,       /* a HIP launch or runtime call failed */
-  KDKL_ERR_ALIGN = 8      /* a pointer is not 16-byte aligned */
+  KDKL_ERR_ALIGN = 8,     /* a pointer is not 16-byte aligned */
+  KDKL_ERR_OPTION = 9     /* a kdkl_options field is out of range or not
+                             available for these sizes and dtype */
 } kdkl_status;
 
 typedef enum { KDKL_F32 = 0, KDKL_BF16 = 1 } kdkl_dtype;
+
+/* Loss computed by kdkl_forward / kdkl_backward (kdkl_options.loss). */
+typedef enum {
+  KDKL_LOSS_KL = 0 /* forward KL(teacher top-K || student), the pages' loss */
+} kdkl_loss;
+
+/* Per-call options of the fused calls. NULL, or a zero-filled struct, means
+ * the defaults: the loss above and the library's own blocking, which it
+ * chooses from the sizes alone (the library reads no environment variable
+ * and keeps no setting between calls). The same options must be passed to
+ * kdkl_workspace_size, kdkl_forward and kdkl_backward of one problem: the
+ * workspace size depends on them. Blocking options never change results
+ * beyond floating-point rounding order.
+ *   loss             kdkl_loss value.
+ *   chunks_per_group 0: the library's choice; n >= 1: take n slices of
+ *                    `chunk` positions per launch (both calls); n > 1 needs
+ *                    the bf16 main loop (bf16 storage, d a multiple of 64).
+ *   vocab_slices     0: as many vocabulary slices per group as chunks per
+ *                    group (the dZ buffer then holds one chunk's worth of
+ *                    elements); n >= 1 (at most 1024): the backward covers
+ *                    a group's vocabulary in slices of ceil(V/n) rows rounded
+ *                    up to whole tiles (so at most n slices; kdkl_plan_info
+ *                    reports the count); its dZ buffer holds group rows x one
+ *                    slice, and dW's fp32 read-modify-write happens once per
+ *                    group and slice.
+ *   dh_w_in_place    0: the library's choice; 1: the dH product reads W in
+ *                    place (no V x d transposed copy in the workspace; needs
+ *                    the bf16 main loop); 2: it reads a W^T copy written once
+ *                    per backward call.
+ *   beta             parameter of the loss, where it has one (ignored
+ *                    otherwise).
+ *   reserved         must be zero. */
+typedef struct {
+  int32_t loss;
+  int32_t chunks_per_group;
+  int32_t vocab_slices;
+  int32_t dh_w_in_place;
+  float beta;
+  int32_t reserved[3];
+} kdkl_options;
+
+/* The blocking the fused calls use for given sizes and options
+ * (kdkl_plan_info). */
+typedef struct {
+  int32_t chunks_per_group; /* slices of `chunk` positions per launch */
+  int32_t vocab_slices;     /* vocabulary slices per group in the backward */
+  int32_t dh_splits;        /* split-K count of the dH product per launch */
+  int32_t dh_w_in_place;    /* 1: dH reads W in place; 0: a W^T copy */
+  int32_t vocab_tile;       /* vocabulary rows per workgroup of the projections */
+  int32_t hidden_tile;      /* hidden-size columns per workgroup of dH and dW */
+  int32_t bf16_main_loop;   /* 1: the bf16 main loop; 0: the generic one */
+  int32_t reserved;
+  uint64_t fwd_bytes;       /* = kdkl_workspace_size's *fwd_bytes */
+  uint64_t bwd_bytes;       /* = kdkl_workspace_size's *bwd_bytes */
+} kdkl_plan;
 
 /* Version of this ABI (KDKL_ABI_VERSION). */
 int kdkl_abi_version(void);
@@ -95,41 +156,34 @@ int kdkl_abi_version(void);
 const char* kdkl_status_string(int status);
 
 /* Bytes of device workspace needed by kdkl_forward (*fwd_bytes) and by
- * kdkl_backward (*bwd_bytes) for these sizes. Either output may be NULL.
- * Host-only; the same validation as the compute calls. On the bf16 path the
- * backward workspace may hold a transposed copy of W (V * d elements) for
- * the dH product: the plan leaves it out, and reads W in place, where that
- * costs less time for these sizes (few dH launches per call, e.g. 8K
- * positions of a Llama-like head); KDKL_DH_W_INPLACE=1 in the environment
- * forces the in-place read (less memory, slightly slower on large calls),
- * KDKL_DH_W_INPLACE=0 the copy. Ask for the size and call kdkl_backward
- * under the same setting (a smaller workspace is rejected with
- * KDKL_ERR_WORKSPACE). */
+ * kdkl_backward (*bwd_bytes) for these sizes and options (NULL: defaults).
+ * Either output may be NULL. Host-only; the same validation as the compute
+ * calls. On the bf16 path the backward workspace may hold a transposed copy
+ * of W (V * d elements) for the dH product: by default the library keeps it
+ * only where the time it saves over reading W in place is worth it (at least
+ * about 0.3 ms per call by the library's model: at the gpt-oss-like head,
+ * d = 2880 and V = 201088 with chunks of 2048, from N = 16385 on), so the
+ * backward workspace steps up by that copy at one N; dh_w_in_place selects
+ * either layout explicitly. */
 kdkl_status kdkl_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K,
-                                int64_t chunk, int dtype,
+                                int64_t chunk, int dtype, const kdkl_options* opts,
                                 size_t* fwd_bytes, size_t* bwd_bytes);
 
-/* How the calls will block the work for these sizes (host-only, the same
- * validation as kdkl_workspace_size; each output may be NULL):
- *   *chunks_per_group: slices of `chunk` positions taken together per launch
- *     (1 = one slice at a time); the backward covers the vocabulary of a
- *     group in *vocab_slices consecutive slices, so dW's fp32
- *     read-modify-write happens once per group and slice;
- *   *dh_splits: split-K count of the dH product per launch (fp32 partials
- *     summed in a fixed order).
+/* The blocking the calls will use for these sizes and options (host-only,
+ * the same validation as kdkl_workspace_size), written to *out (not NULL).
  * The blocking never changes the results beyond rounding order; it is
  * reported so that callers and tests can tell which launch shapes a size
  * exercises. The slices themselves are the chunks over positions that the
  * loss is computed in [P1 "Making knowledge distillation cheap enough to
  * run at scale", section "Two system changes", fused chunked KL bullet]. */
 kdkl_status kdkl_plan_info(int64_t N, int64_t d, int64_t V, int32_t K,
-                           int64_t chunk, int dtype, int* chunks_per_group,
-                           int* vocab_slices, int* dh_splits);
+                           int64_t chunk, int dtype, const kdkl_options* opts,
+                           kdkl_plan* out);
 
 /* Forward pass of the fused chunked KL loss.
  *   H [N, d] dtype, W [V, d] dtype, topk_ids [N, K] int32, topk_logits
  *   [N, K] fp32; T > 0; chunk = positions per slice (>= 1; the last slice may
- *   be short); 1 <= K <= min(V, 1024).
+ *   be short); 1 <= K <= min(V, 1024); opts as for kdkl_workspace_size.
  * Outputs (device): loss [1] fp32 (mean KL over kept positions; NaN when
  *   none, e.g. N == 0),
  *   row_lse [N] fp32 = logsumexp_v(s_iv) (keep it for kdkl_backward),
@@ -138,20 +192,20 @@ kdkl_status kdkl_plan_info(int64_t N, int64_t d, int64_t V, int32_t K,
 kdkl_status kdkl_forward(const void* H, const void* W,
                          const int32_t* topk_ids, const float* topk_logits,
                          int64_t N, int64_t d, int64_t V, int32_t K,
-                         float T, int64_t chunk, int dtype,
+                         float T, int64_t chunk, int dtype, const kdkl_options* opts,
                          float* loss, float* row_lse, float* row_kl,
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /* Backward pass: recomputes each slice's logits and writes
  *   dH [N, d] in the storage dtype, dW [V, d] fp32.
- * row_lse is the forward's output for the same inputs. grad_loss is a device
+ * row_lse is the forward's output for the same inputs and options. grad_loss is a device
  * pointer to the upstream scalar g (NULL means g = 1). accumulate_dW != 0
  * adds into dW instead of overwriting it (gradient accumulation across
  * micro-batches). Workspace: >= *bwd_bytes from kdkl_workspace_size. */
 kdkl_status kdkl_backward(const void* H, const void* W,
                           const int32_t* topk_ids, const float* topk_logits,
                           int64_t N, int64_t d, int64_t V, int32_t K,
-                          float T, int64_t chunk, int dtype,
+                          float T, int64_t chunk, int dtype, const kdkl_options* opts,
                           const float* row_lse, const float* grad_loss,
                           void* dH, float* dW, int accumulate_dW,
                           void* workspace, size_t workspace_bytes, void* stream);
@@ -243,8 +297,10 @@ kdkl_status kdkl_check_ids(const int32_t* topk_ids, int64_t N, int32_t K, int64_
  * the launch stream. kdkl_profile_end() waits for those events and returns,
  * per kernel name, the launch count, the summed event time and the summed
  * algorithmic work (flop and HBM bytes by the formulas the library states for
- * each kernel). Process-wide, not thread-safe against concurrent compute
- * calls; it creates HIP events but allocates no device buffers. */
+ * each kernel). The timing table is the library's only process-wide mutable
+ * state: one table for the process, guarded by a lock (a compute call on
+ * another thread while profiling is switched on or off is timed or not,
+ * never torn). It creates HIP events but allocates no device buffers. */
 typedef struct {
   char name[48];
   int64_t launches;

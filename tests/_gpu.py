@@ -17,17 +17,17 @@ def to_dev(x, dev="cuda:0"):
     return {k: v.to(dev) for k, v in x.items()}
 
 
-def run_gpu(x, T, chunk, g=None, accumulate_dW=False, dW_init=None, stream=None):
+def run_gpu(x, T, chunk, g=None, accumulate_dW=False, dW_init=None, stream=None, options=None):
     """Forward + backward on cuda:0; returns numpy fp64 results."""
     import chunked_kl_loss_amd as kd
 
     d = to_dev(x)
     loss, row_lse, row_kl = kd.kdkl_forward(d["H"], d["W"], d["ids"], d["logits"], T, chunk,
-                                            stream=stream)
+                                            stream=stream, options=options)
     gt = None if g is None else torch.tensor([g], dtype=torch.float32, device="cuda:0")
     dW = None if dW_init is None else dW_init.clone().to("cuda:0")
     dH, dW = kd.kdkl_backward(d["H"], d["W"], d["ids"], d["logits"], T, chunk, row_lse, gt,
-                              dW=dW, accumulate_dW=accumulate_dW, stream=stream)
+                              dW=dW, accumulate_dW=accumulate_dW, stream=stream, options=options)
     torch.cuda.synchronize()
     return {
         "loss": float(loss.item()),

@@ -11,7 +11,7 @@ from chunked_kl_loss_amd import _lib as L
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
-OK, NULL, SHAPE, VALUE, DTYPE, WORKSPACE, OVERFLOW, HIP, ALIGN = range(9)
+OK, NULL, SHAPE, VALUE, DTYPE, WORKSPACE, OVERFLOW, HIP, ALIGN, OPTION = range(10)
 FAKE = 0x10000  # 16-byte aligned, never dereferenced on the host
 
 
@@ -40,16 +40,26 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.kdkl_abi_version() == 1
-    for s in list(range(9)) + [99, -1]:
+    assert lib.kdkl_abi_version() == 2
+    for s in list(range(10)) + [99, -1]:
         v = lib.kdkl_status_string(s)
         assert v is not None and len(v) > 0
     assert lib.kdkl_status_string(WORKSPACE).startswith(b"KDKL_ERR_WORKSPACE")
 
 
-def ws(lib, N, d, V, K, chunk, dt):
+def opts(**kw):
+    o = L.Options()
+    for k, v in kw.items():
+        if k == "reserved":
+            o.reserved[0] = v
+        else:
+            setattr(o, k, v)
+    return C.byref(o)
+
+
+def ws(lib, N, d, V, K, chunk, dt, o=None):
     f, b = C.c_size_t(), C.c_size_t()
-    st = lib.kdkl_workspace_size(N, d, V, K, chunk, dt, C.byref(f), C.byref(b))
+    st = lib.kdkl_workspace_size(N, d, V, K, chunk, dt, o, C.byref(f), C.byref(b))
     return st, f.value, b.value
 
 
@@ -77,7 +87,7 @@ def test_workspace_size_arithmetic(lib):
     _, _, b32 = ws(lib, 32768, 2880, 201088, 100, 2048, L.KDKL_F32)
     assert b32 > b
     # outputs may be NULL
-    assert lib.kdkl_workspace_size(10, 8, 16, 2, 4, L.KDKL_BF16, None, None) == OK
+    assert lib.kdkl_workspace_size(10, 8, 16, 2, 4, L.KDKL_BF16, None, None, None) == OK
 
 
 @pytest.mark.parametrize("args,status", [
@@ -100,20 +110,20 @@ def test_workspace_size_rejects(lib, args, status):
 
 def fwd(lib, **kw):
     a = dict(H=FAKE, W=FAKE, ids=FAKE, lg=FAKE, N=64, d=64, V=1000, K=8, T=1.0, chunk=16,
-             dt=L.KDKL_BF16, loss=FAKE, lse=FAKE, kl=None, ws=FAKE, wsb=1 << 40, stream=None)
+             dt=L.KDKL_BF16, o=None, loss=FAKE, lse=FAKE, kl=None, ws=FAKE, wsb=1 << 40, stream=None)
     a.update(kw)
     return lib.kdkl_forward(a["H"], a["W"], a["ids"], a["lg"], a["N"], a["d"], a["V"], a["K"],
-                            a["T"], a["chunk"], a["dt"], a["loss"], a["lse"], a["kl"], a["ws"],
+                            a["T"], a["chunk"], a["dt"], a["o"], a["loss"], a["lse"], a["kl"], a["ws"],
                             a["wsb"], a["stream"])
 
 
 def bwd(lib, **kw):
     a = dict(H=FAKE, W=FAKE, ids=FAKE, lg=FAKE, N=64, d=64, V=1000, K=8, T=1.0, chunk=16,
-             dt=L.KDKL_BF16, lse=FAKE, g=None, dH=FAKE, dW=FAKE, acc=0, ws=FAKE, wsb=1 << 40,
+             dt=L.KDKL_BF16, o=None, lse=FAKE, g=None, dH=FAKE, dW=FAKE, acc=0, ws=FAKE, wsb=1 << 40,
              stream=None)
     a.update(kw)
     return lib.kdkl_backward(a["H"], a["W"], a["ids"], a["lg"], a["N"], a["d"], a["V"], a["K"],
-                             a["T"], a["chunk"], a["dt"], a["lse"], a["g"], a["dH"], a["dW"],
+                             a["T"], a["chunk"], a["dt"], a["o"], a["lse"], a["g"], a["dH"], a["dW"],
                              a["acc"], a["ws"], a["wsb"], a["stream"])
 
 
@@ -137,6 +147,14 @@ def bwd(lib, **kw):
     (dict(H=FAKE + 8), ALIGN),
     (dict(W=FAKE + 2), ALIGN),
     (dict(ws=FAKE + 4), ALIGN),
+    (dict(o=opts(loss=7)), OPTION),
+    (dict(o=opts(chunks_per_group=-1)), OPTION),
+    (dict(o=opts(vocab_slices=1025)), OPTION),
+    (dict(o=opts(dh_w_in_place=3)), OPTION),
+    (dict(o=opts(reserved=1)), OPTION),
+    (dict(o=opts(dh_w_in_place=1), dt=L.KDKL_F32), OPTION),      # in place needs the bf16 main loop
+    (dict(o=opts(chunks_per_group=2), dt=L.KDKL_F32), OPTION),   # so do groups of chunks
+    (dict(o=opts(chunks_per_group=2), d=72), OPTION),
 ])
 def test_compute_calls_reject_bad_arguments(lib, call, kw, status):
     assert call(lib, **kw) == status
@@ -338,29 +356,28 @@ def test_binding_output_checks():
     assert kd._nbytes(torch.zeros(5, dtype=torch.float32)) == 20
 
 
-def test_dh_reading_w_in_place_drops_the_transposed_copy(lib, monkeypatch):
-    # the bf16 backward normally keeps W^T [d, Vp]; with KDKL_DH_W_INPLACE=1
+def test_dh_reading_w_in_place_drops_the_transposed_copy(lib):
+    # the bf16 backward at gpt-oss 32K keeps W^T [d, Vp]; with dh_w_in_place=1
     # its dH product reads W in place and the workspace shrinks by that copy
     N, d, V, K, chunk = 32768, 2880, 201088, 100, 2048
-    monkeypatch.delenv("KDKL_DH_W_INPLACE", raising=False)
     _, f0, b0 = ws(lib, N, d, V, K, chunk, L.KDKL_BF16)
-    monkeypatch.setenv("KDKL_DH_W_INPLACE", "1")
-    _, f1, b1 = ws(lib, N, d, V, K, chunk, L.KDKL_BF16)
+    _, f1, b1 = ws(lib, N, d, V, K, chunk, L.KDKL_BF16, opts(dh_w_in_place=1))
     Vp = (V + 383) // 384 * 384
     assert f1 == f0
     assert b0 - b1 >= d * Vp * 2 and b0 - b1 < d * Vp * 2 + 512
-    # the generic path (d not a multiple of 64) always keeps W^T
-    _, _, g1 = ws(lib, N, 2888, V, K, chunk, L.KDKL_BF16)
-    monkeypatch.delenv("KDKL_DH_W_INPLACE")
+    # the generic path (d not a multiple of 64) always keeps W^T and cannot
+    # read in place
     _, _, g0 = ws(lib, N, 2888, V, K, chunk, L.KDKL_BF16)
-    assert g1 == g0
+    _, _, g2 = ws(lib, N, 2888, V, K, chunk, L.KDKL_BF16, opts(dh_w_in_place=2))
+    assert g2 == g0
+    assert ws(lib, N, 2888, V, K, chunk, L.KDKL_BF16, opts(dh_w_in_place=1))[0] == OPTION
 
 
-def plan(lib, N, d, V, K, chunk, dt):
-    g, v, s = C.c_int(), C.c_int(), C.c_int()
-    st = lib.kdkl_plan_info(N, d, V, K, chunk, dt, C.byref(g), C.byref(v), C.byref(s))
+def plan(lib, N, d, V, K, chunk, dt, o=None):
+    p = L.Plan()
+    st = lib.kdkl_plan_info(N, d, V, K, chunk, dt, o, C.byref(p))
     assert st == OK, L_status(lib, st)
-    return g.value, v.value, s.value
+    return p
 
 
 def L_status(lib, st):
@@ -382,47 +399,92 @@ def L_status(lib, st):
     ((2048, 1024, 32000, 100, 256), 1),
 ])
 def test_plan_groups(lib, sizes, groups):
-    g, v, s = plan(lib, *sizes, L.KDKL_BF16)
-    assert g == groups
-    assert v == groups  # as many vocabulary slices as chunks per group
-    assert s >= 1
+    p = plan(lib, *sizes, L.KDKL_BF16)
+    assert p.chunks_per_group == groups
+    assert p.vocab_slices == groups  # as many vocabulary slices as chunks per group
+    assert p.dh_splits >= 1 and p.bf16_main_loop == 1
 
 
 def test_plan_groups_never_exceed_the_chunks(lib):
     # two chunks only: a group never spans more chunks than there are
-    g, v, _ = plan(lib, 128, 64, 524001, 20, 64, L.KDKL_BF16)
-    assert g <= 2 and v == g
+    p = plan(lib, 128, 64, 524001, 20, 64, L.KDKL_BF16)
+    assert p.chunks_per_group <= 2 and p.vocab_slices == p.chunks_per_group
 
 
 def test_plan_fp32_takes_one_chunk_at_a_time(lib):
-    assert plan(lib, 128, 256, 4096, 16, 32, L.KDKL_F32)[:2] == (1, 1)
+    p = plan(lib, 128, 256, 4096, 16, 32, L.KDKL_F32)
+    assert (p.chunks_per_group, p.vocab_slices, p.bf16_main_loop, p.dh_w_in_place) == (1, 1, 0, 0)
 
 
 def test_plan_dh_splits_fill_the_rounds(lib):
     # gpt-oss at 32K: 8192-row groups by 2880 columns on 256 x 320 tiles is
     # 288 tiles; six splits fill 96.4% of seven rounds of 256 workgroups
-    assert plan(lib, 32768, 2880, 201088, 100, 2048, L.KDKL_BF16)[2] == 6
+    p = plan(lib, 32768, 2880, 201088, 100, 2048, L.KDKL_BF16)
+    assert p.dh_splits == 6 and p.hidden_tile == 320 and p.vocab_tile == 384
 
 
 def test_plan_info_validates_like_the_compute_calls(lib):
-    assert lib.kdkl_plan_info(10, 8, 16, 0, 4, L.KDKL_BF16, None, None, None) != OK
-    assert lib.kdkl_plan_info(10, 8, 16, 2, 4, L.KDKL_BF16, None, None, None) == OK
+    p = L.Plan()
+    assert lib.kdkl_plan_info(10, 8, 16, 0, 4, L.KDKL_BF16, None, C.byref(p)) == SHAPE
+    assert lib.kdkl_plan_info(10, 8, 16, 2, 4, L.KDKL_BF16, None, None) == NULL
+    assert lib.kdkl_plan_info(10, 8, 16, 2, 4, L.KDKL_BF16, None, C.byref(p)) == OK
+    assert lib.kdkl_plan_info(10, 8, 16, 2, 4, L.KDKL_BF16, opts(vocab_slices=-2), C.byref(p)) == OPTION
+    # the sizes it reports are kdkl_workspace_size's
+    q = plan(lib, 32768, 2880, 201088, 100, 2048, L.KDKL_BF16)
+    assert (q.fwd_bytes, q.bwd_bytes) == ws(lib, 32768, 2880, 201088, 100, 2048, L.KDKL_BF16)[1:]
+
+
+def test_options_select_the_blocking(lib):
+    sizes = (32768, 2880, 201088, 100, 2048)
+    base = plan(lib, *sizes, L.KDKL_BF16)
+    # vocabulary slices apart from the chunks per group: the dZ buffer holds
+    # group rows x V/slices columns, slices starting on 768-row boundaries
+    # (16 slices of a 4-chunk group: 8192 rows x 13056 columns, 214 MB,
+    # against 8192 x 50688, 830 MB, for the default 4 slices)
+    p16 = plan(lib, *sizes, L.KDKL_BF16, opts(vocab_slices=16))
+    assert (p16.chunks_per_group, p16.vocab_slices) == (4, 16)
+    assert p16.dh_splits == base.dh_splits
+    assert base.bwd_bytes - p16.bwd_bytes == 8192 * (50688 - 13056) * 2
+    p1 = plan(lib, *sizes, L.KDKL_BF16, opts(chunks_per_group=1))
+    assert (p1.chunks_per_group, p1.vocab_slices) == (1, 1)
+    p8 = plan(lib, *sizes, L.KDKL_BF16, opts(chunks_per_group=8, vocab_slices=32))
+    # 32 slices asked: ceil(V/32) = 6284 rows rounded up to 6912 give 30
+    assert (p8.chunks_per_group, p8.vocab_slices) == (8, 30)
+    # the forward's workspace follows the group size
+    assert p8.fwd_bytes > base.fwd_bytes > p1.fwd_bytes
+    # explicit W layouts
+    assert plan(lib, *sizes, L.KDKL_BF16, opts(dh_w_in_place=1)).dh_w_in_place == 1
+    assert plan(lib, *sizes, L.KDKL_BF16, opts(dh_w_in_place=2)).dh_w_in_place == 0
+    # zero-filled options are the defaults
+    z = plan(lib, *sizes, L.KDKL_BF16, opts())
+    assert (z.chunks_per_group, z.vocab_slices, z.dh_splits, z.dh_w_in_place, z.bwd_bytes) == \
+        (base.chunks_per_group, base.vocab_slices, base.dh_splits, base.dh_w_in_place, base.bwd_bytes)
 
 
 @pytest.mark.parametrize("sizes,in_place", [
     ((8192, 3072, 128256, 100, 1024), True),     # Llama-like head, 8K: 8 dH launches per call
+    ((16384, 2880, 201088, 100, 2048), True),    # gpt-oss-like head, 16K: 8 launches
+    ((16385, 2880, 201088, 100, 2048), False),   # one position more: 12 launches
     ((32768, 2880, 201088, 100, 2048), False),   # gpt-oss-like head, 32K: 16 launches
     ((262144, 2880, 201088, 100, 4096), False),  # the same head at 256K: 64 launches
 ])
-def test_w_copy_chosen_per_shape(lib, monkeypatch, sizes, in_place):
-    # by default the dH product reads W in place only where one call's slower
-    # dH launches cost less than writing the W^T copy; the environment forces either
-    monkeypatch.delenv("KDKL_DH_W_INPLACE", raising=False)
+def test_w_copy_chosen_per_shape(lib, sizes, in_place):
+    # by default the dH product reads W in place unless the copy saves at
+    # least about 0.3 ms per call by the library's model; the options force
+    # either. The backward workspace steps up by the copy where the choice
+    # flips (gpt-oss-like head with chunks of 2048: between 16384 and 16385).
+    assert plan(lib, *sizes, L.KDKL_BF16).dh_w_in_place == int(in_place)
     _, _, b_default = ws(lib, *sizes, L.KDKL_BF16)
-    monkeypatch.setenv("KDKL_DH_W_INPLACE", "1")
-    _, _, b_in_place = ws(lib, *sizes, L.KDKL_BF16)
-    monkeypatch.setenv("KDKL_DH_W_INPLACE", "0")
-    _, _, b_copy = ws(lib, *sizes, L.KDKL_BF16)
+    _, _, b_in_place = ws(lib, *sizes, L.KDKL_BF16, opts(dh_w_in_place=1))
+    _, _, b_copy = ws(lib, *sizes, L.KDKL_BF16, opts(dh_w_in_place=2))
     d, V = sizes[1], sizes[2]
     assert b_copy - b_in_place >= d * V * 2
     assert b_default == (b_in_place if in_place else b_copy)
+
+
+def test_library_reads_no_environment(lib):
+    # the library is configured by arguments only
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", L.LIB_PATH], capture_output=True, text=True)
+    assert out.returncode == 0
+    assert "getenv" not in out.stdout

@@ -68,45 +68,58 @@ def _check_properties(w, x, got):
     assert abs(wd - hd) <= 1e-3 * scale
 
 
-def test_gptoss20b_32k_full_size():
-    w = wl.get_config("gptoss20b_32k")
-    x = wl.generate(w)
-    got = _run(w, x)
-    # full-row comparison with the oracle's stored per-row results
-    g = np.load(os.path.join(GOLDEN, "oracle_gptoss20b_32k_rows.npz"))
+def _check_against_stored_oracle(w, x, got, rng):
+    """Every row's lse and KL and the loss against the oracle's stored
+    per-row results (written by tests/golden/make_fullsize_oracle.py, which
+    calls only the oracle), and sampled rows of dW, which need every row's
+    lse (the stored oracle values)."""
+    g = np.load(os.path.join(GOLDEN, f"oracle_{w.name}_rows.npz"))
     assert int(g["seed"]) == wl.seed_for(w)
+    assert g["row_lse"].shape == (w.N,)
     rel = abs(got["loss"] - float(g["loss"])) / abs(float(g["loss"]))
     e_lse = np.abs(got["row_lse"] - g["row_lse"]).max() / np.abs(g["row_lse"]).max()
     e_kl = np.abs(got["row_kl"] - g["row_kl"]).max() / np.abs(g["row_kl"]).max()
-    print(f"full rows: loss rel {rel:.2e} lse {e_lse:.2e} kl {e_kl:.2e}", flush=True)
+    print(f"{w.name} full rows: loss {got['loss']:.9g} vs {float(g['loss']):.9g} rel {rel:.2e}; "
+          f"lse {e_lse:.2e} kl {e_kl:.2e}", flush=True)
     assert rel <= 1e-3 and e_lse <= 1e-3 and e_kl <= 1e-3
-    rng = np.random.default_rng(7)
-    _check_rows(w, x, got, _sample_rows(w, rng))
-    # sampled rows of dW (they need every row's lse: the stored oracle values)
     ids = x["ids"].numpy()
     vrows = sorted({0, 1, 5, 255, 256, int(ids[0, 0]), int(ids[123, 7]), w.V - 129, w.V - 1}
                    | set(rng.choice(w.V, size=8, replace=False).tolist()))
     ref = oracle.dw_rows(x["H"], x["W"], x["ids"], x["logits"], w.T, vrows, g["row_lse"])
     dw = got["dW"][vrows].double().numpy()
     e_dw = np.abs(dw - ref).max() / np.abs(ref).max()
-    print(f"sampled dW rows {len(vrows)}: {e_dw:.2e}", flush=True)
+    print(f"{w.name} sampled dW rows {len(vrows)}: {e_dw:.2e}", flush=True)
     assert e_dw <= 2e-2
+
+
+def test_gptoss20b_32k_full_size():
+    w = wl.get_config("gptoss20b_32k")
+    x = wl.generate(w)
+    got = _run(w, x)
+    rng = np.random.default_rng(7)
+    _check_against_stored_oracle(w, x, got, rng)
+    _check_rows(w, x, got, _sample_rows(w, rng))
     _check_properties(w, x, got)
 
 
 def test_longctx_256k_full_size():
+    # the launch configuration the default bench times (T = 2, chunks of 4096
+    # in groups of four, W^T copy)
     w = wl.get_config("longctx_256k")
     x = wl.generate(w)
     got = _run(w, x)
     rng = np.random.default_rng(8)
+    _check_against_stored_oracle(w, x, got, rng)
     _check_rows(w, x, got, _sample_rows(w, rng, n=6))
     _check_properties(w, x, got)
 
 
 def test_llama3b_8k_full_size():
+    # groups of eight chunks over eight vocabulary slices, W read in place
     w = wl.get_config("llama3b_8k")
     x = wl.generate(w)
     got = _run(w, x)
     rng = np.random.default_rng(9)
+    _check_against_stored_oracle(w, x, got, rng)
     _check_rows(w, x, got, _sample_rows(w, rng))
     _check_properties(w, x, got)
