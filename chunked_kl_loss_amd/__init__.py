@@ -24,6 +24,7 @@ __all__ = [
     "plan_info",
     "kdkl_forward",
     "kdkl_backward",
+    "kdkl_forward_noalloc",
     "FusedKLLoss",
     "fused_kl_loss",
     "logits_forward",
@@ -180,6 +181,23 @@ def kdkl_backward(H, W, ids, logits, T: float, chunk: int, row_lse, grad_loss=No
                                _ptr(workspace), _nbytes(workspace), _stream(dev, stream)),
           "kdkl_backward")
     return dH, dW
+
+
+def kdkl_forward_noalloc(H, W, ids, logits, T: float, chunk: int, *, loss, row_lse, row_kl,
+                         stream=None, options=None):
+    """Run ``kdkl_forward_noalloc``: the forward on the library's static
+    device scratch; every output is the caller's (nothing is allocated)."""
+    _need_gpu(H, W, ids, logits, loss, row_lse, row_kl)
+    N, d, V, K = _check_shapes(H, W, ids, logits)
+    dev = H.device
+    _want(loss, (1,), torch.float32, dev, "loss")
+    _want(row_lse, (N,), torch.float32, dev, "row_lse")
+    _want(row_kl, (N,), torch.float32, dev, "row_kl")
+    check(_load().kdkl_forward_noalloc(_ptr(H), _ptr(W), _ptr(ids), _ptr(logits), N, d, V, K,
+                                      float(T), chunk, _dtype_code(H), _options(options), _ptr(loss),
+                                      _ptr(row_lse), _ptr(row_kl), _stream(dev, stream)),
+          "kdkl_forward_noalloc")
+    return loss, row_lse, row_kl
 
 
 class FusedKLLoss(torch.autograd.Function):

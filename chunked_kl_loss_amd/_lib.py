@@ -18,6 +18,7 @@ STATUS = {
     7: "KDKL_ERR_HIP", 8: "KDKL_ERR_ALIGN", 9: "KDKL_ERR_OPTION",
 }
 ABI_VERSION = 2
+NOALLOC_SCRATCH_BYTES = 64 << 20  # KDKL_NOALLOC_SCRATCH_BYTES
 KDKL_LOSS_KL = 0
 
 
@@ -79,6 +80,8 @@ SIGNATURES = {
                                  C.POINTER(Plan)]),
     "kdkl_forward": (C.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, C.c_float, _I64,
                                C.c_int, C.POINTER(Options), _P, _P, _P, _P, C.c_size_t, _P]),
+    "kdkl_forward_noalloc": (C.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, C.c_float, _I64,
+                                       C.c_int, C.POINTER(Options), _P, _P, _P, _P]),
     "kdkl_backward": (C.c_int, [_P, _P, _P, _P, _I64, _I64, _I64, _I32, C.c_float, _I64,
                                 C.c_int, C.POINTER(Options), _P, _P, _P, _P, C.c_int, _P,
                                 C.c_size_t, _P]),

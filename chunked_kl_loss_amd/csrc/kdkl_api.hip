@@ -405,20 +405,13 @@ kdkl_status kdkl_plan_info(int64_t N, int64_t d, int64_t V, int32_t K, int64_t c
   return KDKL_OK;
 }
 
-kdkl_status kdkl_forward(const void* H, const void* W, const int32_t* ids, const float* lg, int64_t N,
-                         int64_t d, int64_t V, int32_t K, float T, int64_t chunk, int dtype,
-                         const kdkl_options* opts, float* loss, float* row_lse, float* row_kl, void* workspace,
-                         size_t workspace_bytes, void* stream) {
-  Plan P;
-  kdkl_status st = make_plan(N, d, V, K, chunk, dtype, opts, &P);
-  if (st != KDKL_OK) return st;
-  if ((st = check_common(H, W, ids, lg, N, T)) != KDKL_OK) return st;
-  if (!loss || (N > 0 && !row_lse) || !workspace) return KDKL_ERR_NULL;
-  if (workspace_bytes < P.f_bytes) return KDKL_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return KDKL_ERR_ALIGN;
-  hipStream_t s = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  float* kl = row_kl ? row_kl : (float*)(ws + P.f_rowkl);
+// The forward's launch sequence on a checked workspace `ws`: per group of
+// rows, the teacher products, the projection with its online logsumexp and
+// teacher-gather epilogue, and the split merge; then the loss.
+static hipError_t forward_launches(const Plan& P, const void* H, const void* W, const int32_t* ids,
+                                  const float* lg, float T, float* loss, float* row_lse, float* kl, char* ws,
+                                  hipStream_t s) {
+  const int64_t N = P.N, V = P.V, d = P.d;
   hipError_t e = hipSuccess;
   const int64_t group = P.bg * P.chunk;  // rows per launch: the backward's group
   for (int64_t r0 = 0; r0 < N && e == hipSuccess; r0 += group) {
@@ -432,7 +425,7 @@ kdkl_status kdkl_forward(const void* H, const void* W, const int32_t* ids, const
     g.part = (float4*)(ws + P.f_part);
     const double fl = 2.0 * rows * (double)V * d;
     const double by = ((double)V + rows) * d * P.es + (double)rows * P.n_vt * 16.0;
-    e = timed(K_FWD_GEMM, fl, by, s, [&] { return launch_gemm(dtype, EPI_FWD, g, s); });
+    e = timed(K_FWD_GEMM, fl, by, s, [&] { return launch_gemm(P.dtype, EPI_FWD, g, s); });
     if (e != hipSuccess) break;
     MergeArgs m;
     m.part = (const float4*)(ws + P.f_part); m.n_vt = (int)P.n_vt; m.rows = rows;
@@ -441,7 +434,90 @@ kdkl_status kdkl_forward(const void* H, const void* W, const int32_t* ids, const
     e = timed(K_MERGE, 0.0, (double)rows * P.n_vt * 16.0, s, [&] { return launch_merge(m, s); });
   }
   if (e == hipSuccess)
-    e = timed(K_LOSS, 0.0, (double)N * 8.0, s, [&] { return launch_loss(kl, ids, K, N, loss, s); });
+    e = timed(K_LOSS, 0.0, (double)N * 8.0, s, [&] { return launch_loss(kl, ids, (int)P.K, N, loss, s); });
+  return e;
+}
+
+kdkl_status kdkl_forward(const void* H, const void* W, const int32_t* ids, const float* lg, int64_t N,
+                         int64_t d, int64_t V, int32_t K, float T, int64_t chunk, int dtype,
+                         const kdkl_options* opts, float* loss, float* row_lse, float* row_kl, void* workspace,
+                         size_t workspace_bytes, void* stream) {
+  Plan P;
+  kdkl_status st = make_plan(N, d, V, K, chunk, dtype, opts, &P);
+  if (st != KDKL_OK) return st;
+  if ((st = check_common(H, W, ids, lg, N, T)) != KDKL_OK) return st;
+  if (!loss || (N > 0 && !row_lse) || !workspace) return KDKL_ERR_NULL;
+  if (workspace_bytes < P.f_bytes) return KDKL_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return KDKL_ERR_ALIGN;
+  char* ws = (char*)workspace;
+  float* kl = row_kl ? row_kl : (float*)(ws + P.f_rowkl);
+  const hipError_t e = forward_launches(P, H, W, ids, lg, T, loss, row_lse, kl, ws, (hipStream_t)stream);
+  return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
+}
+
+// ---------------------- allocation-free forward ------------------------------
+// For callers that cannot allocate device memory, the forward's workspace can
+// be a file-scope device array. Its name in host code is a host-side
+// stand-in, not a device address: the address is looked up once per device
+// (with that device current) by hipGetSymbolAddress, and only that pointer
+// is ever passed to kernels. The forward needs no part of its workspace
+// cleared (every region is written before it is read), so the array keeps
+// whatever the last call left in it.
+static_assert(KDKL_NOALLOC_SCRATCH_BYTES % 256 == 0, "the scratch holds whole 256-byte regions");
+static __device__ __align__(256) char scratch[KDKL_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];  // per device, set once
+
+// Device address of `scratch` on the device of `stream` (NULL: the current
+// device).
+static hipError_t scratch_address(hipStream_t stream, void** out) {
+  int cur = -1, dev = -1;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return e;
+  dev = cur;
+  if (stream != nullptr && (e = hipStreamGetDevice(stream, &dev)) != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return e;
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    const hipError_t back = dev != cur ? hipSetDevice(cur) : hipSuccess;
+    if (e != hipSuccess) return e;
+    if (back != hipSuccess) return back;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+kdkl_status kdkl_forward_noalloc(const void* H, const void* W, const int32_t* ids, const float* lg, int64_t N,
+                                 int64_t d, int64_t V, int32_t K, float T, int64_t chunk, int dtype,
+                                 const kdkl_options* opts, float* loss, float* row_lse, float* row_kl,
+                                 void* stream) {
+  Plan P;
+  kdkl_status st = make_plan(N, d, V, K, chunk, dtype, opts, &P);
+  if (st != KDKL_OK) return st;
+  if ((st = check_common(H, W, ids, lg, N, T)) != KDKL_OK) return st;
+  if (!loss || (N > 0 && (!row_lse || !row_kl))) return KDKL_ERR_NULL;
+  // row_kl is the caller's, so the forward needs its workspace up to the
+  // per-row KL scratch (the last region); where the library chooses the
+  // group size, take fewer chunks per group until that fits the array
+  kdkl_options o = opts ? *opts : kdkl_options{};
+  if (o.chunks_per_group == 0) {
+    for (int bg = P.bg; bg > 1 && P.f_rowkl > (size_t)KDKL_NOALLOC_SCRATCH_BYTES;) {
+      bg /= 2;
+      o.chunks_per_group = bg;
+      if ((st = make_plan(N, d, V, K, chunk, dtype, &o, &P)) != KDKL_OK) return st;
+    }
+  }
+  if (P.f_rowkl > (size_t)KDKL_NOALLOC_SCRATCH_BYTES) return KDKL_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  void* ws = nullptr;
+  hipError_t e = scratch_address(s, &ws);
+  if (e == hipSuccess) e = forward_launches(P, H, W, ids, lg, T, loss, row_lse, row_kl, (char*)ws, s);
   return e == hipSuccess ? KDKL_OK : KDKL_ERR_HIP;
 }
 

@@ -196,6 +196,32 @@ kdkl_status kdkl_forward(const void* H, const void* W,
                          float* loss, float* row_lse, float* row_kl,
                          void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- allocation-free forward ------------------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving or evaluation loops, harnesses that forbid
+ * allocation. kdkl_forward_noalloc computes what kdkl_forward computes (the
+ * same arguments and outputs, bit for bit equal results) without a workspace
+ * argument: its scratch is a static device array of
+ * KDKL_NOALLOC_SCRATCH_BYTES that each GPU the library runs on holds from
+ * the library's load until the process ends. Its address is looked up on
+ * the first call on each device (no allocation). row_kl is required (not
+ * NULL). Where the library chooses the blocking (opts NULL or
+ * chunks_per_group 0), it takes fewer chunks per launch until the forward's
+ * scratch fits the array; sizes whose scratch does not fit even one chunk at
+ * a time (or at the chunks per group the options fix) return
+ * KDKL_ERR_WORKSPACE before any HIP call. Every call on one GPU uses that
+ * GPU's one array, which keeps the last call's contents (the forward clears
+ * nothing it needs: every region is written before it is read): calls that
+ * overlap on one GPU, from several streams or threads, race and must be
+ * serialised by the caller. The call allocates nothing: no hipMalloc,
+ * hipFree or allocating library routine. */
+#define KDKL_NOALLOC_SCRATCH_BYTES (64u << 20)
+kdkl_status kdkl_forward_noalloc(const void* H, const void* W,
+                                 const int32_t* topk_ids, const float* topk_logits,
+                                 int64_t N, int64_t d, int64_t V, int32_t K,
+                                 float T, int64_t chunk, int dtype, const kdkl_options* opts,
+                                 float* loss, float* row_lse, float* row_kl, void* stream);
+
 /* Backward pass: recomputes each slice's logits and writes
  *   dH [N, d] in the storage dtype, dW [V, d] fp32.
  * row_lse is the forward's output for the same inputs and options. grad_loss is a device
@@ -298,8 +324,9 @@ kdkl_status kdkl_check_ids(const int32_t* topk_ids, int64_t N, int32_t K, int64_
  * per kernel name, the launch count, the summed event time and the summed
  * algorithmic work (flop and HBM bytes by the formulas the library states for
  * each kernel). The timing table is the library's only process-wide mutable
- * state: one table for the process, guarded by a lock (a compute call on
- * another thread while profiling is switched on or off is timed or not,
+ * state besides kdkl_forward_noalloc's scratch (and its per-device address,
+ * set once): one table for the process, guarded by a lock (a compute call
+ * on another thread while profiling is switched on or off is timed or not,
  * never torn). It creates HIP events but allocates no device buffers. */
 typedef struct {
   char name[48];

@@ -488,3 +488,58 @@ def test_library_reads_no_environment(lib):
     out = subprocess.run(["nm", "-D", "--undefined-only", L.LIB_PATH], capture_output=True, text=True)
     assert out.returncode == 0
     assert "getenv" not in out.stdout
+
+
+# --- allocation-free forward ------------------------------------------------------
+
+def fna(lib, **kw):
+    a = dict(H=FAKE, W=FAKE, ids=FAKE, lg=FAKE, N=64, d=64, V=1000, K=8, T=1.0, chunk=16,
+             dt=L.KDKL_BF16, o=None, loss=FAKE, lse=FAKE, kl=FAKE, stream=None)
+    a.update(kw)
+    return lib.kdkl_forward_noalloc(a["H"], a["W"], a["ids"], a["lg"], a["N"], a["d"], a["V"], a["K"],
+                                    a["T"], a["chunk"], a["dt"], a["o"], a["loss"], a["lse"], a["kl"],
+                                    a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), NULL),
+    (dict(H=None), NULL),
+    (dict(kl=None), NULL),       # the per-row KL is the caller's: no scratch grows with N
+    (dict(lse=None), NULL),
+    (dict(loss=None), NULL),
+    (dict(T=0.0), VALUE),
+    (dict(d=60), SHAPE),
+    (dict(dt=9), DTYPE),
+    (dict(H=FAKE + 8), ALIGN),
+    (dict(o=opts(vocab_slices=-1)), OPTION),
+    # one chunk of 8192 positions over gpt-oss's vocabulary needs 8192 x 524
+    # vocabulary tiles x 16 bytes of split partials alone: more than the array
+    (dict(N=8192, d=2880, V=201088, K=100, chunk=8192), WORKSPACE),
+    # the options fix four chunks of 2048 per launch: 84 MB of scratch
+    (dict(N=32768, d=2880, V=201088, K=100, chunk=2048, o=opts(chunks_per_group=4)), WORKSPACE),
+])
+def test_forward_noalloc_rejects_before_any_hip_call(lib, kw, status):
+    assert fna(lib, **kw) == status
+
+
+def test_forward_noalloc_scratch_is_modest():
+    # the static array is 64 MiB per GPU; the library's default forward
+    # blocking at the gpt-oss-like 32K and 256K workloads needs more, and the
+    # allocation-free entry point halves the chunks per launch to fit
+    assert L.NOALLOC_SCRATCH_BYTES == 64 << 20
+    lib = L.load()
+    for sizes in ((32768, 2880, 201088, 100, 2048), (262144, 2880, 201088, 100, 4096)):
+        full = plan(lib, *sizes, L.KDKL_BF16)
+        assert full.fwd_bytes > L.NOALLOC_SCRATCH_BYTES
+        half = plan(lib, *sizes, L.KDKL_BF16, opts(chunks_per_group=full.chunks_per_group // 2))
+        one = plan(lib, *sizes, L.KDKL_BF16, opts(chunks_per_group=1))
+        assert one.fwd_bytes - sizes[0] * 4 < L.NOALLOC_SCRATCH_BYTES
+        assert half.fwd_bytes < full.fwd_bytes
+
+
+def test_library_never_allocates_device_memory():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", L.LIB_PATH], capture_output=True, text=True)
+    assert out.returncode == 0
+    for sym in ("hipMalloc", "hipFree", "hipMallocAsync", "hipExtMallocWithFlags", "hipHostMalloc"):
+        assert sym not in out.stdout, sym
