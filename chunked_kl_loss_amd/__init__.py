@@ -17,7 +17,8 @@ from typing import Optional, Tuple
 
 import torch
 
-from ._lib import KDKL_BF16, KDKL_F32, KdklError, KernelStat, Options, Plan, check, load as _load
+from ._lib import (KDKL_BF16, KDKL_F32, KDKL_LOSS_JSD, KDKL_LOSS_KL, KdklError, KernelStat, Options, Plan,
+                   check, load as _load)
 
 __all__ = [
     "workspace_size",

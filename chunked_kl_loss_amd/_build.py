@@ -7,7 +7,8 @@ from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "libkdkl.so")
-SOURCES = ["csrc/kdkl_api.hip", "csrc/kdkl_kernels.hip", "csrc/kdkl_logits.hip", "csrc/kdkl_check.hip"]
+SOURCES = ["csrc/kdkl_api.hip", "csrc/kdkl_kernels.hip", "csrc/kdkl_logits.hip", "csrc/kdkl_check.hip",
+           "csrc/kdkl_jsd.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

@@ -20,6 +20,7 @@ STATUS = {
 ABI_VERSION = 2
 NOALLOC_SCRATCH_BYTES = 64 << 20  # KDKL_NOALLOC_SCRATCH_BYTES
 KDKL_LOSS_KL = 0
+KDKL_LOSS_JSD = 1
 
 
 class KdklError(RuntimeError):

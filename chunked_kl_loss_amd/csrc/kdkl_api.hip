@@ -22,7 +22,8 @@ const char* kernel_name(int id) {
       "teacher_prep", "fwd_gemm_lse", "split_merge", "loss_reduce", "transpose_w",
       "transpose_h",  "dz_gemm",      "dh_gemm",     "dh_reduce",   "dw_gemm",
       "logits_fwd",   "logits_bwd",   "grad_scale",  "dense_gemm",  "dense_student",
-      "dense_teacher", "dense_kl",    "dense_grad"};
+      "dense_teacher", "dense_kl",    "dense_grad",  "gather_logits", "jsd_merge",
+      "jsd_prep"};
   return (id >= 0 && id < K_COUNT) ? names[id] : "?";
 }
 
@@ -108,10 +109,13 @@ struct Plan {
   bool fast;       // bf16 main loop: reads W, H and dZ in place (no transposes)
   bool wt;         // the dH product reads W^T written once per backward call (else W in place)
   int dtile;       // N-tile width of the dH and dW products (hidden-size axis)
+  int loss;        // kdkl_loss
+  float beta;      // the loss's parameter (JSD)
   // offsets into the forward workspace
-  size_t f_ent, f_erow, f_keep, f_tstart, f_part, f_rowkl, f_bytes;
+  size_t f_ent, f_erow, f_keep, f_tstart, f_part, f_sk, f_rowkl, f_bytes;
   // offsets into the backward workspace
-  size_t b_ent, b_erow, b_keep, b_scale, b_tstart, b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart, b_dhacc, b_bytes;
+  size_t b_ent, b_erow, b_keep, b_scale, b_tstart, b_sk, b_rowcoef, b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart,
+      b_dhacc, b_bytes;
 };
 
 // The dH product on the bf16 main loop reads either a W^T copy written once
@@ -182,7 +186,8 @@ constexpr int kMaxChunksPerGroup = 64;
 
 static kdkl_status check_options(const kdkl_options* o) {
   if (o == nullptr) return KDKL_OK;
-  if (o->loss != KDKL_LOSS_KL) return KDKL_ERR_OPTION;
+  if (o->loss != KDKL_LOSS_KL && o->loss != KDKL_LOSS_JSD) return KDKL_ERR_OPTION;
+  if (o->loss == KDKL_LOSS_JSD && !(o->beta > 0.f && o->beta < 1.f)) return KDKL_ERR_OPTION;
   if (o->chunks_per_group < 0 || o->chunks_per_group > kMaxChunksPerGroup) return KDKL_ERR_OPTION;
   if (o->vocab_slices < 0 || o->vocab_slices > kMaxVocabSlices) return KDKL_ERR_OPTION;
   if (o->dh_w_in_place < 0 || o->dh_w_in_place > 2) return KDKL_ERR_OPTION;
@@ -216,6 +221,8 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   kdkl_status ost = check_options(opts);
   if (ost != KDKL_OK) return ost;
   const kdkl_options o = opts ? *opts : kdkl_options{};
+  P->loss = o.loss;
+  P->beta = o.loss == KDKL_LOSS_JSD ? o.beta : 0.f;
   if (o.chunks_per_group > 0) {
     // more than one chunk per launch needs the bf16 main loop, whose 32-bit
     // load offsets must still cover the group's operands
@@ -272,6 +279,11 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   ok &= region(&cur, t1, &P->f_tstart);
   ok &= mul_ok(P->Cg, P->n_vt, &t2) && mul_ok(t2, 16, &t2);
   ok &= region(&cur, t2, &P->f_part);
+  // the JSD's student logits at the sorted teacher entries [Cg, K]
+  int64_t sk = 0;
+  if (P->loss == KDKL_LOSS_JSD) ok &= mul_ok(P->Cg, K, &sk) && mul_ok(sk, 4, &sk);
+  P->f_sk = 0;
+  if (sk) ok &= region(&cur, sk, &P->f_sk);
   ok &= region(&cur, (N > 0 ? N : 1) * 4, &P->f_rowkl);
   P->f_bytes = cur;
 
@@ -283,6 +295,8 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   ok &= region(&cur, P->Cg * 4, &P->b_erow) && region(&cur, P->Cg * 4, &P->b_keep);
   ok &= region(&cur, 16, &P->b_scale);
   ok &= region(&cur, g1, &P->b_tstart);
+  P->b_sk = P->b_rowcoef = 0;
+  if (sk) ok &= region(&cur, sk, &P->b_sk) && region(&cur, P->Cg * 4, &P->b_rowcoef);
   int64_t wt, ht, dz, dhp;
   ok &= mul_ok(d, P->Vp, &wt) && mul_ok(wt, P->es, &wt);
   ok &= mul_ok(d, P->Cg, &ht) && mul_ok(ht, P->es, &ht);
@@ -350,6 +364,18 @@ static GemmArgs projection_args(const Plan& P, const void* H, const void* W, flo
   g.Vp = P.Vp;
   g.a_layout = g.b_layout = LAYOUT_KC;
   return g;
+}
+
+static JsdArgs jsd_args(const Plan& P, const void* H, const void* W, float T, int64_t r0, int rows, char* ws,
+                        size_t o_ent, size_t o_sk, size_t o_keep) {
+  JsdArgs j;
+  memset(&j, 0, sizeof(j));
+  j.H = H; j.W = W; j.d = P.d; j.V = P.V; j.r0 = r0; j.rows = rows; j.K = (int)P.K;
+  j.inv_T = 1.0f / T; j.beta = P.beta;
+  j.log_beta = (float)log((double)P.beta);
+  j.log_omb = (float)log1p(-(double)P.beta);
+  j.ent = (int2*)(ws + o_ent); j.sk = (float*)(ws + o_sk); j.keep = (const float*)(ws + o_keep);
+  return j;
 }
 
 }  // namespace kdkl
@@ -427,6 +453,18 @@ static hipError_t forward_launches(const Plan& P, const void* H, const void* W, 
     const double by = ((double)V + rows) * d * P.es + (double)rows * P.n_vt * 16.0;
     e = timed(K_FWD_GEMM, fl, by, s, [&] { return launch_gemm(P.dtype, EPI_FWD, g, s); });
     if (e != hipSuccess) break;
+    if (P.loss == KDKL_LOSS_JSD) {
+      // the student's logits at the teacher entries, then lse and JSD per row
+      JsdArgs j = jsd_args(P, H, W, T, r0, rows, ws, P.f_ent, P.f_sk, P.f_keep);
+      j.part = (const float4*)(ws + P.f_part); j.n_vt = (int)P.n_vt;
+      j.row_lse = row_lse + r0; j.row_kl = kl + r0;
+      e = timed(K_GATHER_LOGITS, 2.0 * rows * P.K * d, (double)rows * P.K * (d * P.es + 12.0), s,
+                [&] { return launch_gather_logits(P.dtype, j, s); });
+      if (e == hipSuccess)
+        e = timed(K_JSD_MERGE, 0.0, (double)rows * (P.n_vt * 16.0 + P.K * 12.0), s,
+                  [&] { return launch_jsd_merge(j, s); });
+      continue;
+    }
     MergeArgs m;
     m.part = (const float4*)(ws + P.f_part); m.n_vt = (int)P.n_vt; m.rows = rows;
     m.erow = (const float*)(ws + P.f_erow); m.keep = (const float*)(ws + P.f_keep);
@@ -634,6 +672,18 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
     e = timed(K_TRANSPOSE_H, 0.0, 2.0 * (double)rows * d * P.es, s, [&] {
       return launch_transpose((int)P.es, Hg, rows, d, d, ws + P.b_ht, rows_pad, P.Cg, s);
     });
+    if (e == hipSuccess && P.loss == KDKL_LOSS_JSD) {
+      // the student's logits at the teacher entries; from them and the
+      // forward's lse, each row's coefficient of q in dZ and the support
+      // corrections (written over the entries' probabilities)
+      JsdArgs j = jsd_args(P, H, W, T, r0, rows, ws, P.b_ent, P.b_sk, P.b_keep);
+      j.row_lse_in = row_lse + r0; j.scale = (const float*)(ws + P.b_scale);
+      j.rowcoef = (float*)(ws + P.b_rowcoef);
+      e = timed(K_GATHER_LOGITS, 2.0 * rows * P.K * d, (double)rows * P.K * (d * P.es + 12.0), s,
+                [&] { return launch_gather_logits(dtype, j, s); });
+      if (e == hipSuccess)
+        e = timed(K_JSD_PREP, 0.0, (double)rows * P.K * 20.0, s, [&] { return launch_jsd_prep(j, s); });
+    }
     for (int part = 0; part < P.n_parts && e == hipSuccess; ++part) {
       // recompute the group's logits over the slice's vocabulary rows and
       // form dZ (token-major; the generic path also writes the
@@ -646,6 +696,7 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
       g.tiles_m = (int)((vlen + P.vt - 1) / P.vt);
       g.Cp = P.Cg; g.Vp = P.vpart;
       g.row_lse = row_lse + r0; g.scale = (const float*)(ws + P.b_scale); g.keep = (const float*)(ws + P.b_keep);
+      g.rowcoef = P.loss == KDKL_LOSS_JSD ? (const float*)(ws + P.b_rowcoef) : nullptr;
       g.dz_cv = ws + P.b_dzcv; g.dz_vc = P.fast ? nullptr : ws + P.b_dzvc;
       const double fl = 2.0 * rows * (double)vlen * d;
       e = timed(K_DZ_GEMM, fl,

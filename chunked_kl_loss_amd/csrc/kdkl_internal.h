@@ -35,6 +35,9 @@ enum KernelId {
   K_DENSE_TEACHER,
   K_DENSE_KL,
   K_DENSE_GRAD,
+  K_GATHER_LOGITS,
+  K_JSD_MERGE,
+  K_JSD_PREP,
   K_COUNT
 };
 
@@ -78,6 +81,7 @@ struct GemmArgs {
   const float* row_lse;          // backward: lse of this chunk's rows
   const float* scale;            // backward: device scalar g / (N_kept * T)
   const float* keep;             // backward: keep flags of this chunk's rows [Cp]
+  const float* rowcoef;          // backward, JSD: per-row coefficient of q in dZ [Cp] (else scale[0])
   int raw;                       // EPI_DZ only: store the logits z themselves (dense path)
   void* dz_cv;                   // [Cp, Vp]
   void* dz_vc;                   // [Vp, Cp]
@@ -122,6 +126,31 @@ struct MergeArgs {
   float* row_lse;       // chunk-offset
   float* row_kl;        // chunk-offset
 };
+
+// The generalised Jensen-Shannon divergence (the alternative loss): one
+// wavefront per position of a group of rows [r0, r0 + rows).
+struct JsdArgs {
+  const void* H;         // [N, d] storage dtype (whole problem)
+  const void* W;         // [V, d]
+  int64_t d, V;
+  int64_t r0;
+  int rows, K;
+  float inv_T, beta;
+  float log_beta, log_omb;  // log(beta), log(1 - beta)
+  int2* ent;             // [Cp, K] sorted teacher entries (id, bits of p); jsd_prep writes .y
+  float* sk;             // [Cp, K] s = z / T at each sorted entry
+  const float* keep;     // [Cp]
+  const float4* part;    // forward: split-vocabulary partials [Cp, n_vt]
+  int n_vt;
+  const float* row_lse_in;  // backward: the forward's lse (group-offset)
+  float* row_lse;        // forward outputs (group-offset)
+  float* row_kl;
+  const float* scale;    // backward: device scalar g / (N_kept T)
+  float* rowcoef;        // backward: [Cp] coefficient of q in dZ
+};
+hipError_t launch_gather_logits(int dtype, const JsdArgs& a, hipStream_t s);
+hipError_t launch_jsd_merge(const JsdArgs& a, hipStream_t s);
+hipError_t launch_jsd_prep(const JsdArgs& a, hipStream_t s);
 
 hipError_t launch_teacher(const TeacherArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);

@@ -526,7 +526,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
           v.y = p.tstart[(int64_t)(p.tm0 + t.tm + 1) * p.Cp + col];
           if constexpr (EPI == EPI_DZ) {
             if (p.keep[col] != 0.f) {
-              v.z = __float_as_int(p.scale[0]);
+              v.z = __float_as_int(p.rowcoef ? p.rowcoef[col] : p.scale[0]);
               v.w = __float_as_int(p.row_lse[col] * kLog2e);
             }
           }
@@ -621,7 +621,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
       p.part[(int64_t)col * p.n_vt + t.tm] = make_float4(m, s, g, 0.f);
     }
   } else if constexpr (EPI == EPI_DZ) {
-    // dZ = coef * (softmax(s) - teacher) for the tile, written to the chunk
+    // dZ = coef * (softmax(s) - teacher) for the tile (for the JSD, the
+    // column's own coefficient times softmax(s) minus the support
+    // corrections held where the KL holds the teacher probabilities), written to the chunk
     // buffers token-major (dz_cv [Cp, Vp]) and vocabulary-major (dz_vc [Vp, Cp]).
     // coef = g / (N_kept T); an ignored position's column is zero (its
     // teacher mass is zero as well). In raw mode (the dense path) the tile of

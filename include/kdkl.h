@@ -96,8 +96,26 @@ typedef enum { KDKL_F32 = 0, KDKL_BF16 = 1 } kdkl_dtype;
 
 /* Loss computed by kdkl_forward / kdkl_backward (kdkl_options.loss). */
 typedef enum {
-  KDKL_LOSS_KL = 0 /* forward KL(teacher top-K || student), the pages' loss */
+  KDKL_LOSS_KL = 0, /* forward KL(teacher top-K || student), the pages' loss */
+  KDKL_LOSS_JSD = 1 /* generalised Jensen-Shannon divergence, weight beta */
 } kdkl_loss;
+
+/* The alternative loss, KDKL_LOSS_JSD (a reading: the pages report
+ * ablations on the choice of loss function without naming the losses [P1
+ * "Making knowledge distillation cheap enough to run at scale", section "The
+ * resulting student model"]). With P_i the teacher's renormalised top-K
+ * probabilities placed on the vocabulary (repeated ids add their mass, ids
+ * outside [0, V) have no entry), q_i the student's softmax(s_i) over all V
+ * entries and M_i = beta P_i + (1 - beta) q_i:
+ *     JSD_i = beta KL(P_i || M_i) + (1 - beta) KL(q_i || M_i)
+ *     loss  = (1/N) sum_i JSD_i        (row_kl holds JSD_i)
+ *     dZ_iv = g / (N T) q_iv (g_iv - sum_u q_iu g_iu),
+ *             g_iv = (1 - beta) log(q_iv / M_iv)
+ * beta = 1/2 is the Jensen-Shannon divergence. It runs on the same fused
+ * products (the vocabulary x sequence grid is never built); the student's
+ * logits at the K teacher entries come from K dot products per position.
+ * Ignored positions as for the KL. Only the fused calls (kdkl_forward,
+ * kdkl_forward_noalloc, kdkl_backward) take it. */
 
 /* Per-call options of the fused calls. NULL, or a zero-filled struct, means
  * the defaults: the loss above and the library's own blocking, which it
@@ -123,7 +141,7 @@ typedef enum {
  *                    the bf16 main loop); 2: it reads a W^T copy written once
  *                    per backward call.
  *   beta             parameter of the loss, where it has one (ignored
- *                    otherwise).
+ *                    otherwise): the JSD's weight, 0 < beta < 1.
  *   reserved         must be zero. */
 typedef struct {
   int32_t loss;

@@ -543,3 +543,23 @@ def test_library_never_allocates_device_memory():
     assert out.returncode == 0
     for sym in ("hipMalloc", "hipFree", "hipMallocAsync", "hipExtMallocWithFlags", "hipHostMalloc"):
         assert sym not in out.stdout, sym
+
+
+def test_jsd_options(lib):
+    sizes = (32768, 2880, 201088, 100, 2048)
+    assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=L.KDKL_LOSS_JSD))[0] == OPTION             # beta 0
+    assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=L.KDKL_LOSS_JSD, beta=1.0))[0] == OPTION
+    assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=L.KDKL_LOSS_JSD, beta=float("nan")))[0] == OPTION
+    assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=2, beta=0.5))[0] == OPTION
+    st, f, b = ws(lib, *sizes, L.KDKL_BF16, opts(loss=L.KDKL_LOSS_JSD, beta=0.5))
+    _, f0, b0 = ws(lib, *sizes, L.KDKL_BF16)
+    assert st == OK
+    # the student logits at the sorted teacher entries [group rows, K] fp32 in
+    # both workspaces, and the per-row coefficient of q in the backward's
+    g = plan(lib, *sizes, L.KDKL_BF16).chunks_per_group * 2048
+    assert f - f0 == g * 100 * 4
+    assert b - b0 == g * 100 * 4 + g * 4
+    # beta is ignored by the KL
+    assert ws(lib, *sizes, L.KDKL_BF16, opts(beta=7.0))[1:] == (f0, b0)
+    assert fwd(lib, o=opts(loss=L.KDKL_LOSS_JSD, beta=-0.5)) == OPTION
+    assert bwd(lib, o=opts(loss=L.KDKL_LOSS_JSD, beta=1.5)) == OPTION
