@@ -80,7 +80,7 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4, "launches": 3}))
 
 
-def cpu_baseline(w, x, rows: int):
+def cpu_baseline(w, x, rows: int, loss: str = "kl", beta: float = 0.5):
     """The CPU oracle, as it stands, on the first `rows` positions of the same
     workload (full vocabulary and hidden size)."""
     import oracle
@@ -92,8 +92,12 @@ def cpu_baseline(w, x, rows: int):
         threads = len(os.sched_getaffinity(0))
     H, ids, lg = x["H"][:rows], x["ids"][:rows], x["logits"][:rows]
     t0 = time.perf_counter()
-    oracle.forward(H, x["W"], ids, lg, w.T)
-    oracle.backward(H, x["W"], ids, lg, w.T)
+    if loss == "jsd":
+        oracle.jsd_forward(H, x["W"], ids, lg, w.T, beta)
+        oracle.jsd_backward(H, x["W"], ids, lg, w.T, beta)
+    else:
+        oracle.forward(H, x["W"], ids, lg, w.T)
+        oracle.backward(H, x["W"], ids, lg, w.T)
     dt = time.perf_counter() - t0
     return {"value": rows / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {rows} of {w.N} positions of {w.name} (full V={w.V}, d={w.d}); "
@@ -324,6 +328,10 @@ def main():
     ap.add_argument("--gen-reading", choices=("1based", "0based"), default="1based",
                     help="reading of the workload list's cross-references for the teacher "
                          "generator of the 8K and 256K workloads (1based: uniform ids, N(0, 2))")
+    ap.add_argument("--loss", choices=("kl", "jsd"), default="kl",
+                    help="kl: the pages' forward KL (default); jsd: the generalised Jensen-Shannon "
+                         "divergence (kdkl_options.loss = KDKL_LOSS_JSD)")
+    ap.add_argument("--beta", type=float, default=0.5, help="the JSD's weight beta")
     ap.add_argument("--chunks-per-group", type=int, default=0,
                     help="kdkl_options.chunks_per_group (0: the library's choice)")
     ap.add_argument("--vocab-slices", type=int, default=0,
@@ -373,6 +381,8 @@ def main():
     H, W, ids, lg = (x[k].to(dev) for k in ("H", "W", "ids", "logits"))
     opts = {"chunks_per_group": args.chunks_per_group, "vocab_slices": args.vocab_slices,
             "dh_w_in_place": args.dh_w_in_place}
+    if args.loss == "jsd":
+        opts.update(loss=kd.KDKL_LOSS_JSD, beta=args.beta)
     plan = kd.plan_info(w.N, w.d, w.V, w.K, w.chunk, H.dtype, opts)
     log(f"bench: plan {plan}")
     fb, bb = kd.workspace_size(w.N, w.d, w.V, w.K, w.chunk, H.dtype, opts)
@@ -443,6 +453,7 @@ def main():
                    "T": w.T, "teacher_ids": w.id_dist, "teacher_logit_var": w.logit_var,
                    "gen_reading": args.gen_reading,
                    "seed": args.seed if args.seed is not None else wl.seed_for(w),
+                   "loss": args.loss if args.loss == "kl" else f"jsd(beta={args.beta})",
                    "plan": plan,
                    "parallelism": "single GPU"},
         "mfma_util_pct": round(mfma_pct, 2),
@@ -458,7 +469,7 @@ def main():
     if not args.no_cpu_baseline:
         rows = min(args.cpu_rows, w.N)
         log(f"bench: timing the CPU oracle on {rows} positions")
-        out["cpu_baseline"] = cpu_baseline(w, x, rows)
+        out["cpu_baseline"] = cpu_baseline(w, x, rows, args.loss, args.beta)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -112,9 +112,9 @@ struct Plan {
   int loss;        // kdkl_loss
   float beta;      // the loss's parameter (JSD)
   // offsets into the forward workspace
-  size_t f_ent, f_erow, f_keep, f_tstart, f_part, f_sk, f_rowkl, f_bytes;
+  size_t f_ent, f_erow, f_keep, f_tstart, f_part, f_sk, f_red, f_rowkl, f_bytes;
   // offsets into the backward workspace
-  size_t b_ent, b_erow, b_keep, b_scale, b_tstart, b_sk, b_rowcoef, b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart,
+  size_t b_ent, b_erow, b_keep, b_scale, b_red, b_tstart, b_sk, b_rowcoef, b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart,
       b_dhacc, b_bytes;
 };
 
@@ -284,6 +284,7 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   if (P->loss == KDKL_LOSS_JSD) ok &= mul_ok(P->Cg, K, &sk) && mul_ok(sk, 4, &sk);
   P->f_sk = 0;
   if (sk) ok &= region(&cur, sk, &P->f_sk);
+  ok &= region(&cur, (int64_t)kReduceBytes, &P->f_red);  // the loss's partial sums
   ok &= region(&cur, (N > 0 ? N : 1) * 4, &P->f_rowkl);
   P->f_bytes = cur;
 
@@ -294,6 +295,7 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   ok &= region(&cur, g0, &P->b_ent);
   ok &= region(&cur, P->Cg * 4, &P->b_erow) && region(&cur, P->Cg * 4, &P->b_keep);
   ok &= region(&cur, 16, &P->b_scale);
+  ok &= region(&cur, (int64_t)kReduceBytes, &P->b_red);  // the kept count's partial sums
   ok &= region(&cur, g1, &P->b_tstart);
   P->b_sk = P->b_rowcoef = 0;
   if (sk) ok &= region(&cur, sk, &P->b_sk) && region(&cur, P->Cg * 4, &P->b_rowcoef);
@@ -472,7 +474,8 @@ static hipError_t forward_launches(const Plan& P, const void* H, const void* W, 
     e = timed(K_MERGE, 0.0, (double)rows * P.n_vt * 16.0, s, [&] { return launch_merge(m, s); });
   }
   if (e == hipSuccess)
-    e = timed(K_LOSS, 0.0, (double)N * 8.0, s, [&] { return launch_loss(kl, ids, (int)P.K, N, loss, s); });
+    e = timed(K_LOSS, 0.0, (double)N * 8.0, s,
+              [&] { return launch_loss_ws(kl, ids, (int)P.K, N, ws + P.f_red, loss, s); });
   return e;
 }
 
@@ -614,6 +617,9 @@ static hipError_t part_products(const Plan& P, int dtype, const void* W, char* w
   h.out = (float*)(ws + P.b_dhpart); h.ldo = d; h.Cp = P.Cg;
   const int splits = h.splits;
   // the first slice starts the fp32 sum, the last one writes dH in its dtype
+  // (a read-modify-write of the split partials by each later slice instead
+  // of this pass measured slower: the epilogue's scattered 4-byte reads cost
+  // more per dH launch than the pass)
   const bool first = part == 0, last = part == P.n_parts - 1;
   const float* acc_in = first ? nullptr : (const float*)(ws + P.b_dhacc);
   void* out = last ? (void*)((char*)dH + r0 * d * P.es) : (void*)(ws + P.b_dhacc);
@@ -656,8 +662,9 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
       });
   // g / (N_kept T): the mean runs over the positions that are not ignored
   if (e == hipSuccess)
-    e = timed(K_GRAD_SCALE, 0.0, (double)N * 4.0, s,
-              [&] { return launch_grad_scale(ids, K, N, grad_loss, T, (float*)(ws + P.b_scale), s); });
+    e = timed(K_GRAD_SCALE, 0.0, (double)N * 4.0, s, [&] {
+      return launch_grad_scale_ws(ids, K, N, grad_loss, T, ws + P.b_red, (float*)(ws + P.b_scale), s);
+    });
   const int64_t group = P.bg * P.chunk;
   for (int64_t r0 = 0; r0 < N && e == hipSuccess; r0 += group) {
     const int rows = (int)((N - r0) < group ? (N - r0) : group);

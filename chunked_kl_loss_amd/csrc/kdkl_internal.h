@@ -162,6 +162,14 @@ hipError_t launch_loss(const float* row_kl, const int32_t* ids, int K, int64_t N
 // out[0] = g / (N_kept T) with g = grad[0] (1 if grad is NULL); 0 if none kept.
 hipError_t launch_grad_scale(const int32_t* ids, int K, int64_t N, const float* grad, float T,
                              float* out, hipStream_t s);
+// The same two reductions in two deterministic stages (many workgroups, then
+// one), with kReduceBytes of workspace `part` (16-byte aligned).
+constexpr int kReduceBlocks = 512;
+constexpr size_t kReduceBytes = (size_t)kReduceBlocks * 16;
+hipError_t launch_loss_ws(const float* row_kl, const int32_t* ids, int K, int64_t N, void* part, float* loss,
+                          hipStream_t s);
+hipError_t launch_grad_scale_ws(const int32_t* ids, int K, int64_t N, const float* grad, float T, void* part,
+                                float* out, hipStream_t s);
 // out[c, r] = in[r, c] for r < R, 0 for R <= r < Rp; c < C.
 hipError_t launch_transpose(int elem_bytes, const void* in, int64_t R, int64_t C,
                             int64_t ldi, void* out, int64_t Rp, int64_t ldo,

@@ -54,15 +54,23 @@ __device__ __forceinline__ T shfl_xor(T v, int mask) {
 //   (id, p) pairs sorted by id, and for each vocabulary tile t the number of
 //   sorted ids below t * vt (so a tile's teacher entries are the
 //   contiguous range [tstart[t], tstart[t+1])).
+// A workgroup takes kTeacherRows consecutive positions; their tile starts
+// are staged in LDS and written as one 16-byte vector per tile (the table is
+// position-minor, [n_vt + 1, Cp], for the projection epilogues' reads).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(64) void teacher_prep_kernel(TeacherArgs a) {
-  __shared__ int32_t s_ids[1024];
-  __shared__ int32_t s_sorted[1024];
-  const int row = blockIdx.x;
-  const int lane = threadIdx.x;
+constexpr int kTeacherRows = 8;
+constexpr int kTeacherTiles = 512;  // tile starts staged per pass
+__global__ __launch_bounds__(64 * kTeacherRows) void teacher_prep_kernel(TeacherArgs a) {
+  __shared__ __attribute__((aligned(16))) int32_t s_ids[kTeacherRows][1024];
+  __shared__ int32_t s_sorted[kTeacherRows][1024];
+  __shared__ __attribute__((aligned(16))) uint16_t s_ts[kTeacherTiles][kTeacherRows];
+  const int w = threadIdx.x >> 6;
+  const int row = blockIdx.x * kTeacherRows + w;
+  const int lane = threadIdx.x & 63;
   const int K = a.K;
-  const int64_t g = (a.r0 + row) * (int64_t)K;
-  const bool keep = a.ids[g] != kIgnoreId;  // an ignored row's teacher is never used
+  const bool valid = row < a.rows;  // uniform per wavefront; every thread reaches each barrier
+  const int64_t g = (a.r0 + (valid ? row : 0)) * (int64_t)K;
+  const bool keep = valid && a.ids[g] != kIgnoreId;  // an ignored row's teacher is never used
   constexpr int MAXE = 1024 / 64;
   float av[MAXE];
   int32_t iv[MAXE];
@@ -70,16 +78,21 @@ __global__ __launch_bounds__(64) void teacher_prep_kernel(TeacherArgs a) {
 #pragma unroll
   for (int j = 0; j < MAXE; ++j) {
     const int k = lane + 64 * j;
-    if (k < K) {
+    if (valid && k < K) {
       av[j] = a.logits[g + k] * a.inv_T;
       iv[j] = a.ids[g + k];
-      s_ids[k] = iv[j];
+      s_ids[w][k] = iv[j];
       mx = fmaxf(mx, av[j]);
     } else {
       av[j] = kNegInf;
       iv[j] = 0;
     }
   }
+  // pad the ids to a multiple of four with the largest int, which no rank
+  // comparison below counts (ids are compared as (o < id) or (o == id and
+  // o's position < id's position, which a pad's position never is)
+  const int K4 = (K + 3) & ~3;
+  if (valid && K + lane < K4) s_ids[w][K + lane] = INT32_MAX;
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, shfl_xor(mx, o));
   float se = 0.f;
 #pragma unroll
@@ -88,45 +101,67 @@ __global__ __launch_bounds__(64) void teacher_prep_kernel(TeacherArgs a) {
   for (int o = 32; o > 0; o >>= 1) se += shfl_xor(se, o);
   const float lse = mx + fast_log(se);
   __syncthreads();
-  float ent = 0.f;
+  if (valid) {
+    float ent = 0.f;
 #pragma unroll
-  for (int j = 0; j < MAXE; ++j) {
-    const int k = lane + 64 * j;
-    if (k < K) {
-      const float lp = av[j] - lse;
-      const float p = keep ? fast_exp(lp) : 0.f;
-      ent += p * lp;
-      // rank of (id, k) in ascending id order, ties by position
-      int rank = 0;
-      const int id = iv[j];
-      for (int q = 0; q < K; ++q) {
-        const int o = s_ids[q];
-        rank += (o < id) | ((o == id) & (q < k));
+    for (int j = 0; j < MAXE; ++j) {
+      const int k = lane + 64 * j;
+      if (k < K) {
+        const float lp = av[j] - lse;
+        const float p = keep ? fast_exp(lp) : 0.f;
+        ent += p * lp;
+        // rank of (id, k) in ascending id order, ties by position; the ids
+        // are read four at a time
+        int rank = 0;
+        const int id = iv[j];
+        for (int q = 0; q < K4; q += 4) {
+          const int4 o = *(const int4*)&s_ids[w][q];
+          rank += (o.x < id) | ((o.x == id) & (q < k));
+          rank += (o.y < id) | ((o.y == id) & (q + 1 < k));
+          rank += (o.z < id) | ((o.z == id) & (q + 2 < k));
+          rank += (o.w < id) | ((o.w == id) & (q + 3 < k));
+        }
+        a.ent[(int64_t)row * K + rank] = make_int2(id, __float_as_int(p));
+        s_sorted[w][rank] = id;
       }
-      a.ent[(int64_t)row * K + rank] = make_int2(id, __float_as_int(p));
-      s_sorted[rank] = id;
+    }
+    for (int o = 32; o > 0; o >>= 1) ent += shfl_xor(ent, o);
+    if (lane == 0) {
+      a.erow[row] = keep ? ent : 0.f;
+      a.keep[row] = keep ? 1.f : 0.f;
     }
   }
-  for (int o = 32; o > 0; o >>= 1) ent += shfl_xor(ent, o);
-  if (lane == 0) {
-    a.erow[row] = keep ? ent : 0.f;
-    a.keep[row] = keep ? 1.f : 0.f;
-  }
-  __syncthreads();
-  for (int t = lane; t <= a.n_vt; t += 64) {
-    const int64_t bound = (int64_t)t * a.vt;
-    int lo = 0, hi = K;  // first index with sorted id >= bound
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if ((int64_t)s_sorted[mid] < bound) lo = mid + 1; else hi = mid;
+  // tile starts, kTeacherTiles at a time: each wavefront fills its column of
+  // the staging table, then the workgroup writes one 16-byte row per tile
+  // (positions past the chunk get 0; the epilogues never read them)
+  for (int t0 = 0; t0 <= a.n_vt; t0 += kTeacherTiles) {
+    __syncthreads();
+    for (int tt = lane; tt < kTeacherTiles && t0 + tt <= a.n_vt; tt += 64) {
+      int lo = 0;
+      if (valid) {
+        const int64_t bound = (int64_t)(t0 + tt) * a.vt;
+        int hi = K;  // first index with sorted id >= bound
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if ((int64_t)s_sorted[w][mid] < bound) lo = mid + 1; else hi = mid;
+        }
+      }
+      s_ts[tt][w] = (uint16_t)lo;
     }
-    a.tstart[(int64_t)t * a.Cp + row] = (uint16_t)lo;
+    __syncthreads();
+    for (int tt = threadIdx.x; tt < kTeacherTiles && t0 + tt <= a.n_vt; tt += 64 * kTeacherRows)
+      *(uint4*)(a.tstart + (int64_t)(t0 + tt) * a.Cp + (int64_t)blockIdx.x * kTeacherRows) = *(const uint4*)s_ts[tt];
   }
 }
 
 hipError_t launch_teacher(const TeacherArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(teacher_prep_kernel, dim3(a.rows), dim3(64), 0, s, a);
+  // the 16-byte rows of the tile-start table need a position pitch that
+  // covers whole workgroups of rows
+  if (a.Cp % kTeacherRows != 0 || a.Cp < (int64_t)(a.rows + kTeacherRows - 1) / kTeacherRows * kTeacherRows)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(teacher_prep_kernel, dim3((a.rows + kTeacherRows - 1) / kTeacherRows),
+                     dim3(64 * kTeacherRows), 0, s, a);
   return hipGetLastError();
 }
 
@@ -232,6 +267,84 @@ hipError_t launch_grad_scale(const int32_t* ids, int K, int64_t N, const float* 
                              hipStream_t s) {
   hipLaunchKernelGGL(grad_scale_kernel, dim3(1), dim3(1024), 0, s, ids, K, N, grad, T, out);
   return hipGetLastError();
+}
+
+// The same two reductions in two stages for long inputs: up to
+// kReduceBlocks workgroups each sum one contiguous range of rows (KL in fp64
+// and the kept count) in a fixed order, then one workgroup sums their
+// partials in block order. Deterministic; every row is read by many compute
+// units at once instead of one.
+template <int NT>
+__device__ __forceinline__ void block_sum_pair(double& a, double& c, double* ra, double* rc) {
+  ra[threadIdx.x] = a;
+  rc[threadIdx.x] = c;
+  __syncthreads();
+  for (int w = NT / 2; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      ra[threadIdx.x] += ra[threadIdx.x + w];
+      rc[threadIdx.x] += rc[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  a = ra[0];
+  c = rc[0];
+}
+
+__global__ __launch_bounds__(256) void rows_partial_kernel(const float* row_kl, const int32_t* ids, int K, int64_t N,
+                                                          int64_t per, double2* part) {
+  __shared__ double ra[256], rc[256];
+  const int64_t b0 = (int64_t)blockIdx.x * per;
+  const int64_t b1 = b0 + per < N ? b0 + per : N;
+  double acc = 0.0, kept = 0.0;
+#pragma unroll 4
+  for (int64_t i = b0 + threadIdx.x; i < b1; i += 256) {
+    if (row_kl) acc += (double)row_kl[i];
+    kept += ids[i * K] != kIgnoreId ? 1.0 : 0.0;
+  }
+  block_sum_pair<256>(acc, kept, ra, rc);
+  if (threadIdx.x == 0) part[blockIdx.x] = make_double2(acc, kept);
+}
+
+// mode 0: loss = sum / kept (NaN when nothing is kept); mode 1: the
+// backward's scale g / (kept T), 0 when nothing is kept.
+__global__ __launch_bounds__(kReduceBlocks) void rows_finish_kernel(const double2* part, int nb, int mode,
+                                                                   const float* grad, float T, float* out) {
+  __shared__ double ra[kReduceBlocks], rc[kReduceBlocks];
+  double acc = 0.0, kept = 0.0;
+  if ((int)threadIdx.x < nb) {
+    const double2 v = part[threadIdx.x];
+    acc = v.x;
+    kept = v.y;
+  }
+  block_sum_pair<kReduceBlocks>(acc, kept, ra, rc);
+  if (threadIdx.x != 0) return;
+  if (mode == 0) {
+    out[0] = (float)(acc / kept);
+  } else {
+    const double g = grad ? (double)grad[0] : 1.0;
+    out[0] = kept > 0.0 ? (float)(g / (kept * (double)T)) : 0.f;
+  }
+}
+
+static hipError_t launch_rows_two_stage(const float* row_kl, const int32_t* ids, int K, int64_t N, void* part,
+                                        int mode, const float* grad, float T, float* out, hipStream_t s) {
+  const int64_t per = N > 0 ? (N + kReduceBlocks - 1) / kReduceBlocks : 1;
+  const int nb = N > 0 ? (int)((N + per - 1) / per) : 0;
+  if (nb > 0)
+    hipLaunchKernelGGL(rows_partial_kernel, dim3(nb), dim3(256), 0, s, row_kl, ids, K, N, per, (double2*)part);
+  hipLaunchKernelGGL(rows_finish_kernel, dim3(1), dim3(kReduceBlocks), 0, s, (const double2*)part, nb, mode, grad,
+                     T, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_loss_ws(const float* row_kl, const int32_t* ids, int K, int64_t N, void* part, float* loss,
+                          hipStream_t s) {
+  return launch_rows_two_stage(row_kl, ids, K, N, part, 0, nullptr, 1.f, loss, s);
+}
+
+hipError_t launch_grad_scale_ws(const int32_t* ids, int K, int64_t N, const float* grad, float T, void* part,
+                                float* out, hipStream_t s) {
+  return launch_rows_two_stage(nullptr, ids, K, N, part, 1, grad, T, out, s);
 }
 
 // ---------------------------------------------------------------------------
