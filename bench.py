@@ -39,7 +39,7 @@ def log(*a):
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("kdkl_kernels.hip", "kdkl_logits.hip", "kdkl_api.hip", "kdkl_internal.h"):
+    for f in ("kdkl_kernels.hip", "kdkl_logits.hip", "kdkl_jsd.hip", "kdkl_api.hip", "kdkl_internal.h"):
         with open(os.path.join(ROOT, "chunked_kl_loss_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
