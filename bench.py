@@ -389,7 +389,7 @@ def main():
     ws_f = torch.empty(fb, dtype=torch.uint8, device=dev)
     ws_b = torch.empty(bb, dtype=torch.uint8, device=dev)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
-    row_lse = torch.empty(w.N, dtype=torch.float32, device=dev)
+    row_lse = torch.empty(kd.saved_shape(w.N, opts), dtype=torch.float32, device=dev)
     dH = torch.empty_like(H)
     dW = torch.empty((w.V, w.d), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)

@@ -22,6 +22,7 @@ from ._lib import (KDKL_BF16, KDKL_F32, KDKL_LOSS_JSD, KDKL_LOSS_KL, KdklError, 
 
 __all__ = [
     "workspace_size",
+    "saved_shape",
     "plan_info",
     "kdkl_forward",
     "kdkl_backward",
@@ -94,6 +95,15 @@ def _options(options):
     return C.byref(o)
 
 
+def saved_shape(N: int, options=None) -> Tuple[int, ...]:
+    """Shape of the per-position state the forward saves for the backward
+    (``row_lse``): [N] for the KL, [2, N] for the JSD (logsumexp, then
+    sum_v q_v g_v)."""
+    if options is not None and int(options.get("loss", KDKL_LOSS_KL)) == KDKL_LOSS_JSD:
+        return (2, N)
+    return (N,)
+
+
 def workspace_size(N: int, d: int, V: int, K: int, chunk: int, dtype: torch.dtype,
                    options=None) -> Tuple[int, int]:
     """(forward bytes, backward bytes) of device workspace."""
@@ -134,11 +144,11 @@ def kdkl_forward(H, W, ids, logits, T: float, chunk: int, *, loss=None, row_lse=
     if loss is None:
         loss = torch.empty(1, dtype=torch.float32, device=dev)
     if row_lse is None:
-        row_lse = torch.empty(N, dtype=torch.float32, device=dev)
+        row_lse = torch.empty(saved_shape(N, options), dtype=torch.float32, device=dev)
     if row_kl is None and want_row_kl:
         row_kl = torch.empty(N, dtype=torch.float32, device=dev)
     _want(loss, (1,), torch.float32, dev, "loss")
-    _want(row_lse, (N,), torch.float32, dev, "row_lse")
+    _want(row_lse, saved_shape(N, options), torch.float32, dev, "row_lse")
     if row_kl is not None:
         _want(row_kl, (N,), torch.float32, dev, "row_kl")
     fb, _ = workspace_size(N, d, V, K, chunk, H.dtype, options)
@@ -167,7 +177,7 @@ def kdkl_backward(H, W, ids, logits, T: float, chunk: int, row_lse, grad_loss=No
         dW = torch.empty((V, d), dtype=torch.float32, device=dev)
     if grad_loss is not None and grad_loss.dtype != torch.float32:
         raise TypeError("grad_loss must be float32")
-    _want(row_lse, (N,), torch.float32, dev, "row_lse")
+    _want(row_lse, saved_shape(N, options), torch.float32, dev, "row_lse")
     _want(dH, tuple(H.shape), H.dtype, dev, "dH")
     _want(dW, (V, d), torch.float32, dev, "dW")
     if grad_loss is not None:
@@ -192,7 +202,7 @@ def kdkl_forward_noalloc(H, W, ids, logits, T: float, chunk: int, *, loss, row_l
     N, d, V, K = _check_shapes(H, W, ids, logits)
     dev = H.device
     _want(loss, (1,), torch.float32, dev, "loss")
-    _want(row_lse, (N,), torch.float32, dev, "row_lse")
+    _want(row_lse, saved_shape(N, options), torch.float32, dev, "row_lse")
     _want(row_kl, (N,), torch.float32, dev, "row_kl")
     check(_load().kdkl_forward_noalloc(_ptr(H), _ptr(W), _ptr(ids), _ptr(logits), N, d, V, K,
                                       float(T), chunk, _dtype_code(H), _options(options), _ptr(loss),

@@ -22,8 +22,7 @@ const char* kernel_name(int id) {
       "teacher_prep", "fwd_gemm_lse", "split_merge", "loss_reduce", "transpose_w",
       "transpose_h",  "dz_gemm",      "dh_gemm",     "dh_reduce",   "dw_gemm",
       "logits_fwd",   "logits_bwd",   "grad_scale",  "dense_gemm",  "dense_student",
-      "dense_teacher", "dense_kl",    "dense_grad",  "gather_logits", "jsd_merge",
-      "jsd_prep"};
+      "dense_teacher", "dense_kl",    "dense_grad",  "jsd_merge",     "jsd_prep"};
   return (id >= 0 && id < K_COUNT) ? names[id] : "?";
 }
 
@@ -114,7 +113,7 @@ struct Plan {
   // offsets into the forward workspace
   size_t f_ent, f_erow, f_keep, f_tstart, f_part, f_sk, f_red, f_rowkl, f_bytes;
   // offsets into the backward workspace
-  size_t b_ent, b_erow, b_keep, b_scale, b_red, b_tstart, b_sk, b_rowcoef, b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart,
+  size_t b_ent, b_erow, b_keep, b_scale, b_red, b_tstart, b_rowcoef, b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart,
       b_dhacc, b_bytes;
 };
 
@@ -297,8 +296,8 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   ok &= region(&cur, 16, &P->b_scale);
   ok &= region(&cur, (int64_t)kReduceBytes, &P->b_red);  // the kept count's partial sums
   ok &= region(&cur, g1, &P->b_tstart);
-  P->b_sk = P->b_rowcoef = 0;
-  if (sk) ok &= region(&cur, sk, &P->b_sk) && region(&cur, P->Cg * 4, &P->b_rowcoef);
+  P->b_rowcoef = 0;
+  if (P->loss == KDKL_LOSS_JSD) ok &= region(&cur, P->Cg * 4, &P->b_rowcoef);
   int64_t wt, ht, dz, dhp;
   ok &= mul_ok(d, P->Vp, &wt) && mul_ok(wt, P->es, &wt);
   ok &= mul_ok(d, P->Cg, &ht) && mul_ok(ht, P->es, &ht);
@@ -368,15 +367,13 @@ static GemmArgs projection_args(const Plan& P, const void* H, const void* W, flo
   return g;
 }
 
-static JsdArgs jsd_args(const Plan& P, const void* H, const void* W, float T, int64_t r0, int rows, char* ws,
-                        size_t o_ent, size_t o_sk, size_t o_keep) {
+static JsdArgs jsd_args(const Plan& P, int rows, char* ws, size_t o_ent, size_t o_keep) {
   JsdArgs j;
   memset(&j, 0, sizeof(j));
-  j.H = H; j.W = W; j.d = P.d; j.V = P.V; j.r0 = r0; j.rows = rows; j.K = (int)P.K;
-  j.inv_T = 1.0f / T; j.beta = P.beta;
+  j.V = P.V; j.rows = rows; j.K = (int)P.K; j.beta = P.beta;
   j.log_beta = (float)log((double)P.beta);
   j.log_omb = (float)log1p(-(double)P.beta);
-  j.ent = (int2*)(ws + o_ent); j.sk = (float*)(ws + o_sk); j.keep = (const float*)(ws + o_keep);
+  j.ent = (int2*)(ws + o_ent); j.keep = (const float*)(ws + o_keep);
   return j;
 }
 
@@ -451,20 +448,22 @@ static hipError_t forward_launches(const Plan& P, const void* H, const void* W, 
     GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.f_ent, P.f_tstart);
     g.Cp = P.Cg;
     g.part = (float4*)(ws + P.f_part);
+    // the JSD needs s at each teacher entry: the epilogue keeps it as it
+    // meets the entry
+    g.sk = P.loss == KDKL_LOSS_JSD ? (float*)(ws + P.f_sk) : nullptr;
     const double fl = 2.0 * rows * (double)V * d;
     const double by = ((double)V + rows) * d * P.es + (double)rows * P.n_vt * 16.0;
     e = timed(K_FWD_GEMM, fl, by, s, [&] { return launch_gemm(P.dtype, EPI_FWD, g, s); });
     if (e != hipSuccess) break;
     if (P.loss == KDKL_LOSS_JSD) {
-      // the student's logits at the teacher entries, then lse and JSD per row
-      JsdArgs j = jsd_args(P, H, W, T, r0, rows, ws, P.f_ent, P.f_sk, P.f_keep);
+      // lse, JSD and gbar per row from the partials and the kept student
+      // logits; gbar is saved after the N logsumexps for the backward
+      JsdArgs j = jsd_args(P, rows, ws, P.f_ent, P.f_keep);
+      j.sk = (const float*)(ws + P.f_sk);
       j.part = (const float4*)(ws + P.f_part); j.n_vt = (int)P.n_vt;
-      j.row_lse = row_lse + r0; j.row_kl = kl + r0;
-      e = timed(K_GATHER_LOGITS, 2.0 * rows * P.K * d, (double)rows * P.K * (d * P.es + 12.0), s,
-                [&] { return launch_gather_logits(P.dtype, j, s); });
-      if (e == hipSuccess)
-        e = timed(K_JSD_MERGE, 0.0, (double)rows * (P.n_vt * 16.0 + P.K * 12.0), s,
-                  [&] { return launch_jsd_merge(j, s); });
+      j.row_lse = row_lse + r0; j.row_kl = kl + r0; j.row_gbar = row_lse + N + r0;
+      e = timed(K_JSD_MERGE, 0.0, (double)rows * (P.n_vt * 16.0 + P.K * 12.0), s,
+                [&] { return launch_jsd_merge(j, s); });
       continue;
     }
     MergeArgs m;
@@ -680,16 +679,12 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
       return launch_transpose((int)P.es, Hg, rows, d, d, ws + P.b_ht, rows_pad, P.Cg, s);
     });
     if (e == hipSuccess && P.loss == KDKL_LOSS_JSD) {
-      // the student's logits at the teacher entries; from them and the
-      // forward's lse, each row's coefficient of q in dZ and the support
-      // corrections (written over the entries' probabilities)
-      JsdArgs j = jsd_args(P, H, W, T, r0, rows, ws, P.b_ent, P.b_sk, P.b_keep);
-      j.row_lse_in = row_lse + r0; j.scale = (const float*)(ws + P.b_scale);
+      // from the forward's gbar, each row's coefficient of q in dZ; the
+      // teacher mass of each distinct id over its first entry
+      JsdArgs j = jsd_args(P, rows, ws, P.b_ent, P.b_keep);
+      j.row_gbar_in = row_lse + N + r0; j.scale = (const float*)(ws + P.b_scale);
       j.rowcoef = (float*)(ws + P.b_rowcoef);
-      e = timed(K_GATHER_LOGITS, 2.0 * rows * P.K * d, (double)rows * P.K * (d * P.es + 12.0), s,
-                [&] { return launch_gather_logits(dtype, j, s); });
-      if (e == hipSuccess)
-        e = timed(K_JSD_PREP, 0.0, (double)rows * P.K * 20.0, s, [&] { return launch_jsd_prep(j, s); });
+      e = timed(K_JSD_PREP, 0.0, (double)rows * (P.K * 16.0 + 8.0), s, [&] { return launch_jsd_prep(j, s); });
     }
     for (int part = 0; part < P.n_parts && e == hipSuccess; ++part) {
       // recompute the group's logits over the slice's vocabulary rows and
@@ -704,6 +699,7 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
       g.Cp = P.Cg; g.Vp = P.vpart;
       g.row_lse = row_lse + r0; g.scale = (const float*)(ws + P.b_scale); g.keep = (const float*)(ws + P.b_keep);
       g.rowcoef = P.loss == KDKL_LOSS_JSD ? (const float*)(ws + P.b_rowcoef) : nullptr;
+      g.beta = P.loss == KDKL_LOSS_JSD ? P.beta : 0.f;
       g.dz_cv = ws + P.b_dzcv; g.dz_vc = P.fast ? nullptr : ws + P.b_dzvc;
       const double fl = 2.0 * rows * (double)vlen * d;
       e = timed(K_DZ_GEMM, fl,

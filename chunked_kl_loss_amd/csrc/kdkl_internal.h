@@ -35,7 +35,6 @@ enum KernelId {
   K_DENSE_TEACHER,
   K_DENSE_KL,
   K_DENSE_GRAD,
-  K_GATHER_LOGITS,
   K_JSD_MERGE,
   K_JSD_PREP,
   K_COUNT
@@ -78,10 +77,12 @@ struct GemmArgs {
   const int2* ent;               // [Cp, K] teacher entries (id, bits of p), ids ascending per row
   const uint16_t* tstart;
   float4* part;                  // forward: [Cp, n_vt] (max, sumexp, gamma, -)
+  float* sk;                     // forward, JSD: s = z / T at each sorted teacher entry [Cp, K] (else NULL)
   const float* row_lse;          // backward: lse of this chunk's rows
   const float* scale;            // backward: device scalar g / (N_kept * T)
   const float* keep;             // backward: keep flags of this chunk's rows [Cp]
   const float* rowcoef;          // backward, JSD: per-row coefficient of q in dZ [Cp] (else scale[0])
+  float beta;                    // backward, JSD: the weight beta (0 for the KL); the entries hold P per id
   int raw;                       // EPI_DZ only: store the logits z themselves (dense path)
   void* dz_cv;                   // [Cp, Vp]
   void* dz_vc;                   // [Vp, Cp]
@@ -128,27 +129,24 @@ struct MergeArgs {
 };
 
 // The generalised Jensen-Shannon divergence (the alternative loss): one
-// wavefront per position of a group of rows [r0, r0 + rows).
+// wavefront per position of a group of rows.
 struct JsdArgs {
-  const void* H;         // [N, d] storage dtype (whole problem)
-  const void* W;         // [V, d]
-  int64_t d, V;
-  int64_t r0;
+  int64_t V;
   int rows, K;
-  float inv_T, beta;
+  float beta;
   float log_beta, log_omb;  // log(beta), log(1 - beta)
   int2* ent;             // [Cp, K] sorted teacher entries (id, bits of p); jsd_prep writes .y
-  float* sk;             // [Cp, K] s = z / T at each sorted entry
+  const float* sk;       // forward: [Cp, K] s = z / T at each sorted entry (from the epilogue)
   const float* keep;     // [Cp]
   const float4* part;    // forward: split-vocabulary partials [Cp, n_vt]
   int n_vt;
-  const float* row_lse_in;  // backward: the forward's lse (group-offset)
-  float* row_lse;        // forward outputs (group-offset)
+  float* row_lse;        // forward outputs (group-offset): logsumexp, JSD, gbar
   float* row_kl;
+  float* row_gbar;
+  const float* row_gbar_in;  // backward: the forward's gbar (group-offset)
   const float* scale;    // backward: device scalar g / (N_kept T)
   float* rowcoef;        // backward: [Cp] coefficient of q in dZ
 };
-hipError_t launch_gather_logits(int dtype, const JsdArgs& a, hipStream_t s);
 hipError_t launch_jsd_merge(const JsdArgs& a, hipStream_t s);
 hipError_t launch_jsd_prep(const JsdArgs& a, hipStream_t s);
 

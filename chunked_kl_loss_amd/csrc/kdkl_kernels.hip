@@ -703,6 +703,9 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
 #pragma unroll
           for (int rr = 0; rr < 16; ++rr) v = (mb * 16 + rr == slot) ? acc[mb][nb][rr] : v;
         gz += __int_as_float(e.y) * v;
+        // the JSD keeps s at each teacher entry (met by exactly this lane of
+        // this tile)
+        if (p.sk) p.sk[(int64_t)col * p.K + h] = v * p.inv_T;
       }
       gz += shfl_xor(gz, 32);
       const float gam = gz * p.inv_T;
@@ -774,7 +777,20 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
         const int2 e = p.ent[(int64_t)col * p.K + h];
         const int slot = hit_slot<G>(e.x - p.v0, p.V, m0, wm, lane);
         if (slot < 0) continue;
-        const float pk = coef * __int_as_float(e.y);
+        float pk = coef * __int_as_float(e.y);
+        if (p.beta > 0.f) {
+          // JSD: the entry holds the teacher mass P of its id (0 on a
+          // repeat); with q = acc / qs here (acc = qs q), the correction is
+          // coef (1 - beta) q log(1 + beta P / ((1 - beta) q))
+          float v = 0.f;
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int rr = 0; rr < 16; ++rr) v = (mb * 16 + rr == slot) ? acc[mb][nb][rr] : v;
+          const float P = __int_as_float(e.y), omb = 1.f - p.beta;
+          const float q = qs > 0.f ? v / qs : 0.f;
+          pk = (q > 0.f && P > 0.f) ? coef * omb * q * log1pf(p.beta * P / (omb * q)) : 0.f;
+        }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll

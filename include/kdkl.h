@@ -112,10 +112,13 @@ typedef enum {
  *     dZ_iv = g / (N T) q_iv (g_iv - sum_u q_iu g_iu),
  *             g_iv = (1 - beta) log(q_iv / M_iv)
  * beta = 1/2 is the Jensen-Shannon divergence. It runs on the same fused
- * products (the vocabulary x sequence grid is never built); the student's
- * logits at the K teacher entries come from K dot products per position.
- * Ignored positions as for the KL. Only the fused calls (kdkl_forward,
- * kdkl_forward_noalloc, kdkl_backward) take it. */
+ * products (the vocabulary x sequence grid is never built): the forward's
+ * projection epilogue keeps the student's logit at each teacher entry, and
+ * the backward forms the support terms in its dZ epilogue from the
+ * recomputed logits. Its saved per-position state is two floats, so
+ * row_lse is [2, N] for this loss: each position's logsumexp, then
+ * sum_v q_iv g_iv. Ignored positions as for the KL. Only the fused calls
+ * (kdkl_forward, kdkl_forward_noalloc, kdkl_backward) take it. */
 
 /* Per-call options of the fused calls. NULL, or a zero-filled struct, means
  * the defaults: the loss above and the library's own blocking, which it
@@ -204,7 +207,8 @@ kdkl_status kdkl_plan_info(int64_t N, int64_t d, int64_t V, int32_t K,
  *   be short); 1 <= K <= min(V, 1024); opts as for kdkl_workspace_size.
  * Outputs (device): loss [1] fp32 (mean KL over kept positions; NaN when
  *   none, e.g. N == 0),
- *   row_lse [N] fp32 = logsumexp_v(s_iv) (keep it for kdkl_backward),
+ *   row_lse [N] fp32 = logsumexp_v(s_iv) (keep it for kdkl_backward; [2, N]
+ *     for KDKL_LOSS_JSD, see above),
  *   row_kl [N] fp32 per-position KL, or NULL if not wanted.
  * Workspace: >= *fwd_bytes from kdkl_workspace_size. */
 kdkl_status kdkl_forward(const void* H, const void* W,

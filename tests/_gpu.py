@@ -29,9 +29,10 @@ def run_gpu(x, T, chunk, g=None, accumulate_dW=False, dW_init=None, stream=None,
     dH, dW = kd.kdkl_backward(d["H"], d["W"], d["ids"], d["logits"], T, chunk, row_lse, gt,
                               dW=dW, accumulate_dW=accumulate_dW, stream=stream, options=options)
     torch.cuda.synchronize()
+    lse = row_lse[0] if row_lse.dim() == 2 else row_lse  # the JSD saves [lse; gbar]
     return {
         "loss": float(loss.item()),
-        "row_lse": row_lse.double().cpu().numpy(),
+        "row_lse": lse.double().cpu().numpy(),
         "row_kl": row_kl.double().cpu().numpy(),
         "dH": dH.double().cpu().numpy(),
         "dW": dW.double().cpu().numpy(),
