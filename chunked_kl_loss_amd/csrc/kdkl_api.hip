@@ -698,13 +698,14 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
       g.tiles_m = (int)((vlen + P.vt - 1) / P.vt);
       g.Cp = P.Cg; g.Vp = P.vpart;
       g.row_lse = row_lse + r0; g.scale = (const float*)(ws + P.b_scale); g.keep = (const float*)(ws + P.b_keep);
-      g.rowcoef = P.loss == KDKL_LOSS_JSD ? (const float*)(ws + P.b_rowcoef) : nullptr;
-      g.beta = P.loss == KDKL_LOSS_JSD ? P.beta : 0.f;
+      const bool jsd = P.loss == KDKL_LOSS_JSD;
+      g.rowcoef = jsd ? (const float*)(ws + P.b_rowcoef) : nullptr;
+      g.beta = jsd ? P.beta : 0.f;
       g.dz_cv = ws + P.b_dzcv; g.dz_vc = P.fast ? nullptr : ws + P.b_dzvc;
       const double fl = 2.0 * rows * (double)vlen * d;
       e = timed(K_DZ_GEMM, fl,
                 ((double)vlen + rows) * d * P.es + (P.fast ? 1.0 : 2.0) * rows * (double)vlen * P.es, s,
-                [&] { return launch_gemm(dtype, EPI_DZ, g, s); });
+                [&] { return launch_gemm(dtype, jsd ? EPI_DZJ : EPI_DZ, g, s); });
       if (e != hipSuccess) break;
       e = part_products(P, dtype, W, ws, r0, rows, part, dH, dW, r0 > 0 || accumulate_dW, s);
     }

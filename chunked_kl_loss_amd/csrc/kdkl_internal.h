@@ -82,7 +82,7 @@ struct GemmArgs {
   const float* scale;            // backward: device scalar g / (N_kept * T)
   const float* keep;             // backward: keep flags of this chunk's rows [Cp]
   const float* rowcoef;          // backward, JSD: per-row coefficient of q in dZ [Cp] (else scale[0])
-  float beta;                    // backward, JSD: the weight beta (0 for the KL); the entries hold P per id
+  float beta;                    // EPI_DZJ: the JSD's weight beta; the entries hold P per id
   int raw;                       // EPI_DZ only: store the logits z themselves (dense path)
   void* dz_cv;                   // [Cp, Vp]
   void* dz_vc;                   // [Vp, Cp]
@@ -186,7 +186,9 @@ hipError_t launch_check_ids(const int32_t* ids, int64_t N, int K, int64_t V, voi
 hipError_t launch_dh_reduce(int dtype, const float* part, int splits, int rows,
                             int64_t d, int64_t Cp, const float* acc_in, void* out, hipStream_t s);
 
-enum Epilogue { EPI_FWD = 0, EPI_DZ = 1, EPI_DH = 2, EPI_DW = 3 };
+// EPI_DZJ: the dZ epilogue of the JSD (support corrections formed at the
+// teacher entries), a kernel of its own so that the KL's is untouched.
+enum Epilogue { EPI_FWD = 0, EPI_DZ = 1, EPI_DH = 2, EPI_DW = 3, EPI_DZJ = 4 };
 // dtype: 0 = fp32, 1 = bf16
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s);
 int gemm_k_step(int dtype);  // elements per k-step of the GEMM main loop

@@ -606,7 +606,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
   constexpr int MB = G::MB, NB = G::NB, NT = G::kThreads;
   constexpr int BM = G::BM, BN = G::BN;
   constexpr int kDzPitch = BM + 8;  // bf16 row pitch of the dZ staging tile
-  static_assert(BM == 256 || EPI == EPI_FWD || EPI == EPI_DZ, "vocabulary-row tiles of dH / dW are 256 high");
+  constexpr bool DZ = EPI == EPI_DZ || EPI == EPI_DZJ;  // the two dZ epilogues
+  static_assert(BM == 256 || EPI == EPI_FWD || DZ, "vocabulary-row tiles of dH / dW are 256 high");
   static_assert(BN == 256 || EPI == EPI_DH || EPI == EPI_DW, "token-axis tiles are 256 wide");
   const int tid = threadIdx.x, lane = tid & 63;
   const int wm = G::wm(), wn = G::wn();
@@ -625,11 +626,11 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
   // below keep no per-column registers (which would spill next to the
   // accumulators).
   constexpr int kRedBytes = G::kWavesM * BN * 3 * 4;
-  constexpr int kStageBytes = (EPI == EPI_DZ && ES == 2) ? 128 * kDzPitch * 2 : 0;
+  constexpr int kStageBytes = (DZ && ES == 2) ? 128 * kDzPitch * 2 : 0;
   constexpr int kInfoOff = ((kRedBytes > kStageBytes ? kRedBytes : kStageBytes) + 255) / 256 * 256;
   static_assert(kInfoOff + BN * 16 <= 128 * 1024, "the column table fits every projection kernel's LDS");
   const int4* info = (const int4*)(smem + kInfoOff);
-  if constexpr (EPI == EPI_FWD || EPI == EPI_DZ) {
+  if constexpr (EPI == EPI_FWD || DZ) {
     if (!p.raw) {
       for (int c = tid; c < BN; c += NT) {
         const int col = n0 + c;
@@ -637,7 +638,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
         if (col < p.N) {
           v.x = p.tstart[(int64_t)(p.tm0 + t.tm) * p.Cp + col];
           v.y = p.tstart[(int64_t)(p.tm0 + t.tm + 1) * p.Cp + col];
-          if constexpr (EPI == EPI_DZ) {
+          if constexpr (DZ) {
             if (p.keep[col] != 0.f) {
               v.z = __float_as_int(p.rowcoef ? p.rowcoef[col] : p.scale[0]);
               v.w = __float_as_int(p.row_lse[col] * kLog2e);
@@ -736,7 +737,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
       }
       p.part[(int64_t)col * p.n_vt + t.tm] = make_float4(m, s, g, 0.f);
     }
-  } else if constexpr (EPI == EPI_DZ) {
+  } else if constexpr (DZ) {
     // dZ = coef * (softmax(s) - teacher) for the tile (for the JSD, the
     // column's own coefficient times softmax(s) minus the support
     // corrections held where the KL holds the teacher probabilities), written to the chunk
@@ -778,7 +779,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
         const int slot = hit_slot<G>(e.x - p.v0, p.V, m0, wm, lane);
         if (slot < 0) continue;
         float pk = coef * __int_as_float(e.y);
-        if (p.beta > 0.f) {
+        if constexpr (EPI == EPI_DZJ) {
           // JSD: the entry holds the teacher mass P of its id (0 on a
           // repeat); with q = acc / qs here (acc = qs q), the correction is
           // coef (1 - beta) q log(1 + beta P / ((1 - beta) q))
@@ -1467,7 +1468,7 @@ int gemm_d_tile(bool fast, int64_t d) {
 
 template <int EPI, int LA, int LB>
 static hipError_t launch_fast(const GemmArgs& a, dim3 grid, hipStream_t s) {
-  if constexpr (EPI == EPI_FWD || EPI == EPI_DZ) {
+  if constexpr (EPI == EPI_FWD || EPI == EPI_DZ || EPI == EPI_DZJ) {
     if (a.bm == 384) {
       // 384 x 256 tiles on a 4 x 2 grid: wavefront tiles of 96 x 128
       using GV = Grid<4, 2, 256, 384>;
@@ -1525,6 +1526,7 @@ hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s) {
   switch (epi) {
     case EPI_FWD: return launch_gemm_e<EPI_FWD>(dtype, a, s);
     case EPI_DZ: return launch_gemm_e<EPI_DZ>(dtype, a, s);
+    case EPI_DZJ: return launch_gemm_e<EPI_DZJ>(dtype, a, s);
     case EPI_DH: return launch_gemm_e<EPI_DH>(dtype, a, s);
     default: return launch_gemm_e<EPI_DW>(dtype, a, s);
   }
