@@ -124,6 +124,71 @@ def cpu_baseline_logits(w, Z_rows, x, rows: int):
                       f"fp64 numpy forward+backward, {dt:.1f} s"}
 
 
+class PowerSampler:
+    """Socket power and gfx clock of the device, sampled in a thread (amdsmi,
+    no HIP) while the timed steps run. The sensor reports a running average
+    that trails the load by about a second, so samples from the first
+    `settle` seconds are dropped."""
+
+    def __init__(self, interval=0.02, settle=1.0):
+        self.interval, self.settle = interval, settle
+        self.samples, self.error, self._stop = [], None, None
+
+    def _handle(self, amdsmi, dev):
+        handles = amdsmi.amdsmi_get_processor_handles()
+        if len(handles) == 1:
+            return handles[0]
+        props = torch.cuda.get_device_properties(dev)
+        bus = getattr(props, "pci_bus_id", None)
+        for h in handles:
+            bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+            if bus is not None and int(bdf.split(":")[1], 16) == bus:
+                return h
+        raise RuntimeError(f"cannot match the device among {len(handles)} amdsmi handles")
+
+    def start(self, dev):
+        import threading
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            h = self._handle(amdsmi, dev)
+        except Exception as e:  # no sensor access: report why, time as usual
+            self.error = repr(e)
+            return
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    pw = amdsmi.amdsmi_get_power_info(h)["current_socket_power"]
+                    clk = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"]
+                    self.samples.append((time.time(), float(pw), float(clk)))
+                except Exception as e:
+                    self.error = repr(e)
+                    return
+                time.sleep(self.interval)
+
+        self._t0 = time.time()
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        self._amdsmi = amdsmi
+
+    def stop(self, ms_per_step):
+        if self._stop is None:
+            return {"error": self.error}
+        self._stop.set()
+        self._thread.join()
+        self._amdsmi.amdsmi_shut_down()
+        kept = [s for s in self.samples if s[0] >= self._t0 + self.settle]
+        if not kept:
+            return {"error": self.error or "no samples after the settling time (time more steps)"}
+        avg_w = sum(s[1] for s in kept) / len(kept)
+        return {"avg_w": round(avg_w, 1), "max_w": max(s[1] for s in kept),
+                "gfx_mhz": round(sum(s[2] for s in kept) / len(kept), 1),
+                "joules_per_step": round(avg_w * ms_per_step / 1e3, 2), "samples": len(kept),
+                "settle_s": self.settle}
+
+
 def kernel_table(kstats, steps):
     kernels = {}
     for name, s in kstats.items():
@@ -340,6 +405,8 @@ def main():
                     help="kdkl_options.dh_w_in_place (0: the library's choice, 1: in place, 2: W^T copy)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured into a HIP graph")
+    ap.add_argument("--power", action="store_true",
+                    help="sample socket power and the gfx clock (amdsmi) over the timed steps (eager only)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -436,8 +503,11 @@ def main():
         kstats = kd.profile_end()
         ksteps = min(args.steps, 3)
     else:
+        sampler = PowerSampler() if args.power else None
         kd.profile_begin()
         torch.cuda.synchronize(dev)
+        if sampler:
+            sampler.start(dev)
         ev0.record(stream)
         for _ in range(args.steps):
             step()
@@ -446,6 +516,7 @@ def main():
         kstats = kd.profile_end()
         ksteps = args.steps
     ms = ev0.elapsed_time(ev1) / args.steps
+    power = sampler.stop(ms) if (args.power and not args.graph) else None
     peak_gib = torch.cuda.max_memory_allocated(dev) / 2**30
     log(f"bench: {ms:.2f} ms/step")
 
@@ -496,6 +567,8 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
     }
+    if power is not None:
+        out["power"] = power
     if not args.no_cpu_baseline:
         rows = min(args.cpu_rows, w.N)
         log(f"bench: timing the CPU oracle on {rows} positions")

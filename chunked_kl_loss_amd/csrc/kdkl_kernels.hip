@@ -1178,6 +1178,21 @@ __device__ __forceinline__ void wait_vmcnt() {
 #ifndef KDKL_EARLY_BARRIER
 #define KDKL_EARLY_BARRIER 1
 #endif
+#ifndef KDKL_FRAG_FENCE
+#define KDKL_FRAG_FENCE 1
+#endif
+// Keeps the fragment reads of the next k-group where the source puts them,
+// ahead of the MFMAs of the current one: left to itself the scheduler sinks
+// them below most of those MFMAs (giving both fragment buffers the same
+// registers), and the next k-group then waits for reads issued one to three
+// MFMAs earlier. Applied where the fragments are double-buffered (dH, dW);
+// the forward and dZ tiles, whose B fragments are single-buffered, spill
+// under it.
+template <bool ON>
+__device__ __forceinline__ void frag_fence() {
+  if constexpr (ON && KDKL_FRAG_FENCE) __builtin_amdgcn_sched_barrier(0);
+}
+
 template <class G, int EPI, int BK, int NSTAGE, int LA, int LB>
 __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArgs p) {
   constexpr int MB = G::MB, NB = G::NB;
@@ -1386,6 +1401,7 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
           load_frags(kt, kk + 1, (kk + 1) & 1, !SB);
         else if (EB && next)
           load_frags(kt + 1, 0, 0, !SB);
+        frag_fence<!SB>();
         if constexpr (SB) {
           // each B fragment is replaced by the next k-group's once its MFMAs
           // are issued (with EB, after the last k-group: the next stage's first)
@@ -1396,10 +1412,12 @@ __global__ __launch_bounds__(G::kThreads, 1) void gemm_bf16_kernel(const GemmArg
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb)
               acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk & 1][mb], fb[0][nb], acc[mb][nb], 0, 0, 0);
+            frag_fence<false>();
             if (kk + 1 < KG)
               fb[0][nb] = frag(LB, sB, wn * G::WN + nb * 32, kk + 1, G::BN);
             else if (EB && next)
               fb[0][nb] = frag(LB, sBn, wn * G::WN + nb * 32, 0, G::BN);
+            frag_fence<false>();
           }
         } else {
 #pragma unroll
