@@ -132,7 +132,7 @@ class PowerSampler:
 
     def __init__(self, interval=0.02, settle=1.0):
         self.interval, self.settle = interval, settle
-        self.samples, self.error, self._stop = [], None, None
+        self.samples, self.error, self._stop, self.limit = [], None, None, None
 
     def _handle(self, amdsmi, dev):
         handles = amdsmi.amdsmi_get_processor_handles()
@@ -160,7 +160,9 @@ class PowerSampler:
         def run():
             while not self._stop.is_set():
                 try:
-                    pw = amdsmi.amdsmi_get_power_info(h)["current_socket_power"]
+                    info = amdsmi.amdsmi_get_power_info(h)
+                    pw = info["current_socket_power"]
+                    self.limit = info.get("power_limit")
                     clk = amdsmi.amdsmi_get_clock_info(h, amdsmi.AmdSmiClkType.GFX)["clk"]
                     self.samples.append((time.time(), float(pw), float(clk)))
                 except Exception as e:
@@ -186,7 +188,7 @@ class PowerSampler:
         return {"avg_w": round(avg_w, 1), "max_w": max(s[1] for s in kept),
                 "gfx_mhz": round(sum(s[2] for s in kept) / len(kept), 1),
                 "joules_per_step": round(avg_w * ms_per_step / 1e3, 2), "samples": len(kept),
-                "settle_s": self.settle}
+                "settle_s": self.settle, "power_limit": self.limit}
 
 
 def kernel_table(kstats, steps):
