@@ -23,4 +23,8 @@ from .kl import (  # noqa: F401
     jsd_forward,
     jsd_backward,
     jsd_loss_and_grads,
+    ALT_LOSSES,
+    alt_forward,
+    alt_backward,
+    alt_loss_and_grads,
 )

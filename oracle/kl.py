@@ -58,6 +58,11 @@ Readings where the pages are silent (temperature on both sides with no T**2
 factor, forward KL direction, mean reduction, duplicate ids add their mass)
 are listed with the rest of the design notes.
 
+Alternative losses on the same distributions (readings: the pages report
+ablations on the choice of loss without naming them [P1, section "The
+resulting student model", last paragraphs]): the generalised Jensen-Shannon
+divergence, the skew KL and the skew reverse KL, in their own section below.
+
 Rows are processed in blocks only to bound memory; rows are independent, so
 the block size does not enter the result except through summation order.
 """
@@ -85,6 +90,10 @@ __all__ = [
     "jsd_forward",
     "jsd_backward",
     "jsd_loss_and_grads",
+    "ALT_LOSSES",
+    "alt_forward",
+    "alt_backward",
+    "alt_loss_and_grads",
 ]
 
 
@@ -479,9 +488,79 @@ def _check_beta(beta: float) -> float:
     return beta
 
 
-def jsd_forward(H, W, ids, logits, T: float, beta: float = 0.5, block: int = 256) -> Dict[str, object]:
-    """Loss, per-row logsumexp of z/T and per-row JSD_beta; fp64."""
-    beta = _check_beta(beta)
+# ---------------------------------------------------------------------------
+# Two more alternative losses of the same kind: the skew KL and the skew
+# reverse KL divergences between the teacher's top-K distribution and the
+# student (readings like the JSD above: the pages name no loss).
+# ---------------------------------------------------------------------------
+# With P_i and q_i as above and a parameter alpha:
+#
+#   SKL_i  = KL(P_i || alpha P_i + (1 - alpha) q_i),        0 <= alpha < 1,
+#   SRKL_i = KL(q_i || alpha q_i + (1 - alpha) P_i),        0 < alpha <= 1.
+#
+# The skew KL at alpha = 0 is the forward KL above (for rows whose teacher
+# ids are all in range). The skew reverse KL stays finite although P_i is
+# zero off the top-K (there its mixture is alpha q_i), and tends to the
+# reverse KL(q_i || P_i) as alpha -> 0 where P_i covers the vocabulary.
+# Since each mixture is at least alpha times the distribution in front,
+# both are at most -log(alpha) per position. The loss is the mean over the
+# kept positions, ignored positions as above. Gradient (derived here), of the
+# JSD's form: d L_i / d s_v = q_v (g_v - gbar_i), gbar_i = sum_v q_v g_v, with
+# g_v the derivative of L_i in q_v:
+#
+#   SKL:  g_v = -(1 - alpha) P_v / M_v                  (0 where P_v = 0),
+#   SRKL: g_v = log(q_v / M_v) + 1 - alpha q_v / M_v    (-log alpha where P_v = 0).
+
+
+def _skl_parts(logq: np.ndarray, P: np.ndarray, alpha: float):
+    """Per row: (SKL, q, g), M = alpha P + (1 - alpha) q in the log domain."""
+    with np.errstate(divide="ignore"):
+        logP = np.log(P)
+    la = math.log(alpha) if alpha > 0.0 else -math.inf
+    logM = np.logaddexp(la + logP, math.log1p(-alpha) + logq)
+    on = P > 0
+    lp = np.where(on, logP, 0.0)
+    loss = np.where(on, P * (lp - logM), 0.0).sum(axis=1)
+    g = np.where(on, -(1.0 - alpha) * np.exp(lp - logM), 0.0)
+    return loss, np.exp(logq), g
+
+
+def _srkl_parts(logq: np.ndarray, P: np.ndarray, alpha: float):
+    """Per row: (SRKL, q, g), M = alpha q + (1 - alpha) P in the log domain
+    (M >= alpha q > 0, so log(q / M) is finite everywhere)."""
+    with np.errstate(divide="ignore"):
+        logP = np.log(P)
+    lb = math.log1p(-alpha) if alpha < 1.0 else -math.inf
+    logM = np.logaddexp(math.log(alpha) + logq, lb + logP)
+    q = np.exp(logq)
+    r = logq - logM  # log(q / M)
+    loss = (q * r).sum(axis=1)
+    g = r + 1.0 - alpha * np.exp(r)
+    return loss, q, g
+
+
+# loss name -> (per-row parts, admissible parameter range as a predicate)
+ALT_LOSSES = {
+    "jsd": (_jsd_parts, lambda a: 0.0 < a < 1.0),
+    "skl": (_skl_parts, lambda a: 0.0 <= a < 1.0),
+    "srkl": (_srkl_parts, lambda a: 0.0 < a <= 1.0),
+}
+
+
+def _check_alt(loss: str, a: float):
+    if loss not in ALT_LOSSES:
+        raise ValueError(f"unknown loss {loss!r}")
+    parts, ok = ALT_LOSSES[loss]
+    a = float(a)
+    if not ok(a):
+        raise ValueError(f"parameter {a} out of range for {loss}")
+    return parts, a
+
+
+def alt_forward(H, W, ids, logits, T: float, loss: str, a: float, block: int = 256) -> Dict[str, object]:
+    """Loss, per-row logsumexp of z/T and per-row value of an alternative
+    loss ("jsd": weight beta = a; "skl", "srkl": alpha = a); fp64."""
+    parts, a = _check_alt(loss, a)
     H = _f64(H)
     W = _f64(W)
     ids = _ids(ids)
@@ -495,18 +574,19 @@ def jsd_forward(H, W, ids, logits, T: float, beta: float = 0.5, block: int = 256
         r1 = min(n_rows, r0 + block)
         logq, lse = student_log_softmax(H[r0:r1], W, T)
         P = _teacher_grid(ids[r0:r1], lg[r0:r1], T, V)
-        row_kl[r0:r1], _, _ = _jsd_parts(logq, P, beta)
+        row_kl[r0:r1], _, _ = parts(logq, P, a)
         row_lse[r0:r1] = lse
     row_kl[~kept] = 0.0
     N = int(kept.sum())  # the mean runs over the kept positions
-    loss = math.fsum(row_kl.tolist()) / N if N else float("nan")
-    return {"loss": loss, "row_lse": row_lse, "row_kl": row_kl}
+    loss_v = math.fsum(row_kl.tolist()) / N if N else float("nan")
+    return {"loss": loss_v, "row_lse": row_lse, "row_kl": row_kl}
 
 
-def jsd_backward(H, W, ids, logits, T: float, beta: float = 0.5, g: float = 1.0,
+def alt_backward(H, W, ids, logits, T: float, loss: str, a: float, g: float = 1.0,
                  block: int = 256) -> Tuple[np.ndarray, np.ndarray]:
-    """Gradients (dH [N, d], dW [V, d]) of ``g * loss`` for JSD_beta; fp64."""
-    beta = _check_beta(beta)
+    """Gradients (dH [N, d], dW [V, d]) of ``g * loss`` for an alternative
+    loss; fp64."""
+    parts, a = _check_alt(loss, a)
     H = _f64(H)
     W = _f64(W)
     ids = _ids(ids)
@@ -522,7 +602,7 @@ def jsd_backward(H, W, ids, logits, T: float, beta: float = 0.5, g: float = 1.0,
         r1 = min(n_rows, r0 + block)
         logq, _ = student_log_softmax(H[r0:r1], W, T)
         P = _teacher_grid(ids[r0:r1], lg[r0:r1], T, V)
-        _, q, gv = _jsd_parts(logq, P, beta)
+        _, q, gv = parts(logq, P, a)
         gbar = (q * gv).sum(axis=1)
         dZ = coef * q * (gv - gbar[:, None])
         dZ[~kept[r0:r1]] = 0.0
@@ -531,8 +611,24 @@ def jsd_backward(H, W, ids, logits, T: float, beta: float = 0.5, g: float = 1.0,
     return dH, dW
 
 
+def alt_loss_and_grads(H, W, ids, logits, T: float, loss: str, a: float, g: float = 1.0,
+                       block: int = 256) -> Dict[str, object]:
+    out = alt_forward(H, W, ids, logits, T, loss, a, block)
+    out["dH"], out["dW"] = alt_backward(H, W, ids, logits, T, loss, a, g, block)
+    return out
+
+
+def jsd_forward(H, W, ids, logits, T: float, beta: float = 0.5, block: int = 256) -> Dict[str, object]:
+    """Loss, per-row logsumexp of z/T and per-row JSD_beta; fp64."""
+    return alt_forward(H, W, ids, logits, T, "jsd", _check_beta(beta), block)
+
+
+def jsd_backward(H, W, ids, logits, T: float, beta: float = 0.5, g: float = 1.0,
+                 block: int = 256) -> Tuple[np.ndarray, np.ndarray]:
+    """Gradients (dH [N, d], dW [V, d]) of ``g * loss`` for JSD_beta; fp64."""
+    return alt_backward(H, W, ids, logits, T, "jsd", _check_beta(beta), g, block)
+
+
 def jsd_loss_and_grads(H, W, ids, logits, T: float, beta: float = 0.5, g: float = 1.0,
                        block: int = 256) -> Dict[str, object]:
-    out = jsd_forward(H, W, ids, logits, T, beta, block)
-    out["dH"], out["dW"] = jsd_backward(H, W, ids, logits, T, beta, g, block)
-    return out
+    return alt_loss_and_grads(H, W, ids, logits, T, "jsd", beta, g, block)

@@ -725,6 +725,205 @@ def pin_jsd_invariants(o):
     _close(mW, rW, 1e-13, what="JSD ignored: dW")
 
 
+# --- the skew KL and skew reverse KL ----------------------------------------
+
+def pin_skl_alpha_zero_is_forward_kl(o):
+    """The skew KL at alpha = 0 is the forward KL pinned above (rows with
+    distinct in-range ids), loss, rows and gradients; near alpha = 1 the
+    mixture is the teacher itself and the loss vanishes."""
+    if not hasattr(o, "alt_forward"):
+        return
+    rng = np.random.default_rng(41)
+    N, d, V, K, T, g = 6, 5, 23, 5, 1.2, 0.8
+    H, W, ids, logits = _rand_problem(rng, N, d, V, K)
+    f = o.forward(H, W, ids, logits, T)
+    s = o.alt_forward(H, W, ids, logits, T, "skl", 0.0)
+    _close(s["row_kl"], f["row_kl"], 1e-12, what="SKL(0) rows vs KL")
+    _close(s["loss"], f["loss"], 1e-12, what="SKL(0) loss vs KL")
+    _close(s["row_lse"], f["row_lse"], 1e-14, what="SKL lse")
+    dH, dW = o.backward(H, W, ids, logits, T, g)
+    sH, sW = o.alt_backward(H, W, ids, logits, T, "skl", 0.0, g)
+    _close(sH, dH, 1e-12, what="SKL(0) dH vs KL dH")
+    _close(sW, dW, 1e-12, what="SKL(0) dW vs KL dW")
+    near = o.alt_forward(H, W, ids, logits, T, "skl", 1.0 - 1e-9)
+    assert np.max(np.abs(near["row_kl"])) < 1e-7, near["row_kl"]
+
+
+def pin_skew_losses_torch_autograd(o):
+    """Both losses through torch (kl_div on the dense grid, P with zeros off
+    the top-K) and their gradients by autograd."""
+    if not hasattr(o, "alt_forward"):
+        return
+    rng = np.random.default_rng(42)
+    N, d, V, K, T, g = 5, 4, 15, 4, 0.9, 1.2
+    H, W, ids, logits = _rand_problem(rng, N, d, V, K)
+    P = np.zeros((N, V))
+    for i in range(N):
+        P[i, ids[i]] = sps.softmax(logits[i] / T)
+    for loss, a in (("skl", 0.3), ("srkl", 0.2)):
+        Ht = torch.tensor(H, requires_grad=True)
+        Wt = torch.tensor(W, requires_grad=True)
+        Pt = torch.tensor(P)
+        q = torch.softmax(Ht @ Wt.T / T, dim=1)
+        if loss == "skl":
+            val = F.kl_div(torch.log(a * Pt + (1 - a) * q), Pt, reduction="sum") / N
+        else:
+            val = F.kl_div(torch.log(a * q + (1 - a) * Pt), q, reduction="sum") / N
+        (g * val).backward()
+        out = o.alt_forward(H, W, ids, logits, T, loss, a)
+        _close(out["loss"], val.item(), 1e-12, what=f"{loss} loss vs kl_div")
+        aH, aW = o.alt_backward(H, W, ids, logits, T, loss, a, g)
+        _close(aH, Ht.grad.numpy(), 1e-11, what=f"{loss} dH vs autograd")
+        _close(aW, Wt.grad.numpy(), 1e-11, what=f"{loss} dW vs autograd")
+
+
+def pin_skew_losses_brute_force_and_finite_differences(o):
+    """Pure-Python loops (math module only) with ids outside [0, V) and a
+    repeated id, over the teacher's support (for the skew reverse KL the
+    entries off it add -log(alpha) times the student's mass there); central
+    differences of the loss for every entry of H and W."""
+    if not hasattr(o, "alt_forward"):
+        return
+    rng = np.random.default_rng(43)
+    N, d, V, K, T, g = 4, 3, 6, 3, 1.4, 0.6
+    H = rng.standard_normal((N, d))
+    W = rng.standard_normal((V, d))
+    ids = np.array([[0, 5, 2], [7, 1, -2], [3, 3, 4], [6, -5, 0]])
+    logits = rng.standard_normal((N, K))
+    for loss, a in (("skl", 0.25), ("srkl", 0.15)):
+        ref = []
+        for i in range(N):
+            t = [logits[i, k] / T for k in range(K)]
+            mt = max(t)
+            zt = sum(math.exp(x - mt) for x in t)
+            p = [math.exp(x - mt) / zt for x in t]
+            s = [sum(H[i, j] * W[v, j] for j in range(d)) / T for v in range(V)]
+            ms = max(s)
+            lse = ms + math.log(sum(math.exp(x - ms) for x in s))
+            support = sorted({int(v) for v in ids[i] if 0 <= v < V})
+            val, qs = 0.0, 0.0
+            for v in support:
+                Pv = sum(p[k] for k in range(K) if ids[i, k] == v)
+                qv = math.exp(s[v] - lse)
+                if loss == "skl":
+                    val += Pv * math.log(Pv / (a * Pv + (1 - a) * qv))
+                else:
+                    val += qv * math.log(qv / (a * qv + (1 - a) * Pv))
+                qs += qv
+            if loss == "srkl":
+                val += -math.log(a) * (1 - qs)
+            ref.append(val)
+        out = o.alt_forward(H, W, ids, logits, T, loss, a)
+        _close(out["row_kl"], ref, 1e-13, what=f"{loss} brute force")
+        dH, dW = o.alt_backward(H, W, ids, logits, T, loss, a, g)
+        h = 1e-6
+
+        def L(Hx, Wx):
+            return g * o.alt_forward(Hx, Wx, ids, logits, T, loss, a)["loss"]
+
+        for X, dX, name in ((H, dH, "dH"), (W, dW, "dW")):
+            fd = np.zeros_like(X)
+            for idx in np.ndindex(X.shape):
+                Xp = X.copy(); Xp[idx] += h
+                Xm = X.copy(); Xm[idx] -= h
+                fd[idx] = (L(Xp, W) - L(Xm, W)) / (2 * h) if X is H else (L(H, Xp) - L(H, Xm)) / (2 * h)
+            _close(dX, fd, 1e-6, what=f"{loss} finite differences {name}")
+
+
+def pin_skew_losses_bounds_and_limits(o):
+    """0 <= value <= -log(alpha) per position (distinct in-range ids); the
+    skew reverse KL equals -log(alpha) when the student puts no mass on the
+    teacher's support, and tends to scipy's reverse KL(q || P) as alpha -> 0
+    when the teacher covers the vocabulary (K = V)."""
+    if not hasattr(o, "alt_forward"):
+        return
+    rng = np.random.default_rng(44)
+    N, d, V, K, T = 7, 5, 19, 6, 1.1
+    H, W, ids, logits = _rand_problem(rng, N, d, V, K, scale=2.0)
+    for loss, a in (("skl", 0.1), ("skl", 0.6), ("srkl", 0.1), ("srkl", 0.6)):
+        r = o.alt_forward(H, W, ids, logits, T, loss, a)["row_kl"]
+        assert np.all(r >= -1e-15) and np.all(r <= -math.log(a) + 1e-15), (loss, a, r)
+    # the student's mass off the teacher's support: one hidden unit, the
+    # support's logits 60 below the rest
+    a = 0.3
+    H1 = np.ones((3, 1))
+    ids1 = np.array([[1, 4], [0, 2], [5, 3]])
+    lg1 = rng.standard_normal((3, 2))
+    for i in range(3):
+        W1 = np.zeros((V, 1))
+        W1[ids1[i]] = -60.0
+        r = o.alt_forward(H1[i:i + 1], W1, ids1[i:i + 1], lg1[i:i + 1], 1.0, "srkl", a)["row_kl"]
+        _close(r, [-math.log(a)], 1e-12, what="SRKL, student off the support")
+    # K = V: reverse KL as alpha -> 0
+    ids2 = np.stack([rng.permutation(V) for _ in range(N)])
+    lg2 = rng.standard_normal((N, V))
+    q = sps.softmax(H @ W.T / T, axis=1)
+    P = np.zeros((N, V))
+    for i in range(N):
+        P[i, ids2[i]] = sps.softmax(lg2[i] / T)
+    rkl = sps.rel_entr(q, P).sum(axis=1)
+    r = o.alt_forward(H, W, ids2, lg2, T, "srkl", 1e-9)["row_kl"]
+    _close(r, rkl, 1e-6, what="SRKL(alpha -> 0) vs scipy rel_entr(q, P)")
+
+
+def pin_skew_losses_invariants(o):
+    if not hasattr(o, "alt_forward"):
+        return
+    rng = np.random.default_rng(45)
+    N, d, V, K, T, g = 8, 5, 21, 5, 1.5, 1.1
+    H, W, ids, logits = _rand_problem(rng, N, d, V, K)
+    for loss, a in (("skl", 0.2), ("srkl", 0.3)):
+        base = o.alt_forward(H, W, ids, logits, T, loss, a)
+        dH, dW = o.alt_backward(H, W, ids, logits, T, loss, a, g)
+        # teacher equal to the student over the whole vocabulary
+        ide = np.stack([rng.permutation(V) for _ in range(N)])
+        eq = np.take_along_axis(H @ W.T, ide, axis=1)
+        e = o.alt_forward(H, W, ide, eq, T, loss, a)
+        assert np.max(np.abs(e["row_kl"])) < 1e-13, (loss, e["row_kl"])
+        eH, eW = o.alt_backward(H, W, ide, eq, T, loss, a, g)
+        assert np.max(np.abs(eH)) < 1e-13 and np.max(np.abs(eW)) < 1e-13
+        perm = rng.permutation(K)
+        _close(o.alt_forward(H, W, ids[:, perm], logits[:, perm], T, loss, a)["row_kl"], base["row_kl"],
+               1e-13, what=f"{loss} K-permutation")
+        for blk in (1, 3):
+            _close(o.alt_forward(H, W, ids, logits, T, loss, a, block=blk)["loss"], base["loss"], 1e-13,
+                   what=f"{loss} block {blk}")
+            bH, bW = o.alt_backward(H, W, ids, logits, T, loss, a, g, block=blk)
+            _close(bH, dH, 1e-13, what=f"{loss} block {blk} dH")
+            _close(bW, dW, 1e-12, what=f"{loss} block {blk} dW")
+        lH, lW = o.alt_backward(H, W, ids, logits, T, loss, a, 2.5 * g)
+        _close(lH, 2.5 * dH, 1e-13, what=f"{loss} linear in g")
+        c = rng.standard_normal(d)
+        _close(o.alt_forward(H, W + c, ids, logits, T, loss, a)["row_kl"], base["row_kl"], 1e-11,
+               what=f"{loss} W shift")
+        _close(dW.sum(axis=0), np.zeros(d), 0.0, atol=1e-14 * max(1.0, np.abs(dW).max() * V),
+               what=f"{loss} column sums of dW")
+        t1 = o.alt_forward(H / T, W, ids, logits / T, 1.0, loss, a)
+        _close(t1["loss"], base["loss"], 1e-13, what=f"{loss} temperature identity")
+        tH, tW = o.alt_backward(H / T, W, ids, logits / T, 1.0, loss, a, g)
+        _close(tH / T, dH, 1e-12, what=f"{loss} temperature identity dH")
+        _close(tW, dW, 1e-12, what=f"{loss} temperature identity dW")
+        ign = np.array([1, 6])
+        keep = np.setdiff1d(np.arange(N), ign)
+        ids_m = ids.copy()
+        ids_m[ign, 0] = -1
+        m = o.alt_forward(H, W, ids_m, logits, T, loss, a)
+        _close(m["loss"], o.alt_forward(H[keep], W, ids[keep], logits[keep], T, loss, a)["loss"], 1e-13,
+               what=f"{loss} ignored: loss")
+        assert np.all(m["row_kl"][ign] == 0.0)
+        mH, mW = o.alt_backward(H, W, ids_m, logits, T, loss, a, g)
+        rH, rW = o.alt_backward(H[keep], W, ids[keep], logits[keep], T, loss, a, g)
+        assert np.all(mH[ign] == 0.0)
+        _close(mH[keep], rH, 1e-13, what=f"{loss} ignored: dH")
+        _close(mW, rW, 1e-13, what=f"{loss} ignored: dW")
+    for loss, bad in (("skl", 1.0), ("skl", -0.1), ("srkl", 0.0), ("srkl", 1.5), ("jsd", 1.0)):
+        try:
+            o.alt_forward(H, W, ids, logits, T, loss, bad)
+        except ValueError:
+            continue
+        raise AssertionError(f"{loss} accepted parameter {bad}")
+
+
 ALL_PINS = [
     pin_two_token_softplus,
     pin_uniform_student,
@@ -747,4 +946,9 @@ ALL_PINS = [
     pin_jsd_torch_autograd,
     pin_jsd_brute_force_and_finite_differences,
     pin_jsd_invariants,
+    pin_skl_alpha_zero_is_forward_kl,
+    pin_skew_losses_torch_autograd,
+    pin_skew_losses_brute_force_and_finite_differences,
+    pin_skew_losses_bounds_and_limits,
+    pin_skew_losses_invariants,
 ]

@@ -63,6 +63,19 @@ MUTANTS = [
     ("jsd_grid_wraps_negative_ids", "    ok = _in_vocab(ids_rows, V)\n    rr, kk", "    ok = ids_rows < V\n    rr, kk"),
     ("jsd_teacher_term_sign", "kl_p = np.where(on, P * (np.where(on, logP, 0.0) - logM), 0.0)",
      "kl_p = np.where(on, P * (logM - np.where(on, logP, 0.0)), 0.0)"),
+    # the skew KL and skew reverse KL
+    ("skl_gradient_sign", "g = np.where(on, -(1.0 - alpha) * np.exp(lp - logM), 0.0)",
+     "g = np.where(on, (1.0 - alpha) * np.exp(lp - logM), 0.0)"),
+    ("skl_gradient_without_weight", "g = np.where(on, -(1.0 - alpha) * np.exp(lp - logM), 0.0)",
+     "g = np.where(on, -np.exp(lp - logM), 0.0)"),
+    ("skl_mixture_swapped", "logM = np.logaddexp(la + logP, math.log1p(-alpha) + logq)",
+     "logM = np.logaddexp(la + logq, math.log1p(-alpha) + logP)"),
+    ("skl_loss_sign", "loss = np.where(on, P * (lp - logM), 0.0).sum(axis=1)",
+     "loss = np.where(on, P * (logM - lp), 0.0).sum(axis=1)"),
+    ("srkl_gradient_without_alpha", "g = r + 1.0 - alpha * np.exp(r)", "g = r + 1.0 - np.exp(r)"),
+    ("srkl_mixture_ignores_alpha", "logM = np.logaddexp(math.log(alpha) + logq, lb + logP)",
+     "logM = np.logaddexp(math.log(0.5) + logq, math.log(0.5) + logP)"),
+    ("srkl_loss_sign", "loss = (q * r).sum(axis=1)", "loss = (q * -r).sum(axis=1)"),
     # ignored positions
     ("ignored_counted_in_mean", "N = int(kept.sum())  # the mean runs over the kept positions",
      "N = kept.size  # the mean runs over the kept positions"),
