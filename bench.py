@@ -92,9 +92,9 @@ def cpu_baseline(w, x, rows: int, loss: str = "kl", beta: float = 0.5):
         threads = len(os.sched_getaffinity(0))
     H, ids, lg = x["H"][:rows], x["ids"][:rows], x["logits"][:rows]
     t0 = time.perf_counter()
-    if loss == "jsd":
-        oracle.jsd_forward(H, x["W"], ids, lg, w.T, beta)
-        oracle.jsd_backward(H, x["W"], ids, lg, w.T, beta)
+    if loss != "kl":
+        oracle.alt_forward(H, x["W"], ids, lg, w.T, loss, beta)
+        oracle.alt_backward(H, x["W"], ids, lg, w.T, loss, beta)
     else:
         oracle.forward(H, x["W"], ids, lg, w.T)
         oracle.backward(H, x["W"], ids, lg, w.T)
@@ -395,10 +395,11 @@ def main():
     ap.add_argument("--gen-reading", choices=("1based", "0based"), default="1based",
                     help="reading of the workload list's cross-references for the teacher "
                          "generator of the 8K and 256K workloads (1based: uniform ids, N(0, 2))")
-    ap.add_argument("--loss", choices=("kl", "jsd"), default="kl",
+    ap.add_argument("--loss", choices=("kl", "jsd", "skl", "srkl"), default="kl",
                     help="kl: the pages' forward KL (default); jsd: the generalised Jensen-Shannon "
-                         "divergence (kdkl_options.loss = KDKL_LOSS_JSD)")
+                         "divergence; skl / srkl: the skew KL / skew reverse KL (kdkl_options.loss)")
     ap.add_argument("--beta", type=float, default=0.5, help="the JSD's weight beta")
+    ap.add_argument("--alpha", type=float, default=0.1, help="the skew losses' alpha")
     ap.add_argument("--chunks-per-group", type=int, default=0,
                     help="kdkl_options.chunks_per_group (0: the library's choice)")
     ap.add_argument("--vocab-slices", type=int, default=0,
@@ -452,8 +453,10 @@ def main():
     H, W, ids, lg = (x[k].to(dev) for k in ("H", "W", "ids", "logits"))
     opts = {"chunks_per_group": args.chunks_per_group, "vocab_slices": args.vocab_slices,
             "dh_w_in_place": args.dh_w_in_place}
-    if args.loss == "jsd":
-        opts.update(loss=kd.KDKL_LOSS_JSD, beta=args.beta)
+    loss_param = args.beta if args.loss == "jsd" else args.alpha
+    if args.loss != "kl":
+        codes = {"jsd": kd.KDKL_LOSS_JSD, "skl": kd.KDKL_LOSS_SKL, "srkl": kd.KDKL_LOSS_SRKL}
+        opts.update(loss=codes[args.loss], beta=loss_param)
     plan = kd.plan_info(w.N, w.d, w.V, w.K, w.chunk, H.dtype, opts)
     log(f"bench: plan {plan}")
     fb, bb = kd.workspace_size(w.N, w.d, w.V, w.K, w.chunk, H.dtype, opts)
@@ -556,7 +559,8 @@ def main():
                    "T": w.T, "teacher_ids": w.id_dist, "teacher_logit_var": w.logit_var,
                    "gen_reading": args.gen_reading,
                    "seed": args.seed if args.seed is not None else wl.seed_for(w),
-                   "loss": args.loss if args.loss == "kl" else f"jsd(beta={args.beta})",
+                   "loss": (args.loss if args.loss == "kl" else
+                            f"jsd(beta={args.beta})" if args.loss == "jsd" else f"{args.loss}(alpha={args.alpha})"),
                    "plan": plan,
                    "parallelism": "single GPU"},
         "mfma_util_pct": round(mfma_pct, 2),
@@ -574,7 +578,7 @@ def main():
     if not args.no_cpu_baseline:
         rows = min(args.cpu_rows, w.N)
         log(f"bench: timing the CPU oracle on {rows} positions")
-        out["cpu_baseline"] = cpu_baseline(w, x, rows, args.loss, args.beta)
+        out["cpu_baseline"] = cpu_baseline(w, x, rows, args.loss, loss_param)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -21,6 +21,8 @@ ABI_VERSION = 2
 NOALLOC_SCRATCH_BYTES = 64 << 20  # KDKL_NOALLOC_SCRATCH_BYTES
 KDKL_LOSS_KL = 0
 KDKL_LOSS_JSD = 1
+KDKL_LOSS_SKL = 2
+KDKL_LOSS_SRKL = 3
 
 
 class KdklError(RuntimeError):

@@ -109,7 +109,7 @@ struct Plan {
   bool wt;         // the dH product reads W^T written once per backward call (else W in place)
   int dtile;       // N-tile width of the dH and dW products (hidden-size axis)
   int loss;        // kdkl_loss
-  float beta;      // the loss's parameter (JSD)
+  float beta;      // the loss's parameter (JSD beta, skew alpha)
   // offsets into the forward workspace
   size_t f_ent, f_erow, f_keep, f_tstart, f_part, f_sk, f_red, f_rowkl, f_bytes;
   // offsets into the backward workspace
@@ -179,14 +179,23 @@ static bool region(size_t* cursor, int64_t bytes, size_t* off) {
   return true;
 }
 
+static_assert(ALT_JSD == KDKL_LOSS_JSD && ALT_SKL == KDKL_LOSS_SKL && ALT_SRKL == KDKL_LOSS_SRKL,
+              "the kernels number the alternative losses as the C-ABI does");
+
 // Largest accepted kdkl_options.vocab_slices and chunks_per_group.
 constexpr int kMaxVocabSlices = 1024;
 constexpr int kMaxChunksPerGroup = 64;
 
 static kdkl_status check_options(const kdkl_options* o) {
   if (o == nullptr) return KDKL_OK;
-  if (o->loss != KDKL_LOSS_KL && o->loss != KDKL_LOSS_JSD) return KDKL_ERR_OPTION;
-  if (o->loss == KDKL_LOSS_JSD && !(o->beta > 0.f && o->beta < 1.f)) return KDKL_ERR_OPTION;
+  const float a = o->beta;
+  switch (o->loss) {
+    case KDKL_LOSS_KL: break;
+    case KDKL_LOSS_JSD: if (!(a > 0.f && a < 1.f)) return KDKL_ERR_OPTION; break;
+    case KDKL_LOSS_SKL: if (!(a >= 0.f && a < 1.f)) return KDKL_ERR_OPTION; break;
+    case KDKL_LOSS_SRKL: if (!(a > 0.f && a <= 1.f)) return KDKL_ERR_OPTION; break;
+    default: return KDKL_ERR_OPTION;
+  }
   if (o->chunks_per_group < 0 || o->chunks_per_group > kMaxChunksPerGroup) return KDKL_ERR_OPTION;
   if (o->vocab_slices < 0 || o->vocab_slices > kMaxVocabSlices) return KDKL_ERR_OPTION;
   if (o->dh_w_in_place < 0 || o->dh_w_in_place > 2) return KDKL_ERR_OPTION;
@@ -221,7 +230,7 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   if (ost != KDKL_OK) return ost;
   const kdkl_options o = opts ? *opts : kdkl_options{};
   P->loss = o.loss;
-  P->beta = o.loss == KDKL_LOSS_JSD ? o.beta : 0.f;
+  P->beta = o.loss != KDKL_LOSS_KL ? o.beta : 0.f;
   if (o.chunks_per_group > 0) {
     // more than one chunk per launch needs the bf16 main loop, whose 32-bit
     // load offsets must still cover the group's operands
@@ -278,9 +287,9 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   ok &= region(&cur, t1, &P->f_tstart);
   ok &= mul_ok(P->Cg, P->n_vt, &t2) && mul_ok(t2, 16, &t2);
   ok &= region(&cur, t2, &P->f_part);
-  // the JSD's student logits at the sorted teacher entries [Cg, K]
+  // the alternative losses' student logits at the sorted teacher entries [Cg, K]
   int64_t sk = 0;
-  if (P->loss == KDKL_LOSS_JSD) ok &= mul_ok(P->Cg, K, &sk) && mul_ok(sk, 4, &sk);
+  if (P->loss != KDKL_LOSS_KL) ok &= mul_ok(P->Cg, K, &sk) && mul_ok(sk, 4, &sk);
   P->f_sk = 0;
   if (sk) ok &= region(&cur, sk, &P->f_sk);
   ok &= region(&cur, (int64_t)kReduceBytes, &P->f_red);  // the loss's partial sums
@@ -297,7 +306,7 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   ok &= region(&cur, (int64_t)kReduceBytes, &P->b_red);  // the kept count's partial sums
   ok &= region(&cur, g1, &P->b_tstart);
   P->b_rowcoef = 0;
-  if (P->loss == KDKL_LOSS_JSD) ok &= region(&cur, P->Cg * 4, &P->b_rowcoef);
+  if (P->loss != KDKL_LOSS_KL) ok &= region(&cur, P->Cg * 4, &P->b_rowcoef);
   int64_t wt, ht, dz, dhp;
   ok &= mul_ok(d, P->Vp, &wt) && mul_ok(wt, P->es, &wt);
   ok &= mul_ok(d, P->Cg, &ht) && mul_ok(ht, P->es, &ht);
@@ -370,7 +379,7 @@ static GemmArgs projection_args(const Plan& P, const void* H, const void* W, flo
 static JsdArgs jsd_args(const Plan& P, int rows, char* ws, size_t o_ent, size_t o_keep) {
   JsdArgs j;
   memset(&j, 0, sizeof(j));
-  j.V = P.V; j.rows = rows; j.K = (int)P.K; j.beta = P.beta;
+  j.V = P.V; j.rows = rows; j.K = (int)P.K; j.loss = P.loss; j.beta = P.beta;
   j.log_beta = (float)log((double)P.beta);
   j.log_omb = (float)log1p(-(double)P.beta);
   j.ent = (int2*)(ws + o_ent); j.keep = (const float*)(ws + o_keep);
@@ -448,15 +457,15 @@ static hipError_t forward_launches(const Plan& P, const void* H, const void* W, 
     GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.f_ent, P.f_tstart);
     g.Cp = P.Cg;
     g.part = (float4*)(ws + P.f_part);
-    // the JSD needs s at each teacher entry: the epilogue keeps it as it
-    // meets the entry
-    g.sk = P.loss == KDKL_LOSS_JSD ? (float*)(ws + P.f_sk) : nullptr;
+    // the alternative losses need s at each teacher entry: the epilogue
+    // keeps it as it meets the entry
+    g.sk = P.loss != KDKL_LOSS_KL ? (float*)(ws + P.f_sk) : nullptr;
     const double fl = 2.0 * rows * (double)V * d;
     const double by = ((double)V + rows) * d * P.es + (double)rows * P.n_vt * 16.0;
     e = timed(K_FWD_GEMM, fl, by, s, [&] { return launch_gemm(P.dtype, EPI_FWD, g, s); });
     if (e != hipSuccess) break;
-    if (P.loss == KDKL_LOSS_JSD) {
-      // lse, JSD and gbar per row from the partials and the kept student
+    if (P.loss != KDKL_LOSS_KL) {
+      // lse, the loss and gbar per row from the partials and the kept student
       // logits; gbar is saved after the N logsumexps for the backward
       JsdArgs j = jsd_args(P, rows, ws, P.f_ent, P.f_keep);
       j.sk = (const float*)(ws + P.f_sk);
@@ -678,7 +687,7 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
     e = timed(K_TRANSPOSE_H, 0.0, 2.0 * (double)rows * d * P.es, s, [&] {
       return launch_transpose((int)P.es, Hg, rows, d, d, ws + P.b_ht, rows_pad, P.Cg, s);
     });
-    if (e == hipSuccess && P.loss == KDKL_LOSS_JSD) {
+    if (e == hipSuccess && P.loss != KDKL_LOSS_KL) {
       // from the forward's gbar, each row's coefficient of q in dZ; the
       // teacher mass of each distinct id over its first entry
       JsdArgs j = jsd_args(P, rows, ws, P.b_ent, P.b_keep);
@@ -698,14 +707,15 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
       g.tiles_m = (int)((vlen + P.vt - 1) / P.vt);
       g.Cp = P.Cg; g.Vp = P.vpart;
       g.row_lse = row_lse + r0; g.scale = (const float*)(ws + P.b_scale); g.keep = (const float*)(ws + P.b_keep);
-      const bool jsd = P.loss == KDKL_LOSS_JSD;
-      g.rowcoef = jsd ? (const float*)(ws + P.b_rowcoef) : nullptr;
-      g.beta = jsd ? P.beta : 0.f;
+      const bool alt = P.loss != KDKL_LOSS_KL;
+      g.rowcoef = alt ? (const float*)(ws + P.b_rowcoef) : nullptr;
+      g.beta = alt ? P.beta : 0.f;
+      g.alt = alt ? P.loss : 0;
       g.dz_cv = ws + P.b_dzcv; g.dz_vc = P.fast ? nullptr : ws + P.b_dzvc;
       const double fl = 2.0 * rows * (double)vlen * d;
       e = timed(K_DZ_GEMM, fl,
                 ((double)vlen + rows) * d * P.es + (P.fast ? 1.0 : 2.0) * rows * (double)vlen * P.es, s,
-                [&] { return launch_gemm(dtype, jsd ? EPI_DZJ : EPI_DZ, g, s); });
+                [&] { return launch_gemm(dtype, alt ? EPI_DZJ : EPI_DZ, g, s); });
       if (e != hipSuccess) break;
       e = part_products(P, dtype, W, ws, r0, rows, part, dH, dW, r0 > 0 || accumulate_dW, s);
     }

@@ -77,12 +77,13 @@ struct GemmArgs {
   const int2* ent;               // [Cp, K] teacher entries (id, bits of p), ids ascending per row
   const uint16_t* tstart;
   float4* part;                  // forward: [Cp, n_vt] (max, sumexp, gamma, -)
-  float* sk;                     // forward, JSD: s = z / T at each sorted teacher entry [Cp, K] (else NULL)
+  float* sk;                     // forward, alternative losses: s = z / T at each sorted teacher entry [Cp, K] (else NULL)
   const float* row_lse;          // backward: lse of this chunk's rows
   const float* scale;            // backward: device scalar g / (N_kept * T)
   const float* keep;             // backward: keep flags of this chunk's rows [Cp]
-  const float* rowcoef;          // backward, JSD: per-row coefficient of q in dZ [Cp] (else scale[0])
-  float beta;                    // EPI_DZJ: the JSD's weight beta; the entries hold P per id
+  const float* rowcoef;          // backward, alternative losses: per-row coefficient of q in dZ [Cp] (else scale[0])
+  float beta;                    // EPI_DZJ: the loss's parameter (JSD beta, skew alpha); the entries hold P per id
+  int alt;                       // EPI_DZJ: which alternative loss (kdkl_loss value)
   int raw;                       // EPI_DZ only: store the logits z themselves (dense path)
   void* dz_cv;                   // [Cp, Vp]
   void* dz_vc;                   // [Vp, Cp]
@@ -128,13 +129,17 @@ struct MergeArgs {
   float* row_kl;        // chunk-offset
 };
 
-// The generalised Jensen-Shannon divergence (the alternative loss): one
-// wavefront per position of a group of rows.
+// The alternative losses, numbered as kdkl_loss (the C-ABI checks the match).
+enum AltLoss { ALT_JSD = 1, ALT_SKL = 2, ALT_SRKL = 3 };
+
+// The alternative losses (generalised Jensen-Shannon divergence, skew KL,
+// skew reverse KL): one wavefront per position of a group of rows.
 struct JsdArgs {
   int64_t V;
   int rows, K;
-  float beta;
-  float log_beta, log_omb;  // log(beta), log(1 - beta)
+  int loss;                 // kdkl_loss value (one of the alternative losses)
+  float beta;               // the loss's parameter (JSD beta, skew alpha)
+  float log_beta, log_omb;  // log(beta), log(1 - beta) (-inf at 0)
   int2* ent;             // [Cp, K] sorted teacher entries (id, bits of p); jsd_prep writes .y
   const float* sk;       // forward: [Cp, K] s = z / T at each sorted entry (from the epilogue)
   const float* keep;     // [Cp]
@@ -186,8 +191,9 @@ hipError_t launch_check_ids(const int32_t* ids, int64_t N, int K, int64_t V, voi
 hipError_t launch_dh_reduce(int dtype, const float* part, int splits, int rows,
                             int64_t d, int64_t Cp, const float* acc_in, void* out, hipStream_t s);
 
-// EPI_DZJ: the dZ epilogue of the JSD (support corrections formed at the
-// teacher entries), a kernel of its own so that the KL's is untouched.
+// EPI_DZJ: the dZ epilogue of the alternative losses (support corrections
+// formed at the teacher entries), a kernel of its own so that the KL's is
+// untouched.
 enum Epilogue { EPI_FWD = 0, EPI_DZ = 1, EPI_DH = 2, EPI_DW = 3, EPI_DZJ = 4 };
 // dtype: 0 = fp32, 1 = bf16
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& a, hipStream_t s);

@@ -1,30 +1,36 @@
-// Device kernels of the alternative loss: the generalised Jensen-Shannon
-// divergence between the teacher's top-K distribution and the student's
-// full-vocabulary distribution, on the fused chunked path's products.
+// Device kernels of the alternative losses on the fused chunked path's
+// products: the generalised Jensen-Shannon divergence, the skew KL and the
+// skew reverse KL between the teacher's top-K distribution and the student's
+// full-vocabulary distribution.
 //
 // The pages report ablations on the choice of loss for the distilled
 // student without naming the losses [P1 "Making knowledge distillation cheap
-// enough to run at scale", section "The resulting student model"]; this is
-// the reading taken. Per position, with P the teacher's top-K probabilities
+// enough to run at scale", section "The resulting student model"]; these are
+// the readings taken. Per position, with P the teacher's top-K probabilities
 // placed on the vocabulary (repeated ids add their mass, ids outside [0, V)
-// have no entry), q = softmax(s), s = z / T, and M = beta P + (1 - beta) q:
-//   JSD = beta KL(P || M) + (1 - beta) KL(q || M).
-// Off the teacher's support M = (1 - beta) q, so those V - |S| entries add
-// -(1 - beta) log(1 - beta) (1 - sum_S q) in closed form; only the support
-// (at most K entries per position) needs the student's logits individually.
-// The gradient is dZ_v = coef q_v (g_v - gbar) with g_v = (1 - beta)
-// log(q_v / M_v) (= -(1 - beta) log(1 - beta) off the support) and gbar =
-// sum_v q_v g_v. The projection epilogue forms it as a per-position
-// coefficient of q_v, coef (g_off - gbar), minus at each support entry
-// coef (1 - beta) q log(1 + beta P / ((1 - beta) q)), the same shape as the
-// KL's softmax-minus-teacher; gbar comes from the forward (saved per
-// position beside the logsumexp), so the backward needs no pass over the
-// support before its projections.
+// have no entry), q = softmax(s), s = z / T, and a parameter a:
+//   JSD   = a KL(P || M) + (1 - a) KL(q || M),  M = a P + (1 - a) q
+//   SKL   = KL(P || M),                         M = a P + (1 - a) q
+//   SRKL  = KL(q || M),                         M = a q + (1 - a) P
+// Each gradient has the form dZ_v = coef q_v (g_v - gbar), gbar = sum_v q_v
+// g_v, with g_v the derivative of the loss in q_v:
+//   JSD   g = (1 - a) log(q / M)             off the support: -(1 - a) log(1 - a)
+//   SKL   g = -(1 - a) P / M                 off the support: 0
+//   SRKL  g = log(q / M) + 1 - a q / M       off the support: -log(a)
+// Off the teacher's support each loss adds a constant per unit of student
+// mass there (-(1 - a) log(1 - a), 0 and -log(a) respectively), so only the
+// support (at most K entries per position) needs the student's logits
+// individually. The projection epilogue forms dZ as a per-position
+// coefficient of q_v, coef (g_off - gbar) >= 0 (g_v <= g_off on the support
+// for all three), minus coef q_v (g_off - g_v) at each support entry, the
+// same shape as the KL's softmax-minus-teacher; gbar comes from the forward
+// (saved per position beside the logsumexp), so the backward needs no pass
+// over the support before its projections.
 //
 // Two kernels, one wavefront per position:
 //   jsd_merge  forward: lse from the split-vocabulary partials, then, from
 //              s at each teacher entry (kept by the projection epilogue as it
-//              meets the entry), JSD and gbar
+//              meets the entry), the loss and gbar
 //   jsd_prep   backward: each position's coefficient of q in dZ, and the
 //              teacher mass of each distinct id written over its first
 //              entry's probability (0 over repeats) for the dZ epilogue
@@ -52,10 +58,16 @@ __device__ __forceinline__ float wsum(float v) {
 }
 
 struct Sums {
-  float tp;  // beta sum_S P log(P / M)
-  float tq;  // (1 - beta) sum_S q log(q / M)
+  float t;   // the support's part of the loss
+  float gq;  // the support's part of gbar: sum_S q g
   float qs;  // sum_S q
 };
+
+// log(exp(u) + exp(w)), either of them possibly -inf (not both)
+__device__ __forceinline__ float log_add(float u, float w) {
+  const float hi = fmaxf(u, w), lo = fminf(u, w);
+  return hi + log1pf(exp_hw(lo - hi));
+}
 
 // The support terms of one position (each lane its share of the sorted
 // entries; not yet summed over the wavefront).
@@ -63,7 +75,7 @@ __device__ __forceinline__ Sums support_terms(const JsdArgs& a, int row, float l
   const int lane = threadIdx.x & 63;
   const int2* ent = a.ent + (int64_t)row * a.K;
   const float* sk = a.sk + (int64_t)row * a.K;
-  const float beta = a.beta, omb = 1.f - beta;
+  const float al = a.beta, oma = 1.f - al;
   Sums r{0.f, 0.f, 0.f};
   for (int j = lane; j < a.K; j += 64) {
     const int2 e = ent[j];
@@ -74,15 +86,32 @@ __device__ __forceinline__ Sums support_terms(const JsdArgs& a, int row, float l
     const float lq = sk[j] - lse;  // log q
     const float q = exp_hw(lq);
     const float lp = log_hw(P);
-    // log M = log(beta P + (1 - beta) q), in the log domain
-    const float u = a.log_beta + lp, w = a.log_omb + lq;
-    const float hi = fmaxf(u, w), lo = fminf(u, w);
-    const float lm = hi + log1pf(exp_hw(lo - hi));
-    r.tp += beta * P * (lp - lm);
-    r.tq += omb * q * (lq - lm);
+    if (a.loss == ALT_SRKL) {
+      // log M = log(a q + (1 - a) P)
+      const float rq = lq - log_add(a.log_beta + lq, a.log_omb + lp);  // log(q / M)
+      r.t += q * rq;
+      r.gq += q * (rq + 1.f - al * exp_hw(rq));
+    } else {
+      // log M = log(a P + (1 - a) q)
+      const float lm = log_add(a.log_beta + lp, a.log_omb + lq);
+      if (a.loss == ALT_SKL) {
+        r.t += P * (lp - lm);
+        r.gq += -oma * exp_hw(lq + lp - lm);  // q P / M as one bounded exponential
+      } else {
+        r.t += al * P * (lp - lm) + oma * q * (lq - lm);
+        r.gq += oma * q * (lq - lm);
+      }
+    }
     r.qs += q;
   }
   return r;
+}
+
+// The loss's value and g per unit of student mass off the teacher's support.
+__device__ __forceinline__ float off_support(const JsdArgs& a) {
+  if (a.loss == ALT_SKL) return 0.f;
+  if (a.loss == ALT_SRKL) return -a.log_beta;
+  return -(1.f - a.beta) * a.log_omb;
 }
 
 // Online logsumexp of one position's split-vocabulary partials (max, sum of
@@ -118,16 +147,15 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void jsd_merge_kernel(JsdArgs a
   const float lse = lse_of_partials(a.part + (int64_t)row * a.n_vt, a.n_vt);
   // an ignored position's entries were never met by the epilogue
   Sums r = keep ? support_terms(a, row, lse) : Sums{0.f, 0.f, 0.f};
-  r.tp = wsum(r.tp);
-  r.tq = wsum(r.tq);
+  r.t = wsum(r.t);
+  r.gq = wsum(r.gq);
   r.qs = wsum(r.qs);
   if (lane == 0) {
-    const float omb = 1.f - a.beta;
-    // the off-support entries: (1 - beta) q log(1 / (1 - beta)) each
-    const float off = -omb * a.log_omb * (1.f - r.qs);
+    // the off-support entries: the same constant in the loss and in g
+    const float off = off_support(a) * (1.f - r.qs);
     a.row_lse[row] = lse;
-    a.row_kl[row] = keep ? r.tp + r.tq + off : 0.f;
-    a.row_gbar[row] = keep ? r.tq + off : 0.f;  // sum_v q_v g_v
+    a.row_kl[row] = keep ? r.t + off : 0.f;
+    a.row_gbar[row] = keep ? r.gq + off : 0.f;  // sum_v q_v g_v
   }
 }
 
@@ -158,10 +186,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void jsd_prep_kernel(JsdArgs a)
     const int j = lane + 64 * t;
     if (j < a.K) ent[j].y = __float_as_int(mass[t]);
   }
-  if (lane == 0) {
-    const float goff = -(1.f - a.beta) * a.log_omb;  // g off the support
-    a.rowcoef[row] = keep ? a.scale[0] * (goff - a.row_gbar_in[row]) : 0.f;
-  }
+  if (lane == 0) a.rowcoef[row] = keep ? a.scale[0] * (off_support(a) - a.row_gbar_in[row]) : 0.f;
 }
 
 dim3 rows_grid(int rows) { return dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)); }

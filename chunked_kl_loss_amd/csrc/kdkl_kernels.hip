@@ -780,17 +780,36 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, f32x16_t (&acc)
         if (slot < 0) continue;
         float pk = coef * __int_as_float(e.y);
         if constexpr (EPI == EPI_DZJ) {
-          // JSD: the entry holds the teacher mass P of its id (0 on a
-          // repeat); with q = acc / qs here (acc = qs q), the correction is
-          // coef (1 - beta) q log(1 + beta P / ((1 - beta) q))
+          // The entry holds the teacher mass P of its id (0 on a repeat);
+          // with q = acc / qs here (acc = qs q, qs >= 0), the correction is
+          // coef q (g_off - g) at the entry, a = the loss's parameter:
+          //   JSD   coef (1 - a) q log(1 + a P / ((1 - a) q))
+          //   SKL   coef (1 - a) P q / M,  M = a P + (1 - a) q   (coef P at a = 0)
+          //   SRKL  coef q (-log(1 - u) - u),  u = (1 - a) P / M,  M = a q + (1 - a) P
+          //         (as coef q (y - 1 - log y), y = 1 - u = a q / M, where u
+          //         is not small; 0 once a q underflows, where q is)
           float v = 0.f;
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
             for (int rr = 0; rr < 16; ++rr) v = (mb * 16 + rr == slot) ? acc[mb][nb][rr] : v;
-          const float P = __int_as_float(e.y), omb = 1.f - p.beta;
+          const float P = __int_as_float(e.y), a = p.beta, oma = 1.f - a;
           const float q = qs > 0.f ? v / qs : 0.f;
-          pk = (q > 0.f && P > 0.f) ? coef * omb * q * log1pf(p.beta * P / (omb * q)) : 0.f;
+          if (!(P > 0.f)) {
+            pk = 0.f;
+          } else if (p.alt == ALT_SKL) {
+            // at a = 0 the KL's teacher term, whatever q (which may underflow)
+            pk = a == 0.f ? coef * P : coef * oma * P * (q / (a * P + oma * q));
+          } else if (!(q > 0.f)) {
+            pk = 0.f;
+          } else if (p.alt == ALT_SRKL) {
+            const float M = a * q + oma * P;
+            const float u = oma * P / M, y = a * q / M;
+            const float t = u < 0.5f ? -log1pf(-u) - u : (y > 0.f ? y - 1.f - logf(y) : 0.f);
+            pk = coef * q * t;
+          } else {
+            pk = coef * oma * q * log1pf(a * P / (oma * q));
+          }
         }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)

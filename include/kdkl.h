@@ -96,29 +96,40 @@ typedef enum { KDKL_F32 = 0, KDKL_BF16 = 1 } kdkl_dtype;
 
 /* Loss computed by kdkl_forward / kdkl_backward (kdkl_options.loss). */
 typedef enum {
-  KDKL_LOSS_KL = 0, /* forward KL(teacher top-K || student), the pages' loss */
-  KDKL_LOSS_JSD = 1 /* generalised Jensen-Shannon divergence, weight beta */
+  KDKL_LOSS_KL = 0,  /* forward KL(teacher top-K || student), the pages' loss */
+  KDKL_LOSS_JSD = 1, /* generalised Jensen-Shannon divergence, weight beta */
+  KDKL_LOSS_SKL = 2, /* skew KL(P || alpha P + (1 - alpha) q), alpha = beta */
+  KDKL_LOSS_SRKL = 3 /* skew reverse KL(q || alpha q + (1 - alpha) P), alpha = beta */
 } kdkl_loss;
 
-/* The alternative loss, KDKL_LOSS_JSD (a reading: the pages report
- * ablations on the choice of loss function without naming the losses [P1
- * "Making knowledge distillation cheap enough to run at scale", section "The
- * resulting student model"]). With P_i the teacher's renormalised top-K
- * probabilities placed on the vocabulary (repeated ids add their mass, ids
- * outside [0, V) have no entry), q_i the student's softmax(s_i) over all V
- * entries and M_i = beta P_i + (1 - beta) q_i:
- *     JSD_i = beta KL(P_i || M_i) + (1 - beta) KL(q_i || M_i)
- *     loss  = (1/N) sum_i JSD_i        (row_kl holds JSD_i)
- *     dZ_iv = g / (N T) q_iv (g_iv - sum_u q_iu g_iu),
- *             g_iv = (1 - beta) log(q_iv / M_iv)
- * beta = 1/2 is the Jensen-Shannon divergence. It runs on the same fused
- * products (the vocabulary x sequence grid is never built): the forward's
- * projection epilogue keeps the student's logit at each teacher entry, and
- * the backward forms the support terms in its dZ epilogue from the
- * recomputed logits. Its saved per-position state is two floats, so
- * row_lse is [2, N] for this loss: each position's logsumexp, then
- * sum_v q_iv g_iv. Ignored positions as for the KL. Only the fused calls
- * (kdkl_forward, kdkl_forward_noalloc, kdkl_backward) take it. */
+/* The alternative losses (readings: the pages report ablations on the
+ * choice of loss function without naming the losses [P1 "Making knowledge
+ * distillation cheap enough to run at scale", section "The resulting student
+ * model"]). With P_i the teacher's renormalised top-K probabilities placed
+ * on the vocabulary (repeated ids add their mass, ids outside [0, V) have no
+ * entry) and q_i the student's softmax(s_i) over all V entries:
+ *   KDKL_LOSS_JSD   M_i = beta P_i + (1 - beta) q_i, 0 < beta < 1:
+ *                   L_i = beta KL(P_i || M_i) + (1 - beta) KL(q_i || M_i),
+ *                   g_iv = (1 - beta) log(q_iv / M_iv);
+ *                   beta = 1/2 is the Jensen-Shannon divergence.
+ *   KDKL_LOSS_SKL   M_i = alpha P_i + (1 - alpha) q_i, 0 <= alpha < 1:
+ *                   L_i = KL(P_i || M_i), g_iv = -(1 - alpha) P_iv / M_iv;
+ *                   alpha = 0 is the forward KL (where every id is in range).
+ *   KDKL_LOSS_SRKL  M_i = alpha q_i + (1 - alpha) P_i, 0 < alpha <= 1:
+ *                   L_i = KL(q_i || M_i),
+ *                   g_iv = log(q_iv / M_iv) + 1 - alpha q_iv / M_iv;
+ *                   finite although P_i is zero off the top-K.
+ * with alpha passed in kdkl_options.beta, and for each of them
+ *     loss  = (1/N) sum_i L_i          (row_kl holds L_i)
+ *     dZ_iv = g / (N T) q_iv (g_iv - sum_u q_iu g_iu).
+ * They run on the same fused products (the vocabulary x sequence grid is
+ * never built): the forward's projection epilogue keeps the student's logit
+ * at each teacher entry, and the backward forms the support terms in its dZ
+ * epilogue from the recomputed logits. Their saved per-position state is
+ * two floats, so row_lse is [2, N] for these losses: each position's
+ * logsumexp, then sum_v q_iv g_iv. Ignored positions as for the KL. Only the
+ * fused calls (kdkl_forward, kdkl_forward_noalloc, kdkl_backward) take
+ * them. */
 
 /* Per-call options of the fused calls. NULL, or a zero-filled struct, means
  * the defaults: the loss above and the library's own blocking, which it
@@ -144,7 +155,9 @@ typedef enum {
  *                    the bf16 main loop); 2: it reads a W^T copy written once
  *                    per backward call.
  *   beta             parameter of the loss, where it has one (ignored
- *                    otherwise): the JSD's weight, 0 < beta < 1.
+ *                    otherwise): the JSD's weight, 0 < beta < 1; the skew
+ *                    losses' alpha, 0 <= alpha < 1 (KDKL_LOSS_SKL) or
+ *                    0 < alpha <= 1 (KDKL_LOSS_SRKL).
  *   reserved         must be zero. */
 typedef struct {
   int32_t loss;
@@ -208,7 +221,7 @@ kdkl_status kdkl_plan_info(int64_t N, int64_t d, int64_t V, int32_t K,
  * Outputs (device): loss [1] fp32 (mean KL over kept positions; NaN when
  *   none, e.g. N == 0),
  *   row_lse [N] fp32 = logsumexp_v(s_iv) (keep it for kdkl_backward; [2, N]
- *     for KDKL_LOSS_JSD, see above),
+ *     for the alternative losses, see above),
  *   row_kl [N] fp32 per-position KL, or NULL if not wanted.
  * Workspace: >= *fwd_bytes from kdkl_workspace_size. */
 kdkl_status kdkl_forward(const void* H, const void* W,

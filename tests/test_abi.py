@@ -550,7 +550,8 @@ def test_jsd_options(lib):
     assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=L.KDKL_LOSS_JSD))[0] == OPTION             # beta 0
     assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=L.KDKL_LOSS_JSD, beta=1.0))[0] == OPTION
     assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=L.KDKL_LOSS_JSD, beta=float("nan")))[0] == OPTION
-    assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=2, beta=0.5))[0] == OPTION
+    assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=4, beta=0.5))[0] == OPTION
+    assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=-1, beta=0.5))[0] == OPTION
     st, f, b = ws(lib, *sizes, L.KDKL_BF16, opts(loss=L.KDKL_LOSS_JSD, beta=0.5))
     _, f0, b0 = ws(lib, *sizes, L.KDKL_BF16)
     assert st == OK
@@ -563,3 +564,18 @@ def test_jsd_options(lib):
     assert ws(lib, *sizes, L.KDKL_BF16, opts(beta=7.0))[1:] == (f0, b0)
     assert fwd(lib, o=opts(loss=L.KDKL_LOSS_JSD, beta=-0.5)) == OPTION
     assert bwd(lib, o=opts(loss=L.KDKL_LOSS_JSD, beta=1.5)) == OPTION
+
+
+def test_skew_loss_options(lib):
+    """The skew KL takes 0 <= alpha < 1, the skew reverse KL 0 < alpha <= 1
+    (kdkl_options.beta); both keep the JSD's extra workspace."""
+    sizes = (32768, 2880, 201088, 100, 2048)
+    _, fj, bj = ws(lib, *sizes, L.KDKL_BF16, opts(loss=L.KDKL_LOSS_JSD, beta=0.5))
+    for loss, good, bad in ((L.KDKL_LOSS_SKL, (0.0, 0.1, 0.999), (1.0, -0.1, float("nan"), 2.0)),
+                            (L.KDKL_LOSS_SRKL, (1.0, 0.1, 1e-6), (0.0, -0.1, float("nan"), 1.5))):
+        for a in good:
+            assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=loss, beta=a)) == (OK, fj, bj), (loss, a)
+        for a in bad:
+            assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=loss, beta=a))[0] == OPTION, (loss, a)
+        assert fwd(lib, o=opts(loss=loss, beta=bad[0])) == OPTION
+        assert bwd(lib, o=opts(loss=loss, beta=bad[1])) == OPTION
