@@ -138,32 +138,89 @@ static bool dh_reads_w_in_place(const Plan& P, int64_t N) {
 #ifndef KDKL_DH_BUSY
 #define KDKL_DH_BUSY 0.96
 #endif
+// Largest accepted kdkl_options.vocab_slices and chunks_per_group.
+constexpr int kMaxVocabSlices = 1024;
+constexpr int kMaxChunksPerGroup = 64;
+
 #ifndef KDKL_BWD_GROUP
-#define KDKL_BWD_GROUP 8
+#define KDKL_BWD_GROUP 16
 #endif
 #ifndef KDKL_GROUP_FILL
 #define KDKL_GROUP_FILL 95
 #endif
+// Largest dZ buffer (group rows x slice rows x element bytes) of the
+// library's own blocking: about 1.5% of the device's memory, independent of
+// the number of positions.
+constexpr int64_t kDzBudget = (int64_t)4 << 30;
 
-// Chunks per group (both calls) on the bf16 main loop: the largest of 8, 4,
-// 2 whose vocabulary slice still gives the dW product a full round of
-// workgroups (one per compute unit) and fills its rounds to 95% or more (a
-// partial last round costs more than the read-modify-writes saved), over no
-// more chunks than there are.
-static int backward_group(const Plan& P, int64_t N) {
-  int bg = KDKL_BWD_GROUP;
-  if (!P.fast || bg < 2) return 1;
-  const int64_t chunks = (N + P.chunk - 1) / P.chunk;
-  const int64_t dtiles = (P.d + P.dtile - 1) / P.dtile;
-  for (; bg > 1; bg >>= 1) {
-    if (bg > chunks || !gemm_fast_path(P.dtype, P.d, P.Vp, round_up(bg * P.chunk, kTokenTile))) continue;
-    const int64_t align = P.vt % 256 == 0 ? P.vt : P.vt * 2;  // slice starts, as make_plan sets them
-    const int64_t vpart = round_up((P.V + bg - 1) / bg, align);
-    const int64_t tiles = (vpart + 255) / 256 * dtiles;
-    const int64_t rounds = (tiles + kComputeUnits - 1) / kComputeUnits;
-    if (tiles >= kComputeUnits && tiles * 100 >= rounds * kComputeUnits * KDKL_GROUP_FILL) break;
+// Rows of each vocabulary slice (the last one may be shorter) when a group's
+// vocabulary is cut in `slices`: slices start on a tile boundary of both the
+// dZ product (vt rows) and the dW product (256 rows).
+static int64_t slice_rows(const Plan& P, int64_t slices) {
+  if (slices <= 1) return P.Vp;
+  const int64_t align = P.vt % 256 == 0 ? P.vt : P.vt * 2;
+  return round_up((P.V + slices - 1) / slices, align);
+}
+
+// Whether a slice of `vpart` rows gives the dW product at least one full
+// round of workgroups (one per compute unit) and fills its rounds to 95% or
+// more (a partial last round costs more than the read-modify-writes a
+// larger group saves).
+static bool dw_fills(const Plan& P, int64_t vpart) {
+  const int64_t tiles = (vpart + 255) / 256 * ((P.d + P.dtile - 1) / P.dtile);
+  const int64_t rounds = (tiles + kComputeUnits - 1) / kComputeUnits;
+  return tiles >= kComputeUnits && tiles * 100 >= rounds * kComputeUnits * KDKL_GROUP_FILL;
+}
+
+// The fewest vocabulary slices for a group of `rows` (padded) positions
+// whose dZ buffer fits kDzBudget and, with `fill`, whose slices fill dW's
+// rounds; 0 if there is none.
+static int64_t fewest_slices(const Plan& P, int64_t rows, bool fill) {
+  for (int64_t s = 1; s <= kMaxVocabSlices; ++s) {
+    const int64_t vp = slice_rows(P, s);
+    if (s > 1 && vp == slice_rows(P, s - 1)) continue;  // the same slicing as s - 1
+    if (vp * rows * P.es > kDzBudget) continue;
+    if (!fill || dw_fills(P, vp)) return s;
   }
-  return bg;
+  return 0;
+}
+
+// The library's own blocking on the bf16 main loop (kdkl_options fields 0):
+// the largest group of 16, 8, 4 or 2 chunks (no more than there are) that has
+// such a slicing, with its fewest slices; else one chunk per group. Larger
+// groups lengthen dW's contraction (one fp32 read-modify-write of dW per
+// group and slice) and let dH fill the device with fewer split-K partials;
+// fewer slices mean fewer dZ and dH launches and running sums. A set option
+// is kept and the other field chosen around it.
+static void choose_blocking(const Plan& P, int64_t N, int bg_set, int64_t slices_set, int* bg_out,
+                            int64_t* slices_out) {
+  const int64_t chunks = (N + P.chunk - 1) / P.chunk;
+  auto slices_for = [&](int bg, bool fill) -> int64_t {
+    const int64_t rows = round_up(bg * P.chunk, kTokenTile);
+    if (slices_set > 0) return slice_rows(P, slices_set) * rows * P.es <= kDzBudget || bg == 1 ? slices_set : 0;
+    return fewest_slices(P, rows, fill);
+  };
+  if (bg_set > 0 || !P.fast) {
+    const int bg = bg_set > 0 ? bg_set : 1;
+    int64_t s = slices_for(bg, true);
+    if (s == 0) s = slices_for(bg, false);
+    *bg_out = bg;
+    *slices_out = s > 0 ? s : kMaxVocabSlices;
+    return;
+  }
+  for (int bg = KDKL_BWD_GROUP; bg > 1; bg >>= 1) {
+    if (bg > chunks || !gemm_fast_path(P.dtype, P.d, P.Vp, round_up(bg * P.chunk, kTokenTile))) continue;
+    const int64_t s = slices_for(bg, true);
+    if (s > 0) {
+      *bg_out = bg;
+      *slices_out = s;
+      return;
+    }
+  }
+  int64_t s = slices_for(1, true);
+  if (s == 0) s = slices_for(1, false);
+  *bg_out = 1;
+  *slices_out = s > 0 ? s : kMaxVocabSlices;
 }
 
 static bool mul_ok(int64_t a, int64_t b, int64_t* out) {
@@ -182,9 +239,6 @@ static bool region(size_t* cursor, int64_t bytes, size_t* off) {
 static_assert(ALT_JSD == KDKL_LOSS_JSD && ALT_SKL == KDKL_LOSS_SKL && ALT_SRKL == KDKL_LOSS_SRKL,
               "the kernels number the alternative losses as the C-ABI does");
 
-// Largest accepted kdkl_options.vocab_slices and chunks_per_group.
-constexpr int kMaxVocabSlices = 1024;
-constexpr int kMaxChunksPerGroup = 64;
 
 static kdkl_status check_options(const kdkl_options* o) {
   if (o == nullptr) return KDKL_OK;
@@ -231,27 +285,19 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   const kdkl_options o = opts ? *opts : kdkl_options{};
   P->loss = o.loss;
   P->beta = o.loss != KDKL_LOSS_KL ? o.beta : 0.f;
-  if (o.chunks_per_group > 0) {
+  if (o.chunks_per_group > 1) {
     // more than one chunk per launch needs the bf16 main loop, whose 32-bit
     // load offsets must still cover the group's operands
-    P->bg = o.chunks_per_group;
-    if (P->bg > 1 && (!P->fast || !gemm_fast_path(dtype, d, P->Vp, round_up(P->bg * P->chunk, kTokenTile))))
+    if (!P->fast || !gemm_fast_path(dtype, d, P->Vp, round_up((int64_t)o.chunks_per_group * P->chunk, kTokenTile)))
       return KDKL_ERR_OPTION;
-  } else {
-    P->bg = backward_group(*P, N);
   }
+  int bg = 1;
+  int64_t slices = 1;
+  choose_blocking(*P, N, o.chunks_per_group, o.vocab_slices, &bg, &slices);
+  P->bg = bg;
   P->Cg = round_up(P->bg * P->chunk, kTokenTile);
   if (P->Cg > INT32_MAX / 4) return KDKL_ERR_OVERFLOW;
-  // vocabulary slices of a group: as many as chunks per group unless set
-  const int64_t slices = o.vocab_slices > 0 ? o.vocab_slices : P->bg;
-  if (slices <= 1) {
-    P->vpart = P->Vp;
-  } else {
-    // slices start on a tile boundary of both the dZ product (vt rows) and
-    // the dW product (256 rows)
-    const int64_t align = P->vt % 256 == 0 ? P->vt : P->vt * 2;
-    P->vpart = round_up((V + slices - 1) / slices, align);
-  }
+  P->vpart = slice_rows(*P, slices);
   P->n_parts = (int)((V + P->vpart - 1) / P->vpart);
   if (o.dh_w_in_place == 1 && !P->fast) return KDKL_ERR_OPTION;
   P->wt = !P->fast || (o.dh_w_in_place == 2) || (o.dh_w_in_place == 0 && !dh_reads_w_in_place(*P, N));
@@ -805,7 +851,12 @@ struct DensePlan {
 };
 
 static kdkl_status make_dense_plan(int64_t N, int64_t d, int64_t V, int32_t K, int dtype, DensePlan* D) {
-  kdkl_status st = make_plan(N, d, V, K, N > 0 ? N : 1, dtype, nullptr, &D->P);
+  // the dense baseline keeps its whole dZ grid: one chunk of every position,
+  // one vocabulary slice
+  kdkl_options o{};
+  o.chunks_per_group = 1;
+  o.vocab_slices = 1;
+  kdkl_status st = make_plan(N, d, V, K, N > 0 ? N : 1, dtype, &o, &D->P);
   if (st != KDKL_OK) return st;
   const Plan& P = D->P;
   int64_t z, g;

@@ -142,14 +142,22 @@ typedef enum {
  *   chunks_per_group 0: the library's choice; n >= 1: take n slices of
  *                    `chunk` positions per launch (both calls); n > 1 needs
  *                    the bf16 main loop (bf16 storage, d a multiple of 64).
- *   vocab_slices     0: as many vocabulary slices per group as chunks per
- *                    group (the dZ buffer then holds one chunk's worth of
- *                    elements); n >= 1 (at most 1024): the backward covers
- *                    a group's vocabulary in slices of ceil(V/n) rows rounded
- *                    up to whole tiles (so at most n slices; kdkl_plan_info
- *                    reports the count); its dZ buffer holds group rows x one
- *                    slice, and dW's fp32 read-modify-write happens once per
- *                    group and slice.
+ *   vocab_slices     0: the library's choice; n >= 1 (at most 1024): the
+ *                    backward covers a group's vocabulary in slices of
+ *                    ceil(V/n) rows rounded up to whole tiles (so at most n
+ *                    slices; kdkl_plan_info reports the count); its dZ buffer
+ *                    holds group rows x one slice, and dW's fp32
+ *                    read-modify-write happens once per group and slice.
+ *   The library's choice (fields 0) on the bf16 main loop: the largest group
+ *   of 16, 8, 4 or 2 chunks (no more than there are) that has a vocabulary
+ *   slicing whose dZ buffer stays within 4 GiB and whose slices give the dW
+ *   product whole rounds of workgroups (at least one per compute unit, 95%
+ *   full), with its fewest slices; else one chunk at a time. It depends on
+ *   the sizes only, and on N only while there are fewer than 16 chunks; the
+ *   fp32 / generic path takes one chunk and the whole vocabulary. A set
+ *   field is kept and the other chosen around it. Smaller groups and more
+ *   slices trade speed for memory (e.g. chunks_per_group 4, vocab_slices 4
+ *   on the 256K gpt-oss-like workload: 2.2 GiB less, about 2% slower).
  *   dh_w_in_place    0: the library's choice; 1: the dH product reads W in
  *                    place (no V x d transposed copy in the workspace; needs
  *                    the bf16 main loop); 2: it reads a W^T copy written once
@@ -198,7 +206,9 @@ const char* kdkl_status_string(int status);
  * about 0.3 ms per call by the library's model: at the gpt-oss-like head,
  * d = 2880 and V = 201088 with chunks of 2048, from N = 16385 on), so the
  * backward workspace steps up by that copy at one N; dh_w_in_place selects
- * either layout explicitly. */
+ * either layout explicitly. The default group of chunks (and with it the
+ * dZ buffer and the forward's per-group products) also grows with N until
+ * N spans 16 chunks, then stays fixed (see kdkl_options). */
 kdkl_status kdkl_workspace_size(int64_t N, int64_t d, int64_t V, int32_t K,
                                 int64_t chunk, int dtype, const kdkl_options* opts,
                                 size_t* fwd_bytes, size_t* bwd_bytes);

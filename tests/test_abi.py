@@ -73,19 +73,24 @@ def test_workspace_size_arithmetic(lib):
     st, f, b = ws(lib, 32768, 2880, 201088, 100, 2048, L.KDKL_BF16)
     assert st == OK
     Vp = (201088 + 255) // 256 * 256
-    assert b >= 2048 * Vp * 2
-    assert b < 2048 * Vp * 2 + 2880 * Vp * 2 + 2**30
+    p = plan(lib, 32768, 2880, 201088, 100, 2048, L.KDKL_BF16)
+    rows = p.chunks_per_group * 2048
+    vpart = -(-201088 // p.vocab_slices) // 768 * 768 + (768 if -(-201088 // p.vocab_slices) % 768 else 0)
+    assert b >= rows * vpart * 2 and rows * vpart * 2 <= 4 * 2**30  # the dZ buffer, within its budget
+    assert b < 4 * 2**30 + 2880 * Vp * 2 + 2**30
     # d not a multiple of 64: the generic path also keeps W^T, H_c^T and a
     # vocabulary-major copy of dZ
     _, _, bg = ws(lib, 32768, 2888, 201088, 100, 2048, L.KDKL_BF16)
     assert bg >= 2 * 2048 * Vp * 2 + 2888 * Vp * 2
-    assert f < 128 * 2**20  # per-group teacher products and split partials
+    assert f < 512 * 2**20  # per-group teacher products and split partials (32768 rows)
     # memory is independent of N apart from O(N) scratch
     _, f2, b2 = ws(lib, 262144, 2880, 201088, 100, 2048, L.KDKL_BF16)
     assert b2 == b and f2 - f == (262144 - 32768) * 4
-    # fp32 storage doubles the element-sized regions
+    # fp32 storage doubles the element-sized regions (against bf16 at the
+    # fp32 path's blocking: one chunk at a time, the whole vocabulary)
     _, _, b32 = ws(lib, 32768, 2880, 201088, 100, 2048, L.KDKL_F32)
-    assert b32 > b
+    _, _, b1 = ws(lib, 32768, 2880, 201088, 100, 2048, L.KDKL_BF16, opts(chunks_per_group=1, vocab_slices=1))
+    assert b32 > b1
     # outputs may be NULL
     assert lib.kdkl_workspace_size(10, 8, 16, 2, 4, L.KDKL_BF16, None, None, None) == OK
 
@@ -384,31 +389,34 @@ def L_status(lib, st):
     return lib.kdkl_status_string(st).decode()
 
 
-@pytest.mark.parametrize("sizes,groups", [
+@pytest.mark.parametrize("sizes,groups,slices", [
     # the GPU parity cases for backward groups: each must exercise its size
-    ((150, 64, 131001, 16, 64), 2),
-    ((148, 64, 262001, 12, 32), 4),
-    ((133, 64, 524001, 20, 16), 8),
-    # the named workloads (N, d, V, K, chunk): an eighth of gpt-oss's
-    # vocabulary would leave dW's last round of workgroups about half empty,
-    # an eighth of Llama's fills 98% of three rounds; the 2K workload's
-    # slices are too small for a full round
-    ((32768, 2880, 201088, 100, 2048), 4),
-    ((262144, 2880, 201088, 100, 4096), 4),
-    ((8192, 3072, 128256, 100, 1024), 8),
-    ((2048, 1024, 32000, 100, 256), 1),
+    ((150, 64, 131001, 16, 64), 2, 1),
+    ((148, 64, 262001, 12, 32), 4, 1),
+    ((133, 64, 524001, 20, 16), 8, 1),
+    # the named workloads (N, d, V, K, chunk): the largest group of 16, 8, 4
+    # or 2 chunks with a vocabulary slicing whose dZ buffer fits 4 GiB and
+    # whose slices fill dW's rounds to 95%, with its fewest slices. gpt-oss
+    # at 32K: all 16 chunks, quarters of the vocabulary (32768 x 50688 bf16,
+    # 3.3 GB; halves would take 6.6 GB). At 256K (chunks of 4096): 16 chunks
+    # would need eighths, whose dW leaves the last of four rounds 48% empty,
+    # so 8 chunks over quarters. Llama at 8K and the 2K workload: all chunks,
+    # the whole vocabulary.
+    ((32768, 2880, 201088, 100, 2048), 16, 4),
+    ((262144, 2880, 201088, 100, 4096), 8, 4),
+    ((8192, 3072, 128256, 100, 1024), 8, 1),
+    ((2048, 1024, 32000, 100, 256), 8, 1),
 ])
-def test_plan_groups(lib, sizes, groups):
+def test_plan_groups(lib, sizes, groups, slices):
     p = plan(lib, *sizes, L.KDKL_BF16)
-    assert p.chunks_per_group == groups
-    assert p.vocab_slices == groups  # as many vocabulary slices as chunks per group
+    assert (p.chunks_per_group, p.vocab_slices) == (groups, slices)
     assert p.dh_splits >= 1 and p.bf16_main_loop == 1
 
 
 def test_plan_groups_never_exceed_the_chunks(lib):
     # two chunks only: a group never spans more chunks than there are
     p = plan(lib, 128, 64, 524001, 20, 64, L.KDKL_BF16)
-    assert p.chunks_per_group <= 2 and p.vocab_slices == p.chunks_per_group
+    assert p.chunks_per_group <= 2
 
 
 def test_plan_fp32_takes_one_chunk_at_a_time(lib):
@@ -417,10 +425,12 @@ def test_plan_fp32_takes_one_chunk_at_a_time(lib):
 
 
 def test_plan_dh_splits_fill_the_rounds(lib):
-    # gpt-oss at 32K: 8192-row groups by 2880 columns on 256 x 320 tiles is
-    # 288 tiles; six splits fill 96.4% of seven rounds of 256 workgroups
+    # gpt-oss at 32K: 32768-row groups by 2880 columns on 256 x 320 tiles is
+    # 1152 tiles; two splits fill nine rounds of 256 workgroups exactly. With
+    # 8192-row groups (288 tiles) six splits fill 96.4% of seven rounds.
     p = plan(lib, 32768, 2880, 201088, 100, 2048, L.KDKL_BF16)
-    assert p.dh_splits == 6 and p.hidden_tile == 320 and p.vocab_tile == 384
+    assert p.dh_splits == 2 and p.hidden_tile == 320 and p.vocab_tile == 384
+    assert plan(lib, 32768, 2880, 201088, 100, 2048, L.KDKL_BF16, opts(chunks_per_group=4)).dh_splits == 6
 
 
 def test_plan_info_validates_like_the_compute_calls(lib):
@@ -439,19 +449,26 @@ def test_options_select_the_blocking(lib):
     base = plan(lib, *sizes, L.KDKL_BF16)
     # vocabulary slices apart from the chunks per group: the dZ buffer holds
     # group rows x V/slices columns, slices starting on 768-row boundaries
-    # (16 slices of a 4-chunk group: 8192 rows x 13056 columns, 214 MB,
-    # against 8192 x 50688, 830 MB, for the default 4 slices)
+    # (16 slices of the 16-chunk group: 32768 rows x 13056 columns, 856 MB,
+    # against 32768 x 50688, 3.3 GB, for the default 4 slices)
+    assert (base.chunks_per_group, base.vocab_slices) == (16, 4)
     p16 = plan(lib, *sizes, L.KDKL_BF16, opts(vocab_slices=16))
-    assert (p16.chunks_per_group, p16.vocab_slices) == (4, 16)
+    assert (p16.chunks_per_group, p16.vocab_slices) == (16, 16)
     assert p16.dh_splits == base.dh_splits
-    assert base.bwd_bytes - p16.bwd_bytes == 8192 * (50688 - 13056) * 2
+    assert base.bwd_bytes - p16.bwd_bytes == 32768 * (50688 - 13056) * 2
+    # a set group size keeps its own fewest slices within the budget
+    p4 = plan(lib, *sizes, L.KDKL_BF16, opts(chunks_per_group=4))
+    assert (p4.chunks_per_group, p4.vocab_slices) == (4, 1)
     p1 = plan(lib, *sizes, L.KDKL_BF16, opts(chunks_per_group=1))
     assert (p1.chunks_per_group, p1.vocab_slices) == (1, 1)
+    # a set slicing too large for the budget at 16 chunks takes a smaller group
+    p2s = plan(lib, *sizes, L.KDKL_BF16, opts(vocab_slices=2))
+    assert (p2s.chunks_per_group, p2s.vocab_slices) == (8, 2)
     p8 = plan(lib, *sizes, L.KDKL_BF16, opts(chunks_per_group=8, vocab_slices=32))
     # 32 slices asked: ceil(V/32) = 6284 rows rounded up to 6912 give 30
     assert (p8.chunks_per_group, p8.vocab_slices) == (8, 30)
     # the forward's workspace follows the group size
-    assert p8.fwd_bytes > base.fwd_bytes > p1.fwd_bytes
+    assert base.fwd_bytes > p8.fwd_bytes > p4.fwd_bytes > p1.fwd_bytes
     # explicit W layouts
     assert plan(lib, *sizes, L.KDKL_BF16, opts(dh_w_in_place=1)).dh_w_in_place == 1
     assert plan(lib, *sizes, L.KDKL_BF16, opts(dh_w_in_place=2)).dh_w_in_place == 0

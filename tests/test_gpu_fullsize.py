@@ -104,7 +104,7 @@ def test_gptoss20b_32k_full_size():
 
 def test_longctx_256k_full_size():
     # the launch configuration the default bench times (T = 2, chunks of 4096
-    # in groups of four, W^T copy)
+    # in groups of eight over vocabulary quarters, W^T copy)
     w = wl.get_config("longctx_256k")
     x = wl.generate(w)
     got = _run(w, x)
@@ -115,7 +115,7 @@ def test_longctx_256k_full_size():
 
 
 def test_llama3b_8k_full_size():
-    # groups of eight chunks over eight vocabulary slices, W read in place
+    # all eight chunks in one group over the whole vocabulary, W read in place
     w = wl.get_config("llama3b_8k")
     x = wl.generate(w)
     got = _run(w, x)
