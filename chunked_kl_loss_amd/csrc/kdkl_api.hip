@@ -294,6 +294,19 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   int bg = 1;
   int64_t slices = 1;
   choose_blocking(*P, N, o.chunks_per_group, o.vocab_slices, &bg, &slices);
+  if (P->fast && bg > 1) {
+    // the vocabulary tile was chosen for one chunk's token tiles, but the
+    // projections launch a whole group: choose it again for the group's,
+    // and the blocking once more (slices start on tile boundaries)
+    const int64_t rows = round_up((int64_t)bg * P->chunk, kTokenTile);
+    const int vtg = gemm_vocab_tile(true, V, rows / kTokenTile);
+    if (vtg != P->vt && gemm_fast_path(dtype, d, round_up(V, vtg), rows)) {
+      P->vt = vtg;
+      P->Vp = round_up(V, vtg);
+      P->n_vt = P->Vp / P->vt;
+      choose_blocking(*P, N, o.chunks_per_group, o.vocab_slices, &bg, &slices);
+    }
+  }
   P->bg = bg;
   P->Cg = round_up(P->bg * P->chunk, kTokenTile);
   if (P->Cg > INT32_MAX / 4) return KDKL_ERR_OVERFLOW;
