@@ -191,7 +191,8 @@ static int64_t fewest_slices(const Plan& P, int64_t rows, bool fill) {
 // groups lengthen dW's contraction (one fp32 read-modify-write of dW per
 // group and slice) and let dH fill the device with fewer split-K partials;
 // fewer slices mean fewer dZ and dH launches and running sums. A set option
-// is kept and the other field chosen around it.
+// is kept and the other field chosen around it. The generic main loop (fp32,
+// or d not a multiple of 64) keeps one chunk and the whole vocabulary.
 static void choose_blocking(const Plan& P, int64_t N, int bg_set, int64_t slices_set, int* bg_out,
                             int64_t* slices_out) {
   const int64_t chunks = (N + P.chunk - 1) / P.chunk;
@@ -200,11 +201,16 @@ static void choose_blocking(const Plan& P, int64_t N, int bg_set, int64_t slices
     if (slices_set > 0) return slice_rows(P, slices_set) * rows * P.es <= kDzBudget || bg == 1 ? slices_set : 0;
     return fewest_slices(P, rows, fill);
   };
-  if (bg_set > 0 || !P.fast) {
-    const int bg = bg_set > 0 ? bg_set : 1;
-    int64_t s = slices_for(bg, true);
-    if (s == 0) s = slices_for(bg, false);
-    *bg_out = bg;
+  if (!P.fast) {
+    // the generic path: one chunk at a time over the whole vocabulary
+    *bg_out = bg_set > 0 ? bg_set : 1;
+    *slices_out = slices_set > 0 ? slices_set : 1;
+    return;
+  }
+  if (bg_set > 0) {
+    int64_t s = slices_for(bg_set, true);
+    if (s == 0) s = slices_for(bg_set, false);
+    *bg_out = bg_set;
     *slices_out = s > 0 ? s : kMaxVocabSlices;
     return;
   }

@@ -596,3 +596,34 @@ def test_skew_loss_options(lib):
             assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=loss, beta=a))[0] == OPTION, (loss, a)
         assert fwd(lib, o=opts(loss=loss, beta=bad[0])) == OPTION
         assert bwd(lib, o=opts(loss=loss, beta=bad[1])) == OPTION
+
+
+@pytest.mark.parametrize("N,d,V,K,chunk,dt", [
+    (N, d, V, 16, chunk, dt)
+    for N in (1, 700, 5000, 40000, 300000)
+    for d, V in ((64, 1000), (1024, 32000), (2880, 201088), (3072, 128256), (2888, 50000), (4096, 262144))
+    for chunk in (32, 1024, 4096)
+    for dt in (L.KDKL_BF16, L.KDKL_F32)
+    if not (dt == L.KDKL_BF16 and d % 8) and not (dt == L.KDKL_F32 and d % 4)
+])
+def test_default_blocking_invariants(lib, N, d, V, K, chunk, dt):
+    """The library's own blocking over a grid of shapes: groups never span
+    more chunks than there are, the dZ buffer (group rows x slice rows x
+    element bytes) stays within 4 GiB, the generic path keeps one chunk and
+    the whole vocabulary, and the workspace query agrees with the plan."""
+    p = plan(lib, N, d, V, K, chunk, dt)
+    chunks = max(1, -(-N // chunk))
+    c = min(chunk, max(N, 1))
+    if not p.bf16_main_loop:
+        assert (p.chunks_per_group, p.vocab_slices) == (1, 1)
+        return
+    assert 1 <= p.chunks_per_group <= max(1, min(16, chunks))
+    vt = p.vocab_tile
+    align = vt if vt % 256 == 0 else 2 * vt
+    s = p.vocab_slices
+    vpart = -(-V // vt) * vt if s <= 1 else -(-(-(-V // s)) // align) * align
+    rows = -(-(p.chunks_per_group * c) // 256) * 256
+    assert rows * vpart * 2 <= 4 * 2 ** 30, (rows, vpart)
+    assert -(-V // vpart) == s  # the reported count is the slices the backward visits
+    st, f, b = ws(lib, N, d, V, K, chunk, dt)
+    assert st == OK and (f, b) == (p.fwd_bytes, p.bwd_bytes)
