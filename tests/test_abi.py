@@ -394,6 +394,7 @@ def L_status(lib, st):
     ((150, 64, 131001, 16, 64), 2, 1),
     ((148, 64, 262001, 12, 32), 4, 1),
     ((133, 64, 524001, 20, 16), 8, 1),
+    ((261, 64, 524001, 20, 16), 16, 1),
     # the named workloads (N, d, V, K, chunk): the largest group of 16, 8, 4
     # or 2 chunks with a vocabulary slicing whose dZ buffer fits 4 GiB and
     # whose slices fill dW's rounds to 95%, with its fewest slices. gpt-oss

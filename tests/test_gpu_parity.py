@@ -35,15 +35,16 @@ CASES = [
     # ragged second chunk
     ("bf16_vtile384_exact", "small_bf16", dict(N=2048, d=128, V=12288, K=16, chunk=2048, T=1.1), 13),
     ("bf16_vtile384_one_row", "small_bf16", dict(N=2100, d=192, V=11905, K=8, chunk=2048, T=0.9), 14),
-    # vocabularies whose slices give the dW product 256 tiles (a full round)
-    # so that both calls take several chunks at a time over as many
-    # vocabulary slices, each last slice ending in a partial tile: three
-    # chunks (groups of two: a full group, then one partial chunk), five (a
-    # full group of four, then one partial chunk), nine (a group of eight,
-    # then one partial chunk)
+    # vocabularies large enough for the dW product to fill its rounds of
+    # workgroups, so that both calls take several chunks at a time (over the
+    # whole vocabulary, a partial last tile): three chunks (groups of two: a
+    # full group, then one partial chunk), five (a full group of four, then
+    # one partial chunk), nine (a group of eight, then one partial chunk),
+    # seventeen (a group of sixteen, then five rows)
     ("bf16_backward_groups2", "small_bf16", dict(N=150, d=64, V=131001, K=16, chunk=64, T=1.2), 15),
     ("bf16_backward_groups4", "small_bf16", dict(N=148, d=64, V=262001, K=12, chunk=32, T=0.8), 16),
     ("bf16_backward_groups8", "small_bf16", dict(N=133, d=64, V=524001, K=20, chunk=16, T=1.1), 21),
+    ("bf16_backward_groups16", "small_bf16", dict(N=261, d=64, V=524001, K=20, chunk=16, T=1.1), 29),
     # the largest teacher top-K the boundary takes, over a small vocabulary:
     # dozens of teacher entries per column in every vocabulary tile
     ("bf16_max_K", "small_bf16", dict(N=100, d=128, V=6000, K=1024, chunk=64, T=1.0), 17),
