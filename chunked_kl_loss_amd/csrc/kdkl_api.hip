@@ -196,37 +196,38 @@ static int64_t fewest_slices(const Plan& P, int64_t rows, bool fill) {
 static void choose_blocking(const Plan& P, int64_t N, int bg_set, int64_t slices_set, int* bg_out,
                             int64_t* slices_out) {
   const int64_t chunks = (N + P.chunk - 1) / P.chunk;
-  auto slices_for = [&](int bg, bool fill) -> int64_t {
-    const int64_t rows = round_up(bg * P.chunk, kTokenTile);
-    if (slices_set > 0) return slice_rows(P, slices_set) * rows * P.es <= kDzBudget || bg == 1 ? slices_set : 0;
-    return fewest_slices(P, rows, fill);
+  auto group_rows = [&](int bg) { return round_up((int64_t)bg * P.chunk, kTokenTile); };
+  // the fewest slices within the budget for a group, filling dW's rounds if
+  // any slicing does; the most slices if even they exceed the budget
+  auto own_slices = [&](int bg) {
+    int64_t s = fewest_slices(P, group_rows(bg), true);
+    if (s == 0) s = fewest_slices(P, group_rows(bg), false);
+    return s > 0 ? s : (int64_t)kMaxVocabSlices;
   };
-  if (!P.fast) {
-    // the generic path: one chunk at a time over the whole vocabulary
-    *bg_out = bg_set > 0 ? bg_set : 1;
-    *slices_out = slices_set > 0 ? slices_set : 1;
-    return;
-  }
-  if (bg_set > 0) {
-    int64_t s = slices_for(bg_set, true);
-    if (s == 0) s = slices_for(bg_set, false);
-    *bg_out = bg_set;
-    *slices_out = s > 0 ? s : kMaxVocabSlices;
+  *bg_out = bg_set > 0 ? bg_set : 1;
+  *slices_out = slices_set > 0 ? slices_set : 1;
+  if (!P.fast) return;  // the generic path: one chunk at a time over the whole vocabulary
+  if (bg_set > 0) {     // a set group size: the library's slices around it
+    if (slices_set == 0) *slices_out = own_slices(bg_set);
     return;
   }
   for (int bg = KDKL_BWD_GROUP; bg > 1; bg >>= 1) {
-    if (bg > chunks || !gemm_fast_path(P.dtype, P.d, P.Vp, round_up(bg * P.chunk, kTokenTile))) continue;
-    const int64_t s = slices_for(bg, true);
+    if (bg > chunks || !gemm_fast_path(P.dtype, P.d, P.Vp, group_rows(bg))) continue;
+    if (slices_set > 0) {  // a set slicing: the largest group whose dZ buffer it keeps within the budget
+      if (slice_rows(P, slices_set) * group_rows(bg) * P.es <= kDzBudget) {
+        *bg_out = bg;
+        return;
+      }
+      continue;
+    }
+    const int64_t s = fewest_slices(P, group_rows(bg), true);
     if (s > 0) {
       *bg_out = bg;
       *slices_out = s;
       return;
     }
   }
-  int64_t s = slices_for(1, true);
-  if (s == 0) s = slices_for(1, false);
-  *bg_out = 1;
-  *slices_out = s > 0 ? s : kMaxVocabSlices;
+  if (slices_set == 0) *slices_out = own_slices(1);
 }
 
 static bool mul_ok(int64_t a, int64_t b, int64_t* out) {

@@ -465,6 +465,9 @@ def test_options_select_the_blocking(lib):
     # a set slicing too large for the budget at 16 chunks takes a smaller group
     p2s = plan(lib, *sizes, L.KDKL_BF16, opts(vocab_slices=2))
     assert (p2s.chunks_per_group, p2s.vocab_slices) == (8, 2)
+    # both set: kept as given, whatever the dZ buffer (16 chunks over halves: 6.6 GB)
+    p16_2 = plan(lib, *sizes, L.KDKL_BF16, opts(chunks_per_group=16, vocab_slices=2))
+    assert (p16_2.chunks_per_group, p16_2.vocab_slices) == (16, 2)
     p8 = plan(lib, *sizes, L.KDKL_BF16, opts(chunks_per_group=8, vocab_slices=32))
     # 32 slices asked: ceil(V/32) = 6284 rows rounded up to 6912 give 30
     assert (p8.chunks_per_group, p8.vocab_slices) == (8, 30)
