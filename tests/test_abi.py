@@ -483,11 +483,11 @@ def test_options_select_the_blocking(lib):
 
 
 @pytest.mark.parametrize("sizes,in_place", [
-    ((8192, 3072, 128256, 100, 1024), True),     # Llama-like head, 8K: 8 dH launches per call
-    ((16384, 2880, 201088, 100, 2048), True),    # gpt-oss-like head, 16K: 8 launches
-    ((16385, 2880, 201088, 100, 2048), False),   # one position more: 12 launches
-    ((32768, 2880, 201088, 100, 2048), False),   # gpt-oss-like head, 32K: 16 launches
-    ((262144, 2880, 201088, 100, 4096), False),  # the same head at 256K: 64 launches
+    ((8192, 3072, 128256, 100, 1024), True),     # Llama-like head, 8K: 1 dH launch per call
+    ((16384, 2880, 201088, 100, 2048), True),    # gpt-oss-like head, 16K: one group over halves, 2 launches
+    ((16385, 2880, 201088, 100, 2048), False),   # one position more: a second group, 4 launches
+    ((32768, 2880, 201088, 100, 2048), False),   # gpt-oss-like head, 32K: one group over quarters, 4 launches
+    ((262144, 2880, 201088, 100, 4096), False),  # the same head at 256K: 8 groups over quarters, 32 launches
 ])
 def test_w_copy_chosen_per_shape(lib, sizes, in_place):
     # by default the dH product reads W in place unless the copy saves at
