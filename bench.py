@@ -175,20 +175,25 @@ class PowerSampler:
         self._thread.start()
         self._amdsmi = amdsmi
 
-    def stop(self, ms_per_step):
+    def stop(self, ms_per_step, t_end=None):
+        """Summary of the samples from `settle` seconds after start to t_end."""
         if self._stop is None:
             return {"error": self.error}
         self._stop.set()
         self._thread.join()
         self._amdsmi.amdsmi_shut_down()
-        kept = [s for s in self.samples if s[0] >= self._t0 + self.settle]
+        t_end = t_end if t_end is not None else time.time()
+        kept = [s for s in self.samples if self._t0 + self.settle <= s[0] <= t_end]
         if not kept:
             return {"error": self.error or "no samples after the settling time (time more steps)"}
         avg_w = sum(s[1] for s in kept) / len(kept)
         return {"avg_w": round(avg_w, 1), "max_w": max(s[1] for s in kept),
                 "gfx_mhz": round(sum(s[2] for s in kept) / len(kept), 1),
                 "joules_per_step": round(avg_w * ms_per_step / 1e3, 2), "samples": len(kept),
-                "settle_s": self.settle, "power_limit": self.limit}
+                "settle_s": self.settle,
+                # amdsmi reports the limit in microwatts
+                "power_limit_w": (round(self.limit / 1e6, 1) if isinstance(self.limit, (int, float)) and self.limit > 1e5
+                                  else self.limit)}
 
 
 def kernel_table(kstats, steps):
@@ -408,8 +413,8 @@ def main():
                     help="kdkl_options.dh_w_in_place (0: the library's choice, 1: in place, 2: W^T copy)")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of one step captured into a HIP graph")
-    ap.add_argument("--power", action="store_true",
-                    help="sample socket power and the gfx clock (amdsmi) over the timed steps (eager only)")
+    ap.add_argument("--no-power", action="store_true",
+                    help="do not sample socket power and the gfx clock (amdsmi) over the timed steps")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -481,6 +486,8 @@ def main():
 
     ev0 = torch.cuda.Event(enable_timing=True)
     ev1 = torch.cuda.Event(enable_timing=True)
+    sampler = None if args.no_power else PowerSampler()
+    samples_end = None
     if args.graph:
         # one step captured into a HIP graph and replayed (the library
         # launches only its own kernels on the given stream, no memset
@@ -496,11 +503,14 @@ def main():
         stream = torch.cuda.current_stream(dev)  # replay() runs on the current stream
         graph.replay()
         torch.cuda.synchronize(dev)
+        if sampler:
+            sampler.start(dev)
         ev0.record(stream)
         for _ in range(args.steps):
             graph.replay()
         ev1.record(stream)
         torch.cuda.synchronize(dev)
+        samples_end = time.time()
         kd.profile_begin()
         for _ in range(min(args.steps, 3)):
             step()
@@ -508,7 +518,6 @@ def main():
         kstats = kd.profile_end()
         ksteps = min(args.steps, 3)
     else:
-        sampler = PowerSampler() if args.power else None
         kd.profile_begin()
         torch.cuda.synchronize(dev)
         if sampler:
@@ -518,10 +527,11 @@ def main():
             step()
         ev1.record(stream)
         torch.cuda.synchronize(dev)
+        samples_end = time.time()
         kstats = kd.profile_end()
         ksteps = args.steps
     ms = ev0.elapsed_time(ev1) / args.steps
-    power = sampler.stop(ms) if (args.power and not args.graph) else None
+    power = sampler.stop(ms, samples_end) if sampler else None
     peak_gib = torch.cuda.max_memory_allocated(dev) / 2**30
     log(f"bench: {ms:.2f} ms/step")
 
