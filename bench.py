@@ -423,8 +423,8 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the multi-GPU sharding is a design note, not code)", file=sys.stderr)
+        print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
+              "(sharding across GPUs is described, not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch
