@@ -292,28 +292,29 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   const kdkl_options o = opts ? *opts : kdkl_options{};
   P->loss = o.loss;
   P->beta = o.loss != KDKL_LOSS_KL ? o.beta : 0.f;
+  int bg = 1;
+  int64_t slices = 1;
+  if (P->fast) {
+    // the vocabulary tile was chosen for one chunk's token tiles, but the
+    // projections launch a whole group: choose it for the group the
+    // library's own blocking takes (not the options', so that blocking
+    // options never change it, nor the results' rounding)
+    choose_blocking(*P, N, 0, 0, &bg, &slices);
+    const int64_t rows = round_up((int64_t)bg * P->chunk, kTokenTile);
+    const int vtg = gemm_vocab_tile(true, V, rows / kTokenTile);
+    if (bg > 1 && vtg != P->vt && gemm_fast_path(dtype, d, round_up(V, vtg), rows)) {
+      P->vt = vtg;
+      P->Vp = round_up(V, vtg);
+      P->n_vt = P->Vp / P->vt;
+    }
+  }
   if (o.chunks_per_group > 1) {
     // more than one chunk per launch needs the bf16 main loop, whose 32-bit
     // load offsets must still cover the group's operands
     if (!P->fast || !gemm_fast_path(dtype, d, P->Vp, round_up((int64_t)o.chunks_per_group * P->chunk, kTokenTile)))
       return KDKL_ERR_OPTION;
   }
-  int bg = 1;
-  int64_t slices = 1;
   choose_blocking(*P, N, o.chunks_per_group, o.vocab_slices, &bg, &slices);
-  if (P->fast && bg > 1) {
-    // the vocabulary tile was chosen for one chunk's token tiles, but the
-    // projections launch a whole group: choose it again for the group's,
-    // and the blocking once more (slices start on tile boundaries)
-    const int64_t rows = round_up((int64_t)bg * P->chunk, kTokenTile);
-    const int vtg = gemm_vocab_tile(true, V, rows / kTokenTile);
-    if (vtg != P->vt && gemm_fast_path(dtype, d, round_up(V, vtg), rows)) {
-      P->vt = vtg;
-      P->Vp = round_up(V, vtg);
-      P->n_vt = P->Vp / P->vt;
-      choose_blocking(*P, N, o.chunks_per_group, o.vocab_slices, &bg, &slices);
-    }
-  }
   P->bg = bg;
   P->Cg = round_up(P->bg * P->chunk, kTokenTile);
   if (P->Cg > INT32_MAX / 4) return KDKL_ERR_OVERFLOW;

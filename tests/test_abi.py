@@ -631,3 +631,22 @@ def test_default_blocking_invariants(lib, N, d, V, K, chunk, dt):
     assert -(-V // vpart) == s  # the reported count is the slices the backward visits
     st, f, b = ws(lib, N, d, V, K, chunk, dt)
     assert st == OK and (f, b) == (p.fwd_bytes, p.bwd_bytes)
+
+
+@pytest.mark.parametrize("N,d,V,chunk", [
+    (8192, 2880, 201088, 2048), (32768, 2880, 201088, 2048), (262144, 2880, 201088, 4096),
+    (8192, 3072, 128256, 1024), (2048, 1024, 32000, 256), (20000, 512, 50000, 512), (3000, 256, 100000, 64),
+])
+def test_blocking_options_keep_the_vocabulary_tile(lib, N, d, V, chunk):
+    """The vocabulary tile depends on the sizes only: every group size and
+    slice count a caller (or the allocation-free forward, which takes fewer
+    chunks per launch) may set gives the same tile, hence the same per-tile
+    partials and the same rounding of the forward's results."""
+    base = plan(lib, N, d, V, 100, chunk, L.KDKL_BF16).vocab_tile
+    for cpg in (1, 2, 4, 8, 16):
+        for vs in (0, 1, 3):
+            p = L.Plan()
+            st = lib.kdkl_plan_info(N, d, V, 100, chunk, L.KDKL_BF16, opts(chunks_per_group=cpg, vocab_slices=vs),
+                                    C.byref(p))
+            if st == OK:
+                assert p.vocab_tile == base, (cpg, vs, p.vocab_tile, base)
