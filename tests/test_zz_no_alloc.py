@@ -14,18 +14,18 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def _both(w, x):
+def _both(w, x, options=None):
     import chunked_kl_loss_amd as kd
 
     dev = torch.device(DEV)
     H, W, ids, lg = (x[k].to(dev) for k in ("H", "W", "ids", "logits"))
-    ref_loss, ref_lse, ref_kl = kd.kdkl_forward(H, W, ids, lg, w.T, w.chunk)
+    ref_loss, ref_lse, ref_kl = kd.kdkl_forward(H, W, ids, lg, w.T, w.chunk, options=options)
     loss = torch.full((1,), float("nan"), device=dev)
-    lse = torch.full((w.N,), float("nan"), device=dev)
+    lse = torch.full(kd.saved_shape(w.N, options), float("nan"), device=dev)
     kl = torch.full((w.N,), float("nan"), device=dev)
     torch.cuda.synchronize(dev)
     before = torch.cuda.memory_allocated(dev)
-    kd.kdkl_forward_noalloc(H, W, ids, lg, w.T, w.chunk, loss=loss, row_lse=lse, row_kl=kl)
+    kd.kdkl_forward_noalloc(H, W, ids, lg, w.T, w.chunk, loss=loss, row_lse=lse, row_kl=kl, options=options)
     torch.cuda.synchronize(dev)
     assert torch.cuda.memory_allocated(dev) == before
     return (ref_loss.item(), ref_lse.cpu().numpy(), ref_kl.cpu().numpy()), \
@@ -61,3 +61,24 @@ def test_forward_noalloc_matches_forward_twice():
         e_kl = np.abs(got[2][rows] - o["row_kl"]).max() / np.abs(o["row_kl"]).max()
         print(f"noalloc N={w.N}: loss {got[0]:.7g}; oracle rows lse {e_lse:.2e} kl {e_kl:.2e}", flush=True)
         assert e_lse <= 1e-3 and e_kl <= 1e-3
+
+
+def test_forward_noalloc_alternative_loss():
+    """An alternative loss (the skew reverse KL) through the allocation-free
+    forward: its extra per-group buffer of student logits at the teacher
+    entries also lives in the static array; results equal kdkl_forward's bit
+    for bit, both saved rows (logsumexp and gbar) included."""
+    import chunked_kl_loss_amd as kd
+
+    w = wl.get_config("gptoss20b_32k").with_(N=8192)
+    opts = {"loss": kd.KDKL_LOSS_SRKL, "beta": 0.1}
+    x = wl.generate(w, seed=63)
+    print(f"case noalloc srkl N={w.N} chunk={w.chunk}", flush=True)
+    ref, got = _both(w, x, opts)
+    assert got[0] == ref[0], (got[0], ref[0])
+    assert np.array_equal(got[1], ref[1]) and np.array_equal(got[2], ref[2])
+    rows = [0, w.chunk, w.N - 1]
+    sub = {k: x[k][rows] for k in ("H", "ids", "logits")}
+    o = oracle.alt_forward(sub["H"], x["W"], sub["ids"], sub["logits"], w.T, "srkl", 0.1)
+    e_kl = np.abs(got[2][rows] - o["row_kl"]).max() / np.abs(o["row_kl"]).max()
+    assert e_kl <= 1e-3, e_kl
