@@ -243,7 +243,7 @@ static bool region(size_t* cursor, int64_t bytes, size_t* off) {
   return true;
 }
 
-static_assert(ALT_JSD == KDKL_LOSS_JSD && ALT_SKL == KDKL_LOSS_SKL && ALT_SRKL == KDKL_LOSS_SRKL,
+static_assert((int)ALT_JSD == (int)KDKL_LOSS_JSD && (int)ALT_SKL == (int)KDKL_LOSS_SKL && (int)ALT_SRKL == (int)KDKL_LOSS_SRKL,
               "the kernels number the alternative losses as the C-ABI does");
 
 

@@ -4,9 +4,12 @@
 // position [P1 "Making knowledge distillation cheap enough to run at scale",
 // section "Two system changes", forward-chunked KL bullet].
 //
-// Both passes stream Z once and are bound by HBM bandwidth. One wavefront
-// owns one row (position): rows are independent, so the pages' slicing over
-// positions is the grid itself and no chunk buffer exists.
+// Both passes stream Z once and are bound by HBM bandwidth. Rows are
+// independent, so the pages' slicing over positions is the grid itself and
+// no chunk buffer exists: in the forward one wavefront owns one row
+// (position); the backward gives a long row of whole 16-byte vectors to
+// 256-thread workgroups in contiguous pieces (consecutive workgroups stream
+// consecutive memory) and any other row to one wavefront.
 //   forward : lse_i = log sum_v exp(z_iv / T) (online, base 2), and
 //             KL_i = e_i - gamma_i + lse_i with e_i = sum_k p_ik log p_ik and
 //             gamma_i = sum_k p_ik z_i[id_ik] / T.
@@ -129,25 +132,41 @@ struct TeacherRow {
   bool ok[KPL];
   float e;  // wavefront total
 
-  // gather = false skips reading the student logits (z stays 0)
-  __device__ void load(const LogitsArgs& a, int64_t row, int lane, bool gather = true) {
+  float av[KPL];  // l / T between request() and finish()
+
+  // Requests the row's entries and, with gather, the student logits at their
+  // ids (z stays 0 otherwise). Every lane issues its loads unconditionally
+  // (clamped to valid addresses) and nothing waits for them here but the
+  // gathers' own wait for the ids, so the requests stay in flight while the
+  // caller goes on; finish() uses them.
+  __device__ void request(const LogitsArgs& a, int64_t row, int lane, bool gather = true) {
     const int K = a.K;
     const int64_t g = row * (int64_t)K;
     const TE* zr = (const TE*)a.Z + row * a.V;
-    float av[KPL];
-    float mx = kNegInf;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
       const int k = lane + 64 * j;
-      av[j] = kNegInf;
-      id[j] = -1;
-      if (k < K) {
-        av[j] = a.logits[g + k] * a.inv_T;
-        id[j] = a.ids[g + k];
-        mx = fmaxf(mx, av[j]);
-      }
+      const int kk = k < K ? k : K - 1;
+      av[j] = a.logits[g + kk];
+      id[j] = a.ids[g + kk];
+    }
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      if (lane + 64 * j >= K) id[j] = -1;
       ok[j] = id[j] >= 0 && (int64_t)id[j] < a.V;
-      z[j] = (gather && ok[j]) ? Elem<TE>::load(zr + id[j]) : 0.f;
+      z[j] = gather ? Elem<TE>::load(zr + (ok[j] ? id[j] : 0)) : 0.f;
+    }
+  }
+  // p = softmax over K of l / T and e = sum_k p_k log p_k (wavefront total);
+  // z at an id outside [0, V) reads as 0.
+  __device__ void finish(const LogitsArgs& a, int lane) {
+    const int K = a.K;
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      av[j] = lane + 64 * j < K ? av[j] * a.inv_T : kNegInf;
+      mx = fmaxf(mx, av[j]);
+      z[j] = ok[j] ? z[j] : 0.f;
     }
     mx = wave_max(mx);
     float se = 0.f;
@@ -167,43 +186,110 @@ struct TeacherRow {
     }
     e = wave_sum(ent);
   }
+  __device__ void load(const LogitsArgs& a, int64_t row, int lane, bool gather = true) {
+    request(a, row, lane, gather);
+    finish(a, lane);
+  }
 };
 
-// Online (max, sum 2^(x - max)) over base-2 scaled logits x.
+// Sum of a vector of terms as a balanced tree (shorter dependency chains
+// than a running sum; N a power of two).
+template <int N>
+__device__ __forceinline__ float tree_sum(const float (&e)[N]) {
+  float t[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) t[j] = e[j];
+#pragma unroll
+  for (int w = N / 2; w > 0; w /= 2)
+#pragma unroll
+    for (int j = 0; j < w; ++j) t[j] = t[2 * j] + t[2 * j + 1];
+  return t[0];
+}
+
+// Online (max, sum 2^(c (z - max))) over raw logits z with c = log2(e) / T:
+// the max is taken over z itself (c > 0 keeps the order), so each term is
+// one fused multiply-add and one exp2. The logsumexp of s = z / T is
+// (m c + log2 sum) ln 2.
 struct OnlineLse {
-  float m = kNegInf, s = 0.f;
-  __device__ void add(float x) {
-    if (x == kNegInf) return;
-    if (x > m) {
-      s = s * exp2_hw(m - x) + 1.f;
-      m = x;
+  float c, m = kNegInf, s = 0.f;
+  __device__ explicit OnlineLse(float c_) : c(c_) {}
+  __device__ void add(float z) {
+    if (z == kNegInf) return;
+    if (z > m) {
+      s = s * exp2_hw((m - z) * c) + 1.f;
+      m = z;
     } else {
-      s += exp2_hw(x - m);
+      s += exp2_hw(__builtin_fmaf(z, c, -m * c));
     }
   }
   template <int N>
-  __device__ void add_vec(const float (&x)[N]) {
-    float mv = x[0];
+  __device__ void add_vec(const float (&z)[N]) {
+    float mv = z[0];
 #pragma unroll
-    for (int j = 1; j < N; ++j) mv = fmaxf(mv, x[j]);
+    for (int j = 1; j < N; ++j) mv = fmaxf(mv, z[j]);
     if (mv == kNegInf) return;
     if (mv > m) {
-      s *= exp2_hw(m - mv);
+      s *= exp2_hw((m - mv) * c);
       m = mv;
     }
+    const float mc = -m * c;
+    float e[N];
 #pragma unroll
-    for (int j = 0; j < N; ++j) s += exp2_hw(x[j] - m);
+    for (int j = 0; j < N; ++j) e[j] = exp2_hw(__builtin_fmaf(z[j], c, mc));
+    s += tree_sum(e);
+  }
+  // A group of U vectors of storage type TE with the running max allowed to
+  // lag: the terms are formed against the current max and may exceed 1 (up
+  // to 2^kLag) before it is raised, so the rescale runs only when some lane
+  // of the wavefront meets a value that far above it (in practice at the
+  // row's first group), and that group's terms are then formed again.
+  static constexpr float kLag = 64.f;
+  template <typename TE, int U>
+  __device__ float group_terms(const uint4 (&u)[U], float& mv) const {
+    constexpr int N = Elem<TE>::kVec;
+    const float mc = m == kNegInf ? 0.f : -m * c;
+    float sg = 0.f;
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      float z[N], e[N];
+      Elem<TE>::unpack(u[q], z);
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        mv = fmaxf(mv, z[j]);
+        e[j] = exp2_hw(__builtin_fmaf(z[j], c, mc));
+      }
+      sg += tree_sum(e);
+    }
+    return sg;
+  }
+  template <typename TE, int U>
+  __device__ void add_group(const uint4 (&u)[U]) {
+    float mv = kNegInf;
+    float sg = group_terms<TE>(u, mv);
+    // (mv - m) c is NaN, so false, for a group of -inf under m = -inf
+    if (__builtin_amdgcn_ballot_w64((mv - m) * c > kLag) != 0) {
+      const float nm = fmaxf(m, mv);
+      if (nm > m) {
+        s *= exp2_hw((m - nm) * c);
+        m = nm;
+        float unused = kNegInf;
+        sg = group_terms<TE>(u, unused);
+      }
+    }
+    s += sg;
   }
   __device__ void wave_merge() {
     for (int o = 32; o > 0; o >>= 1) {
       const float om = wave_xor(m, o), os = wave_xor(s, o);
       const float nm = fmaxf(m, om);
       if (nm > kNegInf) {
-        s = (m > kNegInf ? s * exp2_hw(m - nm) : 0.f) + (om > kNegInf ? os * exp2_hw(om - nm) : 0.f);
+        s = (m > kNegInf ? s * exp2_hw((m - nm) * c) : 0.f) + (om > kNegInf ? os * exp2_hw((om - nm) * c) : 0.f);
         m = nm;
       }
     }
   }
+  // natural-log logsumexp of z / T (after wave_merge)
+  __device__ float lse() const { return (m * c + log2_hw(s)) * kLn2; }
 };
 
 constexpr int kUnroll = 4;  // 16-byte loads in flight per lane
@@ -220,53 +306,70 @@ __device__ __forceinline__ uint4 load_stream(const uint4* p) {
 __device__ __forceinline__ void store_stream(uint4* p, uint4 v) {
   __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w}, (u32x4_t*)p);
 }
+// kUnroll vectors STRIDE apart from p (one wavefront-wide group)
+template <int STRIDE = 64>
+__device__ __forceinline__ void load_group(uint4 (&u)[kUnroll], const uint4* p) {
+#pragma unroll
+  for (int q = 0; q < kUnroll; ++q) u[q] = load_stream(p + STRIDE * q);
+}
 
 template <typename TE, int KPL>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void logits_fwd_kernel(LogitsArgs a) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+  // the row is uniform over the wavefront: its addresses live in scalar registers
+  const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (row >= a.N) return;
   constexpr int VEC = Elem<TE>::kVec;
-  TeacherRow<TE, KPL> t;
-  t.load(a, row, lane);
-  const bool keep = a.ids[row * a.K] != kIgnoreId;
-  float gam = 0.f;
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) gam += t.ok[j] ? t.p[j] * t.z[j] : 0.f;
-  gam = wave_sum(gam) * a.inv_T;
-
-  const float c = kLog2e * a.inv_T;
   const int64_t start = row * a.V;
   const TE* zr = (const TE*)a.Z + start;
   const RowSplit rs = split_row<VEC>(start, a.V);
-  OnlineLse acc;
-  if (lane < rs.head) acc.add(Elem<TE>::load(zr + lane) * c);
   const uint4* vp = (const uint4*)(zr + rs.head);
-  int64_t i = lane;
-  for (; i + 64 * (kUnroll - 1) < rs.nvec; i += 64 * kUnroll) {
-    uint4 u[kUnroll];
-#pragma unroll
-    for (int q = 0; q < kUnroll; ++q) u[q] = load_stream(vp + i + 64 * q);
-#pragma unroll
-    for (int q = 0; q < kUnroll; ++q) {
-      float x[VEC];
-      Elem<TE>::unpack(u[q], x);
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) x[j] *= c;
-      acc.add_vec(x);
-    }
+  // Whole groups of kUnroll vectors per lane (the same count for every lane
+  // of the wavefront), streamed with two register buffers: the next group
+  // is in flight while the current one is reduced. The row's first group is
+  // requested before the teacher entries, so their round trips overlap.
+  const int64_t G = rs.nvec / (64 * kUnroll);
+  const uint4* gp = vp + lane;
+  uint4 A[kUnroll], B[kUnroll];
+  if (G > 0) load_group(A, gp);
+  TeacherRow<TE, KPL> t;
+  t.request(a, row, lane);
+  const bool keep = a.ids[row * a.K] != kIgnoreId;
+
+  OnlineLse acc(kLog2e * a.inv_T);
+  if (lane < rs.head) acc.add(Elem<TE>::load(zr + lane));
+  auto reduce = [&](const uint4(&u)[kUnroll]) { acc.add_group<TE>(u); };
+  // (the loads in the loop are unconditional, so each wait covers only the
+  // group about to be used)
+  int64_t g = 0;
+  for (; g + 2 < G; g += 2) {
+    load_group(B, gp + (g + 1) * 64 * kUnroll);
+    reduce(A);
+    load_group(A, gp + (g + 2) * 64 * kUnroll);
+    reduce(B);
   }
+  if (g + 1 < G) {
+    load_group(B, gp + (g + 1) * 64 * kUnroll);
+    reduce(A);
+    reduce(B);
+  } else if (g < G) {
+    reduce(A);
+  }
+  int64_t i = G * 64 * kUnroll + lane;
   for (; i < rs.nvec; i += 64) {
     float x[VEC];
     Elem<TE>::unpack(load_stream(vp + i), x);
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) x[j] *= c;
     acc.add_vec(x);
   }
-  if (lane < rs.tail) acc.add(Elem<TE>::load(zr + rs.head + rs.nvec * VEC + lane) * c);
+  if (lane < rs.tail) acc.add(Elem<TE>::load(zr + rs.head + rs.nvec * VEC + lane));
   acc.wave_merge();
+  t.finish(a, lane);
+  float gam = 0.f;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) gam += t.p[j] * t.z[j];
+  gam = wave_sum(gam) * a.inv_T;
   if (lane == 0) {
-    const float lse = (acc.m + log2_hw(acc.s)) * kLn2;
+    const float lse = acc.lse();
     a.row_lse[row] = lse;
     a.row_kl[row] = keep ? t.e - gam + lse : 0.f;
   }
@@ -276,7 +379,7 @@ template <typename TE, int KPL>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void logits_bwd_kernel(LogitsArgs a) {
   __shared__ int32_t s_id[kRowsPerBlock][64 * KPL];
   __shared__ float s_p[kRowsPerBlock][64 * KPL];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + w;
   if (row >= a.N) return;
   constexpr int VEC = Elem<TE>::kVec;
@@ -344,6 +447,163 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void logits_bwd_kernel(LogitsAr
   }
 }
 
+// The backward on rows that are whole 16-byte vectors (V a multiple of the
+// vector width), each row cut into `pieces` contiguous pieces of `len`
+// vectors with one 256-thread workgroup per piece. Consecutive workgroups
+// then stream consecutive memory (one wavefront per row interleaves four
+// rows per workgroup), which the memory system serves faster for a read and
+// write stream. The workgroup gathers the student logits at the row's teacher
+// ids inside its piece before anything is written (so dZ may be Z), streams
+// the dense part coef * q, and then rewrites those entries with the teacher
+// mass subtracted (one rounding, as the row kernel does).
+constexpr int kPieceThreads = 256;
+constexpr int64_t kPieceVec = 16384;    // target 16-byte vectors per piece
+constexpr int64_t kPieceMinVec = 2048;  // shorter rows take one wavefront each
+
+template <typename TE, int KPS>  // teacher entries per thread: K <= 256 KPS
+__global__ __launch_bounds__(kPieceThreads) void logits_bwd_piece_kernel(LogitsArgs a, int pieces, int64_t len) {
+  constexpr int NT = kPieceThreads;
+  __shared__ int32_t s_id[NT * KPS];
+  __shared__ float s_p[NT * KPS];
+  __shared__ float s_z[NT * KPS];
+  constexpr int VEC = Elem<TE>::kVec;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t row = blockIdx.x / (unsigned)pieces;
+  const int64_t pc = blockIdx.x - row * pieces;
+  const int64_t nvec = a.V / VEC;
+  const int64_t v0 = pc * len;
+  const int64_t v1 = v0 + len < nvec ? v0 + len : nvec;
+  const int64_t c0 = v0 * VEC, c1 = v1 * VEC;  // the piece's columns
+  const TE* zr = (const TE*)a.Z + row * a.V;
+  TE* dr = (TE*)a.dZ + row * a.V;
+  const uint4* vp = (const uint4*)zr;
+  uint4* op = (uint4*)dr;
+  // Whole groups of kUnroll vectors per thread (the same count for the whole
+  // workgroup), streamed with two register buffers A and B, one group ahead.
+  // The first two groups are requested around the teacher entries, so the
+  // piece's first round trips overlap.
+  const int64_t G = (v1 - v0) / (NT * kUnroll);
+  const uint4* gp = vp + v0 + tid;
+  uint4* go = op + v0 + tid;
+  uint4 A[kUnroll], B[kUnroll];
+  if (G > 0) load_group<NT>(A, gp);
+  // The teacher entries (loads clamped to valid addresses, unconditional).
+  const int K = a.K;
+  const int32_t* idr = a.ids + row * K;
+  const float* lgr = a.logits + row * K;
+  int id[KPS];
+  float l[KPS], z[KPS];
+#pragma unroll
+  for (int j = 0; j < KPS; ++j) {
+    const int k = tid + NT * j;
+    const int kk = k < K ? k : K - 1;
+    id[j] = idr[kk];
+    l[j] = lgr[kk] * a.inv_T;
+  }
+  const float scale = a.scale[0];
+  const float lse2 = a.row_lse[row] * kLog2e;
+  // the student logits at the ids inside this piece, read before any store
+  // of the piece (dZ may be Z)
+#pragma unroll
+  for (int j = 0; j < KPS; ++j) {
+    if (tid + NT * j >= K) id[j] = -1;
+    const bool in = id[j] >= c0 && id[j] < c1;
+    z[j] = Elem<TE>::load(zr + (in ? id[j] : c0));
+  }
+  if (G > 1) load_group<NT>(B, gp + NT * kUnroll);
+  const bool keep = __builtin_amdgcn_readfirstlane(idr[0]) != kIgnoreId;
+  const float coef = keep ? scale : 0.f;  // an ignored row's gradient is zero
+  if (keep) {
+    // p = softmax over K of l / T over the whole workgroup
+    __shared__ float s_red[NT / 64];
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < KPS; ++j) mx = fmaxf(mx, tid + NT * j < K ? l[j] : kNegInf);
+    mx = wave_max(mx);
+    if (lane == 0) s_red[tid >> 6] = mx;
+    __syncthreads();
+    mx = s_red[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) mx = fmaxf(mx, s_red[w]);
+    float se = 0.f;
+#pragma unroll
+    for (int j = 0; j < KPS; ++j)
+      if (tid + NT * j < K) se += exp2_hw((l[j] - mx) * kLog2e);
+    se = wave_sum(se);
+    __syncthreads();  // every wavefront has read the maxima
+    if (lane == 0) s_red[tid >> 6] = se;
+    __syncthreads();
+    se = s_red[0];
+#pragma unroll
+    for (int w = 1; w < NT / 64; ++w) se += s_red[w];
+    const float lt = mx + log2_hw(se) * kLn2;
+#pragma unroll
+    for (int j = 0; j < KPS; ++j) {
+      s_id[tid + NT * j] = id[j];
+      s_p[tid + NT * j] = tid + NT * j < K ? exp2_hw((l[j] - lt) * kLog2e) : 0.f;
+      s_z[tid + NT * j] = z[j];
+    }
+  }
+  // Every gather of the workgroup has completed before any store: each
+  // thread waits for its own, then the barrier.
+  __syncthreads();
+  const float c = kLog2e * a.inv_T;
+  auto dense = [&](const uint4& v) {
+    float x[VEC];
+    Elem<TE>::unpack(v, x);
+#pragma unroll
+    for (int j = 0; j < VEC; ++j) x[j] = coef * exp2_hw(__builtin_fmaf(x[j], c, -lse2));
+    return Elem<TE>::pack(x);
+  };
+  auto write = [&](const uint4(&u)[kUnroll], int64_t g) {
+#pragma unroll
+    for (int q = 0; q < kUnroll; ++q) store_stream(go + g * NT * kUnroll + NT * q, dense(u[q]));
+  };
+  // A holds group g and B group g + 1 (in flight) at the top of each step;
+  // the loads in the loop are unconditional, so each wait covers only the
+  // group about to be written
+  int64_t g = 0;
+  for (; g + 3 < G; g += 2) {
+    write(A, g);
+    load_group<NT>(A, gp + (g + 2) * NT * kUnroll);
+    write(B, g + 1);
+    load_group<NT>(B, gp + (g + 3) * NT * kUnroll);
+  }
+  if (g + 2 < G) {
+    write(A, g);
+    load_group<NT>(A, gp + (g + 2) * NT * kUnroll);
+    write(B, g + 1);
+    write(A, g + 2);
+  } else if (g + 1 < G) {
+    write(A, g);
+    write(B, g + 1);
+  } else if (g < G) {
+    write(A, g);
+  }
+  for (int64_t i = v0 + G * NT * kUnroll + tid; i < v1; i += NT) store_stream(op + i, dense(load_stream(vp + i)));
+  if (!keep) return;
+  // Teacher entries of the piece: overwritten with the full value once every
+  // wavefront's dense stores have been performed (same addresses, written
+  // later). Repeated ids add their mass; the first entry of an id writes.
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < KPS; ++j) {
+    const int k = tid + NT * j;
+    const int idk = k < K ? s_id[k] : -1;
+    if (idk < c0 || idk >= c1) continue;
+    float mass = 0.f;
+    bool first = true;
+    for (int q = 0; q < K; ++q) {
+      if (s_id[q] == idk) {
+        mass += s_p[q];
+        first = first && q >= k;
+      }
+    }
+    if (first) Elem<TE>::store(dr + idk, coef * (exp2_hw(__builtin_fmaf(s_z[k], c, -lse2)) - mass));
+  }
+}
+
 // ------------------------------ dense KL ------------------------------------
 // The pages' dense baseline builds the full teacher probability grid from the
 // cached top-K and compares it with the student's full log-probability grid
@@ -363,17 +623,15 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void dense_student_kernel(Dense
   const int tail = (int)(a.V - nvec * VEC);
   const float c = kLog2e * a.inv_T;
   const uint4* vp = (const uint4*)zr;
-  OnlineLse acc;
+  OnlineLse acc(c);
   for (int64_t i = lane; i < nvec; i += 64) {
     float x[VEC];
     Elem<TE>::unpack(load_stream(vp + i), x);
-#pragma unroll
-    for (int j = 0; j < VEC; ++j) x[j] *= c;
     acc.add_vec(x);
   }
-  if (lane < tail) acc.add(Elem<TE>::load(zr + nvec * VEC + lane) * c);
+  if (lane < tail) acc.add(Elem<TE>::load(zr + nvec * VEC + lane));
   acc.wave_merge();
-  const float lse = (acc.m + log2_hw(acc.s)) * kLn2;
+  const float lse = acc.lse();
   for (int64_t i = lane; i < nvec; i += 64) {
     float x[VEC];
     Elem<TE>::unpack(load_stream(vp + i), x);
@@ -517,10 +775,31 @@ hipError_t launch_logits_fwd(int dtype, const LogitsArgs& a, hipStream_t s) {
   return dtype == 1 ? launch_k<FwdLaunch, uint16_t>(a, s) : launch_k<FwdLaunch, float>(a, s);
 }
 
+template <typename TE>
+static hipError_t launch_bwd(const LogitsArgs& a, hipStream_t s) {
+  constexpr int64_t VEC = Elem<TE>::kVec;
+  const int64_t nvec = a.V / VEC;
+  if (a.V % VEC == 0 && nvec >= kPieceMinVec) {
+    const int64_t pieces = (nvec + kPieceVec - 1) / kPieceVec;
+    const int64_t len = (nvec + pieces - 1) / pieces;
+    if (a.N * pieces <= INT32_MAX) {
+      const dim3 grid((unsigned)(a.N * pieces)), block(kPieceThreads);
+      if (a.K <= kPieceThreads)
+        hipLaunchKernelGGL((logits_bwd_piece_kernel<TE, 1>), grid, block, 0, s, a, (int)pieces, len);
+      else if (a.K <= 2 * kPieceThreads)
+        hipLaunchKernelGGL((logits_bwd_piece_kernel<TE, 2>), grid, block, 0, s, a, (int)pieces, len);
+      else
+        hipLaunchKernelGGL((logits_bwd_piece_kernel<TE, 4>), grid, block, 0, s, a, (int)pieces, len);
+      return hipGetLastError();
+    }
+  }
+  return launch_k<BwdLaunch, TE>(a, s);
+}
+
 hipError_t launch_logits_bwd(int dtype, const LogitsArgs& a, hipStream_t s) {
   if (a.N <= 0) return hipSuccess;
   if (a.K < 1 || a.K > 1024) return hipErrorInvalidValue;
-  return dtype == 1 ? launch_k<BwdLaunch, uint16_t>(a, s) : launch_k<BwdLaunch, float>(a, s);
+  return dtype == 1 ? launch_bwd<uint16_t>(a, s) : launch_bwd<float>(a, s);
 }
 
 static dim3 dense_grid(int64_t rows) { return dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)); }

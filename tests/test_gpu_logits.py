@@ -74,6 +74,36 @@ def test_logits_parity_vs_oracle(dtype, kind, N, V, K, T, g):
     _check(got, Z, ids, lg, T, 1.0 if g is None else g, kind, f"{kind} N={N} V={V} K={K}")
 
 
+@pytest.mark.parametrize("dtype,kind,N,V,K,T", [
+    (torch.bfloat16, "bf16", 24, 150000, 100, 1.0),  # two pieces per row
+    (torch.float32, "fp32", 12, 70000, 300, 1.5),    # fp32, two teacher entries per thread
+    (torch.bfloat16, "bf16", 8, 16384, 1024, 1.0),   # one piece per row, K = 1024
+    (torch.bfloat16, "bf16", 10, 16376, 100, 1.0),   # a vector short of the piece path
+])
+def test_logits_long_rows(dtype, kind, N, V, K, T):
+    """Rows of whole 16-byte vectors long enough for the backward's
+    workgroup-per-piece layout (and one just short of it): repeated and
+    dropped ids, an id on each side of a piece boundary, an ignored row, and
+    the in-place gradient equal to the out-of-place one."""
+    print(f"case logits long rows {kind} N={N} V={V} K={K}", flush=True)
+    Z, ids, lg = _problem(dtype, N, V, K, seed=N + V + K)
+    es = 2 if dtype == torch.bfloat16 else 4
+    nvec = V * es // 16
+    pieces = -(-nvec // 16384)
+    edge = -(-nvec // pieces) * (16 // es)  # first column of the second piece
+    ids[0, 1] = ids[0, 0]                      # repeated: the masses add
+    ids[1, 2], ids[1, 3] = V, -3               # outside [0, V): dropped
+    ids[2, 0] = -1                             # ignored position
+    ids[3, 4], ids[3, 5] = edge - 1, min(edge, V - 1)
+    ids[4, 6], ids[4, 7] = 0, V - 1
+    g = 0.9
+    got = _run(Z, ids, lg, T, g)
+    inp = _run(Z, ids, lg, T, g, inplace=True)
+    assert np.array_equal(got["dZ"], inp["dZ"])
+    assert np.all(got["dZ"][2] == 0.0) and got["row_kl"][2] == 0.0
+    _check(got, Z, ids, lg, T, g, kind, f"long rows {kind} N={N} V={V} K={K}")
+
+
 def test_logits_k1_cross_entropy_and_single_entry_vocab():
     import torch.nn.functional as F
 
