@@ -135,19 +135,17 @@ static bool dh_reads_w_in_place(const Plan& P, int64_t N) {
   const double transpose_ms = 4.0 * (double)P.V * (double)P.d / 5.0e9;
   return launches * dh_ms * penalty < transpose_ms + 0.3;
 }
-#ifndef KDKL_DH_BUSY
-#define KDKL_DH_BUSY 0.96
-#endif
+// The dH split count keeps the device within this share of as busy as the
+// best split count does.
+constexpr double kDhBusy = 0.96;
 // Largest accepted kdkl_options.vocab_slices and chunks_per_group.
 constexpr int kMaxVocabSlices = 1024;
 constexpr int kMaxChunksPerGroup = 64;
-
-#ifndef KDKL_BWD_GROUP
-#define KDKL_BWD_GROUP 16
-#endif
-#ifndef KDKL_GROUP_FILL
-#define KDKL_GROUP_FILL 95
-#endif
+// Largest group of the library's own blocking (chunks per backward launch),
+// and the least share (percent) of dW's last round of workgroups its slices
+// must fill.
+constexpr int kMaxOwnGroup = 16;
+constexpr int64_t kDwRoundFill = 95;
 // Largest dZ buffer (group rows x slice rows x element bytes) of the
 // library's own blocking: about 1.5% of the device's memory, independent of
 // the number of positions.
@@ -169,7 +167,7 @@ static int64_t slice_rows(const Plan& P, int64_t slices) {
 static bool dw_fills(const Plan& P, int64_t vpart) {
   const int64_t tiles = (vpart + 255) / 256 * ((P.d + P.dtile - 1) / P.dtile);
   const int64_t rounds = (tiles + kComputeUnits - 1) / kComputeUnits;
-  return tiles >= kComputeUnits && tiles * 100 >= rounds * kComputeUnits * KDKL_GROUP_FILL;
+  return tiles >= kComputeUnits && tiles * 100 >= rounds * kComputeUnits * kDwRoundFill;
 }
 
 // The fewest vocabulary slices for a group of `rows` (padded) positions
@@ -211,7 +209,7 @@ static void choose_blocking(const Plan& P, int64_t N, int bg_set, int64_t slices
     if (slices_set == 0) *slices_out = own_slices(bg_set);
     return;
   }
-  for (int bg = KDKL_BWD_GROUP; bg > 1; bg >>= 1) {
+  for (int bg = kMaxOwnGroup; bg > 1; bg >>= 1) {
     if (bg > chunks || !gemm_fast_path(P.dtype, P.d, P.Vp, group_rows(bg))) continue;
     if (slices_set > 0) {  // a set slicing: the largest group whose dZ buffer it keeps within the budget
       if (slice_rows(P, slices_set) * group_rows(bg) * P.es <= kDzBudget) {
@@ -338,7 +336,7 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   double best = 0.0;
   for (int64_t c = 1; c <= smax; ++c) best = busy(c) > best ? busy(c) : best;
   int64_t S = 1;
-  while (S < smax && busy(S) < KDKL_DH_BUSY * best) ++S;
+  while (S < smax && busy(S) < kDhBusy * best) ++S;
   P->dh_splits = (int)S;
   P->dh_ksplit = round_up((P->vpart + S - 1) / S, kstep);
 
@@ -796,7 +794,8 @@ static kdkl_status check_logits(const void* Z, const int32_t* ids, const float* 
                                 int32_t K, float T, int dtype) {
   if (dtype != KDKL_F32 && dtype != KDKL_BF16) return KDKL_ERR_DTYPE;
   if (N < 0 || V <= 0 || K <= 0 || K > 1024 || K > V) return KDKL_ERR_SHAPE;
-  if (V > ((int64_t)1 << 40) || N > ((int64_t)1 << 40) || N * V > ((int64_t)1 << 60)) return KDKL_ERR_OVERFLOW;
+  if (V > ((int64_t)1 << 40) || N > ((int64_t)1 << 40)) return KDKL_ERR_OVERFLOW;
+  if (N > 0 && V > ((int64_t)1 << 60) / N) return KDKL_ERR_OVERFLOW;  // N V elements, without forming N V
   if (N > 0 && (!Z || !ids || !lg)) return KDKL_ERR_NULL;
   if (!(T > 0.f) || !isfinite(T)) return KDKL_ERR_VALUE;
   if (!aligned16(Z)) return KDKL_ERR_ALIGN;

@@ -229,6 +229,8 @@ def lbwd(lib, **kw):
     (dict(V=0), SHAPE),
     (dict(N=-1), SHAPE),
     (dict(N=1 << 41), OVERFLOW),
+    (dict(N=1 << 40, V=1 << 40), OVERFLOW),  # each size in range, the grid not
+    (dict(N=1 << 31, V=1 << 30), OVERFLOW),
     (dict(dt=3), DTYPE),
     (dict(Z=FAKE + 2), ALIGN),
 ])
