@@ -27,4 +27,8 @@ from .kl import (  # noqa: F401
     alt_forward,
     alt_backward,
     alt_loss_and_grads,
+    topk_rkl_forward,
+    topk_rkl_backward,
+    topk_rkl_loss_and_grads,
+    topk_rkl_sampled,
 )

@@ -94,6 +94,10 @@ __all__ = [
     "alt_forward",
     "alt_backward",
     "alt_loss_and_grads",
+    "topk_rkl_forward",
+    "topk_rkl_backward",
+    "topk_rkl_loss_and_grads",
+    "topk_rkl_sampled",
 ]
 
 
@@ -632,3 +636,158 @@ def jsd_backward(H, W, ids, logits, T: float, beta: float = 0.5, g: float = 1.0,
 def jsd_loss_and_grads(H, W, ids, logits, T: float, beta: float = 0.5, g: float = 1.0,
                        block: int = 256) -> Dict[str, object]:
     return alt_loss_and_grads(H, W, ids, logits, T, "jsd", beta, g, block)
+
+
+# ---------------------------------------------------------------------------
+# Reverse KL over the teacher's top-K support (a reading: the pages report
+# ablations on the choice of loss without naming the losses [P1 "Making
+# knowledge distillation cheap enough to run at scale", section "The
+# resulting student model"]).
+# ---------------------------------------------------------------------------
+# The reverse KL(q || P) is infinite wherever the student puts mass off the
+# teacher's top-K, so it is taken over the support: with P_i the teacher's
+# probabilities on the vocabulary as above (repeated ids add their mass, ids
+# outside [0, V) have none) and S_i = {v : P_iv > 0}, the student's
+# distribution is restricted to S_i and renormalised there,
+#
+#   qt_iv = exp(s_iv) / sum_{u in S_i} exp(s_iu)       (v in S_i),
+#   TRKL_i = KL(qt_i || P_i) = sum_{v in S_i} qt_iv (log qt_iv - log P_iv),
+#
+# and 0 for a position whose support is empty. It depends on the student's
+# logits at S_i only. The loss is the mean over the kept positions (ignored
+# positions as above). Gradient (derived here): with r_v = log(qt_v / P_v),
+# d TRKL_i / d s_v = qt_v (r_v - TRKL_i) on S_i and 0 off it, so
+# dZ_i = g / (N T) * that, dH = dZ W, dW = dZ^T H.
+
+
+def _topk_rkl_parts(s: np.ndarray, P: np.ndarray):
+    """Per row: (TRKL, logsumexp of s over the support, dTRKL/ds) from the
+    tempered student logits ``s`` and the teacher grid ``P`` ([rows, V])."""
+    on = P > 0
+    has = on.any(axis=1)
+    s_on = np.where(on, s, -np.inf)
+    m = np.where(has, s_on.max(axis=1), 0.0)
+    with np.errstate(divide="ignore"):
+        lse = np.where(has, m + np.log(np.exp(s_on - m[:, None]).sum(axis=1)), -np.inf)
+        logP = np.where(on, np.log(np.where(on, P, 1.0)), 0.0)
+    log_qt = np.where(on, s - np.where(has, lse, 0.0)[:, None], 0.0)
+    qt = np.where(on, np.exp(log_qt), 0.0)
+    r = np.where(on, log_qt - logP, 0.0)
+    loss = (qt * r).sum(axis=1)
+    grad = qt * (r - loss[:, None])
+    return loss, lse, grad
+
+
+def topk_rkl_forward(H, W, ids, logits, T: float, block: int = 256) -> Dict[str, object]:
+    """Loss, per-row logsumexp of s = z/T over the teacher's support, and
+    per-row TRKL; fp64 (the student logits formed in full, then restricted)."""
+    H = _f64(H)
+    W = _f64(W)
+    ids = _ids(ids)
+    lg = _f64(logits)
+    n_rows, V = H.shape[0], W.shape[0]
+    kept = kept_positions(ids)
+    ids = _usable_ids(ids, kept)
+    row_lse = np.empty(n_rows)
+    row_kl = np.empty(n_rows)
+    for r0 in range(0, n_rows, block):
+        r1 = min(n_rows, r0 + block)
+        s = (H[r0:r1] @ W.T) / float(T)
+        P = _teacher_grid(ids[r0:r1], lg[r0:r1], T, V)
+        row_kl[r0:r1], row_lse[r0:r1], _ = _topk_rkl_parts(s, P)
+    row_kl[~kept] = 0.0
+    N = int(kept.sum())  # the mean runs over the kept positions
+    loss_v = math.fsum(row_kl.tolist()) / N if N else float("nan")
+    return {"loss": loss_v, "row_lse": row_lse, "row_kl": row_kl}
+
+
+def topk_rkl_backward(H, W, ids, logits, T: float, g: float = 1.0,
+                      block: int = 256) -> Tuple[np.ndarray, np.ndarray]:
+    """Gradients (dH [N, d], dW [V, d]) of ``g * loss`` for TRKL; fp64."""
+    H = _f64(H)
+    W = _f64(W)
+    ids = _ids(ids)
+    lg = _f64(logits)
+    n_rows, V = H.shape[0], W.shape[0]
+    kept = kept_positions(ids)
+    ids = _usable_ids(ids, kept)
+    N = int(kept.sum())
+    coef = float(g) / (N * float(T)) if N else 0.0
+    dH = np.empty_like(H)
+    dW = np.zeros_like(W)
+    for r0 in range(0, n_rows, block):
+        r1 = min(n_rows, r0 + block)
+        s = (H[r0:r1] @ W.T) / float(T)
+        P = _teacher_grid(ids[r0:r1], lg[r0:r1], T, V)
+        _, _, grad = _topk_rkl_parts(s, P)
+        dZ = coef * grad
+        dZ[~kept[r0:r1]] = 0.0
+        dH[r0:r1] = dZ @ W
+        dW += dZ.T @ H[r0:r1]
+    return dH, dW
+
+
+def topk_rkl_loss_and_grads(H, W, ids, logits, T: float, g: float = 1.0,
+                            block: int = 256) -> Dict[str, object]:
+    out = topk_rkl_forward(H, W, ids, logits, T, block)
+    out["dH"], out["dW"] = topk_rkl_backward(H, W, ids, logits, T, g, block)
+    return out
+
+
+def topk_rkl_sampled(H, W, ids, logits, T: float, rows: Iterable[int], vrows: Iterable[int],
+                     g: float = 1.0) -> Dict[str, np.ndarray]:
+    """TRKL results for a few rows of a large problem, and rows ``vrows`` of
+    dW. The loss depends on the student's logits at the support only, so
+    each needed position's logits are formed at its own ids (the same
+    values as the full row, without the rest of it): per sampled position
+    its logsumexp over the support, TRKL and dH row; each dW row sums the
+    positions whose support holds it. The gradient scale counts every kept
+    position of the problem."""
+    Wf = _f64(W)
+    ids_all = _ids(ids)
+    lg_all = _f64(logits)
+    kept = kept_positions(ids_all)
+    N = int(kept.sum())
+    coef = float(g) / (N * float(T)) if N else 0.0
+    V = Wf.shape[0]
+
+    def row_parts(r):
+        idr = ids_all[r]
+        if not kept[r]:
+            return None
+        p, _ = teacher_distribution(lg_all[r:r + 1], T)
+        sup = sorted({int(v) for v in idr if 0 <= v < V})
+        Pv = np.array([p[0][idr == v].sum() for v in sup])
+        on = Pv > 0
+        sup = [v for v, o in zip(sup, on) if o]
+        Pv = Pv[on]
+        if not sup:
+            return sup, np.zeros(0), -np.inf, 0.0
+        s = (Wf[sup] @ _f64(H[r:r + 1])[0]) / float(T)
+        m = s.max()
+        lse = m + math.log(np.exp(s - m).sum())
+        qt = np.exp(s - lse)
+        rv = (s - lse) - np.log(Pv)
+        L = float((qt * rv).sum())
+        return sup, coef * qt * (rv - L), lse, L
+
+    rows = np.asarray(list(rows), dtype=np.int64)
+    lse_out = np.empty(rows.size)
+    kl_out = np.zeros(rows.size)
+    dh_out = np.zeros((rows.size, Wf.shape[1]))
+    for j, r in enumerate(rows.tolist()):
+        parts = row_parts(r)
+        if parts is None:
+            lse_out[j] = np.nan  # not written for an ignored position
+            continue
+        sup, dz, lse_out[j], kl_out[j] = parts
+        if sup:
+            dh_out[j] = dz @ Wf[sup]
+    vrows = np.asarray(list(vrows), dtype=np.int64)
+    dw_out = np.zeros((vrows.size, Wf.shape[1]))
+    for j, v in enumerate(vrows.tolist()):
+        for r in np.nonzero((ids_all == v).any(axis=1) & kept)[0].tolist():
+            sup, dz, _, _ = row_parts(r)
+            if v in sup:
+                dw_out[j] += dz[sup.index(v)] * _f64(H[r:r + 1])[0]
+    return {"rows": rows, "row_lse": lse_out, "row_kl": kl_out, "dH_rows": dh_out, "dW_rows": dw_out}

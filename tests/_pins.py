@@ -924,6 +924,169 @@ def pin_skew_losses_invariants(o):
         raise AssertionError(f"{loss} accepted parameter {bad}")
 
 
+# --- reverse KL over the teacher's top-K support -----------------------------
+
+def _support_problem(rng, N, d, V, K, T):
+    """Random problem with distinct in-range ids; the student's tempered
+    logits at them and the teacher's probabilities, per row."""
+    H, W, ids, logits = _rand_problem(rng, N, d, V, K)
+    s_at = np.stack([(W[ids[i]] @ H[i]) / T for i in range(N)])
+    p = np.stack([sps.softmax(logits[i] / T) for i in range(N)])
+    return H, W, ids, logits, s_at, p
+
+
+def pin_topk_rkl_scipy_entropy(o):
+    """With distinct in-range ids, each position's loss is scipy's relative
+    entropy of the student's softmax over the teacher's ids against the
+    teacher's probabilities (scipy normalises its first argument)."""
+    if not hasattr(o, "topk_rkl_forward"):
+        return
+    rng = np.random.default_rng(61)
+    for T in (1.0, 1.8):
+        N, d, V, K = 6, 5, 23, 7
+        H, W, ids, logits, s_at, p = _support_problem(rng, N, d, V, K, T)
+        ref = np.array([sst.entropy(np.exp(s_at[i] - s_at[i].max()), p[i]) for i in range(N)])
+        out = o.topk_rkl_forward(H, W, ids, logits, T)
+        _close(out["row_kl"], ref, 1e-12, what=f"TRKL rows vs scipy entropy, T={T}")
+        _close(out["loss"], ref.mean(), 1e-12, what=f"TRKL loss vs scipy entropy, T={T}")
+        lse = np.array([sps.logsumexp(s_at[i]) for i in range(N)])
+        _close(out["row_lse"], lse, 1e-12, what="logsumexp over the support")
+
+
+def pin_topk_rkl_torch_autograd(o):
+    """The loss through torch (log-softmax over the gathered student logits,
+    kl_div with log targets) and its gradients by autograd."""
+    if not hasattr(o, "topk_rkl_backward"):
+        return
+    rng = np.random.default_rng(62)
+    N, d, V, K, T, g = 5, 4, 17, 5, 1.3, 0.8
+    H, W, ids, logits = _rand_problem(rng, N, d, V, K)
+    Ht = torch.tensor(H, requires_grad=True)
+    Wt = torch.tensor(W, requires_grad=True)
+    idt = torch.tensor(ids)
+    s = Ht @ Wt.T / T
+    log_qt = torch.log_softmax(torch.gather(s, 1, idt), dim=1)
+    log_p = torch.log_softmax(torch.tensor(logits) / T, dim=1)
+    val = F.kl_div(log_p, log_qt, reduction="sum", log_target=True) / N
+    (g * val).backward()
+    out = o.topk_rkl_forward(H, W, ids, logits, T)
+    _close(out["loss"], val.item(), 1e-12, what="TRKL loss vs kl_div")
+    dH, dW = o.topk_rkl_backward(H, W, ids, logits, T, g)
+    _close(dH, Ht.grad.numpy(), 1e-11, what="TRKL dH vs autograd")
+    _close(dW, Wt.grad.numpy(), 1e-11, what="TRKL dW vs autograd")
+
+
+def pin_topk_rkl_brute_force_and_finite_differences(o):
+    """Pure-Python loops (math module only) with ids outside [0, V), a
+    repeated id (its masses add) and an ignored position; central
+    differences of the loss for every entry of H and W."""
+    if not hasattr(o, "topk_rkl_backward"):
+        return
+    rng = np.random.default_rng(63)
+    N, d, V, K, T, g = 5, 3, 7, 4, 1.6, 0.7
+    H = rng.standard_normal((N, d))
+    W = rng.standard_normal((V, d))
+    ids = np.array([[0, 6, 2, 9], [7, 1, -2, 4], [3, 3, 5, 1], [-1, 2, 0, 4], [6, -5, 0, 6]])
+    logits = rng.standard_normal((N, K))
+    vals = []
+    for i in range(N):
+        if ids[i, 0] == -1:
+            vals.append(0.0)
+            continue
+        t = [logits[i, k] / T for k in range(K)]
+        mt = max(t)
+        zt = sum(math.exp(x - mt) for x in t)
+        p = [math.exp(x - mt) / zt for x in t]
+        sup = sorted({int(v) for v in ids[i] if 0 <= v < V})
+        s = {v: sum(H[i, j] * W[v, j] for j in range(d)) / T for v in sup}
+        ms = max(s.values())
+        lse = ms + math.log(sum(math.exp(s[v] - ms) for v in sup))
+        val = 0.0
+        for v in sup:
+            Pv = sum(p[k] for k in range(K) if ids[i, k] == v)
+            qv = math.exp(s[v] - lse)
+            val += qv * math.log(qv / Pv)
+        vals.append(val)
+    out = o.topk_rkl_forward(H, W, ids, logits, T)
+    _close(out["row_kl"], vals, 1e-12, what="TRKL rows vs brute force")
+    _close(out["loss"], sum(vals) / 4, 1e-12, what="TRKL mean over the kept positions")
+    dH, dW = o.topk_rkl_backward(H, W, ids, logits, T, g)
+    eps = 1e-6
+
+    def loss_at(Hx, Wx):
+        return g * o.topk_rkl_forward(Hx, Wx, ids, logits, T)["loss"]
+
+    fdH = np.zeros_like(H)
+    for i in range(N):
+        for j in range(d):
+            Hp, Hm = H.copy(), H.copy()
+            Hp[i, j] += eps
+            Hm[i, j] -= eps
+            fdH[i, j] = (loss_at(Hp, W) - loss_at(Hm, W)) / (2 * eps)
+    fdW = np.zeros_like(W)
+    for v in range(V):
+        for j in range(d):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[v, j] += eps
+            Wm[v, j] -= eps
+            fdW[v, j] = (loss_at(H, Wp) - loss_at(H, Wm)) / (2 * eps)
+    _close(dH, fdH, 1e-7, what="TRKL dH vs central differences")
+    _close(dW, fdW, 1e-7, what="TRKL dW vs central differences")
+
+
+def pin_topk_rkl_closed_forms_and_invariants(o):
+    """Zero at the teacher (student logits log P + c at the support), zero
+    for a single support entry, the two-entry closed form with the logistic
+    function, independence of the student's logits off the support (no
+    gradient there either), shift invariance, and non-negativity."""
+    if not hasattr(o, "topk_rkl_backward"):
+        return
+    rng = np.random.default_rng(64)
+    # zero at the teacher: W rows at the ids are unit vectors, H_i = T (log p + c)
+    K, V, T = 4, 9, 1.5
+    ids = np.array([[2, 7, 0, 5]])
+    logits = rng.standard_normal((1, K))
+    logp = np.log(sps.softmax(logits[0] / T))
+    W = rng.standard_normal((V, K))
+    W[ids[0]] = np.eye(K)
+    H = (T * (logp + 0.7))[None, :]
+    out = o.topk_rkl_forward(H, W, ids, logits, T)
+    _close(out["loss"], 0.0, 0.0, atol=1e-14, what="TRKL at the teacher")
+    dH, dW = o.topk_rkl_backward(H, W, ids, logits, T)
+    _close(dH, 0.0, 0.0, atol=1e-14, what="TRKL gradient at the teacher")
+    _close(dW, 0.0, 0.0, atol=1e-14, what="TRKL gradient at the teacher")
+    # one support entry: qt = P = 1
+    H1, W1, ids1, lg1 = _rand_problem(rng, 3, 4, 8, 1)
+    _close(o.topk_rkl_forward(H1, W1, ids1, lg1, 1.2)["loss"], 0.0, 0.0, atol=1e-15, what="K = 1")
+    _close(o.topk_rkl_backward(H1, W1, ids1, lg1, 1.2)[0], 0.0, 0.0, atol=1e-15, what="K = 1 gradient")
+    # two entries: qt_1 = expit(s_1 - s_2)
+    N, d, V, T = 4, 3, 6, 0.8
+    H2, W2, ids2, lg2 = _rand_problem(rng, N, d, V, 2)
+    ref = []
+    for i in range(N):
+        s1, s2 = (W2[ids2[i]] @ H2[i]) / T
+        q1, q2 = sps.expit(s1 - s2), sps.expit(s2 - s1)
+        p1, p2 = sps.expit((lg2[i, 0] - lg2[i, 1]) / T), sps.expit((lg2[i, 1] - lg2[i, 0]) / T)
+        ref.append(q1 * math.log(q1 / p1) + q2 * math.log(q2 / p2))
+    _close(o.topk_rkl_forward(H2, W2, ids2, lg2, T)["row_kl"], ref, 1e-12, what="two-entry closed form")
+    # off the support: other vocabulary rows change nothing and get no gradient
+    N, d, V, K, T = 5, 4, 20, 3, 1.1
+    H3, W3, ids3, lg3 = _rand_problem(rng, N, d, V, K)
+    off = np.setdiff1d(np.arange(V), ids3.reshape(-1))
+    W3b = W3.copy()
+    W3b[off] = rng.standard_normal((off.size, d)) * 25.0
+    a = o.topk_rkl_forward(H3, W3, ids3, lg3, T)
+    b = o.topk_rkl_forward(H3, W3b, ids3, lg3, T)
+    _close(b["row_kl"], a["row_kl"], 1e-12, what="TRKL independent of off-support logits")
+    _, dW3 = o.topk_rkl_backward(H3, W3b, ids3, lg3, T)
+    assert np.all(dW3[off] == 0.0), "TRKL gradient off the support"
+    assert np.all(a["row_kl"] >= -1e-15), "TRKL is a divergence"
+    # shift: one more hidden unit adding the same constant to every logit
+    H4 = np.concatenate([H3, np.ones((N, 1))], axis=1)
+    W4 = np.concatenate([W3, np.full((V, 1), 3.7)], axis=1)
+    _close(o.topk_rkl_forward(H4, W4, ids3, lg3, T)["row_kl"], a["row_kl"], 1e-12, what="shift invariance")
+
+
 ALL_PINS = [
     pin_two_token_softplus,
     pin_uniform_student,
@@ -951,4 +1114,8 @@ ALL_PINS = [
     pin_skew_losses_brute_force_and_finite_differences,
     pin_skew_losses_bounds_and_limits,
     pin_skew_losses_invariants,
+    pin_topk_rkl_scipy_entropy,
+    pin_topk_rkl_torch_autograd,
+    pin_topk_rkl_brute_force_and_finite_differences,
+    pin_topk_rkl_closed_forms_and_invariants,
 ]

@@ -76,6 +76,14 @@ MUTANTS = [
     ("srkl_mixture_ignores_alpha", "logM = np.logaddexp(math.log(alpha) + logq, lb + logP)",
      "logM = np.logaddexp(math.log(0.5) + logq, math.log(0.5) + logP)"),
     ("srkl_loss_sign", "loss = (q * r).sum(axis=1)", "loss = (q * -r).sum(axis=1)"),
+    # the reverse KL over the teacher's top-K support
+    ("trkl_full_vocabulary_normaliser", "    s_on = np.where(on, s, -np.inf)\n", "    s_on = s\n"),
+    ("trkl_gradient_without_mean", "grad = qt * (r - loss[:, None])", "grad = qt * r"),
+    ("trkl_teacher_log_sign", "r = np.where(on, log_qt - logP, 0.0)", "r = np.where(on, log_qt + logP, 0.0)"),
+    ("trkl_student_no_temperature", "        s = (H[r0:r1] @ W.T) / float(T)\n        P = _teacher_grid(ids[r0:r1], lg[r0:r1], T, V)\n        row_kl[r0:r1], row_lse[r0:r1], _ = _topk_rkl_parts(s, P)",
+     "        s = (H[r0:r1] @ W.T)\n        P = _teacher_grid(ids[r0:r1], lg[r0:r1], T, V)\n        row_kl[r0:r1], row_lse[r0:r1], _ = _topk_rkl_parts(s, P)"),
+    ("trkl_gradient_dense_off_support", "grad = qt * (r - loss[:, None])",
+     "grad = np.where(on, qt * (r - loss[:, None]), -np.exp(s - np.where(has, lse, 0.0)[:, None]) * 1e-3)"),
     # ignored positions
     ("ignored_counted_in_mean", "N = int(kept.sum())  # the mean runs over the kept positions",
      "N = kept.size  # the mean runs over the kept positions"),
