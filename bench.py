@@ -92,7 +92,10 @@ def cpu_baseline(w, x, rows: int, loss: str = "kl", beta: float = 0.5):
         threads = len(os.sched_getaffinity(0))
     H, ids, lg = x["H"][:rows], x["ids"][:rows], x["logits"][:rows]
     t0 = time.perf_counter()
-    if loss != "kl":
+    if loss == "trkl":
+        oracle.topk_rkl_forward(H, x["W"], ids, lg, w.T)
+        oracle.topk_rkl_backward(H, x["W"], ids, lg, w.T)
+    elif loss != "kl":
         oracle.alt_forward(H, x["W"], ids, lg, w.T, loss, beta)
         oracle.alt_backward(H, x["W"], ids, lg, w.T, loss, beta)
     else:
@@ -400,9 +403,10 @@ def main():
     ap.add_argument("--gen-reading", choices=("1based", "0based"), default="1based",
                     help="reading of the workload list's cross-references for the teacher "
                          "generator of the 8K and 256K workloads (1based: uniform ids, N(0, 2))")
-    ap.add_argument("--loss", choices=("kl", "jsd", "skl", "srkl"), default="kl",
+    ap.add_argument("--loss", choices=("kl", "jsd", "skl", "srkl", "trkl"), default="kl",
                     help="kl: the pages' forward KL (default); jsd: the generalised Jensen-Shannon "
-                         "divergence; skl / srkl: the skew KL / skew reverse KL (kdkl_options.loss)")
+                         "divergence; skl / srkl: the skew KL / skew reverse KL; trkl: the reverse KL "
+                         "over the teacher's top-K support (kdkl_options.loss)")
     ap.add_argument("--beta", type=float, default=0.5, help="the JSD's weight beta")
     ap.add_argument("--alpha", type=float, default=0.1, help="the skew losses' alpha")
     ap.add_argument("--chunks-per-group", type=int, default=0,
@@ -460,7 +464,8 @@ def main():
             "dh_w_in_place": args.dh_w_in_place}
     loss_param = args.beta if args.loss == "jsd" else args.alpha
     if args.loss != "kl":
-        codes = {"jsd": kd.KDKL_LOSS_JSD, "skl": kd.KDKL_LOSS_SKL, "srkl": kd.KDKL_LOSS_SRKL}
+        codes = {"jsd": kd.KDKL_LOSS_JSD, "skl": kd.KDKL_LOSS_SKL, "srkl": kd.KDKL_LOSS_SRKL,
+                 "trkl": kd.KDKL_LOSS_TRKL}
         opts.update(loss=codes[args.loss], beta=loss_param)
     plan = kd.plan_info(w.N, w.d, w.V, w.K, w.chunk, H.dtype, opts)
     log(f"bench: plan {plan}")
@@ -536,7 +541,12 @@ def main():
     log(f"bench: {ms:.2f} ms/step")
 
     dtype = "bf16" if w.dtype == "bf16" else "fp32"
-    flops_step = 8.0 * w.N * w.V * w.d
+    # the matrix work of a step: four vocabulary-wide products (forward,
+    # recompute, dH, dW); the reverse KL over the top-K support runs the dH
+    # and dW products only, plus the support's dot products (2 N K d flop in
+    # each call)
+    flops_step = (4.0 * w.N * w.V * w.d + 4.0 * w.N * w.K * w.d if args.loss == "trkl"
+                  else 8.0 * w.N * w.V * w.d)
     peak = PEAK_TFLOPS[dtype]
     tok_s = w.N / (ms / 1e3)
     mfma_pct = 100.0 * flops_step / (ms / 1e3) / (peak * 1e12)
@@ -569,14 +579,14 @@ def main():
                    "T": w.T, "teacher_ids": w.id_dist, "teacher_logit_var": w.logit_var,
                    "gen_reading": args.gen_reading,
                    "seed": args.seed if args.seed is not None else wl.seed_for(w),
-                   "loss": (args.loss if args.loss == "kl" else
+                   "loss": (args.loss if args.loss in ("kl", "trkl") else
                             f"jsd(beta={args.beta})" if args.loss == "jsd" else f"{args.loss}(alpha={args.alpha})"),
                    "plan": plan,
                    "parallelism": "single GPU"},
         "mfma_util_pct": round(mfma_pct, 2),
         # the same time against the 6 N V d flop of forward + dH + dW alone
         # (the recompute is part of the method and counted above)
-        "mfma_util_pct_without_recompute": round(mfma_pct * 0.75, 2),
+        "mfma_util_pct_without_recompute": None if args.loss == "trkl" else round(mfma_pct * 0.75, 2),
         "flop_per_step": flops_step,
         "peak_hbm_gib": round(peak_gib, 3),
         "workspace_gib": {"forward": round(fb / 2**30, 3), "backward": round(bb / 2**30, 3)},

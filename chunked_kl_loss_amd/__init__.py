@@ -17,7 +17,8 @@ from typing import Optional, Tuple
 
 import torch
 
-from ._lib import (KDKL_BF16, KDKL_F32, KDKL_LOSS_JSD, KDKL_LOSS_KL, KDKL_LOSS_SKL, KDKL_LOSS_SRKL, KdklError,
+from ._lib import (KDKL_BF16, KDKL_F32, KDKL_LOSS_JSD, KDKL_LOSS_KL, KDKL_LOSS_SKL, KDKL_LOSS_SRKL, KDKL_LOSS_TRKL,
+                   KdklError,
                    KernelStat, Options, Plan,
                    check, load as _load)
 
@@ -99,7 +100,8 @@ def _options(options):
 def saved_shape(N: int, options=None) -> Tuple[int, ...]:
     """Shape of the per-position state the forward saves for the backward
     (``row_lse``): [N] for the KL, [2, N] for the alternative losses (JSD,
-    skew KL, skew reverse KL: logsumexp, then sum_v q_v g_v)."""
+    skew KL, skew reverse KL: logsumexp, then sum_v q_v g_v; reverse KL over
+    the top-K support: logsumexp over the support, then the loss)."""
     if options is not None and int(options.get("loss", KDKL_LOSS_KL)) != KDKL_LOSS_KL:
         return (2, N)
     return (N,)

@@ -23,6 +23,7 @@ KDKL_LOSS_KL = 0
 KDKL_LOSS_JSD = 1
 KDKL_LOSS_SKL = 2
 KDKL_LOSS_SRKL = 3
+KDKL_LOSS_TRKL = 4
 
 
 class KdklError(RuntimeError):

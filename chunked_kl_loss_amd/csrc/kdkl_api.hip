@@ -22,7 +22,8 @@ const char* kernel_name(int id) {
       "teacher_prep", "fwd_gemm_lse", "split_merge", "loss_reduce", "transpose_w",
       "transpose_h",  "dz_gemm",      "dh_gemm",     "dh_reduce",   "dw_gemm",
       "logits_fwd",   "logits_bwd",   "grad_scale",  "dense_gemm",  "dense_student",
-      "dense_teacher", "dense_kl",    "dense_grad",  "jsd_merge",     "jsd_prep"};
+      "dense_teacher", "dense_kl",    "dense_grad",  "jsd_merge",     "jsd_prep",
+      "topk_rkl",      "topk_scatter"};
   return (id >= 0 && id < K_COUNT) ? names[id] : "?";
 }
 
@@ -110,11 +111,13 @@ struct Plan {
   int dtile;       // N-tile width of the dH and dW products (hidden-size axis)
   int loss;        // kdkl_loss
   float beta;      // the loss's parameter (JSD beta, skew alpha)
+  bool epi_alt;    // an alternative loss formed in the projections' epilogues (JSD, skew KL, skew reverse KL)
+  bool trkl;       // the reverse KL over the top-K support (no vocabulary-wide forward)
   // offsets into the forward workspace
   size_t f_ent, f_erow, f_keep, f_tstart, f_part, f_sk, f_red, f_rowkl, f_bytes;
   // offsets into the backward workspace
-  size_t b_ent, b_erow, b_keep, b_scale, b_red, b_tstart, b_rowcoef, b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart,
-      b_dhacc, b_bytes;
+  size_t b_ent, b_erow, b_keep, b_scale, b_red, b_tstart, b_rowcoef, b_dzent, b_wt, b_ht, b_dzcv, b_dzvc,
+      b_dhpart, b_dhacc, b_bytes;
 };
 
 // The dH product on the bf16 main loop reads either a W^T copy written once
@@ -253,6 +256,7 @@ static kdkl_status check_options(const kdkl_options* o) {
     case KDKL_LOSS_JSD: if (!(a > 0.f && a < 1.f)) return KDKL_ERR_OPTION; break;
     case KDKL_LOSS_SKL: if (!(a >= 0.f && a < 1.f)) return KDKL_ERR_OPTION; break;
     case KDKL_LOSS_SRKL: if (!(a > 0.f && a <= 1.f)) return KDKL_ERR_OPTION; break;
+    case KDKL_LOSS_TRKL: break;
     default: return KDKL_ERR_OPTION;
   }
   if (o->chunks_per_group < 0 || o->chunks_per_group > kMaxChunksPerGroup) return KDKL_ERR_OPTION;
@@ -289,7 +293,9 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   if (ost != KDKL_OK) return ost;
   const kdkl_options o = opts ? *opts : kdkl_options{};
   P->loss = o.loss;
-  P->beta = o.loss != KDKL_LOSS_KL ? o.beta : 0.f;
+  P->epi_alt = o.loss == KDKL_LOSS_JSD || o.loss == KDKL_LOSS_SKL || o.loss == KDKL_LOSS_SRKL;
+  P->trkl = o.loss == KDKL_LOSS_TRKL;
+  P->beta = P->epi_alt ? o.beta : 0.f;
   int bg = 1;
   int64_t slices = 1;
   if (P->fast) {
@@ -354,7 +360,7 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   ok &= region(&cur, t2, &P->f_part);
   // the alternative losses' student logits at the sorted teacher entries [Cg, K]
   int64_t sk = 0;
-  if (P->loss != KDKL_LOSS_KL) ok &= mul_ok(P->Cg, K, &sk) && mul_ok(sk, 4, &sk);
+  if (P->epi_alt) ok &= mul_ok(P->Cg, K, &sk) && mul_ok(sk, 4, &sk);
   P->f_sk = 0;
   if (sk) ok &= region(&cur, sk, &P->f_sk);
   ok &= region(&cur, (int64_t)kReduceBytes, &P->f_red);  // the loss's partial sums
@@ -371,7 +377,9 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   ok &= region(&cur, (int64_t)kReduceBytes, &P->b_red);  // the kept count's partial sums
   ok &= region(&cur, g1, &P->b_tstart);
   P->b_rowcoef = 0;
-  if (P->loss != KDKL_LOSS_KL) ok &= region(&cur, P->Cg * 4, &P->b_rowcoef);
+  if (P->epi_alt) ok &= region(&cur, P->Cg * 4, &P->b_rowcoef);
+  P->b_dzent = 0;
+  if (P->trkl) ok &= region(&cur, g0 / 2, &P->b_dzent);  // [Cg, K] fp32 entry gradients
   int64_t wt, ht, dz, dhp;
   ok &= mul_ok(d, P->Vp, &wt) && mul_ok(wt, P->es, &wt);
   ok &= mul_ok(d, P->Cg, &ht) && mul_ok(ht, P->es, &ht);
@@ -451,6 +459,16 @@ static JsdArgs jsd_args(const Plan& P, int rows, char* ws, size_t o_ent, size_t 
   return j;
 }
 
+static TopkArgs topk_args(const Plan& P, const void* H, const void* W, float T, int64_t r0, int rows, char* ws,
+                          size_t o_ent, size_t o_keep) {
+  TopkArgs t;
+  memset(&t, 0, sizeof(t));
+  t.H = (const char*)H + r0 * P.d * P.es; t.W = W;
+  t.V = P.V; t.d = P.d; t.rows = rows; t.K = (int)P.K; t.inv_T = 1.0f / T;
+  t.ent = (const int2*)(ws + o_ent); t.keep = (const float*)(ws + o_keep);
+  return t;
+}
+
 }  // namespace kdkl
 
 using namespace kdkl;
@@ -519,17 +537,25 @@ static hipError_t forward_launches(const Plan& P, const void* H, const void* W, 
         teacher_args(P, ids, lg, T, r0, rows, P.Cg, ws, P.f_ent, P.f_erow, P.f_keep, P.f_tstart);
     e = timed(K_TEACHER, 0.0, (double)rows * P.K * 8.0 * 2.0, s, [&] { return launch_teacher(ta, s); });
     if (e != hipSuccess) break;
+    if (P.trkl) {
+      // the student's logits at the support only: no projection
+      TopkArgs t = topk_args(P, H, W, T, r0, rows, ws, P.f_ent, P.f_keep);
+      t.row_lse = row_lse + r0; t.row_loss = row_lse + N + r0; t.row_kl = kl + r0;
+      e = timed(K_TOPK_RKL, 2.0 * rows * (double)P.K * d, (double)rows * P.K * (d * P.es + 8.0), s,
+                [&] { return launch_topk_rkl(P.dtype, t, false, s); });
+      continue;
+    }
     GemmArgs g = projection_args(P, H, W, T, r0, rows, ws, P.f_ent, P.f_tstart);
     g.Cp = P.Cg;
     g.part = (float4*)(ws + P.f_part);
     // the alternative losses need s at each teacher entry: the epilogue
     // keeps it as it meets the entry
-    g.sk = P.loss != KDKL_LOSS_KL ? (float*)(ws + P.f_sk) : nullptr;
+    g.sk = P.epi_alt ? (float*)(ws + P.f_sk) : nullptr;
     const double fl = 2.0 * rows * (double)V * d;
     const double by = ((double)V + rows) * d * P.es + (double)rows * P.n_vt * 16.0;
     e = timed(K_FWD_GEMM, fl, by, s, [&] { return launch_gemm(P.dtype, EPI_FWD, g, s); });
     if (e != hipSuccess) break;
-    if (P.loss != KDKL_LOSS_KL) {
+    if (P.epi_alt) {
       // lse, the loss and gbar per row from the partials and the kept student
       // logits; gbar is saved after the N logsumexps for the backward
       JsdArgs j = jsd_args(P, rows, ws, P.f_ent, P.f_keep);
@@ -752,7 +778,27 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
     e = timed(K_TRANSPOSE_H, 0.0, 2.0 * (double)rows * d * P.es, s, [&] {
       return launch_transpose((int)P.es, Hg, rows, d, d, ws + P.b_ht, rows_pad, P.Cg, s);
     });
-    if (e == hipSuccess && P.loss != KDKL_LOSS_KL) {
+    if (e == hipSuccess && P.trkl) {
+      // the loss's gradient at each support entry, from the forward's
+      // logsumexp and loss; each vocabulary slice's dZ is zero elsewhere
+      TopkArgs t = topk_args(P, H, W, T, r0, rows, ws, P.b_ent, P.b_keep);
+      t.row_lse = const_cast<float*>(row_lse) + r0; t.row_loss = const_cast<float*>(row_lse) + N + r0;
+      t.scale = (const float*)(ws + P.b_scale); t.dz = (float*)(ws + P.b_dzent);
+      e = timed(K_TOPK_RKL, 2.0 * rows * (double)P.K * d, (double)rows * P.K * (d * P.es + 12.0), s,
+                [&] { return launch_topk_rkl(dtype, t, true, s); });
+      for (int part = 0; part < P.n_parts && e == hipSuccess; ++part) {
+        const int64_t v0 = part * P.vpart;
+        const int64_t vlen = V - v0 < P.vpart ? V - v0 : P.vpart;
+        e = timed(K_TOPK_SCATTER, 0.0, (P.fast ? 1.0 : 2.0) * (double)P.Cg * P.vpart * P.es, s, [&] {
+          return launch_topk_scatter(dtype, (const int2*)(ws + P.b_ent), (const float*)(ws + P.b_dzent), rows,
+                                     (int)P.K, v0, vlen, ws + P.b_dzcv, P.vpart,
+                                     P.fast ? nullptr : ws + P.b_dzvc, P.Cg, P.Cg * P.vpart, s);
+        });
+        if (e == hipSuccess) e = part_products(P, dtype, W, ws, r0, rows, part, dH, dW, r0 > 0 || accumulate_dW, s);
+      }
+      continue;
+    }
+    if (e == hipSuccess && P.epi_alt) {
       // from the forward's gbar, each row's coefficient of q in dZ; the
       // teacher mass of each distinct id over its first entry
       JsdArgs j = jsd_args(P, rows, ws, P.b_ent, P.b_keep);
@@ -772,7 +818,7 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
       g.tiles_m = (int)((vlen + P.vt - 1) / P.vt);
       g.Cp = P.Cg; g.Vp = P.vpart;
       g.row_lse = row_lse + r0; g.scale = (const float*)(ws + P.b_scale); g.keep = (const float*)(ws + P.b_keep);
-      const bool alt = P.loss != KDKL_LOSS_KL;
+      const bool alt = P.epi_alt;
       g.rowcoef = alt ? (const float*)(ws + P.b_rowcoef) : nullptr;
       g.beta = alt ? P.beta : 0.f;
       g.alt = alt ? P.loss : 0;

@@ -37,6 +37,8 @@ enum KernelId {
   K_DENSE_GRAD,
   K_JSD_MERGE,
   K_JSD_PREP,
+  K_TOPK_RKL,
+  K_TOPK_SCATTER,
   K_COUNT
 };
 
@@ -154,6 +156,36 @@ struct JsdArgs {
 };
 hipError_t launch_jsd_merge(const JsdArgs& a, hipStream_t s);
 hipError_t launch_jsd_prep(const JsdArgs& a, hipStream_t s);
+
+// The reverse KL over the teacher's top-K support. Per position, the support
+// is the first sorted entry of each teacher id in [0, V) with teacher mass
+// (the masses of repeated ids added); the student's logits there are dot
+// products of W's rows with the position's H (no vocabulary-wide work).
+// Forward: their logsumexp and the loss per position. Backward: the loss's
+// gradient g / (N_kept T) dTRKL/ds at each support entry (0 at every other
+// sorted entry), from the forward's logsumexp and loss.
+struct TopkArgs {
+  const void* H;      // [rows, d] storage dtype, the group's first position
+  const void* W;      // [V, d]
+  int64_t V, d;
+  int rows, K;
+  float inv_T;
+  const int2* ent;    // [Cp, K] sorted teacher entries (id, bits of p)
+  const float* keep;  // [Cp]
+  float* row_lse;     // forward out, backward in (group-offset): logsumexp of s over the support
+  float* row_loss;    // forward out, backward in (group-offset): the loss per position
+  float* row_kl;      // forward out (group-offset): the loss, 0 at ignored positions
+  const float* scale; // backward: device scalar g / (N_kept T)
+  float* dz;          // backward out: [Cp, K] per sorted entry
+};
+hipError_t launch_topk_rkl(int dtype, const TopkArgs& a, bool backward, hipStream_t s);
+// A slice [v0, v0 + vlen) of the dZ buffers of `rows` positions from the
+// entry gradients: both buffers zeroed (cv: cv_elems elements; vc, when not
+// NULL, as many), then each nonzero entry gradient with an id in the slice
+// written to cv[r, id - v0] (row pitch ld_cv) and vc[id - v0, r] (pitch ld_vc).
+hipError_t launch_topk_scatter(int dtype, const int2* ent, const float* dz, int rows, int K, int64_t v0,
+                               int64_t vlen, void* cv, int64_t ld_cv, void* vc, int64_t ld_vc,
+                               int64_t cv_elems, hipStream_t s);
 
 hipError_t launch_teacher(const TeacherArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);

@@ -191,6 +191,156 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void jsd_prep_kernel(JsdArgs a)
 
 dim3 rows_grid(int rows) { return dim3((unsigned)((rows + kRowsPerBlock - 1) / kRowsPerBlock)); }
 
+// ---------------------------------------------------------------------------
+// Reverse KL over the teacher's top-K support (one wavefront per position):
+// the student's distribution restricted to the support S (the distinct
+// in-range teacher ids with mass) and renormalised there, qt = softmax(s_S),
+// and TRKL = sum_S qt (log qt - log P). It needs the student's logits at S
+// only: each is a dot product of a row of W with the position's H, read as
+// 16-byte vectors across the wavefront. Its gradient in s is
+// qt (log(qt / P) - TRKL) on S and 0 elsewhere.
+// ---------------------------------------------------------------------------
+template <typename TE>
+struct Vec16;
+template <>
+struct Vec16<uint16_t> {  // bf16 bits
+  static constexpr int kN = 8;
+  __device__ static void unpack(const uint4& u, float (&x)[8]) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[2 * j] = __builtin_bit_cast(float, w[j] << 16);
+      x[2 * j + 1] = __builtin_bit_cast(float, w[j] & 0xffff0000u);
+    }
+  }
+  __device__ static void store(uint16_t* p, float v) { *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
+};
+template <>
+struct Vec16<float> {
+  static constexpr int kN = 4;
+  __device__ static void unpack(const uint4& u, float (&x)[4]) {
+    x[0] = __builtin_bit_cast(float, u.x);
+    x[1] = __builtin_bit_cast(float, u.y);
+    x[2] = __builtin_bit_cast(float, u.z);
+    x[3] = __builtin_bit_cast(float, u.w);
+  }
+  __device__ static void store(float* p, float v) { *p = v; }
+};
+
+__device__ __forceinline__ float wmax(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+template <typename TE>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_kernel(TopkArgs a, int backward) {
+  __shared__ float s_s[kRowsPerBlock][1024];  // s at each sorted entry of the support
+  __shared__ float s_P[kRowsPerBlock][1024];  // its teacher mass (0 off the support)
+  constexpr int VEC = Vec16<TE>::kN;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = blockIdx.x * kRowsPerBlock + w;
+  if (row >= a.rows) return;
+  const int K = a.K;
+  const int2* ent = a.ent + (int64_t)row * K;
+  const bool keep = a.keep[row] != 0.f;
+  const int64_t nvec = a.d / VEC;
+  const uint4* hp = (const uint4*)((const TE*)a.H + (int64_t)row * a.d);
+  for (int k = 0; k < K; ++k) {  // the same entry across the wavefront
+    const int2 e = ent[k];
+    float P = 0.f;
+    if (keep && e.x >= 0 && e.x < a.V && (k == 0 || ent[k - 1].x != e.x)) {
+      P = __int_as_float(e.y);
+      for (int k2 = k + 1; k2 < K && ent[k2].x == e.x; ++k2) P += __int_as_float(ent[k2].y);
+    }
+    float sv = 0.f;
+    if (P > 0.f) {
+      const uint4* wp = (const uint4*)((const TE*)a.W + (int64_t)e.x * a.d);
+      float acc = 0.f;
+      for (int64_t j = lane; j < nvec; j += 64) {
+        float x[VEC], y[VEC];
+        Vec16<TE>::unpack(wp[j], x);
+        Vec16<TE>::unpack(hp[j], y);
+#pragma unroll
+        for (int q = 0; q < VEC; ++q) acc = __builtin_fmaf(x[q], y[q], acc);
+      }
+      sv = wsum(acc) * a.inv_T;
+    }
+    if (lane == 0) {
+      s_s[w][k] = sv;
+      s_P[w][k] = P;
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (!backward) {
+    float m = kNegInf;
+    for (int k = lane; k < K; k += 64)
+      if (s_P[w][k] > 0.f) m = fmaxf(m, s_s[w][k]);
+    m = wmax(m);
+    float se = 0.f;
+    for (int k = lane; k < K; k += 64)
+      if (s_P[w][k] > 0.f) se += exp_hw(s_s[w][k] - m);
+    se = wsum(se);
+    const float lse = m > kNegInf ? m + log_hw(se) : kNegInf;
+    float L = 0.f;
+    for (int k = lane; k < K; k += 64) {
+      const float P = s_P[w][k];
+      if (P > 0.f) {
+        const float lq = s_s[w][k] - lse;
+        L += exp_hw(lq) * (lq - log_hw(P));
+      }
+    }
+    L = wsum(L);
+    if (lane == 0) {
+      a.row_lse[row] = lse;
+      a.row_loss[row] = L;
+      a.row_kl[row] = keep ? L : 0.f;
+    }
+    return;
+  }
+  // the gradient at each sorted entry, from the forward's logsumexp and loss
+  const float lse = a.row_lse[row], L = a.row_loss[row];
+  const float coef = keep ? a.scale[0] : 0.f;
+  for (int k = lane; k < K; k += 64) {
+    const float P = s_P[w][k];
+    float gk = 0.f;
+    if (P > 0.f) {
+      const float lq = s_s[w][k] - lse;
+      gk = coef * exp_hw(lq) * (lq - log_hw(P) - L);
+    }
+    a.dz[(int64_t)row * K + k] = gk;
+  }
+}
+
+__global__ __launch_bounds__(256) void zero16_kernel(uint4* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+template <typename TE>
+__global__ __launch_bounds__(256) void topk_scatter_kernel(const int2* ent, const float* dz, int64_t n, int K,
+                                                           int64_t v0, int64_t vlen, TE* cv, int64_t ld_cv,
+                                                           TE* vc, int64_t ld_vc) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const float g = dz[i];
+  if (g == 0.f) return;  // off the support (the buffers are zero there)
+  const int64_t c = (int64_t)ent[i].x - v0;
+  if (c < 0 || c >= vlen) return;
+  const int64_t r = i / K;
+  Vec16<TE>::store(cv + r * ld_cv + c, g);
+  if (vc) Vec16<TE>::store(vc + c * ld_vc + r, g);
+}
+
+hipError_t zero_bytes(void* p, int64_t bytes, hipStream_t s) {
+  const int64_t n = bytes / 16;
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(zero16_kernel, dim3((unsigned)blocks), dim3(256), 0, s, (uint4*)p, n);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_jsd_merge(const JsdArgs& a, hipStream_t s) {
@@ -204,6 +354,38 @@ hipError_t launch_jsd_prep(const JsdArgs& a, hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
   if (a.K < 1 || a.K > 1024) return hipErrorInvalidValue;
   hipLaunchKernelGGL(jsd_prep_kernel, rows_grid(a.rows), dim3(64 * kRowsPerBlock), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_rkl(int dtype, const TopkArgs& a, bool backward, hipStream_t s) {
+  if (a.rows <= 0) return hipSuccess;
+  if (a.K < 1 || a.K > 1024) return hipErrorInvalidValue;
+  if (a.d % (dtype == 1 ? 8 : 4) != 0) return hipErrorInvalidValue;  // rows of whole 16-byte vectors
+  if (dtype == 1)
+    hipLaunchKernelGGL(topk_rkl_kernel<uint16_t>, rows_grid(a.rows), dim3(64 * kRowsPerBlock), 0, s, a,
+                       backward ? 1 : 0);
+  else
+    hipLaunchKernelGGL(topk_rkl_kernel<float>, rows_grid(a.rows), dim3(64 * kRowsPerBlock), 0, s, a,
+                       backward ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_scatter(int dtype, const int2* ent, const float* dz, int rows, int K, int64_t v0,
+                               int64_t vlen, void* cv, int64_t ld_cv, void* vc, int64_t ld_vc,
+                               int64_t cv_elems, hipStream_t s) {
+  const int64_t es = dtype == 1 ? 2 : 4;
+  if ((cv_elems * es) % 16 != 0) return hipErrorInvalidValue;
+  hipError_t e = zero_bytes(cv, cv_elems * es, s);
+  if (e == hipSuccess && vc) e = zero_bytes(vc, cv_elems * es, s);
+  const int64_t n = (int64_t)rows * K;
+  if (e != hipSuccess || n <= 0) return e;
+  const dim3 grid((unsigned)((n + 255) / 256));
+  if (dtype == 1)
+    hipLaunchKernelGGL(topk_scatter_kernel<uint16_t>, grid, dim3(256), 0, s, ent, dz, n, K, v0, vlen,
+                       (uint16_t*)cv, ld_cv, (uint16_t*)vc, ld_vc);
+  else
+    hipLaunchKernelGGL(topk_scatter_kernel<float>, grid, dim3(256), 0, s, ent, dz, n, K, v0, vlen, (float*)cv,
+                       ld_cv, (float*)vc, ld_vc);
   return hipGetLastError();
 }
 

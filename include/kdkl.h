@@ -99,7 +99,8 @@ typedef enum {
   KDKL_LOSS_KL = 0,  /* forward KL(teacher top-K || student), the pages' loss */
   KDKL_LOSS_JSD = 1, /* generalised Jensen-Shannon divergence, weight beta */
   KDKL_LOSS_SKL = 2, /* skew KL(P || alpha P + (1 - alpha) q), alpha = beta */
-  KDKL_LOSS_SRKL = 3 /* skew reverse KL(q || alpha q + (1 - alpha) P), alpha = beta */
+  KDKL_LOSS_SRKL = 3, /* skew reverse KL(q || alpha q + (1 - alpha) P), alpha = beta */
+  KDKL_LOSS_TRKL = 4  /* reverse KL over the teacher's top-K support */
 } kdkl_loss;
 
 /* The alternative losses (readings: the pages report ablations on the
@@ -129,7 +130,23 @@ typedef enum {
  * two floats, so row_lse is [2, N] for these losses: each position's
  * logsumexp, then sum_v q_iv g_iv. Ignored positions as for the KL. Only the
  * fused calls (kdkl_forward, kdkl_forward_noalloc, kdkl_backward) take
- * them. */
+ * them.
+ *   KDKL_LOSS_TRKL  the reverse KL over the teacher's top-K support (no
+ *                   parameter): with S_i = {v : P_iv > 0} (at most K ids)
+ *                   and the student's distribution restricted to S_i and
+ *                   renormalised there, qt_iv = exp(s_iv) / sum_{u in S_i}
+ *                   exp(s_iu),
+ *                   L_i = KL(qt_i || P_i) = sum_{v in S_i} qt_iv log(qt_iv / P_iv)
+ *                   (0 for an empty support), loss = (1/N) sum_i L_i, and
+ *                   dZ_iv = g / (N T) qt_iv (log(qt_iv / P_iv) - L_i) on S_i,
+ *                   0 elsewhere. It needs the student's logits at S_i only:
+ *                   the forward forms them as dot products of W's rows with
+ *                   H (no projection over the vocabulary); the backward
+ *                   forms dZ at S_i the same way, writes it into zeroed dZ
+ *                   slices and runs the dH and dW products on them (fixed
+ *                   reduction order without sorting the entries by id).
+ *                   row_lse is [2, N]: the logsumexp of s_i over S_i (-inf
+ *                   for an empty support), then L_i. */
 
 /* Per-call options of the fused calls. NULL, or a zero-filled struct, means
  * the defaults: the loss above and the library's own blocking, which it

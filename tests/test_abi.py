@@ -573,7 +573,7 @@ def test_jsd_options(lib):
     assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=L.KDKL_LOSS_JSD))[0] == OPTION             # beta 0
     assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=L.KDKL_LOSS_JSD, beta=1.0))[0] == OPTION
     assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=L.KDKL_LOSS_JSD, beta=float("nan")))[0] == OPTION
-    assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=4, beta=0.5))[0] == OPTION
+    assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=5, beta=0.5))[0] == OPTION
     assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=-1, beta=0.5))[0] == OPTION
     st, f, b = ws(lib, *sizes, L.KDKL_BF16, opts(loss=L.KDKL_LOSS_JSD, beta=0.5))
     _, f0, b0 = ws(lib, *sizes, L.KDKL_BF16)
@@ -602,6 +602,22 @@ def test_skew_loss_options(lib):
             assert ws(lib, *sizes, L.KDKL_BF16, opts(loss=loss, beta=a))[0] == OPTION, (loss, a)
         assert fwd(lib, o=opts(loss=loss, beta=bad[0])) == OPTION
         assert bwd(lib, o=opts(loss=loss, beta=bad[1])) == OPTION
+
+
+def test_topk_rkl_options(lib):
+    """The reverse KL over the top-K support takes no parameter (beta is
+    ignored), keeps the KL's forward workspace and adds the per-entry
+    gradients [group rows, K] fp32 to the backward's."""
+    sizes = (32768, 2880, 201088, 100, 2048)
+    _, f0, b0 = ws(lib, *sizes, L.KDKL_BF16)
+    g = plan(lib, *sizes, L.KDKL_BF16).chunks_per_group * 2048
+    for beta in (0.0, 0.5, -3.0, float("nan")):
+        st, f, b = ws(lib, *sizes, L.KDKL_BF16, opts(loss=L.KDKL_LOSS_TRKL, beta=beta))
+        assert (st, f) == (OK, f0) and b - b0 == g * 100 * 4, beta
+    assert ws(lib, *sizes, L.KDKL_F32, opts(loss=L.KDKL_LOSS_TRKL))[0] == OK
+    # the same blocking as the KL's, options included
+    p = plan(lib, *sizes, L.KDKL_BF16, opts(loss=L.KDKL_LOSS_TRKL, chunks_per_group=4, vocab_slices=3))
+    assert (p.chunks_per_group, p.vocab_slices) == (4, 3)
 
 
 @pytest.mark.parametrize("N,d,V,K,chunk,dt", [
