@@ -232,10 +232,10 @@ __device__ __forceinline__ float wmax(float v) {
   return v;
 }
 
-template <typename TE>
+template <typename TE, int KMAX>  // K <= KMAX
 __global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_kernel(TopkArgs a, int backward) {
-  __shared__ float s_s[kRowsPerBlock][1024];  // s at each sorted entry of the support
-  __shared__ float s_P[kRowsPerBlock][1024];  // its teacher mass (0 off the support)
+  __shared__ float s_s[kRowsPerBlock][KMAX];  // s at each sorted entry of the support
+  __shared__ float s_P[kRowsPerBlock][KMAX];  // its teacher mass (0 off the support)
   constexpr int VEC = Vec16<TE>::kN;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -246,29 +246,46 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_kernel(TopkArgs a
   const bool keep = a.keep[row] != 0.f;
   const int64_t nvec = a.d / VEC;
   const uint4* hp = (const uint4*)((const TE*)a.H + (int64_t)row * a.d);
-  for (int k = 0; k < K; ++k) {  // the same entry across the wavefront
+  // the support and its masses (each lane its entries)
+  for (int k = lane; k < K; k += 64) {
     const int2 e = ent[k];
     float P = 0.f;
     if (keep && e.x >= 0 && e.x < a.V && (k == 0 || ent[k - 1].x != e.x)) {
       P = __int_as_float(e.y);
       for (int k2 = k + 1; k2 < K && ent[k2].x == e.x; ++k2) P += __int_as_float(ent[k2].y);
     }
-    float sv = 0.f;
-    if (P > 0.f) {
-      const uint4* wp = (const uint4*)((const TE*)a.W + (int64_t)e.x * a.d);
-      float acc = 0.f;
-      for (int64_t j = lane; j < nvec; j += 64) {
-        float x[VEC], y[VEC];
-        Vec16<TE>::unpack(wp[j], x);
-        Vec16<TE>::unpack(hp[j], y);
+    s_P[w][k] = P;
+  }
+  __builtin_amdgcn_wave_barrier();
+  // the student's logits there, kDots entries at a time across the
+  // wavefront (their rows of W read together; an entry off the support
+  // reads row 0 and is not kept)
+  constexpr int kDots = 4;
+  for (int k0 = 0; k0 < K; k0 += kDots) {
+    const uint4* wp[kDots];
+    bool on[kDots];
 #pragma unroll
-        for (int q = 0; q < VEC; ++q) acc = __builtin_fmaf(x[q], y[q], acc);
-      }
-      sv = wsum(acc) * a.inv_T;
+    for (int q = 0; q < kDots; ++q) {
+      const int k = k0 + q;
+      on[q] = k < K && s_P[w][k] > 0.f;
+      wp[q] = (const uint4*)((const TE*)a.W + (on[q] ? (int64_t)ent[k].x : 0) * a.d);
     }
-    if (lane == 0) {
-      s_s[w][k] = sv;
-      s_P[w][k] = P;
+    float acc[kDots] = {};
+    for (int64_t j = lane; j < nvec; j += 64) {
+      float y[VEC];
+      Vec16<TE>::unpack(hp[j], y);
+#pragma unroll
+      for (int q = 0; q < kDots; ++q) {
+        float x[VEC];
+        Vec16<TE>::unpack(wp[q][j], x);
+#pragma unroll
+        for (int i = 0; i < VEC; ++i) acc[q] = __builtin_fmaf(x[i], y[i], acc[q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kDots; ++q) {
+      const float sv = wsum(acc[q]) * a.inv_T;
+      if (lane == 0 && k0 + q < K) s_s[w][k0 + q] = on[q] ? sv : 0.f;
     }
   }
   __builtin_amdgcn_wave_barrier();
@@ -361,12 +378,15 @@ hipError_t launch_topk_rkl(int dtype, const TopkArgs& a, bool backward, hipStrea
   if (a.rows <= 0) return hipSuccess;
   if (a.K < 1 || a.K > 1024) return hipErrorInvalidValue;
   if (a.d % (dtype == 1 ? 8 : 4) != 0) return hipErrorInvalidValue;  // rows of whole 16-byte vectors
-  if (dtype == 1)
-    hipLaunchKernelGGL(topk_rkl_kernel<uint16_t>, rows_grid(a.rows), dim3(64 * kRowsPerBlock), 0, s, a,
-                       backward ? 1 : 0);
-  else
-    hipLaunchKernelGGL(topk_rkl_kernel<float>, rows_grid(a.rows), dim3(64 * kRowsPerBlock), 0, s, a,
-                       backward ? 1 : 0);
+  const dim3 grid = rows_grid(a.rows), block(64 * kRowsPerBlock);
+  const int b = backward ? 1 : 0;
+  if (dtype == 1) {
+    if (a.K <= 128) hipLaunchKernelGGL((topk_rkl_kernel<uint16_t, 128>), grid, block, 0, s, a, b);
+    else hipLaunchKernelGGL((topk_rkl_kernel<uint16_t, 1024>), grid, block, 0, s, a, b);
+  } else {
+    if (a.K <= 128) hipLaunchKernelGGL((topk_rkl_kernel<float, 128>), grid, block, 0, s, a, b);
+    else hipLaunchKernelGGL((topk_rkl_kernel<float, 1024>), grid, block, 0, s, a, b);
+  }
   return hipGetLastError();
 }
 
