@@ -542,10 +542,10 @@ def main():
 
     dtype = "bf16" if w.dtype == "bf16" else "fp32"
     # the matrix work of a step: four vocabulary-wide products (forward,
-    # recompute, dH, dW); the reverse KL over the top-K support runs the dH
-    # and dW products only, plus the support's dot products (2 N K d flop in
-    # each call)
-    flops_step = (4.0 * w.N * w.V * w.d + 4.0 * w.N * w.K * w.d if args.loss == "trkl"
+    # recompute, dH, dW); the reverse KL over the top-K support runs the dW
+    # product only, plus its support's dot products (forward and backward)
+    # and dH over the support (2 N K d flop each)
+    flops_step = (2.0 * w.N * w.V * w.d + 6.0 * w.N * w.K * w.d if args.loss == "trkl"
                   else 8.0 * w.N * w.V * w.d)
     peak = PEAK_TFLOPS[dtype]
     tok_s = w.N / (ms / 1e3)

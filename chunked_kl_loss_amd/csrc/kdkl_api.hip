@@ -325,7 +325,9 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   P->vpart = slice_rows(*P, slices);
   P->n_parts = (int)((V + P->vpart - 1) / P->vpart);
   if (o.dh_w_in_place == 1 && !P->fast) return KDKL_ERR_OPTION;
-  P->wt = !P->fast || (o.dh_w_in_place == 2) || (o.dh_w_in_place == 0 && !dh_reads_w_in_place(*P, N));
+  // (the top-K reverse KL forms dH from W's rows at the support: no W^T)
+  P->wt = !P->trkl &&
+          (!P->fast || (o.dh_w_in_place == 2) || (o.dh_w_in_place == 0 && !dh_reads_w_in_place(*P, N)));
   // dH split-K: the fewest splits S whose launch keeps the 256 compute units
   // within 4% as busy as the best S does, when every workgroup does 1/S of a
   // tile's work and the units take them in rounds (fewer splits, fewer fp32
@@ -398,9 +400,10 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
     ok &= region(&cur, dz, &P->b_dzcv) && region(&cur, dz, &P->b_dzvc);
   }
   ok &= mul_ok(S * P->Cg, d, &dhp) && mul_ok(dhp, 4, &dhp);
-  ok &= region(&cur, dhp, &P->b_dhpart);
+  P->b_dhpart = 0;
+  if (!P->trkl) ok &= region(&cur, dhp, &P->b_dhpart);  // (the top-K reverse KL forms dH itself)
   P->b_dhacc = 0;
-  if (P->n_parts > 1) {
+  if (P->n_parts > 1 && !P->trkl) {
     int64_t acc;
     ok &= mul_ok(P->Cg, d, &acc) && mul_ok(acc, 4, &acc);
     ok &= region(&cur, acc, &P->b_dhacc);
@@ -780,12 +783,14 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
     });
     if (e == hipSuccess && P.trkl) {
       // the loss's gradient at each support entry, from the forward's
-      // logsumexp and loss; each vocabulary slice's dZ is zero elsewhere
+      // logsumexp and loss, and dH over those entries; dW from each
+      // vocabulary slice's dZ, zero off the support
       TopkArgs t = topk_args(P, H, W, T, r0, rows, ws, P.b_ent, P.b_keep);
       t.row_lse = const_cast<float*>(row_lse) + r0; t.row_loss = const_cast<float*>(row_lse) + N + r0;
       t.scale = (const float*)(ws + P.b_scale); t.dz = (float*)(ws + P.b_dzent);
-      e = timed(K_TOPK_RKL, 2.0 * rows * (double)P.K * d, (double)rows * P.K * (d * P.es + 12.0), s,
-                [&] { return launch_topk_rkl(dtype, t, true, s); });
+      t.dH = (char*)dH + r0 * d * P.es;
+      e = timed(K_TOPK_RKL, 4.0 * rows * (double)P.K * d, (double)rows * (P.K * (2.0 * d * P.es + 12.0) + d * P.es),
+                s, [&] { return launch_topk_rkl(dtype, t, true, s); });
       for (int part = 0; part < P.n_parts && e == hipSuccess; ++part) {
         const int64_t v0 = part * P.vpart;
         const int64_t vlen = V - v0 < P.vpart ? V - v0 : P.vpart;
@@ -794,7 +799,7 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
                                      (int)P.K, v0, vlen, ws + P.b_dzcv, P.vpart,
                                      P.fast ? nullptr : ws + P.b_dzvc, P.Cg, P.Cg * P.vpart, s);
         });
-        if (e == hipSuccess) e = part_products(P, dtype, W, ws, r0, rows, part, dH, dW, r0 > 0 || accumulate_dW, s);
+        if (e == hipSuccess) e = dw_product(P, dtype, ws, rows, part, dW, r0 > 0 || accumulate_dW, s);
       }
       continue;
     }

@@ -163,7 +163,8 @@ hipError_t launch_jsd_prep(const JsdArgs& a, hipStream_t s);
 // products of W's rows with the position's H (no vocabulary-wide work).
 // Forward: their logsumexp and the loss per position. Backward: the loss's
 // gradient g / (N_kept T) dTRKL/ds at each support entry (0 at every other
-// sorted entry), from the forward's logsumexp and loss.
+// sorted entry), from the forward's logsumexp and loss, and dH = dZ W over
+// those entries (each position's row by its own wavefront, in entry order).
 struct TopkArgs {
   const void* H;      // [rows, d] storage dtype, the group's first position
   const void* W;      // [V, d]
@@ -177,6 +178,7 @@ struct TopkArgs {
   float* row_kl;      // forward out (group-offset): the loss, 0 at ignored positions
   const float* scale; // backward: device scalar g / (N_kept T)
   float* dz;          // backward out: [Cp, K] per sorted entry
+  void* dH;           // backward out: [rows, d] storage dtype (group-offset), sum_k dz_k W[id_k]
 };
 hipError_t launch_topk_rkl(int dtype, const TopkArgs& a, bool backward, hipStream_t s);
 // A slice [v0, v0 + vlen) of the dZ buffers of `rows` positions from the

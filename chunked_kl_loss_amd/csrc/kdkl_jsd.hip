@@ -214,6 +214,14 @@ struct Vec16<uint16_t> {  // bf16 bits
     }
   }
   __device__ static void store(uint16_t* p, float v) { *p = __builtin_bit_cast(uint16_t, static_cast<__bf16>(v)); }
+  __device__ static void store_vec(uint16_t* p, const float (&x)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[2 * j])) |
+             ((uint32_t)__builtin_bit_cast(uint16_t, static_cast<__bf16>(x[2 * j + 1])) << 16);
+    *(uint4*)p = make_uint4(w[0], w[1], w[2], w[3]);
+  }
 };
 template <>
 struct Vec16<float> {
@@ -225,6 +233,7 @@ struct Vec16<float> {
     x[3] = __builtin_bit_cast(float, u.w);
   }
   __device__ static void store(float* p, float v) { *p = v; }
+  __device__ static void store_vec(float* p, const float (&x)[4]) { *(float4*)p = make_float4(x[0], x[1], x[2], x[3]); }
 };
 
 __device__ __forceinline__ float wmax(float v) {
@@ -267,8 +276,9 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_kernel(TopkArgs a
 #pragma unroll
     for (int q = 0; q < kDots; ++q) {
       const int k = k0 + q;
-      on[q] = k < K && s_P[w][k] > 0.f;
-      wp[q] = (const uint4*)((const TE*)a.W + (on[q] ? (int64_t)ent[k].x : 0) * a.d);
+      const int kc = k < K ? k : K - 1;
+      on[q] = k < K && s_P[w][kc] > 0.f;
+      wp[q] = (const uint4*)((const TE*)a.W + (on[q] ? (int64_t)ent[kc].x : 0) * a.d);
     }
     float acc[kDots] = {};
     for (int64_t j = lane; j < nvec; j += 64) {
@@ -316,6 +326,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_kernel(TopkArgs a
     return;
   }
   // the gradient at each sorted entry, from the forward's logsumexp and loss
+  // (kept in s_s in place of s)
   const float lse = a.row_lse[row], L = a.row_loss[row];
   const float coef = keep ? a.scale[0] : 0.f;
   for (int k = lane; k < K; k += 64) {
@@ -326,6 +337,45 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_kernel(TopkArgs a
       gk = coef * exp_hw(lq) * (lq - log_hw(P) - L);
     }
     a.dz[(int64_t)row * K + k] = gk;
+    s_s[w][k] = gk;
+  }
+  __builtin_amdgcn_wave_barrier();
+  // dH row = sum over the support of dz_k W[id_k], in entry order: kRep
+  // vectors per lane at a time, the rows of kDots entries read together
+  constexpr int kRep = 2;
+  TE* dh = (TE*)a.dH + (int64_t)row * a.d;
+  for (int64_t j0 = 0; j0 < nvec; j0 += 64 * kRep) {
+    float acc[kRep][VEC] = {};
+    for (int k0 = 0; k0 < K; k0 += kDots) {
+      const uint4* wp[kDots];
+      float gq[kDots];
+#pragma unroll
+      for (int q = 0; q < kDots; ++q) {
+        const int k = k0 + q;
+        const int kc = k < K ? k : K - 1;
+        gq[q] = k < K ? s_s[w][kc] : 0.f;
+        wp[q] = (const uint4*)((const TE*)a.W + (gq[q] != 0.f ? (int64_t)ent[kc].x : 0) * a.d);
+      }
+#pragma unroll
+      for (int r = 0; r < kRep; ++r) {
+        const int64_t j = j0 + lane + 64 * r;
+        if (j < nvec) {
+#pragma unroll
+          for (int q = 0; q < kDots; ++q) {
+            float x[VEC];
+            Vec16<TE>::unpack(wp[q][j], x);
+            // (an entry without gradient read row 0, which must add nothing)
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) acc[r][i] = gq[q] != 0.f ? __builtin_fmaf(gq[q], x[i], acc[r][i]) : acc[r][i];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRep; ++r) {
+      const int64_t j = j0 + lane + 64 * r;
+      if (j < nvec) Vec16<TE>::store_vec(dh + j * VEC, acc[r]);
+    }
   }
 }
 

@@ -142,9 +142,10 @@ typedef enum {
  *                   0 elsewhere. It needs the student's logits at S_i only:
  *                   the forward forms them as dot products of W's rows with
  *                   H (no projection over the vocabulary); the backward
- *                   forms dZ at S_i the same way, writes it into zeroed dZ
- *                   slices and runs the dH and dW products on them (fixed
- *                   reduction order without sorting the entries by id).
+ *                   forms dZ at S_i the same way and dH from the same rows,
+ *                   then writes dZ into zeroed slices for the dW product
+ *                   (a fixed reduction order without sorting the entries by
+ *                   id).
  *                   row_lse is [2, N]: the logsumexp of s_i over S_i (-inf
  *                   for an empty support), then L_i. */
 
