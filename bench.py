@@ -542,11 +542,11 @@ def main():
 
     dtype = "bf16" if w.dtype == "bf16" else "fp32"
     # the matrix work of a step: four vocabulary-wide products (forward,
-    # recompute, dH, dW); the reverse KL over the top-K support runs the dW
-    # product only, plus its support's dot products (forward and backward)
-    # and dH over the support (2 N K d flop each)
-    flops_step = (2.0 * w.N * w.V * w.d + 6.0 * w.N * w.K * w.d if args.loss == "trkl"
-                  else 8.0 * w.N * w.V * w.d)
+    # recompute, dH, dW); the reverse KL over the top-K support has none, only
+    # its support's dot products (forward and backward), dH and dW over the
+    # support (2 N K d flop each, on the vector units)
+    trkl = args.loss == "trkl"
+    flops_step = 8.0 * w.N * w.K * w.d if trkl else 8.0 * w.N * w.V * w.d
     peak = PEAK_TFLOPS[dtype]
     tok_s = w.N / (ms / 1e3)
     mfma_pct = 100.0 * flops_step / (ms / 1e3) / (peak * 1e12)
@@ -556,11 +556,18 @@ def main():
     ds = kstats[dom]
     achieved = ds["flops"] / (ds["total_ms"] / 1e3) / 1e12
     traffic = load_traffic(dom, w.name)
-    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
-                "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                "traffic": traffic,
-                "avg_launch_ms": round(ds["total_ms"] / ds["launches"], 4),
-                "flop_per_launch": ds["flops"] / ds["launches"]}
+    if trkl:  # gathers of W and H rows: bound by HBM
+        achieved_gbs = ds["bytes"] / (ds["total_ms"] / 1e3) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "avg_launch_ms": round(ds["total_ms"] / ds["launches"], 4),
+                    "bytes_per_launch": ds["bytes"] / ds["launches"]}
+    else:
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": peak,
+                    "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                    "traffic": traffic,
+                    "avg_launch_ms": round(ds["total_ms"] / ds["launches"], 4),
+                    "flop_per_launch": ds["flops"] / ds["launches"]}
 
     out = {
         "metric": METRIC,
@@ -583,10 +590,10 @@ def main():
                             f"jsd(beta={args.beta})" if args.loss == "jsd" else f"{args.loss}(alpha={args.alpha})"),
                    "plan": plan,
                    "parallelism": "single GPU"},
-        "mfma_util_pct": round(mfma_pct, 2),
+        "mfma_util_pct": None if trkl else round(mfma_pct, 2),
         # the same time against the 6 N V d flop of forward + dH + dW alone
         # (the recompute is part of the method and counted above)
-        "mfma_util_pct_without_recompute": None if args.loss == "trkl" else round(mfma_pct * 0.75, 2),
+        "mfma_util_pct_without_recompute": None if trkl else round(mfma_pct * 0.75, 2),
         "flop_per_step": flops_step,
         "peak_hbm_gib": round(peak_gib, 3),
         "workspace_gib": {"forward": round(fb / 2**30, 3), "backward": round(bb / 2**30, 3)},

@@ -23,7 +23,7 @@ const char* kernel_name(int id) {
       "transpose_h",  "dz_gemm",      "dh_gemm",     "dh_reduce",   "dw_gemm",
       "logits_fwd",   "logits_bwd",   "grad_scale",  "dense_gemm",  "dense_student",
       "dense_teacher", "dense_kl",    "dense_grad",  "jsd_merge",     "jsd_prep",
-      "topk_rkl",      "topk_scatter"};
+      "topk_rkl",      "topk_dw"};
   return (id >= 0 && id < K_COUNT) ? names[id] : "?";
 }
 
@@ -116,8 +116,8 @@ struct Plan {
   // offsets into the forward workspace
   size_t f_ent, f_erow, f_keep, f_tstart, f_part, f_sk, f_red, f_rowkl, f_bytes;
   // offsets into the backward workspace
-  size_t b_ent, b_erow, b_keep, b_scale, b_red, b_tstart, b_rowcoef, b_dzent, b_wt, b_ht, b_dzcv, b_dzvc,
-      b_dhpart, b_dhacc, b_bytes;
+  size_t b_ent, b_erow, b_keep, b_scale, b_red, b_tstart, b_rowcoef, b_dzent, b_cnt, b_scans, b_list, b_part,
+      b_wt, b_ht, b_dzcv, b_dzvc, b_dhpart, b_dhacc, b_bytes;
 };
 
 // The dH product on the bf16 main loop reads either a W^T copy written once
@@ -380,8 +380,20 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
   ok &= region(&cur, g1, &P->b_tstart);
   P->b_rowcoef = 0;
   if (P->epi_alt) ok &= region(&cur, P->Cg * 4, &P->b_rowcoef);
-  P->b_dzent = 0;
-  if (P->trkl) ok &= region(&cur, g0 / 2, &P->b_dzent);  // [Cg, K] fp32 entry gradients
+  P->b_dzent = P->b_cnt = P->b_scans = P->b_list = P->b_part = 0;
+  if (P->trkl) {
+    // the entry gradients [Cg, K] fp32 and the sparse dW's counting sort:
+    // per-block counts, five scans over the ids (int64), the sorted entries,
+    // and the partial rows of the ids with more than one run of entries
+    ok &= region(&cur, g0 / 2, &P->b_dzent);
+    ok &= region(&cur, trkl_count_bytes(P->Cg, V), &P->b_cnt);
+    ok &= region(&cur, 5 * (V + 1) * 8, &P->b_scans);
+    ok &= region(&cur, g0, &P->b_list);
+    ok &= region(&cur, trkl_part_bytes(P->Cg * K, d), &P->b_part);
+    P->b_wt = P->b_ht = P->b_dzcv = P->b_dzvc = P->b_dhpart = P->b_dhacc = 0;
+    P->b_bytes = cur;
+    return ok ? KDKL_OK : KDKL_ERR_OVERFLOW;  // (no dZ buffer, W^T or dH partials)
+  }
   int64_t wt, ht, dz, dhp;
   ok &= mul_ok(d, P->Vp, &wt) && mul_ok(wt, P->es, &wt);
   ok &= mul_ok(d, P->Cg, &ht) && mul_ok(ht, P->es, &ht);
@@ -778,29 +790,27 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
     // H_g^T [d, Cg], zero-padded past the group's rows: the dW product
     // contracts over the group's tokens.
     const char* Hg = (const char*)H + r0 * d * P.es;
-    e = timed(K_TRANSPOSE_H, 0.0, 2.0 * (double)rows * d * P.es, s, [&] {
-      return launch_transpose((int)P.es, Hg, rows, d, d, ws + P.b_ht, rows_pad, P.Cg, s);
-    });
+    if (!P.trkl)
+      e = timed(K_TRANSPOSE_H, 0.0, 2.0 * (double)rows * d * P.es, s, [&] {
+        return launch_transpose((int)P.es, Hg, rows, d, d, ws + P.b_ht, rows_pad, P.Cg, s);
+      });
     if (e == hipSuccess && P.trkl) {
       // the loss's gradient at each support entry, from the forward's
-      // logsumexp and loss, and dH over those entries; dW from each
-      // vocabulary slice's dZ, zero off the support
+      // logsumexp and loss, and dH over those entries; then dW over them
       TopkArgs t = topk_args(P, H, W, T, r0, rows, ws, P.b_ent, P.b_keep);
       t.row_lse = const_cast<float*>(row_lse) + r0; t.row_loss = const_cast<float*>(row_lse) + N + r0;
       t.scale = (const float*)(ws + P.b_scale); t.dz = (float*)(ws + P.b_dzent);
       t.dH = (char*)dH + r0 * d * P.es;
       e = timed(K_TOPK_RKL, 4.0 * rows * (double)P.K * d, (double)rows * (P.K * (2.0 * d * P.es + 12.0) + d * P.es),
                 s, [&] { return launch_topk_rkl(dtype, t, true, s); });
-      for (int part = 0; part < P.n_parts && e == hipSuccess; ++part) {
-        const int64_t v0 = part * P.vpart;
-        const int64_t vlen = V - v0 < P.vpart ? V - v0 : P.vpart;
-        e = timed(K_TOPK_SCATTER, 0.0, (P.fast ? 1.0 : 2.0) * (double)P.Cg * P.vpart * P.es, s, [&] {
-          return launch_topk_scatter(dtype, (const int2*)(ws + P.b_ent), (const float*)(ws + P.b_dzent), rows,
-                                     (int)P.K, v0, vlen, ws + P.b_dzcv, P.vpart,
-                                     P.fast ? nullptr : ws + P.b_dzvc, P.Cg, P.Cg * P.vpart, s);
-        });
-        if (e == hipSuccess) e = dw_product(P, dtype, ws, rows, part, dW, r0 > 0 || accumulate_dW, s);
-      }
+      if (e == hipSuccess)
+        e = timed(K_TOPK_DW, 2.0 * rows * (double)P.K * d, (double)rows * P.K * (d * P.es + 16.0) + 8.0 * V * d, s,
+                  [&] {
+                    return launch_trkl_dw(dtype, (const int2*)(ws + P.b_ent), (const float*)(ws + P.b_dzent), rows,
+                                          (int)P.K, V, Hg, d, dW, r0 > 0 || accumulate_dW, (int*)(ws + P.b_cnt),
+                                          (int64_t*)(ws + P.b_scans), (int2*)(ws + P.b_list),
+                                          (float*)(ws + P.b_part), s);
+                  });
       continue;
     }
     if (e == hipSuccess && P.epi_alt) {

@@ -38,7 +38,7 @@ enum KernelId {
   K_JSD_MERGE,
   K_JSD_PREP,
   K_TOPK_RKL,
-  K_TOPK_SCATTER,
+  K_TOPK_DW,
   K_COUNT
 };
 
@@ -181,13 +181,24 @@ struct TopkArgs {
   void* dH;           // backward out: [rows, d] storage dtype (group-offset), sum_k dz_k W[id_k]
 };
 hipError_t launch_topk_rkl(int dtype, const TopkArgs& a, bool backward, hipStream_t s);
-// A slice [v0, v0 + vlen) of the dZ buffers of `rows` positions from the
-// entry gradients: both buffers zeroed (cv: cv_elems elements; vc, when not
-// NULL, as many), then each nonzero entry gradient with an id in the slice
-// written to cv[r, id - v0] (row pitch ld_cv) and vc[id - v0, r] (pitch ld_vc).
-hipError_t launch_topk_scatter(int dtype, const int2* ent, const float* dz, int rows, int K, int64_t v0,
-                               int64_t vlen, void* cv, int64_t ld_cv, void* vc, int64_t ld_vc,
-                               int64_t cv_elems, hipStream_t s);
+// dW (+)= the reverse KL's dZ^T H for one group of `rows` positions, from the
+// entry gradients dz [rows, K] at the sorted entries `ent`, without a dense
+// product: the nonzero entries sorted by id in position order, then each id's
+// entries summed in order by one workgroup per run of 1024 (a bucket of
+// several runs through fp32 partial rows added in run order); dW is zeroed
+// first unless accumulating. Workspace: cnt (trkl_count_bytes), scans
+// (5 (V + 1) int64), list [rows K] int2, part (trkl_part_bytes).
+inline int64_t trkl_count_bytes(int64_t rows, int64_t V) {
+  const int64_t nb = (rows + 255) / 256;  // positions per counting block: 256
+  return (nb * V * 4 + 15) / 16 * 16;
+}
+inline int64_t trkl_part_bytes(int64_t entries, int64_t d) {
+  // buckets of more than one run of 1024 entries hold at most 2 entries / 1024 runs
+  return (2 * (entries / 1024) + 1) * d * 4;
+}
+hipError_t launch_trkl_dw(int dtype, const int2* ent, const float* dz, int rows, int K, int64_t V,
+                          const void* H, int64_t d, float* dW, bool accumulate, int* cnt, int64_t* scans,
+                          int2* list, float* part, hipStream_t s);
 
 hipError_t launch_teacher(const TeacherArgs& a, hipStream_t s);
 hipError_t launch_merge(const MergeArgs& a, hipStream_t s);

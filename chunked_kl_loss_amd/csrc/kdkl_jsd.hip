@@ -384,19 +384,210 @@ __global__ __launch_bounds__(256) void zero16_kernel(uint4* __restrict__ p, int6
     p[i] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-template <typename TE>
-__global__ __launch_bounds__(256) void topk_scatter_kernel(const int2* ent, const float* dz, int64_t n, int K,
-                                                           int64_t v0, int64_t vlen, TE* cv, int64_t ld_cv,
-                                                           TE* vc, int64_t ld_vc) {
+// ---------------------------------------------------------------------------
+// dW of the reverse KL over the top-K support without a dense product:
+// dW_v = sum over the positions r whose support holds v of dz_rv H_r, summed
+// in position order. The support entries (nonzero entry gradients) are
+// bucketed by id with a counting sort that keeps position order: per block
+// of kBucketRows positions, counts per id (integer atomics: the counts do not
+// depend on their order); an exclusive scan over the blocks per id and over
+// the ids; then each block's workgroup walks its positions in order and
+// places their entries (one entry per id per position, so the atomic that
+// hands out slots runs in position order); one workgroup per id then sums
+// its bucket.
+// ---------------------------------------------------------------------------
+constexpr int kBucketRows = 256;
+static_assert(kBucketRows == 256, "trkl_count_bytes counts blocks of 256 positions");
+
+__global__ __launch_bounds__(256) void trkl_count_kernel(const int2* ent, const float* dz, int64_t n, int K,
+                                                         int64_t V, int* cnt) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
-  const float g = dz[i];
-  if (g == 0.f) return;  // off the support (the buffers are zero there)
-  const int64_t c = (int64_t)ent[i].x - v0;
-  if (c < 0 || c >= vlen) return;
-  const int64_t r = i / K;
-  Vec16<TE>::store(cv + r * ld_cv + c, g);
-  if (vc) Vec16<TE>::store(vc + c * ld_vc + r, g);
+  if (i >= n || dz[i] == 0.f) return;
+  const int v = ent[i].x;
+  if (v < 0 || v >= V) return;  // (a nonzero gradient is only ever at an id in range)
+  const int64_t b = (i / K) / kBucketRows;
+  atomicAdd(&cnt[b * V + v], 1);
+}
+
+// per id: the counts of the blocks turned into exclusive offsets within the
+// id's bucket, and the bucket's size
+__global__ __launch_bounds__(256) void trkl_scan_blocks_kernel(int* cnt, int nb, int64_t V, int64_t* total) {
+  const int64_t v = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (v >= V) return;
+  int acc = 0;
+  for (int b = 0; b < nb; ++b) {
+    const int c = cnt[(int64_t)b * V + v];
+    cnt[(int64_t)b * V + v] = acc;
+    acc += c;
+  }
+  total[v] = acc;
+}
+
+// A bucket of more than kChunk entries is summed by several workgroups, one
+// per run of kChunk entries, into fp32 partial rows that a second pass adds
+// to dW in run order (the Zipf-like head of the teacher ids puts one id at
+// nearly every position).
+constexpr int64_t kChunk = 1024;
+__device__ __forceinline__ int64_t trkl_runs(int64_t n) { return (n + kChunk - 1) / kChunk; }
+
+// Exclusive scans over the ids (one workgroup: a contiguous run of ids per
+// thread, then a scan of the runs' sums), each with its total at index V:
+//   base:   bucket sizes (the bucket's first slot in the sorted list)
+//   rstart: runs of kChunk entries (the workgroup of a bucket's first run)
+//   pstart: the same over the buckets of more than one run (partial rows)
+//   mstart: the buckets of more than one run
+__global__ __launch_bounds__(1024) void trkl_scan_ids_kernel(const int64_t* total, int64_t V, int64_t* base,
+                                                            int64_t* rstart, int64_t* pstart, int64_t* mstart) {
+  __shared__ int64_t s[4][1024];
+  const int t = threadIdx.x;
+  const int64_t per = (V + 1023) / 1024;
+  const int64_t lo = t * per < V ? t * per : V;
+  const int64_t hi = lo + per < V ? lo + per : V;
+  int64_t sum[4] = {0, 0, 0, 0};
+  for (int64_t i = lo; i < hi; ++i) {
+    const int64_t n = total[i], r = trkl_runs(n);
+    sum[0] += n;
+    sum[1] += r;
+    sum[2] += r > 1 ? r : 0;
+    sum[3] += r > 1 ? 1 : 0;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) s[c][t] = sum[c];
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int64_t x[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) x[c] = t >= o ? s[c][t - o] : 0;
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < 4; ++c) s[c][t] += x[c];
+    __syncthreads();
+  }
+  int64_t run[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) run[c] = t ? s[c][t - 1] : 0;
+  for (int64_t i = lo; i < hi; ++i) {
+    const int64_t n = total[i], r = trkl_runs(n);
+    base[i] = run[0];
+    rstart[i] = run[1];
+    pstart[i] = run[2];
+    mstart[i] = run[3];
+    run[0] += n;
+    run[1] += r;
+    run[2] += r > 1 ? r : 0;
+    run[3] += r > 1 ? 1 : 0;
+  }
+  if (t == 1023) {
+    base[V] = s[0][1023];
+    rstart[V] = s[1][1023];
+    pstart[V] = s[2][1023];
+    mstart[V] = s[3][1023];
+  }
+}
+
+// the id whose range [start[v], start[v + 1]) holds w (start nondecreasing)
+__device__ __forceinline__ int64_t find_range(const int64_t* start, int64_t V, int64_t w) {
+  int64_t lo = 0, hi = V;  // start[lo] <= w < start[hi]
+  while (hi - lo > 1) {
+    const int64_t mid = (lo + hi) >> 1;
+    if (start[mid] <= w) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void trkl_place_kernel(const int2* ent, const float* dz, int rows, int K,
+                                                         int64_t V, int* cnt, const int64_t* base, int2* list) {
+  const int b = blockIdx.x;
+  const int r0 = b * kBucketRows;
+  const int r1 = r0 + kBucketRows < rows ? r0 + kBucketRows : rows;
+  for (int r = r0; r < r1; ++r) {
+    for (int k = threadIdx.x; k < K; k += 256) {
+      const int64_t i = (int64_t)r * K + k;
+      const float g = dz[i];
+      const int v = ent[i].x;
+      if (g != 0.f && v >= 0 && v < V) {
+        const int o = atomicAdd(&cnt[(int64_t)b * V + v], 1);
+        list[base[v] + o] = make_int2(r, __float_as_int(g));
+      }
+    }
+    __syncthreads();  // the next position's slots after this one's
+  }
+}
+
+// One workgroup per run of a bucket (launched for the most runs there can
+// be; the ones past the total exit): the run's sum of dz H_r over its
+// entries in order, added to dW's row for a bucket of one run, else written
+// as the run's partial row.
+template <typename TE>
+__global__ __launch_bounds__(256) void trkl_dw_runs_kernel(const int2* list, const int64_t* base,
+                                                           const int64_t* rstart, const int64_t* pstart, int64_t V,
+                                                           const void* H, int64_t d, float* dW, float* part) {
+  constexpr int VEC = Vec16<TE>::kN;
+  constexpr int kRep = 2;
+  const int64_t w = blockIdx.x;
+  if (w >= rstart[V]) return;
+  const int64_t v = find_range(rstart, V, w);
+  const int64_t c = w - rstart[v];
+  const int64_t runs = rstart[v + 1] - rstart[v];
+  const int64_t lo = base[v] + c * kChunk;
+  const int64_t hi = lo + kChunk < base[v + 1] ? lo + kChunk : base[v + 1];
+  const int64_t nvec = d / VEC;
+  const uint4* h = (const uint4*)H;
+  float* out = runs == 1 ? dW + v * d : part + (pstart[v] + c) * d;
+  for (int64_t j0 = 0; j0 < nvec; j0 += 256 * kRep) {
+    float acc[kRep][VEC] = {};
+    for (int64_t e = lo; e < hi; ++e) {
+      const int2 en = list[e];
+      const float g = __int_as_float(en.y);
+#pragma unroll
+      for (int q = 0; q < kRep; ++q) {
+        const int64_t j = j0 + threadIdx.x + 256 * q;
+        if (j < nvec) {
+          float x[VEC];
+          Vec16<TE>::unpack(h[(int64_t)en.x * nvec + j], x);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[q][i] = __builtin_fmaf(g, x[i], acc[q][i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kRep; ++q) {
+      const int64_t j = j0 + threadIdx.x + 256 * q;
+      if (j < nvec) {
+        float4* o4 = (float4*)(out + j * VEC);
+#pragma unroll
+        for (int i = 0; i < VEC / 4; ++i) {
+          float4 y = make_float4(acc[q][4 * i], acc[q][4 * i + 1], acc[q][4 * i + 2], acc[q][4 * i + 3]);
+          if (runs == 1) {  // dW += the bucket's sum
+            const float4 old = o4[i];
+            y.x += old.x; y.y += old.y; y.z += old.z; y.w += old.w;
+          }
+          o4[i] = y;
+        }
+      }
+    }
+  }
+}
+
+// One workgroup per bucket of more than one run: dW's row += its runs'
+// partial rows, in run order.
+__global__ __launch_bounds__(256) void trkl_dw_combine_kernel(const int64_t* rstart, const int64_t* pstart,
+                                                              const int64_t* mstart, int64_t V, int64_t d,
+                                                              const float* part, float* dW) {
+  const int64_t m = blockIdx.x;
+  if (m >= mstart[V]) return;
+  const int64_t v = find_range(mstart, V, m);
+  const int64_t runs = rstart[v + 1] - rstart[v];
+  const float* p = part + pstart[v] * d;
+  float* out = dW + v * d;
+  for (int64_t j = threadIdx.x; j < d / 4; j += 256) {
+    float4 y = ((const float4*)out)[j];
+    for (int64_t c = 0; c < runs; ++c) {
+      const float4 x = ((const float4*)(p + c * d))[j];
+      y.x += x.x; y.y += x.y; y.z += x.z; y.w += x.w;
+    }
+    ((float4*)out)[j] = y;
+  }
 }
 
 hipError_t zero_bytes(void* p, int64_t bytes, hipStream_t s) {
@@ -440,23 +631,54 @@ hipError_t launch_topk_rkl(int dtype, const TopkArgs& a, bool backward, hipStrea
   return hipGetLastError();
 }
 
-hipError_t launch_topk_scatter(int dtype, const int2* ent, const float* dz, int rows, int K, int64_t v0,
-                               int64_t vlen, void* cv, int64_t ld_cv, void* vc, int64_t ld_vc,
-                               int64_t cv_elems, hipStream_t s) {
-  const int64_t es = dtype == 1 ? 2 : 4;
-  if ((cv_elems * es) % 16 != 0) return hipErrorInvalidValue;
-  hipError_t e = zero_bytes(cv, cv_elems * es, s);
-  if (e == hipSuccess && vc) e = zero_bytes(vc, cv_elems * es, s);
+hipError_t launch_trkl_dw(int dtype, const int2* ent, const float* dz, int rows, int K, int64_t V,
+                          const void* H, int64_t d, float* dW, bool accumulate, int* cnt, int64_t* scans,
+                          int2* list, float* part, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  if (K < 1 || K > 1024 || d % (dtype == 1 ? 8 : 4) != 0 || V >= INT32_MAX) return hipErrorInvalidValue;
+  const int nb = (rows + kBucketRows - 1) / kBucketRows;
   const int64_t n = (int64_t)rows * K;
-  if (e != hipSuccess || n <= 0) return e;
-  const dim3 grid((unsigned)((n + 255) / 256));
+  int64_t* total = scans;
+  int64_t* base = scans + (V + 1);
+  int64_t* rstart = scans + 2 * (V + 1);
+  int64_t* pstart = scans + 3 * (V + 1);
+  int64_t* mstart = scans + 4 * (V + 1);
+  hipError_t e = zero_bytes(cnt, trkl_count_bytes(rows, V), s);
+  if (e == hipSuccess && !accumulate) e = zero_bytes(dW, V * d * 4, s);  // V d a multiple of 4 (d is)
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(trkl_count_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ent, dz, n, K, V, cnt);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(trkl_scan_blocks_kernel, dim3((unsigned)((V + 255) / 256)), dim3(256), 0, s, cnt, nb, V,
+                       total);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(trkl_scan_ids_kernel, dim3(1), dim3(1024), 0, s, total, V, base, rstart, pstart, mstart);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(trkl_place_kernel, dim3((unsigned)nb), dim3(256), 0, s, ent, dz, rows, K, V, cnt, base, list);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) return e;
+  // at most one run per id plus one per kChunk entries; at most n / kChunk
+  // ids have more than one run
+  const dim3 run_grid((unsigned)(V + n / kChunk + 1)), block(256);
   if (dtype == 1)
-    hipLaunchKernelGGL(topk_scatter_kernel<uint16_t>, grid, dim3(256), 0, s, ent, dz, n, K, v0, vlen,
-                       (uint16_t*)cv, ld_cv, (uint16_t*)vc, ld_vc);
+    hipLaunchKernelGGL(trkl_dw_runs_kernel<uint16_t>, run_grid, block, 0, s, list, base, rstart, pstart, V, H, d,
+                       dW, part);
   else
-    hipLaunchKernelGGL(topk_scatter_kernel<float>, grid, dim3(256), 0, s, ent, dz, n, K, v0, vlen, (float*)cv,
-                       ld_cv, (float*)vc, ld_vc);
-  return hipGetLastError();
+    hipLaunchKernelGGL(trkl_dw_runs_kernel<float>, run_grid, block, 0, s, list, base, rstart, pstart, V, H, d, dW,
+                       part);
+  e = hipGetLastError();
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(trkl_dw_combine_kernel, dim3((unsigned)(n / kChunk + 1)), block, 0, s, rstart, pstart,
+                       mstart, V, d, part, dW);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace kdkl

@@ -142,10 +142,9 @@ typedef enum {
  *                   0 elsewhere. It needs the student's logits at S_i only:
  *                   the forward forms them as dot products of W's rows with
  *                   H (no projection over the vocabulary); the backward
- *                   forms dZ at S_i the same way and dH from the same rows,
- *                   then writes dZ into zeroed slices for the dW product
- *                   (a fixed reduction order without sorting the entries by
- *                   id).
+ *                   forms dZ at S_i the same way, dH from the same rows of
+ *                   W, and dW from the entries sorted by id (each row of dW
+ *                   summed in position order).
  *                   row_lse is [2, N]: the logsumexp of s_i over S_i (-inf
  *                   for an empty support), then L_i. */
 

@@ -103,6 +103,24 @@ def test_topk_rkl_gradient_only_on_the_support_and_accumulate():
     assert maxrel(acc["dW"][used] - base[used], got["dW"][used]) <= 1e-5
 
 
+def test_topk_rkl_hot_id_over_several_runs():
+    """One id at every one of 3000 positions (the head of a Zipf-like id
+    distribution): its dW row is summed by several workgroups, one per run of
+    1024 entries, and their partial rows in order; bitwise reproducible."""
+    w, x = _case("small_bf16", dict(N=3000, d=128, V=2000, K=8, chunk=512, T=1.0), 133)
+    ids = x["ids"].clone()
+    hot = 7
+    ids[~(ids == hot).any(dim=1), 0] = hot
+    x2 = dict(x, ids=ids)
+    print("case trkl hot id over several runs", flush=True)
+    got = run_gpu(x2, w.T, w.chunk, g=0.9, options=TRKL)
+    ref = oracle.topk_rkl_loss_and_grads(x2["H"], x2["W"], x2["ids"], x2["logits"], w.T, g=0.9)
+    _check(got, ref, x2, w.dtype, "trkl hot id")
+    assert maxrel(got["dW"][hot], ref["dW"][hot]) <= 1e-2
+    again = run_gpu(x2, w.T, w.chunk, g=0.9, options=TRKL)
+    assert np.array_equal(got["dW"], again["dW"]) and np.array_equal(got["dH"], again["dH"])
+
+
 def test_topk_rkl_noalloc_forward_and_determinism():
     import chunked_kl_loss_amd as kd
 
@@ -143,7 +161,8 @@ def test_topk_rkl_autograd():
 def test_topk_rkl_full_size_gptoss20b_32k():
     """The 32K gpt-oss-like workload in the bench's launch configuration:
     sampled positions (loss, logsumexp over the support, dH rows) and dW rows
-    of rarely used ids against the oracle, unused ids' dW rows exactly zero,
+    of rarely used ids and of the most used one (summed over several runs)
+    against the oracle, unused ids' dW rows exactly zero,
     the loss as the mean of the per-row values, and <W, dW> = <H, dH>."""
     import chunked_kl_loss_amd as kd
 
@@ -159,7 +178,7 @@ def test_topk_rkl_full_size_gptoss20b_32k():
     rows = sorted({0, 1, w.chunk, w.N - 1} | set(rng.choice(w.N, 8, replace=False).tolist()))
     counts = np.bincount(x["ids"].numpy().reshape(-1), minlength=w.V)
     rare = np.nonzero((counts >= 1) & (counts <= 40))[0]
-    vrows = sorted(rng.choice(rare, 4, replace=False).tolist())
+    vrows = sorted(rng.choice(rare, 4, replace=False).tolist()) + [int(np.argmax(counts))]  # and the most used id
     ref = oracle.topk_rkl_sampled(x["H"], x["W"], x["ids"], x["logits"], w.T, rows, vrows)
     lse = row_lse[0].double().cpu().numpy()
     kl = row_kl.double().cpu().numpy()
