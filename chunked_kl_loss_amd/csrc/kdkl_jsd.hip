@@ -430,58 +430,85 @@ __global__ __launch_bounds__(256) void trkl_scan_blocks_kernel(int* cnt, int nb,
 constexpr int64_t kChunk = 1024;
 __device__ __forceinline__ int64_t trkl_runs(int64_t n) { return (n + kChunk - 1) / kChunk; }
 
-// Exclusive scans over the ids (one workgroup: a contiguous run of ids per
-// thread, then a scan of the runs' sums), each with its total at index V:
+__device__ __forceinline__ int64_t shfl_up64(int64_t v, int d) {
+  const int lo = __shfl_up((int)(uint32_t)v, d, 64), hi = __shfl_up((int)(v >> 32), d, 64);
+  return ((int64_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ int64_t shfl_xor64(int64_t v, int m) {
+  const int lo = __shfl_xor((int)(uint32_t)v, m, 64), hi = __shfl_xor((int)(v >> 32), m, 64);
+  return ((int64_t)hi << 32) | (uint32_t)lo;
+}
+__device__ __forceinline__ int64_t shfl64(int64_t v, int src) {
+  const int lo = __shfl((int)(uint32_t)v, src, 64), hi = __shfl((int)(v >> 32), src, 64);
+  return ((int64_t)hi << 32) | (uint32_t)lo;
+}
+
+// the four quantities an id's bucket adds to the scans below
+__device__ __forceinline__ void trkl_terms(int64_t n, int64_t (&x)[4]) {
+  const int64_t r = trkl_runs(n);
+  x[0] = n;
+  x[1] = r;
+  x[2] = r > 1 ? r : 0;
+  x[3] = r > 1 ? 1 : 0;
+}
+
+// Exclusive scans over the ids, each with its total at index V:
 //   base:   bucket sizes (the bucket's first slot in the sorted list)
 //   rstart: runs of kChunk entries (the workgroup of a bucket's first run)
 //   pstart: the same over the buckets of more than one run (partial rows)
 //   mstart: the buckets of more than one run
+// One workgroup of 16 wavefronts, each over a contiguous range of ids in
+// tiles of 64 (coalesced reads, prefix sums across the lanes): the ranges'
+// sums first, then the scan of each range from its offset.
 __global__ __launch_bounds__(1024) void trkl_scan_ids_kernel(const int64_t* total, int64_t V, int64_t* base,
                                                             int64_t* rstart, int64_t* pstart, int64_t* mstart) {
-  __shared__ int64_t s[4][1024];
-  const int t = threadIdx.x;
-  const int64_t per = (V + 1023) / 1024;
-  const int64_t lo = t * per < V ? t * per : V;
+  __shared__ int64_t s_sum[4][16];
+  int64_t* out[4] = {base, rstart, pstart, mstart};
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t per = ((V + 15) / 16 + 63) / 64 * 64;  // ids per wavefront, whole tiles
+  const int64_t lo = w * per < V ? w * per : V;
   const int64_t hi = lo + per < V ? lo + per : V;
-  int64_t sum[4] = {0, 0, 0, 0};
-  for (int64_t i = lo; i < hi; ++i) {
-    const int64_t n = total[i], r = trkl_runs(n);
-    sum[0] += n;
-    sum[1] += r;
-    sum[2] += r > 1 ? r : 0;
-    sum[3] += r > 1 ? 1 : 0;
-  }
-#pragma unroll
-  for (int c = 0; c < 4; ++c) s[c][t] = sum[c];
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
+  int64_t acc[4] = {0, 0, 0, 0};
+  for (int64_t i = lo + lane; i < hi; i += 64) {
     int64_t x[4];
+    trkl_terms(total[i], x);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) x[c] = t >= o ? s[c][t - o] : 0;
-    __syncthreads();
-#pragma unroll
-    for (int c = 0; c < 4; ++c) s[c][t] += x[c];
-    __syncthreads();
+    for (int c = 0; c < 4; ++c) acc[c] += x[c];
   }
-  int64_t run[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) run[c] = t ? s[c][t - 1] : 0;
-  for (int64_t i = lo; i < hi; ++i) {
-    const int64_t n = total[i], r = trkl_runs(n);
-    base[i] = run[0];
-    rstart[i] = run[1];
-    pstart[i] = run[2];
-    mstart[i] = run[3];
-    run[0] += n;
-    run[1] += r;
-    run[2] += r > 1 ? r : 0;
-    run[3] += r > 1 ? 1 : 0;
+  for (int c = 0; c < 4; ++c) {
+    for (int o = 32; o > 0; o >>= 1) acc[c] += shfl_xor64(acc[c], o);
+    if (lane == 0) s_sum[c][w] = acc[c];
   }
-  if (t == 1023) {
-    base[V] = s[0][1023];
-    rstart[V] = s[1][1023];
-    pstart[V] = s[2][1023];
-    mstart[V] = s[3][1023];
+  __syncthreads();
+  int64_t off[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    off[c] = 0;
+    for (int u = 0; u < w; ++u) off[c] += s_sum[c][u];
+  }
+  for (int64_t i0 = lo; i0 < hi; i0 += 64) {
+    const int64_t i = i0 + lane;
+    int64_t x[4] = {0, 0, 0, 0};
+    if (i < hi) trkl_terms(total[i], x);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      int64_t inc = x[c];  // inclusive prefix across the lanes
+      for (int d = 1; d < 64; d <<= 1) {
+        const int64_t y = shfl_up64(inc, d);
+        if (lane >= d) inc += y;
+      }
+      if (i < hi) out[c][i] = off[c] + inc - x[c];
+      off[c] += shfl64(inc, 63);
+    }
+  }
+  if (w == 15 && lane == 0) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      int64_t t = 0;
+      for (int u = 0; u < 16; ++u) t += s_sum[c][u];
+      out[c][V] = t;
+    }
   }
 }
 
