@@ -187,10 +187,14 @@ hipError_t launch_topk_rkl(int dtype, const TopkArgs& a, bool backward, hipStrea
 // entries summed in order by one workgroup per run of 1024 (a bucket of
 // several runs through fp32 partial rows added in run order); dW is zeroed
 // first unless accumulating. Workspace: cnt (trkl_count_bytes), scans
-// (5 (V + 1) int64), list [rows K] int2, part (trkl_part_bytes).
+// (trkl_scan_bytes), list [rows K] int2, part (trkl_part_bytes).
 inline int64_t trkl_count_bytes(int64_t rows, int64_t V) {
   const int64_t nb = (rows + 255) / 256;  // positions per counting block: 256
   return (nb * V * 4 + 15) / 16 * 16;
+}
+inline int64_t trkl_scan_bytes(int64_t V) {
+  // five int64 arrays of V + 1 and four of the 256-id tiles' sums
+  return (5 * (V + 1) + 4 * ((V + 255) / 256)) * 8;
 }
 inline int64_t trkl_part_bytes(int64_t entries, int64_t d) {
   // buckets of more than one run of 1024 entries hold at most 2 entries / 1024 runs

@@ -434,15 +434,6 @@ __device__ __forceinline__ int64_t shfl_up64(int64_t v, int d) {
   const int lo = __shfl_up((int)(uint32_t)v, d, 64), hi = __shfl_up((int)(v >> 32), d, 64);
   return ((int64_t)hi << 32) | (uint32_t)lo;
 }
-__device__ __forceinline__ int64_t shfl_xor64(int64_t v, int m) {
-  const int lo = __shfl_xor((int)(uint32_t)v, m, 64), hi = __shfl_xor((int)(v >> 32), m, 64);
-  return ((int64_t)hi << 32) | (uint32_t)lo;
-}
-__device__ __forceinline__ int64_t shfl64(int64_t v, int src) {
-  const int lo = __shfl((int)(uint32_t)v, src, 64), hi = __shfl((int)(v >> 32), src, 64);
-  return ((int64_t)hi << 32) | (uint32_t)lo;
-}
-
 // the four quantities an id's bucket adds to the scans below
 __device__ __forceinline__ void trkl_terms(int64_t n, int64_t (&x)[4]) {
   const int64_t r = trkl_runs(n);
@@ -457,58 +448,82 @@ __device__ __forceinline__ void trkl_terms(int64_t n, int64_t (&x)[4]) {
 //   rstart: runs of kChunk entries (the workgroup of a bucket's first run)
 //   pstart: the same over the buckets of more than one run (partial rows)
 //   mstart: the buckets of more than one run
-// One workgroup of 16 wavefronts, each over a contiguous range of ids in
-// tiles of 64 (coalesced reads, prefix sums across the lanes): the ranges'
-// sums first, then the scan of each range from its offset.
-__global__ __launch_bounds__(1024) void trkl_scan_ids_kernel(const int64_t* total, int64_t V, int64_t* base,
-                                                            int64_t* rstart, int64_t* pstart, int64_t* mstart) {
-  __shared__ int64_t s_sum[4][16];
-  int64_t* out[4] = {base, rstart, pstart, mstart};
+// in three passes over tiles of 256 ids (one per thread): the tiles' sums,
+// their exclusive scan (one workgroup), and each tile's scan from its offset.
+constexpr int kScanTile = 256;
+constexpr int kScanWaves = kScanTile / 64;
+
+// inclusive prefix sums of x across the workgroup's threads (wavefront
+// scans, then the scan of the wavefront totals); tot gets the total
+__device__ __forceinline__ void block_scan4(int64_t (&x)[4], int64_t (&tot)[4], int64_t (*s_w)[kScanWaves]) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t per = ((V + 15) / 16 + 63) / 64 * 64;  // ids per wavefront, whole tiles
-  const int64_t lo = w * per < V ? w * per : V;
-  const int64_t hi = lo + per < V ? lo + per : V;
-  int64_t acc[4] = {0, 0, 0, 0};
-  for (int64_t i = lo + lane; i < hi; i += 64) {
-    int64_t x[4];
-    trkl_terms(total[i], x);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[c] += x[c];
-  }
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    for (int o = 32; o > 0; o >>= 1) acc[c] += shfl_xor64(acc[c], o);
-    if (lane == 0) s_sum[c][w] = acc[c];
+    for (int d = 1; d < 64; d <<= 1) {
+      const int64_t y = shfl_up64(x[c], d);
+      if (lane >= d) x[c] += y;
+    }
+    if (lane == 63) s_w[c][w] = x[c];
   }
   __syncthreads();
-  int64_t off[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
-    off[c] = 0;
-    for (int u = 0; u < w; ++u) off[c] += s_sum[c][u];
+    int64_t off = 0;
+    tot[c] = 0;
+    for (int u = 0; u < kScanWaves; ++u) {
+      off += u < w ? s_w[c][u] : 0;
+      tot[c] += s_w[c][u];
+    }
+    x[c] += off;
   }
-  for (int64_t i0 = lo; i0 < hi; i0 += 64) {
-    const int64_t i = i0 + lane;
-    int64_t x[4] = {0, 0, 0, 0};
-    if (i < hi) trkl_terms(total[i], x);
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kScanTile) void trkl_scan_tiles_kernel(const int64_t* total, int64_t V, int64_t* tsum) {
+  __shared__ int64_t s_w[4][kScanWaves];
+  const int64_t i = (int64_t)blockIdx.x * kScanTile + threadIdx.x;
+  int64_t x[4] = {0, 0, 0, 0}, tot[4];
+  if (i < V) trkl_terms(total[i], x);
+  block_scan4(x, tot, s_w);
+  if (threadIdx.x < 4) tsum[(int64_t)threadIdx.x * gridDim.x + blockIdx.x] = tot[threadIdx.x];
+}
+
+// exclusive scan of the tiles' sums (nt of each quantity), in place, in
+// chunks of 1024 with a running offset
+__global__ __launch_bounds__(kScanTile) void trkl_scan_sums_kernel(int64_t* tsum, int64_t nt) {
+  __shared__ int64_t s_w[4][kScanWaves];
+  int64_t run[4] = {0, 0, 0, 0};
+  for (int64_t t0 = 0; t0 < nt; t0 += kScanTile) {
+    const int64_t t = t0 + threadIdx.x;
+    int64_t x[4], own[4], tot[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) own[c] = x[c] = t < nt ? tsum[c * nt + t] : 0;
+    block_scan4(x, tot, s_w);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
-      int64_t inc = x[c];  // inclusive prefix across the lanes
-      for (int d = 1; d < 64; d <<= 1) {
-        const int64_t y = shfl_up64(inc, d);
-        if (lane >= d) inc += y;
-      }
-      if (i < hi) out[c][i] = off[c] + inc - x[c];
-      off[c] += shfl64(inc, 63);
+      if (t < nt) tsum[c * nt + t] = run[c] + x[c] - own[c];
+      run[c] += tot[c];
     }
   }
-  if (w == 15 && lane == 0) {
+}
+
+__global__ __launch_bounds__(kScanTile) void trkl_scan_out_kernel(const int64_t* total, int64_t V, const int64_t* tsum,
+                                                                 int64_t* base, int64_t* rstart, int64_t* pstart,
+                                                                 int64_t* mstart) {
+  __shared__ int64_t s_w[4][kScanWaves];
+  int64_t* out[4] = {base, rstart, pstart, mstart};
+  const int64_t nt = gridDim.x;
+  const int64_t i = (int64_t)blockIdx.x * kScanTile + threadIdx.x;
+  int64_t x[4] = {0, 0, 0, 0}, own[4], tot[4];
+  if (i < V) trkl_terms(total[i], x);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      int64_t t = 0;
-      for (int u = 0; u < 16; ++u) t += s_sum[c][u];
-      out[c][V] = t;
-    }
+  for (int c = 0; c < 4; ++c) own[c] = x[c];
+  block_scan4(x, tot, s_w);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int64_t off = tsum[c * nt + blockIdx.x];
+    if (i < V) out[c][i] = off + x[c] - own[c];
+    if (blockIdx.x == nt - 1 && threadIdx.x == 0) out[c][V] = off + tot[c];
   }
 }
 
@@ -681,8 +696,19 @@ hipError_t launch_trkl_dw(int dtype, const int2* ent, const float* dz, int rows,
                        total);
     e = hipGetLastError();
   }
+  const int64_t nt = (V + kScanTile - 1) / kScanTile;
+  int64_t* tsum = scans + 5 * (V + 1);  // [4, nt]
   if (e == hipSuccess) {
-    hipLaunchKernelGGL(trkl_scan_ids_kernel, dim3(1), dim3(1024), 0, s, total, V, base, rstart, pstart, mstart);
+    hipLaunchKernelGGL(trkl_scan_tiles_kernel, dim3((unsigned)nt), dim3(kScanTile), 0, s, total, V, tsum);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(trkl_scan_sums_kernel, dim3(1), dim3(kScanTile), 0, s, tsum, nt);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(trkl_scan_out_kernel, dim3((unsigned)nt), dim3(kScanTile), 0, s, total, V, tsum, base, rstart,
+                       pstart, mstart);
     e = hipGetLastError();
   }
   if (e == hipSuccess) {
