@@ -801,8 +801,11 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
       t.row_lse = const_cast<float*>(row_lse) + r0; t.row_loss = const_cast<float*>(row_lse) + N + r0;
       t.scale = (const float*)(ws + P.b_scale); t.dz = (float*)(ws + P.b_dzent);
       t.dH = (char*)dH + r0 * d * P.es;
-      e = timed(K_TOPK_RKL, 4.0 * rows * (double)P.K * d, (double)rows * (P.K * (2.0 * d * P.es + 12.0) + d * P.es),
-                s, [&] { return launch_topk_rkl(dtype, t, true, s); });
+      // each support row of W read once or twice, H read and dH written
+      const double w_reads = topk_rkl_one_pass(dtype, d) ? 1.0 : 2.0;
+      e = timed(K_TOPK_RKL, 4.0 * rows * (double)P.K * d,
+                (double)rows * (P.K * (w_reads * d * P.es + 12.0) + 2.0 * d * P.es), s,
+                [&] { return launch_topk_rkl(dtype, t, true, s); });
       if (e == hipSuccess)
         e = timed(K_TOPK_DW, 2.0 * rows * (double)P.K * d, (double)rows * P.K * (d * P.es + 16.0) + 8.0 * V * d, s,
                   [&] {

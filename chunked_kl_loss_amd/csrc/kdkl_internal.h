@@ -181,6 +181,9 @@ struct TopkArgs {
   void* dH;           // backward out: [rows, d] storage dtype (group-offset), sum_k dz_k W[id_k]
 };
 hipError_t launch_topk_rkl(int dtype, const TopkArgs& a, bool backward, hipStream_t s);
+// whether the backward reads each support row of W once (rows of at most 6
+// 16-byte vectors per lane: d <= 3072 in bf16, 1536 in fp32) or twice
+inline bool topk_rkl_one_pass(int dtype, int64_t d) { return d / (dtype == 1 ? 8 : 4) <= 64 * 6; }
 // dW (+)= the reverse KL's dZ^T H for one group of `rows` positions, from the
 // entry gradients dz [rows, K] at the sorted entries `ent`, without a dense
 // product: the nonzero entries sorted by id in position order, then each id's

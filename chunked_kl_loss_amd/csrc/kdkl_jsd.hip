@@ -241,6 +241,30 @@ __device__ __forceinline__ float wmax(float v) {
   return v;
 }
 
+// The support of a kept position and its masses, each lane its entries: an
+// id's first entry (the entries are sorted by id) gets the summed mass of its
+// repeats, every other entry 0, and so does every entry of an id outside
+// [0, V) and of an ignored position.
+__device__ __forceinline__ void support_masses(const int2* ent, int K, int64_t V, bool keep, int lane, float* sP) {
+  for (int k = lane; k < K; k += 64) {
+    const int2 e = ent[k];
+    float P = 0.f;
+    if (keep && e.x >= 0 && e.x < V && (k == 0 || ent[k - 1].x != e.x)) {
+      P = __int_as_float(e.y);
+      for (int k2 = k + 1; k2 < K && ent[k2].x == e.x; ++k2) P += __int_as_float(ent[k2].y);
+    }
+    sP[k] = P;
+  }
+  __builtin_amdgcn_wave_barrier();
+}
+
+// a row's gradient at one support entry from its logit, the forward's
+// logsumexp over the support and the forward's loss
+__device__ __forceinline__ float trkl_grad(float s, float P, float lse, float L, float coef) {
+  const float lq = s - lse;
+  return coef * exp_hw(lq) * (lq - log_hw(P) - L);
+}
+
 template <typename TE, int KMAX>  // K <= KMAX
 __global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_kernel(TopkArgs a, int backward) {
   __shared__ float s_s[kRowsPerBlock][KMAX];  // s at each sorted entry of the support
@@ -255,17 +279,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_kernel(TopkArgs a
   const bool keep = a.keep[row] != 0.f;
   const int64_t nvec = a.d / VEC;
   const uint4* hp = (const uint4*)((const TE*)a.H + (int64_t)row * a.d);
-  // the support and its masses (each lane its entries)
-  for (int k = lane; k < K; k += 64) {
-    const int2 e = ent[k];
-    float P = 0.f;
-    if (keep && e.x >= 0 && e.x < a.V && (k == 0 || ent[k - 1].x != e.x)) {
-      P = __int_as_float(e.y);
-      for (int k2 = k + 1; k2 < K && ent[k2].x == e.x; ++k2) P += __int_as_float(ent[k2].y);
-    }
-    s_P[w][k] = P;
-  }
-  __builtin_amdgcn_wave_barrier();
+  support_masses(ent, K, a.V, keep, lane, s_P[w]);
   // the student's logits there, kDots entries at a time across the
   // wavefront (their rows of W read together; an entry off the support
   // reads row 0 and is not kept)
@@ -331,11 +345,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_kernel(TopkArgs a
   const float coef = keep ? a.scale[0] : 0.f;
   for (int k = lane; k < K; k += 64) {
     const float P = s_P[w][k];
-    float gk = 0.f;
-    if (P > 0.f) {
-      const float lq = s_s[w][k] - lse;
-      gk = coef * exp_hw(lq) * (lq - log_hw(P) - L);
-    }
+    const float gk = P > 0.f ? trkl_grad(s_s[w][k], P, lse, L, coef) : 0.f;
     a.dz[(int64_t)row * K + k] = gk;
     s_s[w][k] = gk;
   }
@@ -377,6 +387,104 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_kernel(TopkArgs a
       if (j < nvec) Vec16<TE>::store_vec(dh + j * VEC, acc[r]);
     }
   }
+}
+
+// The backward in one pass over the support's rows of W, for rows of at most
+// 64 JMAX 16-byte vectors: with the forward's logsumexp and loss at hand, an
+// entry's gradient needs only its own logit, so each row is read once, into
+// registers, for its dot product and then for its share of the dH row (half
+// the bytes of the two-pass form, whose second pass reads the rows again).
+// Rows go kDots at a time, two groups in flight. The products and the order
+// of every sum are those of the two-pass backward above (the dot products
+// lane by lane in vector order, dH in entry order), so both give the same
+// bits.
+template <typename TE, int KMAX, int JMAX>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_bwd_kernel(TopkArgs a) {
+  __shared__ float s_g[kRowsPerBlock][KMAX];  // the gradient at each sorted entry
+  __shared__ float s_P[kRowsPerBlock][KMAX];  // its teacher mass (0 off the support)
+  constexpr int VEC = Vec16<TE>::kN;
+  constexpr int kDots = 2;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = blockIdx.x * kRowsPerBlock + w;
+  if (row >= a.rows) return;
+  const int K = a.K;
+  const int2* ent = a.ent + (int64_t)row * K;
+  const bool keep = a.keep[row] != 0.f;
+  const int nvec = (int)(a.d / VEC);  // <= 64 JMAX
+  // each lane's vectors of a row, clamped to the row's last so that every
+  // load is a whole 16-byte load (the vectors past the row are not used)
+  int jv[JMAX];
+#pragma unroll
+  for (int r = 0; r < JMAX; ++r) jv[r] = min(lane + 64 * r, nvec - 1);
+  const uint4* hp = (const uint4*)((const TE*)a.H + (int64_t)row * a.d);
+  uint4 hv[JMAX];
+#pragma unroll
+  for (int r = 0; r < JMAX; ++r) hv[r] = hp[jv[r]];
+  support_masses(ent, K, a.V, keep, lane, s_P[w]);
+  const float lse = a.row_lse[row], L = a.row_loss[row];
+  const float coef = keep ? a.scale[0] : 0.f;
+  float acc[JMAX][VEC] = {};
+  // a group's rows (an entry off the support, or past K, reads row 0 and is
+  // not kept)
+  auto load_group = [&](uint4 (&xv)[kDots][JMAX], float (&P)[kDots], int k0) {
+#pragma unroll
+    for (int q = 0; q < kDots; ++q) {
+      const int k = k0 + q;
+      const int kc = k < K ? k : K - 1;
+      P[q] = k < K ? s_P[w][kc] : 0.f;
+      const int id = __builtin_amdgcn_readfirstlane(P[q] > 0.f ? ent[kc].x : 0);
+      const uint4* wp = (const uint4*)((const TE*)a.W + (int64_t)id * a.d);
+#pragma unroll
+      for (int r = 0; r < JMAX; ++r) xv[q][r] = wp[jv[r]];
+    }
+  };
+  // its dot products, gradients and shares of the dH row
+  auto use_group = [&](const uint4 (&xv)[kDots][JMAX], const float (&P)[kDots], int k0) {
+#pragma unroll
+    for (int q = 0; q < kDots; ++q) {
+      float dot = 0.f;
+#pragma unroll
+      for (int r = 0; r < JMAX; ++r) {
+        if (lane + 64 * r < nvec) {
+          float x[VEC], y[VEC];
+          Vec16<TE>::unpack(xv[q][r], x);
+          Vec16<TE>::unpack(hv[r], y);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) dot = __builtin_fmaf(x[i], y[i], dot);
+        }
+      }
+      const float sv = wsum(dot) * a.inv_T;
+      const float gk = P[q] > 0.f ? trkl_grad(sv, P[q], lse, L, coef) : 0.f;
+      if (lane == 0 && k0 + q < K) s_g[w][k0 + q] = gk;
+      if (gk != 0.f) {  // (wave-uniform)
+#pragma unroll
+        for (int r = 0; r < JMAX; ++r) {
+          float x[VEC];
+          Vec16<TE>::unpack(xv[q][r], x);
+#pragma unroll
+          for (int i = 0; i < VEC; ++i) acc[r][i] = __builtin_fmaf(gk, x[i], acc[r][i]);
+        }
+      }
+    }
+  };
+  // two groups in flight: the next group's loads go out before the current
+  // group's arithmetic
+  uint4 xa[kDots][JMAX], xb[kDots][JMAX];
+  float Pa[kDots], Pb[kDots];
+  load_group(xa, Pa, 0);
+  for (int k0 = 0; k0 < K; k0 += 2 * kDots) {
+    load_group(xb, Pb, k0 + kDots);
+    use_group(xa, Pa, k0);
+    load_group(xa, Pa, k0 + 2 * kDots);
+    use_group(xb, Pb, k0 + kDots);
+  }
+  __builtin_amdgcn_wave_barrier();
+  for (int k = lane; k < K; k += 64) a.dz[(int64_t)row * K + k] = s_g[w][k];
+  TE* dh = (TE*)a.dH + (int64_t)row * a.d;
+#pragma unroll
+  for (int r = 0; r < JMAX; ++r)
+    if (lane + 64 * r < nvec) Vec16<TE>::store_vec(dh + (int64_t)(lane + 64 * r) * VEC, acc[r]);
 }
 
 __global__ __launch_bounds__(256) void zero16_kernel(uint4* __restrict__ p, int64_t n) {
@@ -663,6 +771,16 @@ hipError_t launch_topk_rkl(int dtype, const TopkArgs& a, bool backward, hipStrea
   if (a.d % (dtype == 1 ? 8 : 4) != 0) return hipErrorInvalidValue;  // rows of whole 16-byte vectors
   const dim3 grid = rows_grid(a.rows), block(64 * kRowsPerBlock);
   const int b = backward ? 1 : 0;
+  if (backward && topk_rkl_one_pass(dtype, a.d)) {
+    if (dtype == 1) {
+      if (a.K <= 128) hipLaunchKernelGGL((topk_rkl_bwd_kernel<uint16_t, 128, 6>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((topk_rkl_bwd_kernel<uint16_t, 1024, 6>), grid, block, 0, s, a);
+    } else {
+      if (a.K <= 128) hipLaunchKernelGGL((topk_rkl_bwd_kernel<float, 128, 6>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((topk_rkl_bwd_kernel<float, 1024, 6>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+  }
   if (dtype == 1) {
     if (a.K <= 128) hipLaunchKernelGGL((topk_rkl_kernel<uint16_t, 128>), grid, block, 0, s, a, b);
     else hipLaunchKernelGGL((topk_rkl_kernel<uint16_t, 1024>), grid, block, 0, s, a, b);

@@ -26,6 +26,11 @@ CASES = [
     ("gptoss_geometry", "gptoss20b_32k", dict(N=80, chunk=32), 125, None),
     ("longctx_geometry_T2", "longctx_256k", dict(N=64, chunk=24), 126, None),
     ("bf16_max_K", "small_bf16", dict(N=100, d=128, V=6000, K=1024, chunk=64, T=1.0), 127, None),
+    # the backward holds rows of up to 6 vectors per lane in registers
+    # (d <= 3072 in bf16, 1536 in fp32); wider rows take two passes
+    ("bf16_rows_at_register_limit", "small_bf16", dict(N=90, d=3072, V=5000, K=20, chunk=32, T=1.0), 134, None),
+    ("bf16_wide_rows_two_pass", "small_bf16", dict(N=90, d=3080, V=5000, K=20, chunk=32, T=1.0), 135, None),
+    ("fp32_wide_rows_two_pass", "tiny_fp32", dict(N=50, d=1540, V=3000, K=9, chunk=32, T=1.0), 136, None),
 ]
 
 
