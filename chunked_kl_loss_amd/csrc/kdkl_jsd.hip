@@ -265,6 +265,36 @@ __device__ __forceinline__ float trkl_grad(float s, float P, float lse, float L,
   return coef * exp_hw(lq) * (lq - log_hw(P) - L);
 }
 
+// The forward's outputs of a position from its support logits sS and masses
+// sP (each lane its entries): the logsumexp over the support (-inf for an
+// empty one) and the loss.
+__device__ __forceinline__ void trkl_forward_out(const TopkArgs& a, int row, int lane, int K, bool keep,
+                                                 const float* sS, const float* sP) {
+  float m = kNegInf;
+  for (int k = lane; k < K; k += 64)
+    if (sP[k] > 0.f) m = fmaxf(m, sS[k]);
+  m = wmax(m);
+  float se = 0.f;
+  for (int k = lane; k < K; k += 64)
+    if (sP[k] > 0.f) se += exp_hw(sS[k] - m);
+  se = wsum(se);
+  const float lse = m > kNegInf ? m + log_hw(se) : kNegInf;
+  float L = 0.f;
+  for (int k = lane; k < K; k += 64) {
+    const float P = sP[k];
+    if (P > 0.f) {
+      const float lq = sS[k] - lse;
+      L += exp_hw(lq) * (lq - log_hw(P));
+    }
+  }
+  L = wsum(L);
+  if (lane == 0) {
+    a.row_lse[row] = lse;
+    a.row_loss[row] = L;
+    a.row_kl[row] = keep ? L : 0.f;
+  }
+}
+
 template <typename TE, int KMAX>  // K <= KMAX
 __global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_kernel(TopkArgs a, int backward) {
   __shared__ float s_s[kRowsPerBlock][KMAX];  // s at each sorted entry of the support
@@ -314,29 +344,7 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_kernel(TopkArgs a
   }
   __builtin_amdgcn_wave_barrier();
   if (!backward) {
-    float m = kNegInf;
-    for (int k = lane; k < K; k += 64)
-      if (s_P[w][k] > 0.f) m = fmaxf(m, s_s[w][k]);
-    m = wmax(m);
-    float se = 0.f;
-    for (int k = lane; k < K; k += 64)
-      if (s_P[w][k] > 0.f) se += exp_hw(s_s[w][k] - m);
-    se = wsum(se);
-    const float lse = m > kNegInf ? m + log_hw(se) : kNegInf;
-    float L = 0.f;
-    for (int k = lane; k < K; k += 64) {
-      const float P = s_P[w][k];
-      if (P > 0.f) {
-        const float lq = s_s[w][k] - lse;
-        L += exp_hw(lq) * (lq - log_hw(P));
-      }
-    }
-    L = wsum(L);
-    if (lane == 0) {
-      a.row_lse[row] = lse;
-      a.row_loss[row] = L;
-      a.row_kl[row] = keep ? L : 0.f;
-    }
+    trkl_forward_out(a, row, lane, K, keep, s_s[w], s_P[w]);
     return;
   }
   // the gradient at each sorted entry, from the forward's logsumexp and loss
@@ -389,18 +397,18 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_kernel(TopkArgs a
   }
 }
 
-// The backward in one pass over the support's rows of W, for rows of at most
-// 64 JMAX 16-byte vectors: with the forward's logsumexp and loss at hand, an
-// entry's gradient needs only its own logit, so each row is read once, into
-// registers, for its dot product and then for its share of the dH row (half
-// the bytes of the two-pass form, whose second pass reads the rows again).
-// Rows go kDots at a time, two groups in flight. The products and the order
-// of every sum are those of the two-pass backward above (the dot products
-// lane by lane in vector order, dH in entry order), so both give the same
-// bits.
-template <typename TE, int KMAX, int JMAX>
-__global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_bwd_kernel(TopkArgs a) {
-  __shared__ float s_g[kRowsPerBlock][KMAX];  // the gradient at each sorted entry
+// Both calls with each support row of W read once, into registers, for rows
+// of at most 64 JMAX 16-byte vectors: the forward takes each row's dot
+// product; the backward, with the forward's logsumexp and loss at hand, needs
+// only an entry's own logit for its gradient, so it adds the row's share of
+// the dH row while the row is still in registers (half the bytes of the
+// two-pass form above, whose second pass reads the rows again). Rows go
+// kDots at a time, two groups in flight. The products and the order of every
+// sum are those of the two-pass kernel (the dot products lane by lane in
+// vector order, dH in entry order), so both give the same bits.
+template <typename TE, int KMAX, int JMAX, bool BWD>
+__global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_rows_kernel(TopkArgs a) {
+  __shared__ float s_g[kRowsPerBlock][KMAX];  // forward: s at each sorted entry; backward: the gradient there
   __shared__ float s_P[kRowsPerBlock][KMAX];  // its teacher mass (0 off the support)
   constexpr int VEC = Vec16<TE>::kN;
   constexpr int kDots = 2;
@@ -422,8 +430,8 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_bwd_kernel(TopkAr
 #pragma unroll
   for (int r = 0; r < JMAX; ++r) hv[r] = hp[jv[r]];
   support_masses(ent, K, a.V, keep, lane, s_P[w]);
-  const float lse = a.row_lse[row], L = a.row_loss[row];
-  const float coef = keep ? a.scale[0] : 0.f;
+  const float lse = BWD ? a.row_lse[row] : 0.f, L = BWD ? a.row_loss[row] : 0.f;
+  const float coef = BWD && keep ? a.scale[0] : 0.f;
   float acc[JMAX][VEC] = {};
   // a group's rows (an entry off the support, or past K, reads row 0 and is
   // not kept)
@@ -455,6 +463,10 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_bwd_kernel(TopkAr
         }
       }
       const float sv = wsum(dot) * a.inv_T;
+      if (!BWD) {
+        if (lane == 0 && k0 + q < K) s_g[w][k0 + q] = P[q] > 0.f ? sv : 0.f;
+        continue;
+      }
       const float gk = P[q] > 0.f ? trkl_grad(sv, P[q], lse, L, coef) : 0.f;
       if (lane == 0 && k0 + q < K) s_g[w][k0 + q] = gk;
       if (gk != 0.f) {  // (wave-uniform)
@@ -480,6 +492,10 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void topk_rkl_bwd_kernel(TopkAr
     use_group(xb, Pb, k0 + kDots);
   }
   __builtin_amdgcn_wave_barrier();
+  if (!BWD) {
+    trkl_forward_out(a, row, lane, K, keep, s_g[w], s_P[w]);
+    return;
+  }
   for (int k = lane; k < K; k += 64) a.dz[(int64_t)row * K + k] = s_g[w][k];
   TE* dh = (TE*)a.dH + (int64_t)row * a.d;
 #pragma unroll
@@ -771,13 +787,23 @@ hipError_t launch_topk_rkl(int dtype, const TopkArgs& a, bool backward, hipStrea
   if (a.d % (dtype == 1 ? 8 : 4) != 0) return hipErrorInvalidValue;  // rows of whole 16-byte vectors
   const dim3 grid = rows_grid(a.rows), block(64 * kRowsPerBlock);
   const int b = backward ? 1 : 0;
-  if (backward && topk_rkl_one_pass(dtype, a.d)) {
+  if (topk_rkl_one_pass(dtype, a.d)) {
     if (dtype == 1) {
-      if (a.K <= 128) hipLaunchKernelGGL((topk_rkl_bwd_kernel<uint16_t, 128, 6>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL((topk_rkl_bwd_kernel<uint16_t, 1024, 6>), grid, block, 0, s, a);
+      if (a.K <= 128) {
+        if (backward) hipLaunchKernelGGL((topk_rkl_rows_kernel<uint16_t, 128, 6, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((topk_rkl_rows_kernel<uint16_t, 128, 6, false>), grid, block, 0, s, a);
+      } else {
+        if (backward) hipLaunchKernelGGL((topk_rkl_rows_kernel<uint16_t, 1024, 6, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((topk_rkl_rows_kernel<uint16_t, 1024, 6, false>), grid, block, 0, s, a);
+      }
     } else {
-      if (a.K <= 128) hipLaunchKernelGGL((topk_rkl_bwd_kernel<float, 128, 6>), grid, block, 0, s, a);
-      else hipLaunchKernelGGL((topk_rkl_bwd_kernel<float, 1024, 6>), grid, block, 0, s, a);
+      if (a.K <= 128) {
+        if (backward) hipLaunchKernelGGL((topk_rkl_rows_kernel<float, 128, 6, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((topk_rkl_rows_kernel<float, 128, 6, false>), grid, block, 0, s, a);
+      } else {
+        if (backward) hipLaunchKernelGGL((topk_rkl_rows_kernel<float, 1024, 6, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((topk_rkl_rows_kernel<float, 1024, 6, false>), grid, block, 0, s, a);
+      }
     }
     return hipGetLastError();
   }
