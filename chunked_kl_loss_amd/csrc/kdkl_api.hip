@@ -807,7 +807,9 @@ kdkl_status kdkl_backward(const void* H, const void* W, const int32_t* ids, cons
                 (double)rows * (P.K * (w_reads * d * P.es + 12.0) + 2.0 * d * P.es), s,
                 [&] { return launch_topk_rkl(dtype, t, true, s); });
       if (e == hipSuccess)
-        e = timed(K_TOPK_DW, 2.0 * rows * (double)P.K * d, (double)rows * P.K * (d * P.es + 16.0) + 8.0 * V * d, s,
+        // dW written (4 V d bytes) or read and written (8 V d)
+        e = timed(K_TOPK_DW, 2.0 * rows * (double)P.K * d,
+                  (double)rows * P.K * (d * P.es + 16.0) + ((r0 > 0 || accumulate_dW) ? 8.0 : 4.0) * V * d, s,
                   [&] {
                     return launch_trkl_dw(dtype, (const int2*)(ws + P.b_ent), (const float*)(ws + P.b_dzent), rows,
                                           (int)P.K, V, Hg, d, dW, r0 > 0 || accumulate_dW, (int*)(ws + P.b_cnt),

@@ -188,8 +188,9 @@ inline bool topk_rkl_one_pass(int dtype, int64_t d) { return d / (dtype == 1 ? 8
 // entry gradients dz [rows, K] at the sorted entries `ent`, without a dense
 // product: the nonzero entries sorted by id in position order, then each id's
 // entries summed in order by one workgroup per run of 1024 (a bucket of
-// several runs through fp32 partial rows added in run order); dW is zeroed
-// first unless accumulating. Workspace: cnt (trkl_count_bytes), scans
+// several runs through fp32 partial rows added in run order); unless
+// accumulating, each row of dW is written rather than added to (zeros for
+// the ids without entries). Workspace: cnt (trkl_count_bytes), scans
 // (trkl_scan_bytes), list [rows K] int2, part (trkl_part_bytes).
 inline int64_t trkl_count_bytes(int64_t rows, int64_t V) {
   const int64_t nb = (rows + 255) / 256;  // positions per counting block: 256

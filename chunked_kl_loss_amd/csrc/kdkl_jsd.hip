@@ -682,12 +682,13 @@ __global__ __launch_bounds__(256) void trkl_place_kernel(const int2* ent, const 
 
 // One workgroup per run of a bucket (launched for the most runs there can
 // be; the ones past the total exit): the run's sum of dz H_r over its
-// entries in order, added to dW's row for a bucket of one run, else written
-// as the run's partial row.
+// entries in order, added to dW's row for a bucket of one run (written over
+// it when dW is overwritten), else written as the run's partial row.
 template <typename TE>
 __global__ __launch_bounds__(256) void trkl_dw_runs_kernel(const int2* list, const int64_t* base,
                                                            const int64_t* rstart, const int64_t* pstart, int64_t V,
-                                                           const void* H, int64_t d, float* dW, float* part) {
+                                                           const void* H, int64_t d, float* dW, float* part,
+                                                           int overwrite) {
   constexpr int VEC = Vec16<TE>::kN;
   constexpr int kRep = 2;
   const int64_t w = blockIdx.x;
@@ -724,7 +725,7 @@ __global__ __launch_bounds__(256) void trkl_dw_runs_kernel(const int2* list, con
 #pragma unroll
         for (int i = 0; i < VEC / 4; ++i) {
           float4 y = make_float4(acc[q][4 * i], acc[q][4 * i + 1], acc[q][4 * i + 2], acc[q][4 * i + 3]);
-          if (runs == 1) {  // dW += the bucket's sum
+          if (runs == 1 && !overwrite) {  // dW += the bucket's sum
             const float4 old = o4[i];
             y.x += old.x; y.y += old.y; y.z += old.z; y.w += old.w;
           }
@@ -736,10 +737,10 @@ __global__ __launch_bounds__(256) void trkl_dw_runs_kernel(const int2* list, con
 }
 
 // One workgroup per bucket of more than one run: dW's row += its runs'
-// partial rows, in run order.
+// partial rows, in run order (from zero when dW is overwritten).
 __global__ __launch_bounds__(256) void trkl_dw_combine_kernel(const int64_t* rstart, const int64_t* pstart,
                                                               const int64_t* mstart, int64_t V, int64_t d,
-                                                              const float* part, float* dW) {
+                                                              const float* part, float* dW, int overwrite) {
   const int64_t m = blockIdx.x;
   if (m >= mstart[V]) return;
   const int64_t v = find_range(mstart, V, m);
@@ -747,13 +748,22 @@ __global__ __launch_bounds__(256) void trkl_dw_combine_kernel(const int64_t* rst
   const float* p = part + pstart[v] * d;
   float* out = dW + v * d;
   for (int64_t j = threadIdx.x; j < d / 4; j += 256) {
-    float4 y = ((const float4*)out)[j];
+    float4 y = overwrite ? make_float4(0.f, 0.f, 0.f, 0.f) : ((const float4*)out)[j];
     for (int64_t c = 0; c < runs; ++c) {
       const float4 x = ((const float4*)(p + c * d))[j];
       y.x += x.x; y.y += x.y; y.z += x.z; y.w += x.w;
     }
     ((float4*)out)[j] = y;
   }
+}
+
+// dW's rows of the ids without entries, when dW is written rather than added
+// to (the other rows are written whole by the runs or their combination)
+__global__ __launch_bounds__(256) void trkl_zero_rows_kernel(const int64_t* total, int64_t V, int64_t d, float* dW) {
+  const int64_t v = blockIdx.x;
+  if (v >= V || total[v] != 0) return;
+  float4* out = (float4*)(dW + v * d);
+  for (int64_t j = threadIdx.x; j < d / 4; j += 256) out[j] = make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
 hipError_t zero_bytes(void* p, int64_t bytes, hipStream_t s) {
@@ -830,7 +840,6 @@ hipError_t launch_trkl_dw(int dtype, const int2* ent, const float* dz, int rows,
   int64_t* pstart = scans + 3 * (V + 1);
   int64_t* mstart = scans + 4 * (V + 1);
   hipError_t e = zero_bytes(cnt, trkl_count_bytes(rows, V), s);
-  if (e == hipSuccess && !accumulate) e = zero_bytes(dW, V * d * 4, s);  // V d a multiple of 4 (d is)
   if (e == hipSuccess) {
     hipLaunchKernelGGL(trkl_count_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ent, dz, n, K, V, cnt);
     e = hipGetLastError();
@@ -838,6 +847,10 @@ hipError_t launch_trkl_dw(int dtype, const int2* ent, const float* dz, int rows,
   if (e == hipSuccess) {
     hipLaunchKernelGGL(trkl_scan_blocks_kernel, dim3((unsigned)((V + 255) / 256)), dim3(256), 0, s, cnt, nb, V,
                        total);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess && !accumulate) {  // (d a multiple of 4: whole float4 rows)
+    hipLaunchKernelGGL(trkl_zero_rows_kernel, dim3((unsigned)V), dim3(256), 0, s, total, V, d, dW);
     e = hipGetLastError();
   }
   const int64_t nt = (V + kScanTile - 1) / kScanTile;
@@ -865,14 +878,14 @@ hipError_t launch_trkl_dw(int dtype, const int2* ent, const float* dz, int rows,
   const dim3 run_grid((unsigned)(V + n / kChunk + 1)), block(256);
   if (dtype == 1)
     hipLaunchKernelGGL(trkl_dw_runs_kernel<uint16_t>, run_grid, block, 0, s, list, base, rstart, pstart, V, H, d,
-                       dW, part);
+                       dW, part, accumulate ? 0 : 1);
   else
     hipLaunchKernelGGL(trkl_dw_runs_kernel<float>, run_grid, block, 0, s, list, base, rstart, pstart, V, H, d, dW,
-                       part);
+                       part, accumulate ? 0 : 1);
   e = hipGetLastError();
   if (e == hipSuccess) {
     hipLaunchKernelGGL(trkl_dw_combine_kernel, dim3((unsigned)(n / kChunk + 1)), block, 0, s, rstart, pstart,
-                       mstart, V, d, part, dW);
+                       mstart, V, d, part, dW, accumulate ? 0 : 1);
     e = hipGetLastError();
   }
   return e;

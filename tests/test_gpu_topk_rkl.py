@@ -94,13 +94,16 @@ def test_topk_rkl_bad_ids_and_ignored_positions(name, over, seed):
 
 def test_topk_rkl_gradient_only_on_the_support_and_accumulate():
     """dW rows of ids in no position's support are exactly zero (overwritten,
-    or left as they were with accumulate_dW)."""
+    also over NaNs, or left as they were with accumulate_dW)."""
     w, x = _case("small_bf16", dict(N=200, d=256, V=7000, K=16, chunk=64, T=1.0), 130)
     print("case trkl support-only dW and accumulate", flush=True)
     got = run_gpu(x, w.T, w.chunk, options=TRKL)
     used = np.zeros(w.V, dtype=bool)
     used[x["ids"].numpy().reshape(-1)] = True
     assert np.all(got["dW"][~used] == 0.0)
+    # without accumulate_dW every row is written, whatever dW held
+    poisoned = run_gpu(x, w.T, w.chunk, options=TRKL, dW_init=torch.full((w.V, w.d), float("nan")))
+    assert np.array_equal(poisoned["dW"], got["dW"])
     init = torch.randn(w.V, w.d) * 1e-2  # (the sum's fp32 rounding stays far below the tolerance)
     acc = run_gpu(x, w.T, w.chunk, options=TRKL, accumulate_dW=True, dW_init=init)
     base = init.double().numpy()
