@@ -1,8 +1,9 @@
-"""The fused forward + backward captured once into a HIP graph (torch's CUDA
-graph API on ROCm) and replayed: each replay, run after eager work and a
-synchronisation, must equal the eager result bit for bit (the path launches
-only its own kernels on the caller's stream and records no memset nodes).
-Also the forward-chunked path."""
+"""The fused forward + backward (the KL and two of the alternative losses)
+captured once into a HIP graph (torch's CUDA graph API on ROCm) and
+replayed: each replay, run after eager work and a synchronisation, must
+equal the eager result bit for bit (the path launches only its own kernels
+on the caller's stream and records no memset nodes). Also the
+forward-chunked path."""
 import numpy as np
 import pytest
 import torch
@@ -14,22 +15,29 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def test_fused_step_graph_replays_match_eager():
+# the KL, the generalised JSD and the reverse KL over the top-K support
+# (whose sparse dW counts entries with integer atomics and must still give
+# the same bits on every replay)
+LOSSES = [("kl", None), ("jsd", {"loss": 1, "beta": 0.5}), ("trkl", {"loss": 4})]
+
+
+@pytest.mark.parametrize("name,options", LOSSES, ids=[c[0] for c in LOSSES])
+def test_fused_step_graph_replays_match_eager(name, options):
     import chunked_kl_loss_amd as kd
 
     w = wl.get_config("small_bf16").with_(N=640, d=576, V=5000, K=32, chunk=256)
-    print("case graph capture fused step", flush=True)
+    print(f"case graph capture fused step, loss {name}", flush=True)
     inputs = [wl.generate(w, seed=s) for s in (51, 52, 53)]
     dev = torch.device(DEV)
     H = inputs[0]["H"].to(dev)
     W = inputs[0]["W"].to(dev)
     ids = inputs[0]["ids"].to(dev)
     lg = inputs[0]["logits"].to(dev)
-    fb, bb = kd.workspace_size(w.N, w.d, w.V, w.K, w.chunk, H.dtype)
+    fb, bb = kd.workspace_size(w.N, w.d, w.V, w.K, w.chunk, H.dtype, options=options)
     ws_f = torch.empty(fb, dtype=torch.uint8, device=dev)
     ws_b = torch.empty(bb, dtype=torch.uint8, device=dev)
     loss = torch.empty(1, dtype=torch.float32, device=dev)
-    lse = torch.empty(w.N, dtype=torch.float32, device=dev)
+    lse = torch.empty(kd.saved_shape(w.N, options), dtype=torch.float32, device=dev)
     kl = torch.empty(w.N, dtype=torch.float32, device=dev)
     g = torch.tensor([0.7], dtype=torch.float32, device=dev)
     dH = torch.empty_like(H)
@@ -37,9 +45,9 @@ def test_fused_step_graph_replays_match_eager():
 
     def step(stream):
         kd.kdkl_forward(H, W, ids, lg, w.T, w.chunk, loss=loss, row_lse=lse, row_kl=kl,
-                        workspace=ws_f, stream=stream)
+                        workspace=ws_f, stream=stream, options=options)
         kd.kdkl_backward(H, W, ids, lg, w.T, w.chunk, lse, g, dH=dH, dW=dW, workspace=ws_b,
-                         stream=stream)
+                         stream=stream, options=options)
 
     side = torch.cuda.Stream(device=dev)
     side.wait_stream(torch.cuda.current_stream(dev))
