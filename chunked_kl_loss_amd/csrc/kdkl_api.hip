@@ -387,7 +387,7 @@ static kdkl_status make_plan(int64_t N, int64_t d, int64_t V, int32_t K, int64_t
     // and the partial rows of the ids with more than one run of entries
     ok &= region(&cur, g0 / 2, &P->b_dzent);
     ok &= region(&cur, trkl_count_bytes(P->Cg, V), &P->b_cnt);
-    ok &= region(&cur, trkl_scan_bytes(V), &P->b_scans);
+    ok &= region(&cur, trkl_scan_bytes(V, P->Cg * K), &P->b_scans);
     ok &= region(&cur, g0, &P->b_list);
     ok &= region(&cur, trkl_part_bytes(P->Cg * K, d), &P->b_part);
     P->b_wt = P->b_ht = P->b_dzcv = P->b_dzvc = P->b_dhpart = P->b_dhacc = 0;

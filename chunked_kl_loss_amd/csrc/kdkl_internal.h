@@ -196,9 +196,12 @@ inline int64_t trkl_count_bytes(int64_t rows, int64_t V) {
   const int64_t nb = (rows + 255) / 256;  // positions per counting block: 256
   return (nb * V * 4 + 15) / 16 * 16;
 }
-inline int64_t trkl_scan_bytes(int64_t V) {
-  // five int64 arrays of V + 1 and four of the 256-id tiles' sums
-  return (5 * (V + 1) + 4 * ((V + 255) / 256)) * 8;
+inline int64_t trkl_scan_bytes(int64_t V, int64_t entries) {
+  // five int64 arrays of V + 1 and four of the 256-id tiles' sums, then the
+  // id of each run of 1024 entries (at most V + entries / 1024) and of each
+  // bucket of several runs (at most entries / 1024), int32
+  const int64_t tables = (V + 2 * (entries / 1024) + 2) * 4;
+  return (5 * (V + 1) + 4 * ((V + 255) / 256)) * 8 + (tables + 15) / 16 * 16;
 }
 inline int64_t trkl_part_bytes(int64_t entries, int64_t d) {
   // buckets of more than one run of 1024 entries hold at most 2 entries / 1024 runs

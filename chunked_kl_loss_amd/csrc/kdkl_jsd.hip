@@ -631,9 +631,11 @@ __global__ __launch_bounds__(kScanTile) void trkl_scan_sums_kernel(int64_t* tsum
   }
 }
 
+// Also the tables that map a run to its id and a bucket of several runs to
+// its id (for the workgroups that sum them).
 __global__ __launch_bounds__(kScanTile) void trkl_scan_out_kernel(const int64_t* total, int64_t V, const int64_t* tsum,
                                                                  int64_t* base, int64_t* rstart, int64_t* pstart,
-                                                                 int64_t* mstart) {
+                                                                 int64_t* mstart, int* run_id, int* multi_id) {
   __shared__ int64_t s_w[4][kScanWaves];
   int64_t* out[4] = {base, rstart, pstart, mstart};
   const int64_t nt = gridDim.x;
@@ -648,17 +650,12 @@ __global__ __launch_bounds__(kScanTile) void trkl_scan_out_kernel(const int64_t*
     const int64_t off = tsum[c * nt + blockIdx.x];
     if (i < V) out[c][i] = off + x[c] - own[c];
     if (blockIdx.x == nt - 1 && threadIdx.x == 0) out[c][V] = off + tot[c];
+    x[c] = off + x[c] - own[c];  // this id's exclusive offset
   }
-}
-
-// the id whose range [start[v], start[v + 1]) holds w (start nondecreasing)
-__device__ __forceinline__ int64_t find_range(const int64_t* start, int64_t V, int64_t w) {
-  int64_t lo = 0, hi = V;  // start[lo] <= w < start[hi]
-  while (hi - lo > 1) {
-    const int64_t mid = (lo + hi) >> 1;
-    if (start[mid] <= w) lo = mid; else hi = mid;
+  if (i < V) {
+    for (int64_t r = 0; r < own[1]; ++r) run_id[x[1] + r] = (int)i;
+    if (own[3]) multi_id[x[3]] = (int)i;
   }
-  return lo;
 }
 
 __global__ __launch_bounds__(256) void trkl_place_kernel(const int2* ent, const float* dz, int rows, int K,
@@ -686,14 +683,14 @@ __global__ __launch_bounds__(256) void trkl_place_kernel(const int2* ent, const 
 // it when dW is overwritten), else written as the run's partial row.
 template <typename TE>
 __global__ __launch_bounds__(256) void trkl_dw_runs_kernel(const int2* list, const int64_t* base,
-                                                           const int64_t* rstart, const int64_t* pstart, int64_t V,
-                                                           const void* H, int64_t d, float* dW, float* part,
-                                                           int overwrite) {
+                                                           const int64_t* rstart, const int64_t* pstart,
+                                                           const int* run_id, int64_t V, const void* H, int64_t d,
+                                                           float* dW, float* part, int overwrite) {
   constexpr int VEC = Vec16<TE>::kN;
   constexpr int kRep = 2;
   const int64_t w = blockIdx.x;
   if (w >= rstart[V]) return;
-  const int64_t v = find_range(rstart, V, w);
+  const int64_t v = run_id[w];
   const int64_t c = w - rstart[v];
   const int64_t runs = rstart[v + 1] - rstart[v];
   const int64_t lo = base[v] + c * kChunk;
@@ -739,11 +736,12 @@ __global__ __launch_bounds__(256) void trkl_dw_runs_kernel(const int2* list, con
 // One workgroup per bucket of more than one run: dW's row += its runs'
 // partial rows, in run order (from zero when dW is overwritten).
 __global__ __launch_bounds__(256) void trkl_dw_combine_kernel(const int64_t* rstart, const int64_t* pstart,
-                                                              const int64_t* mstart, int64_t V, int64_t d,
-                                                              const float* part, float* dW, int overwrite) {
+                                                              const int64_t* mstart, const int* multi_id, int64_t V,
+                                                              int64_t d, const float* part, float* dW,
+                                                              int overwrite) {
   const int64_t m = blockIdx.x;
   if (m >= mstart[V]) return;
-  const int64_t v = find_range(mstart, V, m);
+  const int64_t v = multi_id[m];
   const int64_t runs = rstart[v + 1] - rstart[v];
   const float* p = part + pstart[v] * d;
   float* out = dW + v * d;
@@ -839,6 +837,9 @@ hipError_t launch_trkl_dw(int dtype, const int2* ent, const float* dz, int rows,
   int64_t* rstart = scans + 2 * (V + 1);
   int64_t* pstart = scans + 3 * (V + 1);
   int64_t* mstart = scans + 4 * (V + 1);
+  // after the tiles' sums: the id of each run, then of each bucket of several runs
+  int* run_id = (int*)(scans + 5 * (V + 1) + 4 * ((V + kScanTile - 1) / kScanTile));
+  int* multi_id = run_id + V + n / kChunk + 1;
   hipError_t e = zero_bytes(cnt, trkl_count_bytes(rows, V), s);
   if (e == hipSuccess) {
     hipLaunchKernelGGL(trkl_count_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, ent, dz, n, K, V, cnt);
@@ -865,7 +866,7 @@ hipError_t launch_trkl_dw(int dtype, const int2* ent, const float* dz, int rows,
   }
   if (e == hipSuccess) {
     hipLaunchKernelGGL(trkl_scan_out_kernel, dim3((unsigned)nt), dim3(kScanTile), 0, s, total, V, tsum, base, rstart,
-                       pstart, mstart);
+                       pstart, mstart, run_id, multi_id);
     e = hipGetLastError();
   }
   if (e == hipSuccess) {
@@ -877,15 +878,15 @@ hipError_t launch_trkl_dw(int dtype, const int2* ent, const float* dz, int rows,
   // ids have more than one run
   const dim3 run_grid((unsigned)(V + n / kChunk + 1)), block(256);
   if (dtype == 1)
-    hipLaunchKernelGGL(trkl_dw_runs_kernel<uint16_t>, run_grid, block, 0, s, list, base, rstart, pstart, V, H, d,
-                       dW, part, accumulate ? 0 : 1);
+    hipLaunchKernelGGL(trkl_dw_runs_kernel<uint16_t>, run_grid, block, 0, s, list, base, rstart, pstart, run_id, V,
+                       H, d, dW, part, accumulate ? 0 : 1);
   else
-    hipLaunchKernelGGL(trkl_dw_runs_kernel<float>, run_grid, block, 0, s, list, base, rstart, pstart, V, H, d, dW,
-                       part, accumulate ? 0 : 1);
+    hipLaunchKernelGGL(trkl_dw_runs_kernel<float>, run_grid, block, 0, s, list, base, rstart, pstart, run_id, V, H,
+                       d, dW, part, accumulate ? 0 : 1);
   e = hipGetLastError();
   if (e == hipSuccess) {
     hipLaunchKernelGGL(trkl_dw_combine_kernel, dim3((unsigned)(n / kChunk + 1)), block, 0, s, rstart, pstart,
-                       mstart, V, d, part, dW, accumulate ? 0 : 1);
+                       mstart, multi_id, V, d, part, dW, accumulate ? 0 : 1);
     e = hipGetLastError();
   }
   return e;
