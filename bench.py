@@ -558,8 +558,13 @@ def main():
     traffic = load_traffic(dom, w.name)
     if trkl:  # gathers of W and H rows: bound by HBM
         achieved_gbs = ds["bytes"] / (ds["total_ms"] / 1e3) / 1e9
+        if dom == "topk_rkl":  # its forward and backward launches alternate: their mean
+            tf, tb = load_traffic("topk_rkl_fwd", w.name), load_traffic("topk_rkl_bwd", w.name)
+            traffic = (tf + tb) / 2 if tf is not None and tb is not None else None
+        else:  # (the counters cover dW's summing kernel, not the whole sort)
+            traffic = None
         roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved_gbs, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(achieved_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                     "avg_launch_ms": round(ds["total_ms"] / ds["launches"], 4),
                     "bytes_per_launch": ds["bytes"] / ds["launches"]}
     else:
