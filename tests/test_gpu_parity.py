@@ -207,21 +207,26 @@ def test_uniform_student_closed_form():
     assert np.abs(got["dH"]).max() == 0.0
 
 
-def test_empty_input():
+@pytest.mark.parametrize("options", [None, {"loss": 1, "beta": 0.5}, {"loss": 4}], ids=["kl", "jsd", "trkl"])
+def test_empty_input(options):
+    """No positions: the loss is NaN (a mean over none), dW is zeroed, or
+    left as it was with accumulate_dW; for the KL, the generalised JSD and the
+    reverse KL over the top-K support."""
     import chunked_kl_loss_amd as kd
 
     dev = "cuda:0"
+    print(f"case empty input, options {options}", flush=True)
     H = torch.zeros(0, 64, dtype=torch.bfloat16, device=dev)
     W = torch.randn(300, 64, device=dev).to(torch.bfloat16)
     ids = torch.zeros(0, 4, dtype=torch.int32, device=dev)
     lg = torch.zeros(0, 4, device=dev)
-    loss, lse, kl = kd.kdkl_forward(H, W, ids, lg, 1.0, 16)
+    loss, lse, kl = kd.kdkl_forward(H, W, ids, lg, 1.0, 16, options=options)
     dW0 = torch.full((300, 64), 5.0, device=dev)
-    dH, dW = kd.kdkl_backward(H, W, ids, lg, 1.0, 16, lse, dW=dW0.clone())
+    dH, dW = kd.kdkl_backward(H, W, ids, lg, 1.0, 16, lse, dW=dW0.clone(), options=options)
     torch.cuda.synchronize()
     assert math.isnan(loss.item())
     assert torch.count_nonzero(dW).item() == 0
-    _, dWa = kd.kdkl_backward(H, W, ids, lg, 1.0, 16, lse, dW=dW0.clone(), accumulate_dW=True)
+    _, dWa = kd.kdkl_backward(H, W, ids, lg, 1.0, 16, lse, dW=dW0.clone(), accumulate_dW=True, options=options)
     assert torch.equal(dWa, dW0)
 
 
