@@ -71,6 +71,27 @@ def test_topk_rkl_parity_vs_oracle(case, name, over, seed, blocking):
 
 
 @pytest.mark.parametrize("name,over,seed", [
+    ("tiny_fp32", dict(N=40, d=64, V=500, K=1, chunk=16, T=1.0), 137),
+    ("small_bf16", dict(N=70, d=128, V=800, K=1, chunk=32, T=2.0), 138),
+])
+def test_topk_rkl_single_entry_support(name, over, seed):
+    """K = 1: the renormalised student and teacher both put all their mass on
+    the one id, so the loss, every per-row value and both gradients are
+    exactly zero; the logsumexp over the support is that id's logit (against
+    the oracle)."""
+    w, x = _case(name, over, seed)
+    print(f"case trkl K=1 {name}", flush=True)
+    got = run_gpu(x, w.T, w.chunk, options=TRKL)
+    ref = oracle.topk_rkl_loss_and_grads(x["H"], x["W"], x["ids"], x["logits"], w.T)
+    assert got["loss"] == 0.0 and np.all(got["row_kl"] == 0.0)
+    assert np.all(got["dH"] == 0.0) and np.all(got["dW"] == 0.0)
+    kept = oracle.kept_positions(x["ids"])
+    e = maxrel(got["row_lse"][kept], ref["row_lse"][kept])
+    print(f"lse {e:.2e}", flush=True)
+    assert e <= TOL[w.dtype]["loss"]
+
+
+@pytest.mark.parametrize("name,over,seed", [
     ("tiny_fp32", dict(N=60, V=1000, K=6, chunk=16, T=1.1), 128),
     ("small_bf16", dict(N=300, d=576, V=3001, K=20, chunk=128, T=1.3), 129),
 ])
